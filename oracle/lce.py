@@ -1,0 +1,284 @@
+"""Plain float64 definitions of fused linear cross-entropy and its gradients.
+
+Sources (page title, then section / equation):
+  [P1] "Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways
+       Around It" -- "The setting" (per-token forward, mean reduction with
+       ignore_index -100), "The identity that makes fused fwbw possible" (boxed
+       dl/dz = softmax(z) - onehot(y); consequence 3, the max-shifted LSE),
+       "From dlogits to grad_input and grad_W" (scaled dlogits; boxed
+       grad_input and grad_W GEMMs; grad_b column sum), "The chunk-size trick"
+       (inc_factor / chunk_size / num_chunks table).
+  [P2] "Cut Cross Entropy visualized" -- "Breakdown: Forward Pass" (inputs E,
+       C, bias, targets; mean and sum reductions), "Breakdown: Backward Pass"
+       (S = exp(z - LSE), S - Y).
+  [P3] "Greyhound -- Cross-Entropy" -- opening formulas (loss_i and the z-loss
+       term z_i = LSE_i**2), "Kernel design" (softmax term scaled by the z-loss
+       derivative before the target column is adjusted; ignored rows get a zero
+       gradient and are not counted), "Raw kernel helper" (loss = ce_sum /
+       max(n_valid, 1)).
+
+Readings where the pages leave a step open:
+  * z-loss in the fused loss: L = c * sum_valid [LSE - z_y + mu * LSE**2]; its
+    logit gradient is p * (1 + 2 mu LSE) - onehot(y).
+  * c = 1 / max(n_valid, 1) for "mean" (so an all-ignored batch gives 0, as the
+    clamp in [P3] does), c = 1 for "sum".
+  * A target outside [0, V) that is not ignore_index is an error.
+  * The standalone helper's dlogits are the unscaled gradient of
+    ce_sum + mu * z_sum.
+
+Memory is bounded by processing rows in chunks; each row is still computed on
+its own from the definition, so chunking changes nothing numerically beyond
+BLAS summation order.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+IGNORE_INDEX = -100
+_CHUNK_BYTES = 1 << 28  # rows per chunk chosen so a float64 [rows, V] block is <= 256 MiB
+
+
+class TargetRangeError(ValueError):
+    """A target is neither ignore_index nor a vocabulary id."""
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def _valid_mask(targets: np.ndarray, V: int, ignore_index: int) -> np.ndarray:
+    """Rows that count: y != ignore_index ([P1] "The setting"); others must be in [0, V)."""
+    y = np.asarray(targets, dtype=np.int64)
+    valid = y != ignore_index
+    bad = valid & ((y < 0) | (y >= V))
+    if np.any(bad):
+        raise TargetRangeError(f"{int(bad.sum())} targets outside [0, {V}) and != {ignore_index}")
+    return valid
+
+
+def _scale(n_valid: int, reduction: str) -> float:
+    """c = 1/max(n_valid, 1) for mean ([P1] mean reduction; [P3] clamp), 1 for sum ([P2])."""
+    if reduction == "mean":
+        return 1.0 / max(n_valid, 1)
+    if reduction == "sum":
+        return 1.0
+    raise ValueError(f"reduction must be 'mean' or 'sum', got {reduction!r}")
+
+
+def _rows_per_chunk(V: int) -> int:
+    return max(1, _CHUNK_BYTES // (8 * max(V, 1)))
+
+
+def _logits(h: np.ndarray, W: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """z = W . hidden[t] (+ b) for a block of rows ([P1] "The setting"; bias per [P2] inputs)."""
+    z = h @ W.T
+    if b is not None:
+        z = z + b[None, :]
+    return z
+
+
+def _lse(z: np.ndarray) -> np.ndarray:
+    """LSE(z) = max z + log sum exp(z - max z), per row ([P1] consequence 3)."""
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+def _dlogits(z: np.ndarray, lse: np.ndarray, y: np.ndarray, valid: np.ndarray,
+             c: float, mu: float) -> np.ndarray:
+    """c * valid * (softmax(z) * (1 + 2 mu LSE) - onehot(y)) ([P1] boxed identity and
+    scaled dlogits; [P3] z-loss derivative applied before the target column)."""
+    p = np.exp(z - lse[:, None])
+    g = p * (1.0 + 2.0 * mu * lse)[:, None]
+    rows = np.nonzero(valid)[0]
+    g[rows, y[rows]] -= 1.0
+    g[~valid, :] = 0.0
+    return c * g
+
+
+def lce_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDEX,
+               z_loss: float = 0.0, reduction: str = "mean", grads: bool = True,
+               rows_per_chunk: Optional[int] = None) -> dict:
+    """Fused linear cross-entropy: loss and (optionally) grad_input, grad_W, grad_b.
+
+    hidden [BT, H], weight [V, H] (nn.Linear layout), bias [V] or None, targets
+    [BT] int.  Returns a dict with loss, n_valid, lse [BT], ce_sum, z_sum and,
+    with grads=True, grad_input [BT, H], grad_weight [V, H], grad_bias [V] or None.
+    All float results are float64.
+    """
+    h = _f64(hidden)
+    W = _f64(weight)
+    b = _f64(bias)
+    y = np.asarray(targets, dtype=np.int64)
+    BT, H = h.shape
+    V = W.shape[0]
+    valid = _valid_mask(y, V, ignore_index)
+    n_valid = int(valid.sum())
+    c = _scale(n_valid, reduction)
+    mu = float(z_loss)
+
+    lse = np.empty(BT)
+    zy = np.zeros(BT)
+    gi = np.zeros((BT, H)) if grads else None
+    gw = np.zeros((V, H)) if grads else None
+    gb = np.zeros(V) if (grads and b is not None) else None
+    R = rows_per_chunk or _rows_per_chunk(V)
+    for r0 in range(0, BT, R):
+        r1 = min(BT, r0 + R)
+        z = _logits(h[r0:r1], W, b)
+        lse[r0:r1] = _lse(z)
+        vr = valid[r0:r1]
+        idx = np.nonzero(vr)[0]
+        zy[r0 + idx] = z[idx, y[r0:r1][idx]]
+        if grads:
+            g = _dlogits(z, lse[r0:r1], y[r0:r1], vr, c, mu)
+            gi[r0:r1] = g @ W                      # grad_input = dlogits . W
+            gw += g.T @ h[r0:r1]                   # grad_W = dlogits^T . hidden
+            if gb is not None:
+                gb += g.sum(axis=0)                # grad_b = sum_t dlogits[t, :]
+    ce_terms = np.where(valid, lse - zy, 0.0)
+    z_terms = np.where(valid, lse * lse, 0.0)
+    ce_sum = math.fsum(ce_terms.tolist())
+    z_sum = math.fsum(z_terms.tolist()) if mu != 0.0 else 0.0
+    loss = c * (ce_sum + mu * z_sum)
+    out = dict(loss=loss, n_valid=n_valid, lse=lse, z_target=zy, ce_sum=ce_sum, z_sum=z_sum,
+               scale=c)
+    if grads:
+        out.update(grad_input=gi, grad_weight=gw, grad_bias=gb)
+    return out
+
+
+def ce_oracle(logits, targets, *, ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
+              rows_per_chunk: Optional[int] = None) -> dict:
+    """Standalone cross-entropy on existing logits ([P3] opening formulas, "Kernel design").
+
+    Returns ce_sum = sum_valid (LSE - x_y), z_sum = sum_valid LSE**2 (0 when z-loss is
+    off), n_valid, lse [B] and dlogits [B, V] = valid * (softmax * (1 + 2 mu LSE) - onehot),
+    the unscaled gradient of ce_sum + mu * z_sum.
+    """
+    X = _f64(logits)
+    y = np.asarray(targets, dtype=np.int64)
+    B, V = X.shape
+    valid = _valid_mask(y, V, ignore_index)
+    mu = float(z_loss)
+    lse = np.empty(B)
+    xy = np.zeros(B)
+    d = np.empty((B, V))
+    R = rows_per_chunk or _rows_per_chunk(V)
+    for r0 in range(0, B, R):
+        r1 = min(B, r0 + R)
+        z = X[r0:r1]
+        lse[r0:r1] = _lse(z)
+        vr = valid[r0:r1]
+        idx = np.nonzero(vr)[0]
+        xy[r0 + idx] = z[idx, y[r0:r1][idx]]
+        d[r0:r1] = _dlogits(z, lse[r0:r1], y[r0:r1], vr, 1.0, mu)
+    ce_sum = math.fsum(np.where(valid, lse - xy, 0.0).tolist())
+    z_sum = math.fsum(np.where(valid, lse * lse, 0.0).tolist()) if mu != 0.0 else 0.0
+    return dict(ce_sum=ce_sum, z_sum=z_sum, n_valid=int(valid.sum()), lse=lse, dlogits=d)
+
+
+# ---------------------------------------------------------------------------
+# Row-at-a-time pieces for full-size checks: each output entry is computed from
+# the same definitions as above, one row (or one vocabulary column) at a time.
+# ---------------------------------------------------------------------------
+
+def lse_rows(hidden, weight, bias, rows) -> np.ndarray:
+    """LSE of z_t = W . hidden[t] + b for the listed token rows."""
+    W = _f64(weight)
+    b = _f64(bias)
+    h = _f64(np.asarray(hidden)[np.asarray(rows)])
+    return _lse(_logits(h, W, b))
+
+
+def lse_all(hidden, weight, bias, rows_per_chunk: Optional[int] = None) -> np.ndarray:
+    """LSE of every token row (the forward statistic the backward reuses, [P2] backward)."""
+    hidden = np.asarray(hidden)
+    BT = hidden.shape[0]
+    V = np.asarray(weight).shape[0]
+    W = _f64(weight)
+    b = _f64(bias)
+    out = np.empty(BT)
+    R = rows_per_chunk or _rows_per_chunk(V)
+    for r0 in range(0, BT, R):
+        r1 = min(BT, r0 + R)
+        out[r0:r1] = _lse(_logits(_f64(hidden[r0:r1]), W, b))
+    return out
+
+
+def grad_input_rows(hidden, weight, bias, targets, rows, *, ignore_index: int = IGNORE_INDEX,
+                    z_loss: float = 0.0, reduction: str = "mean") -> np.ndarray:
+    """Rows of grad_input = dlogits . W for the listed tokens ([P1] boxed grad_input)."""
+    W = _f64(weight)
+    b = _f64(bias)
+    y_all = np.asarray(targets, dtype=np.int64)
+    V = W.shape[0]
+    valid_all = _valid_mask(y_all, V, ignore_index)
+    c = _scale(int(valid_all.sum()), reduction)
+    rows = np.asarray(rows)
+    z = _logits(_f64(np.asarray(hidden)[rows]), W, b)
+    lse = _lse(z)
+    g = _dlogits(z, lse, y_all[rows], valid_all[rows], c, float(z_loss))
+    return g @ W
+
+
+def _dlogit_columns(hidden, weight, bias, targets, vocab, lse, ignore_index, z_loss, reduction,
+                    rows_per_chunk=None):
+    """dlogits[:, v] for the listed vocabulary ids, given every row's LSE."""
+    hidden = np.asarray(hidden)
+    W = _f64(weight)
+    b = _f64(bias)
+    y = np.asarray(targets, dtype=np.int64)
+    V = W.shape[0]
+    valid = _valid_mask(y, V, ignore_index)
+    c = _scale(int(valid.sum()), reduction)
+    mu = float(z_loss)
+    vocab = np.asarray(vocab)
+    Wv = W[vocab]
+    bv = None if b is None else b[vocab]
+    BT = hidden.shape[0]
+    G = np.empty((BT, vocab.shape[0]))
+    R = rows_per_chunk or max(1, (1 << 26) // max(vocab.shape[0], 1))
+    for r0 in range(0, BT, R):
+        r1 = min(BT, r0 + R)
+        z = _f64(hidden[r0:r1]) @ Wv.T
+        if bv is not None:
+            z = z + bv[None, :]
+        p = np.exp(z - lse[r0:r1, None]) * (1.0 + 2.0 * mu * lse[r0:r1])[:, None]
+        p -= (y[r0:r1, None] == vocab[None, :])
+        p[~valid[r0:r1], :] = 0.0
+        G[r0:r1] = c * p
+    return G
+
+
+def grad_weight_rows(hidden, weight, bias, targets, vocab, lse, *,
+                     ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
+                     reduction: str = "mean") -> np.ndarray:
+    """Rows grad_W[v, :] = sum_t dlogits[t, v] hidden[t, :] ([P1] boxed grad_W), given LSE."""
+    G = _dlogit_columns(hidden, weight, bias, targets, vocab, np.asarray(lse, np.float64),
+                        ignore_index, z_loss, reduction)
+    return G.T @ _f64(hidden)
+
+
+def grad_bias_entries(hidden, weight, bias, targets, vocab, lse, *,
+                      ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
+                      reduction: str = "mean") -> np.ndarray:
+    """Entries grad_b[v] = sum_t dlogits[t, v] ([P1] grad_b column sum), given LSE."""
+    G = _dlogit_columns(hidden, weight, bias, targets, vocab, np.asarray(lse, np.float64),
+                        ignore_index, z_loss, reduction)
+    return G.sum(axis=0)
+
+
+def liger_chunk_plan(BT: int, V: int, H: int) -> dict:
+    """Token-chunk sizing of [P1] "The chunk-size trick": inc_factor = ceil(V/H),
+    chunk_size = next power of two >= ceil(BT/inc_factor), num_chunks = ceil(BT/chunk_size),
+    and the bytes of one fp32 logits chunk (chunk_size x V x 4), the extra-memory budget."""
+    inc = -(-V // H)
+    need = -(-BT // inc)
+    cs = 1
+    while cs < need:
+        cs *= 2
+    return dict(inc_factor=inc, chunk_size=cs, num_chunks=-(-BT // cs), chunk_bytes=cs * V * 4)
