@@ -42,10 +42,14 @@ def test_config_mask_counts(name, n_valid):
     BT = getattr(c, "BT", None) or c.B
     frac = c.ignore_frac
     assert BT - int(round(frac * BT)) == n_valid
-    if name in ("tiny_f32", "ce_only"):
+    if name == "tiny_f32":
         from workloads import make_config
         inp = make_config(name)
         assert int((inp.targets != -100).sum()) == n_valid
+    if name == "ce_only":
+        from workloads import ce_targets
+        y = ce_targets(c.B, c.V, seed=c.seed, ignore_frac=c.ignore_frac)
+        assert int((y != -100).sum()) == n_valid
 
 
 def test_small_config_values():

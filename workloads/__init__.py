@@ -17,5 +17,6 @@ from .synth import (  # noqa: F401
     make_ce,
     zipf_targets,
     make_config,
+    ce_targets,
     IGNORE_INDEX,
 )

@@ -35,11 +35,14 @@ IGNORE_INDEX = -100
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    # finite inputs only: u + 0x8000 stays below 2**32 for every finite float32
+    lsb = (u >> 16) & np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 def zipf_targets(rng: np.random.Generator, n: int, V: int, s: float = 1.1) -> np.ndarray:
@@ -159,16 +162,22 @@ def make_ce(B: int, V: int, *, dtype: str = "bf16", seed: int = 0, logit_std: fl
             ignore_frac: float = 0.0) -> CEInputs:
     """Seeded logits/labels for the standalone cross-entropy kernel."""
     ss = np.random.SeedSequence(seed).spawn(2)
-    g_x, g_y = (np.random.Generator(np.random.PCG64(s)) for s in ss)
+    g_x = np.random.Generator(np.random.PCG64(ss[0]))
     x = g_x.standard_normal((B, V), dtype=np.float32)
     x *= np.float32(logit_std)
-    y = g_y.integers(0, V, size=B, dtype=np.int64)
-    y = _mask_ignored(g_y, y, ignore_frac)
+    y = ce_targets(B, V, seed=seed, ignore_frac=ignore_frac)
     if dtype == "bf16":
         x = bf16_round(x)
     elif dtype != "f32":
         raise ValueError(dtype)
     return CEInputs(x, y, dtype)
+
+
+def ce_targets(B: int, V: int, *, seed: int = 0, ignore_frac: float = 0.0) -> np.ndarray:
+    """Labels of the standalone workload (uniform ids, then the ignore mask)."""
+    g_y = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(2)[1]))
+    y = g_y.integers(0, V, size=B, dtype=np.int64)
+    return _mask_ignored(g_y, y, ignore_frac)
 
 
 def make_config(name: str):
