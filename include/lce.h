@@ -1,0 +1,162 @@
+/*
+ * lce.h -- C ABI of the MI355X (gfx950) fused linear cross-entropy library (liblce.so).
+ *
+ * The operations follow three pages:
+ *   [P1] "Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It"
+ *   [P2] "Cut Cross Entropy visualized"
+ *   [P3] "Greyhound -- Cross-Entropy"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller.  The library never
+ *    allocates device memory and keeps no state between calls; scratch space is the
+ *    caller's `workspace` buffer, sized by the matching *_workspace_bytes function.
+ *  - Layouts are dense row-major: hidden [BT, H], W [V, H] (nn.Linear layout, [P1] "The
+ *    setting"), logits [B, V]; targets are int64.  Tensor pointers and the workspace must
+ *    be 16-byte aligned.  H must be a multiple of 8.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and is
+ *    asynchronous: outputs are valid once the stream has completed.  Nothing is copied
+ *    to the host unless LCE_FLAG_CHECK_TARGETS is given.
+ *  - Errors are returned, never thrown.  Argument errors (LCE_ERR_NULL .. LCE_ERR_ARG)
+ *    are detected on the host before any device work is enqueued; in that case no
+ *    output is touched.
+ *  - Identical inputs give identical output bits: every cross-workgroup reduction has a
+ *    fixed order and no floating-point atomics are used.
+ */
+#ifndef LCE_H_
+#define LCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lce_status {
+  LCE_OK = 0,
+  LCE_ERR_NULL = 1,         /* a required pointer is NULL */
+  LCE_ERR_SHAPE = 2,        /* a size is out of range (negative, V < 1, H not a multiple of 8, ...) */
+  LCE_ERR_DTYPE = 3,        /* dtype not supported by this entry point */
+  LCE_ERR_ALIGNMENT = 4,    /* a tensor or workspace pointer is not 16-byte aligned */
+  LCE_ERR_WORKSPACE = 5,    /* workspace_bytes smaller than the *_workspace_bytes requirement */
+  LCE_ERR_ARG = 6,          /* bad scalar argument (reduction, z_loss_mult < 0 or NaN, grad_b without bias) */
+  LCE_ERR_TARGET_RANGE = 7, /* (check mode only) a target is neither ignore_index nor in [0, V) */
+  LCE_ERR_HIP = 8           /* a HIP runtime call or kernel launch failed */
+} lce_status;
+
+typedef enum lce_dtype {
+  LCE_DTYPE_F32 = 0,
+  LCE_DTYPE_BF16 = 1
+} lce_dtype;
+
+typedef enum lce_reduction {
+  LCE_REDUCTION_MEAN = 0, /* loss and grads scaled by 1 / max(n_valid, 1) */
+  LCE_REDUCTION_SUM = 1   /* unscaled */
+} lce_reduction;
+
+/* Synchronise `stream` after the target pre-pass and return LCE_ERR_TARGET_RANGE if any
+ * target is neither ignore_index nor a vocabulary id.  Without it such rows are treated
+ * as ignored (no loss, zero gradient) and the call still returns LCE_OK. */
+#define LCE_FLAG_CHECK_TARGETS 1u
+
+/* Number of device kernels one lce_fwd_bwd call may launch (for lce_fwd_bwd_profiled). */
+#define LCE_NUM_STAGES 7
+
+/*
+ * lce_fwd_bwd -- fused linear cross-entropy, forward and backward in one call.
+ *
+ * Computes z_t = W . hidden[t] + b for every token without materialising the [BT, V]
+ * logits ([P1] "The setting"; [P2] "Forward Kernel"), the loss
+ *     L = c * sum_{t : y_t != ignore_index} ( LSE(z_t) - z_t[y_t] + z_loss_mult * LSE(z_t)^2 )
+ * with c = 1 / max(n_valid, 1) for LCE_REDUCTION_MEAN and c = 1 for LCE_REDUCTION_SUM
+ * ([P1] "The setting"; z-loss term from [P3] opening formulas), and its gradients
+ *     dlogits[t, :] = c * valid_t * ( softmax(z_t) * (1 + 2 * z_loss_mult * LSE(z_t)) - onehot(y_t) )
+ *     grad_input    = dlogits . W,     grad_W = dlogits^T . hidden,     grad_b = sum_t dlogits[t, :]
+ * ([P1] "The identity that makes fused fwbw possible" and "From dlogits to grad_input
+ * and grad_W"; [P3] "Kernel design" for the z-loss factor).
+ *
+ * Arguments
+ *   hidden      [BT, H] in `dtype`.                     W      [V, H] in `dtype`.
+ *   bias        [V] in `dtype`, or NULL for no bias.
+ *   targets     [BT] int64; ignore_index marks rows that contribute nothing.
+ *   BT >= 0, H >= 8 and a multiple of 8, V >= 1.
+ *   dtype       LCE_DTYPE_BF16 or LCE_DTYPE_F32 (arithmetic: products accumulated in fp32;
+ *               softmax statistics in fp32; bf16 dlogits operands rounded to nearest even).
+ *   ignore_index  target value of ignored rows (usually -100).
+ *   z_loss_mult   >= 0; 0 disables the z-loss term.
+ *   reduction   LCE_REDUCTION_MEAN or LCE_REDUCTION_SUM.
+ *   flags       0 or LCE_FLAG_CHECK_TARGETS.
+ *   loss_out    device float[1]: the loss L.                          (required)
+ *   grad_input  device [BT, H] in `dtype`, fully overwritten, or NULL to skip it.
+ *   grad_W      device [V, H] in `dtype`, fully overwritten, or NULL to skip it.
+ *   grad_b      device [V] in `dtype`, fully overwritten, or NULL; must be NULL when bias is NULL.
+ *   n_valid_out device int64[1]: number of rows with y != ignore_index, or NULL.
+ *   lse_out     device float[BT]: LSE(z_t) per row (the statistic the backward reuses,
+ *               [P2] "Breakdown: Backward Pass"), or NULL.
+ *   workspace   device scratch of at least lce_fwd_bwd_workspace_bytes(BT, H, V, dtype, flags)
+ *               bytes; contents on entry are ignored and on exit undefined.
+ *   stream      hipStream_t to enqueue on.
+ */
+lce_status lce_fwd_bwd(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                       int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                       float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
+                       void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                       float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as lce_fwd_bwd; in addition, when ev_start/ev_stop are non-NULL arrays of
+ * LCE_NUM_STAGES hipEvent_t handles created by the caller, records ev_start[k] and
+ * ev_stop[k] on `stream` around the launch of stage k (names: lce_stage_name).  Stages
+ * that a call does not launch get no records.  For per-kernel timing by benchmarks. */
+lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* bias,
+                                const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+                                lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
+                                lce_reduction reduction, uint32_t flags, float* loss_out,
+                                void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                                float* lse_out, void* workspace, size_t workspace_bytes,
+                                void* stream, void* const* ev_start, void* const* ev_stop);
+
+/* Exact number of workspace bytes lce_fwd_bwd needs for these sizes (its whole extra
+ * device memory), or 0 if the sizes are invalid. */
+size_t lce_fwd_bwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);
+
+/* Name of stage k of lce_fwd_bwd ("targets", "fwd_lse", "target_logit", "merge",
+ * "loss", "bwd_dinput", "bwd_dweight"), or NULL if k is out of range. */
+const char* lce_stage_name(int k);
+
+/*
+ * lce_ce_with_grad_inplace -- cross-entropy on existing logits, with dlogits written over
+ * the logits in place ([P3] "Kernel design" and "Raw kernel helper").
+ *
+ * For each row i of logits [B, V]:  ce_i = LSE(x_i) - x_i[y_i];  z_i = LSE(x_i)^2.
+ *   ce_sum_out  device float[1] = sum over valid rows of ce_i.
+ *   z_sum_out   device float[1] = sum over valid rows of z_i if z_loss_mult != 0, else 0.
+ *   n_valid_out device int64[1] = number of rows with y_i != ignore_index.
+ * On return logits holds the gradient of ce_sum + z_loss_mult * z_sum:
+ *   dlogits_i = valid_i * ( softmax(x_i) * (1 + 2 * z_loss_mult * LSE(x_i)) - onehot(y_i) ),
+ * rounded to the logits' dtype; ignored rows are written as zeros.  A mean-reduced loss is
+ * ce_sum / max(n_valid, 1) and its gradient is these dlogits times the same factor.
+ *   logits      [B, V] in `dtype` (LCE_DTYPE_BF16 or LCE_DTYPE_F32), read then overwritten.
+ *   targets     [B] int64.   B >= 0, V >= 1.   z_loss_mult >= 0.
+ *   workspace   >= lce_ce_workspace_bytes(B, V, dtype) bytes.
+ * Targets outside [0, V) that are not ignore_index are treated as ignored.
+ */
+lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_t B, int64_t V,
+                                    lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
+                                    float* ce_sum_out, float* z_sum_out, int64_t* n_valid_out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes lce_ce_with_grad_inplace needs (per-row partial results), or 0 if invalid. */
+size_t lce_ce_workspace_bytes(int64_t B, int64_t V, lce_dtype dtype);
+
+/* Human-readable text for a status code (static storage). */
+const char* lce_status_string(lce_status s);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* lce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H_ */

@@ -1,0 +1,194 @@
+"""Fused linear cross-entropy for MI355X (gfx950): Python binding of liblce.so.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/lce.h); this module only marshals torch tensors (device memory and the
+current stream) into that ABI.  There is no CPU or PyTorch fallback: if the
+library is missing or the tensors are not on a GPU, the calls raise.
+
+  lce_fwd_bwd(hidden, weight, bias, targets, ...)   -> dict(loss, grad_input, grad_weight, grad_bias, n_valid, lse)
+  lce_ce_with_grad_inplace(logits, targets, ...)    -> (ce_sum, z_sum, n_valid); logits become dlogits
+  linear_cross_entropy(hidden, weight, targets, bias=None, ...)  -> loss with autograd
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import LCEError, load  # noqa: F401
+
+__all__ = ["lce_fwd_bwd", "lce_ce_with_grad_inplace", "linear_cross_entropy", "fwd_bwd_workspace_bytes",
+           "ce_workspace_bytes", "stage_names", "version", "LCEError", "load"]
+
+_DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_F32}
+_REDUCTIONS = {"mean": _lib.REDUCTION_MEAN, "sum": _lib.REDUCTION_SUM}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    return _DTYPES[t.dtype]
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU path exists)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def version() -> str:
+    return load().lce_version().decode()
+
+
+def stage_names():
+    lib = load()
+    return [lib.lce_stage_name(k).decode() for k in range(_lib.NUM_STAGES)]
+
+
+def fwd_bwd_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype) -> int:
+    return int(load().lce_fwd_bwd_workspace_bytes(BT, H, V, _DTYPES[dtype], 0))
+
+
+def ce_workspace_bytes(B: int, V: int, dtype: torch.dtype) -> int:
+    return int(load().lce_ce_workspace_bytes(B, V, _DTYPES[dtype]))
+
+
+def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                targets: torch.Tensor, *, ignore_index: int = -100, z_loss: float = 0.0,
+                reduction: str = "mean", grad_input: bool = True, grad_weight: bool = True,
+                grad_bias: Optional[bool] = None, return_lse: bool = False,
+                check_targets: bool = False, workspace: Optional[torch.Tensor] = None,
+                out: Optional[dict] = None, events=None) -> dict:
+    """One call of lce_fwd_bwd: loss and the requested gradients (fully overwritten).
+
+    `out` may hold preallocated tensors under the keys loss, grad_input, grad_weight,
+    grad_bias, n_valid, lse; `events` = (start_list, stop_list) of hipEvent_t handles
+    selects lce_fwd_bwd_profiled.
+    """
+    lib = load()
+    _need_gpu(hidden, weight, bias, targets)
+    BT, H = hidden.shape
+    V = weight.shape[0]
+    dt = _dtype_code(hidden)
+    if weight.dtype != hidden.dtype or (bias is not None and bias.dtype != hidden.dtype):
+        raise TypeError("hidden, weight and bias must share a dtype")
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    if grad_bias is None:
+        grad_bias = bias is not None
+    dev = hidden.device
+    o = dict(out or {})
+    loss = o.get("loss")
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    gi = o.get("grad_input") if grad_input else None
+    if grad_input and gi is None:
+        gi = torch.empty_like(hidden)
+    gw = o.get("grad_weight") if grad_weight else None
+    if grad_weight and gw is None:
+        gw = torch.empty_like(weight)
+    gb = o.get("grad_bias") if grad_bias else None
+    if grad_bias and gb is None:
+        gb = torch.empty_like(bias)
+    nv = o.get("n_valid")
+    if nv is None:
+        nv = torch.empty((), dtype=torch.int64, device=dev)
+    lse = o.get("lse") if return_lse else None
+    if return_lse and lse is None:
+        lse = torch.empty(BT, dtype=torch.float32, device=dev)
+    flags = _lib.FLAG_CHECK_TARGETS if check_targets else 0
+    need = int(lib.lce_fwd_bwd_workspace_bytes(BT, H, V, dt, flags))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (_ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), BT, H, V, dt, ignore_index,
+            float(z_loss), _REDUCTIONS[reduction], flags, _ptr(loss), _ptr(gi), _ptr(gw), _ptr(gb),
+            _ptr(nv), _ptr(lse), _ptr(workspace), workspace.numel(), stream)
+    if events is None:
+        st = lib.lce_fwd_bwd(*args)
+    else:
+        arr_t = ctypes.c_void_p * _lib.NUM_STAGES
+        ev0 = arr_t(*[ctypes.c_void_p(e) for e in events[0]])
+        ev1 = arr_t(*[ctypes.c_void_p(e) for e in events[1]])
+        st = lib.lce_fwd_bwd_profiled(*args, ev0, ev1)
+    _lib.check(st, "lce_fwd_bwd")
+    return dict(loss=loss, grad_input=gi, grad_weight=gw, grad_bias=gb, n_valid=nv, lse=lse,
+                workspace=workspace)
+
+
+def lce_ce_with_grad_inplace(logits: torch.Tensor, targets: torch.Tensor, *, ignore_index: int = -100,
+                             z_loss: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                             out: Optional[dict] = None):
+    """Cross-entropy on existing logits; logits are overwritten with dlogits.
+
+    Returns device tensors (ce_sum, z_sum, n_valid); the mean loss is
+    ce_sum / n_valid.clamp(min=1).
+    """
+    lib = load()
+    _need_gpu(logits, targets)
+    B, V = logits.shape
+    dt = _dtype_code(logits)
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    dev = logits.device
+    o = dict(out or {})
+    ce = o.get("ce_sum")
+    if ce is None:
+        ce = torch.empty((), dtype=torch.float32, device=dev)
+    zs = o.get("z_sum")
+    if zs is None:
+        zs = torch.empty((), dtype=torch.float32, device=dev)
+    nv = o.get("n_valid")
+    if nv is None:
+        nv = torch.empty((), dtype=torch.int64, device=dev)
+    need = int(lib.lce_ce_workspace_bytes(B, V, dt))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = lib.lce_ce_with_grad_inplace(_ptr(logits), _ptr(targets), B, V, dt, ignore_index, float(z_loss),
+                                      _ptr(ce), _ptr(zs), _ptr(nv), _ptr(workspace), workspace.numel(),
+                                      stream)
+    _lib.check(st, "lce_ce_with_grad_inplace")
+    return ce, zs, nv
+
+
+class _LinearCrossEntropy(torch.autograd.Function):
+    """Loss with gradients computed in the same fused call (the backward only rescales)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss, reduction):
+        r = lce_fwd_bwd(hidden.contiguous(), weight.contiguous(),
+                        None if bias is None else bias.contiguous(), targets.contiguous(),
+                        ignore_index=ignore_index, z_loss=z_loss, reduction=reduction,
+                        grad_input=ctx.needs_input_grad[0], grad_weight=ctx.needs_input_grad[1],
+                        grad_bias=bias is not None and ctx.needs_input_grad[2])
+        ctx.save_for_backward(r["grad_input"], r["grad_weight"], r["grad_bias"])
+        return r["loss"]
+
+    @staticmethod
+    def backward(ctx, g):
+        gi, gw, gb = ctx.saved_tensors
+        scale = None if g is None else g.to(torch.float32)
+
+        def mul(t):
+            if t is None or scale is None:
+                return t
+            return (t.to(torch.float32) * scale).to(t.dtype)
+
+        return mul(gi), mul(gw), mul(gb), None, None, None, None
+
+
+def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, *, ignore_index: int = -100,
+                         z_loss: float = 0.0, reduction: str = "mean") -> torch.Tensor:
+    """loss = reduction over rows of CE(hidden @ weight.T + bias, targets) (+ z-loss), differentiable."""
+    return _LinearCrossEntropy.apply(hidden, weight, bias, targets, ignore_index, z_loss, reduction)

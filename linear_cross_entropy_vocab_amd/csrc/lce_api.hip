@@ -1,0 +1,198 @@
+// Host side of the C ABI declared in include/lce.h: argument validation (before any HIP
+// call), workspace sizing and carving, and the launch sequence on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "lce.h"
+#include "lce_launch.h"
+
+namespace lce {
+
+size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
+  (void)H;
+  (void)bf16;
+  const int64_t bt = BT > 0 ? BT : 1;
+  const int64_t nt = (V + kFwdTileV - 1) / kFwdTileV;
+  const int64_t nblk = (bt + kMergeThreads - 1) / kMergeThreads;
+  size_t n = ws_align(16);                         // n_valid, n_bad
+  n += ws_align((size_t)nt * (size_t)bt * 4);      // lse_part
+  n += ws_align((size_t)bt * 4);                   // lse
+  n += ws_align((size_t)bt * 4);                   // zy
+  n += ws_align((size_t)nblk * 2 * 8);             // block sums
+  return n;
+}
+
+FusedWs fused_carve(void* ws, int64_t BT, int64_t V) {
+  const int64_t bt = BT > 0 ? BT : 1;
+  FusedWs w;
+  w.nt = (V + kFwdTileV - 1) / kFwdTileV;
+  w.nblk = (BT + kMergeThreads - 1) / kMergeThreads;
+  const int64_t nblk_alloc = (bt + kMergeThreads - 1) / kMergeThreads;
+  char* p = static_cast<char*>(ws);
+  w.n_valid = reinterpret_cast<int64_t*>(p);
+  w.n_bad = reinterpret_cast<int32_t*>(p + 8);
+  p += ws_align(16);
+  w.lse_part = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)w.nt * (size_t)bt * 4);
+  w.lse = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)bt * 4);
+  w.zy = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)bt * 4);
+  w.blk = reinterpret_cast<double*>(p);
+  (void)nblk_alloc;
+  return w;
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static const char* kStageNames[kNumStages] = {"targets", "fwd_lse", "target_logit", "merge",
+                                               "loss",    "bwd_dinput", "bwd_dweight"};
+
+static lce_status fused_call(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                             int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                             float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
+                             void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                             float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* ev_start, void* const* ev_stop) {
+  // ---- validation: no HIP calls before this block has passed
+  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
+  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 40) || H > ((int64_t)1 << 24)) return LCE_ERR_SHAPE;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_DTYPE;
+  if (W == nullptr || loss_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
+  if (BT > 0 && (hidden == nullptr || targets == nullptr)) return LCE_ERR_NULL;
+  if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_SUM) return LCE_ERR_ARG;
+  if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
+  if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
+  if ((flags & ~LCE_FLAG_CHECK_TARGETS) != 0) return LCE_ERR_ARG;
+  const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(grad_input, 16) || !aligned(grad_W, 16) ||
+      !aligned(workspace, 16) || !aligned(bias, es) || !aligned(grad_b, es) || !aligned(targets, 8) ||
+      !aligned(loss_out, 4) || !aligned(n_valid_out, 8) || !aligned(lse_out, 4))
+    return LCE_ERR_ALIGNMENT;
+  if (workspace_bytes < fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16)) return LCE_ERR_WORKSPACE;
+
+  FusedArgs a;
+  a.hidden = hidden;
+  a.W = W;
+  a.bias = bias;
+  a.targets = targets;
+  a.BT = BT;
+  a.H = H;
+  a.V = V;
+  a.bf16 = dtype == LCE_DTYPE_BF16;
+  a.ignore_index = ignore_index;
+  a.mu = z_loss_mult;
+  a.mean = reduction == LCE_REDUCTION_MEAN;
+  a.loss_out = loss_out;
+  a.grad_input = grad_input;
+  a.grad_W = grad_W;
+  a.grad_b = grad_b;
+  a.n_valid_out = n_valid_out;
+  a.lse_out = lse_out;
+  const FusedWs w = fused_carve(workspace, BT, V);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  typedef hipError_t (*Launch)(const FusedArgs&, const FusedWs&, hipStream_t);
+  static const Launch kLaunch[kNumStages] = {launch_targets,    launch_fwd_lse,    launch_target_logit,
+                                             launch_merge,      launch_loss,       launch_bwd_dinput,
+                                             launch_bwd_dweight};
+  for (int k = 0; k < kNumStages; ++k) {
+    if (ev_start && ev_start[k] && hipEventRecord(static_cast<hipEvent_t>(ev_start[k]), st) != hipSuccess)
+      return LCE_ERR_HIP;
+    if (kLaunch[k](a, w, st) != hipSuccess) return LCE_ERR_HIP;
+    if (ev_stop && ev_stop[k] && hipEventRecord(static_cast<hipEvent_t>(ev_stop[k]), st) != hipSuccess)
+      return LCE_ERR_HIP;
+    if (k == kStTargets && (flags & LCE_FLAG_CHECK_TARGETS)) {
+      int32_t bad = 0;
+      if (hipMemcpyAsync(&bad, w.n_bad, sizeof(bad), hipMemcpyDeviceToHost, st) != hipSuccess) return LCE_ERR_HIP;
+      if (hipStreamSynchronize(st) != hipSuccess) return LCE_ERR_HIP;
+      if (bad != 0) return LCE_ERR_TARGET_RANGE;
+    }
+  }
+  return LCE_OK;
+}
+
+}  // namespace lce
+
+extern "C" {
+
+size_t lce_fwd_bwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
+  (void)flags;
+  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return 0;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return 0;
+  return lce::fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16);
+}
+
+lce_status lce_fwd_bwd(const void* hidden, const void* W, const void* bias, const int64_t* targets, int64_t BT,
+                       int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
+                       lce_reduction reduction, uint32_t flags, float* loss_out, void* grad_input,
+                       void* grad_W, void* grad_b, int64_t* n_valid_out, float* lse_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
+                         flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
+                         workspace_bytes, stream, nullptr, nullptr);
+}
+
+lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                                int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                                float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
+                                void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                                float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* ev_start, void* const* ev_stop) {
+  return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
+                         flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
+                         workspace_bytes, stream, ev_start, ev_stop);
+}
+
+const char* lce_stage_name(int k) {
+  if (k < 0 || k >= lce::kNumStages) return nullptr;
+  return lce::kStageNames[k];
+}
+
+size_t lce_ce_workspace_bytes(int64_t B, int64_t V, lce_dtype dtype) {
+  if (B < 0 || V < 1) return 0;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return 0;
+  return lce::ce_workspace_bytes(B);
+}
+
+lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_t B, int64_t V, lce_dtype dtype,
+                                    int64_t ignore_index, float z_loss_mult, float* ce_sum_out,
+                                    float* z_sum_out, int64_t* n_valid_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (B < 0 || V < 1 || V > ((int64_t)1 << 40) || B > ((int64_t)1 << 31) - 1) return LCE_ERR_SHAPE;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_DTYPE;
+  if (ce_sum_out == nullptr || z_sum_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
+  if (B > 0 && (logits == nullptr || targets == nullptr)) return LCE_ERR_NULL;
+  if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
+  const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
+  if (!lce::aligned(logits, 16) || !lce::aligned(workspace, 16) || !lce::aligned(targets, 8) ||
+      !lce::aligned(ce_sum_out, 4) || !lce::aligned(z_sum_out, 4) || !lce::aligned(n_valid_out, 8))
+    return LCE_ERR_ALIGNMENT;
+  (void)es;
+  if (workspace_bytes < lce::ce_workspace_bytes(B)) return LCE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (lce::launch_ce_inplace(logits, dtype == LCE_DTYPE_BF16, targets, B, V, ignore_index, z_loss_mult,
+                             ce_sum_out, z_sum_out, n_valid_out, workspace, st) != hipSuccess)
+    return LCE_ERR_HIP;
+  return LCE_OK;
+}
+
+const char* lce_status_string(lce_status s) {
+  switch (s) {
+    case LCE_OK: return "ok";
+    case LCE_ERR_NULL: return "a required pointer is NULL";
+    case LCE_ERR_SHAPE: return "invalid shape (need BT >= 0, V >= 1, H >= 8 and a multiple of 8)";
+    case LCE_ERR_DTYPE: return "unsupported dtype";
+    case LCE_ERR_ALIGNMENT: return "misaligned pointer (tensors and workspace must be 16-byte aligned)";
+    case LCE_ERR_WORKSPACE: return "workspace too small";
+    case LCE_ERR_ARG: return "invalid argument";
+    case LCE_ERR_TARGET_RANGE: return "a target is neither ignore_index nor in [0, V)";
+    case LCE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* lce_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Device-side building blocks shared by the gfx950 kernels: storage types, bf16
+// rounding, MFMA fragment types and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round to nearest bfloat16, ties to even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Element type traits: storage type and conversions.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float to_f(bf16_t v) { return bf2f(v); }
+  __device__ __forceinline__ static bf16_t from_f(float v) { return f2bf(v); }
+};
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float to_f(float v) { return v; }
+  __device__ __forceinline__ static float from_f(float v) { return v; }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32 tiles with K = 16 per step.
+//
+// Operand fragment: each lane holds 8 consecutive K values of one row (A) or one
+// column (B): lane l covers row/col (l % 32) and K values 8*(l/32) .. 8*(l/32)+7.
+// For bf16 that is one v_mfma_f32_32x32x16_bf16; for fp32 it is eight
+// v_mfma_f32_32x32x2_f32 where sub-step s pairs K values s and 8+s (the same
+// K permutation on both operands, so the sum over K is unchanged).
+// Accumulator layout (both): lane l holds column l % 32 and rows
+//   8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  bf16x8_t v;
+};
+template <> struct Frag<float> {
+  float v[8];
+};
+
+__device__ __forceinline__ void mfma_32x32x16(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x16_t& c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_32x32x16(const Frag<float>& a, const Frag<float>& b, f32x16_t& c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+
+// Row index (within a 32x32 accumulator tile) of accumulator register r in lane l.
+__device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Load 8 consecutive elements (16 B for bf16, 32 B for fp32); ptr must be 16-byte aligned.
+__device__ __forceinline__ void load8(Frag<bf16_t>& f, const bf16_t* p) {
+  f.v = *reinterpret_cast<const bf16x8_t*>(p);
+}
+__device__ __forceinline__ void load8(Frag<float>& f, const float* p) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void zero8(Frag<bf16_t>& f) { f.v = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0}; }
+__device__ __forceinline__ void zero8(Frag<float>& f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane (4*r + c) supplies the address of
+// row r, columns 4c..4c+3 of a 4 x 16 block of 16-bit values; lane i of the group receives
+// column i, rows 0..3.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Combine two (max, sum-of-exp(x - max)) pairs.  A pair with m = -inf and s = 0 is the
+// identity; no -inf - -inf is ever formed.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  if (m2 > m) {
+    s = s * __expf(m - m2) + s2;
+    m = m2;
+  } else if (m2 != -INFINITY) {
+    s = s + s2 * __expf(m2 - m);
+  }
+}
+
+__device__ __forceinline__ void wave_ms(float& m, float& s) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    float m2 = __shfl_xor(m, off, kWave);
+    float s2 = __shfl_xor(s, off, kWave);
+    ms_merge(m, s, m2, s2);
+  }
+}
+
+}  // namespace lce

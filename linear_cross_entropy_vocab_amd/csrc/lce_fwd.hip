@@ -1,0 +1,354 @@
+// Forward half of fused linear cross-entropy on gfx950.
+//
+//   targets  : valid-row count (integer) and range check.
+//   fwd_lse  : vocabulary-tiled logits GEMM on MFMA with a fused fp32 (max, sum-exp)
+//              epilogue; one partial log-sum-exp per (vocab tile, token).  The logits
+//              tile lives only in accumulator registers ("Fused Linear Cross-Entropy: The
+//              Math, the Memory Wall, and Two Ways Around It", Strategy 2, forward and the
+//              online-softmax update; "Cut Cross Entropy visualized", "Forward Kernel").
+//   target_logit : indexed dot z_y = W[y] . h + b[y] ("Cut Cross Entropy visualized",
+//              "Breakdown: Forward Pass", first kernel).
+//   merge    : log-add-exp of the partials per token (the global LSE, starting from -inf),
+//              per-row loss terms and fixed-order block sums.
+//   loss     : final fixed-order sum and the 1/max(n_valid, 1) scale.
+#include "lce_common.h"
+#include "lce_launch.h"
+
+namespace lce {
+
+// ------------------------------------------------------------------ targets
+constexpr int kTgtThreads = 1024;
+
+__global__ void __launch_bounds__(kTgtThreads) targets_kernel(const int64_t* __restrict__ y, int64_t BT,
+                                                               int64_t V, int64_t ignore_index,
+                                                               int64_t* n_valid, int32_t* n_bad) {
+  __shared__ long long s_v[kTgtThreads / kWave], s_b[kTgtThreads / kWave];
+  long long nv = 0, nb = 0;
+  for (int64_t i = threadIdx.x; i < BT; i += kTgtThreads) {
+    const int64_t t = y[i];
+    if (t != ignore_index) {
+      if (t >= 0 && t < V) ++nv;
+      else ++nb;
+    }
+  }
+  nv = wave_sum_ll(nv);
+  nb = wave_sum_ll(nb);
+  if (threadIdx.x % kWave == 0) { s_v[threadIdx.x / kWave] = nv; s_b[threadIdx.x / kWave] = nb; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long a = 0, b = 0;
+    for (int i = 0; i < kTgtThreads / kWave; ++i) { a += s_v[i]; b += s_b[i]; }
+    *n_valid = a;
+    *n_bad = (int32_t)(b > 0x7fffffff ? 0x7fffffff : b);
+  }
+}
+
+hipError_t launch_targets(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  hipLaunchKernelGGL(targets_kernel, dim3(1), dim3(kTgtThreads), 0, st, a.targets, a.BT, a.V,
+                     a.ignore_index, w.n_valid, w.n_bad);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fwd_lse
+// Workgroup tile: kFwdTileV (256) vocabulary rows x kFwdTileT (128) tokens, computed as
+// z^T = W_tile . h_tile^T so that the accumulator's register index runs over vocabulary
+// rows and the per-token reduction over the vocabulary stays mostly inside each lane.
+// Four waves in a 2 x 2 grid; each wave owns 128 vocab rows x 64 tokens = 4 x 2 MFMA tiles.
+// K is staged through LDS 128 bytes per row at a time, double buffered.
+constexpr int kFwdThreads = 256;
+constexpr int kStageBytes = 128;          // K bytes per row per stage
+constexpr int kLdsRow = kStageBytes + 16; // padded LDS row stride (bank-conflict free 16 B reads)
+
+__device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t n) {
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of
+  // the tile order so workgroups sharing operand tiles share an L2.
+  const int64_t x = id % 8, q = id / 8, Q = n / 8, r = n % 8;
+  return (x < r) ? x * (Q + 1) + q : r * (Q + 1) + (x - r) * Q + q;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kFwdThreads) fwd_lse_kernel(const T* __restrict__ W,
+                                                               const T* __restrict__ h,
+                                                               const T* __restrict__ bias,
+                                                               int64_t BT, int64_t H, int64_t V,
+                                                               int64_t nt_v, int64_t nt_t,
+                                                               float* __restrict__ lse_part) {
+  constexpr int ES = sizeof(T);
+  constexpr int EPC = 16 / ES;                 // elements per 16 B chunk
+  constexpr int KSTEPS = kStageBytes / (16 * ES);  // MFMA k-steps (16 elements) per stage
+  constexpr int A_CH = kFwdTileV * 8 / kFwdThreads;  // 16 B chunks per thread per stage
+  constexpr int B_CH = kFwdTileT * 8 / kFwdThreads;
+  __shared__ __attribute__((aligned(16))) char sA[2][kFwdTileV * kLdsRow];
+  __shared__ __attribute__((aligned(16))) char sB[2][kFwdTileT * kLdsRow];
+  __shared__ float s_bias[kFwdTileV];
+  __shared__ float red_m[2][kFwdTileT], red_s[2][kFwdTileT];
+
+  const int64_t nwg = nt_v * nt_t;
+  const int64_t id = xcd_remap(blockIdx.x, nwg);
+  // grouped raster: groups of 8 token tiles, vocab tiles inside a group
+  constexpr int GT = 8;
+  const int64_t group = id / (GT * nt_v);
+  const int64_t first_t = group * GT;
+  const int64_t gsize = (nt_t - first_t) < GT ? (nt_t - first_t) : GT;
+  const int64_t in_g = id % (GT * nt_v);
+  const int64_t ttile = first_t + in_g % gsize;
+  const int64_t vtile = in_g / gsize;
+  const int64_t v0 = vtile * kFwdTileV;
+  const int64_t t0 = ttile * kFwdTileT;
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wv = wave >> 1, wt = wave & 1;
+
+  if (tid < kFwdTileV) {
+    const int64_t v = v0 + tid;
+    s_bias[tid] = (bias != nullptr && v < V) ? Elem<T>::to_f(bias[v]) : 0.f;
+  }
+
+  uint4 ra[A_CH], rb[B_CH];
+  const int64_t nk = (H * ES + kStageBytes - 1) / kStageBytes;
+
+  auto gload = [&](int64_t ks) {
+    const int64_t kel0 = ks * (kStageBytes / ES);
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + kFwdThreads * i, row = c >> 3, cc = c & 7;
+      const int64_t v = v0 + row, k = kel0 + cc * EPC;
+      ra[i] = (v < V && k < H) ? *reinterpret_cast<const uint4*>(W + v * H + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + kFwdThreads * i, row = c >> 3, cc = c & 7;
+      const int64_t t = t0 + row, k = kel0 + cc * EPC;
+      rb[i] = (t < BT && k < H) ? *reinterpret_cast<const uint4*>(h + t * H + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + kFwdThreads * i, row = c >> 3, cc = c & 7;
+      *reinterpret_cast<uint4*>(&sA[buf][row * kLdsRow + cc * 16]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + kFwdThreads * i, row = c >> 3, cc = c & 7;
+      *reinterpret_cast<uint4*>(&sB[buf][row * kLdsRow + cc * 16]) = rb[i];
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int64_t ks = 0; ks < nk; ++ks) {
+    const int buf = (int)(ks & 1);
+    if (ks + 1 < nk) gload(ks + 1);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int boff = kk * 16 * ES + (lane >> 5) * 8 * ES;
+      Frag<T> fa[4], fb[2];
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+        load8(fa[vb], reinterpret_cast<const T*>(&sA[buf][(wv * 128 + vb * 32 + (lane & 31)) * kLdsRow + boff]));
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        load8(fb[tb], reinterpret_cast<const T*>(&sB[buf][(wt * 64 + tb * 32 + (lane & 31)) * kLdsRow + boff]));
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fa[vb], fb[tb], acc[vb][tb]);
+    }
+    if (ks + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: per token column, (max, sum exp) over this wave's 128 vocab rows, then over
+  // the two vocab halves of the tile; columns past V count as -inf (they are skipped).
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vr = wv * 128 + vb * 32 + acc_row(lane, r);
+        if (v0 + vr < V) m = fmaxf(m, acc[vb][tb][r] + s_bias[vr]);
+      }
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int vr = wv * 128 + vb * 32 + acc_row(lane, r);
+          if (v0 + vr < V) s += __expf(acc[vb][tb][r] + s_bias[vr] - m);
+        }
+    }
+    ms_merge(m, s, __shfl_xor(m, 32, kWave), __shfl_xor(s, 32, kWave));
+    if (lane < 32) {
+      red_m[wv][wt * 64 + tb * 32 + lane] = m;
+      red_s[wv][wt * 64 + tb * 32 + lane] = s;
+    }
+  }
+  __syncthreads();
+  if (tid < kFwdTileT) {
+    float m = red_m[0][tid], s = red_s[0][tid];
+    ms_merge(m, s, red_m[1][tid], red_s[1][tid]);
+    const int64_t t = t0 + tid;
+    if (t < BT) lse_part[vtile * BT + t] = m + __logf(s);
+  }
+}
+
+hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  if (a.BT == 0) return hipSuccess;
+  const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
+  const int64_t n = w.nt * nt_t;
+  if (a.bf16)
+    hipLaunchKernelGGL(fwd_lse_kernel<bf16_t>, dim3((unsigned)n), dim3(kFwdThreads), 0, st,
+                       (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
+                       a.V, w.nt, nt_t, w.lse_part);
+  else
+    hipLaunchKernelGGL(fwd_lse_kernel<float>, dim3((unsigned)n), dim3(kFwdThreads), 0, st,
+                       (const float*)a.W, (const float*)a.hidden, (const float*)a.bias, a.BT, a.H, a.V,
+                       w.nt, nt_t, w.lse_part);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ target_logit
+constexpr int kTlWaves = 4;
+
+template <typename T>
+__global__ void __launch_bounds__(kTlWaves * kWave) target_logit_kernel(
+    const T* __restrict__ h, const T* __restrict__ W, const T* __restrict__ bias,
+    const int64_t* __restrict__ y, int64_t BT, int64_t H, int64_t V, int64_t ignore_index,
+    float* __restrict__ zy) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kTlWaves + threadIdx.x / kWave;
+  if (t >= BT) return;
+  const int64_t yt = y[t];
+  if (yt == ignore_index || yt < 0 || yt >= V) {
+    if (lane == 0) zy[t] = 0.f;
+    return;
+  }
+  const T* hr = h + t * H;
+  const T* wr = W + yt * H;
+  float acc = 0.f;
+  for (int64_t c = lane; c < H / EPC; c += kWave) {
+    Frag<T> fh, fw;  // 8 elements; for fp32 only the first 4 are used per chunk
+    if constexpr (sizeof(T) == 2) {
+      load8(fh, hr + c * EPC);
+      load8(fw, wr + c * EPC);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += bf2f((bf16_t)fh.v[e]) * bf2f((bf16_t)fw.v[e]);
+    } else {
+      const float4 a4 = reinterpret_cast<const float4*>(hr)[c];
+      const float4 b4 = reinterpret_cast<const float4*>(wr)[c];
+      acc += a4.x * b4.x + a4.y * b4.y + a4.z * b4.z + a4.w * b4.w;
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) zy[t] = acc + (bias != nullptr ? Elem<T>::to_f(bias[yt]) : 0.f);
+}
+
+hipError_t launch_target_logit(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  if (a.BT == 0) return hipSuccess;
+  const unsigned g = (unsigned)((a.BT + kTlWaves - 1) / kTlWaves);
+  if (a.bf16)
+    hipLaunchKernelGGL(target_logit_kernel<bf16_t>, dim3(g), dim3(kTlWaves * kWave), 0, st,
+                       (const bf16_t*)a.hidden, (const bf16_t*)a.W, (const bf16_t*)a.bias, a.targets, a.BT,
+                       a.H, a.V, a.ignore_index, w.zy);
+  else
+    hipLaunchKernelGGL(target_logit_kernel<float>, dim3(g), dim3(kTlWaves * kWave), 0, st,
+                       (const float*)a.hidden, (const float*)a.W, (const float*)a.bias, a.targets, a.BT,
+                       a.H, a.V, a.ignore_index, w.zy);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ merge
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(
+    const float* __restrict__ part, int64_t nt, int64_t BT, const float* __restrict__ zy,
+    const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float* __restrict__ lse,
+    float* __restrict__ lse_out, double* __restrict__ blk_ce, double* __restrict__ blk_z,
+    int64_t nblk) {
+  __shared__ double s_a[kMergeThreads / kWave], s_b[kMergeThreads / kWave];
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  double ce = 0.0, zz = 0.0;
+  if (t < BT) {
+    float m = -INFINITY, s = 0.f;
+    for (int64_t k = 0; k < nt; ++k) {
+      const float p = part[k * BT + t];
+      if (p > m) {
+        s = s * __expf(m - p) + 1.f;
+        m = p;
+      } else {
+        s += __expf(p - m);
+      }
+    }
+    const float L = m + __logf(s);
+    lse[t] = L;
+    if (lse_out) lse_out[t] = L;
+    const int64_t yt = y[t];
+    if (yt != ignore_index && yt >= 0 && yt < V) {
+      ce = (double)L - (double)zy[t];
+      zz = (double)L * (double)L;
+    }
+  }
+  ce = wave_sum_d(ce);
+  zz = wave_sum_d(zz);
+  if (threadIdx.x % kWave == 0) { s_a[threadIdx.x / kWave] = ce; s_b[threadIdx.x / kWave] = zz; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = 0.0, b = 0.0;
+    for (int i = 0; i < kMergeThreads / kWave; ++i) { a += s_a[i]; b += s_b[i]; }
+    blk_ce[blockIdx.x] = a;
+    blk_z[blockIdx.x] = b;
+  }
+}
+
+hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  if (a.BT == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)w.nblk), dim3(kMergeThreads), 0, st, w.lse_part, w.nt,
+                     a.BT, w.zy, a.targets, a.V, a.ignore_index, w.lse, a.lse_out, w.blk,
+                     w.blk + w.nblk, w.nblk);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ loss
+constexpr int kLossThreads = 256;
+
+__global__ void __launch_bounds__(kLossThreads) loss_kernel(const double* __restrict__ blk_ce,
+                                                             const double* __restrict__ blk_z,
+                                                             int64_t nblk, const int64_t* __restrict__ n_valid,
+                                                             float mu, int mean, float* loss_out,
+                                                             int64_t* n_valid_out) {
+  __shared__ double s_a[kLossThreads / kWave], s_b[kLossThreads / kWave];
+  double ce = 0.0, zz = 0.0;
+  for (int64_t i = threadIdx.x; i < nblk; i += kLossThreads) { ce += blk_ce[i]; zz += blk_z[i]; }
+  ce = wave_sum_d(ce);
+  zz = wave_sum_d(zz);
+  if (threadIdx.x % kWave == 0) { s_a[threadIdx.x / kWave] = ce; s_b[threadIdx.x / kWave] = zz; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double a = 0.0, b = 0.0;
+    for (int i = 0; i < kLossThreads / kWave; ++i) { a += s_a[i]; b += s_b[i]; }
+    const long long n = *n_valid;
+    const double c = mean ? 1.0 / (double)(n > 1 ? n : 1) : 1.0;
+    *loss_out = (float)(c * (a + (double)mu * b));
+    if (n_valid_out) *n_valid_out = n;
+  }
+}
+
+hipError_t launch_loss(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(kLossThreads), 0, st, w.blk, w.blk + w.nblk, w.nblk,
+                     w.n_valid, a.mu, a.mean ? 1 : 0, a.loss_out, a.n_valid_out);
+  return hipGetLastError();
+}
+
+}  // namespace lce

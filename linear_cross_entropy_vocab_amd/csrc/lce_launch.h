@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI host layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lce {
+
+constexpr size_t kWsAlign = 256;
+inline size_t ws_align(size_t n) { return (n + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Forward logits tile of the fused path: vocabulary rows per tile (one partial LSE per
+// token per tile is kept in the workspace) and tokens per tile.
+constexpr int kFwdTileV = 256;
+constexpr int kFwdTileT = 128;
+
+// Workspace carve-up of the fused path (all offsets 256-byte aligned).
+struct FusedWs {
+  int64_t* n_valid;   // [1] rows with y != ignore_index and y in range
+  int32_t* n_bad;     // [1] targets neither ignore_index nor in [0, V)
+  float* lse_part;    // [NT][BT] per-vocab-tile log-sum-exp partials
+  float* lse;         // [BT]
+  float* zy;          // [BT] target logits
+  double* blk;        // [2][nblk] per-block sums of ce and LSE^2 terms
+  int64_t nt;         // number of vocab tiles
+  int64_t nblk;       // number of merge blocks
+};
+constexpr int kMergeThreads = 256;
+
+size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16);
+FusedWs fused_carve(void* ws, int64_t BT, int64_t V);
+
+struct FusedArgs {
+  const void* hidden;
+  const void* W;
+  const void* bias;
+  const int64_t* targets;
+  int64_t BT, H, V;
+  bool bf16;
+  int64_t ignore_index;
+  float mu;
+  bool mean;
+  float* loss_out;
+  void* grad_input;
+  void* grad_W;
+  void* grad_b;
+  int64_t* n_valid_out;
+  float* lse_out;
+};
+
+// Stages of the fused call, in launch order.
+enum Stage { kStTargets = 0, kStFwd, kStTargetLogit, kStMerge, kStLoss, kStBwdDX, kStBwdDW, kNumStages };
+
+hipError_t launch_targets(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_target_logit(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_loss(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_bwd_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_bwd_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+
+// Standalone cross-entropy.
+size_t ce_workspace_bytes(int64_t B);
+hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, int64_t B, int64_t V,
+                             int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
+                             int64_t* n_valid, void* workspace, hipStream_t st);
+
+}  // namespace lce

@@ -152,30 +152,36 @@ def lce_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDE
 
 
 def ce_oracle(logits, targets, *, ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
-              rows_per_chunk: Optional[int] = None) -> dict:
+              rows_per_chunk: Optional[int] = None, dlogit_rows=None) -> dict:
     """Standalone cross-entropy on existing logits ([P3] opening formulas, "Kernel design").
 
     Returns ce_sum = sum_valid (LSE - x_y), z_sum = sum_valid LSE**2 (0 when z-loss is
     off), n_valid, lse [B] and dlogits [B, V] = valid * (softmax * (1 + 2 mu LSE) - onehot),
-    the unscaled gradient of ce_sum + mu * z_sum.
+    the unscaled gradient of ce_sum + mu * z_sum.  With dlogit_rows (an index array) only
+    those rows of dlogits are returned, in that order (bounds memory for large inputs).
     """
-    X = _f64(logits)
     y = np.asarray(targets, dtype=np.int64)
-    B, V = X.shape
+    B, V = np.shape(logits)
     valid = _valid_mask(y, V, ignore_index)
     mu = float(z_loss)
     lse = np.empty(B)
     xy = np.zeros(B)
-    d = np.empty((B, V))
+    full = dlogit_rows is None
+    d = np.empty((B, V)) if full else None
     R = rows_per_chunk or _rows_per_chunk(V)
     for r0 in range(0, B, R):
         r1 = min(B, r0 + R)
-        z = X[r0:r1]
+        z = _f64(logits[r0:r1])
         lse[r0:r1] = _lse(z)
         vr = valid[r0:r1]
         idx = np.nonzero(vr)[0]
         xy[r0 + idx] = z[idx, y[r0:r1][idx]]
-        d[r0:r1] = _dlogits(z, lse[r0:r1], y[r0:r1], vr, 1.0, mu)
+        if full:
+            d[r0:r1] = _dlogits(z, lse[r0:r1], y[r0:r1], vr, 1.0, mu)
+    if not full:
+        rows = np.asarray(dlogit_rows)
+        z = _f64(np.asarray(logits)[rows])
+        d = _dlogits(z, lse[rows], y[rows], valid[rows], 1.0, mu)
     ce_sum = math.fsum(np.where(valid, lse - xy, 0.0).tolist())
     z_sum = math.fsum(np.where(valid, lse * lse, 0.0).tolist()) if mu != 0.0 else 0.0
     return dict(ce_sum=ce_sum, z_sum=z_sum, n_valid=int(valid.sum()), lse=lse, dlogits=d)

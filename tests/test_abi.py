@@ -1,0 +1,144 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, sizes its
+workspace within the one-logits-chunk budget, and rejects bad arguments on the host
+before any HIP call (fake but well-formed device pointers are passed, so reaching a
+launch would be a bug these tests would expose)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_vocab_amd import _lib
+from oracle import liger_chunk_plan
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lce.h")
+
+BF16, F32 = _lib.DTYPE_BF16, _lib.DTYPE_F32
+MEAN, SUM = _lib.REDUCTION_MEAN, _lib.REDUCTION_SUM
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_are_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:lce_status|size_t|const char\*)\s+(lce_\w+)\s*\(", text, re.M))
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert b"gfx950" in lib.lce_version()
+    for code in range(9):
+        assert lib.lce_status_string(code)
+    names = [lib.lce_stage_name(k).decode() for k in range(_lib.NUM_STAGES)]
+    assert names == ["targets", "fwd_lse", "target_logit", "merge", "loss", "bwd_dinput", "bwd_dweight"]
+    assert lib.lce_stage_name(_lib.NUM_STAGES) is None and lib.lce_stage_name(-1) is None
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "gemma_like", "headline", "qwen_like"])
+def test_workspace_within_one_logits_chunk(lib, name):
+    c = CONFIGS[name]
+    dt = BF16 if c.dtype == "bf16" else F32
+    ws = lib.lce_fwd_bwd_workspace_bytes(c.BT, c.H, c.V, dt, 0)
+    budget = liger_chunk_plan(c.BT, c.V, c.H)["chunk_bytes"]
+    assert 0 < ws <= budget, (ws, budget)
+
+
+def test_workspace_sizes(lib):
+    assert lib.lce_fwd_bwd_workspace_bytes(-1, 64, 10, BF16, 0) == 0
+    assert lib.lce_fwd_bwd_workspace_bytes(10, 12, 10, BF16, 0) == 0   # H % 8 != 0
+    assert lib.lce_fwd_bwd_workspace_bytes(10, 64, 0, BF16, 0) == 0
+    assert lib.lce_fwd_bwd_workspace_bytes(10, 64, 10, 7, 0) == 0
+    assert lib.lce_fwd_bwd_workspace_bytes(0, 64, 10, BF16, 0) > 0
+    B, V = 8192, 128256
+    ws = lib.lce_ce_workspace_bytes(B, V, BF16)
+    assert 0 < ws <= 16 * B
+    assert lib.lce_ce_workspace_bytes(-1, V, BF16) == 0
+
+
+# Fake device addresses: 16-byte aligned, never dereferenced on the host.
+P = 0x7f0000000000
+OK_WS = 1 << 40
+
+
+def fused(lib, **kw):
+    a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
+             dtype=BF16, ignore=-100, mu=0.0, red=MEAN, flags=0, loss=P + 0x300000,
+             gi=P + 0x400000, gw=P + 0x500000, gb=None, nv=P + 0x600000, lse=None,
+             ws=P + 0x700000, wsb=OK_WS, stream=None)
+    a.update(kw)
+    return lib.lce_fwd_bwd(a["hidden"], a["W"], a["bias"], a["targets"], a["BT"], a["H"], a["V"],
+                           a["dtype"], a["ignore"], a["mu"], a["red"], a["flags"], a["loss"], a["gi"],
+                           a["gw"], a["gb"], a["nv"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), 1), (dict(loss=None), 1), (dict(ws=None), 1), (dict(hidden=None), 1),
+    (dict(targets=None), 1),
+    (dict(BT=-1), 2), (dict(V=0), 2), (dict(H=0), 2), (dict(H=12), 2), (dict(H=4), 2),
+    (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(hidden=P + 8), 4), (dict(W=P + 4), 4), (dict(gi=P + 2), 4), (dict(ws=P + 8), 4),
+    (dict(targets=P + 4), 4), (dict(loss=P + 2), 4),
+    (dict(wsb=16), 5),
+    (dict(red=2), 6), (dict(mu=-1.0), 6), (dict(mu=float("nan")), 6), (dict(mu=float("inf")), 6),
+    (dict(gb=P + 0x800000), 6), (dict(flags=2), 6),
+])
+def test_fused_host_errors(lib, kw, status):
+    assert fused(lib, **kw) == status
+
+
+def test_fused_errors_before_device_work_with_empty_batch(lib):
+    # BT = 0 may pass NULL hidden/targets; a too-small workspace is still rejected on the host
+    assert fused(lib, BT=0, hidden=None, targets=None, wsb=0) == 5
+
+
+def ce(lib, **kw):
+    a = dict(logits=P, targets=P + 0x100000, B=10, V=1000, dtype=BF16, ignore=-100, mu=0.0,
+             ce=P + 0x200000, z=P + 0x300000, nv=P + 0x400000, ws=P + 0x500000, wsb=OK_WS, stream=None)
+    a.update(kw)
+    return lib.lce_ce_with_grad_inplace(a["logits"], a["targets"], a["B"], a["V"], a["dtype"],
+                                        a["ignore"], a["mu"], a["ce"], a["z"], a["nv"], a["ws"],
+                                        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), 1), (dict(ce=None), 1), (dict(z=None), 1), (dict(ws=None), 1),
+    (dict(B=-1), 2), (dict(V=0), 2), (dict(dtype=5), 3),
+    (dict(logits=P + 2), 4), (dict(ws=P + 4), 4), (dict(targets=P + 4), 4),
+    (dict(wsb=8), 5), (dict(mu=-0.5), 6), (dict(mu=math.nan), 6),
+])
+def test_ce_host_errors(lib, kw, status):
+    assert ce(lib, **kw) == status
+
+
+def test_status_strings_are_distinct(lib):
+    s = {lib.lce_status_string(k) for k in range(9)}
+    assert len(s) == 9
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import linear_cross_entropy_vocab_amd as lce
+    h = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        lce.lce_fwd_bwd(h, torch.zeros(5, 8), None, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        lce.lce_ce_with_grad_inplace(torch.zeros(4, 5), torch.zeros(4, dtype=torch.int64))
+
+
+def test_oracle_not_imported_by_product_package():
+    pkg = os.path.join(ROOT, "linear_cross_entropy_vocab_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

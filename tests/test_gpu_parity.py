@@ -1,0 +1,185 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle on the same
+seeded inputs, at sizes the oracle finishes in seconds: several tiles, ragged tails,
+each kernel variant (single-chunk and column-chunked backward, bf16 and fp32 MFMA),
+bias, z-loss, both reductions, and the edge cases (V = 1, all rows ignored, empty batch,
+H not a multiple of the per-wave K quarter)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_cross_entropy_vocab_amd as lce
+from workloads import make_config, make_fused, make_ce
+from gpu_util import TOL, CE_TOL, dev, host64, rel, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(inp, **kw):
+    b = None if inp.bias is None else dev(inp.bias, inp.dtype)
+    r = lce.lce_fwd_bwd(dev(inp.hidden, inp.dtype), dev(inp.weight, inp.dtype), b,
+                        dev(inp.targets), z_loss=inp.z_loss, reduction=inp.reduction,
+                        return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def check_fused(inp, r, ref):
+    tol = TOL[inp.dtype]
+    assert int(r["n_valid"].item()) == ref["n_valid"]
+    assert rel(r["loss"].item(), ref["loss"]) <= tol["loss"] or abs(ref["loss"]) < 1e-12 and \
+        abs(r["loss"].item()) < 1e-6, (r["loss"].item(), ref["loss"])
+    lse = host64(r["lse"])
+    assert np.max(np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))) <= tol["lse"]
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        if ref.get(k) is None or r.get(k) is None:
+            continue
+        e = rel_fro(host64(r[k]), ref[k])
+        assert e <= tol["grad"], (k, e)
+    # rows of ignored tokens get an exactly zero grad_input
+    if r["grad_input"] is not None:
+        ign = inp.targets == -100
+        if ign.any():
+            assert np.all(host64(r["grad_input"])[ign] == 0.0)
+
+
+CASES = [
+    # (dtype, BT, H, V, bias_std, z_loss, reduction, ignore_frac, seed)
+    ("bf16", 200, 128, 1000, None, 0.0, "mean", 0.2, 11),
+    ("bf16", 333, 256, 3001, 0.1, 1e-3, "sum", 0.1, 12),
+    ("bf16", 130, 1024, 700, None, 0.0, "mean", 0.0, 13),
+    ("bf16", 97, 200, 513, 0.2, 1e-2, "mean", 0.3, 14),
+    ("bf16", 100, 1152, 600, 0.1, 1e-4, "mean", 0.1, 15),
+    ("bf16", 65, 2304, 257, None, 0.0, "sum", 0.05, 16),
+    ("f32", 77, 520, 300, 0.1, 1e-3, "mean", 0.1, 17),
+    ("f32", 150, 64, 2000, None, 0.0, "sum", 0.2, 18),
+    ("bf16", 1, 8, 5, None, 0.0, "mean", 0.0, 19),
+    ("bf16", 64, 64, 1, 0.1, 0.0, "mean", 0.0, 20),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}" for c in CASES])
+def test_fused_small_vs_oracle(case):
+    dt, BT, H, V, bstd, mu, red, ign, seed = case
+    print(f"case {case}", flush=True)
+    inp = make_fused(BT, H, V, dtype=dt, seed=seed, bias_std=bstd, ignore_frac=ign, z_loss=mu,
+                     reduction=red)
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=mu, reduction=red)
+    r = run_fused(inp)
+    check_fused(inp, r, ref)
+
+
+def test_tiny_f32_config():
+    inp = make_config("tiny_f32")
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=inp.z_loss,
+                            reduction=inp.reduction)
+    r = run_fused(inp)
+    assert int(r["n_valid"].item()) == 230
+    check_fused(inp, r, ref)
+
+
+def test_all_ignored_and_empty():
+    inp = make_fused(50, 64, 300, dtype="bf16", seed=3, bias_std=0.1)
+    inp.targets[:] = -100
+    r = run_fused(inp)
+    assert r["loss"].item() == 0.0 and int(r["n_valid"].item()) == 0
+    assert torch.count_nonzero(r["grad_input"]) == 0
+    assert torch.count_nonzero(r["grad_weight"]) == 0
+    assert torch.count_nonzero(r["grad_bias"]) == 0
+    empty = make_fused(0, 64, 300, dtype="bf16", seed=3)
+    r = run_fused(empty, out=dict(grad_weight=torch.full((300, 64), 7.0, dtype=torch.bfloat16,
+                                                          device="cuda")))
+    assert r["loss"].item() == 0.0 and int(r["n_valid"].item()) == 0
+    assert torch.count_nonzero(r["grad_weight"]) == 0  # fully overwritten with zeros
+
+
+def test_grad_subsets():
+    inp = make_fused(120, 256, 900, dtype="bf16", seed=21, bias_std=0.1, ignore_frac=0.1)
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets)
+    r = run_fused(inp, grad_input=False, grad_weight=False, grad_bias=True)
+    assert r["grad_input"] is None and r["grad_weight"] is None
+    assert rel_fro(host64(r["grad_bias"]), ref["grad_bias"]) <= TOL["bf16"]["grad"]
+    r = run_fused(inp, grad_weight=False, grad_bias=False)
+    assert rel_fro(host64(r["grad_input"]), ref["grad_input"]) <= TOL["bf16"]["grad"]
+
+
+def test_deterministic_bits():
+    inp = make_fused(333, 256, 3001, dtype="bf16", seed=12, bias_std=0.1, ignore_frac=0.1, z_loss=1e-3)
+    a = run_fused(inp)
+    b = run_fused(inp)
+    for k in ("loss", "grad_input", "grad_weight", "grad_bias", "lse"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_target_range_check():
+    inp = make_fused(40, 64, 100, dtype="bf16", seed=5)
+    inp.targets[7] = 100  # == V: out of range
+    with pytest.raises(lce.LCEError) as e:
+        run_fused(inp, check_targets=True)
+    assert e.value.status == 7
+    # without the check the row counts as ignored
+    r = run_fused(inp)
+    y = inp.targets.copy()
+    y[7] = -100
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, y)
+    check_fused(inp, r, ref)
+
+
+def test_autograd_wrapper_scales_by_upstream_grad():
+    inp = make_fused(64, 128, 500, dtype="f32", seed=8, bias_std=0.1, ignore_frac=0.1)
+    h = dev(inp.hidden).requires_grad_(True)
+    W = dev(inp.weight).requires_grad_(True)
+    b = dev(inp.bias).requires_grad_(True)
+    y = dev(inp.targets)
+    loss = lce.linear_cross_entropy(h, W, y, b)
+    (2.5 * loss).backward()
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets)
+    assert rel(loss.item(), ref["loss"]) < 1e-5
+    assert rel_fro(host64(h.grad), 2.5 * ref["grad_input"]) < 1e-4
+    assert rel_fro(host64(W.grad), 2.5 * ref["grad_weight"]) < 1e-4
+    assert rel_fro(host64(b.grad), 2.5 * ref["grad_bias"]) < 1e-4
+
+
+# ------------------------------------------------------------------ standalone CE
+
+CE_CASES = [
+    ("bf16", 64, 1000, 0.0, 0.1, 31),
+    ("bf16", 64, 1000, 1e-3, 0.1, 32),
+    ("bf16", 33, 1001, 1e-4, 0.2, 33),     # row bytes not a multiple of 16: streaming path
+    ("f32", 16, 5000, 1e-3, 0.1, 34),
+    ("f32", 6, 70000, 0.0, 0.0, 35),       # too long for the register cache: streaming path
+    ("bf16", 8, 131072, 1e-4, 0.25, 36),   # largest register-cached bf16 row
+    ("bf16", 5, 1, 0.0, 0.2, 37),
+]
+
+
+@pytest.mark.parametrize("case", CE_CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}-mu{c[3]}" for c in CE_CASES])
+def test_ce_small_vs_oracle(case):
+    dt, B, V, mu, ign, seed = case
+    print(f"ce case {case}", flush=True)
+    inp = make_ce(B, V, dtype=dt, seed=seed, ignore_frac=ign)
+    ref = oracle.ce_oracle(inp.logits, inp.targets, z_loss=mu)
+    x = dev(inp.logits, dt)
+    ptr = x.data_ptr()
+    ce_sum, z_sum, nv = lce.lce_ce_with_grad_inplace(x, dev(inp.targets), z_loss=mu)
+    torch.cuda.synchronize()
+    assert x.data_ptr() == ptr
+    tol = CE_TOL[dt]
+    assert int(nv.item()) == ref["n_valid"]
+    assert rel(ce_sum.item(), ref["ce_sum"]) <= tol["sums"]
+    if mu == 0.0:
+        assert z_sum.item() == 0.0
+    else:
+        assert rel(z_sum.item(), ref["z_sum"]) <= tol["sums"]
+    d = host64(x)
+    assert rel_fro(d, ref["dlogits"]) <= tol["dlogits"]
+    ign_rows = inp.targets == -100
+    assert np.all(d[ign_rows] == 0.0)
+
+
+def test_ce_empty_batch():
+    x = torch.empty(0, 100, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(0, dtype=torch.int64, device="cuda")
+    ce_sum, z_sum, nv = lce.lce_ce_with_grad_inplace(x, y, z_loss=1e-4)
+    assert ce_sum.item() == 0.0 and z_sum.item() == 0.0 and int(nv.item()) == 0
