@@ -80,7 +80,7 @@ typedef enum lce_reduction {
  *   hidden      [BT, H] in `dtype`.                     W      [V, H] in `dtype`.
  *   bias        [V] in `dtype`, or NULL for no bias.
  *   targets     [BT] int64; ignore_index marks rows that contribute nothing.
- *   BT >= 0, H >= 8 and a multiple of 8, V >= 1.
+ *   BT >= 0, 8 <= H <= 2^20 with H a multiple of 8, V >= 1.
  *   dtype       LCE_DTYPE_BF16 or LCE_DTYPE_F32 (arithmetic: products accumulated in fp32;
  *               softmax statistics in fp32; bf16 dlogits operands rounded to nearest even).
  *   ignore_index  target value of ignored rows (usually -100).

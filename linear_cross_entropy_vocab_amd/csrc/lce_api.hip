@@ -57,7 +57,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
                              void* const* ev_start, void* const* ev_stop) {
   // ---- validation: no HIP calls before this block has passed
   if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
-  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 40) || H > ((int64_t)1 << 24)) return LCE_ERR_SHAPE;
+  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 40) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
   if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_DTYPE;
   if (W == nullptr || loss_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
   if (BT > 0 && (hidden == nullptr || targets == nullptr)) return LCE_ERR_NULL;

@@ -31,7 +31,6 @@ namespace lce {
 constexpr int kBwdThreads = 256;
 constexpr int kBS = 64;  // stationary rows per workgroup
 constexpr int kBX = 32;  // streamed rows per tile
-constexpr int kZStride = 36;  // floats per row of a partial-z buffer (padded)
 
 template <typename T>
 struct BwdArgs {
@@ -58,12 +57,11 @@ __device__ __forceinline__ void store8(char* p, const float* v, float) {
   reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
-__device__ __forceinline__ void store_frag(char* p, const Frag<bf16_t>& f) {
-  *reinterpret_cast<bf16x8_t*>(p) = f.v;
+__device__ __forceinline__ void store4(char* p, const float* v, bf16_t) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
 }
-__device__ __forceinline__ void store_frag(char* p, const Frag<float>& f) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+__device__ __forceinline__ void store4(char* p, const float* v, float) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ void lds_frag(Frag<bf16_t>& f, const char* p) {
   f.v = *reinterpret_cast<const bf16x8_t*>(p);
@@ -75,37 +73,59 @@ __device__ __forceinline__ void lds_frag(Frag<float>& f, const char* p) {
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
-// B operand of GEMM3 from the row-major X tile in LDS: lane l needs column (l % 32) of a
-// 32-column block and K rows kbase + 8*(l/32) .. +7.
-__device__ __forceinline__ void xt_frag(Frag<bf16_t>& f, const char* xt, int row_bytes, int kbase,
-                                        int col0, int lane) {
+// LDS tiles read by GEMM3 are row-major with a row stride of 64 (mod 256) bytes and the low
+// two bits of the 16-byte chunk index XORed with bits 2..3 of the row.  Sixteen consecutive
+// rows then cover all 64 banks for 16-byte stores, while the four consecutive rows of a
+// transposed read (same bits 2..3) keep the conflict-free layout of the padded stride, and
+// column offsets that are multiples of 64 bytes stay immediate offsets.
+template <int ROW, int NCH>
+__device__ __forceinline__ int swz(int row, int byte_col) {
+  static_assert(NCH % 4 == 0, "rows must hold a multiple of four 16-byte chunks");
+  return row * ROW + ((((byte_col >> 4) ^ ((row >> 2) & 3)) << 4) | (byte_col & 15));
+}
+
+// Store an 8-element fragment (one 16-byte chunk for bf16, two for fp32) into a swizzled tile.
+template <int ROW, int NCH>
+__device__ __forceinline__ void store_frag(char* t, int row, int byte_col, const Frag<bf16_t>& f) {
+  *reinterpret_cast<bf16x8_t*>(t + swz<ROW, NCH>(row, byte_col)) = f.v;
+}
+template <int ROW, int NCH>
+__device__ __forceinline__ void store_frag(char* t, int row, int byte_col, const Frag<float>& f) {
+  *reinterpret_cast<float4*>(t + swz<ROW, NCH>(row, byte_col)) = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+  *reinterpret_cast<float4*>(t + swz<ROW, NCH>(row, byte_col + 16)) = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
+}
+
+// MFMA operand from a swizzled row-major LDS tile whose rows run along K: lane l needs
+// column (l % 32) of a 32-column block starting at col0 and K rows kbase + 8*(l/32) .. +7.
+template <int ROW, int NCH>
+__device__ __forceinline__ void tile_frag(Frag<bf16_t>& f, const char* t, int kbase, int col0, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int col = col0 + (g & 1) * 16 + 4 * (i & 3);
   const int row = kbase + (g >> 1) * 8 + (i >> 2);
-  const bf16_t* p0 = reinterpret_cast<const bf16_t*>(xt + row * row_bytes + col * 2);
-  const bf16_t* p1 = reinterpret_cast<const bf16_t*>(xt + (row + 4) * row_bytes + col * 2);
-  const i16x4_t a = lds_read_tr16(p0);
-  const i16x4_t b = lds_read_tr16(p1);
+  const i16x4_t a = lds_read_tr16(reinterpret_cast<const bf16_t*>(t + swz<ROW, NCH>(row, col * 2)));
+  const i16x4_t b = lds_read_tr16(reinterpret_cast<const bf16_t*>(t + swz<ROW, NCH>(row + 4, col * 2)));
   f.v = bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-__device__ __forceinline__ void xt_frag(Frag<float>& f, const char* xt, int row_bytes, int kbase,
-                                        int col0, int lane) {
+template <int ROW, int NCH>
+__device__ __forceinline__ void tile_frag(Frag<float>& f, const char* t, int kbase, int col0, int lane) {
   const int col = col0 + (lane & 31);
   const int row = kbase + 8 * (lane >> 5);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = *reinterpret_cast<const float*>(xt + (row + s) * row_bytes + col * 4);
+  for (int s = 0; s < 8; ++s) f.v[s] = *reinterpret_cast<const float*>(t + swz<ROW, NCH>(row + s, col * 4));
 }
 
-template <typename T>
-__device__ __forceinline__ bool load_frag_masked(Frag<T>& f, const T* base, int64_t row, int64_t nrows,
-                                                 int64_t k, int64_t H) {
-  if (row < nrows && k < H) {
-    load8(f, base + row * H + k);
-    return true;
-  }
-  zero8(f);
-  return false;
+__device__ __forceinline__ void zero_unless(Frag<bf16_t>& f, bool keep) {
+  const bf16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+  f.v = keep ? f.v : z;
 }
+__device__ __forceinline__ void zero_unless(Frag<float>& f, bool keep) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = keep ? f.v[i] : 0.f;
+}
+
+// Padding that makes a row stride equal 64 (mod 256) bytes: four consecutive rows then fall
+// on disjoint LDS banks for the 16-lane groups of the transposed reads.
+constexpr int pad_64mod256(int bytes) { return ((64 - bytes % 256) % 256 + 256) % 256; }
 
 // SINGLE: whole H handled by one workgroup, NB = H-columns per wave / 32 (= K quarter / 32).
 // CHUNKED: output columns split into nchunks chunks of 4*NB*32; S streamed from L2.
@@ -113,58 +133,80 @@ template <typename T, bool DW, bool SINGLE, int NB>
 __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
   constexpr int ES = sizeof(T);
   constexpr int NCOL = NB * 32;
-  constexpr int XT_ROW = NCOL * ES + 64;            // bytes per row of a wave's X tile
-  constexpr int G_ROW = kBX * ES + 16;              // bytes per row of the dlogits tile
-  constexpr int KS1S = 2 * NB;                      // GEMM1 k-steps per wave (SINGLE)
-  __shared__ __attribute__((aligned(16))) float zpart[4][kBS * kZStride];
-  __shared__ __attribute__((aligned(16))) char gtile[kBS * G_ROW];
+  constexpr int XT_ROW = NCOL * ES + pad_64mod256(NCOL * ES);  // bytes per row of a wave's X tile
+  constexpr int G_ROW = kBS * ES + pad_64mod256(kBS * ES);      // bytes per row of the dlogits tile
+  constexpr int XT_NCH = NCOL * ES / 16;
+  constexpr int G_NCH = kBS * ES / 16;
+  constexpr int ZCOL = kBS + 4;                                   // floats per column of a partial z
+  constexpr int KS1S = 2 * NB;                                    // GEMM1 k-steps per wave (SINGLE)
+  constexpr int XCH = NCOL * ES / 16;                             // 16 B chunks per row (CHUNKED)
+  constexpr int XCH_LANE = kBX * XCH / kWave;
+  // Layouts: partial z is column-major [x][s]; the dlogits tile is [x][s] (the K index of
+  // GEMM3 runs along x, read back with transposed LDS reads); each wave's X tile is
+  // row-major [x][its NCOL columns].
+  __shared__ __attribute__((aligned(16))) float zpart[4][kBX * ZCOL];
+  __shared__ __attribute__((aligned(16))) char gtile[kBX * G_ROW];
   __shared__ __attribute__((aligned(16))) char xtile[4][kBX * XT_ROW];
+  __shared__ __attribute__((aligned(16))) float s_a[kBS];
+  __shared__ __attribute__((aligned(16))) float s_b[kBS];
+  __shared__ __attribute__((aligned(16))) int32_t s_y[kBS];
 
-  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
   const int64_t s_tile = blockIdx.x / p.nchunks;
   const int64_t chunk = blockIdx.x % p.nchunks;
   const int64_t s0 = s_tile * kBS;
-  const int64_t h0 = chunk * (4 * NCOL);            // first output column of this workgroup
-  const int64_t hw0 = h0 + w * NCOL;                // first output column of this wave
+  const int64_t h0 = chunk * (4 * NCOL);  // first output column of this workgroup
+  const int64_t hw0 = h0 + w * NCOL;      // first output column of this wave
   const int64_t H = p.H;
-  // GEMM1 K range of this wave
-  const int64_t KW = SINGLE ? (int64_t)NCOL : ((H + 63) / 64) * 16;
+  const int64_t KW = SINGLE ? (int64_t)NCOL : ((H + 63) / 64) * 16;  // GEMM1 K range per wave
   const int64_t kw0 = w * KW;
-  const int ks1 = SINGLE ? KS1S : (int)(KW / 16);
+  const int ks1 = (int)(KW / 16);
+  const int khalf = 8 * (lane >> 5);
 
   const long long nvalid = *p.n_valid;
   const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
 
-  // Reduce-step assignment: row rr of the 64, columns c0 .. c0+7 of the 32.
-  const int rr = 16 * w + (lane >> 2);
-  const int c0 = (lane & 3) * 8;
-  const int64_t srow = s0 + rr;
-  // Per stationary-row quantities.
-  float row_lse = 0.f, row_f = 0.f, row_bias = 0.f;
-  int64_t row_y = -1;
-  bool row_ok = false;
-  if (!DW) {
-    if (srow < p.BT) {
-      const int64_t yt = p.y[srow];
-      row_ok = (yt != p.ignore_index) && yt >= 0 && yt < p.V;
-      row_y = yt;
-      row_lse = p.lse[srow];
-      row_f = 1.f + 2.f * p.mu * row_lse;
+  // Per stationary-row tables.
+  //   grad_input: s_a = LSE, s_b = 1 + 2 mu LSE, s_y = target (or -1 if the token row does not count)
+  //   grad_W:     s_a = bias of the vocab row, s_y = 1 if the vocab row exists
+  if (tid < kBS) {
+    const int64_t r = s0 + tid;
+    if (!DW) {
+      float L = 0.f;
+      int32_t yv = -1;
+      if (r < p.BT) {
+        const int64_t yt = p.y[r];
+        if (yt != p.ignore_index && yt >= 0 && yt < p.V) {
+          yv = (int32_t)yt;
+          L = p.lse[r];
+        }
+      }
+      s_a[tid] = L;
+      s_b[tid] = 1.f + 2.f * p.mu * L;
+      s_y[tid] = yv;
+    } else {
+      s_a[tid] = (p.bias != nullptr && r < p.V) ? Elem<T>::to_f(p.bias[r]) : 0.f;
+      s_b[tid] = 0.f;
+      s_y[tid] = r < p.V ? 1 : 0;
     }
-  } else {
-    row_ok = srow < p.V;
-    row_bias = (p.bias != nullptr && row_ok) ? Elem<T>::to_f(p.bias[srow]) : 0.f;
   }
-  float gb_acc = 0.f;
 
-  // Stationary fragments (SINGLE only): S rows s0 + sb*32 + lane%32, K quarter of wave w.
+  // Stationary fragments (SINGLE): S rows s0 + sb*32 + lane%32, this wave's K quarter.
+  // Buffer descriptors: S rebased at the workgroup's first row, X rebased per tile, so rows
+  // past the end read as zero.  K past H (the last wave's quarter when H is not a multiple of
+  // 4 x 32 x NB) reads the next row's data, which meets a zeroed S fragment.
+  const int64_t row_bytes = H * ES;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.S + s0 * H, (p.nS - s0) * row_bytes);
+  const uint32_t off_lane = (uint32_t)((lane & 31) * row_bytes + (kw0 + khalf) * ES);
   Frag<T> sf[SINGLE ? KS1S : 1][2];
-  if (SINGLE) {
+  if constexpr (SINGLE) {
 #pragma unroll
     for (int ks = 0; ks < KS1S; ++ks)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-        load_frag_masked(sf[ks][sb], p.S, s0 + sb * 32 + (lane & 31), p.nS, kw0 + ks * 16 + 8 * (lane >> 5), H);
+      for (int sb = 0; sb < 2; ++sb) {
+        load8(sf[ks][sb], rs, off_lane + (uint32_t)(sb * 32 * row_bytes + ks * 16 * ES));
+        zero_unless(sf[ks][sb], kw0 + ks * 16 + khalf < H);
+      }
   }
 
   f32x16_t acc[2][NB];
@@ -174,109 +216,178 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
     for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[sb][cb][r] = 0.f;
+  float gb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gb[e] = 0.f;
+
+  // Per streamed-column quantities of the next tile (prefetched with its X rows):
+  //   grad_input: bias of the vocab column;  grad_W: LSE and target (or -1) of the token column.
+  float pc_a = 0.f;
+  int32_t pc_y = -1;
+  auto load_col = [&](int64_t x0n) {
+    const int64_t xc = x0n + (lane & 31);
+    if (!DW) {
+      pc_a = p.bias != nullptr ? Elem<T>::to_f(p.bias[xc < p.V ? xc : p.V - 1]) : 0.f;
+      pc_y = 0;
+    } else {
+      const int64_t t = xc < p.BT ? xc : p.BT - 1;
+      const int64_t yt = p.y[t];
+      pc_a = p.lse[t];
+      pc_y = (xc < p.BT && yt != p.ignore_index && yt >= 0 && yt < p.V) ? (int32_t)yt : -1;
+    }
+  };
+
+  // X fragments of GEMM1: the first PF k-steps of the next tile are prefetched during the
+  // current tile; the remaining ones are issued when the tile starts (register budget).
+  constexpr int PF = (SINGLE && KS1S > 8) ? KS1S - 4 : KS1S;
+  Frag<T> xf[SINGLE ? KS1S : 1];
+  auto x_rsrc = [&](int64_t x0n) { return make_rsrc(p.X + x0n * H, (p.nX - x0n) * row_bytes); };
+  auto load_x = [&](int64_t x0n, int from, int to) {
+    const __amdgpu_buffer_rsrc_t rx = x_rsrc(x0n);
+#pragma unroll
+    for (int ks = 0; ks < (SINGLE ? KS1S : 1); ++ks)
+      if (ks >= from && ks < to) load8(xf[ks], rx, off_lane + (uint32_t)(ks * 16 * ES));
+  };
 
   char* xt = xtile[w];
+  const int c = lane & 31;                // reduce step: streamed column of this lane
+  const int r0 = 16 * w + 8 * (lane >> 5);  // reduce step: first of this lane's 8 stationary rows
   const int64_t ntiles = (p.nX + kBX - 1) / kBX;
+  if (ntiles > 0) {
+    if constexpr (SINGLE) load_x(0, 0, PF);
+    load_col(0);
+  }
   for (int64_t xtl = 0; xtl < ntiles; ++xtl) {
     const int64_t x0 = xtl * kBX;
-    const int64_t xrow = x0 + (lane & 31);
-    // ---------------- GEMM1: partial z over this wave's K quarter
+    const float col_a = pc_a;
+    const int32_t col_y = pc_y;
+    // ---------------- GEMM1: partial z[64 x 32] over this wave's K quarter
     f32x16_t zp[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) zp[sb][r] = 0.f;
-    if (SINGLE) {
+    if constexpr (SINGLE) {
+      if constexpr (PF < KS1S) load_x(x0, PF, KS1S);
 #pragma unroll
       for (int ks = 0; ks < KS1S; ++ks) {
-        Frag<T> xf;
-        load_frag_masked(xf, p.X, xrow, p.nX, kw0 + ks * 16 + 8 * (lane >> 5), H);
-        // the same X values are GEMM3's operand for this wave's columns
-        store_frag(xt + (lane & 31) * XT_ROW + (ks * 16 + 8 * (lane >> 5)) * ES, xf);
-        mfma_32x32x16(sf[ks][0], xf, zp[0]);
-        mfma_32x32x16(sf[ks][1], xf, zp[1]);
+        // the same X values are GEMM3's operand for this wave's output columns
+        store_frag<XT_ROW, XT_NCH>(xt, lane & 31, (ks * 16 + khalf) * ES, xf[ks]);
+        mfma_32x32x16(sf[ks][0], xf[ks], zp[0]);
+        mfma_32x32x16(sf[ks][1], xf[ks], zp[1]);
+      }
+      if (xtl + 1 < ntiles) {  // prefetch the next tile into the registers just consumed
+        load_x(x0 + kBX, 0, PF);
+        load_col(x0 + kBX);
       }
     } else {
-      for (int ks = 0; ks < ks1; ++ks) {
-        const int64_t k = kw0 + ks * 16 + 8 * (lane >> 5);
-        Frag<T> xf, a0, a1;
-        load_frag_masked(xf, p.X, xrow, p.nX, k, H);
-        load_frag_masked(a0, p.S, s0 + (lane & 31), p.nS, k, H);
-        load_frag_masked(a1, p.S, s0 + 32 + (lane & 31), p.nS, k, H);
-        mfma_32x32x16(a0, xf, zp[0]);
-        mfma_32x32x16(a1, xf, zp[1]);
-      }
-      // X rows for this wave's output columns
-      constexpr int CH = NCOL * ES / 16;  // 16 B chunks per row
+      // X rows for this wave's output columns: issued first, stored to LDS after GEMM1
+      const __amdgpu_buffer_rsrc_t rx = x_rsrc(x0);
+      uint4 xg[XCH_LANE];
 #pragma unroll
-      for (int i = 0; i < (kBX * CH + kWave - 1) / kWave; ++i) {
-        const int c = lane + kWave * i;
-        if (c < kBX * CH) {
-          const int r = c / CH, cc = c % CH;
-          const int64_t col = hw0 + cc * (16 / ES);
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (x0 + r < p.nX && col < H) v = *reinterpret_cast<const uint4*>(p.X + (x0 + r) * H + col);
-          *reinterpret_cast<uint4*>(xt + r * XT_ROW + cc * 16) = v;
+      for (int i = 0; i < XCH_LANE; ++i) {
+        const int cidx = lane + kWave * i, r = cidx / XCH, cc = cidx % XCH;
+        const int64_t col = hw0 + cc * (16 / ES);
+        // columns past H read the next row (or zero past the end): they only feed
+        // output columns >= H, which are never stored
+        xg[i] = load16(rx, (uint32_t)(r * row_bytes + col * ES));
+      }
+      // GEMM1 with a 4-deep register pipeline over the K steps
+      constexpr int P = 4;
+      Frag<T> rxf[P], ra[P], rb[P];
+      auto ld = [&](int j, int ks) {
+        const uint32_t o = off_lane + (uint32_t)(ks * 16 * ES);
+        load8(rxf[j], rx, o);
+        load8(ra[j], rs, o);
+        load8(rb[j], rs, o + (uint32_t)(32 * row_bytes));
+        const bool kin = kw0 + ks * 16 + khalf < H;
+        zero_unless(ra[j], kin);
+        zero_unless(rb[j], kin);
+      };
+#pragma unroll
+      for (int j = 0; j < P; ++j) ld(j, j);
+      for (int ks = 0; ks < ks1; ks += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          if (ks + j < ks1) {
+            mfma_32x32x16(ra[j], rxf[j], zp[0]);
+            mfma_32x32x16(rb[j], rxf[j], zp[1]);
+          }
+          ld(j, ks + j + P);
         }
       }
+#pragma unroll
+      for (int i = 0; i < XCH_LANE; ++i) {
+        const int cidx = lane + kWave * i, r = cidx / XCH, cc = cidx % XCH;
+        *reinterpret_cast<uint4*>(xt + swz<XT_ROW, XT_NCH>(r, cc * 16)) = xg[i];
+      }
+      if (xtl + 1 < ntiles) load_col(x0 + kBX);
     }
-    // ---------------- partial z to LDS
+    // ---------------- partial z to LDS, column-major, 16-byte stores
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) zpart[w][(sb * 32 + acc_row(lane, r)) * kZStride + (lane & 31)] = zp[sb][r];
+      for (int j = 0; j < 4; ++j) {
+        const int row = sb * 32 + 8 * j + 4 * (lane >> 5);
+        *reinterpret_cast<float4*>(&zpart[w][(lane & 31) * ZCOL + row]) =
+            make_float4(zp[sb][4 * j], zp[sb][4 * j + 1], zp[sb][4 * j + 2], zp[sb][4 * j + 3]);
+      }
     __syncthreads();
-    // ---------------- z for row rr, columns c0..c0+7; dlogits
-    float z[8];
+    // ---------------- z and dlogits for column c, rows r0 .. r0+7, in two halves of 4 rows
+    // (bounds the live registers of this step)
+    const int64_t xc = x0 + c;
+#pragma unroll 1
+    for (int hf = 0; hf < 2; ++hf) {
+      const int rh = r0 + 4 * hf;
+      float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) z[e] = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a = *reinterpret_cast<const float4*>(&zpart[q][rr * kZStride + c0]);
-      const float4 b = *reinterpret_cast<const float4*>(&zpart[q][rr * kZStride + c0 + 4]);
-      z[0] += a.x; z[1] += a.y; z[2] += a.z; z[3] += a.w;
-      z[4] += b.x; z[5] += b.y; z[6] += b.z; z[7] += b.w;
-    }
-    float g[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t xc = x0 + c0 + e;  // streamed row index of this column
-      float gv = 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = *reinterpret_cast<const float4*>(&zpart[q][c * ZCOL + rh]);
+        z[0] += a.x; z[1] += a.y; z[2] += a.z; z[3] += a.w;
+      }
+      const float4 ta = *reinterpret_cast<const float4*>(&s_a[rh]);
+      const int4 ty = *reinterpret_cast<const int4*>(&s_y[rh]);
+      const float va[4] = {ta.x, ta.y, ta.z, ta.w};
+      const int32_t vy[4] = {ty.x, ty.y, ty.z, ty.w};
+      float g[4];
       if (!DW) {
-        // token = srow, vocab = xc
-        if (row_ok && xc < p.V) {
-          const float b = p.bias != nullptr ? Elem<T>::to_f(p.bias[xc]) : 0.f;
-          gv = __expf(z[e] + b - row_lse) * row_f - (xc == row_y ? 1.f : 0.f);
+        const float4 tb = *reinterpret_cast<const float4*>(&s_b[rh]);
+        const float vf[4] = {tb.x, tb.y, tb.z, tb.w};
+        const bool colok = xc < p.V;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ex = __expf(z[e] + col_a - va[e]) * vf[e] - ((int64_t)vy[e] == xc ? 1.f : 0.f);
+          g[e] = (vy[e] >= 0 && colok) ? ex : 0.f;
         }
       } else {
-        // vocab = srow, token = xc
-        if (row_ok && xc < p.BT) {
-          const int64_t yt = p.y[xc];
-          if (yt != p.ignore_index && yt >= 0 && yt < p.V) {
-            const float L = p.lse[xc];
-            gv = __expf(z[e] + row_bias - L) * (1.f + 2.f * p.mu * L) - (yt == srow ? 1.f : 0.f);
-          }
+        const float ft = 1.f + 2.f * p.mu * col_a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t srow = s0 + rh + e;
+          const float ex = __expf(z[e] + va[e] - col_a) * ft - ((int64_t)col_y == srow ? 1.f : 0.f);
+          g[e] = (vy[e] != 0 && col_y >= 0) ? ex : 0.f;
+        }
+        if (hf == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gb[e] += g[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gb[4 + e] += g[e];
         }
       }
-      g[e] = gv;
+      store4(gtile + swz<G_ROW, G_NCH>(c, rh * ES), g, T());
     }
-    if (DW) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) gb_acc += g[e];
-    }
-    store8(gtile + rr * G_ROW + c0 * ES, g, T());
     __syncthreads();
     // ---------------- GEMM3: acc += g . X[:, wave columns]
 #pragma unroll
     for (int kk = 0; kk < kBX / 16; ++kk) {
       Frag<T> ga[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-        lds_frag(ga[sb], gtile + (sb * 32 + (lane & 31)) * G_ROW + (kk * 16 + 8 * (lane >> 5)) * ES);
+      for (int sb = 0; sb < 2; ++sb) tile_frag<G_ROW, G_NCH>(ga[sb], gtile, kk * 16, sb * 32, lane);
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
         Frag<T> xb;
-        xt_frag(xb, xt, XT_ROW, kk * 16, cb * 32, lane);
+        tile_frag<XT_ROW, XT_NCH>(xb, xt, kk * 16, cb * 32, lane);
         mfma_32x32x16(ga[0], xb, acc[0][cb]);
         mfma_32x32x16(ga[1], xb, acc[1][cb]);
       }
@@ -284,22 +395,351 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
   }
 
   // ---------------- write c * acc
+  if (p.out != nullptr) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t col = hw0 + cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+          if (row < p.nS && col < H) p.out[row * H + col] = Elem<T>::from_f(cscale * acc[sb][cb][r]);
+        }
+      }
+  }
+  if (DW && p.grad_b != nullptr && chunk == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = gb[e];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, kWave);
+      const int64_t srow = s0 + r0 + e;
+      if (c == 0 && srow < p.V) p.grad_b[srow] = Elem<T>::from_f(cscale * v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16, whole H in one workgroup (H <= 1024): streamed tiles arrive by buffer->LDS DMA,
+// double buffered, so no registers stage them and the next tile's transfer overlaps the
+// current tile's work.  GEMM1 reads its X fragments from LDS; each wave keeps the partial
+// z of its own 16 reduce rows in registers and only sends the other 48 rows through LDS.
+// LDS: X tiles 2 x 4 x 32 x (64 NB) bytes (128 KiB at NB = 8), partial z 24 KiB,
+// dlogits 4 KiB, per-row tables 768 B.
+// ---------------------------------------------------------------------------
+constexpr int kZBlk = 32 * 16 * 4;  // one partial-z block: 32 columns x 16 rows, fp32
+
+// X-tile chunk swizzle: bijective on any 16 consecutive rows (16-byte reads of GEMM1 hit
+// distinct banks) and, for four consecutive rows starting at a multiple of 4, spreads the
+// two chunks each of them reads over 8 distinct chunks (transposed reads of GEMM3).
+template <int XNCH>
+__device__ __forceinline__ int xsw(int row) {
+  return (((row & 3) << 1) | ((row >> 2) & 1) | (row & 8)) & (XNCH - 1);
+}
+__device__ __forceinline__ int gsw(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int zslot(int writer, int reader) { return writer * 3 + (reader < writer ? reader : reader - 1); }
+
+// Operand from a [K rows][32-column blocks] bf16 LDS tile read with transposed reads; `sw`
+// maps a row to the XOR applied to its 16-byte chunk index.
+template <int ROWB, typename SW>
+__device__ __forceinline__ void tr_frag(Frag<bf16_t>& f, const char* t, int kbase, int col0, int lane, SW sw) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = col0 + (g & 1) * 16 + 4 * (i & 3);
+  const int r0 = kbase + (g >> 1) * 8 + (i >> 2), r1 = r0 + 4;
+  const int ch = col >> 3, within = (col & 7) * 2;
+  const i16x4_t a = lds_read_tr16(reinterpret_cast<const bf16_t*>(t + r0 * ROWB + ((ch ^ sw(r0)) << 4) + within));
+  const i16x4_t b = lds_read_tr16(reinterpret_cast<const bf16_t*>(t + r1 * ROWB + ((ch ^ sw(r1)) << 4) + within));
+  f.v = bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool DW, int NB>
+__global__ void __launch_bounds__(kBwdThreads, 1) bwd_dma_kernel(BwdArgs<bf16_t> p) {
+  typedef bf16_t T;
+  constexpr int NCOL = 32 * NB;      // output columns of a wave = its GEMM1 K quarter
+  constexpr int XROW = NCOL * 2;     // bytes per X-tile row
+  constexpr int XNCH = XROW / 16;
+  constexpr int XWAVE = kBX * XROW;  // bytes of a wave's X tile
+  constexpr int NDMA = XWAVE / 1024; // DMA instructions per wave per tile
+  constexpr int KS1 = 2 * NB;
+  constexpr int GROW = kBS * 2;      // bytes per dlogits-tile row
+  static_assert(XNCH >= 4 && (XNCH & (XNCH - 1)) == 0, "power-of-two chunks per row");
+  __shared__ __attribute__((aligned(1024))) char xtile[2][4][XWAVE];
+  __shared__ __attribute__((aligned(16))) char zpart[12 * kZBlk];
+  __shared__ __attribute__((aligned(16))) char gtile[kBX * GROW];
+  __shared__ __attribute__((aligned(16))) float s_a[kBS];
+  __shared__ __attribute__((aligned(16))) float s_b[kBS];
+  __shared__ __attribute__((aligned(16))) int32_t s_y[kBS];
+
+  const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
+  const int h = lane >> 5, c = lane & 31;
+  const int64_t s0 = (int64_t)blockIdx.x * kBS;
+  const int64_t H = p.H;
+  const int64_t row_bytes = H * 2;
+  const int kw0 = w * NCOL;
+  const long long nvalid = *p.n_valid;
+  const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+
+  if (tid < kBS) {
+    const int64_t r = s0 + tid;
+    if (!DW) {
+      float L = 0.f;
+      int32_t yv = -1;
+      if (r < p.BT) {
+        const int64_t yt = p.y[r];
+        if (yt != p.ignore_index && yt >= 0 && yt < p.V) {
+          yv = (int32_t)yt;
+          L = p.lse[r];
+        }
+      }
+      s_a[tid] = L;
+      s_b[tid] = 1.f + 2.f * p.mu * L;
+      s_y[tid] = yv;
+    } else {
+      s_a[tid] = (p.bias != nullptr && r < p.V) ? bf2f(p.bias[r]) : 0.f;
+      s_b[tid] = 0.f;
+      s_y[tid] = r < p.V ? 1 : 0;
+    }
+  }
+
+  // Stationary fragments: S rows s0 + sb*32 + lane%32, K quarter of this wave.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.S + s0 * H, (p.nS - s0) * row_bytes);
+  const uint32_t s_off = (uint32_t)(c * row_bytes + (kw0 + 8 * h) * 2);
+  Frag<T> sf[KS1][2];
+#pragma unroll
+  for (int ks = 0; ks < KS1; ++ks)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      load8(sf[ks][sb], rs, s_off + (uint32_t)(sb * 32 * row_bytes + ks * 32));
+      zero_unless(sf[ks][sb], kw0 + ks * 16 + 8 * h < H);
+    }
+
+  f32x16_t acc[2][NB];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      const int64_t col = hw0 + cb * 32 + (lane & 31);
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-        if (p.out != nullptr && row < p.nS && col < H) p.out[row * H + col] = Elem<T>::from_f(cscale * acc[sb][cb][r]);
+      for (int r = 0; r < 16; ++r) acc[sb][cb][r] = 0.f;
+  float gb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gb[e] = 0.f;
+
+  // DMA of this wave's quarter of a tile: instruction j fills bytes [1024 j, 1024 j + 1024)
+  // of the wave's region; lane l lands at 16 l, i.e. row (1024 j + 16 l) / XROW and
+  // physical chunk ((1024 j + 16 l) % XROW) / 16, which holds logical chunk
+  // (physical ^ xsw(row)).  Rows past the end of X read as zeros.
+  auto dma = [&](int64_t x0n, int buf, int ln) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X + x0n * H, (p.nX - x0n) * row_bytes);
+    char* dst = xtile[buf][w];
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int b = 1024 * j + 16 * ln;
+      const int row = b / XROW, pch = (b % XROW) / 16;
+      const int lch = pch ^ xsw<XNCH>(row);
+      const uint32_t off = (uint32_t)(row * row_bytes + (kw0 + lch * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+  float pc_a = 0.f;
+  int32_t pc_y = -1;
+  auto load_col = [&](int64_t x0n) {
+    const int64_t xc = x0n + c;
+    if (!DW) {
+      pc_a = p.bias != nullptr ? bf2f(p.bias[xc < p.V ? xc : p.V - 1]) : 0.f;
+      pc_y = 0;
+    } else {
+      const int64_t t = xc < p.BT ? xc : p.BT - 1;
+      const int64_t yt = p.y[t];
+      pc_a = p.lse[t];
+      pc_y = (xc < p.BT && yt != p.ignore_index && yt >= 0 && yt < p.V) ? (int32_t)yt : -1;
+    }
+  };
+
+  const int64_t ntiles = (p.nX + kBX - 1) / kBX;
+  if (ntiles > 0) {
+    load_col(0);
+    dma(0, 0, lane);
+  }
+  for (int64_t xtl = 0; xtl < ntiles; ++xtl) {
+    const int64_t x0 = xtl * kBX;
+    const int buf = (int)(xtl & 1);
+    const float col_a = pc_a;
+    const int32_t col_y = pc_y;
+    // An opaque copy of the lane index: LDS/DMA addresses derived from it are recomputed
+    // where they are used instead of being hoisted out of the loop into live registers.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lc = ln & 31, lh = ln >> 5;
+    if (xtl + 1 < ntiles) {
+      load_col(x0 + kBX);
+      dma(x0 + kBX, buf ^ 1, ln);
+      wait_vmcnt<NDMA>();  // everything before the next tile's DMA has landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    const char* xt = xtile[buf][w];
+    // ---------------- GEMM1: partial z[64 x 32] over this wave's K quarter
+    f32x16_t zp[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zp[sb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS1; ++ks) {
+      Frag<T> xf;
+      lds_frag(xf, xt + lc * XROW + (((2 * ks + lh) ^ xsw<XNCH>(lc)) << 4));
+      mfma_32x32x16(sf[ks][0], xf, zp[0]);
+      mfma_32x32x16(sf[ks][1], xf, zp[1]);
+      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the reads in flight
+    }
+    // ---------------- partial z: the other waves' rows to LDS, own rows kept
+    // Rows 16 w' .. 16 w' + 15 live in zp[w' / 2], registers 8 (w' % 2) .. + 7 (local rows
+    // 8 j + 4 h + q for register 8 (w' % 2) + 4 j + q).
+    float own[8];
+#pragma unroll
+    for (int wp = 0; wp < 4; ++wp) {
+      const f32x16_t& zb = zp[wp >> 1];
+      const int rb = 8 * (wp & 1);
+      if (wp == w) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) own[q] = zb[rb + q];
+      } else {
+        char* blk = zpart + zslot(w, wp) * kZBlk + lc * 64;
+        const int sw = (lc >> 2) & 3;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          *reinterpret_cast<float4*>(blk + (((2 * j + lh) ^ sw) << 4)) =
+              make_float4(zb[rb + 4 * j], zb[rb + 4 * j + 1], zb[rb + 4 * j + 2], zb[rb + 4 * j + 3]);
       }
     }
-  if (DW && p.grad_b != nullptr && chunk == 0) {
-    gb_acc += __shfl_xor(gb_acc, 1, kWave);
-    gb_acc += __shfl_xor(gb_acc, 2, kWave);
-    if ((lane & 3) == 0 && srow < p.V) p.grad_b[srow] = Elem<T>::from_f(cscale * gb_acc);
+    // own holds local rows 4h + q (q < 4) and 8 + 4h + q; the reduce step wants 8h .. 8h + 7:
+    // swap one half with the partner lane (l ^ 32).
+    float z[8];
+    {
+      float snd[4], rcv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) snd[q] = h ? own[q] : own[4 + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rcv[q] = __shfl_xor(snd[q], 32, kWave);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        z[q] = h ? rcv[q] : own[q];
+        z[4 + q] = h ? own[4 + q] : rcv[q];
+      }
+    }
+    __syncthreads();
+    // ---------------- z and dlogits for column c, rows 16 w + 8 h .. + 7
+    {
+      const int sw = (lc >> 2) & 3;
+#pragma unroll
+      for (int wp = 0; wp < 4; ++wp) {
+        if (wp == w) continue;
+        const char* blk = zpart + zslot(wp, w) * kZBlk + lc * 64;
+        const float4 a = *reinterpret_cast<const float4*>(blk + (((2 * lh) ^ sw) << 4));
+        const float4 b = *reinterpret_cast<const float4*>(blk + (((2 * lh + 1) ^ sw) << 4));
+        z[0] += a.x; z[1] += a.y; z[2] += a.z; z[3] += a.w;
+        z[4] += b.x; z[5] += b.y; z[6] += b.z; z[7] += b.w;
+      }
+    }
+    const int r0 = 16 * w + 8 * h;
+    const int64_t xc = x0 + c;
+    float g[8];
+    {
+      const float4 a0 = *reinterpret_cast<const float4*>(&s_a[r0]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s_a[r0 + 4]);
+      const int4 y0 = *reinterpret_cast<const int4*>(&s_y[r0]);
+      const int4 y1 = *reinterpret_cast<const int4*>(&s_y[r0 + 4]);
+      const float va[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const int32_t vy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+      if (!DW) {
+        const float4 b0 = *reinterpret_cast<const float4*>(&s_b[r0]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&s_b[r0 + 4]);
+        const float vf[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const bool colok = xc < p.V;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ex = __expf(z[e] + col_a - va[e]) * vf[e] - ((int64_t)vy[e] == xc ? 1.f : 0.f);
+          g[e] = (vy[e] >= 0 && colok) ? ex : 0.f;
+        }
+      } else {
+        const float ft = 1.f + 2.f * p.mu * col_a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t srow = s0 + r0 + e;
+          const float ex = __expf(z[e] + va[e] - col_a) * ft - ((int64_t)col_y == srow ? 1.f : 0.f);
+          g[e] = (vy[e] != 0 && col_y >= 0) ? ex : 0.f;
+          gb[e] += g[e];
+        }
+      }
+    }
+    // dlogits tile [x = c][s = r0 .. r0 + 7]: one 16-byte chunk (index r0 / 8 = 2 w + h)
+    *reinterpret_cast<uint4*>(gtile + lc * GROW + (((2 * w + lh) ^ gsw(lc)) << 4)) =
+        make_uint4(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]), pack_bf2(g[4], g[5]), pack_bf2(g[6], g[7]));
+    __syncthreads();
+    // ---------------- GEMM3: acc += g . X[:, wave columns]
+#pragma unroll
+    for (int kk = 0; kk < kBX / 16; ++kk) {
+      Frag<T> ga[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) tr_frag<GROW>(ga[sb], gtile, kk * 16, sb * 32, ln, gsw);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        Frag<T> xb;
+        tr_frag<XROW>(xb, xt, kk * 16, cb * 32, ln, xsw<XNCH>);
+        mfma_32x32x16(ga[0], xb, acc[0][cb]);
+        mfma_32x32x16(ga[1], xb, acc[1][cb]);
+        if ((cb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
+
+  // ---------------- write c * acc
+  const int64_t hw0 = kw0;
+  if (p.out != nullptr) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t col = hw0 + cb * 32 + c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+          if (row < p.nS && col < H) p.out[row * H + col] = f2bf(cscale * acc[sb][cb][r]);
+        }
+      }
+  }
+  if (DW && p.grad_b != nullptr) {
+    const int r0 = 16 * w + 8 * h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = gb[e];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, kWave);
+      const int64_t srow = s0 + r0 + e;
+      if (c == 0 && srow < p.V) p.grad_b[srow] = f2bf(cscale * v);
+    }
+  }
+}
+
+template <bool DW>
+static hipError_t launch_bwd_dma(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
+  switch (nb) {
+    case 1: hipLaunchKernelGGL((bwd_dma_kernel<DW, 1>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((bwd_dma_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((bwd_dma_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((bwd_dma_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename T, bool DW, bool SINGLE, int N>
@@ -385,6 +825,13 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
   const int64_t ntile = (a.nS + kBS - 1) / kBS;
   if (ntile == 0) return hipSuccess;
   dim3 grid((unsigned)(ntile * pl.nchunks));
+  if constexpr (sizeof(T) == 2) {
+    if (pl.single) {
+      // whole H per workgroup: the DMA kernel, with the column blocks rounded up to a power of two
+      const int nb2 = pl.nb <= 1 ? 1 : (pl.nb <= 2 ? 2 : (pl.nb <= 4 ? 4 : 8));
+      return dw ? launch_bwd_dma<true>(nb2, a, grid, st) : launch_bwd_dma<false>(nb2, a, grid, st);
+    }
+  }
   if (!dw) {
     return pl.single ? launch_bwd_nb<T, false, true>(pl.nb, a, grid, st)
                      : launch_bwd_nb<T, false, false>(pl.nb, a, grid, st);

@@ -84,10 +84,44 @@ __device__ __forceinline__ void load8(Frag<float>& f, const float* p) {
   f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
+__device__ __forceinline__ void lds_frag_ptr(Frag<bf16_t>& f, const char* p) {
+  f.v = *reinterpret_cast<const bf16x8_t*>(p);
+}
 __device__ __forceinline__ void zero8(Frag<bf16_t>& f) { f.v = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0}; }
 __device__ __forceinline__ void zero8(Frag<float>& f) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads: a scalar descriptor (base, size in bytes) plus a 32-bit per-lane byte
+// offset.  Reads at or past `bytes` return zero, which is how tile edges are masked.
+// Descriptor word 3 = 0x00020000 (gfx9 family: 32-bit data format, no swizzle).
+// ---------------------------------------------------------------------------
+// The arguments must be wave-uniform; readfirstlane keeps the descriptor in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+  n = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
+}
+
+// Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64)); }
+__device__ __forceinline__ void load8(Frag<bf16_t>& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  f.v = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void load8(Frag<float>& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0));
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane (4*r + c) supplies the address of

@@ -205,11 +205,163 @@ __global__ void __launch_bounds__(kFwdThreads) fwd_lse_kernel(const T* __restric
   }
 }
 
+// bf16 forward: 256 vocabulary rows x 256 tokens per workgroup, 8 waves (two per SIMD, so
+// one wave's epilogue and LDS traffic overlap the other's MFMAs), each wave 128 x 64.
+// K is staged 64 elements (128 bytes per row) at a time by buffer->LDS DMA into a double
+// buffer: every wave moves 8 KiB of the stage, rows past V or BT and K past H read as zero
+// (out-of-range buffer offsets).  LDS rows are unpadded: the 16-byte fragment reads of
+// this pattern are conflict free on gfx950.
+constexpr int kFwdThreads2 = 512;
+constexpr int kFwdTileT2 = 256;
+
+// XOR for the 16-byte chunk index of an LDS row of 128 bytes: distinct for any 8 and any
+// 16 consecutive rows.
+__device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+__global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16_t* __restrict__ W,
+                                                                    const bf16_t* __restrict__ h,
+                                                                    const bf16_t* __restrict__ bias,
+                                                                    int64_t BT, int64_t H, int64_t V,
+                                                                    int64_t nt_v, int64_t nt_t,
+                                                                    float* __restrict__ lse_part) {
+  constexpr int ROWB = 128;                       // bytes of one row per stage
+  constexpr int TILE_A = kFwdTileV * ROWB;        // 32 KiB
+  constexpr int TILE_B = kFwdTileT2 * ROWB;       // 32 KiB
+  __shared__ __attribute__((aligned(1024))) char sA[2][TILE_A];
+  __shared__ __attribute__((aligned(1024))) char sB[2][TILE_B];
+  __shared__ float s_bias[kFwdTileV];
+  __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
+
+  const int64_t nwg = nt_v * nt_t;
+  const int64_t id = xcd_remap(blockIdx.x, nwg);
+  constexpr int GT = 4;  // token tiles per raster group
+  const int64_t group = id / (GT * nt_v);
+  const int64_t first_t = group * GT;
+  const int64_t gsize = (nt_t - first_t) < GT ? (nt_t - first_t) : GT;
+  const int64_t in_g = id % (GT * nt_v);
+  const int64_t ttile = first_t + in_g % gsize;
+  const int64_t vtile = in_g / gsize;
+  const int64_t v0 = vtile * kFwdTileV;
+  const int64_t t0 = ttile * kFwdTileT2;
+
+  const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
+  const int wv = w >> 2, wt = w & 3;
+  if (tid < kFwdTileV) {
+    const int64_t v = v0 + tid;
+    s_bias[tid] = (bias != nullptr && v < V) ? bf2f(bias[v]) : 0.f;
+  }
+
+  const int64_t row_bytes = H * 2;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(W + v0 * H, (V - v0) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(h + t0 * H, (BT - t0) * row_bytes);
+  // DMA lane mapping: instruction j of this wave covers rows 8 (4 w + j) .. + 7 of the
+  // stage; lane l lands on row + l / 8, physical 16-byte chunk l % 8, which holds logical
+  // chunk (l % 8) ^ fsw(row).  The swizzle makes the 16-byte fragment reads of 8 and of 16
+  // consecutive rows hit distinct banks.
+  const int drow = lane >> 3, dch = lane & 7;
+  auto dma = [&](int64_t ks, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * (4 * w + j) + drow;
+      const int64_t k = ks * 64 + (dch ^ fsw(row)) * 8;  // first element of this lane's chunk
+      const uint32_t off = k < H ? (uint32_t)(row * row_bytes + k * 2) : 0xfffffff0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(sA[buf] + 1024 * (4 * w + j)),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(sB[buf] + 1024 * (4 * w + j)),
+                                               16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int64_t nk = (H + 63) / 64;
+  dma(0, 0);
+  for (int64_t ks = 0; ks < nk; ++ks) {
+    const int buf = (int)(ks & 1);
+    wait_vm0();
+    __syncthreads();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
+    if (ks + 1 < nk) dma(ks + 1, buf ^ 1);
+    // fragment rows: (wv*128 + vb*32 + lane%32) and (wt*64 + tb*32 + lane%32); the swizzle
+    // depends only on row % 16 = lane % 16, so one XOR value serves every block
+    const int fs = fsw(lane & 31);
+    const char* a_base = sA[buf] + (wv * 128 + (lane & 31)) * ROWB;
+    const char* b_base = sB[buf] + (wt * 64 + (lane & 31)) * ROWB;
+    Frag<bf16_t> fa[2][4], fb[2][2];
+    auto rd = [&](int kk, int slot) {
+      const int off = ((2 * kk + (lane >> 5)) ^ fs) << 4;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) lds_frag_ptr(fa[slot][vb], a_base + vb * 32 * ROWB + off);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) lds_frag_ptr(fb[slot][tb], b_base + tb * 32 * ROWB + off);
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fa[kk & 1][vb], fb[kk & 1][tb], acc[vb][tb]);
+    }
+  }
+
+  // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
+  // two lane halves, then the two vocabulary halves of the tile; rows past V are skipped.
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vr = wv * 128 + vb * 32 + acc_row(lane, r);
+        if (v0 + vr < V) m = fmaxf(m, acc[vb][tb][r] + s_bias[vr]);
+      }
+    float sm = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int vr = wv * 128 + vb * 32 + acc_row(lane, r);
+          if (v0 + vr < V) sm += __expf(acc[vb][tb][r] + s_bias[vr] - m);
+        }
+    }
+    ms_merge(m, sm, __shfl_xor(m, 32, kWave), __shfl_xor(sm, 32, kWave));
+    if (lane < 32) {
+      red_m[wv][wt * 64 + tb * 32 + lane] = m;
+      red_s[wv][wt * 64 + tb * 32 + lane] = sm;
+    }
+  }
+  __syncthreads();
+  if (tid < kFwdTileT2) {
+    float m = red_m[0][tid], sm = red_s[0][tid];
+    ms_merge(m, sm, red_m[1][tid], red_s[1][tid]);
+    const int64_t t = t0 + tid;
+    if (t < BT) lse_part[vtile * BT + t] = m + __logf(sm);
+  }
+}
+
 hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.BT == 0) return hipSuccess;
+  if (a.bf16) {
+    const int64_t nt_t2 = (a.BT + kFwdTileT2 - 1) / kFwdTileT2;
+    hipLaunchKernelGGL(fwd_lse_dma_kernel, dim3((unsigned)(w.nt * nt_t2)), dim3(kFwdThreads2), 0, st,
+                       (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
+                       a.V, w.nt, nt_t2, w.lse_part);
+    return hipGetLastError();
+  }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
   const int64_t n = w.nt * nt_t;
-  if (a.bf16)
+  if (false)
     hipLaunchKernelGGL(fwd_lse_kernel<bf16_t>, dim3((unsigned)n), dim3(kFwdThreads), 0, st,
                        (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
                        a.V, w.nt, nt_t, w.lse_part);
