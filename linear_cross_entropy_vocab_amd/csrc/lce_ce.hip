@@ -28,15 +28,35 @@ struct Vec16;  // 16 bytes of T
 template <> struct Vec16<bf16_t> {
   static constexpr int N = 8;
   uint4 raw;
+  __device__ static uint4 neg_inf() { return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u); }
   __device__ __forceinline__ float get(int i) const {
     const uint32_t w = (&raw.x)[i >> 1];
     return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  // Same value, through an asm statement the optimiser cannot merge with an earlier one,
+  // so a pass over the row does not keep the previous pass's unpacked floats alive.
+  __device__ __forceinline__ float fresh(int i) const {
+    const uint32_t w = (&raw.x)[i >> 1];
+    uint32_t r;
+    if (i & 1)
+      asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w));
+    else
+      asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
+    return __uint_as_float(r);
+  }
+  __device__ static float elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0) << 16);
   }
 };
 template <> struct Vec16<float> {
   static constexpr int N = 4;
   uint4 raw;
+  __device__ static uint4 neg_inf() { return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u); }
   __device__ __forceinline__ float get(int i) const { return __uint_as_float((&raw.x)[i]); }
+  __device__ __forceinline__ float fresh(int i) const { return get(i); }
+  __device__ static float elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  }
 };
 
 __device__ __forceinline__ uint4 pack_out(const float* v, bf16_t) {
@@ -59,78 +79,84 @@ __device__ __forceinline__ void block_ms(float& m, float& s, float* sm, float* s
   for (int i = 0; i < kCEWaves; ++i) ms_merge(m, s, sm[i], ss[i]);  // same order in every thread
 }
 
-// Row cached in registers: NV vectors of 16 B per thread.
+// Row cached in registers: NV vectors of 16 B per thread, all loaded before any is used
+// (buffer loads: bytes past the row read as zero and stores there are dropped).  Only the
+// last vector index can run past the row; those lanes replace it with -inf so neither pass
+// needs a per-element mask.  exp(x - c) is evaluated as exp2(x * log2(e) - c * log2(e)).
 template <typename T, int NV>
 __global__ void __launch_bounds__(kCEThreads) ce_rows_cached(T* __restrict__ logits,
                                                               const int64_t* __restrict__ targets,
                                                               int64_t V, int64_t ignore_index,
                                                               float mu, CERowOut out) {
   constexpr int EPV = Vec16<T>::N;
+  constexpr float kLog2e = 1.4426950408889634f;
+  // one descriptor per vector index j, based at the j-th 16 KiB slice of the row, so every
+  // access uses the same lane offset tid*16 and the bounds check still ends at the row's end
+  constexpr int64_t kSlice = (int64_t)kCEThreads * 16;
   __shared__ float sm[kCEWaves], ss[kCEWaves];
-  __shared__ float s_xy;
   const int64_t row = blockIdx.x;
   T* x = logits + row * V;
-  const int64_t nvec = V / EPV;  // V * sizeof(T) is a multiple of 16 on this path
   const int tid = threadIdx.x;
   const int64_t y = targets[row];
   const bool valid = (y != ignore_index) && (y >= 0) && (y < V);
+  const int64_t row_bytes = V * (int64_t)sizeof(T);
+  const uint32_t lane_off = (uint32_t)tid * 16u;
 
+  // x_y for the row result (thread 0 only; other lanes read past the end and get 0)
+  const float xy = Vec16<T>::elem(make_rsrc(x, row_bytes),
+                                  (tid == 0 && valid) ? (uint32_t)(y * (int64_t)sizeof(T)) : 0xfffffff0u);
   Vec16<T> buf[NV];
+  // the possibly partial last vector first, so its fix-up waits for one load only
+  buf[NV - 1].raw = load16(make_rsrc((const char*)x + (NV - 1) * kSlice, row_bytes - (NV - 1) * kSlice), lane_off);
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int64_t vi = (int64_t)j * kCEThreads + tid;
-    if (vi < nvec) buf[j].raw = reinterpret_cast<const uint4*>(x)[vi];
-    else buf[j].raw = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < NV - 1; ++j)
+    buf[j].raw = load16(make_rsrc((const char*)x + j * kSlice, row_bytes - j * kSlice), lane_off);
+  {
+    const int nvec = (int)(V / EPV);  // V * sizeof(T) is a multiple of 16 on this path
+    const uint32_t keep = ((NV - 1) * kCEThreads + tid < nvec) ? 0xffffffffu : 0u;
+    const uint4 ni = Vec16<T>::neg_inf();
+    uint4& r = buf[NV - 1].raw;
+    r.x = (r.x & keep) | (ni.x & ~keep);
+    r.y = (r.y & keep) | (ni.y & ~keep);
+    r.z = (r.z & keep) | (ni.z & ~keep);
+    r.w = (r.w & keep) | (ni.w & ~keep);
   }
+
   float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int64_t vi = (int64_t)j * kCEThreads + tid;
-    if (vi < nvec) {
+  for (int j = NV - 1; j >= 0; --j)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) m = fmaxf(m, buf[j].get(e));
-    }
-  }
+    for (int e = 0; e < EPV; ++e) m = fmaxf(m, buf[j].get(e));
   float s = 0.f;
-  if (m != -INFINITY) {
+  const float ml = m * kLog2e;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t vi = (int64_t)j * kCEThreads + tid;
-      if (vi < nvec) {
+  for (int j = NV - 1; j >= 0; --j)
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) s += __expf(buf[j].get(e) - m);
-      }
-    }
-  }
-  if (valid) {
-    const int64_t vi = y / EPV;
-    if ((vi % kCEThreads) == tid) {
-      const int j = (int)(vi / kCEThreads);
-#pragma unroll
-      for (int jj = 0; jj < NV; ++jj)
-        if (jj == j) s_xy = buf[jj].get((int)(y % EPV));
-    }
-  }
+    for (int e = 0; e < EPV; ++e) s += __builtin_amdgcn_exp2f(fmaf(buf[j].fresh(e), kLog2e, -ml));
+  if (m == -INFINITY) s = 0.f;
   block_ms(m, s, sm, ss);
   const float lse = m + __logf(s);
   const float scale = valid ? (1.f + 2.f * mu * lse) : 0.f;
+  const float ll = lse * kLog2e;
+  // the lane holding column y subtracts the one-hot term; the test on the wave and the
+  // vector index is wave-uniform, so the other waves branch around it
+  const int yv = valid ? (int)(y / EPV) : 0;
+  const bool owner_wave = valid && ((yv % kCEThreads) / kWave) == wave_id();
+  const bool owner_lane = (yv % kCEThreads) == tid;
+  const int jy = yv / kCEThreads, ey = (int)(y % EPV);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int64_t vi = (int64_t)j * kCEThreads + tid;
-    if (vi < nvec) {
-      float d[EPV];
+    float d[EPV];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int64_t col = vi * EPV + e;
-        float g = __expf(buf[j].get(e) - lse) * scale;
-        if (valid && col == y) g -= 1.f;
-        d[e] = g;
-      }
-      reinterpret_cast<uint4*>(x)[vi] = pack_out(d, T());
+    for (int e = 0; e < EPV; ++e) d[e] = __builtin_amdgcn_exp2f(fmaf(buf[j].fresh(e), kLog2e, -ll)) * scale;
+    if (owner_wave && j == jy) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) d[e] -= (owner_lane && e == ey) ? 1.f : 0.f;
     }
+    store16(make_rsrc((char*)x + j * kSlice, row_bytes - j * kSlice), lane_off, pack_out(d, T()));
   }
   if (tid == 0) {
-    out.ce[row] = valid ? (lse - s_xy) : 0.f;
+    out.ce[row] = valid ? (lse - xy) : 0.f;
     out.zsq[row] = valid ? lse * lse : 0.f;
     out.valid[row] = valid ? 1 : 0;
   }

@@ -27,8 +27,11 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Two floats to packed bfloat16 (round to nearest even) with gfx950's v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_hw));
 }
 
 // Element type traits: storage type and conversions.
@@ -122,6 +125,11 @@ __device__ __forceinline__ void load8(Frag<float>& f, __amdgpu_buffer_rsrc_t r, 
 }
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// Stores at or past the descriptor's size are dropped.
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane (4*r + c) supplies the address of
