@@ -1,6 +1,7 @@
 """Benchmark: fused linear cross-entropy forward + backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ce]
+                    [--copy-calibration]
 
 One step = one lce_fwd_bwd call (loss, grad_input, grad_W) on the headline LM-head
 workload BT=65535, H=1024, V=176245, bf16, mean reduction, no bias, 20% of the targets
@@ -9,6 +10,11 @@ whole-job tokens/s, the dominant kernel's roofline position (per-kernel HIP even
 recorded by the library on the launch stream during the timed steps), the float64 CPU
 oracle timed on a bounded sample of the same workload, and the standalone
 cross-entropy kernel's HBM throughput on [8192, 128256] bf16 logits.
+
+The `traffic` fields are HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter runs of
+this script (profiles/hbm_traffic.json, scaled by the same counters' reading for a plain
+copy of known size, which --copy-calibration adds); they are null when the kernel's
+sources have changed since those counters were taken.
 """
 
 from __future__ import annotations
@@ -28,6 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused LCE fwd+bwd tokens/s & MFMA util (BT=65535,H=1024,V=176245 bf16)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+COPY_CAL_BYTES = 1 << 30    # size of the calibration copy (--copy-calibration)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def _hip():
@@ -50,6 +58,27 @@ def _elapsed(hip, a, b):
     if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
         return float("nan")
     return ms.value
+
+
+def _sha(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing or the kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    for rel, sha in rec["sources"].items():
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path) or _sha(path) != sha:
+            return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def cpu_baseline(inp, n_tokens: int) -> dict:
@@ -96,7 +125,7 @@ def bench_ce(lce, torch, steps: int) -> dict:
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     return {"workload": f"standalone CE+dlogits in place, [{c.B}, {c.V}] bf16, z-loss 0",
             "ms": ms, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+                                   "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("ce_rows")},
             "algorithmic_bytes": algo_bytes}
 
 
@@ -108,6 +137,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ce", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference dispatch for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the fused op "
@@ -134,6 +165,16 @@ def main():
     ws_bytes = lce.fwd_bwd_workspace_bytes(BT, H, V, torch.bfloat16)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     kw = dict(reduction=c.reduction, z_loss=c.z_loss, workspace=ws, out=out)
+
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings give the
+        # factor that turns those counters into bytes for the kernels measured beside it.
+        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: {COPY_CAL_BYTES} bytes copied")
 
     log(f"warmup x{args.warmup}")
     for _ in range(args.warmup):
@@ -184,7 +225,7 @@ def main():
                    "BT": BT, "H": H, "V": V, "reduction": c.reduction, "n_valid": n_valid,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "kernel": dom,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom), "kernel": dom,
                      "algorithmic_flops_per_launch": algo_flops[dom]},
         "tflops_executed": executed,
         "tflops_useful": useful,
