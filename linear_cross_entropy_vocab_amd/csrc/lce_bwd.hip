@@ -23,6 +23,8 @@
 // When the whole of H fits one workgroup (H <= 1024), wave w's K quarter and its output
 // columns coincide, so the X rows loaded for GEMM1 are the ones GEMM3 needs, and the
 // stationary S fragments stay in registers for the whole sweep.
+#include <type_traits>
+
 #include "lce_common.h"
 #include "lce_launch.h"
 
@@ -588,19 +590,22 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dma_kernel(BwdArgs<bf16_t>
     }
     const char* xt = xtile[buf][w];
     // ---------------- GEMM1: partial z[64 x 32] over this wave's K quarter
+    // (accumulated in VGPRs: the AGPR file holds acc)
     f32x16_t zp[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) zp[sb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS1; ++ks) {
       Frag<T> xf;
       lds_frag(xf, xt + lc * XROW + (((2 * ks + lh) ^ xsw<XNCH>(lc)) << 4));
-      mfma_32x32x16(sf[ks][0], xf, zp[0]);
-      mfma_32x32x16(sf[ks][1], xf, zp[1]);
+      if (ks == 0) {
+        mfma_32x32x16_v0(sf[ks][0], xf, zp[0]);
+        mfma_32x32x16_v0(sf[ks][1], xf, zp[1]);
+      } else {
+        mfma_32x32x16_v(sf[ks][0], xf, zp[0]);
+        mfma_32x32x16_v(sf[ks][1], xf, zp[1]);
+      }
       if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the reads in flight
     }
+    mfma_v_drain();
     // ---------------- partial z: the other waves' rows to LDS, own rows kept
     // Rows 16 w' .. 16 w' + 15 live in zp[w' / 2], registers 8 (w' % 2) .. + 7 (local rows
     // 8 j + 4 h + q for register 8 (w' % 2) + 4 j + q).
@@ -730,6 +735,378 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dma_kernel(BwdArgs<bf16_t>
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, H <= 1024: software-pipelined variant.
+//
+// Streamed tiles are 16 rows.  Each wave owns NCOL = 32*NB columns of H (its GEMM1 K range
+// and its GEMM3 output columns), so it only ever touches its own share of a streamed tile:
+// it loads that share into LDS itself (buffer-to-LDS DMA, three buffers per wave) and no
+// barrier guards the tile buffers.  One loop iteration i overlaps two tiles:
+//   phase A: GEMM1 for tile i+1 (16x16x32 MFMA, partial z over the wave's K range)
+//            + the dlogits of tile i from the partial z sums of every wave;   barrier
+//   phase B: GEMM3 for tile i (32x32x16 MFMA, acc += g . X)
+//            + the partial z of tile i+1 written out for the other waves;       barrier
+// and then queues the DMA of tile i+3 into the buffer tile i used.
+//
+// Shared-memory layouts (all reads conflict-free; every address is a per-lane constant plus
+// an immediate, so the loop does almost no address arithmetic):
+//  * a wave's tile share is NB planes of 1 KB; plane j holds the 16-byte chunks 4j..4j+3 of
+//    the 16 rows (columns 32j..32j+31 of the wave's range): chunk (n, 4j+u) sits at
+//    1024 j + 64 n + 16 (u ^ tsw(n)).
+//  * GEMM3 reads 16 of its K rows as four quads; quad k holds tile rows tq(k, 0..3).
+//  * the dlogits tile g[n][m] (n = streamed row, m = stationary row) keeps row n in 128 B
+//    with its four 32-byte groups (16 m values each) permuted by gsw2(n).
+// ---------------------------------------------------------------------------
+constexpr int kPS = 64;   // stationary rows per workgroup (16 per wave after the exchange)
+constexpr int kPX = 16;   // streamed rows per tile
+constexpr int kPBuf = 3;  // tile buffers per wave
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int tsw(int n) { return ((n >> 1) + (n >> 3)) & 3; }
+__device__ __forceinline__ int tq(int k, int r) { return ((k & 1) << 1) + ((k >> 1) << 3) + (r & 1) + ((r >> 1) << 2); }
+__device__ __forceinline__ int gsw2(int n) { return (n & 1) | ((n >> 1) & 2); }
+
+// 16x16x32 bf16 MFMA with a VGPR accumulator (see mfma_32x32x16_v).
+__device__ __forceinline__ void mfma16_v0(const bf16x8_t& a, const bf16x8_t& b, f32x4v& c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_v(const bf16x8_t& a, const bf16x8_t& b, f32x4v& c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ bf16x8_t lds_b128(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+__device__ __forceinline__ bf16x8_t tr_pair(const char* p0, const char* p1) {
+  const i16x4_t a = lds_read_tr16(reinterpret_cast<const bf16_t*>(p0));
+  const i16x4_t b = lds_read_tr16(reinterpret_cast<const bf16_t*>(p1));
+  return bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Loads into LDS issued from inline assembly.  The compiler models a buffer-to-LDS load as a
+// store to LDS of unknown extent and would then wait for every one still in flight before
+// any later LDS read, which would undo the prefetch; here the kernel itself tracks which
+// loads must have landed (vm_wait) before it reads a buffer.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Buffer descriptor words (base, size in bytes; same format as make_rsrc), wave-uniform.
+__device__ __forceinline__ u32x4_t make_rsrc_words(const void* base, int64_t bytes) {
+  uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xffffu;
+  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
+  r.w = 0x00020000u;
+  return r;
+}
+// 16 bytes per lane from rsrc + voff to LDS address lds + 16 * lane.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Plane j of a tile share: 1 KB of LDS from this lane's 16 bytes at off + 64 j.
+template <int J, int N>
+struct DmaPlanes {
+  static __device__ __forceinline__ void run(const u32x4_t& rx, uint32_t lds, uint32_t off) {
+    dma16(rx, lds + 1024 * J, off + 64 * J);
+    DmaPlanes<J + 1, N>::run(rx, lds, off);
+  }
+};
+template <int N>
+struct DmaPlanes<N, N> {
+  static __device__ __forceinline__ void run(const u32x4_t&, uint32_t, uint32_t) {}
+};
+
+template <bool DW, int NB>
+__global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t> p) {
+  constexpr int NCOL = 32 * NB;       // columns of H owned by a wave
+  constexpr int XW = kPX * NCOL * 2;  // bytes of a wave's share of one tile (NB planes)
+  constexpr int NC = DW ? 2 : 1;      // per-tile column loads of a lane (lse, y | bias)
+  constexpr int NQ = NB + NC;         // memory operations queued per tile
+  __shared__ __attribute__((aligned(1024))) char xs[4][kPBuf][XW];
+  __shared__ __attribute__((aligned(1024))) char zx[4][4][1024];  // [writer][row block]
+  __shared__ __attribute__((aligned(256))) char gl[kPX * 128];
+
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int l16 = lane & 15, q = lane >> 4;       // 16x16 operand coordinates
+  const int tc = lane & 3, tr = (lane >> 2) & 3;  // transposed-read coordinates
+  const int64_t s0 = (int64_t)blockIdx.x * kPS;
+  const int64_t H = p.H, row_bytes = H * 2;
+  const int kw0 = w * NCOL;
+  const long long nvalid = *p.n_valid;
+  const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+  const int64_t ntiles = (p.nX + kPX - 1) / kPX;
+
+  // ---- per-lane constants of the stationary rows m = 16 w + 4 q + i (after the exchange)
+  float ra[4], rf[4];
+  int32_t ry[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = s0 + 16 * w + 4 * q + i;
+    if (!DW) {  // token rows: -LSE, z-loss factor, target (-1: row contributes nothing)
+      int32_t yv = -1;
+      float L = 0.f;
+      if (r < p.BT) {
+        const int64_t yt = p.y[r];
+        if (yt != p.ignore_index && yt >= 0 && yt < p.V) {
+          yv = (int32_t)yt;
+          L = p.lse[r];
+        }
+      }
+      ra[i] = -L;
+      rf[i] = 1.f + 2.f * p.mu * L;
+      ry[i] = yv;
+    } else {  // vocabulary rows: bias, validity
+      ra[i] = (p.bias != nullptr && r < p.V) ? bf2f(p.bias[r]) : 0.f;
+      rf[i] = 0.f;
+      ry[i] = r < p.V ? (int32_t)r : -1;
+    }
+  }
+
+  // ---- stationary GEMM1 A fragments: rows 16 rb + l16, k = kw0 + 32 ks + 8 q .. + 7
+  bf16x8_t sf[NB][4];
+  {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.S + s0 * H, (p.nS - s0) * row_bytes);
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int col = kw0 + 32 * ks + 8 * q;
+        const uint32_t off = col < H ? (uint32_t)((16 * rb + l16) * row_bytes + col * 2) : 0x80000000u;
+        sf[ks][rb] = __builtin_bit_cast(bf16x8_t, load16(rs, off));
+      }
+  }
+
+  f32x16_t acc[2][NB];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[sb][cb][r] = 0.f;
+  float gb[4] = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- per-lane LDS offsets
+  // DMA: instruction j of a tile fills plane j; lane l lands at slot l = (row n, chunk u).
+  const int dn = lane >> 2, du = (lane & 3) ^ tsw(lane >> 2);
+  const uint32_t dma_off =
+      (kw0 + 8 * du < H) ? (uint32_t)(dn * row_bytes + (kw0 + 8 * du) * 2) : 0x80000000u;
+  // GEMM1 B operand: tile row l16, chunk 4 ks + q  ->  plane ks, slot (l16, q)
+  const int o_g1 = 64 * l16 + 16 * (q ^ tsw(l16));
+  // GEMM3 B operand (transposed reads): quad 2 (q >> 1) + rd, row tq(.., tr), columns
+  // 16 (q & 1) + 4 tc .. + 3 of the plane's 32
+  int o_g3[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int n = tq(2 * (q >> 1) + rd, tr);
+    const int u = 2 * (q & 1) + (tc >> 1);
+    o_g3[rd] = 64 * n + 16 * (u ^ tsw(n)) + 8 * (tc & 1);
+  }
+  // GEMM3 A operand (dlogits, transposed reads): m group 2 sb + (q & 1)
+  int o_ga[2][2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int n = tq(2 * (q >> 1) + rd, tr);
+      o_ga[sb][rd] = 128 * n + 32 * ((2 * sb + (q & 1)) ^ gsw2(n)) + 8 * tc;
+    }
+  // dlogits writes: column n = l16, rows m = 16 w + 4 q .. + 3
+  const int o_gw = 128 * l16 + 32 * (w ^ gsw2(l16)) + 8 * q;
+
+  char* const xw = xs[w][0];
+  const uint32_t xw_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)xw));
+  auto dma = [&](int64_t tile, int buf) {
+    const int64_t x0 = tile * kPX;
+    const u32x4_t rx = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
+    DmaPlanes<0, NB>::run(rx, xw_lds + (uint32_t)(buf * XW), dma_off);
+  };
+  // column values of tile `tile` for column l16: DW: (-LSE, factor, target) of token x0 + l16;
+  // otherwise the bias of vocabulary row x0 + l16
+  float nc_a = 0.f, nc_f = 0.f;
+  int32_t nc_y = -1;
+  float ld_a = 0.f;
+  int64_t ld_y = 0;
+  auto load_col = [&](int64_t tile) {
+    const int64_t xc = tile * kPX + l16;
+    if (DW) {
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse, p.BT * 4);
+      const __amdgpu_buffer_rsrc_t ryr = make_rsrc(p.y, p.BT * 8);
+      const uint32_t ok = xc < p.BT ? 0u : 0x80000000u;
+      ld_a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (int)(ok | (uint32_t)(xc * 4)), 0, 0));
+      const uint2 yy = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ryr, (int)(ok | (uint32_t)(xc * 8)), 0, 0));
+      ld_y = (int64_t)(((uint64_t)yy.y << 32) | yy.x);
+      if (xc >= p.BT) ld_y = p.ignore_index;
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias != nullptr ? p.V * 2 : 0);
+      ld_a = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                 rb, (int)(xc < p.V ? (uint32_t)(xc * 2) : 0x80000000u), 0, 0) << 16);
+    }
+  };
+  auto take_col = [&](int64_t tile) {  // after the loads of `tile` have landed
+    if (DW) {
+      const bool ok = ld_y != p.ignore_index && ld_y >= 0 && ld_y < p.V;
+      nc_a = ok ? -ld_a : 0.f;
+      nc_f = ok ? 1.f + 2.f * p.mu * ld_a : 0.f;
+      nc_y = ok ? (int32_t)ld_y : -1;
+    } else {
+      const int64_t xc = tile * kPX + l16;
+      nc_a = ld_a;
+      nc_y = xc < p.V ? (int32_t)xc : -1;  // vocabulary index of the column (-1: past V)
+    }
+  };
+
+  // ---- GEMM1 of one tile: partial z[64 x 16] over this wave's K range, four 16-row blocks
+  f32x4v zp[4];
+  auto gemm1 = [&](int buf) {
+    const char* xb = xw + buf * XW + o_g1;
+    bf16x8_t xf[NB];
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks) xf[ks] = lds_b128(xb + 1024 * ks);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) mfma16_v0(sf[0][rb], xf[0], zp[rb]);
+#pragma unroll
+    for (int ks = 1; ks < NB; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) mfma16_v(sf[ks][rb], xf[ks], zp[rb]);
+  };
+  // partial z of the other waves' row blocks to LDS; the own block stays in registers
+  f32x4v zown;
+  auto put_partials = [&]() {
+    // wait states after the last MFMA writing zp, before anything else reads it
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(zp[0]), "+v"(zp[1]), "+v"(zp[2]), "+v"(zp[3]));
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb == w) {
+        zown = zp[rb];
+      } else {
+        *reinterpret_cast<f32x4v*>(zx[w][rb] + 16 * lane) = zp[rb];
+      }
+    }
+  };
+  // dlogits of one tile for rows 16 w + 4 q + i, column l16 -> LDS (bf16)
+  auto dlogits = [&]() {
+    f32x4v z = zown;
+#pragma unroll
+    for (int wp = 0; wp < 4; ++wp) {
+      if (wp == w) continue;
+      z += *reinterpret_cast<const f32x4v*>(zx[wp][w] + 16 * lane);
+    }
+    float g[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float gi;
+      if (!DW) {
+        const bool ok = ry[i] >= 0 && nc_y >= 0;
+        gi = __expf(z[i] + nc_a + ra[i]) * rf[i] - (ry[i] == nc_y ? 1.f : 0.f);
+        g[i] = ok ? gi : 0.f;
+      } else {
+        const bool ok = ry[i] >= 0 && nc_y >= 0;
+        gi = __expf(z[i] + ra[i] + nc_a) * nc_f - (nc_y == ry[i] ? 1.f : 0.f);
+        g[i] = ok ? gi : 0.f;
+        gb[i] += g[i];
+      }
+    }
+    *reinterpret_cast<uint2*>(gl + o_gw) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+  };
+  // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]
+  auto gemm3 = [&](int buf) {
+    const char* xb = xw + buf * XW;
+    Frag<bf16_t> ga[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) ga[sb].v = tr_pair(gl + o_ga[sb][0], gl + o_ga[sb][1]);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      Frag<bf16_t> xf;
+      xf.v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
+      mfma_32x32x16(ga[0], xf, acc[0][cb]);
+      mfma_32x32x16(ga[1], xf, acc[1][cb]);
+    }
+  };
+
+  if (ntiles > 0) {
+    // prologue: tiles 0 and 1, the column values of tile 0, tile 2 (short sweeps repeat the
+    // last tile into buffers that are never read, so the queue always has the same shape)
+    const int64_t last = ntiles - 1;
+    dma(0, 0);
+    dma(last < 1 ? last : 1, 1);
+    load_col(0);
+    dma(last < 2 ? last : 2, 2);
+    vm_wait<2 * NB + NC>();  // tile 0 has landed
+    gemm1(0);
+    put_partials();
+    __syncthreads();
+  }
+  for (int64_t i = 0; i < ntiles; ++i) {
+    const int bi = (int)(i % kPBuf), bn = (int)((i + 1) % kPBuf);
+    const bool more = i + 1 < ntiles;
+    // ---- phase A: GEMM1 of tile i+1, dlogits of tile i
+    if (more) {
+      vm_wait<NQ>();  // tile i+1 has landed (queued after it: column values of i, tile i+2)
+      gemm1(bn);
+    }
+    vm_wait<NB>();  // column values of tile i
+    take_col(i);
+    dlogits();
+    __syncthreads();
+    // ---- phase B: GEMM3 of tile i, partial z of tile i+1 for the other waves
+    gemm3(bi);
+    if (more) put_partials();
+    __syncthreads();
+    // ---- queue the column values of tile i+1 and tile i+3 (into buffer bi, free once this
+    // wave's reads of it are done; past the end the last tile is repeated, never read)
+    if (more) {
+      load_col(i + 1);
+      lgkm_wait0();
+      dma(i + 3 < ntiles ? i + 3 : ntiles - 1, bi);
+    }
+  }
+  vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
+
+  // ---- write c * acc
+  if (p.out != nullptr) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t col = kw0 + cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+          if (row < p.nS && col < H) p.out[row * H + col] = f2bf(cscale * acc[sb][cb][r]);
+        }
+      }
+  }
+  if (DW && p.grad_b != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = gb[i];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
+      const int64_t r = s0 + 16 * w + 4 * q + i;
+      if (l16 == 0 && r < p.V) p.grad_b[r] = f2bf(cscale * v);
+    }
+  }
+}
+
+template <bool DW>
+static hipError_t launch_bwd_pipe(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
+  switch (nb) {
+    case 1: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 1>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <bool DW>
 static hipError_t launch_bwd_dma(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
   switch (nb) {
@@ -829,7 +1206,7 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
     if (pl.single) {
       // whole H per workgroup: the DMA kernel, with the column blocks rounded up to a power of two
       const int nb2 = pl.nb <= 1 ? 1 : (pl.nb <= 2 ? 2 : (pl.nb <= 4 ? 4 : 8));
-      return dw ? launch_bwd_dma<true>(nb2, a, grid, st) : launch_bwd_dma<false>(nb2, a, grid, st);
+      return dw ? launch_bwd_pipe<true>(nb2, a, grid, st) : launch_bwd_pipe<false>(nb2, a, grid, st);
     }
   }
   if (!dw) {

@@ -69,6 +69,20 @@ template <> struct Frag<float> {
 __device__ __forceinline__ void mfma_32x32x16(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x16_t& c) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
 }
+// The same bf16 MFMA with its accumulator in VGPRs.  The builtin puts every MFMA
+// accumulator in AGPRs once a kernel uses them; a kernel whose long-lived accumulator fills
+// the AGPR file uses these for a short-lived second one so the two never compete.
+// Hazards the compiler cannot see through the asm are covered here: two wait states
+// before each MFMA (a VALU write of an operand just before it), and mfma_v_drain() after
+// the last one of a chain, before anything but another MFMA reads the accumulator.
+__device__ __forceinline__ void mfma_32x32x16_v0(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x16_t& c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a.v), "v"(b.v));
+}
+__device__ __forceinline__ void mfma_32x32x16_v(const Frag<bf16_t>& a, const Frag<bf16_t>& b, f32x16_t& c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a.v), "v"(b.v));
+}
+__device__ __forceinline__ void mfma_v_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 __device__ __forceinline__ void mfma_32x32x16(const Frag<float>& a, const Frag<float>& b, f32x16_t& c) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[s], b.v[s], c, 0, 0, 0);
