@@ -767,12 +767,13 @@ __device__ __forceinline__ int tsw(int n) { return ((n >> 1) + (n >> 3)) & 3; }
 __device__ __forceinline__ int tq(int k, int r) { return ((k & 1) << 1) + ((k >> 1) << 3) + (r & 1) + ((r >> 1) << 2); }
 __device__ __forceinline__ int gsw2(int n) { return (n & 1) | ((n >> 1) & 2); }
 
-// 16x16x32 bf16 MFMA with a VGPR accumulator (see mfma_32x32x16_v).
+// 16x16x32 bf16 MFMA with a VGPR accumulator (see mfma_32x32x16_v).  Its operands here come
+// from memory loads only (no VALU writes), so no wait states are needed in front of it.
 __device__ __forceinline__ void mfma16_v0(const bf16x8_t& a, const bf16x8_t& b, f32x4v& c) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma16_v(const bf16x8_t& a, const bf16x8_t& b, f32x4v& c) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ bf16x8_t lds_b128(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 __device__ __forceinline__ bf16x8_t tr_pair(const char* p0, const char* p1) {
@@ -799,7 +800,16 @@ __device__ __forceinline__ u32x4_t make_rsrc_words(const void* base, int64_t byt
 }
 // 16 bytes per lane from rsrc + voff to LDS address lds + 16 * lane.
 __device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rsrc)
+               : "memory", "m0");
+}
+// Same, ordered after the LDS read that produced `dep` has completed (the compiler waits for
+// the registers an asm statement reads): used to refill a buffer region right after its
+// last read.
+__device__ __forceinline__ void dma16_after(const u32x4_t& rsrc, uint32_t lds, uint32_t voff, const bf16x8_t& dep) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rsrc), "v"(dep)
                : "memory", "m0");
 }
 template <int N>
@@ -962,19 +972,24 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     }
   };
 
-  // ---- GEMM1 of one tile: partial z[64 x 16] over this wave's K range, four 16-row blocks
+  // ---- GEMM1 of one tile: partial z[64 x 16] over this wave's K range, four 16-row blocks,
+  // in two halves (the dlogits of the previous tile are computed between them)
   f32x4v zp[4];
-  auto gemm1 = [&](int buf) {
+  bf16x8_t xf1[NB];
+  auto gemm1_reads = [&](int buf) {
     const char* xb = xw + buf * XW + o_g1;
-    bf16x8_t xf[NB];
 #pragma unroll
-    for (int ks = 0; ks < NB; ++ks) xf[ks] = lds_b128(xb + 1024 * ks);
+    for (int ks = 0; ks < NB; ++ks) xf1[ks] = lds_b128(xb + 1024 * ks);
+  };
+  auto gemm1_part = [&](auto k0c, auto k1c) {
+    constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) mfma16_v0(sf[0][rb], xf[0], zp[rb]);
+    for (int ks = K0; ks < K1; ++ks)
 #pragma unroll
-    for (int ks = 1; ks < NB; ++ks)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) mfma16_v(sf[ks][rb], xf[ks], zp[rb]);
+      for (int rb = 0; rb < 4; ++rb) {
+        if (ks == 0) mfma16_v0(sf[ks][rb], xf1[ks], zp[rb]);
+        else mfma16_v(sf[ks][rb], xf1[ks], zp[rb]);
+      }
   };
   // partial z of the other waves' row blocks to LDS; the own block stays in registers
   f32x4v zown;
@@ -990,34 +1005,37 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
       }
     }
   };
+  // the other waves' partial sums of this wave's row block (written before the last barrier)
+  f32x4v zpr[3];
+  auto partial_reads = [&]() {
+#pragma unroll
+    for (int x = 1; x < 4; ++x) zpr[x - 1] = *reinterpret_cast<const f32x4v*>(zx[w ^ x][w] + 16 * lane);
+  };
   // dlogits of one tile for rows 16 w + 4 q + i, column l16 -> LDS (bf16)
   auto dlogits = [&]() {
-    f32x4v z = zown;
-#pragma unroll
-    for (int wp = 0; wp < 4; ++wp) {
-      if (wp == w) continue;
-      z += *reinterpret_cast<const f32x4v*>(zx[wp][w] + 16 * lane);
-    }
+    const f32x4v z = zown + zpr[0] + zpr[1] + zpr[2];
     float g[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const bool ok = ry[i] >= 0 && nc_y >= 0;
       float gi;
       if (!DW) {
-        const bool ok = ry[i] >= 0 && nc_y >= 0;
         gi = __expf(z[i] + nc_a + ra[i]) * rf[i] - (ry[i] == nc_y ? 1.f : 0.f);
-        g[i] = ok ? gi : 0.f;
       } else {
-        const bool ok = ry[i] >= 0 && nc_y >= 0;
         gi = __expf(z[i] + ra[i] + nc_a) * nc_f - (nc_y == ry[i] ? 1.f : 0.f);
-        g[i] = ok ? gi : 0.f;
-        gb[i] += g[i];
       }
+      g[i] = ok ? gi : 0.f;
+      if (DW) gb[i] += g[i];
     }
     *reinterpret_cast<uint2*>(gl + o_gw) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
   };
-  // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]
-  auto gemm3 = [&](int buf) {
+  // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]; with `refill`, plane cb of
+  // the buffer is reloaded (tile `next`) as soon as its last read has completed
+  auto gemm3 = [&](int buf, bool refill, int64_t next) {
     const char* xb = xw + buf * XW;
+    const int64_t x0 = next * kPX;
+    const u32x4_t rx = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
+    const uint32_t lds = xw_lds + (uint32_t)(buf * XW);
     Frag<bf16_t> ga[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) ga[sb].v = tr_pair(gl + o_ga[sb][0], gl + o_ga[sb][1]);
@@ -1027,8 +1045,12 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
       xf.v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
       mfma_32x32x16(ga[0], xf, acc[0][cb]);
       mfma_32x32x16(ga[1], xf, acc[1][cb]);
+      if (refill) dma16_after(rx, lds + 1024 * cb, dma_off + 64 * cb, xf.v);
     }
   };
+  typedef std::integral_constant<int, 0> C0;
+  typedef std::integral_constant<int, NB / 2> CH;
+  typedef std::integral_constant<int, NB> CN;
 
   if (ntiles > 0) {
     // prologue: tiles 0 and 1, the column values of tile 0, tile 2 (short sweeps repeat the
@@ -1039,33 +1061,34 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     load_col(0);
     dma(last < 2 ? last : 2, 2);
     vm_wait<2 * NB + NC>();  // tile 0 has landed
-    gemm1(0);
+    gemm1_reads(0);
+    gemm1_part(C0{}, CN{});
     put_partials();
     __syncthreads();
   }
+  // Memory queue of a wave, oldest first: ..., column values of tile i, tile i+2, column
+  // values of tile i+1, tile i+3, ...; at the top of iteration i everything up to the column
+  // values of tile i (so also tile i+1) must have landed.
   for (int64_t i = 0; i < ntiles; ++i) {
     const int bi = (int)(i % kPBuf), bn = (int)((i + 1) % kPBuf);
     const bool more = i + 1 < ntiles;
-    // ---- phase A: GEMM1 of tile i+1, dlogits of tile i
-    if (more) {
-      vm_wait<NQ>();  // tile i+1 has landed (queued after it: column values of i, tile i+2)
-      gemm1(bn);
-    }
-    vm_wait<NB>();  // column values of tile i
+    // ---- phase A: GEMM1 of tile i+1 around the dlogits of tile i
+    vm_wait<NB>();
+    partial_reads();
     take_col(i);
+    if (more) {
+      gemm1_reads(bn);
+      gemm1_part(C0{}, CH{});
+    }
     dlogits();
+    if (more) gemm1_part(CH{}, CN{});
     __syncthreads();
-    // ---- phase B: GEMM3 of tile i, partial z of tile i+1 for the other waves
-    gemm3(bi);
+    // ---- phase B: GEMM3 of tile i (refilling its buffer with tile i+3 plane by plane; past
+    // the end the last tile is repeated, never read), partial z of tile i+1
+    if (more) load_col(i + 1);
+    gemm3(bi, more, i + 3 < ntiles ? i + 3 : ntiles - 1);
     if (more) put_partials();
     __syncthreads();
-    // ---- queue the column values of tile i+1 and tile i+3 (into buffer bi, free once this
-    // wave's reads of it are done; past the end the last tile is repeated, never read)
-    if (more) {
-      load_col(i + 1);
-      lgkm_wait0();
-      dma(i + 3 < ntiles ? i + 3 : ntiles - 1, bi);
-    }
   }
   vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
 
