@@ -1029,13 +1029,17 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     }
     *reinterpret_cast<uint2*>(gl + o_gw) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
   };
-  // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]; with `refill`, plane cb of
-  // the buffer is reloaded (tile `next`) as soon as its last read has completed
+  // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]; with `refill`, planes
+  // 0 .. NB/2-1 of the buffer are reloaded (tile `next`) as soon as their last read has
+  // completed; the other half is queued during the next phase A (refill_rest), so that the
+  // loads of the four waves spread over both phases.
+  u32x4_t rx_next;
+  uint32_t lds_next = 0;
   auto gemm3 = [&](int buf, bool refill, int64_t next) {
     const char* xb = xw + buf * XW;
     const int64_t x0 = next * kPX;
-    const u32x4_t rx = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
-    const uint32_t lds = xw_lds + (uint32_t)(buf * XW);
+    rx_next = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
+    lds_next = xw_lds + (uint32_t)(buf * XW);
     Frag<bf16_t> ga[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) ga[sb].v = tr_pair(gl + o_ga[sb][0], gl + o_ga[sb][1]);
@@ -1045,8 +1049,13 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
       xf.v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
       mfma_32x32x16(ga[0], xf, acc[0][cb]);
       mfma_32x32x16(ga[1], xf, acc[1][cb]);
-      if (refill) dma16_after(rx, lds + 1024 * cb, dma_off + 64 * cb, xf.v);
+      if (refill && cb < NB / 2) dma16_after(rx_next, lds_next + 1024 * cb, dma_off + 64 * cb, xf.v);
     }
+  };
+  // (the reads of these planes completed in the previous phase: GEMM3 waited for them)
+  auto refill_rest = [&]() {
+#pragma unroll
+    for (int cb = NB / 2; cb < NB; ++cb) dma16(rx_next, lds_next + 1024 * cb, dma_off + 64 * cb);
   };
   typedef std::integral_constant<int, 0> C0;
   typedef std::integral_constant<int, NB / 2> CH;
@@ -1066,16 +1075,18 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     put_partials();
     __syncthreads();
   }
-  // Memory queue of a wave, oldest first: ..., column values of tile i, tile i+2, column
-  // values of tile i+1, tile i+3, ...; at the top of iteration i everything up to the column
-  // values of tile i (so also tile i+1) must have landed.
+  // Memory queue of a wave, oldest first: ..., column values of tile i, first half of tile
+  // i+2, second half of tile i+2, column values of tile i+1, first half of tile i+3, ...; at
+  // the top of iteration i everything up to the column values of tile i (so also all of
+  // tile i+1) must have landed; only the first half of tile i+2 may still be in flight.
   for (int64_t i = 0; i < ntiles; ++i) {
     const int bi = (int)(i % kPBuf), bn = (int)((i + 1) % kPBuf);
     const bool more = i + 1 < ntiles;
     // ---- phase A: GEMM1 of tile i+1 around the dlogits of tile i
-    vm_wait<NB>();
+    vm_wait<NB - NB / 2>();
     partial_reads();
     take_col(i);
+    if (i > 0) refill_rest();  // second half of tile i+2 (the buffer of tile i-1)
     if (more) {
       gemm1_reads(bn);
       gemm1_part(C0{}, CH{});
