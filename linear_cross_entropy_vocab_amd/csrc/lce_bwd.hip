@@ -41,6 +41,7 @@ struct BwdArgs {
   const T* bias;
   const int64_t* y;
   const float* lse;
+  const float2* tok;  // per token: (LSE, target + 1, or 0 for rows that contribute nothing)
   int64_t nS, nX, H, BT, V;
   int64_t ignore_index;
   float mu;
@@ -836,7 +837,7 @@ template <bool DW, int NB>
 __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t> p) {
   constexpr int NCOL = 32 * NB;       // columns of H owned by a wave
   constexpr int XW = kPX * NCOL * 2;  // bytes of a wave's share of one tile (NB planes)
-  constexpr int NC = DW ? 2 : 1;      // per-tile column loads of a lane (lse, y | bias)
+  constexpr int NC = 1;               // per-tile column loads of a lane (token (LSE, target) | bias)
   constexpr int NQ = NB + NC;         // memory operations queued per tile
   __shared__ __attribute__((aligned(1024))) char xs[4][kPBuf][XW];
   __shared__ __attribute__((aligned(1024))) char zx[4][4][1024];  // [writer][row block]
@@ -862,11 +863,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
       int32_t yv = -1;
       float L = 0.f;
       if (r < p.BT) {
-        const int64_t yt = p.y[r];
-        if (yt != p.ignore_index && yt >= 0 && yt < p.V) {
-          yv = (int32_t)yt;
-          L = p.lse[r];
-        }
+        const float2 tk = p.tok[r];
+        yv = __float_as_int(tk.y) - 1;
+        L = yv >= 0 ? tk.x : 0.f;
       }
       ra[i] = -L;
       rf[i] = 1.f + 2.f * p.mu * L;
@@ -874,9 +873,14 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     } else {  // vocabulary rows: bias, validity
       ra[i] = (p.bias != nullptr && r < p.V) ? bf2f(p.bias[r]) : 0.f;
       rf[i] = 0.f;
-      ry[i] = r < p.V ? (int32_t)r : -1;
+      ry[i] = 0;  // (vocabulary rows: the index is rebuilt from vrow0 where it is needed)
     }
   }
+
+  // vocabulary rows (DW): row 16 w + 4 q + i is vocabulary entry vrow0 + i; rows past V
+  // contribute nothing
+  const int32_t vrow0 = (int32_t)(s0 + 16 * w + 4 * q);
+  const int32_t vlim = (int32_t)(p.V < (int64_t)0x7fffffff ? p.V : 0x7fffffff);
 
   // ---- stationary GEMM1 A fragments: rows 16 rb + l16, k = kw0 + 32 ks + 8 q .. + 7
   bf16x8_t sf[NB][4];
@@ -941,33 +945,29 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   // otherwise the bias of vocabulary row x0 + l16
   float nc_a = 0.f, nc_f = 0.f;
   int32_t nc_y = -1;
-  float ld_a = 0.f;
-  int64_t ld_y = 0;
+  uint2 ld = make_uint2(0u, 0u);
   auto load_col = [&](int64_t tile) {
     const int64_t xc = tile * kPX + l16;
-    if (DW) {
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse, p.BT * 4);
-      const __amdgpu_buffer_rsrc_t ryr = make_rsrc(p.y, p.BT * 8);
-      const uint32_t ok = xc < p.BT ? 0u : 0x80000000u;
-      ld_a = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (int)(ok | (uint32_t)(xc * 4)), 0, 0));
-      const uint2 yy = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ryr, (int)(ok | (uint32_t)(xc * 8)), 0, 0));
-      ld_y = (int64_t)(((uint64_t)yy.y << 32) | yy.x);
-      if (xc >= p.BT) ld_y = p.ignore_index;
+    if (DW) {  // rows past BT read as (0, 0): no target
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.tok, p.BT * 8);
+      ld = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                         rt, (int)(xc < p.BT ? (uint32_t)(xc * 8) : 0x80000000u), 0, 0));
     } else {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias != nullptr ? p.V * 2 : 0);
-      ld_a = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                 rb, (int)(xc < p.V ? (uint32_t)(xc * 2) : 0x80000000u), 0, 0) << 16);
+      ld.x = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (int)(xc < p.V ? (uint32_t)(xc * 2) : 0x80000000u),
+                                                            0, 0)
+             << 16;
     }
   };
   auto take_col = [&](int64_t tile) {  // after the loads of `tile` have landed
     if (DW) {
-      const bool ok = ld_y != p.ignore_index && ld_y >= 0 && ld_y < p.V;
-      nc_a = ok ? -ld_a : 0.f;
-      nc_f = ok ? 1.f + 2.f * p.mu * ld_a : 0.f;
-      nc_y = ok ? (int32_t)ld_y : -1;
+      const float L = __uint_as_float(ld.x);
+      nc_y = (int32_t)ld.y - 1;
+      nc_a = nc_y >= 0 ? -L : 0.f;
+      nc_f = nc_y >= 0 ? 1.f + 2.f * p.mu * L : 0.f;
     } else {
       const int64_t xc = tile * kPX + l16;
-      nc_a = ld_a;
+      nc_a = __uint_as_float(ld.x);
       nc_y = xc < p.V ? (int32_t)xc : -1;  // vocabulary index of the column (-1: past V)
     }
   };
@@ -1017,12 +1017,14 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     float g[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = ry[i] >= 0 && nc_y >= 0;
+      bool ok;
       float gi;
       if (!DW) {
+        ok = ry[i] >= 0 && nc_y >= 0;
         gi = __expf(z[i] + nc_a + ra[i]) * rf[i] - (ry[i] == nc_y ? 1.f : 0.f);
       } else {
-        gi = __expf(z[i] + ra[i] + nc_a) * nc_f - (nc_y == ry[i] ? 1.f : 0.f);
+        ok = vrow0 + i < vlim && nc_y >= 0;
+        gi = __expf(z[i] + ra[i] + nc_a) * nc_f - (nc_y == vrow0 + i ? 1.f : 0.f);
       }
       g[i] = ok ? gi : 0.f;
       if (DW) gb[i] += g[i];
@@ -1209,6 +1211,7 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
   a.bias = static_cast<const T*>(fa.bias);
   a.y = fa.targets;
   a.lse = w.lse;
+  a.tok = w.tok;
   a.H = fa.H;
   a.BT = fa.BT;
   a.V = fa.V;

@@ -428,7 +428,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     const float* __restrict__ part, int64_t nt, int64_t BT, const float* __restrict__ zy,
     const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float* __restrict__ lse,
     float* __restrict__ lse_out, double* __restrict__ blk_ce, double* __restrict__ blk_z,
-    int64_t nblk) {
+    int64_t nblk, float2* __restrict__ tok) {
   __shared__ double s_a[kMergeThreads / kWave], s_b[kMergeThreads / kWave];
   const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
   double ce = 0.0, zz = 0.0;
@@ -447,10 +447,12 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     lse[t] = L;
     if (lse_out) lse_out[t] = L;
     const int64_t yt = y[t];
-    if (yt != ignore_index && yt >= 0 && yt < V) {
+    const bool valid = yt != ignore_index && yt >= 0 && yt < V;
+    if (valid) {
       ce = (double)L - (double)zy[t];
       zz = (double)L * (double)L;
     }
+    tok[t] = make_float2(L, __int_as_float(valid ? (int32_t)yt + 1 : 0));
   }
   ce = wave_sum_d(ce);
   zz = wave_sum_d(zz);
@@ -468,7 +470,7 @@ hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.BT == 0) return hipSuccess;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)w.nblk), dim3(kMergeThreads), 0, st, w.lse_part, w.nt,
                      a.BT, w.zy, a.targets, a.V, a.ignore_index, w.lse, a.lse_out, w.blk,
-                     w.blk + w.nblk, w.nblk);
+                     w.blk + w.nblk, w.nblk, w.tok);
   return hipGetLastError();
 }
 
