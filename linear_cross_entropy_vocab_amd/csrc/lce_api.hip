@@ -21,6 +21,7 @@ size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
   n += ws_align((size_t)bt * 4);                   // zy
   n += ws_align((size_t)nblk * 2 * 8);             // block sums
   n += ws_align((size_t)bt * 8);                   // per-token (LSE, target) for the backward
+  n += ws_align((size_t)V * 4);                    // fp32 bias for the backward
   return n;
 }
 
@@ -43,6 +44,8 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t V) {
   w.blk = reinterpret_cast<double*>(p);
   p += ws_align((size_t)nblk_alloc * 2 * 8);
   w.tok = reinterpret_cast<float2*>(p);
+  p += ws_align((size_t)bt * 8);
+  w.biasf = reinterpret_cast<float*>(p);
   return w;
 }
 

@@ -42,6 +42,7 @@ struct BwdArgs {
   const int64_t* y;
   const float* lse;
   const float2* tok;  // per token: (LSE, target + 1, or 0 for rows that contribute nothing)
+  const float* biasf;  // bias in fp32, or NULL
   int64_t nS, nX, H, BT, V;
   int64_t ignore_index;
   float mu;
@@ -760,7 +761,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dma_kernel(BwdArgs<bf16_t>
 // ---------------------------------------------------------------------------
 constexpr int kPS = 64;   // stationary rows per workgroup (16 per wave after the exchange)
 constexpr int kPX = 16;   // streamed rows per tile
-constexpr int kPBuf = 3;  // tile buffers per wave
+constexpr int kPBuf = 4;  // tile buffers per wave
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -808,6 +809,11 @@ __device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t lds, uint32_
 // Same, ordered after the LDS read that produced `dep` has completed (the compiler waits for
 // the registers an asm statement reads): used to refill a buffer region right after its
 // last read.
+// 4 bytes per lane from rsrc + voff to LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma4(const u32x4_t& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma16_after(const u32x4_t& rsrc, uint32_t lds, uint32_t voff, const bf16x8_t& dep) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
                "s"(rsrc), "v"(dep)
@@ -837,11 +843,13 @@ template <bool DW, int NB>
 __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t> p) {
   constexpr int NCOL = 32 * NB;       // columns of H owned by a wave
   constexpr int XW = kPX * NCOL * 2;  // bytes of a wave's share of one tile (NB planes)
-  constexpr int NC = 1;               // per-tile column loads of a lane (token (LSE, target) | bias)
-  constexpr int NQ = NB + NC;         // memory operations queued per tile
+  constexpr int NQ = NB + 1;          // loads queued per tile: its planes and its column values
   __shared__ __attribute__((aligned(1024))) char xs[4][kPBuf][XW];
   __shared__ __attribute__((aligned(1024))) char zx[4][4][1024];  // [writer][row block]
   __shared__ __attribute__((aligned(256))) char gl[kPX * 128];
+  // column values of each buffered tile, loaded with it: per token (LSE, target + 1) (DW)
+  // or the fp32 bias of each vocabulary row
+  __shared__ __attribute__((aligned(256))) char cs[4][kPBuf][256];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int l16 = lane & 15, q = lane >> 4;       // 16x16 operand coordinates
@@ -936,8 +944,18 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   char* const xw = xs[w][0];
   const uint32_t xw_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)xw));
+  const uint32_t cs_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)cs[w][0]));
+  // column values of a tile: 4 bytes per lane (DW: 16 tokens x 8 B; otherwise 16 x 4 B)
+  const uint32_t col_off = lane < (DW ? 32 : 16) ? 4u * lane : 0x80000000u;
+  auto col_rsrc = [&](int64_t tile) {
+    const int64_t x0 = tile * kPX;
+    return DW ? make_rsrc_words(p.tok + x0, (p.BT - x0) * 8)
+              : make_rsrc_words(p.biasf + x0, p.biasf != nullptr ? (p.V - x0) * 4 : 0);
+  };
   auto dma = [&](int64_t tile, int buf) {
     const int64_t x0 = tile * kPX;
+    dma4(col_rsrc(tile), cs_lds + (uint32_t)(buf * 256), col_off);
     const u32x4_t rx = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
     DmaPlanes<0, NB>::run(rx, xw_lds + (uint32_t)(buf * XW), dma_off);
   };
@@ -945,29 +963,16 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   // otherwise the bias of vocabulary row x0 + l16
   float nc_a = 0.f, nc_f = 0.f;
   int32_t nc_y = -1;
-  uint2 ld = make_uint2(0u, 0u);
-  auto load_col = [&](int64_t tile) {
-    const int64_t xc = tile * kPX + l16;
-    if (DW) {  // rows past BT read as (0, 0): no target
-      const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.tok, p.BT * 8);
-      ld = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                         rt, (int)(xc < p.BT ? (uint32_t)(xc * 8) : 0x80000000u), 0, 0));
-    } else {
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias != nullptr ? p.V * 2 : 0);
-      ld.x = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (int)(xc < p.V ? (uint32_t)(xc * 2) : 0x80000000u),
-                                                            0, 0)
-             << 16;
-    }
-  };
-  auto take_col = [&](int64_t tile) {  // after the loads of `tile` have landed
+  auto take_col = [&](int64_t tile, int buf) {  // after the loads of `tile` have landed
     if (DW) {
-      const float L = __uint_as_float(ld.x);
-      nc_y = (int32_t)ld.y - 1;
+      const float2 t = *reinterpret_cast<const float2*>(cs[w][buf] + 8 * l16);
+      const float L = t.x;
+      nc_y = __float_as_int(t.y) - 1;
       nc_a = nc_y >= 0 ? -L : 0.f;
       nc_f = nc_y >= 0 ? 1.f + 2.f * p.mu * L : 0.f;
     } else {
       const int64_t xc = tile * kPX + l16;
-      nc_a = __uint_as_float(ld.x);
+      nc_a = *reinterpret_cast<const float*>(cs[w][buf] + 4 * l16);
       nc_y = xc < p.V ? (int32_t)xc : -1;  // vocabulary index of the column (-1: past V)
     }
   };
@@ -976,10 +981,11 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   // in two halves (the dlogits of the previous tile are computed between them)
   f32x4v zp[4];
   bf16x8_t xf1[NB];
-  auto gemm1_reads = [&](int buf) {
+  auto gemm1_reads = [&](int buf, auto k0c, auto k1c) {
+    constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
     const char* xb = xw + buf * XW + o_g1;
 #pragma unroll
-    for (int ks = 0; ks < NB; ++ks) xf1[ks] = lds_b128(xb + 1024 * ks);
+    for (int ks = K0; ks < K1; ++ks) xf1[ks] = lds_b128(xb + 1024 * ks);
   };
   auto gemm1_part = [&](auto k0c, auto k1c) {
     constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
@@ -1042,6 +1048,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     const int64_t x0 = next * kPX;
     rx_next = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
     lds_next = xw_lds + (uint32_t)(buf * XW);
+    if (refill) dma4(col_rsrc(next), cs_lds + (uint32_t)(buf * 256), col_off);
     Frag<bf16_t> ga[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) ga[sb].v = tr_pair(gl + o_ga[sb][0], gl + o_ga[sb][1]);
@@ -1067,39 +1074,39 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     // prologue: tiles 0 and 1, the column values of tile 0, tile 2 (short sweeps repeat the
     // last tile into buffers that are never read, so the queue always has the same shape)
     const int64_t last = ntiles - 1;
-    dma(0, 0);
-    dma(last < 1 ? last : 1, 1);
-    load_col(0);
-    dma(last < 2 ? last : 2, 2);
-    vm_wait<2 * NB + NC>();  // tile 0 has landed
-    gemm1_reads(0);
+#pragma unroll
+    for (int b = 0; b < kPBuf; ++b) dma(b < last ? b : last, b);
+    vm_wait<(kPBuf - 1) * NQ>();  // tile 0 has landed
+    gemm1_reads(0, C0{}, CN{});
     gemm1_part(C0{}, CN{});
     put_partials();
     __syncthreads();
   }
-  // Memory queue of a wave, oldest first: ..., column values of tile i, first half of tile
-  // i+2, second half of tile i+2, column values of tile i+1, first half of tile i+3, ...; at
-  // the top of iteration i everything up to the column values of tile i (so also all of
-  // tile i+1) must have landed; only the first half of tile i+2 may still be in flight.
+  // Loads of a wave, in issue order: phase B of iteration i queues the column values and
+  // the first half of tile i+4, phase A of iteration i+1 its second half.  At the top of
+  // iteration i, the newest loads are those of B(i-1), A(i-1) and B(i-2) (tiles i+3 and
+  // i+2): everything older, so all of tile i+1, must have landed.
   for (int64_t i = 0; i < ntiles; ++i) {
     const int bi = (int)(i % kPBuf), bn = (int)((i + 1) % kPBuf);
     const bool more = i + 1 < ntiles;
-    // ---- phase A: GEMM1 of tile i+1 around the dlogits of tile i
-    vm_wait<NB - NB / 2>();
+    // GEMM1 of tile i+1 is split over both phases, so that each phase has MFMA work that does
+    // not wait for its barrier: the first half covers the latency of the partial-sum reads
+    // and runs beside the dlogits of tile i, the second half covers the dlogits reads of
+    // GEMM3.  (In the last iteration it works on a stale buffer and its result is unused.)
+    // ---- phase A
+    vm_wait<NQ + NB / 2 + 1>();  // tile i+1 has landed (see above)
     partial_reads();
-    take_col(i);
-    if (i > 0) refill_rest();  // second half of tile i+2 (the buffer of tile i-1)
-    if (more) {
-      gemm1_reads(bn);
-      gemm1_part(C0{}, CH{});
-    }
+    take_col(i, bi);
+    gemm1_reads(bn, C0{}, CH{});
+    gemm1_part(C0{}, CH{});
     dlogits();
-    if (more) gemm1_part(CH{}, CN{});
+    gemm1_reads(bn, CH{}, CN{});  // in flight across the barrier
+    if (i > 0) refill_rest();     // second half of tile i+3 (the buffer of tile i-1)
     __syncthreads();
     // ---- phase B: GEMM3 of tile i (refilling its buffer with tile i+3 plane by plane; past
     // the end the last tile is repeated, never read), partial z of tile i+1
-    if (more) load_col(i + 1);
-    gemm3(bi, more, i + 3 < ntiles ? i + 3 : ntiles - 1);
+    gemm1_part(CH{}, CN{});
+    gemm3(bi, more, i + kPBuf < ntiles ? i + kPBuf : ntiles - 1);
     if (more) put_partials();
     __syncthreads();
   }
@@ -1212,6 +1219,7 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
   a.y = fa.targets;
   a.lse = w.lse;
   a.tok = w.tok;
+  a.biasf = fa.bias != nullptr ? w.biasf : nullptr;
   a.H = fa.H;
   a.BT = fa.BT;
   a.V = fa.V;

@@ -19,9 +19,15 @@ namespace lce {
 // ------------------------------------------------------------------ targets
 constexpr int kTgtThreads = 1024;
 
+// Also copies the bias to fp32 (the backward stages it per tile, 4 bytes per entry).
+template <typename T>
 __global__ void __launch_bounds__(kTgtThreads) targets_kernel(const int64_t* __restrict__ y, int64_t BT,
                                                                int64_t V, int64_t ignore_index,
-                                                               int64_t* n_valid, int32_t* n_bad) {
+                                                               int64_t* n_valid, int32_t* n_bad,
+                                                               const T* __restrict__ bias,
+                                                               float* __restrict__ biasf) {
+  if (bias != nullptr)
+    for (int64_t i = threadIdx.x; i < V; i += kTgtThreads) biasf[i] = Elem<T>::to_f(bias[i]);
   __shared__ long long s_v[kTgtThreads / kWave], s_b[kTgtThreads / kWave];
   long long nv = 0, nb = 0;
   for (int64_t i = threadIdx.x; i < BT; i += kTgtThreads) {
@@ -44,8 +50,12 @@ __global__ void __launch_bounds__(kTgtThreads) targets_kernel(const int64_t* __r
 }
 
 hipError_t launch_targets(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  hipLaunchKernelGGL(targets_kernel, dim3(1), dim3(kTgtThreads), 0, st, a.targets, a.BT, a.V,
-                     a.ignore_index, w.n_valid, w.n_bad);
+  if (a.bf16)
+    hipLaunchKernelGGL(targets_kernel<bf16_t>, dim3(1), dim3(kTgtThreads), 0, st, a.targets, a.BT, a.V,
+                       a.ignore_index, w.n_valid, w.n_bad, static_cast<const bf16_t*>(a.bias), w.biasf);
+  else
+    hipLaunchKernelGGL(targets_kernel<float>, dim3(1), dim3(kTgtThreads), 0, st, a.targets, a.BT, a.V,
+                       a.ignore_index, w.n_valid, w.n_bad, static_cast<const float*>(a.bias), w.biasf);
   return hipGetLastError();
 }
 

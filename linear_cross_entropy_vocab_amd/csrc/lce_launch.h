@@ -24,6 +24,7 @@ struct FusedWs {
   float* zy;          // [BT] target logits
   double* blk;        // [2][nblk] per-block sums of ce and LSE^2 terms
   float2* tok;        // [BT] (LSE, bits of int: target + 1, or 0 for rows that contribute nothing)
+  float* biasf;       // [V] the bias in fp32 (written only when there is a bias)
   int64_t nt;         // number of vocab tiles
   int64_t nblk;       // number of merge blocks
 };
