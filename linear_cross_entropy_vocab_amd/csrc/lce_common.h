@@ -126,6 +126,48 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
 }
 
+// Loads into LDS issued from inline assembly.  The compiler models a buffer-to-LDS load as a
+// store to LDS of unknown extent and would then wait for every one still in flight before
+// any later LDS read, which would undo the prefetch; here the kernel itself tracks which
+// loads must have landed (vm_wait) before it reads a buffer.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Buffer descriptor words (base, size in bytes; same format as make_rsrc), wave-uniform.
+__device__ __forceinline__ u32x4_t make_rsrc_words(const void* base, int64_t bytes) {
+  uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r.x = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xffffu;
+  r.z = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
+  r.w = 0x00020000u;
+  return r;
+}
+// 16 bytes per lane from rsrc + voff to LDS address lds + 16 * lane.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rsrc)
+               : "memory", "m0");
+}
+// Same, ordered after the LDS read that produced `dep` has completed (the compiler waits for
+// the registers an asm statement reads): used to refill a buffer region right after its
+// last read.
+// 4 bytes per lane from rsrc + voff to LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma4(const u32x4_t& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_after(const u32x4_t& rsrc, uint32_t lds, uint32_t voff, const bf16x8_t& dep) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(rsrc), "v"(dep)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64)); }
 __device__ __forceinline__ void load8(Frag<bf16_t>& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {

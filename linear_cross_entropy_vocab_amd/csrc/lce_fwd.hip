@@ -228,8 +228,6 @@ constexpr int kFwdTileT2 = 256;
 // 16 consecutive rows.
 __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
-
 __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16_t* __restrict__ W,
                                                                     const bf16_t* __restrict__ h,
                                                                     const bf16_t* __restrict__ bias,
@@ -264,8 +262,13 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   }
 
   const int64_t row_bytes = H * 2;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(W + v0 * H, (V - v0) * row_bytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(h + t0 * H, (BT - t0) * row_bytes);
+  const u32x4_t ra = make_rsrc_words(W + v0 * H, (V - v0) * row_bytes);
+  const u32x4_t rb = make_rsrc_words(h + t0 * H, (BT - t0) * row_bytes);
+  auto lds_addr = [](const char* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+  };
+  const uint32_t la = lds_addr(sA[0]), lb = lds_addr(sB[0]);
   // DMA lane mapping: instruction j of this wave covers rows 8 (4 w + j) .. + 7 of the
   // stage; lane l lands on row + l / 8, physical 16-byte chunk l % 8, which holds logical
   // chunk (l % 8) ^ fsw(row).  The swizzle makes the 16-byte fragment reads of 8 and of 16
@@ -277,10 +280,8 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       const int row = 8 * (4 * w + j) + drow;
       const int64_t k = ks * 64 + (dch ^ fsw(row)) * 8;  // first element of this lane's chunk
       const uint32_t off = k < H ? (uint32_t)(row * row_bytes + k * 2) : 0xfffffff0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(sA[buf] + 1024 * (4 * w + j)),
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(sB[buf] + 1024 * (4 * w + j)),
-                                               16, off, 0, 0, 0);
+      dma16(ra, la + (uint32_t)(buf * TILE_A + 1024 * (4 * w + j)), off);
+      dma16(rb, lb + (uint32_t)(buf * TILE_B + 1024 * (4 * w + j)), off);
     }
   };
 
@@ -296,7 +297,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   dma(0, 0);
   for (int64_t ks = 0; ks < nk; ++ks) {
     const int buf = (int)(ks & 1);
-    wait_vm0();
+    vm_wait<0>();     // this wave's part of stage ks has landed
     __syncthreads();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
     if (ks + 1 < nk) dma(ks + 1, buf ^ 1);
     // fragment rows: (wv*128 + vb*32 + lane%32) and (wt*64 + tb*32 + lane%32); the swizzle
