@@ -243,27 +243,35 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
 
   const int64_t nwg = nt_v * nt_t;
-  const int64_t id = xcd_remap(blockIdx.x, nwg);
-  constexpr int GT = 4;  // token tiles per raster group
-  const int64_t group = id / (GT * nt_v);
-  const int64_t first_t = group * GT;
-  const int64_t gsize = (nt_t - first_t) < GT ? (nt_t - first_t) : GT;
-  const int64_t in_g = id % (GT * nt_v);
-  const int64_t ttile = first_t + in_g % gsize;
-  const int64_t vtile = in_g / gsize;
-  const int64_t v0 = vtile * kFwdTileV;
-  const int64_t t0 = ttile * kFwdTileT2;
-
   const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
   const int wv = w >> 2, wt = w & 3;
-  if (tid < kFwdTileV) {
-    const int64_t v = v0 + tid;
-    s_bias[tid] = (bias != nullptr && v < V) ? bf2f(bias[v]) : 0.f;
-  }
-
   const int64_t row_bytes = H * 2;
-  const u32x4_t ra = make_rsrc_words(W + v0 * H, (V - v0) * row_bytes);
-  const u32x4_t rb = make_rsrc_words(h + t0 * H, (BT - t0) * row_bytes);
+  const int64_t nk = (H + 63) / 64;
+
+  // Tiles of this workgroup: blockIdx.x, + gridDim.x, ...  Consecutive logical indices go to
+  // one XCD's L2 in contiguous ranges (xcd_remap), then in groups of GT token tiles over
+  // the vocabulary tiles, so that concurrently running workgroups share operand tiles.
+  struct Tile {
+    int64_t v0, t0, vtile;
+  };
+  // (32-bit scalar arithmetic: the tile counts fit, and the results stay in SGPRs)
+  auto tile_of = [&](int64_t blk64) {
+    const uint32_t n = (uint32_t)nwg, ntv = (uint32_t)nt_v, ntt = (uint32_t)nt_t;
+    const uint32_t blk = (uint32_t)blk64;
+    const uint32_t x = blk % 8, q = blk / 8, Q = n / 8, r = n % 8;
+    const uint32_t id = (x < r) ? x * (Q + 1) + q : r * (Q + 1) + (x - r) * Q + q;
+    constexpr uint32_t GT = 4;  // token tiles per raster group
+    const uint32_t group = id / (GT * ntv);
+    const uint32_t first_t = group * GT;
+    const uint32_t gsize = (ntt - first_t) < GT ? (ntt - first_t) : GT;
+    const uint32_t in_g = id % (GT * ntv);
+    Tile t;
+    t.vtile = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(in_g / gsize));
+    t.v0 = t.vtile * kFwdTileV;
+    t.t0 = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(first_t + in_g % gsize)) * kFwdTileT2;
+    return t;
+  };
+
   auto lds_addr = [](const char* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
@@ -274,7 +282,9 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   // chunk (l % 8) ^ fsw(row).  The swizzle makes the 16-byte fragment reads of 8 and of 16
   // consecutive rows hit distinct banks.
   const int drow = lane >> 3, dch = lane & 7;
-  auto dma = [&](int64_t ks, int buf) {
+  auto dma = [&](const Tile& tl, int64_t ks, int buf) {
+    const u32x4_t ra = make_rsrc_words(W + tl.v0 * H, (V - tl.v0) * row_bytes);
+    const u32x4_t rb = make_rsrc_words(h + tl.t0 * H, (BT - tl.t0) * row_bytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = 8 * (4 * w + j) + drow;
@@ -285,87 +295,125 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     }
   };
 
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int64_t nk = (H + 63) / 64;
-  dma(0, 0);
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int buf = (int)(ks & 1);
-    vm_wait<0>();     // this wave's part of stage ks has landed
-    __syncthreads();  // stage ks is in LDS for every wave; stage ks-1 is no longer read
-    if (ks + 1 < nk) dma(ks + 1, buf ^ 1);
-    // fragment rows: (wv*128 + vb*32 + lane%32) and (wt*64 + tb*32 + lane%32); the swizzle
-    // depends only on row % 16 = lane % 16, so one XOR value serves every block
-    const int fs = fsw(lane & 31);
-    const char* a_base = sA[buf] + (wv * 128 + (lane & 31)) * ROWB;
-    const char* b_base = sB[buf] + (wt * 64 + (lane & 31)) * ROWB;
-    Frag<bf16_t> fa[2][4], fb[2][2];
-    auto rd = [&](int kk, int slot) {
-      const int off = ((2 * kk + (lane >> 5)) ^ fs) << 4;
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb) lds_frag_ptr(fa[slot][vb], a_base + vb * 32 * ROWB + off);
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) lds_frag_ptr(fb[slot][tb], b_base + tb * 32 * ROWB + off);
-    };
-    rd(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fa[kk & 1][vb], fb[kk & 1][tb], acc[vb][tb]);
+  // fragment rows: (wv*128 + vb*32 + lane%32) and (wt*64 + tb*32 + lane%32); the swizzle
+  // depends only on row % 16 = lane % 16, so one XOR value serves every block
+  const int fs = fsw(lane & 31);
+  int64_t blk = blockIdx.x;
+  if (blk >= nwg) return;
+  Tile tl = tile_of(blk);
+  int buf = 0;
+  dma(tl, 0, 0);
+  for (;;) {
+    if (tid < kFwdTileV) {  // (the previous tile's epilogue finished reading s_bias)
+      const int64_t v = tl.v0 + tid;
+      s_bias[tid] = (bias != nullptr && v < V) ? bf2f(bias[v]) : 0.f;
     }
-  }
+    const int64_t nblk = blk + gridDim.x;
+    const bool has_next = nblk < nwg;
+    const Tile tn = has_next ? tile_of(nblk) : tl;
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
-  // two lane halves, then the two vocabulary halves of the tile; rows past V are skipped.
+    for (int64_t ks = 0; ks < nk; ++ks) {
+      vm_wait<0>();     // this wave's part of stage ks has landed
+      __syncthreads();  // stage ks is in LDS for every wave; the other buffer is no longer read
+      // the next stage, which after the last one is the first stage of the next tile (so its
+      // load overlaps this tile's epilogue)
+      if (ks + 1 < nk) dma(tl, ks + 1, buf ^ 1);
+      else if (has_next) dma(tn, 0, buf ^ 1);
+      const char* a_base = sA[buf] + (wv * 128 + (lane & 31)) * ROWB;
+      const char* b_base = sB[buf] + (wt * 64 + (lane & 31)) * ROWB;
+      Frag<bf16_t> fa[2][4], fb[2][2];
+      auto rd = [&](int kk, int slot) {
+        const int off = ((2 * kk + (lane >> 5)) ^ fs) << 4;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    float m = -INFINITY;
+        for (int vb = 0; vb < 4; ++vb) lds_frag_ptr(fa[slot][vb], a_base + vb * 32 * ROWB + off);
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+        for (int tb = 0; tb < 2; ++tb) lds_frag_ptr(fb[slot][tb], b_base + tb * 32 * ROWB + off);
+      };
+      rd(0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vr = wv * 128 + vb * 32 + acc_row(lane, r);
-        if (v0 + vr < V) m = fmaxf(m, acc[vb][tb][r] + s_bias[vr]);
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fa[kk & 1][vb], fb[kk & 1][tb], acc[vb][tb]);
       }
-    float sm = 0.f;
-    if (m != -INFINITY) {
+      buf ^= 1;
+    }
+
+    // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
+    // two lane halves, then the two vocabulary halves of the tile; rows past V (only in the
+    // last vocabulary tile) are skipped.
+    const int vlim = (int)((V - tl.v0) < kFwdTileV ? (V - tl.v0) : kFwdTileV);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // keeps the row indices below from being hoisted out of the loop
+    const int vrow = wv * 128 + 4 * (ln >> 5);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float m = -INFINITY;
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int vr = wv * 128 + vb * 32 + acc_row(lane, r);
-          if (v0 + vr < V) sm += __expf(acc[vb][tb][r] + s_bias[vr] - m);
+          const int vr = vrow + vb * 32 + 8 * (r >> 2) + (r & 3);
+          if (vr < vlim) m = fmaxf(m, acc[vb][tb][r] + s_bias[vr]);
         }
+      float sm = 0.f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int vr = vrow + vb * 32 + 8 * (r >> 2) + (r & 3);
+            if (vr < vlim) sm += __expf(acc[vb][tb][r] + s_bias[vr] - m);
+          }
+      }
+      ms_merge(m, sm, __shfl_xor(m, 32, kWave), __shfl_xor(sm, 32, kWave));
+      if (lane < 32) {
+        red_m[wv][wt * 64 + tb * 32 + lane] = m;
+        red_s[wv][wt * 64 + tb * 32 + lane] = sm;
+      }
     }
-    ms_merge(m, sm, __shfl_xor(m, 32, kWave), __shfl_xor(sm, 32, kWave));
-    if (lane < 32) {
-      red_m[wv][wt * 64 + tb * 32 + lane] = m;
-      red_s[wv][wt * 64 + tb * 32 + lane] = sm;
+    __syncthreads();
+    if (tid < kFwdTileT2) {
+      float m = red_m[0][tid], sm = red_s[0][tid];
+      ms_merge(m, sm, red_m[1][tid], red_s[1][tid]);
+      const int64_t t = tl.t0 + tid;
+      if (t < BT) lse_part[tl.vtile * BT + t] = m + __logf(sm);
     }
+    if (!has_next) break;
+    blk = nblk;
+    tl = tn;
   }
-  __syncthreads();
-  if (tid < kFwdTileT2) {
-    float m = red_m[0][tid], sm = red_s[0][tid];
-    ms_merge(m, sm, red_m[1][tid], red_s[1][tid]);
-    const int64_t t = t0 + tid;
-    if (t < BT) lse_part[vtile * BT + t] = m + __logf(sm);
+  vm_wait<0>();
+}
+
+// Workgroups of the persistent forward: one per compute unit of the current device.
+static int64_t fwd_grid(int64_t nwg) {
+  static int cu[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cu[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cu[dev] = n;
   }
+  const int64_t g = cu[dev];
+  return nwg < g ? nwg : g;
 }
 
 hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.BT == 0) return hipSuccess;
   if (a.bf16) {
     const int64_t nt_t2 = (a.BT + kFwdTileT2 - 1) / kFwdTileT2;
-    hipLaunchKernelGGL(fwd_lse_dma_kernel, dim3((unsigned)(w.nt * nt_t2)), dim3(kFwdThreads2), 0, st,
+    hipLaunchKernelGGL(fwd_lse_dma_kernel, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0, st,
                        (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
                        a.V, w.nt, nt_t2, w.lse_part);
     return hipGetLastError();
