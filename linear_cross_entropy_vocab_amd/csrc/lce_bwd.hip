@@ -425,330 +425,20 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16, whole H in one workgroup (H <= 1024): streamed tiles arrive by buffer->LDS DMA,
-// double buffered, so no registers stage them and the next tile's transfer overlaps the
-// current tile's work.  GEMM1 reads its X fragments from LDS; each wave keeps the partial
-// z of its own 16 reduce rows in registers and only sends the other 48 rows through LDS.
-// LDS: X tiles 2 x 4 x 32 x (64 NB) bytes (128 KiB at NB = 8), partial z 24 KiB,
-// dlogits 4 KiB, per-row tables 768 B.
-// ---------------------------------------------------------------------------
-constexpr int kZBlk = 32 * 16 * 4;  // one partial-z block: 32 columns x 16 rows, fp32
-
-// X-tile chunk swizzle: bijective on any 16 consecutive rows (16-byte reads of GEMM1 hit
-// distinct banks) and, for four consecutive rows starting at a multiple of 4, spreads the
-// two chunks each of them reads over 8 distinct chunks (transposed reads of GEMM3).
-template <int XNCH>
-__device__ __forceinline__ int xsw(int row) {
-  return (((row & 3) << 1) | ((row >> 2) & 1) | (row & 8)) & (XNCH - 1);
-}
-__device__ __forceinline__ int gsw(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int zslot(int writer, int reader) { return writer * 3 + (reader < writer ? reader : reader - 1); }
-
-// Operand from a [K rows][32-column blocks] bf16 LDS tile read with transposed reads; `sw`
-// maps a row to the XOR applied to its 16-byte chunk index.
-template <int ROWB, typename SW>
-__device__ __forceinline__ void tr_frag(Frag<bf16_t>& f, const char* t, int kbase, int col0, int lane, SW sw) {
-  const int g = lane >> 4, i = lane & 15;
-  const int col = col0 + (g & 1) * 16 + 4 * (i & 3);
-  const int r0 = kbase + (g >> 1) * 8 + (i >> 2), r1 = r0 + 4;
-  const int ch = col >> 3, within = (col & 7) * 2;
-  const i16x4_t a = lds_read_tr16(reinterpret_cast<const bf16_t*>(t + r0 * ROWB + ((ch ^ sw(r0)) << 4) + within));
-  const i16x4_t b = lds_read_tr16(reinterpret_cast<const bf16_t*>(t + r1 * ROWB + ((ch ^ sw(r1)) << 4) + within));
-  f.v = bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <bool DW, int NB>
-__global__ void __launch_bounds__(kBwdThreads, 1) bwd_dma_kernel(BwdArgs<bf16_t> p) {
-  typedef bf16_t T;
-  constexpr int NCOL = 32 * NB;      // output columns of a wave = its GEMM1 K quarter
-  constexpr int XROW = NCOL * 2;     // bytes per X-tile row
-  constexpr int XNCH = XROW / 16;
-  constexpr int XWAVE = kBX * XROW;  // bytes of a wave's X tile
-  constexpr int NDMA = XWAVE / 1024; // DMA instructions per wave per tile
-  constexpr int KS1 = 2 * NB;
-  constexpr int GROW = kBS * 2;      // bytes per dlogits-tile row
-  static_assert(XNCH >= 4 && (XNCH & (XNCH - 1)) == 0, "power-of-two chunks per row");
-  __shared__ __attribute__((aligned(1024))) char xtile[2][4][XWAVE];
-  __shared__ __attribute__((aligned(16))) char zpart[12 * kZBlk];
-  __shared__ __attribute__((aligned(16))) char gtile[kBX * GROW];
-  __shared__ __attribute__((aligned(16))) float s_a[kBS];
-  __shared__ __attribute__((aligned(16))) float s_b[kBS];
-  __shared__ __attribute__((aligned(16))) int32_t s_y[kBS];
-
-  const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
-  const int h = lane >> 5, c = lane & 31;
-  const int64_t s0 = (int64_t)blockIdx.x * kBS;
-  const int64_t H = p.H;
-  const int64_t row_bytes = H * 2;
-  const int kw0 = w * NCOL;
-  const long long nvalid = *p.n_valid;
-  const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
-
-  if (tid < kBS) {
-    const int64_t r = s0 + tid;
-    if (!DW) {
-      float L = 0.f;
-      int32_t yv = -1;
-      if (r < p.BT) {
-        const int64_t yt = p.y[r];
-        if (yt != p.ignore_index && yt >= 0 && yt < p.V) {
-          yv = (int32_t)yt;
-          L = p.lse[r];
-        }
-      }
-      s_a[tid] = L;
-      s_b[tid] = 1.f + 2.f * p.mu * L;
-      s_y[tid] = yv;
-    } else {
-      s_a[tid] = (p.bias != nullptr && r < p.V) ? bf2f(p.bias[r]) : 0.f;
-      s_b[tid] = 0.f;
-      s_y[tid] = r < p.V ? 1 : 0;
-    }
-  }
-
-  // Stationary fragments: S rows s0 + sb*32 + lane%32, K quarter of this wave.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.S + s0 * H, (p.nS - s0) * row_bytes);
-  const uint32_t s_off = (uint32_t)(c * row_bytes + (kw0 + 8 * h) * 2);
-  Frag<T> sf[KS1][2];
-#pragma unroll
-  for (int ks = 0; ks < KS1; ++ks)
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      load8(sf[ks][sb], rs, s_off + (uint32_t)(sb * 32 * row_bytes + ks * 32));
-      zero_unless(sf[ks][sb], kw0 + ks * 16 + 8 * h < H);
-    }
-
-  f32x16_t acc[2][NB];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[sb][cb][r] = 0.f;
-  float gb[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) gb[e] = 0.f;
-
-  // DMA of this wave's quarter of a tile: instruction j fills bytes [1024 j, 1024 j + 1024)
-  // of the wave's region; lane l lands at 16 l, i.e. row (1024 j + 16 l) / XROW and
-  // physical chunk ((1024 j + 16 l) % XROW) / 16, which holds logical chunk
-  // (physical ^ xsw(row)).  Rows past the end of X read as zeros.
-  auto dma = [&](int64_t x0n, int buf, int ln) {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X + x0n * H, (p.nX - x0n) * row_bytes);
-    char* dst = xtile[buf][w];
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const int b = 1024 * j + 16 * ln;
-      const int row = b / XROW, pch = (b % XROW) / 16;
-      const int lch = pch ^ xsw<XNCH>(row);
-      const uint32_t off = (uint32_t)(row * row_bytes + (kw0 + lch * 8) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
-                                               off, 0, 0, 0);
-    }
-  };
-  float pc_a = 0.f;
-  int32_t pc_y = -1;
-  auto load_col = [&](int64_t x0n) {
-    const int64_t xc = x0n + c;
-    if (!DW) {
-      pc_a = p.bias != nullptr ? bf2f(p.bias[xc < p.V ? xc : p.V - 1]) : 0.f;
-      pc_y = 0;
-    } else {
-      const int64_t t = xc < p.BT ? xc : p.BT - 1;
-      const int64_t yt = p.y[t];
-      pc_a = p.lse[t];
-      pc_y = (xc < p.BT && yt != p.ignore_index && yt >= 0 && yt < p.V) ? (int32_t)yt : -1;
-    }
-  };
-
-  const int64_t ntiles = (p.nX + kBX - 1) / kBX;
-  if (ntiles > 0) {
-    load_col(0);
-    dma(0, 0, lane);
-  }
-  for (int64_t xtl = 0; xtl < ntiles; ++xtl) {
-    const int64_t x0 = xtl * kBX;
-    const int buf = (int)(xtl & 1);
-    const float col_a = pc_a;
-    const int32_t col_y = pc_y;
-    // An opaque copy of the lane index: LDS/DMA addresses derived from it are recomputed
-    // where they are used instead of being hoisted out of the loop into live registers.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int lc = ln & 31, lh = ln >> 5;
-    if (xtl + 1 < ntiles) {
-      load_col(x0 + kBX);
-      dma(x0 + kBX, buf ^ 1, ln);
-      wait_vmcnt<NDMA>();  // everything before the next tile's DMA has landed
-    } else {
-      wait_vmcnt<0>();
-    }
-    const char* xt = xtile[buf][w];
-    // ---------------- GEMM1: partial z[64 x 32] over this wave's K quarter
-    // (accumulated in VGPRs: the AGPR file holds acc)
-    f32x16_t zp[2];
-#pragma unroll
-    for (int ks = 0; ks < KS1; ++ks) {
-      Frag<T> xf;
-      lds_frag(xf, xt + lc * XROW + (((2 * ks + lh) ^ xsw<XNCH>(lc)) << 4));
-      if (ks == 0) {
-        mfma_32x32x16_v0(sf[ks][0], xf, zp[0]);
-        mfma_32x32x16_v0(sf[ks][1], xf, zp[1]);
-      } else {
-        mfma_32x32x16_v(sf[ks][0], xf, zp[0]);
-        mfma_32x32x16_v(sf[ks][1], xf, zp[1]);
-      }
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the reads in flight
-    }
-    mfma_v_drain();
-    // ---------------- partial z: the other waves' rows to LDS, own rows kept
-    // Rows 16 w' .. 16 w' + 15 live in zp[w' / 2], registers 8 (w' % 2) .. + 7 (local rows
-    // 8 j + 4 h + q for register 8 (w' % 2) + 4 j + q).
-    float own[8];
-#pragma unroll
-    for (int wp = 0; wp < 4; ++wp) {
-      const f32x16_t& zb = zp[wp >> 1];
-      const int rb = 8 * (wp & 1);
-      if (wp == w) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) own[q] = zb[rb + q];
-      } else {
-        char* blk = zpart + zslot(w, wp) * kZBlk + lc * 64;
-        const int sw = (lc >> 2) & 3;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          *reinterpret_cast<float4*>(blk + (((2 * j + lh) ^ sw) << 4)) =
-              make_float4(zb[rb + 4 * j], zb[rb + 4 * j + 1], zb[rb + 4 * j + 2], zb[rb + 4 * j + 3]);
-      }
-    }
-    // own holds local rows 4h + q (q < 4) and 8 + 4h + q; the reduce step wants 8h .. 8h + 7:
-    // swap one half with the partner lane (l ^ 32).
-    float z[8];
-    {
-      float snd[4], rcv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) snd[q] = h ? own[q] : own[4 + q];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rcv[q] = __shfl_xor(snd[q], 32, kWave);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        z[q] = h ? rcv[q] : own[q];
-        z[4 + q] = h ? own[4 + q] : rcv[q];
-      }
-    }
-    __syncthreads();
-    // ---------------- z and dlogits for column c, rows 16 w + 8 h .. + 7
-    {
-      const int sw = (lc >> 2) & 3;
-#pragma unroll
-      for (int wp = 0; wp < 4; ++wp) {
-        if (wp == w) continue;
-        const char* blk = zpart + zslot(wp, w) * kZBlk + lc * 64;
-        const float4 a = *reinterpret_cast<const float4*>(blk + (((2 * lh) ^ sw) << 4));
-        const float4 b = *reinterpret_cast<const float4*>(blk + (((2 * lh + 1) ^ sw) << 4));
-        z[0] += a.x; z[1] += a.y; z[2] += a.z; z[3] += a.w;
-        z[4] += b.x; z[5] += b.y; z[6] += b.z; z[7] += b.w;
-      }
-    }
-    const int r0 = 16 * w + 8 * h;
-    const int64_t xc = x0 + c;
-    float g[8];
-    {
-      const float4 a0 = *reinterpret_cast<const float4*>(&s_a[r0]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&s_a[r0 + 4]);
-      const int4 y0 = *reinterpret_cast<const int4*>(&s_y[r0]);
-      const int4 y1 = *reinterpret_cast<const int4*>(&s_y[r0 + 4]);
-      const float va[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const int32_t vy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-      if (!DW) {
-        const float4 b0 = *reinterpret_cast<const float4*>(&s_b[r0]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&s_b[r0 + 4]);
-        const float vf[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const bool colok = xc < p.V;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ex = __expf(z[e] + col_a - va[e]) * vf[e] - ((int64_t)vy[e] == xc ? 1.f : 0.f);
-          g[e] = (vy[e] >= 0 && colok) ? ex : 0.f;
-        }
-      } else {
-        const float ft = 1.f + 2.f * p.mu * col_a;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t srow = s0 + r0 + e;
-          const float ex = __expf(z[e] + va[e] - col_a) * ft - ((int64_t)col_y == srow ? 1.f : 0.f);
-          g[e] = (vy[e] != 0 && col_y >= 0) ? ex : 0.f;
-          gb[e] += g[e];
-        }
-      }
-    }
-    // dlogits tile [x = c][s = r0 .. r0 + 7]: one 16-byte chunk (index r0 / 8 = 2 w + h)
-    *reinterpret_cast<uint4*>(gtile + lc * GROW + (((2 * w + lh) ^ gsw(lc)) << 4)) =
-        make_uint4(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]), pack_bf2(g[4], g[5]), pack_bf2(g[6], g[7]));
-    __syncthreads();
-    // ---------------- GEMM3: acc += g . X[:, wave columns]
-#pragma unroll
-    for (int kk = 0; kk < kBX / 16; ++kk) {
-      Frag<T> ga[2];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) tr_frag<GROW>(ga[sb], gtile, kk * 16, sb * 32, ln, gsw);
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        Frag<T> xb;
-        tr_frag<XROW>(xb, xt, kk * 16, cb * 32, ln, xsw<XNCH>);
-        mfma_32x32x16(ga[0], xb, acc[0][cb]);
-        mfma_32x32x16(ga[1], xb, acc[1][cb]);
-        if ((cb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-
-  // ---------------- write c * acc
-  const int64_t hw0 = kw0;
-  if (p.out != nullptr) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int64_t col = hw0 + cb * 32 + c;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-          if (row < p.nS && col < H) p.out[row * H + col] = f2bf(cscale * acc[sb][cb][r]);
-        }
-      }
-  }
-  if (DW && p.grad_b != nullptr) {
-    const int r0 = 16 * w + 8 * h;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = gb[e];
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, kWave);
-      const int64_t srow = s0 + r0 + e;
-      if (c == 0 && srow < p.V) p.grad_b[srow] = f2bf(cscale * v);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // bf16, H <= 1024: software-pipelined variant.
 //
 // Streamed tiles are 16 rows.  Each wave owns NCOL = 32*NB columns of H (its GEMM1 K range
 // and its GEMM3 output columns), so it only ever touches its own share of a streamed tile:
-// it loads that share into LDS itself (buffer-to-LDS DMA, three buffers per wave) and no
+// it loads that share into LDS itself (buffer-to-LDS loads, four buffers per wave) and no
 // barrier guards the tile buffers.  One loop iteration i overlaps two tiles:
-//   phase A: GEMM1 for tile i+1 (16x16x32 MFMA, partial z over the wave's K range)
-//            + the dlogits of tile i from the partial z sums of every wave;   barrier
-//   phase B: GEMM3 for tile i (32x32x16 MFMA, acc += g . X)
-//            + the partial z of tile i+1 written out for the other waves;       barrier
-// and then queues the DMA of tile i+3 into the buffer tile i used.
+//   phase A: first half of GEMM1 for tile i+1 (16x16x32 MFMA, partial z over the wave's K
+//            range) beside the dlogits of tile i from the partial z sums of every wave;
+//            barrier
+//   phase B: second half of GEMM1 for tile i+1, GEMM3 for tile i (32x32x16 MFMA,
+//            acc += g . X), the partial z of tile i+1 written out for the other waves;
+//            barrier
+// and tile i+4 is requested into the buffer tile i used (half in phase B, half in the next
+// phase A), together with the tile's column values (per token (LSE, target), or the bias).
 //
 // Shared-memory layouts (all reads conflict-free; every address is a per-lane constant plus
 // an immediate, so the loop does almost no address arithmetic):
@@ -1061,7 +751,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     gemm1_reads(bn, CH{}, CN{});  // in flight across the barrier
     if (i > 0) refill_rest();     // second half of tile i+3 (the buffer of tile i-1)
     __syncthreads();
-    // ---- phase B: GEMM3 of tile i (refilling its buffer with tile i+3 plane by plane; past
+    // ---- phase B: GEMM3 of tile i (refilling its buffer with tile i+4 plane by plane; past
     // the end the last tile is repeated, never read), partial z of tile i+1
     gemm1_part(CH{}, CN{});
     gemm3(bi, more, i + kPBuf < ntiles ? i + kPBuf : ntiles - 1);
@@ -1103,18 +793,6 @@ static hipError_t launch_bwd_pipe(int nb, const BwdArgs<bf16_t>& a, dim3 grid, h
     case 2: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
     case 4: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
     case 8: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <bool DW>
-static hipError_t launch_bwd_dma(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
-  switch (nb) {
-    case 1: hipLaunchKernelGGL((bwd_dma_kernel<DW, 1>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((bwd_dma_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((bwd_dma_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((bwd_dma_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
