@@ -20,6 +20,7 @@ from .lce import (  # noqa: F401
     IGNORE_INDEX,
     TargetRangeError,
     lce_oracle,
+    lce_oracle_filtered,
     ce_oracle,
     lse_rows,
     lse_all,

@@ -151,6 +151,75 @@ def lce_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDE
     return out
 
 
+def _block_keep(g: np.ndarray, rows: int, cols: int, eps: float):
+    """Mask of g [R, C] that is False inside every (rows x cols) block, aligned at 0, whose
+    entries all have |g| < eps ([P2] "Gradient Filtering": a block is skipped only if
+    every value in it is below the threshold), and the number of such blocks."""
+    R, C = g.shape
+    keep = np.ones_like(g, dtype=bool)
+    skipped = 0
+    for r0 in range(0, R, rows):
+        for c0 in range(0, C, cols):
+            if np.all(np.abs(g[r0:r0 + rows, c0:c0 + cols]) < eps):
+                keep[r0:r0 + rows, c0:c0 + cols] = False
+                skipped += 1
+    return keep, skipped
+
+
+def lce_oracle_filtered(hidden, weight, bias, targets, *, filter_eps: float,
+                        ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
+                        reduction: str = "mean", stat_rows: int = 64,
+                        stream_rows: int = 16) -> dict:
+    """The gradients with CCE-style gradient filtering ([P2] "Gradient Filtering").
+
+    Each gradient GEMM sees the dlogits in tiles; a tile whose entries are all below
+    filter_eps in magnitude contributes nothing (its contribution is zeroed, not
+    deferred).  The tiles are those of the GEMM that produces the gradient:
+      grad_input: stat_rows tokens x stream_rows vocabulary entries (aligned at 0);
+      grad_W and grad_b: stat_rows vocabulary entries x stream_rows tokens.
+    Reading: the threshold applies to the dlogits of the summed loss, valid * (softmax *
+    (1 + 2 mu LSE) - onehot), i.e. before the 1/n_valid of the mean, so that the test
+    depends on the size of an entry relative to the others in its row and not on the
+    batch size.  The loss is not affected.  Returns the lce_oracle dict with the filtered
+    gradients and the tile counts skipped_input / tiles_input, skipped_weight /
+    tiles_weight.
+    """
+    h = _f64(hidden)
+    W = _f64(weight)
+    b = _f64(bias)
+    y = np.asarray(targets, dtype=np.int64)
+    BT, H = h.shape
+    V = W.shape[0]
+    out = lce_oracle(hidden, weight, bias, targets, ignore_index=ignore_index, z_loss=z_loss,
+                     reduction=reduction, grads=False)
+    valid = _valid_mask(y, V, ignore_index)
+    c = out["scale"]
+    mu = float(z_loss)
+    lse = out["lse"]
+    gi = np.zeros((BT, H))
+    gw = np.zeros((V, H))
+    gb = np.zeros(V) if b is not None else None
+    a = max(stat_rows, stream_rows)
+    R = max(a, (_rows_per_chunk(V) // a) * a)  # chunks start on tile boundaries of both GEMMs
+    skipped_in = skipped_w = 0
+    for r0 in range(0, BT, R):
+        r1 = min(BT, r0 + R)
+        g = _dlogits(_logits(h[r0:r1], W, b), lse[r0:r1], y[r0:r1], valid[r0:r1], 1.0, mu)
+        k_in, n_in = _block_keep(g, stat_rows, stream_rows, filter_eps)
+        k_wt, n_w = _block_keep(g.T, stat_rows, stream_rows, filter_eps)
+        skipped_in += n_in
+        skipped_w += n_w
+        gi[r0:r1] = c * (np.where(k_in, g, 0.0) @ W)       # grad_input = dlogits . W
+        g_w = np.where(k_wt.T, g, 0.0)
+        gw += c * (g_w.T @ h[r0:r1])                       # grad_W = dlogits^T . hidden
+        if gb is not None:
+            gb += c * g_w.sum(axis=0)                      # grad_b = sum_t dlogits[t, :]
+    out.update(grad_input=gi, grad_weight=gw, grad_bias=gb,
+               skipped_input=skipped_in, tiles_input=-(-BT // stat_rows) * -(-V // stream_rows),
+               skipped_weight=skipped_w, tiles_weight=-(-V // stat_rows) * -(-BT // stream_rows))
+    return out
+
+
 def ce_oracle(logits, targets, *, ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
               rows_per_chunk: Optional[int] = None, dlogit_rows=None) -> dict:
     """Standalone cross-entropy on existing logits ([P3] opening formulas, "Kernel design").

@@ -1,0 +1,127 @@
+"""Pins of the gradient-filtering oracle (``oracle.lce_oracle_filtered``).
+
+It follows "Cut Cross Entropy visualized", "Gradient Filtering": a dlogits block whose
+entries are all below filter_eps contributes nothing to the gradient GEMMs.  Pinned by:
+  * eps = 0 skips nothing and gives exactly the unfiltered oracle;
+  * an eps above every |dlogit| skips every tile and gives zero gradients, loss unchanged;
+  * a vocabulary range pushed to probability ~e^-60 by its bias, aligned to the tiles and
+    holding no target, is skipped exactly where the tile geometry says (counts checked
+    tile by tile), and the gradients move by less than what was dropped;
+  * a pure-Python brute force with its own block loop (2 x 3 tiles, so that skipped and
+    kept blocks mix in both GEMMs) agrees to rounding.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_fused
+
+
+def _case(BT, H, V, seed=0, bias=True, ignore_frac=0.2, w_std=0.5):
+    inp = make_fused(BT, H, V, dtype="f32", seed=seed, w_std=w_std,
+                     bias_std=0.3 if bias else None, ignore_frac=ignore_frac)
+    b = None if inp.bias is None else inp.bias.astype(np.float64)
+    return inp.hidden.astype(np.float64), inp.weight.astype(np.float64), b, inp.targets
+
+
+@pytest.mark.parametrize("mu", [0.0, 1e-2])
+def test_zero_eps_is_unfiltered(mu):
+    h, W, b, y = _case(150, 8, 300, seed=1)
+    ref = oracle.lce_oracle(h, W, b, y, z_loss=mu)
+    f = oracle.lce_oracle_filtered(h, W, b, y, filter_eps=0.0, z_loss=mu)
+    assert f["skipped_input"] == 0 and f["skipped_weight"] == 0
+    assert f["loss"] == ref["loss"]
+    np.testing.assert_allclose(f["grad_input"], ref["grad_input"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(f["grad_weight"], ref["grad_weight"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(f["grad_bias"], ref["grad_bias"], rtol=1e-12, atol=1e-15)
+
+
+def test_huge_eps_skips_everything():
+    h, W, b, y = _case(70, 8, 90, seed=2)
+    ref = oracle.lce_oracle(h, W, b, y)
+    f = oracle.lce_oracle_filtered(h, W, b, y, filter_eps=1e9)
+    assert f["tiles_input"] == 2 * 6 and f["tiles_weight"] == 2 * 5  # ceil(70/64)*ceil(90/16), ...
+    assert f["skipped_input"] == f["tiles_input"] and f["skipped_weight"] == f["tiles_weight"]
+    assert f["loss"] == ref["loss"]
+    assert not f["grad_input"].any() and not f["grad_weight"].any() and not f["grad_bias"].any()
+
+
+def test_suppressed_vocabulary_block_is_skipped_where_the_tiles_say():
+    BT, H, V = 150, 8, 192
+    h, W, b, y = _case(BT, H, V, seed=3, ignore_frac=0.1)
+    b = b.copy()
+    b[64:128] = -60.0                       # p ~ e^-60 there
+    y = np.where((y >= 64) & (y < 128), y - 64, y)  # no target in the suppressed range
+    eps = 1e-12
+    ref = oracle.lce_oracle(h, W, b, y)
+    f = oracle.lce_oracle_filtered(h, W, b, y, filter_eps=eps)
+    n_tok64, n_tok16 = -(-BT // 64), -(-BT // 16)
+    # grad_input tiles are 64 tokens x 16 vocab: vocab tiles 4..7 of every token tile
+    assert f["skipped_input"] == 4 * n_tok64
+    # grad_W tiles are 64 vocab x 16 tokens: vocab tile 1 of every token tile
+    assert f["skipped_weight"] == n_tok16
+    # what was dropped is below eps per entry; the gradients move by at most that much
+    c = ref["scale"]
+    bound_in = c * eps * np.abs(W).sum(axis=0).max() * 1.01
+    assert np.abs(f["grad_input"] - ref["grad_input"]).max() <= bound_in
+    assert np.abs(f["grad_weight"][64:128]).max() == 0.0
+    np.testing.assert_allclose(f["grad_weight"][:64], ref["grad_weight"][:64], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(f["grad_weight"][128:], ref["grad_weight"][128:], rtol=1e-12, atol=1e-15)
+    assert np.abs(f["grad_bias"][64:128]).max() == 0.0
+
+
+def _brute_filtered(h, W, b, y, eps, sr, tr, mu=0.0):
+    """Pure-Python filtered gradients (mean reduction) with its own block loop."""
+    BT, H, V = len(h), len(h[0]), len(W)
+    valid = [yy != -100 for yy in y]
+    n = sum(valid)
+    c = 1.0 / max(n, 1)
+    G = [[0.0] * V for _ in range(BT)]
+    for t in range(BT):
+        z = [math.fsum(h[t][k] * W[v][k] for k in range(H)) + b[v] for v in range(V)]
+        m = max(z)
+        lse = m + math.log(math.fsum(math.exp(zz - m) for zz in z))
+        if valid[t]:
+            for v in range(V):
+                G[t][v] = math.exp(z[v] - lse) * (1 + 2 * mu * lse) - (1.0 if v == y[t] else 0.0)
+
+    def keep(rows_of, cols_of, r, col):  # block of (r, col) in a [rows_of x cols_of] grid
+        r0, c0 = (r // sr) * sr, (col // tr) * tr
+        return not all(abs(rows_of(rr, cc)) < eps
+                       for rr in range(r0, min(r0 + sr, len_rows(rows_of)))
+                       for cc in range(c0, min(c0 + tr, len_cols(rows_of))))
+
+    def len_rows(f):
+        return BT if f is gin else V
+
+    def len_cols(f):
+        return V if f is gin else BT
+
+    def gin(r, col):  # tokens x vocab
+        return G[r][col]
+
+    def gwt(r, col):  # vocab x tokens
+        return G[col][r]
+
+    gi = [[c * math.fsum(G[t][v] * W[v][k] for v in range(V) if keep(gin, gin, t, v))
+           for k in range(H)] for t in range(BT)]
+    kw = [[keep(gwt, gwt, v, t) for t in range(BT)] for v in range(V)]
+    gw = [[c * math.fsum(G[t][v] * h[t][k] for t in range(BT) if kw[v][t]) for k in range(H)]
+          for v in range(V)]
+    gb = [c * math.fsum(G[t][v] for t in range(BT) if kw[v][t]) for v in range(V)]
+    return gi, gw, gb
+
+
+def test_brute_force_with_mixed_blocks():
+    h, W, b, y = _case(11, 3, 13, seed=4, w_std=3.0)
+    eps = 0.05
+    f = oracle.lce_oracle_filtered(h, W, b, y, filter_eps=eps, stat_rows=2, stream_rows=3)
+    assert 0 < f["skipped_input"] < f["tiles_input"]   # some blocks skipped, some kept
+    assert 0 < f["skipped_weight"] < f["tiles_weight"]
+    gi, gw, gb = _brute_filtered(h.tolist(), W.tolist(), b.tolist(), y.tolist(), eps, 2, 3)
+    np.testing.assert_allclose(f["grad_input"], np.array(gi), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(f["grad_weight"], np.array(gw), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(f["grad_bias"], np.array(gb), rtol=1e-12, atol=1e-15)
