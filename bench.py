@@ -1,7 +1,7 @@
 """Benchmark: fused linear cross-entropy forward + backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ce]
-                    [--copy-calibration]
+                    [--no-filter] [--filter-eps E] [--copy-calibration]
 
 One step = one lce_fwd_bwd call (loss, grad_input, grad_W) on the headline LM-head
 workload BT=65535, H=1024, V=176245, bf16, mean reduction, no bias, 20% of the targets
@@ -9,7 +9,9 @@ ignored; inputs are seeded synthetic data already resident in HBM.  Prints ONE J
 whole-job tokens/s, the dominant kernel's roofline position (per-kernel HIP events
 recorded by the library on the launch stream during the timed steps), the float64 CPU
 oracle timed on a bounded sample of the same workload, and the standalone
-cross-entropy kernel's HBM throughput on [8192, 128256] bf16 logits.
+cross-entropy kernel's HBM throughput on [8192, 128256] bf16 logits, and (under
+"filtered") the lossy gradient-filtering mode on the same workload: its step time, skipped
+tile fractions and distance from the exact gradients.
 
 The `traffic` fields are HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter runs of
 this script (profiles/hbm_traffic.json, scaled by the same counters' reading for a plain
@@ -36,6 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 COPY_CAL_BYTES = 1 << 30    # size of the calibration copy (--copy-calibration)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+FILTER_EPS = 2.0 ** -12     # gradient-filtering threshold of the lossy leg (a bf16-scale floor)
 
 
 def _hip():
@@ -79,6 +82,35 @@ def measured_traffic(kernel: str):
         if not os.path.exists(path) or _sha(path) != sha:
             return None
     return rec["hbm_bytes_per_launch"]
+
+
+def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT) -> dict:
+    """The lossy gradient-filtering mode on the same workload: time per step, the fraction
+    of skipped tiles in each gradient pass, and how far its gradients are from the exact
+    ones (relative Frobenius norm of the difference)."""
+    counts = torch.zeros(4, dtype=torch.int64, device="cuda")
+    out = dict(loss=torch.empty_like(exact["loss"]), grad_input=torch.empty_like(exact["grad_input"]),
+               grad_weight=torch.empty_like(exact["grad_weight"]), n_valid=torch.empty_like(exact["n_valid"]))
+    fkw = dict(kw, out=out)
+    lce.lce_fwd_bwd(h, W, None, y, filter_eps=eps, filter_counts=counts, **fkw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lce.lce_fwd_bwd(h, W, None, y, filter_eps=eps, filter_counts=counts, **fkw)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    c = counts.cpu().tolist()
+
+    def rdiff(a, b):
+        a = a.float()
+        b = b.float()
+        return float((a - b).norm() / b.norm())
+
+    return {"filter_eps": eps, "ms_per_step": ms, "tokens_per_s": BT / (ms * 1e-3),
+            "skip_fraction_grad_input": c[0] / max(c[1], 1), "skip_fraction_grad_weight": c[2] / max(c[3], 1),
+            "grad_rel_diff_vs_exact": {"grad_input": rdiff(out["grad_input"], exact["grad_input"]),
+                                        "grad_weight": rdiff(out["grad_weight"], exact["grad_weight"])},
+            "loss_equal": bool(torch.equal(out["loss"], exact["loss"]))}
 
 
 def cpu_baseline(inp, n_tokens: int) -> dict:
@@ -137,6 +169,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ce", action="store_true")
+    ap.add_argument("--no-filter", action="store_true", help="skip the gradient-filtering leg")
+    ap.add_argument("--filter-eps", type=float, default=FILTER_EPS)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM counters)")
     args = ap.parse_args()
@@ -236,6 +270,9 @@ def main():
         "loss": loss,
     }
     log(f"fused step {ms_step:.2f} ms")
+    if not args.no_filter:
+        log(f"gradient filtering, eps {args.filter_eps:g}")
+        res["filtered"] = bench_filtered(lce, torch, h, W, y, kw, out, args.filter_eps, args.steps, BT)
     if not args.no_ce:
         log("standalone cross-entropy")
         res["standalone_ce"] = bench_ce(lce, torch, max(args.steps, 10))

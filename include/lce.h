@@ -116,6 +116,32 @@ lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* b
                                 float* lse_out, void* workspace, size_t workspace_bytes,
                                 void* stream, void* const* ev_start, void* const* ev_stop);
 
+/*
+ * lce_fwd_bwd_filtered -- lce_fwd_bwd with gradient filtering ("Cut Cross Entropy
+ * visualized", "Gradient Filtering"): a lossy mode, off in every exact path.
+ *
+ * The gradient GEMMs consume the dlogits in tiles; a tile whose entries are all below
+ * filter_eps in magnitude contributes nothing to the gradient it feeds (its MFMA work is
+ * skipped, and for grad_W its share of grad_b is dropped too).  The tiles are
+ *   grad_input: 64 tokens x 16 vocabulary entries (aligned at token 0, vocabulary entry 0);
+ *   grad_W, grad_b: 64 vocabulary entries x 16 tokens.
+ * The test applies to the dlogits of the summed loss, valid * (softmax * (1 + 2 mu LSE) -
+ * onehot), i.e. before the 1/n_valid of the mean, so it does not depend on the batch size.
+ * The loss, n_valid and LSE are exact.  The gradients differ from lce_fwd_bwd's by the
+ * dropped entries only (each below filter_eps times the reduction scale).
+ *   filter_eps     >= 0 and finite; 0 disables filtering (the call is then lce_fwd_bwd).
+ *   filter_counts  device int64[4] or NULL: skipped and examined tiles of the grad_input
+ *                  pass, then of the grad_W pass (overwritten; only when filter_eps > 0).
+ * Other arguments, errors and workspace as lce_fwd_bwd (LCE_ERR_ARG for a bad filter_eps).
+ */
+lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* bias,
+                                const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+                                lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
+                                lce_reduction reduction, uint32_t flags, float* loss_out,
+                                void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                                float* lse_out, void* workspace, size_t workspace_bytes,
+                                void* stream, float filter_eps, int64_t* filter_counts);
+
 /* Exact number of workspace bytes lce_fwd_bwd needs for these sizes (its whole extra
  * device memory), or 0 if the sizes are invalid. */
 size_t lce_fwd_bwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);

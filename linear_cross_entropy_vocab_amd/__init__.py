@@ -67,12 +67,15 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
                 reduction: str = "mean", grad_input: bool = True, grad_weight: bool = True,
                 grad_bias: Optional[bool] = None, return_lse: bool = False,
                 check_targets: bool = False, workspace: Optional[torch.Tensor] = None,
-                out: Optional[dict] = None, events=None) -> dict:
+                out: Optional[dict] = None, events=None, filter_eps: float = 0.0,
+                filter_counts: Optional[torch.Tensor] = None) -> dict:
     """One call of lce_fwd_bwd: loss and the requested gradients (fully overwritten).
 
     `out` may hold preallocated tensors under the keys loss, grad_input, grad_weight,
     grad_bias, n_valid, lse; `events` = (start_list, stop_list) of hipEvent_t handles
-    selects lce_fwd_bwd_profiled.
+    selects lce_fwd_bwd_profiled.  filter_eps > 0 selects lce_fwd_bwd_filtered (lossy
+    gradient filtering); filter_counts (int64 [4] on the device) then receives the skipped
+    and examined tile counts of the grad_input and grad_W passes.
     """
     lib = load()
     _need_gpu(hidden, weight, bias, targets)
@@ -113,7 +116,15 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     args = (_ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), BT, H, V, dt, ignore_index,
             float(z_loss), _REDUCTIONS[reduction], flags, _ptr(loss), _ptr(gi), _ptr(gw), _ptr(gb),
             _ptr(nv), _ptr(lse), _ptr(workspace), workspace.numel(), stream)
-    if events is None:
+    if filter_eps > 0.0:
+        if events is not None:
+            raise ValueError("events are not supported with filter_eps")
+        if filter_counts is not None:
+            _need_gpu(filter_counts)
+            if filter_counts.dtype != torch.int64 or filter_counts.numel() < 4:
+                raise TypeError("filter_counts must be an int64 tensor of 4 elements")
+        st = lib.lce_fwd_bwd_filtered(*args, float(filter_eps), _ptr(filter_counts))
+    elif events is None:
         st = lib.lce_fwd_bwd(*args)
     else:
         arr_t = ctypes.c_void_p * _lib.NUM_STAGES

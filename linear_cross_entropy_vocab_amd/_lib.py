@@ -19,7 +19,8 @@ REDUCTION_SUM = 1
 FLAG_CHECK_TARGETS = 1
 NUM_STAGES = 7
 
-EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_workspace_bytes", "lce_stage_name",
+EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_fwd_bwd_workspace_bytes",
+           "lce_stage_name",
            "lce_ce_with_grad_inplace", "lce_ce_workspace_bytes", "lce_status_string", "lce_version")
 
 _lib = None
@@ -45,6 +46,8 @@ def load() -> ctypes.CDLL:
     lib.lce_fwd_bwd.restype = ctypes.c_int
     lib.lce_fwd_bwd_profiled.argtypes = fused + [c_vp, c_vp]
     lib.lce_fwd_bwd_profiled.restype = ctypes.c_int
+    lib.lce_fwd_bwd_filtered.argtypes = fused + [c_f, c_vp]
+    lib.lce_fwd_bwd_filtered.restype = ctypes.c_int
     lib.lce_fwd_bwd_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_uint32]
     lib.lce_fwd_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.lce_stage_name.argtypes = [ctypes.c_int]

@@ -59,7 +59,8 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
                              float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
                              void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
                              float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
-                             void* const* ev_start, void* const* ev_stop) {
+                             void* const* ev_start, void* const* ev_stop, float filter_eps,
+                             int64_t* filter_counts) {
   // ---- validation: no HIP calls before this block has passed
   if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
   if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 40) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
@@ -70,10 +71,11 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
   if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
   if ((flags & ~LCE_FLAG_CHECK_TARGETS) != 0) return LCE_ERR_ARG;
+  if (!(filter_eps >= 0.f) || !std::isfinite(filter_eps)) return LCE_ERR_ARG;
   const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
   if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(grad_input, 16) || !aligned(grad_W, 16) ||
       !aligned(workspace, 16) || !aligned(bias, es) || !aligned(grad_b, es) || !aligned(targets, 8) ||
-      !aligned(loss_out, 4) || !aligned(n_valid_out, 8) || !aligned(lse_out, 4))
+      !aligned(loss_out, 4) || !aligned(n_valid_out, 8) || !aligned(lse_out, 4) || !aligned(filter_counts, 8))
     return LCE_ERR_ALIGNMENT;
   if (workspace_bytes < fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16)) return LCE_ERR_WORKSPACE;
 
@@ -95,6 +97,8 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   a.grad_b = grad_b;
   a.n_valid_out = n_valid_out;
   a.lse_out = lse_out;
+  a.filter_eps = filter_eps;
+  a.filter_counts = filter_eps > 0.f ? filter_counts : nullptr;
   const FusedWs w = fused_carve(workspace, BT, V);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -136,7 +140,7 @@ lce_status lce_fwd_bwd(const void* hidden, const void* W, const void* bias, cons
                        size_t workspace_bytes, void* stream) {
   return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
                          flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
-                         workspace_bytes, stream, nullptr, nullptr);
+                         workspace_bytes, stream, nullptr, nullptr, 0.f, nullptr);
 }
 
 lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* bias, const int64_t* targets,
@@ -147,7 +151,18 @@ lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* b
                                 void* const* ev_start, void* const* ev_stop) {
   return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
                          flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
-                         workspace_bytes, stream, ev_start, ev_stop);
+                         workspace_bytes, stream, ev_start, ev_stop, 0.f, nullptr);
+}
+
+lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                                int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                                float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
+                                void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                                float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                                float filter_eps, int64_t* filter_counts) {
+  return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
+                         flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
+                         workspace_bytes, stream, nullptr, nullptr, filter_eps, filter_counts);
 }
 
 const char* lce_stage_name(int k) {

@@ -43,6 +43,8 @@ struct BwdArgs {
   const float* lse;
   const float2* tok;  // per token: (LSE, target + 1, or 0 for rows that contribute nothing)
   const float* biasf;  // bias in fp32, or NULL
+  float filter_eps;     // > 0: skip the GEMM3 work of tiles whose |g| are all below it
+  unsigned long long* filter_counts;  // [2] skipped / examined tiles (atomics), or NULL
   int64_t nS, nX, H, BT, V;
   int64_t ignore_index;
   float mu;
@@ -154,6 +156,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
   __shared__ __attribute__((aligned(16))) float s_a[kBS];
   __shared__ __attribute__((aligned(16))) float s_b[kBS];
   __shared__ __attribute__((aligned(16))) int32_t s_y[kBS];
+  // gradient filtering (p.filter_eps > 0): wave w's share of each 16-column half of the
+  // dlogits tile is negligible
+  __shared__ int s_small[4][2];
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
   const int64_t s_tile = blockIdx.x / p.nchunks;
@@ -257,6 +262,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
   const int c = lane & 31;                // reduce step: streamed column of this lane
   const int r0 = 16 * w + 8 * (lane >> 5);  // reduce step: first of this lane's 8 stationary rows
   const int64_t ntiles = (p.nX + kBX - 1) / kBX;
+  const bool filt = p.filter_eps > 0.f;
+  float gpend[8];  // (filtering) grad_b terms of this tile, added once the tile is kept
+  unsigned long long n_skipped = 0;
   if (ntiles > 0) {
     if constexpr (SINGLE) load_x(0, 0, PF);
     load_col(0);
@@ -340,6 +348,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
     // ---------------- z and dlogits for column c, rows r0 .. r0+7, in two halves of 4 rows
     // (bounds the live registers of this step)
     const int64_t xc = x0 + c;
+    bool small_lane = true;
 #pragma unroll 1
     for (int hf = 0; hf < 2; ++hf) {
       const int rh = r0 + 4 * hf;
@@ -373,18 +382,47 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
         }
         if (hf == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) gb[e] += g[e];
+          for (int e = 0; e < 4; ++e) gpend[e] = g[e];
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) gb[4 + e] += g[e];
+          for (int e = 0; e < 4; ++e) gpend[4 + e] = g[e];
         }
+      }
+      if (filt) {
+        bool sm = true;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm = sm && fabsf(g[e]) < p.filter_eps;
+        small_lane = hf == 0 ? sm : (small_lane && sm);
       }
       store4(gtile + swz<G_ROW, G_NCH>(c, rh * ES), g, T());
     }
+    if (filt) {
+      // columns 0..15 of the tile are lanes 0-15 and 32-47, columns 16..31 the others
+      const unsigned long long big = __builtin_amdgcn_ballot_w64(!small_lane);
+      if (lane == 0) {
+        s_small[w][0] = (big & 0x0000ffff0000ffffull) == 0 ? 1 : 0;
+        s_small[w][1] = (big & 0xffff0000ffff0000ull) == 0 ? 1 : 0;
+      }
+    }
     __syncthreads();
+    // (filtering) a 64 x 16 half of the tile whose dlogits are all negligible adds nothing
+    bool skip_half[2] = {false, false};
+    if (filt) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        skip_half[hh] = (s_small[0][hh] & s_small[1][hh] & s_small[2][hh] & s_small[3][hh]) != 0;
+        if (skip_half[hh] && x0 + 16 * hh < p.nX) ++n_skipped;  // (halves past nX are not tiles)
+      }
+    }
+    if (DW) {
+      const bool keep = !skip_half[c >> 4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gb[e] += keep ? gpend[e] : 0.f;
+    }
     // ---------------- GEMM3: acc += g . X[:, wave columns]
 #pragma unroll
     for (int kk = 0; kk < kBX / 16; ++kk) {
+      if (skip_half[kk]) continue;
       Frag<T> ga[2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) tile_frag<G_ROW, G_NCH>(ga[sb], gtile, kk * 16, sb * 32, lane);
@@ -411,6 +449,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
           if (row < p.nS && col < H) p.out[row * H + col] = Elem<T>::from_f(cscale * acc[sb][cb][r]);
         }
       }
+  }
+  if (filt && p.filter_counts != nullptr && chunk == 0 && threadIdx.x == 0) {
+    atomicAdd(&p.filter_counts[0], n_skipped);
+    atomicAdd(&p.filter_counts[1], (unsigned long long)((p.nX + 15) / 16));
   }
   if (DW && p.grad_b != nullptr && chunk == 0) {
 #pragma unroll
@@ -487,7 +529,11 @@ struct DmaPlanes<N, N> {
   static __device__ __forceinline__ void run(const u32x4_t&, uint32_t, uint32_t) {}
 };
 
-template <bool DW, int NB>
+// FILT: gradient filtering ("Cut Cross Entropy visualized", "Gradient Filtering"): a tile
+// (64 stationary rows x 16 streamed rows) whose dlogits of the summed loss are all below
+// p.filter_eps in magnitude adds nothing to the gradient (its GEMM3 work and its grad_b
+// share are skipped).
+template <bool DW, int NB, bool FILT>
 __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t> p) {
   constexpr int NCOL = 32 * NB;       // columns of H owned by a wave
   constexpr int XW = kPX * NCOL * 2;  // bytes of a wave's share of one tile (NB planes)
@@ -498,6 +544,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   // column values of each buffered tile, loaded with it: per token (LSE, target + 1) (DW)
   // or the fp32 bias of each vocabulary row
   __shared__ __attribute__((aligned(256))) char cs[4][kPBuf][256];
+  __shared__ int s_small[4];  // (FILT) wave w's share of the current dlogits tile is negligible
 
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int l16 = lane & 15, q = lane >> 4;       // 16x16 operand coordinates
@@ -560,6 +607,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[sb][cb][r] = 0.f;
   float gb[4] = {0.f, 0.f, 0.f, 0.f};
+  float gpend[4] = {0.f, 0.f, 0.f, 0.f};
+  unsigned long long n_skipped = 0;
 
   // ---- per-lane LDS offsets
   // DMA: instruction j of a tile fills plane j; lane l lands at slot l = (row n, chunk u).
@@ -681,10 +730,21 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
         gi = __expf(z[i] + ra[i] + nc_a) * nc_f - (nc_y == vrow0 + i ? 1.f : 0.f);
       }
       g[i] = ok ? gi : 0.f;
-      if (DW) gb[i] += g[i];
+      if (DW) {
+        if (FILT) gpend[i] = g[i];  // added to grad_b once the tile is known to be kept
+        else gb[i] += g[i];
+      }
     }
     *reinterpret_cast<uint2*>(gl + o_gw) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+    if (FILT) {
+      const float e = p.filter_eps;
+      const bool small = fabsf(g[0]) < e && fabsf(g[1]) < e && fabsf(g[2]) < e && fabsf(g[3]) < e;
+      const bool all_small = __builtin_amdgcn_ballot_w64(!small) == 0;
+      if (lane == 0) s_small[w] = all_small ? 1 : 0;
+    }
   };
+  // (FILT) after the barrier that follows dlogits: is the whole tile negligible?
+  auto tile_skipped = [&]() { return FILT && (s_small[0] & s_small[1] & s_small[2] & s_small[3]) != 0; };
   // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]; with `refill`, planes
   // 0 .. NB/2-1 of the buffer are reloaded (tile `next`) as soon as their last read has
   // completed; the other half is queued during the next phase A (refill_rest), so that the
@@ -697,6 +757,20 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     rx_next = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
     lds_next = xw_lds + (uint32_t)(buf * XW);
     if (refill) dma4(col_rsrc(next), cs_lds + (uint32_t)(buf * 256), col_off);
+    if (FILT) {
+      if (tile_skipped()) {  // no MFMA work; the buffer refill still happens (nothing reads it)
+        ++n_skipped;
+        if (refill) {
+#pragma unroll
+          for (int cb = 0; cb < NB / 2; ++cb) dma16(rx_next, lds_next + 1024 * cb, dma_off + 64 * cb);
+        }
+        return;
+      }
+      if (DW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gb[i] += gpend[i];
+      }
+    }
     Frag<bf16_t> ga[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) ga[sb].v = tr_pair(gl + o_ga[sb][0], gl + o_ga[sb][1]);
@@ -759,6 +833,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     __syncthreads();
   }
   vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
+  if (FILT && p.filter_counts != nullptr && tid == 0) {
+    atomicAdd(&p.filter_counts[0], n_skipped);
+    atomicAdd(&p.filter_counts[1], (unsigned long long)ntiles);
+  }
 
   // ---- write c * acc
   if (p.out != nullptr) {
@@ -786,16 +864,21 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   }
 }
 
-template <bool DW>
-static hipError_t launch_bwd_pipe(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
+template <bool DW, bool FILT>
+static hipError_t launch_bwd_pipe_f(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
   switch (nb) {
-    case 1: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 1>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 1, FILT>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 2, FILT>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 4, FILT>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((bwd_pipe_kernel<DW, 8, FILT>), grid, dim3(kBwdThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <bool DW>
+static hipError_t launch_bwd_pipe(int nb, const BwdArgs<bf16_t>& a, dim3 grid, hipStream_t st) {
+  return a.filter_eps > 0.f ? launch_bwd_pipe_f<DW, true>(nb, a, grid, st)
+                            : launch_bwd_pipe_f<DW, false>(nb, a, grid, st);
 }
 
 template <typename T, bool DW, bool SINGLE, int N>
@@ -855,6 +938,10 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
   a.y = fa.targets;
   a.lse = w.lse;
   a.tok = w.tok;
+  a.filter_eps = fa.filter_eps;
+  a.filter_counts = fa.filter_counts == nullptr
+                        ? nullptr
+                        : reinterpret_cast<unsigned long long*>(fa.filter_counts + (dw ? 2 : 0));
   a.biasf = fa.bias != nullptr ? w.biasf : nullptr;
   a.H = fa.H;
   a.BT = fa.BT;

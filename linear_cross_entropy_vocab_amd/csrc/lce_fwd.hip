@@ -25,7 +25,9 @@ __global__ void __launch_bounds__(kTgtThreads) targets_kernel(const int64_t* __r
                                                                int64_t V, int64_t ignore_index,
                                                                int64_t* n_valid, int32_t* n_bad,
                                                                const T* __restrict__ bias,
-                                                               float* __restrict__ biasf) {
+                                                               float* __restrict__ biasf,
+                                                               int64_t* __restrict__ filter_counts) {
+  if (filter_counts != nullptr && threadIdx.x < 4) filter_counts[threadIdx.x] = 0;
   if (bias != nullptr)
     for (int64_t i = threadIdx.x; i < V; i += kTgtThreads) biasf[i] = Elem<T>::to_f(bias[i]);
   __shared__ long long s_v[kTgtThreads / kWave], s_b[kTgtThreads / kWave];
@@ -52,10 +54,12 @@ __global__ void __launch_bounds__(kTgtThreads) targets_kernel(const int64_t* __r
 hipError_t launch_targets(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.bf16)
     hipLaunchKernelGGL(targets_kernel<bf16_t>, dim3(1), dim3(kTgtThreads), 0, st, a.targets, a.BT, a.V,
-                       a.ignore_index, w.n_valid, w.n_bad, static_cast<const bf16_t*>(a.bias), w.biasf);
+                       a.ignore_index, w.n_valid, w.n_bad, static_cast<const bf16_t*>(a.bias), w.biasf,
+                       a.filter_counts);
   else
     hipLaunchKernelGGL(targets_kernel<float>, dim3(1), dim3(kTgtThreads), 0, st, a.targets, a.BT, a.V,
-                       a.ignore_index, w.n_valid, w.n_bad, static_cast<const float*>(a.bias), w.biasf);
+                       a.ignore_index, w.n_valid, w.n_bad, static_cast<const float*>(a.bias), w.biasf,
+                       a.filter_counts);
   return hipGetLastError();
 }
 

@@ -49,6 +49,8 @@ struct FusedArgs {
   void* grad_b;
   int64_t* n_valid_out;
   float* lse_out;
+  float filter_eps;          // > 0: gradient filtering (tiles of |dlogits| < eps are skipped)
+  int64_t* filter_counts;    // [4] skipped / examined tiles of the grad_input and grad_W passes, or NULL
 };
 
 // Stages of the fused call, in launch order.

@@ -95,6 +95,28 @@ def test_fused_host_errors(lib, kw, status):
     assert fused(lib, **kw) == status
 
 
+def fused_filtered(lib, eps, counts=None, **kw):
+    a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
+             dtype=BF16, ignore=-100, mu=0.0, red=MEAN, flags=0, loss=P + 0x300000,
+             gi=P + 0x400000, gw=P + 0x500000, gb=None, nv=P + 0x600000, lse=None,
+             ws=P + 0x700000, wsb=OK_WS, stream=None)
+    a.update(kw)
+    return lib.lce_fwd_bwd_filtered(a["hidden"], a["W"], a["bias"], a["targets"], a["BT"], a["H"],
+                                    a["V"], a["dtype"], a["ignore"], a["mu"], a["red"], a["flags"],
+                                    a["loss"], a["gi"], a["gw"], a["gb"], a["nv"], a["lse"], a["ws"],
+                                    a["wsb"], a["stream"], eps, counts)
+
+
+@pytest.mark.parametrize("eps,counts,kw,status", [
+    (-1e-3, None, {}, 6), (math.nan, None, {}, 6), (math.inf, None, {}, 6),
+    (1e-3, P + 4, {}, 4),                 # misaligned count buffer
+    (1e-3, None, dict(W=None), 1),        # the usual checks still apply
+    (1e-3, None, dict(H=12), 2),
+])
+def test_filtered_host_errors(lib, eps, counts, kw, status):
+    assert fused_filtered(lib, eps, counts, **kw) == status
+
+
 def test_fused_errors_before_device_work_with_empty_batch(lib):
     # BT = 0 may pass NULL hidden/targets; a too-small workspace is still rejected on the host
     assert fused(lib, BT=0, hidden=None, targets=None, wsb=0) == 5

@@ -1,0 +1,91 @@
+"""GPU parity of the gradient-filtering mode (lce_fwd_bwd_filtered, "Cut Cross Entropy
+visualized", "Gradient Filtering") against the filtered float64 oracle.
+
+Inputs make every tile decision unambiguous: a vocabulary range, aligned to the tiles and
+holding no target, is pushed to probability ~e^-60 by its bias, and eps = 1e-6 sits far
+from both e^-60 and the smallest probability any other tile can reach.  So the tile counts
+must match the oracle exactly, and the gradients to the usual bf16 / fp32 tolerances.
+Covered: the pipelined kernel (bf16, H <= 1024), the column-chunked kernel (bf16, H > 1024)
+and the fp32 kernel; grad_b; both reductions; and eps below every |dlogit|, where the
+filtered call must reproduce the exact call bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_cross_entropy_vocab_amd as lce
+from workloads import make_fused
+from gpu_util import TOL, dev, host64, rel, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (dtype, BT, H, V, suppressed vocab range, reduction, z_loss, seed)
+    ("bf16", 200, 256, 2048, (512, 1536), "mean", 0.0, 31),
+    ("bf16", 333, 1024, 3001, (1024, 2048), "sum", 1e-3, 32),
+    ("bf16", 150, 1152, 1500, (256, 1024), "mean", 0.0, 33),
+    ("f32", 130, 128, 1200, (128, 896), "mean", 1e-3, 34),
+]
+
+
+def _inputs(dtype, BT, H, V, rng_v, seed, z_loss, reduction):
+    inp = make_fused(BT, H, V, dtype=dtype, seed=seed, w_std=H ** -0.5, bias_std=0.1,
+                     ignore_frac=0.1, z_loss=z_loss, reduction=reduction)
+    lo, hi = rng_v
+    inp.bias[lo:hi] = -60.0
+    y = inp.targets.copy()
+    sel = (y >= lo) & (y < hi)
+    y[sel] = y[sel] % lo if lo > 0 else hi
+    inp.targets = y
+    return inp
+
+
+def _run(inp, eps, counts=None):
+    r = lce.lce_fwd_bwd(dev(inp.hidden, inp.dtype), dev(inp.weight, inp.dtype), dev(inp.bias, inp.dtype),
+                        dev(inp.targets), z_loss=inp.z_loss, reduction=inp.reduction,
+                        filter_eps=eps, filter_counts=counts)
+    torch.cuda.synchronize()
+    return r
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}" for c in CASES])
+def test_filtered_matches_filtered_oracle(case):
+    dtype, BT, H, V, rv, reduction, mu, seed = case
+    print(f"filtered parity {case}", flush=True)
+    inp = _inputs(dtype, BT, H, V, rv, seed, mu, reduction)
+    eps = 1e-6
+    ref = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps,
+                                     z_loss=mu, reduction=reduction)
+    counts = torch.zeros(4, dtype=torch.int64, device="cuda")
+    r = _run(inp, eps, counts)
+    c = counts.cpu().tolist()
+    assert c == [ref["skipped_input"], ref["tiles_input"], ref["skipped_weight"], ref["tiles_weight"]]
+    assert ref["skipped_input"] > 0 and ref["skipped_weight"] > 0
+    tol = TOL[dtype]
+    assert int(r["n_valid"].item()) == ref["n_valid"]
+    assert rel(r["loss"].item(), ref["loss"]) <= tol["loss"]
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        assert rel_fro(host64(r[k]), ref[k]) <= tol["grad"], k
+    # the skipped vocabulary rows get exactly zero grad_W and grad_b
+    lo, hi = rv
+    lo64, hi64 = -(-lo // 64) * 64, (hi // 64) * 64
+    if hi64 > lo64:
+        assert int(torch.count_nonzero(r["grad_weight"][lo64:hi64])) == 0
+        assert int(torch.count_nonzero(r["grad_bias"][lo64:hi64])) == 0
+
+
+@pytest.mark.parametrize("dtype,H", [("bf16", 256), ("bf16", 1152), ("f32", 128)])
+def test_tiny_eps_reproduces_exact_call(dtype, H):
+    inp = make_fused(160, H, 1000, dtype=dtype, seed=35, w_std=H ** -0.5, bias_std=0.1,
+                     ignore_frac=0.1)
+    b = dev(inp.bias, dtype)
+    args = (dev(inp.hidden, dtype), dev(inp.weight, dtype), b, dev(inp.targets))
+    exact = lce.lce_fwd_bwd(*args)
+    counts = torch.zeros(4, dtype=torch.int64, device="cuda")
+    filt = lce.lce_fwd_bwd(*args, filter_eps=1e-38, filter_counts=counts)
+    torch.cuda.synchronize()
+    assert counts[0].item() == 0 and counts[2].item() == 0
+    for k in ("loss", "grad_input", "grad_weight", "grad_bias"):
+        assert torch.equal(exact[k], filt[k]), k
