@@ -92,11 +92,14 @@ def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT) -> dict:
     out = dict(loss=torch.empty_like(exact["loss"]), grad_input=torch.empty_like(exact["grad_input"]),
                grad_weight=torch.empty_like(exact["grad_weight"]), n_valid=torch.empty_like(exact["n_valid"]))
     fkw = dict(kw, out=out)
-    lce.lce_fwd_bwd(h, W, None, y, filter_eps=eps, filter_counts=counts, **fkw)
+    bias = fkw.pop("bias", None)
+    if bias is not None:
+        out["grad_bias"] = torch.empty_like(bias)
+    lce.lce_fwd_bwd(h, W, bias, y, filter_eps=eps, filter_counts=counts, **fkw)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        lce.lce_fwd_bwd(h, W, None, y, filter_eps=eps, filter_counts=counts, **fkw)
+        lce.lce_fwd_bwd(h, W, bias, y, filter_eps=eps, filter_counts=counts, **fkw)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     c = counts.cpu().tolist()
@@ -170,6 +173,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ce", action="store_true")
     ap.add_argument("--no-filter", action="store_true", help="skip the gradient-filtering leg")
+    ap.add_argument("--filter-zipf", action="store_true",
+                    help="only measure gradient filtering on the Zipf-target workloads (Gemma-like, "
+                         "Qwen-like) and print one JSON line per workload")
     ap.add_argument("--filter-eps", type=float, default=FILTER_EPS)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM counters)")
@@ -185,6 +191,44 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.filter_zipf:
+        for name in ("gemma_like", "qwen_like"):
+            c = CONFIGS[name]
+            log(f"generating {name}")
+            inp = make_config(name)
+            dt = torch.bfloat16
+            hh = torch.from_numpy(inp.hidden).to(dt).cuda()
+            WW = torch.from_numpy(inp.weight).to(dt).cuda()
+            bb = None if inp.bias is None else torch.from_numpy(inp.bias).to(dt).cuda()
+            yy = torch.from_numpy(inp.targets).cuda()
+            del inp
+            kw2 = dict(reduction=c.reduction, z_loss=c.z_loss)
+            ex = lce.lce_fwd_bwd(hh, WW, bb, yy, **kw2)
+            torch.cuda.synchronize()
+            hip = _hip()
+            n_st = len(lce.stage_names())
+            evs = [([_event(hip) for _ in range(n_st)], [_event(hip) for _ in range(n_st)])
+                   for _ in range(args.steps)]
+            t0 = time.perf_counter()
+            for k in range(args.steps):
+                ex = lce.lce_fwd_bwd(hh, WW, bb, yy, out=ex, events=evs[k], **kw2)
+            torch.cuda.synchronize()
+            ms_exact = (time.perf_counter() - t0) * 1e3 / args.steps
+            st_ms = {n: float(np.mean([_elapsed(hip, e[0][i], e[1][i]) for e in evs]))
+                     for i, n in enumerate(lce.stage_names())}
+            for e in evs:
+                for x in e[0] + e[1]:
+                    hip.hipEventDestroy(ctypes.c_void_p(x))
+            log(f"{name}: exact {ms_exact:.1f} ms, stages {st_ms}")
+            res_f = bench_filtered(lce, torch, hh, WW, yy, dict(kw2, bias=bb), ex, args.filter_eps,
+                                   args.steps, c.BT)
+            res_f.update(workload=f"{name}: BT={c.BT}, H={c.H}, V={c.V}, Zipf(1.1) targets",
+                         exact_ms_per_step=ms_exact, exact_stage_ms=st_ms)
+            print(json.dumps(res_f), flush=True)
+            del hh, WW, bb, yy, ex
+            torch.cuda.empty_cache()
+        return
 
     c = CONFIGS["headline"]
     log("generating the headline workload")
