@@ -59,6 +59,9 @@ typedef enum lce_reduction {
  * target is neither ignore_index nor a vocabulary id.  Without it such rows are treated
  * as ignored (no loss, zero gradient) and the call still returns LCE_OK. */
 #define LCE_FLAG_CHECK_TARGETS 1u
+/* (lce_fwd_bwd_chunked only) grad_W is float32 [V, H]: the sum over the token chunks is kept
+ * in it directly, so the workspace needs no fp32 accumulator of its own. */
+#define LCE_FLAG_GRAD_W_FP32 2u
 
 /* Number of device kernels one lce_fwd_bwd call may launch (for lce_fwd_bwd_profiled). */
 #define LCE_NUM_STAGES 7
@@ -171,6 +174,32 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
                                     lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
                                     float* ce_sum_out, float* z_sum_out, int64_t* n_valid_out,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lce_fwd_bwd_chunked -- the same loss and gradients by the token-chunked composition
+ * ("Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It",
+ * Strategy 1 and "The chunk-size trick"; "Greyhound -- Cross-Entropy", "Relationship to
+ * Chunked Linear Loss").  bf16 only.
+ *
+ * Tokens are processed in chunks of cs rows, cs = 2 * next_pow2(ceil(BT / ceil(V / H)))
+ * (capped at BT): the chunk's logits are written once to a bf16 buffer of cs x V entries in
+ * the workspace, turned into dlogits in place by the standalone cross-entropy kernel, and
+ * consumed by the two gradient products.  Nothing is recomputed (6 BT V H flops instead of
+ * lce_fwd_bwd's 10), at the price of the chunk buffer and an fp32 grad_W sum in device memory
+ * (V x H x 4 bytes, unless LCE_FLAG_GRAD_W_FP32).  Results agree with lce_fwd_bwd within the
+ * bf16 tolerances; they differ in rounding because the dlogits pass through bf16 storage.
+ *
+ *   flags   0, LCE_FLAG_CHECK_TARGETS and/or LCE_FLAG_GRAD_W_FP32 (grad_W is float32 [V, H]).
+ *   lse_out LSE per row, or NULL.
+ * Other arguments as lce_fwd_bwd, with V <= 2^22; LCE_ERR_DTYPE for float32 inputs.  The workspace must hold
+ * lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags) bytes (0 for float32).
+ */
+size_t lce_fwd_bwd_chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);
+lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                               int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                               float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
+                               void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                               float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes lce_ce_with_grad_inplace needs (per-row partial results), or 0 if invalid. */
 size_t lce_ce_workspace_bytes(int64_t B, int64_t V, lce_dtype dtype);

@@ -58,6 +58,11 @@ def fwd_bwd_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype) -> int:
     return int(load().lce_fwd_bwd_workspace_bytes(BT, H, V, _DTYPES[dtype], 0))
 
 
+def chunked_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype, grad_weight_fp32: bool = False) -> int:
+    flags = _lib.FLAG_GRAD_W_FP32 if grad_weight_fp32 else 0
+    return int(load().lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, _DTYPES[dtype], flags))
+
+
 def ce_workspace_bytes(B: int, V: int, dtype: torch.dtype) -> int:
     return int(load().lce_ce_workspace_bytes(B, V, _DTYPES[dtype]))
 
@@ -68,15 +73,25 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
                 grad_bias: Optional[bool] = None, return_lse: bool = False,
                 check_targets: bool = False, workspace: Optional[torch.Tensor] = None,
                 out: Optional[dict] = None, events=None, filter_eps: float = 0.0,
-                filter_counts: Optional[torch.Tensor] = None) -> dict:
+                filter_counts: Optional[torch.Tensor] = None, method: str = "fused",
+                grad_weight_fp32: bool = False) -> dict:
     """One call of lce_fwd_bwd: loss and the requested gradients (fully overwritten).
 
     `out` may hold preallocated tensors under the keys loss, grad_input, grad_weight,
     grad_bias, n_valid, lse; `events` = (start_list, stop_list) of hipEvent_t handles
     selects lce_fwd_bwd_profiled.  filter_eps > 0 selects lce_fwd_bwd_filtered (lossy
     gradient filtering); filter_counts (int64 [4] on the device) then receives the skipped
-    and examined tile counts of the grad_input and grad_W passes.
+    and examined tile counts of the grad_input and grad_W passes.  method="chunked" selects
+    lce_fwd_bwd_chunked (the token-chunked composition; bf16 only), where grad_weight_fp32
+    makes grad_weight a float32 tensor that holds the sum over the chunks directly.
     """
+    if method not in ("fused", "chunked"):
+        raise ValueError(f"method must be 'fused' or 'chunked', not {method!r}")
+    chunked = method == "chunked"
+    if grad_weight_fp32 and not chunked:
+        raise ValueError("grad_weight_fp32 needs method='chunked'")
+    if chunked and (filter_eps > 0.0 or events is not None):
+        raise ValueError("filter_eps and events are not supported with method='chunked'")
     lib = load()
     _need_gpu(hidden, weight, bias, targets)
     BT, H = hidden.shape
@@ -98,7 +113,7 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
         gi = torch.empty_like(hidden)
     gw = o.get("grad_weight") if grad_weight else None
     if grad_weight and gw is None:
-        gw = torch.empty_like(weight)
+        gw = torch.empty_like(weight, dtype=torch.float32 if grad_weight_fp32 else weight.dtype)
     gb = o.get("grad_bias") if grad_bias else None
     if grad_bias and gb is None:
         gb = torch.empty_like(bias)
@@ -109,14 +124,21 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     if return_lse and lse is None:
         lse = torch.empty(BT, dtype=torch.float32, device=dev)
     flags = _lib.FLAG_CHECK_TARGETS if check_targets else 0
-    need = int(lib.lce_fwd_bwd_workspace_bytes(BT, H, V, dt, flags))
+    if grad_weight_fp32:
+        flags |= _lib.FLAG_GRAD_W_FP32
+        if gw is not None and gw.dtype != torch.float32:
+            raise TypeError("grad_weight must be float32 with grad_weight_fp32")
+    ws_fn = lib.lce_fwd_bwd_chunked_workspace_bytes if chunked else lib.lce_fwd_bwd_workspace_bytes
+    need = int(ws_fn(BT, H, V, dt, flags))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     args = (_ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), BT, H, V, dt, ignore_index,
             float(z_loss), _REDUCTIONS[reduction], flags, _ptr(loss), _ptr(gi), _ptr(gw), _ptr(gb),
             _ptr(nv), _ptr(lse), _ptr(workspace), workspace.numel(), stream)
-    if filter_eps > 0.0:
+    if chunked:
+        st = lib.lce_fwd_bwd_chunked(*args)
+    elif filter_eps > 0.0:
         if events is not None:
             raise ValueError("events are not supported with filter_eps")
         if filter_counts is not None:
@@ -131,7 +153,7 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
         ev0 = arr_t(*[ctypes.c_void_p(e) for e in events[0]])
         ev1 = arr_t(*[ctypes.c_void_p(e) for e in events[1]])
         st = lib.lce_fwd_bwd_profiled(*args, ev0, ev1)
-    _lib.check(st, "lce_fwd_bwd")
+    _lib.check(st, "lce_fwd_bwd_chunked" if chunked else "lce_fwd_bwd")
     return dict(loss=loss, grad_input=gi, grad_weight=gw, grad_bias=gb, n_valid=nv, lse=lse,
                 workspace=workspace)
 

@@ -17,9 +17,11 @@ DTYPE_BF16 = 1
 REDUCTION_MEAN = 0
 REDUCTION_SUM = 1
 FLAG_CHECK_TARGETS = 1
+FLAG_GRAD_W_FP32 = 2
 NUM_STAGES = 7
 
 EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_fwd_bwd_workspace_bytes",
+           "lce_fwd_bwd_chunked", "lce_fwd_bwd_chunked_workspace_bytes",
            "lce_stage_name",
            "lce_ce_with_grad_inplace", "lce_ce_workspace_bytes", "lce_status_string", "lce_version")
 
@@ -50,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.lce_fwd_bwd_filtered.restype = ctypes.c_int
     lib.lce_fwd_bwd_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_uint32]
     lib.lce_fwd_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.lce_fwd_bwd_chunked.argtypes = fused
+    lib.lce_fwd_bwd_chunked.restype = ctypes.c_int
+    lib.lce_fwd_bwd_chunked_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_uint32]
+    lib.lce_fwd_bwd_chunked_workspace_bytes.restype = ctypes.c_size_t
     lib.lce_stage_name.argtypes = [ctypes.c_int]
     lib.lce_stage_name.restype = ctypes.c_char_p
     lib.lce_ce_with_grad_inplace.argtypes = [c_vp, c_vp, c_i64, c_i64, ctypes.c_int, c_i64, c_f, c_vp,

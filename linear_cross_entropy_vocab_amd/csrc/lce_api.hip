@@ -165,6 +165,59 @@ lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* b
                          workspace_bytes, stream, nullptr, nullptr, filter_eps, filter_counts);
 }
 
+size_t lce_fwd_bwd_chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
+  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return 0;
+  if (dtype != LCE_DTYPE_BF16) return 0;
+  return lce::chunked_workspace_bytes(BT, H, V, (flags & LCE_FLAG_GRAD_W_FP32) != 0);
+}
+
+lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                               int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                               float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
+                               void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
+                               float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
+  // (V <= 2^22: the byte offsets inside a 256-row logits tile of the chunk stay 32-bit)
+  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 22) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
+  if (dtype != LCE_DTYPE_BF16) return LCE_ERR_DTYPE;
+  if (W == nullptr || loss_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
+  if (BT > 0 && (hidden == nullptr || targets == nullptr)) return LCE_ERR_NULL;
+  if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_SUM) return LCE_ERR_ARG;
+  if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
+  if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
+  if ((flags & ~(LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32)) != 0) return LCE_ERR_ARG;
+  if (!lce::aligned(hidden, 16) || !lce::aligned(W, 16) || !lce::aligned(grad_input, 16) ||
+      !lce::aligned(grad_W, 16) || !lce::aligned(workspace, 16) || !lce::aligned(bias, 2) ||
+      !lce::aligned(grad_b, 2) || !lce::aligned(targets, 8) || !lce::aligned(loss_out, 4) ||
+      !lce::aligned(n_valid_out, 8) || !lce::aligned(lse_out, 4))
+    return LCE_ERR_ALIGNMENT;
+  const bool gw32 = (flags & LCE_FLAG_GRAD_W_FP32) != 0;
+  if (workspace_bytes < lce::chunked_workspace_bytes(BT, H, V, gw32)) return LCE_ERR_WORKSPACE;
+  lce::FusedArgs a{};
+  a.hidden = hidden;
+  a.W = W;
+  a.bias = bias;
+  a.targets = targets;
+  a.BT = BT;
+  a.H = H;
+  a.V = V;
+  a.bf16 = true;
+  a.ignore_index = ignore_index;
+  a.mu = z_loss_mult;
+  a.mean = reduction == LCE_REDUCTION_MEAN;
+  a.loss_out = loss_out;
+  a.grad_input = grad_input;
+  a.grad_W = grad_W;
+  a.grad_b = grad_b;
+  a.n_valid_out = n_valid_out;
+  a.lse_out = lse_out;
+  bool bad = false;
+  if (lce::chunked_run(a, gw32, (flags & LCE_FLAG_CHECK_TARGETS) != 0, workspace, static_cast<hipStream_t>(stream),
+                       &bad) != hipSuccess)
+    return LCE_ERR_HIP;
+  return bad ? LCE_ERR_TARGET_RANGE : LCE_OK;
+}
+
 const char* lce_stage_name(int k) {
   if (k < 0 || k >= lce::kNumStages) return nullptr;
   return lce::kStageNames[k];
@@ -192,8 +245,8 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
   (void)es;
   if (workspace_bytes < lce::ce_workspace_bytes(B)) return LCE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (lce::launch_ce_inplace(logits, dtype == LCE_DTYPE_BF16, targets, B, V, ignore_index, z_loss_mult,
-                             ce_sum_out, z_sum_out, n_valid_out, workspace, st) != hipSuccess)
+  if (lce::launch_ce_inplace(logits, dtype == LCE_DTYPE_BF16, targets, B, V, V, ignore_index, z_loss_mult,
+                             ce_sum_out, z_sum_out, n_valid_out, nullptr, workspace, st) != hipSuccess)
     return LCE_ERR_HIP;
   return LCE_OK;
 }

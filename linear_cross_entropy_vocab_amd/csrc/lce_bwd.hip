@@ -985,6 +985,294 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
                    : launch_bwd_nb<T, true, false>(pl.nb, a, grid, st);
 }
 
+// ---------------------------------------------------------------------------
+// Gradient GEMMs on stored dlogits (the token-chunked composition of "Fused Linear
+// Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It", Strategy 1: a chunk of
+// tokens has its logits written to HBM, turned into dlogits in place by the standalone
+// cross-entropy kernel, and then consumed by the two gradient products).
+//
+// This is the GEMM3 half of the pipelined kernel above with the g tile read from HBM instead
+// of recomputed: a workgroup owns 64 stationary rows and an output column range of 4 * NCOL
+// columns (any H, in column chunks), streams 16-row tiles of X, and accumulates
+// acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL] per wave.  Loads go to LDS by buffer-to-LDS
+// DMA: each wave loads its own NB planes of the X tile (as in the pipelined kernel) and a
+// quarter of the 2 KiB g tile; one barrier per tile makes the g quarters visible to all.
+//   grad_input (DW = false): stationary = the chunk's tokens, X = W rows (the vocabulary,
+//     optionally split into ranges whose fp32 partial sums are added by mat_reduce_kernel);
+//     the g tile is G[64 tokens][16 vocab], kept as rows of 32 bytes per token.
+//   grad_W (DW = true): stationary = vocabulary rows, X = the chunk's hidden rows; the g tile
+//     is G[16 tokens][64 vocab], kept in the pipelined kernel's layout; the fp32 sum over
+//     chunks lives in `acc` (or in an fp32 output) and the last chunk writes c * sum; grad_b
+//     is the column sum of G, accumulated the same way.
+// ---------------------------------------------------------------------------
+template <bool DW, int NB>
+__global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
+  constexpr int NCOL = 32 * NB;
+  constexpr int XW = kPX * NCOL * 2;
+  constexpr int NQ = NB + 1;            // loads per tile and wave: NB planes + a g quarter
+  constexpr int kGBuf = kPBuf + 1;      // a g slot is refilled one iteration after its last read
+  constexpr int GT = kPX * 128;         // bytes of a g tile
+  __shared__ __attribute__((aligned(1024))) char xs[4][kPBuf][XW];
+  __shared__ __attribute__((aligned(1024))) char gs[kGBuf][GT];
+
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int q = lane >> 4, l16 = lane & 15;
+  const int tc = lane & 3, tr = (lane >> 2) & 3;
+  const int64_t nrt = (p.nS + kPS - 1) / kPS;
+  const int64_t total = nrt * p.hchunks * p.nsplit;
+  const int64_t id = xcd_remap(blockIdx.x, total);
+  const int64_t rt = id % nrt, rest = id / nrt;
+  const int hc = (int)(rest % p.hchunks), split = (int)(rest / p.hchunks);
+  const int64_t s0 = rt * kPS;
+  const int64_t H = p.H, row_bytes = H * 2, ldb = p.ld * 2;
+  const int kw0 = hc * 4 * NCOL + w * NCOL;
+  const int64_t xb0 = (int64_t)split * p.x_split;
+  const int64_t xe = (xb0 + p.x_split) < p.nX ? (xb0 + p.x_split) : p.nX;
+  const int64_t ntiles = xe > xb0 ? (xe - xb0 + kPX - 1) / kPX : 0;
+
+  f32x16_t acc[2][NB];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[sb][cb][r] = 0.f;
+
+  // X planes: as in the pipelined kernel (lane l lands on slot (row l/4, chunk l%4))
+  const int dn = lane >> 2, du = (lane & 3) ^ tsw(lane >> 2);
+  const uint32_t dma_off =
+      (kw0 + 8 * du < H) ? (uint32_t)(dn * row_bytes + (kw0 + 8 * du) * 2) : 0x80000000u;
+  // g quarter of this wave: lanes 0..31, 16 bytes each, landing at 512 w + 16 lane
+  uint32_t g_off;
+  if (DW) {  // row n = 4 w + lane/8 of G[16 tokens][64 vocab]; physical 32-byte group permuted
+    const int n = 4 * w + (lane >> 3), c = lane & 7;
+    const int lg = (c >> 1) ^ gsw2(n);
+    g_off = (uint32_t)(n * ldb + (16 * lg + 8 * (c & 1)) * 2);
+  } else {   // token row m = 16 w + lane/2 of G[64 tokens][16 vocab]
+    g_off = (uint32_t)((16 * w + (lane >> 1)) * ldb + 16 * (lane & 1));
+  }
+  char* const xw = xs[w][0];
+  auto lds_u32 = [](const char* ptr) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)ptr));
+  };
+  const uint32_t xw_lds = lds_u32(xw);
+  const uint32_t gs_lds = lds_u32(gs[0]) + 512u * (uint32_t)w;
+  auto x_rsrc = [&](int64_t tile) {
+    const int64_t x0 = xb0 + tile * kPX;
+    return make_rsrc_words(p.X + x0 * H, (xe - x0) * row_bytes);
+  };
+  auto g_rsrc = [&](int64_t tile) {
+    const int64_t x0 = xb0 + tile * kPX;
+    return DW ? make_rsrc_words(p.G + x0 * p.ld + s0, (p.g_rows - x0) * ldb - s0 * 2)
+              : make_rsrc_words(p.G + s0 * p.ld + x0, (p.g_rows - s0) * ldb - x0 * 2);
+  };
+  auto g_dma = [&](int64_t tile, int slot) {
+    const u32x4_t rg = g_rsrc(tile);
+    if (lane < 32) dma16(rg, gs_lds + (uint32_t)(slot * GT), g_off);
+  };
+  auto x_dma = [&](int64_t tile, int buf) {
+    DmaPlanes<0, NB>::run(x_rsrc(tile), xw_lds + (uint32_t)(buf * XW), dma_off);
+  };
+
+  // GEMM3 operand offsets (as in the pipelined kernel)
+  int o_g3[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int n = tq(2 * (q >> 1) + rd, tr);
+    const int u = 2 * (q & 1) + (tc >> 1);
+    o_g3[rd] = 64 * n + 16 * (u ^ tsw(n)) + 8 * (tc & 1);
+  }
+  int o_ga[2][2];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int n = tq(2 * (q >> 1) + rd, tr);
+      o_ga[sb][rd] = DW ? 128 * n + 32 * ((2 * sb + (q & 1)) ^ gsw2(n)) + 8 * tc
+                        : 32 * (32 * sb + (lane & 31)) + 16 * (lane >> 5);
+    }
+  // (DW) grad_b: lane (q, l16) of wave w sums g[n = 4q..4q+3][m = 16 w + l16]
+  const bool do_gb = DW && p.gb_acc != nullptr && hc == 0;
+  float gbs = 0.f;
+
+  if (ntiles > 0) {
+    const int64_t last = ntiles - 1;
+#pragma unroll
+    for (int b = 0; b < kPBuf; ++b) {
+      const int64_t t = b < last ? b : last;
+      g_dma(t, b);
+      x_dma(t, b);
+    }
+  }
+  for (int64_t i = 0; i < ntiles; ++i) {
+    const int bi = (int)(i % kPBuf), gi = (int)(i % kGBuf);
+    const int64_t nxt = i + kPBuf < ntiles ? i + kPBuf : ntiles - 1;
+    vm_wait<(kPBuf - 1) * NQ>();  // tile i has landed (tiles i+1 .. i+3 may be in flight)
+    __syncthreads();               // every quarter of g(i) is in LDS; slot (i-1) % 5 is free
+    g_dma(nxt, (int)((i + kPBuf) % kGBuf));
+    const char* gb = gs[gi];
+    const char* xb = xw + bi * XW;
+    Frag<bf16_t> ga[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if (DW) {
+        ga[sb].v = tr_pair(gb + o_ga[sb][0], gb + o_ga[sb][1]);
+      } else {
+        // tokens' rows hold vocabulary columns n = 0..15 in order; the B operand pairs its
+        // k index with the columns 0,1,4,5,2,3,6,7 (+8): swap the middle dwords
+        const uint4 r = *reinterpret_cast<const uint4*>(gb + o_ga[sb][0]);
+        ga[sb].v = __builtin_bit_cast(bf16x8_t, make_uint4(r.x, r.z, r.y, r.w));
+      }
+    }
+    if (do_gb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = 4 * q + j;
+        gbs += bf2f(*reinterpret_cast<const bf16_t*>(gb + 128 * n + 32 * (w ^ gsw2(n)) + 2 * l16));
+      }
+    }
+    const u32x4_t rx = x_rsrc(nxt);
+    const uint32_t lds_next = xw_lds + (uint32_t)(bi * XW);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      Frag<bf16_t> xf;
+      xf.v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
+      mfma_32x32x16(ga[0], xf, acc[0][cb]);
+      mfma_32x32x16(ga[1], xf, acc[1][cb]);
+      dma16_after(rx, lds_next + 1024 * cb, dma_off + 64 * cb, xf.v);
+    }
+  }
+  vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
+
+  const long long nvalid = *p.n_valid;
+  const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+  if (!DW) {
+    float* part = p.part + (int64_t)split * p.nS * H;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t col = kw0 + cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+          if (row < p.nS && col < H) part[row * H + col] = acc[sb][cb][r];
+        }
+      }
+  } else {
+    if (p.acc != nullptr || p.out != nullptr) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+          const int64_t col = kw0 + cb * 32 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+            if (row < p.nS && col < H) {
+              const int64_t k = row * H + col;
+              const float v = acc[sb][cb][r] + (p.first ? 0.f : p.acc[k]);
+              if (!p.last) p.acc[k] = v;
+              else if (p.out_f32) static_cast<float*>(p.out)[k] = cscale * v;
+              else static_cast<bf16_t*>(p.out)[k] = f2bf(cscale * v);
+            }
+          }
+        }
+    }
+    if (do_gb) {
+      gbs += __shfl_xor(gbs, 16, kWave);
+      gbs += __shfl_xor(gbs, 32, kWave);
+      const int64_t r = s0 + 16 * w + l16;
+      if (q == 0 && r < p.nS) {
+        const float v = gbs + (p.first ? 0.f : p.gb_acc[r]);
+        if (!p.last) p.gb_acc[r] = v;
+        else p.gb_out[r] = f2bf(cscale * v);
+      }
+    }
+  }
+}
+
+// grad_input rows of a chunk: c * (sum of the per-range partials), in bf16.
+__global__ void __launch_bounds__(256) mat_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                         int64_t n, int64_t stride, bf16_t* __restrict__ out,
+                                                         const int64_t* __restrict__ n_valid, int mean) {
+  const long long nvalid = *n_valid;
+  const float cscale = mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n;
+       i += (int64_t)gridDim.x * blockDim.x * 4) {
+    float4 a = *reinterpret_cast<const float4*>(part + i);
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(part + s * stride + i);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    *reinterpret_cast<uint2*>(out + i) =
+        make_uint2(pack_bf2(cscale * a.x, cscale * a.y), pack_bf2(cscale * a.z, cscale * a.w));
+  }
+}
+
+// Column blocks per wave for the stored-dlogits GEMMs: H <= 1024 in one chunk of 4 * 32 * NB
+// columns; larger H in chunks of 4 * 32 * NB with NB from {8, 6, 4}, the least padding first.
+void mat_plan(int64_t H, int* nb, int* hchunks) {
+  if (H <= 1024) {
+    const int64_t per = (H + 127) / 128;
+    *nb = per <= 1 ? 1 : (per <= 2 ? 2 : (per <= 4 ? 4 : (per <= 6 ? 6 : 8)));
+    *hchunks = 1;
+    return;
+  }
+  int best_nb = 8;
+  int64_t best_waste = -1;
+  for (int cand : {8, 6, 4}) {
+    const int64_t w = 128 * cand;
+    const int64_t waste = (H + w - 1) / w * w - H;
+    if (best_waste < 0 || waste < best_waste) {
+      best_waste = waste;
+      best_nb = cand;
+    }
+  }
+  *nb = best_nb;
+  *hchunks = (int)((H + 128 * best_nb - 1) / (128 * best_nb));
+}
+
+template <bool DW>
+static hipError_t launch_mat_dw(int nb, const MatArgs& a, dim3 grid, hipStream_t st) {
+  switch (nb) {
+    case 1: hipLaunchKernelGGL((mat_gemm_kernel<DW, 1>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((mat_gemm_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((mat_gemm_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((mat_gemm_kernel<DW, 6>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((mat_gemm_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mat_gemm(bool dw, const MatArgs& a, hipStream_t st) {
+  int nb = 0, hc = 0;
+  mat_plan(a.H, &nb, &hc);
+  if (hc != a.hchunks || a.nsplit < 1 || (a.x_split % kPX) != 0) return hipErrorInvalidValue;
+  const int64_t nrt = (a.nS + kPS - 1) / kPS;
+  const int64_t total = nrt * a.hchunks * a.nsplit;
+  if (total == 0) return hipSuccess;
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)total);
+  return dw ? launch_mat_dw<true>(nb, a, grid, st) : launch_mat_dw<false>(nb, a, grid, st);
+}
+
+hipError_t launch_mat_reduce(const float* part, int nsplit, int64_t rows, int64_t H, bf16_t* out,
+                             const int64_t* n_valid, bool mean, hipStream_t st) {
+  const int64_t n = rows * H;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(mat_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, nsplit, n, n, out,
+                     n_valid, mean ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.grad_input == nullptr || a.BT == 0) return hipSuccess;
   return a.bf16 ? launch_bwd<bf16_t>(a, w, false, st) : launch_bwd<float>(a, w, false, st);

@@ -21,6 +21,7 @@ struct CERowOut {
   float* ce;     // [B] LSE - x_y (0 for ignored rows)
   float* zsq;    // [B] LSE^2     (0 for ignored rows)
   int32_t* valid;  // [B] 1 if the row counts
+  float* lse;    // [B] LSE of every row, or NULL
 };
 
 template <typename T>
@@ -79,14 +80,36 @@ __device__ __forceinline__ void block_ms(float& m, float& s, float* sm, float* s
   for (int i = 0; i < kCEWaves; ++i) ms_merge(m, s, sm[i], ss[i]);  // same order in every thread
 }
 
+// Lanes of vector index j whose elements lie at or past V get -inf there (rows are read
+// with the padded row length ld as the bound, so those elements are zero or padding).
+template <typename T>
+__device__ __forceinline__ void mask_tail(Vec16<T>& v, int64_t c0, int64_t V);
+template <>
+__device__ __forceinline__ void mask_tail(Vec16<bf16_t>& v, int64_t c0, int64_t V) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t& x = (&v.raw.x)[d];
+    const uint32_t lo = (c0 + 2 * d < V) ? (x & 0x0000ffffu) : 0x0000ff80u;
+    const uint32_t hi = (c0 + 2 * d + 1 < V) ? (x & 0xffff0000u) : 0xff800000u;
+    x = lo | hi;
+  }
+}
+template <>
+__device__ __forceinline__ void mask_tail(Vec16<float>& v, int64_t c0, int64_t V) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) (&v.raw.x)[d] = (c0 + d < V) ? (&v.raw.x)[d] : 0xff800000u;
+}
+
 // Row cached in registers: NV vectors of 16 B per thread, all loaded before any is used
-// (buffer loads: bytes past the row read as zero and stores there are dropped).  Only the
-// last vector index can run past the row; those lanes replace it with -inf so neither pass
-// needs a per-element mask.  exp(x - c) is evaluated as exp2(x * log2(e) - c * log2(e)).
+// (buffer loads: bytes past the row read as zero and stores there are dropped).  NV is the
+// per-thread vector count rounded up to a power of two, so every vector index below NV/2 is
+// inside the row; the upper half is masked per element (-inf past V), so neither pass needs
+// a mask.  Rows are ld elements apart (ld >= V; ld * sizeof(T) a multiple of 16); the
+// columns V..ld-1 are written as 0.  exp(x - c) is evaluated as exp2(x * log2(e) - c * log2(e)).
 template <typename T, int NV>
 __global__ void __launch_bounds__(kCEThreads) ce_rows_cached(T* __restrict__ logits,
                                                               const int64_t* __restrict__ targets,
-                                                              int64_t V, int64_t ignore_index,
+                                                              int64_t V, int64_t ld, int64_t ignore_index,
                                                               float mu, CERowOut out) {
   constexpr int EPV = Vec16<T>::N;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -95,32 +118,25 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_cached(T* __restrict__ log
   constexpr int64_t kSlice = (int64_t)kCEThreads * 16;
   __shared__ float sm[kCEWaves], ss[kCEWaves];
   const int64_t row = blockIdx.x;
-  T* x = logits + row * V;
+  T* x = logits + row * ld;
   const int tid = threadIdx.x;
   const int64_t y = targets[row];
   const bool valid = (y != ignore_index) && (y >= 0) && (y < V);
-  const int64_t row_bytes = V * (int64_t)sizeof(T);
+  const int64_t row_bytes = ld * (int64_t)sizeof(T);
   const uint32_t lane_off = (uint32_t)tid * 16u;
 
   // x_y for the row result (thread 0 only; other lanes read past the end and get 0)
   const float xy = Vec16<T>::elem(make_rsrc(x, row_bytes),
                                   (tid == 0 && valid) ? (uint32_t)(y * (int64_t)sizeof(T)) : 0xfffffff0u);
   Vec16<T> buf[NV];
-  // the possibly partial last vector first, so its fix-up waits for one load only
-  buf[NV - 1].raw = load16(make_rsrc((const char*)x + (NV - 1) * kSlice, row_bytes - (NV - 1) * kSlice), lane_off);
+  // the possibly partial upper vectors first (last one first), so their fix-up waits for as
+  // few loads as possible
+  constexpr int JM = NV / 2;  // vectors JM .. NV-1 may run past V
 #pragma unroll
-  for (int j = 0; j < NV - 1; ++j)
+  for (int j = NV - 1; j >= 0; --j)
     buf[j].raw = load16(make_rsrc((const char*)x + j * kSlice, row_bytes - j * kSlice), lane_off);
-  {
-    const int nvec = (int)(V / EPV);  // V * sizeof(T) is a multiple of 16 on this path
-    const uint32_t keep = ((NV - 1) * kCEThreads + tid < nvec) ? 0xffffffffu : 0u;
-    const uint4 ni = Vec16<T>::neg_inf();
-    uint4& r = buf[NV - 1].raw;
-    r.x = (r.x & keep) | (ni.x & ~keep);
-    r.y = (r.y & keep) | (ni.y & ~keep);
-    r.z = (r.z & keep) | (ni.z & ~keep);
-    r.w = (r.w & keep) | (ni.w & ~keep);
-  }
+#pragma unroll
+  for (int j = NV - 1; j >= JM; --j) mask_tail(buf[j], ((int64_t)j * kCEThreads + tid) * EPV, V);
 
   float m = -INFINITY;
 #pragma unroll
@@ -159,10 +175,75 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_cached(T* __restrict__ log
     out.ce[row] = valid ? (lse - xy) : 0.f;
     out.zsq[row] = valid ? lse * lse : 0.f;
     out.valid[row] = valid ? 1 : 0;
+    if (out.lse != nullptr) out.lse[row] = lse;
   }
 }
 
-// Any V: two passes over global memory (the second read usually hits the last-level cache).
+// Rows too long for the register cache, 16-byte aligned: two passes over global memory in
+// 16-byte vectors (the second read usually hits the last-level cache); elements past V are
+// masked to -inf and the padding columns are written as 0.
+template <typename T>
+__global__ void __launch_bounds__(kCEThreads) ce_rows_stream_vec(T* __restrict__ logits,
+                                                                  const int64_t* __restrict__ targets,
+                                                                  int64_t V, int64_t ld, int64_t ignore_index,
+                                                                  float mu, CERowOut out) {
+  constexpr int EPV = Vec16<T>::N;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float sm[kCEWaves], ss[kCEWaves];
+  const int64_t row = blockIdx.x;
+  T* x = logits + row * ld;
+  const int tid = threadIdx.x;
+  const int64_t y = targets[row];
+  const bool valid = (y != ignore_index) && (y >= 0) && (y < V);
+  const int64_t row_bytes = ld * (int64_t)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(x, row_bytes);
+  const int64_t nvec = (V + EPV - 1) / EPV;
+  const float xy = Vec16<T>::elem(rs, (tid == 0 && valid) ? (uint32_t)(y * (int64_t)sizeof(T)) : 0xfffffff0u);
+  float m = -INFINITY, s = 0.f;
+  for (int64_t j = tid; j < nvec; j += kCEThreads) {
+    Vec16<T> v;
+    v.raw = load16(rs, (uint32_t)(j * 16));
+    mask_tail(v, j * EPV, V);
+    float vm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, v.get(e));
+    if (vm > m) {
+      s *= __builtin_amdgcn_exp2f((m - vm) * kLog2e);
+      m = vm;
+    }
+    if (m != -INFINITY) {
+      const float ml = m * kLog2e;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) s += __builtin_amdgcn_exp2f(fmaf(v.get(e), kLog2e, -ml));
+    }
+  }
+  if (m == -INFINITY) s = 0.f;
+  block_ms(m, s, sm, ss);
+  const float lse = m + __logf(s);
+  const float scale = valid ? (1.f + 2.f * mu * lse) : 0.f;
+  const float ll = lse * kLog2e;
+  const int64_t nvec_ld = ld / EPV;
+  for (int64_t j = tid; j < nvec_ld; j += kCEThreads) {
+    Vec16<T> v;
+    v.raw = load16(rs, (uint32_t)(j * 16));
+    mask_tail(v, j * EPV, V);
+    float d[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      d[e] = __builtin_amdgcn_exp2f(fmaf(v.get(e), kLog2e, -ll)) * scale;
+      if (valid && j * EPV + e == y) d[e] -= 1.f;
+    }
+    store16(rs, (uint32_t)(j * 16), pack_out(d, T()));
+  }
+  if (tid == 0) {
+    out.ce[row] = valid ? (lse - xy) : 0.f;
+    out.zsq[row] = valid ? lse * lse : 0.f;
+    out.valid[row] = valid ? 1 : 0;
+    if (out.lse != nullptr) out.lse[row] = lse;
+  }
+}
+
+// Any V: two passes over global memory, element by element (rows not 16-byte aligned).
 template <typename T>
 __global__ void __launch_bounds__(kCEThreads) ce_rows_stream(T* __restrict__ logits,
                                                               const int64_t* __restrict__ targets,
@@ -197,6 +278,7 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_stream(T* __restrict__ log
     out.ce[row] = valid ? (lse - xy) : 0.f;
     out.zsq[row] = valid ? lse * lse : 0.f;
     out.valid[row] = valid ? 1 : 0;
+    if (out.lse != nullptr) out.lse[row] = lse;
   }
 }
 
@@ -232,29 +314,34 @@ __global__ void __launch_bounds__(kCEThreads) ce_reduce(const float* __restrict_
 }
 
 template <typename T>
-static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int64_t V,
+static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int64_t V, int64_t ld,
                               int64_t ignore_index, float mu, CERowOut out, hipStream_t st) {
   constexpr int EPV = 16 / (int)sizeof(T);
-  const bool vec_ok = ((V * (int64_t)sizeof(T)) % 16) == 0;
-  const int64_t nvec = V / EPV;
+  const bool vec_ok = ((ld * (int64_t)sizeof(T)) % 16) == 0 &&
+                      (reinterpret_cast<uintptr_t>(logits) % 16) == 0;
+  const int64_t nvec = (V + EPV - 1) / EPV;
   const int64_t per = (nvec + kCEThreads - 1) / kCEThreads;
   dim3 grid((unsigned)B), block(kCEThreads);
   if (vec_ok && per <= 16) {
-    if (per <= 1) hipLaunchKernelGGL((ce_rows_cached<T, 1>), grid, block, 0, st, logits, targets, V, ignore_index, mu, out);
-    else if (per <= 2) hipLaunchKernelGGL((ce_rows_cached<T, 2>), grid, block, 0, st, logits, targets, V, ignore_index, mu, out);
-    else if (per <= 4) hipLaunchKernelGGL((ce_rows_cached<T, 4>), grid, block, 0, st, logits, targets, V, ignore_index, mu, out);
-    else if (per <= 8) hipLaunchKernelGGL((ce_rows_cached<T, 8>), grid, block, 0, st, logits, targets, V, ignore_index, mu, out);
-    else hipLaunchKernelGGL((ce_rows_cached<T, 16>), grid, block, 0, st, logits, targets, V, ignore_index, mu, out);
+    if (per <= 1) hipLaunchKernelGGL((ce_rows_cached<T, 1>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
+    else if (per <= 2) hipLaunchKernelGGL((ce_rows_cached<T, 2>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
+    else if (per <= 4) hipLaunchKernelGGL((ce_rows_cached<T, 4>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
+    else if (per <= 8) hipLaunchKernelGGL((ce_rows_cached<T, 8>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
+    else hipLaunchKernelGGL((ce_rows_cached<T, 16>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
+  } else if (vec_ok) {
+    hipLaunchKernelGGL((ce_rows_stream_vec<T>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
   } else {
+    if (ld != V) return hipErrorInvalidValue;  // padded rows are always 16-byte aligned
     hipLaunchKernelGGL((ce_rows_stream<T>), grid, block, 0, st, logits, targets, V, ignore_index, mu, out);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, int64_t B, int64_t V,
-                             int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
-                             int64_t* n_valid, void* workspace, hipStream_t st) {
+                             int64_t ld, int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
+                             int64_t* n_valid, float* lse_rows, void* workspace, hipStream_t st) {
   CERowOut out;
+  out.lse = lse_rows;
   char* ws = static_cast<char*>(workspace);
   const size_t a = ws_align((size_t)B * 4);
   out.ce = reinterpret_cast<float*>(ws);
@@ -262,8 +349,8 @@ hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, in
   out.valid = reinterpret_cast<int32_t*>(ws + 2 * a);
   hipError_t e = hipSuccess;
   if (B > 0) {
-    e = bf16 ? launch_rows<bf16_t>(static_cast<bf16_t*>(logits), targets, B, V, ignore_index, mu, out, st)
-             : launch_rows<float>(static_cast<float*>(logits), targets, B, V, ignore_index, mu, out, st);
+    e = bf16 ? launch_rows<bf16_t>(static_cast<bf16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, st)
+             : launch_rows<float>(static_cast<float*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(ce_reduce, dim3(1), dim3(kCEThreads), 0, st, out.ce, out.zsq, out.valid, B,

@@ -1,0 +1,180 @@
+// Token-chunked composition of linear cross-entropy ("Fused Linear Cross-Entropy: The Math,
+// the Memory Wall, and Two Ways Around It", Strategy 1 and "The chunk-size trick"; "Greyhound
+// -- Cross-Entropy", "Relationship to Chunked Linear Loss"):
+//
+//   for each chunk of cs tokens:
+//     logits chunk  z = h_chunk W^T + b           (MFMA GEMM, bf16 into one reused buffer)
+//     in place      z <- valid * (softmax(z)(1 + 2 mu LSE) - onehot(y))   (standalone CE)
+//     grad_input[chunk] = c * z . W                (GEMM on the stored dlogits)
+//     grad_W += z^T . h_chunk,  grad_b += column sums of z   (fp32 sums over the chunks)
+//   loss = c * sum over chunks of (ce_sum + mu z_sum)
+//
+// No logits are recomputed (6 BT V H flops in all), at the price of one bf16 logits chunk and
+// an fp32 grad_W accumulator in device memory.  c = 1 / max(n_valid, 1) (mean) or 1 (sum) is
+// known before the first chunk from the target pre-pass, so grad_input rows are final as soon
+// as their chunk is done.
+#include <algorithm>
+
+#include "lce_common.h"
+#include "lce_launch.h"
+
+namespace lce {
+
+// Rows per chunk: the pages' rule sizes an fp32 chunk as next_pow2(ceil(BT / ceil(V / H)))
+// rows; the bf16 buffer of the same byte size holds twice as many.  Rows are padded to a
+// multiple of 64 elements (16-byte aligned rows for the vector loads).
+ChunkPlan chunk_plan(int64_t BT, int64_t H, int64_t V) {
+  ChunkPlan c;
+  const int64_t inc = (V + H - 1) / H;
+  const int64_t want = (BT + inc - 1) / inc;
+  int64_t p2 = 1;
+  while (p2 < want) p2 <<= 1;
+  c.cs = std::max<int64_t>(1, std::min<int64_t>(2 * p2, BT));
+  c.ld = (V + 63) / 64 * 64;
+  c.nchunks = BT > 0 ? (BT + c.cs - 1) / c.cs : 0;
+  mat_plan(H, &c.nb, &c.hchunks);
+  // grad_input: enough vocabulary ranges for about two workgroups per compute unit
+  const int64_t base = ((c.cs + 63) / 64) * c.hchunks;
+  int64_t ns = (512 + base - 1) / base;
+  const int64_t max_ns = std::max<int64_t>(1, (V + 1023) / 1024);  // at least 64 tiles per range
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_ns, 64)));
+  c.x_split = ((V + ns - 1) / ns + 15) / 16 * 16;
+  c.nsplit = (int)((V + c.x_split - 1) / c.x_split);
+  return c;
+}
+
+size_t chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool grad_w_fp32) {
+  const ChunkPlan c = chunk_plan(BT, H, V);
+  const int64_t nch = std::max<int64_t>(1, c.nchunks);
+  size_t n = ws_align(16);                                   // n_valid, n_bad
+  n += ws_align((size_t)c.cs * (size_t)c.ld * 2);            // logits / dlogits chunk
+  n += ws_align(ce_workspace_bytes(c.cs));                   // per-row CE results
+  n += 2 * ws_align((size_t)nch * 4) + ws_align((size_t)nch * 8);  // per-chunk sums
+  n += ws_align((size_t)c.nsplit * (size_t)c.cs * (size_t)H * 4);  // grad_input partials
+  if (!grad_w_fp32) n += ws_align((size_t)V * (size_t)H * 4);       // grad_W fp32 sum
+  n += ws_align((size_t)V * 4);                              // grad_b fp32 sum
+  return n;
+}
+
+// loss = c * sum_k (ce_k + mu z_k) over the chunks in order, in fp64.
+__global__ void chunk_loss_kernel(const float* __restrict__ ce, const float* __restrict__ z, int64_t nch,
+                                  const int64_t* __restrict__ n_valid, float mu, int mean, float* loss_out,
+                                  int64_t* n_valid_out) {
+  if (threadIdx.x != 0) return;
+  double a = 0.0, b = 0.0;
+  for (int64_t k = 0; k < nch; ++k) {
+    a += (double)ce[k];
+    b += (double)z[k];
+  }
+  const long long n = *n_valid;
+  const double c = mean ? 1.0 / (double)(n > 1 ? n : 1) : 1.0;
+  *loss_out = (float)(c * (a + (double)mu * b));
+  if (n_valid_out) *n_valid_out = n;
+}
+
+// Launch sequence of the chunked call (arguments validated by the caller; bf16 only).
+// *bad_targets is set when check_targets found an out-of-range target (nothing after the
+// pre-pass is launched then).
+hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets, void* workspace,
+                       hipStream_t st, bool* bad_targets) {
+  *bad_targets = false;
+  const ChunkPlan c = chunk_plan(a.BT, a.H, a.V);
+  const int64_t nch = std::max<int64_t>(1, c.nchunks);
+  char* p = static_cast<char*>(workspace);
+  FusedWs w{};
+  w.n_valid = reinterpret_cast<int64_t*>(p);
+  w.n_bad = reinterpret_cast<int32_t*>(p + 8);
+  p += ws_align(16);
+  bf16_t* zbuf = reinterpret_cast<bf16_t*>(p);
+  p += ws_align((size_t)c.cs * (size_t)c.ld * 2);
+  void* ce_ws = p;
+  p += ws_align(ce_workspace_bytes(c.cs));
+  float* ce_k = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)nch * 4);
+  float* z_k = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)nch * 4);
+  int64_t* nv_k = reinterpret_cast<int64_t*>(p);
+  p += ws_align((size_t)nch * 8);
+  float* part = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)c.nsplit * (size_t)c.cs * (size_t)a.H * 4);
+  float* gw_acc = nullptr;
+  if (!grad_w_fp32) {
+    gw_acc = reinterpret_cast<float*>(p);
+    p += ws_align((size_t)a.V * (size_t)a.H * 4);
+  } else {
+    gw_acc = static_cast<float*>(a.grad_W);
+  }
+  float* gb_acc = reinterpret_cast<float*>(p);
+
+  // target pre-pass: n_valid (so c is known to every chunk) and the range check
+  FusedArgs t = a;
+  t.bias = nullptr;
+  t.filter_counts = nullptr;
+  hipError_t e = launch_targets(t, w, st);
+  if (e != hipSuccess) return e;
+  if (check_targets) {
+    int32_t bad = 0;
+    if ((e = hipMemcpyAsync(&bad, w.n_bad, sizeof(bad), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+    if (bad != 0) {
+      *bad_targets = true;
+      return hipSuccess;
+    }
+  }
+  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bool want_dw = a.grad_W != nullptr || a.grad_b != nullptr;
+  // (an empty batch still runs one chunk of 0 rows, which writes zero gradients)
+  for (int64_t k = 0; k < nch; ++k) {
+    const int64_t r0 = k * c.cs;
+    const int64_t rows = std::max<int64_t>(0, std::min<int64_t>(c.cs, a.BT - r0));
+    const bf16_t* hk = h + r0 * a.H;
+    if ((e = launch_logits_chunk(W, hk, static_cast<const bf16_t*>(a.bias), rows, a.H, a.V, zbuf, c.ld, st)) !=
+        hipSuccess)
+      return e;
+    if ((e = launch_ce_inplace(zbuf, true, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k,
+                               z_k + k, nv_k + k, a.lse_out ? a.lse_out + r0 : nullptr, ce_ws, st)) != hipSuccess)
+      return e;
+    MatArgs m{};
+    m.G = zbuf;
+    m.ld = c.ld;
+    m.g_rows = rows;
+    m.H = a.H;
+    m.hchunks = c.hchunks;
+    m.n_valid = w.n_valid;
+    m.mean = a.mean ? 1 : 0;
+    if (a.grad_input != nullptr) {
+      m.X = W;
+      m.nS = rows;
+      m.nX = a.V;
+      m.x_split = c.x_split;
+      m.nsplit = c.nsplit;
+      m.part = part;
+      if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
+      if ((e = launch_mat_reduce(part, c.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + r0 * a.H,
+                                 w.n_valid, a.mean, st)) != hipSuccess)
+        return e;
+    }
+    if (want_dw) {
+      m.X = hk;
+      m.nS = a.V;
+      m.nX = rows;
+      m.x_split = (rows + 15) / 16 * 16;
+      m.nsplit = 1;
+      m.part = nullptr;
+      m.acc = a.grad_W != nullptr ? gw_acc : nullptr;
+      m.out = a.grad_W;
+      m.out_f32 = grad_w_fp32 ? 1 : 0;
+      m.first = k == 0 ? 1 : 0;
+      m.last = k == nch - 1 ? 1 : 0;
+      m.gb_acc = a.grad_b != nullptr ? gb_acc : nullptr;
+      m.gb_out = static_cast<bf16_t*>(a.grad_b);
+      if ((e = launch_mat_gemm(true, m, st)) != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(64), 0, st, ce_k, z_k, nch, w.n_valid, a.mu,
+                     a.mean ? 1 : 0, a.loss_out, a.n_valid_out);
+  return hipGetLastError();
+}
+
+}  // namespace lce

@@ -168,6 +168,13 @@ __device__ __forceinline__ void vm_wait() {
 }
 __device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Workgroups are dealt round-robin to the 8 XCDs; this gives each XCD a contiguous range of
+// the logical tile order (0 .. n-1), so workgroups that share operand tiles share an L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t n) {
+  const int64_t x = id % 8, q = id / 8, Q = n / 8, r = n % 8;
+  return (x < r) ? x * (Q + 1) + q : r * (Q + 1) + (x - r) * Q + q;
+}
+
 // Index of the calling wave within its workgroup, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64)); }
 __device__ __forceinline__ void load8(Frag<bf16_t>& f, __amdgpu_buffer_rsrc_t r, uint32_t off) {

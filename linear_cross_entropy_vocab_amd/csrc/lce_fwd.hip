@@ -73,12 +73,6 @@ constexpr int kFwdThreads = 256;
 constexpr int kStageBytes = 128;          // K bytes per row per stage
 constexpr int kLdsRow = kStageBytes + 16; // padded LDS row stride (bank-conflict free 16 B reads)
 
-__device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t n) {
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of
-  // the tile order so workgroups sharing operand tiles share an L2.
-  const int64_t x = id % 8, q = id / 8, Q = n / 8, r = n % 8;
-  return (x < r) ? x * (Q + 1) + q : r * (Q + 1) + (x - r) * Q + q;
-}
 
 template <typename T>
 __global__ void __launch_bounds__(kFwdThreads) fwd_lse_kernel(const T* __restrict__ W,
@@ -232,12 +226,18 @@ constexpr int kFwdTileT2 = 256;
 // 16 consecutive rows.
 __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// STORE: instead of the (max, sum-exp) epilogue, the logits tile z + b is written in bf16 to
+// zout[t][v] (rows ld elements apart, ld a multiple of 64 and >= V; columns V..ld-1 are
+// written as 0): the logits chunk of the token-chunked composition ("Fused Linear
+// Cross-Entropy: ...", Strategy 1).
+template <bool STORE>
 __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16_t* __restrict__ W,
                                                                     const bf16_t* __restrict__ h,
                                                                     const bf16_t* __restrict__ bias,
                                                                     int64_t BT, int64_t H, int64_t V,
                                                                     int64_t nt_v, int64_t nt_t,
-                                                                    float* __restrict__ lse_part) {
+                                                                    float* __restrict__ lse_part,
+                                                                    bf16_t* __restrict__ zout, int64_t ld) {
   constexpr int ROWB = 128;                       // bytes of one row per stage
   constexpr int TILE_A = kFwdTileV * ROWB;        // 32 KiB
   constexpr int TILE_B = kFwdTileT2 * ROWB;       // 32 KiB
@@ -352,13 +352,60 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       buf ^= 1;
     }
 
-    // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
-    // two lane halves, then the two vocabulary halves of the tile; rows past V (only in the
-    // last vocabulary tile) are skipped.
     const int vlim = (int)((V - tl.v0) < kFwdTileV ? (V - tl.v0) : kFwdTileV);
     int ln = lane;
     asm volatile("" : "+v"(ln));  // keeps the row indices below from being hoisted out of the loop
     const int vrow = wv * 128 + 4 * (ln >> 5);
+    if constexpr (STORE) {
+      // Lane (t, half) holds, per 32-row block vb, vocabulary rows 8 rr + 4 half + 0..3 for
+      // rr = 0..3.  Lanes t and t + 32 swap halves so that each owns whole 8-row runs
+      // (rr = 2 p + half, p = 0, 1) and writes them as 16-byte stores along the token's row.
+      const int half = ln >> 5;
+      const int64_t tcol0 = tl.t0 + wt * 64;
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + tl.t0 * ld, (BT - tl.t0) * ld * 2);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int trow = (int)(tcol0 - tl.t0) + tb * 32 + (ln & 31);
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) {
+          uint32_t pk[4][2];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            float f[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int vr = vrow + vb * 32 + 8 * rr + e;
+              f[e] = vr < vlim ? acc[vb][tb][4 * rr + e] + s_bias[vr] : 0.f;
+            }
+            pk[rr][0] = pack_bf2(f[0], f[1]);
+            pk[rr][1] = pack_bf2(f[2], f[3]);
+          }
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            // keep run 2 pp + half, send run 2 pp + (1 - half)
+            const uint32_t k0 = half ? pk[2 * pp + 1][0] : pk[2 * pp][0];
+            const uint32_t k1 = half ? pk[2 * pp + 1][1] : pk[2 * pp][1];
+            const uint32_t s0 = half ? pk[2 * pp][0] : pk[2 * pp + 1][0];
+            const uint32_t s1 = half ? pk[2 * pp][1] : pk[2 * pp + 1][1];
+            const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, kWave);
+            const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32, kWave);
+            // the run's first four rows come from the lane with half = 0
+            const uint4 v = half ? make_uint4(r0, r1, k0, k1) : make_uint4(k0, k1, r0, r1);
+            const int64_t vcol = tl.v0 + wv * 128 + vb * 32 + 8 * (2 * pp + half);
+            if (vcol < ld) store16(rz, (uint32_t)(trow * ld * 2 + vcol * 2), v);
+          }
+        }
+      }
+      (void)lse_part;
+      __syncthreads();  // every wave is done with s_bias before the next tile rewrites it
+      if (!has_next) break;
+      blk = nblk;
+      tl = tn;
+      continue;
+    }
+    // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
+    // two lane halves, then the two vocabulary halves of the tile; rows past V (only in the
+    // last vocabulary tile) are skipped.
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       float m = -INFINITY;
@@ -417,9 +464,9 @@ hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) 
   if (a.BT == 0) return hipSuccess;
   if (a.bf16) {
     const int64_t nt_t2 = (a.BT + kFwdTileT2 - 1) / kFwdTileT2;
-    hipLaunchKernelGGL(fwd_lse_dma_kernel, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0, st,
+    hipLaunchKernelGGL(fwd_lse_dma_kernel<false>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0, st,
                        (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
-                       a.V, w.nt, nt_t2, w.lse_part);
+                       a.V, w.nt, nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0);
     return hipGetLastError();
   }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
@@ -565,6 +612,21 @@ __global__ void __launch_bounds__(kLossThreads) loss_kernel(const double* __rest
 hipError_t launch_loss(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(kLossThreads), 0, st, w.blk, w.blk + w.nblk, w.nblk,
                      w.n_valid, a.mu, a.mean ? 1 : 0, a.loss_out, a.n_valid_out);
+  return hipGetLastError();
+}
+
+}  // namespace lce
+
+namespace lce {
+
+// Logits of a token chunk: zout[t][v] = (h_chunk W^T + b)[t][v] in bf16, rows ld apart.
+hipError_t launch_logits_chunk(const bf16_t* W, const bf16_t* h_chunk, const bf16_t* bias, int64_t rows,
+                               int64_t H, int64_t V, bf16_t* zout, int64_t ld, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
+  const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<true>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0, st,
+                     W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, zout, ld);
   return hipGetLastError();
 }
 

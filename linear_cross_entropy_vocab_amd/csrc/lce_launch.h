@@ -64,10 +64,47 @@ hipError_t launch_loss(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_bwd_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_bwd_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 
+// Gradient GEMMs on stored (unscaled) dlogits G [g_rows][ld] of one token chunk.
+struct MatArgs {
+  const uint16_t* X;  // streamed rows [nX][H] (bf16): W (grad_input) or the chunk's hidden (grad_W)
+  const uint16_t* G;  // dlogits of the chunk, row-major [g_rows][ld] (bf16)
+  int64_t ld, g_rows, H;
+  int64_t nS, nX;     // stationary rows (chunk tokens, resp. V) and streamed rows (V, resp. chunk tokens)
+  int64_t x_split;    // streamed rows per split (multiple of 16)
+  int nsplit, hchunks;
+  float* part;        // grad_input: [nsplit][nS][H] fp32 partial sums
+  float* acc;         // grad_W: [V][H] fp32 sum over the chunks so far (may equal out when out_f32)
+  void* out;          // grad_W output (written by the last chunk, scaled by c), or NULL
+  int out_f32, first, last;
+  float* gb_acc;      // grad_b: [V] fp32 sum over chunks, or NULL (no grad_b)
+  uint16_t* gb_out;   // grad_b output (bf16)
+  const int64_t* n_valid;
+  int mean;
+};
+void mat_plan(int64_t H, int* nb, int* hchunks);
+hipError_t launch_mat_gemm(bool dw, const MatArgs& a, hipStream_t st);
+hipError_t launch_mat_reduce(const float* part, int nsplit, int64_t rows, int64_t H, uint16_t* out,
+                             const int64_t* n_valid, bool mean, hipStream_t st);
+hipError_t launch_logits_chunk(const uint16_t* W, const uint16_t* h_chunk, const uint16_t* bias, int64_t rows,
+                               int64_t H, int64_t V, uint16_t* zout, int64_t ld, hipStream_t st);
+
+// Token-chunked composition (bf16): chunk rows, padded row length of the logits chunk, and
+// the plan of the gradient GEMMs on it.
+struct ChunkPlan {
+  int64_t cs, ld, nchunks, x_split;
+  int nsplit, nb, hchunks;
+};
+ChunkPlan chunk_plan(int64_t BT, int64_t H, int64_t V);
+size_t chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool grad_w_fp32);
+hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets, void* workspace,
+                       hipStream_t st, bool* bad_targets);
+
 // Standalone cross-entropy.
 size_t ce_workspace_bytes(int64_t B);
+// Rows are ld >= V elements apart; with ld > V the rows must be 16-byte aligned and the
+// columns V..ld-1 are overwritten with 0.
 hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, int64_t B, int64_t V,
-                             int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
-                             int64_t* n_valid, void* workspace, hipStream_t st);
+                             int64_t ld, int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
+                             int64_t* n_valid, float* lse_rows, void* workspace, hipStream_t st);
 
 }  // namespace lce
