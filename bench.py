@@ -116,6 +116,32 @@ def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT) -> dict:
             "loss_equal": bool(torch.equal(out["loss"], exact["loss"]))}
 
 
+def bench_chunked(lce, torch, h, W, b, y, kw, exact, steps, BT) -> dict:
+    """The token-chunked composition on the same workload: time per step, its extra device
+    memory, and how far its results are from the fused path's (relative differences)."""
+    ckw = {k: v for k, v in kw.items() if k not in ("workspace", "out")}
+    r = lce.lce_fwd_bwd(h, W, b, y, method="chunked", **ckw)
+    torch.cuda.synchronize()
+    out = {k: r[k] for k in ("loss", "grad_input", "grad_weight", "grad_bias", "n_valid") if r[k] is not None}
+    ws = r["workspace"]
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lce.lce_fwd_bwd(h, W, b, y, method="chunked", workspace=ws, out=out, **ckw)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    def rdiff(a, c):
+        a = a.float()
+        c = c.float()
+        return float((a - c).norm() / c.norm())
+
+    diffs = {k: rdiff(out[k], exact[k]) for k in ("grad_input", "grad_weight", "grad_bias")
+             if out.get(k) is not None and exact.get(k) is not None}
+    diffs["loss"] = abs(out["loss"].item() - exact["loss"].item()) / abs(exact["loss"].item())
+    return {"ms_per_step": ms, "tokens_per_s": BT / (ms * 1e-3), "workspace_bytes": int(ws.numel()),
+            "rel_diff_vs_fused": diffs}
+
+
 def cpu_baseline(inp, n_tokens: int) -> dict:
     """The float64 oracle (as it stands) on the first n_tokens rows of the same workload."""
     import oracle
@@ -177,6 +203,10 @@ def main():
                     help="only measure gradient filtering on the Zipf-target workloads (Gemma-like, "
                          "Qwen-like) and print one JSON line per workload")
     ap.add_argument("--filter-eps", type=float, default=FILTER_EPS)
+    ap.add_argument("--no-chunked", action="store_true", help="skip the token-chunked composition leg")
+    ap.add_argument("--compare-methods", action="store_true",
+                    help="only time the fused path and the token-chunked composition on the three "
+                         "LM-head workloads and print one JSON line per workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM counters)")
     args = ap.parse_args()
@@ -191,6 +221,35 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.compare_methods:
+        for name in ("gemma_like", "headline", "qwen_like"):
+            c = CONFIGS[name]
+            log(f"generating {name}")
+            inp = make_config(name)
+            dt = torch.bfloat16
+            hh = torch.from_numpy(inp.hidden).to(dt).cuda()
+            WW = torch.from_numpy(inp.weight).to(dt).cuda()
+            bb = None if inp.bias is None else torch.from_numpy(inp.bias).to(dt).cuda()
+            yy = torch.from_numpy(inp.targets).cuda()
+            del inp
+            kw2 = dict(reduction=c.reduction, z_loss=c.z_loss)
+            ex = lce.lce_fwd_bwd(hh, WW, bb, yy, **kw2)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                ex = lce.lce_fwd_bwd(hh, WW, bb, yy, out=ex, workspace=ex["workspace"], **kw2)
+            torch.cuda.synchronize()
+            ms_f = (time.perf_counter() - t0) * 1e3 / args.steps
+            log(f"{name}: fused {ms_f:.1f} ms")
+            res_c = bench_chunked(lce, torch, hh, WW, bb, yy, kw2, ex, args.steps, c.BT)
+            log(f"{name}: chunked {res_c['ms_per_step']:.1f} ms")
+            print(json.dumps({"workload": f"{name}: BT={c.BT}, H={c.H}, V={c.V}",
+                              "fused_ms_per_step": ms_f, "fused_workspace_bytes": int(ex["workspace"].numel()),
+                              "chunked": res_c}), flush=True)
+            del hh, WW, bb, yy, ex
+            torch.cuda.empty_cache()
+        return
 
     if args.filter_zipf:
         for name in ("gemma_like", "qwen_like"):
@@ -314,6 +373,9 @@ def main():
         "loss": loss,
     }
     log(f"fused step {ms_step:.2f} ms")
+    if not args.no_chunked:
+        log("token-chunked composition leg")
+        res["chunked"] = bench_chunked(lce, torch, h, W, None, y, kw, out, args.steps, BT)
     if not args.no_filter:
         log(f"gradient filtering, eps {args.filter_eps:g}")
         res["filtered"] = bench_filtered(lce, torch, h, W, y, kw, out, args.filter_eps, args.steps, BT)

@@ -1162,23 +1162,49 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
       }
   } else {
     if (p.acc != nullptr || p.out != nullptr) {
+      // Read-modify-write of the running fp32 sums in 16-byte pieces: each half (32 rows) of
+      // the wave's accumulator block goes through the wave's own tile buffers (no load is in
+      // flight any more; no other wave uses them) and comes back one row per instruction,
+      // 4 consecutive columns per lane, with every load of a half issued before its stores.
+      static_assert(kPBuf * XW == 32 * NCOL * 4, "a half accumulator block fills the wave's tile buffers");
+      float* const tb = reinterpret_cast<float*>(xw);
+      constexpr int NQL = NCOL / 4;  // lanes per row
+      const bool lane_on = lane < NQL;
+      const int64_t col = kw0 + 4 * lane;
+      const bool col_ok = lane_on && col < H;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-          const int64_t col = kw0 + cb * 32 + (lane & 31);
+        for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-            if (row < p.nS && col < H) {
-              const int64_t k = row * H + col;
-              const float v = acc[sb][cb][r] + (p.first ? 0.f : p.acc[k]);
-              if (!p.last) p.acc[k] = v;
-              else if (p.out_f32) static_cast<float*>(p.out)[k] = cscale * v;
-              else static_cast<bf16_t*>(p.out)[k] = f2bf(cscale * v);
-            }
+          for (int r = 0; r < 16; ++r) tb[acc_row(lane, r) * NCOL + cb * 32 + (lane & 31)] = acc[sb][cb][r];
+        float4 old[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int64_t row = s0 + sb * 32 + i;
+          old[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (!p.first && col_ok && row < p.nS) old[i] = *reinterpret_cast<const float4*>(p.acc + row * H + col);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int64_t row = s0 + sb * 32 + i;
+          if (!(col_ok && row < p.nS)) continue;
+          const float4 t = lane_on ? *reinterpret_cast<const float4*>(tb + i * NCOL + 4 * lane) : old[i];
+          const float4 v = make_float4(t.x + old[i].x, t.y + old[i].y, t.z + old[i].z, t.w + old[i].w);
+          const int64_t k = row * H + col;
+          if (!p.last) {
+            *reinterpret_cast<float4*>(p.acc + k) = v;
+          } else if (p.out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + k) =
+                make_float4(cscale * v.x, cscale * v.y, cscale * v.z, cscale * v.w);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.out) + k) =
+                make_uint2(pack_bf2(cscale * v.x, cscale * v.y), pack_bf2(cscale * v.z, cscale * v.w));
           }
         }
+        // (the next half overwrites the buffers only after this wave's reads above)
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      }
     }
     if (do_gb) {
       gbs += __shfl_xor(gbs, 16, kWave);

@@ -117,6 +117,42 @@ def test_filtered_host_errors(lib, eps, counts, kw, status):
     assert fused_filtered(lib, eps, counts, **kw) == status
 
 
+def chunked(lib, **kw):
+    a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
+             dtype=BF16, ignore=-100, mu=0.0, red=MEAN, flags=0, loss=P + 0x300000,
+             gi=P + 0x400000, gw=P + 0x500000, gb=None, nv=P + 0x600000, lse=None,
+             ws=P + 0x700000, wsb=OK_WS, stream=None)
+    a.update(kw)
+    return lib.lce_fwd_bwd_chunked(a["hidden"], a["W"], a["bias"], a["targets"], a["BT"], a["H"], a["V"],
+                                   a["dtype"], a["ignore"], a["mu"], a["red"], a["flags"], a["loss"], a["gi"],
+                                   a["gw"], a["gb"], a["nv"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), 1), (dict(loss=None), 1), (dict(ws=None), 1), (dict(targets=None), 1),
+    (dict(BT=-1), 2), (dict(V=0), 2), (dict(H=12), 2), (dict(V=(1 << 22) + 1), 2),
+    (dict(dtype=F32), 3), (dict(dtype=7), 3),
+    (dict(hidden=P + 8), 4), (dict(gw=P + 4), 4), (dict(targets=P + 4), 4),
+    (dict(wsb=16), 5),
+    (dict(red=2), 6), (dict(mu=-1.0), 6), (dict(gb=P + 0x800000), 6), (dict(flags=4), 6),
+])
+def test_chunked_host_errors(lib, kw, status):
+    assert chunked(lib, **kw) == status
+
+
+def test_chunked_workspace(lib):
+    # one bf16 logits chunk (twice the rows of the pages' fp32 chunk), the grad_input partial
+    # sums and the fp32 grad_W sum (left out when grad_W itself is fp32)
+    BT, H, V = 65535, 1024, 176245
+    ws = lib.lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, BF16, 0)
+    ws32 = lib.lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, BF16, _lib.FLAG_GRAD_W_FP32)
+    chunk = 1024 * ((V + 63) // 64 * 64) * 2
+    assert ws - ws32 >= V * H * 4
+    assert chunk < ws32 < chunk + 256 * 1024 * 1024
+    assert lib.lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, F32, 0) == 0
+    assert lib.lce_fwd_bwd_chunked_workspace_bytes(0, H, V, BF16, 0) > 0
+
+
 def test_fused_errors_before_device_work_with_empty_batch(lib):
     # BT = 0 may pass NULL hidden/targets; a too-small workspace is still rejected on the host
     assert fused(lib, BT=0, hidden=None, targets=None, wsb=0) == 5
