@@ -83,10 +83,16 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     gradient filtering); filter_counts (int64 [4] on the device) then receives the skipped
     and examined tile counts of the grad_input and grad_W passes.  method="chunked" selects
     lce_fwd_bwd_chunked (the token-chunked composition; bf16 only), where grad_weight_fp32
-    makes grad_weight a float32 tensor that holds the sum over the chunks directly.
+    makes grad_weight a float32 tensor that holds the sum over the chunks directly;
+    method="auto" takes the chunked composition for bf16 with H > 1024, else the fused path.
     """
-    if method not in ("fused", "chunked"):
-        raise ValueError(f"method must be 'fused' or 'chunked', not {method!r}")
+    if method not in ("fused", "chunked", "auto"):
+        raise ValueError(f"method must be 'fused', 'chunked' or 'auto', not {method!r}")
+    if method == "auto":
+        # the fused backward keeps a workgroup's rows and accumulators on chip only up to
+        # H = 1024; above that the chunked composition is several times faster
+        method = "chunked" if (hidden.dtype == torch.bfloat16 and hidden.shape[1] > 1024
+                               and filter_eps == 0.0 and events is None) else "fused"
     chunked = method == "chunked"
     if grad_weight_fp32 and not chunked:
         raise ValueError("grad_weight_fp32 needs method='chunked'")
@@ -201,7 +207,7 @@ class _LinearCrossEntropy(torch.autograd.Function):
     def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss, reduction):
         r = lce_fwd_bwd(hidden.contiguous(), weight.contiguous(),
                         None if bias is None else bias.contiguous(), targets.contiguous(),
-                        ignore_index=ignore_index, z_loss=z_loss, reduction=reduction,
+                        ignore_index=ignore_index, z_loss=z_loss, reduction=reduction, method="auto",
                         grad_input=ctx.needs_input_grad[0], grad_weight=ctx.needs_input_grad[1],
                         grad_bias=bias is not None and ctx.needs_input_grad[2])
         ctx.save_for_backward(r["grad_input"], r["grad_weight"], r["grad_bias"])
