@@ -151,6 +151,93 @@ def lce_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDE
     return out
 
 
+def _mean_logit(z: np.ndarray, lse: np.ndarray) -> np.ndarray:
+    """E_p[z] = sum_v p_v z_v per row, p = exp(z - LSE)."""
+    return (np.exp(z - lse[:, None]) * z).sum(axis=1)
+
+
+def _row_coefficients(lse, ez, valid, gl, gp, ge, mu):
+    """(alpha, beta, gamma) of dlogits = p * (alpha + beta * z) - gamma * onehot(y) for the
+    upstream gradients gl (row loss), gp (logprobs), ge (entropy); see lce_rows_oracle."""
+    vf = valid.astype(np.float64)
+    alpha = vf * (gl * (1.0 + 2.0 * mu * lse) - gp) + ge * ez
+    beta = -ge
+    gamma = vf * (gl - gp)
+    return alpha, beta, gamma
+
+
+def lce_rows_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDEX,
+                    z_loss: float = 0.0, grad_row_loss=None, grad_logprobs=None,
+                    grad_entropy=None, rows_per_chunk: Optional[int] = None) -> dict:
+    """Per-row outputs of the LM head for RL-style use, and their gradients.
+
+    [P1] "Strategy 2" names the per-row quantities an RL trainer keeps (each row's
+    log-probability of its target and the entropy of its softmax, beside the LSE); the
+    pages give no formulas for them, so the textbook definitions are used:
+      row_loss[t] = valid_t * (LSE_t - z_t[y_t] + mu * LSE_t**2)   (the fused loss per row)
+      logprobs[t] = valid_t * (z_t[y_t] - LSE_t)                    (log softmax at the target)
+      entropy[t]  = -sum_v p_tv log p_tv = LSE_t - sum_v p_tv z_tv   (every row)
+    With per-row upstream gradients (gl, gp, ge; any may be None = 0) the gradients are
+    those of  sum_t gl_t row_loss_t + gp_t logprobs_t + ge_t entropy_t.  By the chain rule
+    through p = softmax(z) (d LSE / dz_v = p_v; d (sum_u p_u z_u) / dz_v = p_v (1 + z_v - E[z])):
+      dlogits[t, v] = p_tv * (alpha_t + beta_t * z_tv) - gamma_t * [v == y_t]
+      alpha_t = valid_t * (gl_t * (1 + 2 mu LSE_t) - gp_t) + ge_t * E_t[z]
+      beta_t  = -ge_t
+      gamma_t = valid_t * (gl_t - gp_t)
+    and grad_input = dlogits . W, grad_W = dlogits^T . hidden, grad_b = sum_t dlogits
+    ([P1] "From dlogits to grad_input and grad_W").
+    """
+    h = _f64(hidden)
+    W = _f64(weight)
+    b = _f64(bias)
+    y = np.asarray(targets, dtype=np.int64)
+    BT, H = h.shape
+    V = W.shape[0]
+    valid = _valid_mask(y, V, ignore_index)
+    mu = float(z_loss)
+    gl = None if grad_row_loss is None else _f64(grad_row_loss)
+    gp = None if grad_logprobs is None else _f64(grad_logprobs)
+    ge = None if grad_entropy is None else _f64(grad_entropy)
+    want_grads = gl is not None or gp is not None or ge is not None
+
+    lse = np.empty(BT)
+    zy = np.zeros(BT)
+    ez = np.empty(BT)
+    gi = np.zeros((BT, H)) if want_grads else None
+    gw = np.zeros((V, H)) if want_grads else None
+    gb = np.zeros(V) if (want_grads and b is not None) else None
+    R = rows_per_chunk or _rows_per_chunk(V)
+    for r0 in range(0, BT, R):
+        r1 = min(BT, r0 + R)
+        z = _logits(h[r0:r1], W, b)
+        L = _lse(z)
+        lse[r0:r1] = L
+        ez[r0:r1] = _mean_logit(z, L)
+        vr = valid[r0:r1]
+        idx = np.nonzero(vr)[0]
+        zy[r0 + idx] = z[idx, y[r0:r1][idx]]
+        if want_grads:
+            n = r1 - r0
+            glc = gl[r0:r1] if gl is not None else np.zeros(n)
+            gpc = gp[r0:r1] if gp is not None else np.zeros(n)
+            gec = ge[r0:r1] if ge is not None else np.zeros(n)
+            alpha, beta, gamma = _row_coefficients(L, ez[r0:r1], vr, glc, gpc, gec, mu)
+            g = np.exp(z - L[:, None]) * (alpha[:, None] + beta[:, None] * z)
+            g[idx, y[r0:r1][idx]] -= gamma[idx]
+            gi[r0:r1] = g @ W
+            gw += g.T @ h[r0:r1]
+            if gb is not None:
+                gb += g.sum(axis=0)
+    row_loss = np.where(valid, lse - zy + mu * lse * lse, 0.0)
+    logprobs = np.where(valid, zy - lse, 0.0)
+    entropy = lse - ez
+    out = dict(lse=lse, row_loss=row_loss, logprobs=logprobs, entropy=entropy, mean_z=ez,
+               n_valid=int(valid.sum()))
+    if want_grads:
+        out.update(grad_input=gi, grad_weight=gw, grad_bias=gb)
+    return out
+
+
 def _block_keep(g: np.ndarray, rows: int, cols: int, eps: float):
     """Mask of g [R, C] that is False inside every (rows x cols) block, aligned at 0, whose
     entries all have |g| < eps ([P2] "Gradient Filtering": a block is skipped only if
