@@ -201,6 +201,42 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
                                void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
                                float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * lce_rows_forward / lce_rows_backward -- per-row outputs of the LM head for RL-style use
+ * ("Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It",
+ * Strategy 2 keeps each row's target log-probability and softmax entropy beside the LSE)
+ * and the gradients of any per-row weighted sum of them.  bf16 only; computed by the
+ * token-chunked composition (same chunking and workspace as lce_fwd_bwd_chunked).
+ *
+ * For row t with z_t = W h_t + b, LSE_t = log sum_v exp(z_tv), p_t = softmax(z_t) and
+ * valid_t = (y_t != ignore_index):
+ *   row_loss[t] = valid_t (LSE_t - z_t[y_t] + z_loss_mult LSE_t^2)   (reduction 'none')
+ *   logprobs[t] = valid_t (z_t[y_t] - LSE_t)
+ *   entropy[t]  = LSE_t - sum_v p_tv z_tv                              (every row)
+ * lce_rows_forward writes any of lse_out, logprobs_out, entropy_out, row_loss_out (device
+ * float[BT] each, or NULL) and n_valid_out (int64[1] or NULL).
+ * lce_rows_backward writes grad_input, grad_W, grad_b (as lce_fwd_bwd; each may be NULL) for
+ *   F = sum_t grad_row_loss[t] row_loss[t] + grad_logprobs[t] logprobs[t] + grad_entropy[t] entropy[t]
+ * (each upstream gradient a device float[BT], or NULL for zeros).  Its dlogits are
+ *   p_tv (alpha_t + beta_t z_tv) - gamma_t [v == y_t],
+ *   alpha_t = valid_t (gl_t (1 + 2 mu LSE_t) - gp_t) + ge_t E_p[z_t],  beta_t = -ge_t,
+ *   gamma_t = valid_t (gl_t - gp_t).
+ * flags: LCE_FLAG_CHECK_TARGETS; lce_rows_backward also LCE_FLAG_GRAD_W_FP32.  Workspace:
+ * lce_rows_workspace_bytes (= lce_fwd_bwd_chunked_workspace_bytes).  Errors as
+ * lce_fwd_bwd_chunked.
+ */
+size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);
+lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                            int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                            float z_loss_mult, uint32_t flags, float* lse_out, float* logprobs_out,
+                            float* entropy_out, float* row_loss_out, int64_t* n_valid_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+lce_status lce_rows_backward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                             int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                             float z_loss_mult, uint32_t flags, const float* grad_row_loss,
+                             const float* grad_logprobs, const float* grad_entropy, void* grad_input,
+                             void* grad_W, void* grad_b, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes lce_ce_with_grad_inplace needs (per-row partial results), or 0 if invalid. */
 size_t lce_ce_workspace_bytes(int64_t B, int64_t V, lce_dtype dtype);
 

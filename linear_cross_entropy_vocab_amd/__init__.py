@@ -164,6 +164,122 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
                 workspace=workspace)
 
 
+def rows_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype, grad_weight_fp32: bool = False) -> int:
+    flags = _lib.FLAG_GRAD_W_FP32 if grad_weight_fp32 else 0
+    return int(load().lce_rows_workspace_bytes(BT, H, V, _DTYPES[dtype], flags))
+
+
+def _rows_common(hidden, weight, bias, targets):
+    _need_gpu(hidden, weight, bias, targets)
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or (
+            bias is not None and bias.dtype != torch.bfloat16):
+        raise TypeError("the per-row entry points take bf16 hidden, weight and bias")
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    BT, H = hidden.shape
+    return BT, H, weight.shape[0]
+
+
+def lce_rows_forward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                     targets: torch.Tensor, *, ignore_index: int = -100, z_loss: float = 0.0,
+                     outputs=("lse", "logprobs", "entropy", "row_loss"), check_targets: bool = False,
+                     workspace: Optional[torch.Tensor] = None) -> dict:
+    """lce_rows_forward: per-row LSE, target log-probability, softmax entropy and row loss
+    (reduction 'none'), each only if named in `outputs`; also n_valid."""
+    lib = load()
+    BT, H, V = _rows_common(hidden, weight, bias, targets)
+    dev = hidden.device
+    res = {k: (torch.empty(BT, dtype=torch.float32, device=dev) if k in outputs else None)
+           for k in ("lse", "logprobs", "entropy", "row_loss")}
+    nv = torch.empty((), dtype=torch.int64, device=dev)
+    flags = _lib.FLAG_CHECK_TARGETS if check_targets else 0
+    need = int(lib.lce_rows_workspace_bytes(BT, H, V, _lib.DTYPE_BF16, flags))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = lib.lce_rows_forward(_ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), BT, H, V, _lib.DTYPE_BF16,
+                              ignore_index, float(z_loss), flags, _ptr(res["lse"]), _ptr(res["logprobs"]),
+                              _ptr(res["entropy"]), _ptr(res["row_loss"]), _ptr(nv), _ptr(workspace),
+                              workspace.numel(), stream)
+    _lib.check(st, "lce_rows_forward")
+    res.update(n_valid=nv, workspace=workspace)
+    return res
+
+
+def lce_rows_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
+                      targets: torch.Tensor, *, grad_row_loss: Optional[torch.Tensor] = None,
+                      grad_logprobs: Optional[torch.Tensor] = None, grad_entropy: Optional[torch.Tensor] = None,
+                      ignore_index: int = -100, z_loss: float = 0.0, grad_input: bool = True,
+                      grad_weight: bool = True, grad_bias: Optional[bool] = None,
+                      grad_weight_fp32: bool = False, check_targets: bool = False,
+                      workspace: Optional[torch.Tensor] = None) -> dict:
+    """lce_rows_backward: gradients of sum_t gl_t row_loss_t + gp_t logprobs_t + ge_t entropy_t
+    (upstream gradients float32 [BT] on the device, or None for zeros)."""
+    lib = load()
+    BT, H, V = _rows_common(hidden, weight, bias, targets)
+    ups = []
+    for g in (grad_row_loss, grad_logprobs, grad_entropy):
+        if g is not None:
+            _need_gpu(g)
+            if g.dtype != torch.float32 or g.numel() != BT:
+                raise TypeError("upstream per-row gradients must be float32 with BT elements")
+            g = g.contiguous()
+        ups.append(g)
+    if grad_bias is None:
+        grad_bias = bias is not None
+    gi = torch.empty_like(hidden) if grad_input else None
+    gw = torch.empty_like(weight, dtype=torch.float32 if grad_weight_fp32 else weight.dtype) if grad_weight else None
+    gb = torch.empty_like(bias) if grad_bias else None
+    flags = (_lib.FLAG_CHECK_TARGETS if check_targets else 0) | (_lib.FLAG_GRAD_W_FP32 if grad_weight_fp32 else 0)
+    dev = hidden.device
+    need = int(lib.lce_rows_workspace_bytes(BT, H, V, _lib.DTYPE_BF16, flags))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = lib.lce_rows_backward(_ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), BT, H, V, _lib.DTYPE_BF16,
+                               ignore_index, float(z_loss), flags, _ptr(ups[0]), _ptr(ups[1]), _ptr(ups[2]),
+                               _ptr(gi), _ptr(gw), _ptr(gb), _ptr(workspace), workspace.numel(), stream)
+    _lib.check(st, "lce_rows_backward")
+    return dict(grad_input=gi, grad_weight=gw, grad_bias=gb, workspace=workspace)
+
+
+class _LinearRows(torch.autograd.Function):
+    """(logprobs, entropy, row_loss) per row; the backward recomputes the logits chunk by chunk."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss):
+        h, W = hidden.contiguous(), weight.contiguous()
+        b = None if bias is None else bias.contiguous()
+        y = targets.contiguous()
+        r = lce_rows_forward(h, W, b, y, ignore_index=ignore_index, z_loss=z_loss,
+                             outputs=("logprobs", "entropy", "row_loss"))
+        ctx.save_for_backward(h, W, b, y)
+        ctx.opts = (ignore_index, z_loss)
+        return r["logprobs"], r["entropy"], r["row_loss"]
+
+    @staticmethod
+    def backward(ctx, g_lp, g_ent, g_rl):
+        h, W, b, y = ctx.saved_tensors
+        ignore_index, z_loss = ctx.opts
+
+        def f32(g):
+            return None if g is None else g.to(torch.float32).contiguous()
+
+        r = lce_rows_backward(h, W, b, y, grad_row_loss=f32(g_rl), grad_logprobs=f32(g_lp),
+                              grad_entropy=f32(g_ent), ignore_index=ignore_index, z_loss=z_loss,
+                              grad_input=ctx.needs_input_grad[0], grad_weight=ctx.needs_input_grad[1],
+                              grad_bias=b is not None and ctx.needs_input_grad[2])
+        return r["grad_input"], r["grad_weight"], r["grad_bias"], None, None, None
+
+
+def linear_logprobs_entropy(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                            bias: Optional[torch.Tensor] = None, *, ignore_index: int = -100,
+                            z_loss: float = 0.0):
+    """Differentiable per-row (logprobs, entropy, row_loss) of hidden @ weight.T + bias (bf16):
+    the target log-probability, the softmax entropy, and the unreduced loss (reduction 'none')."""
+    return _LinearRows.apply(hidden, weight, bias, targets, ignore_index, z_loss)
+
+
 def lce_ce_with_grad_inplace(logits: torch.Tensor, targets: torch.Tensor, *, ignore_index: int = -100,
                              z_loss: float = 0.0, workspace: Optional[torch.Tensor] = None,
                              out: Optional[dict] = None):

@@ -22,6 +22,7 @@ NUM_STAGES = 7
 
 EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_fwd_bwd_workspace_bytes",
            "lce_fwd_bwd_chunked", "lce_fwd_bwd_chunked_workspace_bytes",
+           "lce_rows_forward", "lce_rows_backward", "lce_rows_workspace_bytes",
            "lce_stage_name",
            "lce_ce_with_grad_inplace", "lce_ce_workspace_bytes", "lce_status_string", "lce_version")
 
@@ -56,6 +57,13 @@ def load() -> ctypes.CDLL:
     lib.lce_fwd_bwd_chunked.restype = ctypes.c_int
     lib.lce_fwd_bwd_chunked_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_uint32]
     lib.lce_fwd_bwd_chunked_workspace_bytes.restype = ctypes.c_size_t
+    lib.lce_rows_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_uint32]
+    lib.lce_rows_workspace_bytes.restype = ctypes.c_size_t
+    rows_head = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_i64, c_f, ctypes.c_uint32]
+    lib.lce_rows_forward.argtypes = rows_head + [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+    lib.lce_rows_forward.restype = ctypes.c_int
+    lib.lce_rows_backward.argtypes = rows_head + [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+    lib.lce_rows_backward.restype = ctypes.c_int
     lib.lce_stage_name.argtypes = [ctypes.c_int]
     lib.lce_stage_name.restype = ctypes.c_char_p
     lib.lce_ce_with_grad_inplace.argtypes = [c_vp, c_vp, c_i64, c_i64, ctypes.c_int, c_i64, c_f, c_vp,

@@ -171,51 +171,117 @@ size_t lce_fwd_bwd_chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce
   return lce::chunked_workspace_bytes(BT, H, V, (flags & LCE_FLAG_GRAD_W_FP32) != 0);
 }
 
+}  // extern "C"
+
+namespace lce {
+
+// Argument checks shared by the chunked entry points (before any HIP call) and the argument
+// block they build.
+static lce_status chunk_args(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                             int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                             float z_loss_mult, uint32_t flags, uint32_t allowed_flags, void* grad_input,
+                             void* grad_W, void* grad_b, int64_t* n_valid_out, void* workspace,
+                             size_t workspace_bytes, FusedArgs* a) {
+  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
+  // (V <= 2^22: the byte offsets inside a 256-row logits tile of the chunk stay 32-bit)
+  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 22) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
+  if (dtype != LCE_DTYPE_BF16) return LCE_ERR_DTYPE;
+  if (W == nullptr || workspace == nullptr) return LCE_ERR_NULL;
+  if (BT > 0 && (hidden == nullptr || targets == nullptr)) return LCE_ERR_NULL;
+  if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
+  if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
+  if ((flags & ~allowed_flags) != 0) return LCE_ERR_ARG;
+  if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(grad_input, 16) || !aligned(grad_W, 16) ||
+      !aligned(workspace, 16) || !aligned(bias, 2) || !aligned(grad_b, 2) || !aligned(targets, 8) ||
+      !aligned(n_valid_out, 8))
+    return LCE_ERR_ALIGNMENT;
+  if (workspace_bytes < chunked_workspace_bytes(BT, H, V, (flags & LCE_FLAG_GRAD_W_FP32) != 0))
+    return LCE_ERR_WORKSPACE;
+  *a = FusedArgs{};
+  a->hidden = hidden;
+  a->W = W;
+  a->bias = bias;
+  a->targets = targets;
+  a->BT = BT;
+  a->H = H;
+  a->V = V;
+  a->bf16 = true;
+  a->ignore_index = ignore_index;
+  a->mu = z_loss_mult;
+  a->grad_input = grad_input;
+  a->grad_W = grad_W;
+  a->grad_b = grad_b;
+  a->n_valid_out = n_valid_out;
+  return LCE_OK;
+}
+
+static lce_status chunk_call(const FusedArgs& a, ChunkMode mode, const RowsHost& io, uint32_t flags, void* ws,
+                             void* stream) {
+  bool bad = false;
+  if (chunk_loop(a, mode, io, (flags & LCE_FLAG_GRAD_W_FP32) != 0, (flags & LCE_FLAG_CHECK_TARGETS) != 0, ws,
+                 static_cast<hipStream_t>(stream), &bad) != hipSuccess)
+    return LCE_ERR_HIP;
+  return bad ? LCE_ERR_TARGET_RANGE : LCE_OK;
+}
+
+}  // namespace lce
+
+extern "C" {
+
 lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bias, const int64_t* targets,
                                int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
                                float z_loss_mult, lce_reduction reduction, uint32_t flags, float* loss_out,
                                void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
                                float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
-  // (V <= 2^22: the byte offsets inside a 256-row logits tile of the chunk stay 32-bit)
-  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 22) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
-  if (dtype != LCE_DTYPE_BF16) return LCE_ERR_DTYPE;
-  if (W == nullptr || loss_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
-  if (BT > 0 && (hidden == nullptr || targets == nullptr)) return LCE_ERR_NULL;
+  lce::FusedArgs a;
+  const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
+                                       LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32, grad_input, grad_W, grad_b,
+                                       n_valid_out, workspace, workspace_bytes, &a);
+  if (s != LCE_OK) return s;
+  if (loss_out == nullptr) return LCE_ERR_NULL;
   if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_SUM) return LCE_ERR_ARG;
-  if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
-  if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
-  if ((flags & ~(LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32)) != 0) return LCE_ERR_ARG;
-  if (!lce::aligned(hidden, 16) || !lce::aligned(W, 16) || !lce::aligned(grad_input, 16) ||
-      !lce::aligned(grad_W, 16) || !lce::aligned(workspace, 16) || !lce::aligned(bias, 2) ||
-      !lce::aligned(grad_b, 2) || !lce::aligned(targets, 8) || !lce::aligned(loss_out, 4) ||
-      !lce::aligned(n_valid_out, 8) || !lce::aligned(lse_out, 4))
-    return LCE_ERR_ALIGNMENT;
-  const bool gw32 = (flags & LCE_FLAG_GRAD_W_FP32) != 0;
-  if (workspace_bytes < lce::chunked_workspace_bytes(BT, H, V, gw32)) return LCE_ERR_WORKSPACE;
-  lce::FusedArgs a{};
-  a.hidden = hidden;
-  a.W = W;
-  a.bias = bias;
-  a.targets = targets;
-  a.BT = BT;
-  a.H = H;
-  a.V = V;
-  a.bf16 = true;
-  a.ignore_index = ignore_index;
-  a.mu = z_loss_mult;
+  if (!lce::aligned(loss_out, 4) || !lce::aligned(lse_out, 4)) return LCE_ERR_ALIGNMENT;
   a.mean = reduction == LCE_REDUCTION_MEAN;
   a.loss_out = loss_out;
-  a.grad_input = grad_input;
-  a.grad_W = grad_W;
-  a.grad_b = grad_b;
-  a.n_valid_out = n_valid_out;
   a.lse_out = lse_out;
-  bool bad = false;
-  if (lce::chunked_run(a, gw32, (flags & LCE_FLAG_CHECK_TARGETS) != 0, workspace, static_cast<hipStream_t>(stream),
-                       &bad) != hipSuccess)
-    return LCE_ERR_HIP;
-  return bad ? LCE_ERR_TARGET_RANGE : LCE_OK;
+  return lce::chunk_call(a, lce::kLoss, lce::RowsHost{}, flags, workspace, stream);
+}
+
+size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
+  return lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags);
+}
+
+lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                            int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                            float z_loss_mult, uint32_t flags, float* lse_out, float* logprobs_out,
+                            float* entropy_out, float* row_loss_out, int64_t* n_valid_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  lce::FusedArgs a;
+  const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
+                                       LCE_FLAG_CHECK_TARGETS, nullptr, nullptr, nullptr, n_valid_out, workspace,
+                                       workspace_bytes, &a);
+  if (s != LCE_OK) return s;
+  if (!lce::aligned(lse_out, 4) || !lce::aligned(logprobs_out, 4) || !lce::aligned(entropy_out, 4) ||
+      !lce::aligned(row_loss_out, 4))
+    return LCE_ERR_ALIGNMENT;
+  const lce::RowsHost io{lse_out, logprobs_out, entropy_out, row_loss_out, nullptr, nullptr, nullptr};
+  return lce::chunk_call(a, lce::kRowStats, io, flags, workspace, stream);
+}
+
+lce_status lce_rows_backward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
+                             int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
+                             float z_loss_mult, uint32_t flags, const float* grad_row_loss,
+                             const float* grad_logprobs, const float* grad_entropy, void* grad_input,
+                             void* grad_W, void* grad_b, void* workspace, size_t workspace_bytes, void* stream) {
+  lce::FusedArgs a;
+  const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
+                                       LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32, grad_input, grad_W, grad_b,
+                                       nullptr, workspace, workspace_bytes, &a);
+  if (s != LCE_OK) return s;
+  if (!lce::aligned(grad_row_loss, 4) || !lce::aligned(grad_logprobs, 4) || !lce::aligned(grad_entropy, 4))
+    return LCE_ERR_ALIGNMENT;
+  const lce::RowsHost io{nullptr, nullptr, nullptr, nullptr, grad_row_loss, grad_logprobs, grad_entropy};
+  return lce::chunk_call(a, lce::kRowGrads, io, flags, workspace, stream);
 }
 
 const char* lce_stage_name(int k) {

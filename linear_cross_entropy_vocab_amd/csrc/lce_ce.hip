@@ -313,6 +313,153 @@ __global__ void __launch_bounds__(kCEThreads) ce_reduce(const float* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-row outputs and their gradients on a logits chunk (bf16, rows ld apart), for
+// RL-style use ("Fused Linear Cross-Entropy: ...", Strategy 2 keeps each row's target
+// log-probability and softmax entropy beside the LSE):
+//   logprobs[t] = valid (z_y - LSE),  entropy[t] = LSE - E_p[z],
+//   row_loss[t] = valid (LSE - z_y + mu LSE^2).
+// With GRAD the row is overwritten with the dlogits of
+//   sum_t gl_t row_loss_t + gp_t logprobs_t + ge_t entropy_t,
+// which is p (alpha + beta z) - gamma onehot(y) with
+//   alpha = valid (gl (1 + 2 mu LSE) - gp) + ge E_p[z],  beta = -ge,  gamma = valid (gl - gp)
+// (d LSE / dz_v = p_v and d E_p[z] / dz_v = p_v (1 + z_v - E_p[z])).
+// Two passes over the row in 16-byte vectors: (max, sum exp, sum exp * z) online, then the
+// outputs (the second read usually hits the last-level cache).
+// ---------------------------------------------------------------------------
+struct RowsIO {
+  float* lse;
+  float* logprobs;
+  float* entropy;
+  float* row_loss;
+  const float* gl;  // upstream gradient of row_loss, or NULL (0)
+  const float* gp;  // of logprobs
+  const float* ge;  // of entropy
+};
+
+// (max, sum exp(x - max), sum exp(x - max) x) merge; m = -inf is the identity.
+__device__ __forceinline__ void mst_merge(float& m, float& s, float& t, float m2, float s2, float t2) {
+  if (m2 > m) {
+    const float f = __expf(m - m2);
+    s = s * f + s2;
+    t = t * f + t2;
+    m = m2;
+  } else if (m2 != -INFINITY) {
+    const float f = __expf(m2 - m);
+    s += s2 * f;
+    t += t2 * f;
+  }
+}
+
+template <bool GRAD>
+__global__ void __launch_bounds__(kCEThreads) rows_stats_kernel(bf16_t* __restrict__ logits,
+                                                                 const int64_t* __restrict__ targets,
+                                                                 int64_t V, int64_t ld, int64_t ignore_index,
+                                                                 float mu, RowsIO io) {
+  typedef Vec16<bf16_t> VT;
+  constexpr int EPV = VT::N;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float sm[kCEWaves], ss[kCEWaves], st[kCEWaves];
+  const int64_t row = blockIdx.x;
+  bf16_t* x = logits + row * ld;
+  const int tid = threadIdx.x;
+  const int64_t y = targets[row];
+  const bool valid = (y != ignore_index) && (y >= 0) && (y < V);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(x, ld * 2);
+  const int64_t nvec = (V + EPV - 1) / EPV;
+  float m = -INFINITY, s = 0.f, t = 0.f;
+  for (int64_t j = tid; j < nvec; j += kCEThreads) {
+    VT v;
+    v.raw = load16(rs, (uint32_t)(j * 16));
+    mask_tail(v, j * EPV, V);
+    float vm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, v.get(e));
+    if (vm > m) {
+      const float f = __builtin_amdgcn_exp2f((m - vm) * kLog2e);
+      s *= f;
+      t *= f;
+      m = vm;
+    }
+    if (m != -INFINITY) {
+      const float ml = m * kLog2e;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float xe = v.get(e);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(xe, kLog2e, -ml));
+        s += pe;
+        t += pe != 0.f ? pe * xe : 0.f;
+      }
+    }
+  }
+  // block-wide merge (every thread ends with the row's values)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, kWave), s2 = __shfl_xor(s, off, kWave), t2 = __shfl_xor(t, off, kWave);
+    mst_merge(m, s, t, m2, s2, t2);
+  }
+  const int w = tid / kWave;
+  if (tid % kWave == 0) {
+    sm[w] = m;
+    ss[w] = s;
+    st[w] = t;
+  }
+  __syncthreads();
+  m = -INFINITY;
+  s = 0.f;
+  t = 0.f;
+  for (int i = 0; i < kCEWaves; ++i) mst_merge(m, s, t, sm[i], ss[i], st[i]);
+  const float lse = m + __logf(s);
+  const float ez = t / s;
+  const float zy = valid ? VT::elem(rs, (uint32_t)(y * 2)) : 0.f;
+  if (tid == 0) {
+    if (io.lse) io.lse[row] = lse;
+    if (io.logprobs) io.logprobs[row] = valid ? zy - lse : 0.f;
+    if (io.entropy) io.entropy[row] = lse - ez;
+    if (io.row_loss) io.row_loss[row] = valid ? lse - zy + mu * lse * lse : 0.f;
+  }
+  if constexpr (GRAD) {
+    const float gl = io.gl ? io.gl[row] : 0.f;
+    const float gp = io.gp ? io.gp[row] : 0.f;
+    const float ge = io.ge ? io.ge[row] : 0.f;
+    const float alpha = (valid ? gl * (1.f + 2.f * mu * lse) - gp : 0.f) + ge * ez;
+    const float beta = -ge;
+    const float gamma = valid ? gl - gp : 0.f;
+    const float ll = lse * kLog2e;
+    const int64_t nvec_ld = ld / EPV;
+    for (int64_t j = tid; j < nvec_ld; j += kCEThreads) {
+      VT v;
+      v.raw = load16(rs, (uint32_t)(j * 16));
+      mask_tail(v, j * EPV, V);
+      float d[EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float xe = v.get(e);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(xe, kLog2e, -ll));
+        d[e] = pe != 0.f ? pe * fmaf(beta, xe, alpha) : 0.f;
+        if (valid && j * EPV + e == y) d[e] -= gamma;
+      }
+      store16(rs, (uint32_t)(j * 16), pack_out(d, bf16_t()));
+    }
+  }
+}
+
+hipError_t launch_rows_stats(void* logits, const int64_t* targets, int64_t B, int64_t V, int64_t ld,
+                             int64_t ignore_index, float mu, float* lse, float* logprobs, float* entropy,
+                             float* row_loss, const float* gl, const float* gp, const float* ge, bool grad,
+                             hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  if ((ld % 8) != 0 || (reinterpret_cast<uintptr_t>(logits) % 16) != 0) return hipErrorInvalidValue;
+  RowsIO io{lse, logprobs, entropy, row_loss, gl, gp, ge};
+  if (grad)
+    hipLaunchKernelGGL(rows_stats_kernel<true>, dim3((unsigned)B), dim3(kCEThreads), 0, st,
+                       static_cast<bf16_t*>(logits), targets, V, ld, ignore_index, mu, io);
+  else
+    hipLaunchKernelGGL(rows_stats_kernel<false>, dim3((unsigned)B), dim3(kCEThreads), 0, st,
+                       static_cast<bf16_t*>(logits), targets, V, ld, ignore_index, mu, io);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int64_t V, int64_t ld,
                               int64_t ignore_index, float mu, CERowOut out, hipStream_t st) {

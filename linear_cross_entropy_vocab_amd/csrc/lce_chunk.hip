@@ -72,11 +72,14 @@ __global__ void chunk_loss_kernel(const float* __restrict__ ce, const float* __r
   if (n_valid_out) *n_valid_out = n;
 }
 
-// Launch sequence of the chunked call (arguments validated by the caller; bf16 only).
+// Launch sequence of the chunked calls (arguments validated by the caller; bf16 only).
+//   kLoss:      loss and gradients of the mean/sum loss (the standalone CE kernel in place)
+//   kRowStats:  per-row outputs only (no gradients)
+//   kRowGrads:  gradients of the per-row weighted sum sum_t gl row_loss + gp logprobs + ge entropy
 // *bad_targets is set when check_targets found an out-of-range target (nothing after the
 // pre-pass is launched then).
-hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets, void* workspace,
-                       hipStream_t st, bool* bad_targets) {
+hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bool grad_w_fp32,
+                      bool check_targets, void* workspace, hipStream_t st, bool* bad_targets) {
   *bad_targets = false;
   const ChunkPlan c = chunk_plan(a.BT, a.H, a.V);
   const int64_t nch = std::max<int64_t>(1, c.nchunks);
@@ -123,7 +126,10 @@ hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets,
   }
   const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  const bool want_dw = a.grad_W != nullptr || a.grad_b != nullptr;
+  const bool grads = mode != kRowStats;
+  const bool want_dw = grads && (a.grad_W != nullptr || a.grad_b != nullptr);
+  auto off = [](const float* q, int64_t r0) { return q ? q + r0 : nullptr; };
+  auto offw = [](float* q, int64_t r0) { return q ? q + r0 : nullptr; };
   // (an empty batch still runs one chunk of 0 rows, which writes zero gradients)
   for (int64_t k = 0; k < nch; ++k) {
     const int64_t r0 = k * c.cs;
@@ -132,9 +138,16 @@ hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets,
     if ((e = launch_logits_chunk(W, hk, static_cast<const bf16_t*>(a.bias), rows, a.H, a.V, zbuf, c.ld, st)) !=
         hipSuccess)
       return e;
-    if ((e = launch_ce_inplace(zbuf, true, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k,
-                               z_k + k, nv_k + k, a.lse_out ? a.lse_out + r0 : nullptr, ce_ws, st)) != hipSuccess)
-      return e;
+    if (mode == kLoss) {
+      e = launch_ce_inplace(zbuf, true, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k, z_k + k,
+                            nv_k + k, offw(a.lse_out, r0), ce_ws, st);
+    } else {
+      e = launch_rows_stats(zbuf, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, offw(io.lse, r0),
+                            offw(io.logprobs, r0), offw(io.entropy, r0), offw(io.row_loss, r0), off(io.gl, r0),
+                            off(io.gp, r0), off(io.ge, r0), mode == kRowGrads, st);
+    }
+    if (e != hipSuccess) return e;
+    if (!grads) continue;
     MatArgs m{};
     m.G = zbuf;
     m.ld = c.ld;
@@ -142,7 +155,7 @@ hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets,
     m.H = a.H;
     m.hchunks = c.hchunks;
     m.n_valid = w.n_valid;
-    m.mean = a.mean ? 1 : 0;
+    m.mean = (mode == kLoss && a.mean) ? 1 : 0;  // per-row weights carry their own scale
     if (a.grad_input != nullptr) {
       m.X = W;
       m.nS = rows;
@@ -152,7 +165,7 @@ hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets,
       m.part = part;
       if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
       if ((e = launch_mat_reduce(part, c.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + r0 * a.H,
-                                 w.n_valid, a.mean, st)) != hipSuccess)
+                                 w.n_valid, m.mean != 0, st)) != hipSuccess)
         return e;
     }
     if (want_dw) {
@@ -172,9 +185,14 @@ hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets,
       if ((e = launch_mat_gemm(true, m, st)) != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(64), 0, st, ce_k, z_k, nch, w.n_valid, a.mu,
-                     a.mean ? 1 : 0, a.loss_out, a.n_valid_out);
-  return hipGetLastError();
+  if (mode == kLoss) {
+    hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(64), 0, st, ce_k, z_k, nch, w.n_valid, a.mu,
+                       a.mean ? 1 : 0, a.loss_out, a.n_valid_out);
+    return hipGetLastError();
+  }
+  if (a.n_valid_out != nullptr)
+    return hipMemcpyAsync(a.n_valid_out, w.n_valid, sizeof(int64_t), hipMemcpyDeviceToDevice, st);
+  return hipSuccess;
 }
 
 }  // namespace lce

@@ -96,8 +96,26 @@ struct ChunkPlan {
 };
 ChunkPlan chunk_plan(int64_t BT, int64_t H, int64_t V);
 size_t chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool grad_w_fp32);
-hipError_t chunked_run(const FusedArgs& a, bool grad_w_fp32, bool check_targets, void* workspace,
-                       hipStream_t st, bool* bad_targets);
+enum ChunkMode { kLoss = 0, kRowStats, kRowGrads };
+struct RowsHost {  // per-row outputs ([BT], each may be NULL) and upstream gradients ([BT] or NULL)
+  float* lse;
+  float* logprobs;
+  float* entropy;
+  float* row_loss;
+  const float* gl;
+  const float* gp;
+  const float* ge;
+};
+hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bool grad_w_fp32,
+                      bool check_targets, void* workspace, hipStream_t st, bool* bad_targets);
+
+// Per-row outputs (LSE, target log-probability, entropy, row loss; each may be NULL) of a
+// bf16 logits chunk with rows ld apart; with grad, the rows are overwritten with the dlogits
+// of sum_t gl_t row_loss_t + gp_t logprobs_t + ge_t entropy_t (gl/gp/ge may be NULL = 0).
+hipError_t launch_rows_stats(void* logits, const int64_t* targets, int64_t B, int64_t V, int64_t ld,
+                             int64_t ignore_index, float mu, float* lse, float* logprobs, float* entropy,
+                             float* row_loss, const float* gl, const float* gp, const float* ge, bool grad,
+                             hipStream_t st);
 
 // Standalone cross-entropy.
 size_t ce_workspace_bytes(int64_t B);

@@ -140,6 +140,43 @@ def test_chunked_host_errors(lib, kw, status):
     assert chunked(lib, **kw) == status
 
 
+def rows_fwd(lib, **kw):
+    a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
+             dtype=BF16, ignore=-100, mu=0.0, flags=0, lse=P + 0x300000, lp=None, ent=None, rl=None,
+             nv=None, ws=P + 0x700000, wsb=OK_WS, stream=None)
+    a.update(kw)
+    return lib.lce_rows_forward(a["hidden"], a["W"], a["bias"], a["targets"], a["BT"], a["H"], a["V"], a["dtype"],
+                                a["ignore"], a["mu"], a["flags"], a["lse"], a["lp"], a["ent"], a["rl"], a["nv"],
+                                a["ws"], a["wsb"], a["stream"])
+
+
+def rows_bwd(lib, **kw):
+    a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
+             dtype=BF16, ignore=-100, mu=0.0, flags=0, gl=P + 0x300000, gp=None, ge=None,
+             gi=P + 0x400000, gw=P + 0x500000, gb=None, ws=P + 0x700000, wsb=OK_WS, stream=None)
+    a.update(kw)
+    return lib.lce_rows_backward(a["hidden"], a["W"], a["bias"], a["targets"], a["BT"], a["H"], a["V"],
+                                 a["dtype"], a["ignore"], a["mu"], a["flags"], a["gl"], a["gp"], a["ge"], a["gi"],
+                                 a["gw"], a["gb"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), 1), (dict(ws=None), 1), (dict(targets=None), 1), (dict(BT=-1), 2), (dict(H=12), 2),
+    (dict(dtype=F32), 3), (dict(lse=P + 2), 4), (dict(ent=P + 0x800002), 4), (dict(wsb=16), 5),
+    (dict(mu=float("nan")), 6), (dict(flags=2), 6),
+])
+def test_rows_forward_host_errors(lib, kw, status):
+    assert rows_fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), 1), (dict(hidden=None), 1), (dict(V=0), 2), (dict(dtype=F32), 3), (dict(gl=P + 2), 4),
+    (dict(gi=P + 8), 4), (dict(wsb=16), 5), (dict(gb=P + 0x800000), 6), (dict(flags=8), 6),
+])
+def test_rows_backward_host_errors(lib, kw, status):
+    assert rows_bwd(lib, **kw) == status
+
+
 def test_chunked_workspace(lib):
     # one bf16 logits chunk (twice the rows of the pages' fp32 chunk), the grad_input partial
     # sums and the fp32 grad_W sum (left out when grad_W itself is fp32)

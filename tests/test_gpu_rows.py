@@ -1,0 +1,132 @@
+"""GPU parity of the per-row entry points (lce_rows_forward / lce_rows_backward: target
+log-probability, softmax entropy, unreduced row loss, and the gradients of a per-row weighted
+sum of them) against the float64 per-row oracle, through the C ABI, plus the autograd
+wrapper.  The logits pass through a bf16 chunk, so each per-row value is within the bf16
+rounding of the row's logits: |error| <= 2 * 2^-8 * max_v |z_tv| (+ fp32 noise)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_cross_entropy_vocab_amd as lce
+from workloads import make_fused
+from gpu_util import TOL, dev, host64, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (BT, H, V, bias_std, z_loss, ignore_frac, seed)
+    (200, 128, 1000, None, 0.0, 0.2, 61),
+    (333, 256, 3001, 0.1, 1e-3, 0.1, 62),
+    (700, 1280, 5000, 0.1, 1e-4, 0.05, 63),   # two token chunks, column chunks
+    (97, 200, 513, None, 0.0, 0.3, 64),
+    (64, 64, 1, 0.1, 0.0, 0.0, 65),           # V = 1: entropy 0, logprob 0
+]
+
+
+def _inputs(case):
+    BT, H, V, bstd, mu, ign, seed = case
+    inp = make_fused(BT, H, V, dtype="bf16", seed=seed, bias_std=bstd, ignore_frac=ign, z_loss=mu)
+    b = None if inp.bias is None else dev(inp.bias, "bf16")
+    return inp, dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), b, dev(inp.targets)
+
+
+def _row_bound(inp):
+    z = inp.hidden.astype(np.float64) @ inp.weight.astype(np.float64).T
+    if inp.bias is not None:
+        z = z + inp.bias.astype(np.float64)[None, :]
+    return 2.0 * 2.0 ** -8 * np.abs(z).max(axis=1) + 1e-4
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in CASES])
+def test_rows_forward_vs_oracle(case):
+    print(f"rows forward case {case}", flush=True)
+    inp, h, W, b, y = _inputs(case)
+    ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=inp.z_loss)
+    r = lce.lce_rows_forward(h, W, b, y, z_loss=inp.z_loss)
+    torch.cuda.synchronize()
+    assert int(r["n_valid"].item()) == ref["n_valid"]
+    bound = _row_bound(inp)
+    for k in ("lse", "logprobs", "entropy"):
+        err = np.abs(host64(r[k]) - ref[k])
+        assert np.all(err <= bound), (k, float((err / bound).max()))
+    # row_loss adds mu LSE^2: its error also scales with 2 mu |LSE|
+    err = np.abs(host64(r["row_loss"]) - ref["row_loss"])
+    assert np.all(err <= bound * (1.0 + 2.0 * inp.z_loss * np.abs(ref["lse"]))), "row_loss"
+    ign = inp.targets == -100
+    assert np.all(host64(r["logprobs"])[ign] == 0.0) and np.all(host64(r["row_loss"])[ign] == 0.0)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in CASES])
+def test_rows_backward_vs_oracle(case):
+    print(f"rows backward case {case}", flush=True)
+    inp, h, W, b, y = _inputs(case)
+    BT = inp.hidden.shape[0]
+    rng = np.random.default_rng(case[-1])
+    gl, gp, ge = (rng.normal(size=BT).astype(np.float32) for _ in range(3))
+    ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=inp.z_loss,
+                                 grad_row_loss=gl, grad_logprobs=gp, grad_entropy=ge)
+    r = lce.lce_rows_backward(h, W, b, y, grad_row_loss=dev(gl), grad_logprobs=dev(gp), grad_entropy=dev(ge),
+                              z_loss=inp.z_loss)
+    torch.cuda.synchronize()
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        if ref[k] is None:
+            continue
+        e = rel_fro(host64(r[k]), ref[k])
+        assert e <= TOL["bf16"]["grad"], (k, e)
+
+
+def test_rows_backward_single_upstreams_and_fp32_weight():
+    inp, h, W, b, y = _inputs((333, 256, 3001, 0.1, 0.0, 0.1, 66))
+    BT = inp.hidden.shape[0]
+    ge = np.random.default_rng(66).normal(size=BT).astype(np.float32)
+    ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, grad_entropy=ge)
+    r = lce.lce_rows_backward(h, W, b, y, grad_entropy=dev(ge), grad_weight_fp32=True)
+    torch.cuda.synchronize()
+    assert r["grad_weight"].dtype == torch.float32
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        assert rel_fro(host64(r[k]), ref[k]) <= TOL["bf16"]["grad"], k
+    # no upstream gradient at all: every gradient is zero
+    z = lce.lce_rows_backward(h, W, b, y)
+    torch.cuda.synchronize()
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        assert int(torch.count_nonzero(z[k])) == 0, k
+
+
+def test_loss_weights_match_fused_gradients():
+    inp, h, W, b, y = _inputs((333, 256, 3001, 0.1, 1e-3, 0.1, 67))
+    valid = inp.targets != -100
+    c = 1.0 / valid.sum()
+    gl = np.where(valid, c, 0.0).astype(np.float32)
+    r = lce.lce_rows_backward(h, W, b, y, grad_row_loss=dev(gl), z_loss=inp.z_loss)
+    f = lce.lce_fwd_bwd(h, W, b, y, z_loss=inp.z_loss, method="chunked")
+    torch.cuda.synchronize()
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        # (two separately rounded bf16 dlogits: about 2^-9 relative noise each)
+        assert rel_fro(host64(r[k]), host64(f[k])) <= 5e-3, k
+
+
+def test_autograd_wrapper():
+    inp, h, W, b, y = _inputs((200, 128, 1000, 0.1, 0.0, 0.2, 68))
+    BT = inp.hidden.shape[0]
+    rng = np.random.default_rng(68)
+    a1, a2, a3 = (rng.normal(size=BT).astype(np.float32) for _ in range(3))
+    hh = h.clone().requires_grad_(True)
+    WW = W.clone().requires_grad_(True)
+    bb = b.clone().requires_grad_(True)
+    lp, ent, rl = lce.linear_logprobs_entropy(hh, WW, y, bb)
+    (lp * dev(a2)).sum().backward(retain_graph=True)
+    g1 = hh.grad.clone()
+    hh.grad = None
+    WW.grad = None
+    bb.grad = None
+    total = (rl * dev(a1)).sum() + (lp * dev(a2)).sum() + (ent * dev(a3)).sum()
+    total.backward()
+    ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, grad_row_loss=a1,
+                                 grad_logprobs=a2, grad_entropy=a3)
+    assert rel_fro(host64(hh.grad), ref["grad_input"]) <= TOL["bf16"]["grad"]
+    assert rel_fro(host64(WW.grad), ref["grad_weight"]) <= TOL["bf16"]["grad"]
+    assert rel_fro(host64(bb.grad), ref["grad_bias"]) <= TOL["bf16"]["grad"]
+    ref1 = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, grad_logprobs=a2)
+    assert rel_fro(host64(g1), ref1["grad_input"]) <= TOL["bf16"]["grad"]
