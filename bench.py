@@ -142,6 +142,31 @@ def bench_chunked(lce, torch, h, W, b, y, kw, exact, steps, BT) -> dict:
             "rel_diff_vs_fused": diffs}
 
 
+def bench_rows(lce, torch, h, W, b, y, steps, BT) -> dict:
+    """Per-row outputs for RL-style use on the same workload: the forward (LSE, target
+    log-probability, entropy, row loss) and the backward of a per-row weighted sum of them."""
+    r = lce.lce_rows_forward(h, W, b, y)
+    ws = r["workspace"]
+    g = [torch.randn(BT, device="cuda", dtype=torch.float32) for _ in range(3)]
+    lce.lce_rows_backward(h, W, b, y, grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2], workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lce.lce_rows_forward(h, W, b, y, workspace=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        lce.lce_rows_backward(h, W, b, y, grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2],
+                              workspace=ws)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    fwd = (t1 - t0) * 1e3 / steps
+    bwd = (t2 - t1) * 1e3 / steps
+    return {"forward_ms": fwd, "backward_ms": bwd, "tokens_per_s": BT / ((fwd + bwd) * 1e-3),
+            "workspace_bytes": int(ws.numel()),
+            "mean_entropy": float(r["entropy"].mean().item())}
+
+
 def cpu_baseline(inp, n_tokens: int) -> dict:
     """The float64 oracle (as it stands) on the first n_tokens rows of the same workload."""
     import oracle
@@ -204,6 +229,7 @@ def main():
                          "Qwen-like) and print one JSON line per workload")
     ap.add_argument("--filter-eps", type=float, default=FILTER_EPS)
     ap.add_argument("--no-chunked", action="store_true", help="skip the token-chunked composition leg")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row outputs leg")
     ap.add_argument("--compare-methods", action="store_true",
                     help="only time the fused path and the token-chunked composition on the three "
                          "LM-head workloads and print one JSON line per workload")
@@ -376,6 +402,9 @@ def main():
     if not args.no_chunked:
         log("token-chunked composition leg")
         res["chunked"] = bench_chunked(lce, torch, h, W, None, y, kw, out, args.steps, BT)
+    if not args.no_rows:
+        log("per-row outputs leg")
+        res["rows"] = bench_rows(lce, torch, h, W, None, y, args.steps, BT)
     if not args.no_filter:
         log(f"gradient filtering, eps {args.filter_eps:g}")
         res["filtered"] = bench_filtered(lce, torch, h, W, y, kw, out, args.filter_eps, args.steps, BT)

@@ -47,7 +47,8 @@ typedef enum lce_status {
 
 typedef enum lce_dtype {
   LCE_DTYPE_F32 = 0,
-  LCE_DTYPE_BF16 = 1
+  LCE_DTYPE_BF16 = 1,
+  LCE_DTYPE_F16 = 2   /* IEEE half: lce_ce_with_grad_inplace only */
 } lce_dtype;
 
 typedef enum lce_reduction {
@@ -165,7 +166,8 @@ const char* lce_stage_name(int k);
  *   dlogits_i = valid_i * ( softmax(x_i) * (1 + 2 * z_loss_mult * LSE(x_i)) - onehot(y_i) ),
  * rounded to the logits' dtype; ignored rows are written as zeros.  A mean-reduced loss is
  * ce_sum / max(n_valid, 1) and its gradient is these dlogits times the same factor.
- *   logits      [B, V] in `dtype` (LCE_DTYPE_BF16 or LCE_DTYPE_F32), read then overwritten.
+ *   logits      [B, V] in `dtype` (LCE_DTYPE_BF16, LCE_DTYPE_F16 or LCE_DTYPE_F32; the page's
+ *               kernel takes float16, bfloat16 and float32 logits), read then overwritten.
  *   targets     [B] int64.   B >= 0, V >= 1.   z_loss_mult >= 0.
  *   workspace   >= lce_ce_workspace_bytes(B, V, dtype) bytes.
  * Targets outside [0, V) that are not ignore_index are treated as ignored.

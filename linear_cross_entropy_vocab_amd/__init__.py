@@ -23,7 +23,7 @@ from ._lib import LCEError, load  # noqa: F401
 __all__ = ["lce_fwd_bwd", "lce_ce_with_grad_inplace", "linear_cross_entropy", "fwd_bwd_workspace_bytes",
            "ce_workspace_bytes", "stage_names", "version", "LCEError", "load"]
 
-_DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_F32}
+_DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float32: _lib.DTYPE_F32, torch.float16: _lib.DTYPE_F16}
 _REDUCTIONS = {"mean": _lib.REDUCTION_MEAN, "sum": _lib.REDUCTION_SUM}
 
 
@@ -33,7 +33,7 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
     return _DTYPES[t.dtype]
 
 

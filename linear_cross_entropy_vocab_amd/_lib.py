@@ -14,6 +14,7 @@ STATUS_NAMES = {0: "LCE_OK", 1: "LCE_ERR_NULL", 2: "LCE_ERR_SHAPE", 3: "LCE_ERR_
                 7: "LCE_ERR_TARGET_RANGE", 8: "LCE_ERR_HIP"}
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 REDUCTION_MEAN = 0
 REDUCTION_SUM = 1
 FLAG_CHECK_TARGETS = 1

@@ -291,7 +291,7 @@ const char* lce_stage_name(int k) {
 
 size_t lce_ce_workspace_bytes(int64_t B, int64_t V, lce_dtype dtype) {
   if (B < 0 || V < 1) return 0;
-  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return 0;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32 && dtype != LCE_DTYPE_F16) return 0;
   return lce::ce_workspace_bytes(B);
 }
 
@@ -300,18 +300,19 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
                                     float* z_sum_out, int64_t* n_valid_out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
   if (B < 0 || V < 1 || V > ((int64_t)1 << 40) || B > ((int64_t)1 << 31) - 1) return LCE_ERR_SHAPE;
-  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_DTYPE;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32 && dtype != LCE_DTYPE_F16) return LCE_ERR_DTYPE;
   if (ce_sum_out == nullptr || z_sum_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
   if (B > 0 && (logits == nullptr || targets == nullptr)) return LCE_ERR_NULL;
   if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
-  const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
+  const size_t es = dtype == LCE_DTYPE_F32 ? 4 : 2;
   if (!lce::aligned(logits, 16) || !lce::aligned(workspace, 16) || !lce::aligned(targets, 8) ||
       !lce::aligned(ce_sum_out, 4) || !lce::aligned(z_sum_out, 4) || !lce::aligned(n_valid_out, 8))
     return LCE_ERR_ALIGNMENT;
   (void)es;
   if (workspace_bytes < lce::ce_workspace_bytes(B)) return LCE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (lce::launch_ce_inplace(logits, dtype == LCE_DTYPE_BF16, targets, B, V, V, ignore_index, z_loss_mult,
+  const int ct = dtype == LCE_DTYPE_BF16 ? lce::kCeBf16 : (dtype == LCE_DTYPE_F16 ? lce::kCeF16 : lce::kCeF32);
+  if (lce::launch_ce_inplace(logits, ct, targets, B, V, V, ignore_index, z_loss_mult,
                              ce_sum_out, z_sum_out, n_valid_out, nullptr, workspace, st) != hipSuccess)
     return LCE_ERR_HIP;
   return LCE_OK;

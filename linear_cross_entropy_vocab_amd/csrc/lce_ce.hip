@@ -49,6 +49,28 @@ template <> struct Vec16<bf16_t> {
     return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0) << 16);
   }
 };
+template <> struct Vec16<f16_t> {
+  static constexpr int N = 8;
+  uint4 raw;
+  __device__ static uint4 neg_inf() { return make_uint4(0xfc00fc00u, 0xfc00fc00u, 0xfc00fc00u, 0xfc00fc00u); }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = (&raw.x)[i >> 1];
+    return (float)__builtin_bit_cast(f16_t, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  // (as for bf16: an asm conversion the optimiser cannot merge with the first pass's)
+  __device__ __forceinline__ float fresh(int i) const {
+    const uint32_t w = (&raw.x)[i >> 1];
+    float r;
+    if (i & 1)
+      asm volatile("v_lshrrev_b32 %0, 16, %1\n\tv_cvt_f32_f16 %0, %0" : "=&v"(r) : "v"(w));
+    else
+      asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(r) : "v"(w));
+    return r;
+  }
+  __device__ static float elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (float)__builtin_bit_cast(f16_t, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+  }
+};
 template <> struct Vec16<float> {
   static constexpr int N = 4;
   uint4 raw;
@@ -63,6 +85,12 @@ template <> struct Vec16<float> {
 __device__ __forceinline__ uint4 pack_out(const float* v, bf16_t) {
   return make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
                     pack_bf2(v[6], v[7]));
+}
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (f16_t)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (f16_t)b) << 16);
+}
+__device__ __forceinline__ uint4 pack_out(const float* v, f16_t) {
+  return make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]), pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
 }
 __device__ __forceinline__ uint4 pack_out(const float* v, float) {
   return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
@@ -91,6 +119,16 @@ __device__ __forceinline__ void mask_tail(Vec16<bf16_t>& v, int64_t c0, int64_t 
     uint32_t& x = (&v.raw.x)[d];
     const uint32_t lo = (c0 + 2 * d < V) ? (x & 0x0000ffffu) : 0x0000ff80u;
     const uint32_t hi = (c0 + 2 * d + 1 < V) ? (x & 0xffff0000u) : 0xff800000u;
+    x = lo | hi;
+  }
+}
+template <>
+__device__ __forceinline__ void mask_tail(Vec16<f16_t>& v, int64_t c0, int64_t V) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t& x = (&v.raw.x)[d];
+    const uint32_t lo = (c0 + 2 * d < V) ? (x & 0x0000ffffu) : 0x0000fc00u;
+    const uint32_t hi = (c0 + 2 * d + 1 < V) ? (x & 0xffff0000u) : 0xfc000000u;
     x = lo | hi;
   }
 }
@@ -484,7 +522,7 @@ static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int6
   return hipGetLastError();
 }
 
-hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, int64_t B, int64_t V,
+hipError_t launch_ce_inplace(void* logits, int dtype, const int64_t* targets, int64_t B, int64_t V,
                              int64_t ld, int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
                              int64_t* n_valid, float* lse_rows, void* workspace, hipStream_t st) {
   CERowOut out;
@@ -496,8 +534,12 @@ hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, in
   out.valid = reinterpret_cast<int32_t*>(ws + 2 * a);
   hipError_t e = hipSuccess;
   if (B > 0) {
-    e = bf16 ? launch_rows<bf16_t>(static_cast<bf16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, st)
-             : launch_rows<float>(static_cast<float*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
+    if (dtype == kCeBf16)
+      e = launch_rows<bf16_t>(static_cast<bf16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
+    else if (dtype == kCeF16)
+      e = launch_rows<f16_t>(static_cast<f16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
+    else
+      e = launch_rows<float>(static_cast<float*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(ce_reduce, dim3(1), dim3(kCEThreads), 0, st, out.ce, out.zsq, out.valid, B,

@@ -139,7 +139,7 @@ hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bo
         hipSuccess)
       return e;
     if (mode == kLoss) {
-      e = launch_ce_inplace(zbuf, true, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k, z_k + k,
+      e = launch_ce_inplace(zbuf, kCeBf16, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k, z_k + k,
                             nv_k + k, offw(a.lse_out, r0), ce_ws, st);
     } else {
       e = launch_rows_stats(zbuf, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, offw(io.lse, r0),

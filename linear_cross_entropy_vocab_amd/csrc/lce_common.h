@@ -41,6 +41,12 @@ template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static float to_f(bf16_t v) { return bf2f(v); }
   __device__ __forceinline__ static bf16_t from_f(float v) { return f2bf(v); }
 };
+typedef _Float16 f16_t;  // IEEE half (standalone cross-entropy only)
+template <> struct Elem<f16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float to_f(f16_t v) { return (float)v; }
+  __device__ __forceinline__ static f16_t from_f(float v) { return (f16_t)v; }  // nearest even
+};
 template <> struct Elem<float> {
   static constexpr int kBytes = 4;
   __device__ __forceinline__ static float to_f(float v) { return v; }

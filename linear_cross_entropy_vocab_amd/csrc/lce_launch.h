@@ -121,7 +121,8 @@ hipError_t launch_rows_stats(void* logits, const int64_t* targets, int64_t B, in
 size_t ce_workspace_bytes(int64_t B);
 // Rows are ld >= V elements apart; with ld > V the rows must be 16-byte aligned and the
 // columns V..ld-1 are overwritten with 0.
-hipError_t launch_ce_inplace(void* logits, bool bf16, const int64_t* targets, int64_t B, int64_t V,
+enum { kCeF32 = 0, kCeBf16 = 1, kCeF16 = 2 };  // element type of the logits
+hipError_t launch_ce_inplace(void* logits, int dtype, const int64_t* targets, int64_t B, int64_t V,
                              int64_t ld, int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
                              int64_t* n_valid, float* lse_rows, void* workspace, hipStream_t st);
 

@@ -12,10 +12,12 @@ TOL = {
 # Standalone cross-entropy: dlogits rounded to the logits' dtype.
 CE_TOL = {
     "bf16": dict(sums=1e-3, dlogits=1e-2),
+    # fp16 logits: sums in fp32 from exact inputs; dlogits rounded once to half (2^-11)
+    "f16": dict(sums=1e-5, dlogits=1e-3),
     "f32": dict(sums=1e-5, dlogits=1e-5),
 }
 
-TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}
 
 
 def dev(a, dtype="f32"):

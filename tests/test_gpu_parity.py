@@ -155,6 +155,11 @@ CE_CASES = [
     ("bf16", 6, 20000, 1e-4, 0.2, 38),     # 3 vectors per thread, cached as 4: partial upper half
     ("f32", 5, 13000, 0.0, 0.0, 39),       # 4 per thread, the last one partial
     ("bf16", 4, 150000, 0.0, 0.25, 40),    # past the register cache, 16-byte rows: vector stream
+    ("f16", 64, 1000, 1e-3, 0.1, 41),      # IEEE half logits
+    ("f16", 6, 20000, 0.0, 0.2, 42),
+    ("f16", 8, 131072, 1e-4, 0.25, 43),    # largest register-cached half row
+    ("f16", 4, 150000, 1e-4, 0.0, 44),     # vector stream
+    ("f16", 7, 1001, 0.0, 0.1, 45),        # scalar stream (row bytes not a multiple of 16)
 ]
 
 

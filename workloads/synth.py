@@ -168,6 +168,8 @@ def make_ce(B: int, V: int, *, dtype: str = "bf16", seed: int = 0, logit_std: fl
     y = ce_targets(B, V, seed=seed, ignore_frac=ignore_frac)
     if dtype == "bf16":
         x = bf16_round(x)
+    elif dtype == "f16":
+        x = x.astype(np.float16).astype(np.float32)  # nearest even in IEEE half
     elif dtype != "f32":
         raise ValueError(dtype)
     return CEInputs(x, y, dtype)
