@@ -60,8 +60,9 @@ typedef enum lce_reduction {
  * target is neither ignore_index nor a vocabulary id.  Without it such rows are treated
  * as ignored (no loss, zero gradient) and the call still returns LCE_OK. */
 #define LCE_FLAG_CHECK_TARGETS 1u
-/* (lce_fwd_bwd_chunked only) grad_W is float32 [V, H]: the sum over the token chunks is kept
- * in it directly, so the workspace needs no fp32 accumulator of its own. */
+/* grad_W is float32 [V, H] for bf16 inputs (rounded once from the fp32 accumulators instead
+ * of to bf16).  In the chunked entry points the sum over the token chunks is kept in it
+ * directly, so their workspace needs no fp32 accumulator of its own. */
 #define LCE_FLAG_GRAD_W_FP32 2u
 
 /* Number of device kernels one lce_fwd_bwd call may launch (for lce_fwd_bwd_profiled). */
@@ -90,10 +91,11 @@ typedef enum lce_reduction {
  *   ignore_index  target value of ignored rows (usually -100).
  *   z_loss_mult   >= 0; 0 disables the z-loss term.
  *   reduction   LCE_REDUCTION_MEAN or LCE_REDUCTION_SUM.
- *   flags       0 or LCE_FLAG_CHECK_TARGETS.
+ *   flags       0, LCE_FLAG_CHECK_TARGETS and/or LCE_FLAG_GRAD_W_FP32.
  *   loss_out    device float[1]: the loss L.                          (required)
  *   grad_input  device [BT, H] in `dtype`, fully overwritten, or NULL to skip it.
- *   grad_W      device [V, H] in `dtype`, fully overwritten, or NULL to skip it.
+ *   grad_W      device [V, H] in `dtype` (float32 with LCE_FLAG_GRAD_W_FP32), fully
+ *               overwritten, or NULL to skip it.
  *   grad_b      device [V] in `dtype`, fully overwritten, or NULL; must be NULL when bias is NULL.
  *   n_valid_out device int64[1]: number of rows with y != ignore_index, or NULL.
  *   lse_out     device float[BT]: LSE(z_t) per row (the statistic the backward reuses,

@@ -82,8 +82,9 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     selects lce_fwd_bwd_profiled.  filter_eps > 0 selects lce_fwd_bwd_filtered (lossy
     gradient filtering); filter_counts (int64 [4] on the device) then receives the skipped
     and examined tile counts of the grad_input and grad_W passes.  method="chunked" selects
-    lce_fwd_bwd_chunked (the token-chunked composition; bf16 only), where grad_weight_fp32
-    makes grad_weight a float32 tensor that holds the sum over the chunks directly;
+    lce_fwd_bwd_chunked (the token-chunked composition; bf16 only).  grad_weight_fp32 (bf16
+    inputs) makes grad_weight a float32 tensor (in the chunked composition it then holds the
+    sum over the chunks directly);
     method="auto" takes the chunked composition for bf16 with H > 1024, else the fused path.
     """
     if method not in ("fused", "chunked", "auto"):
@@ -94,8 +95,8 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
         method = "chunked" if (hidden.dtype == torch.bfloat16 and hidden.shape[1] > 1024
                                and filter_eps == 0.0 and events is None) else "fused"
     chunked = method == "chunked"
-    if grad_weight_fp32 and not chunked:
-        raise ValueError("grad_weight_fp32 needs method='chunked'")
+    if grad_weight_fp32 and hidden.dtype != torch.bfloat16:
+        raise ValueError("grad_weight_fp32 applies to bf16 inputs")
     if chunked and (filter_eps > 0.0 or events is not None):
         raise ValueError("filter_eps and events are not supported with method='chunked'")
     lib = load()

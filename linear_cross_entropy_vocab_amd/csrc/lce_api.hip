@@ -70,7 +70,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_SUM) return LCE_ERR_ARG;
   if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
   if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
-  if ((flags & ~LCE_FLAG_CHECK_TARGETS) != 0) return LCE_ERR_ARG;
+  if ((flags & ~(LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32)) != 0) return LCE_ERR_ARG;
   if (!(filter_eps >= 0.f) || !std::isfinite(filter_eps)) return LCE_ERR_ARG;
   const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
   if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(grad_input, 16) || !aligned(grad_W, 16) ||
@@ -97,6 +97,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   a.grad_b = grad_b;
   a.n_valid_out = n_valid_out;
   a.lse_out = lse_out;
+  a.grad_w_f32 = (flags & LCE_FLAG_GRAD_W_FP32) != 0 && dtype == LCE_DTYPE_BF16;
   a.filter_eps = filter_eps;
   a.filter_counts = filter_eps > 0.f ? filter_counts : nullptr;
   const FusedWs w = fused_carve(workspace, BT, V);

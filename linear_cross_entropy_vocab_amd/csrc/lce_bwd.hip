@@ -51,6 +51,7 @@ struct BwdArgs {
   const int64_t* n_valid;
   int mean;
   T* out;
+  float* out_f32;  // (bf16 inputs) fp32 output instead of out, or NULL
   T* grad_b;
   int64_t nchunks;
 };
@@ -447,6 +448,18 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
         for (int r = 0; r < 16; ++r) {
           const int64_t row = s0 + sb * 32 + acc_row(lane, r);
           if (row < p.nS && col < H) p.out[row * H + col] = Elem<T>::from_f(cscale * acc[sb][cb][r]);
+        }
+      }
+  } else if (p.out_f32 != nullptr) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t col = hw0 + cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+          if (row < p.nS && col < H) p.out_f32[row * H + col] = cscale * acc[sb][cb][r];
         }
       }
   }
@@ -851,6 +864,18 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
           if (row < p.nS && col < H) p.out[row * H + col] = f2bf(cscale * acc[sb][cb][r]);
         }
       }
+  } else if (p.out_f32 != nullptr) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t col = kw0 + cb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+          if (row < p.nS && col < H) p.out_f32[row * H + col] = cscale * acc[sb][cb][r];
+        }
+      }
   }
   if (DW && p.grad_b != nullptr) {
 #pragma unroll
@@ -956,13 +981,15 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
     a.nS = fa.BT;
     a.nX = fa.V;
     a.out = static_cast<T*>(fa.grad_input);
+    a.out_f32 = nullptr;
     a.grad_b = nullptr;
   } else {
     a.S = static_cast<const T*>(fa.W);
     a.X = static_cast<const T*>(fa.hidden);
     a.nS = fa.V;
     a.nX = fa.BT;
-    a.out = static_cast<T*>(fa.grad_W);
+    a.out = fa.grad_w_f32 ? nullptr : static_cast<T*>(fa.grad_W);
+    a.out_f32 = fa.grad_w_f32 ? static_cast<float*>(fa.grad_W) : nullptr;
     a.grad_b = static_cast<T*>(fa.grad_b);
   }
   const BwdPlan pl = bwd_plan(fa.H, sizeof(T) == 2);

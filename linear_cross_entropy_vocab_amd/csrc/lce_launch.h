@@ -49,6 +49,7 @@ struct FusedArgs {
   void* grad_b;
   int64_t* n_valid_out;
   float* lse_out;
+  bool grad_w_f32;           // (bf16 inputs) grad_W is written in fp32
   float filter_eps;          // > 0: gradient filtering (tiles of |dlogits| < eps are skipped)
   int64_t* filter_counts;    // [4] skipped / examined tiles of the grad_input and grad_W passes, or NULL
 };

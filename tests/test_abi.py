@@ -89,7 +89,7 @@ def fused(lib, **kw):
     (dict(targets=P + 4), 4), (dict(loss=P + 2), 4),
     (dict(wsb=16), 5),
     (dict(red=2), 6), (dict(mu=-1.0), 6), (dict(mu=float("nan")), 6), (dict(mu=float("inf")), 6),
-    (dict(gb=P + 0x800000), 6), (dict(flags=2), 6),
+    (dict(gb=P + 0x800000), 6), (dict(flags=4), 6),
 ])
 def test_fused_host_errors(lib, kw, status):
     assert fused(lib, **kw) == status

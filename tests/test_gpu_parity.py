@@ -105,6 +105,21 @@ def test_grad_subsets():
     assert rel_fro(host64(r["grad_input"]), ref["grad_input"]) <= TOL["bf16"]["grad"]
 
 
+def test_fused_grad_weight_fp32():
+    inp = make_fused(333, 256, 3001, dtype="bf16", seed=12, bias_std=0.1, ignore_frac=0.1, z_loss=1e-3)
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=1e-3)
+    r32 = run_fused(inp, grad_weight_fp32=True)
+    assert r32["grad_weight"].dtype == torch.float32
+    check_fused(inp, r32, ref)
+    r16 = run_fused(inp)
+    # the bf16 output is the same fp32 accumulator rounded once more
+    assert torch.equal(r32["grad_weight"].to(torch.bfloat16), r16["grad_weight"])
+    big = make_fused(65, 2304, 257, dtype="bf16", seed=16, ignore_frac=0.05)   # column-chunked kernel
+    a32 = run_fused(big, grad_weight_fp32=True)
+    a16 = run_fused(big)
+    assert torch.equal(a32["grad_weight"].to(torch.bfloat16), a16["grad_weight"])
+
+
 def test_deterministic_bits():
     inp = make_fused(333, 256, 3001, dtype="bf16", seed=12, bias_std=0.1, ignore_frac=0.1, z_loss=1e-3)
     a = run_fused(inp)
