@@ -38,6 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 COPY_CAL_BYTES = 1 << 30    # size of the calibration copy (--copy-calibration)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy.json")
 FILTER_EPS = 2.0 ** -12     # gradient-filtering threshold of the lossy leg (a bf16-scale floor)
 
 
@@ -67,6 +68,21 @@ def _sha(path: str) -> str:
     import hashlib
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _profile_value(path: str, kernel: str, key: str):
+    """A per-kernel figure from a committed counter summary, or None when the summary is
+    missing or the kernel's sources changed since the counters were taken."""
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    for rel, sha in rec["sources"].items():
+        fp = os.path.join(ROOT, rel)
+        if not os.path.exists(fp) or _sha(fp) != sha:
+            return None
+    return rec[key]
 
 
 def measured_traffic(kernel: str):
@@ -389,7 +405,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom), "kernel": dom,
-                     "algorithmic_flops_per_launch": algo_flops[dom]},
+                     "algorithmic_flops_per_launch": algo_flops[dom],
+                     "mfma_busy_counter": _profile_value(MFMA_FILE, dom, "mfma_busy")},
         "tflops_executed": executed,
         "tflops_useful": useful,
         "mfma_util_executed": executed / PEAK_BF16_TFLOPS,
