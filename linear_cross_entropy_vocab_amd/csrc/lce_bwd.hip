@@ -784,16 +784,20 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
         for (int i = 0; i < 4; ++i) gb[i] += gpend[i];
       }
     }
+    // Every operand read is issued before the first refill: a refill is an asm statement with
+    // a memory clobber, so no LDS read can be moved across it, and reads issued after it would
+    // leave the MFMAs waiting for each read's latency.
     Frag<bf16_t> ga[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) ga[sb].v = tr_pair(gl + o_ga[sb][0], gl + o_ga[sb][1]);
+    Frag<bf16_t> xf[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) xf[cb].v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      Frag<bf16_t> xf;
-      xf.v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
-      mfma_32x32x16(ga[0], xf, acc[0][cb]);
-      mfma_32x32x16(ga[1], xf, acc[1][cb]);
-      if (refill && cb < NB / 2) dma16_after(rx_next, lds_next + 1024 * cb, dma_off + 64 * cb, xf.v);
+      mfma_32x32x16(ga[0], xf[cb], acc[0][cb]);
+      mfma_32x32x16(ga[1], xf[cb], acc[1][cb]);
+      if (refill && cb < NB / 2) dma16_after(rx_next, lds_next + 1024 * cb, dma_off + 64 * cb, xf[cb].v);
     }
   };
   // (the reads of these planes completed in the previous phase: GEMM3 waited for them)
@@ -834,6 +838,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     take_col(i, bi);
     gemm1_reads(bn, C0{}, CH{});
     gemm1_part(C0{}, CH{});
+    // (keeps the dlogits arithmetic below the MFMAs, so that it runs while they execute
+    // instead of delaying their issue)
+    __builtin_amdgcn_sched_barrier(0);
     dlogits();
     gemm1_reads(bn, CH{}, CN{});  // in flight across the barrier
     if (i > 0) refill_rest();     // second half of tile i+3 (the buffer of tile i-1)
