@@ -225,10 +225,23 @@ def bench_ce(lce, torch, steps: int) -> dict:
     ms = e0.elapsed_time(e1) / steps
     algo_bytes = 2 * c.B * c.V * 2 + 8 * c.B
     gbs = algo_bytes / (ms * 1e-3) / 1e9
+    # reference: a plain device copy of the same logits moves the same bytes (one read, one
+    # write per element) and shows what streaming rate this device sustains
+    dst = torch.empty_like(x)
+    dst.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_copy = e0.elapsed_time(e1) / steps
+    copy_gbs = 2 * c.B * c.V * 2 / (ms_copy * 1e-3) / 1e9
     return {"workload": f"standalone CE+dlogits in place, [{c.B}, {c.V}] bf16, z-loss 0",
             "ms": ms, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("ce_rows")},
-            "algorithmic_bytes": algo_bytes}
+            "algorithmic_bytes": algo_bytes,
+            "device_copy_same_bytes": {"ms": ms_copy, "GB/s": copy_gbs, "ce_vs_copy": gbs / copy_gbs}}
 
 
 def main():
