@@ -9,11 +9,13 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor argument is a DEVICE pointer owned by the caller.  The library never
- *    allocates device memory and keeps no state between calls; scratch space is the
- *    caller's `workspace` buffer, sized by the matching *_workspace_bytes function.
+ *    allocates device memory and keeps no state between calls (apart from a per-device
+ *    cache of the compute-unit count); scratch space is the caller's `workspace` buffer,
+ *    sized by the matching *_workspace_bytes function.
  *  - Layouts are dense row-major: hidden [BT, H], W [V, H] (nn.Linear layout, [P1] "The
  *    setting"), logits [B, V]; targets are int64.  Tensor pointers and the workspace must
- *    be 16-byte aligned.  H must be a multiple of 8.
+ *    be 16-byte aligned.  H must be a multiple of 8.  Vocabulary sizes and target ids are
+ *    below 2^31 (targets are compared as 32-bit ids on the device).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and is
  *    asynchronous: outputs are valid once the stream has completed.  Nothing is copied
  *    to the host unless LCE_FLAG_CHECK_TARGETS is given.

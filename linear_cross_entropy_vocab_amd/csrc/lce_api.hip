@@ -63,7 +63,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
                              int64_t* filter_counts) {
   // ---- validation: no HIP calls before this block has passed
   if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
-  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 40) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
+  if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 31) - 2 || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
   if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_DTYPE;
   if (W == nullptr || loss_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
   if (BT > 0 && (hidden == nullptr || targets == nullptr)) return LCE_ERR_NULL;
@@ -300,7 +300,7 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
                                     int64_t ignore_index, float z_loss_mult, float* ce_sum_out,
                                     float* z_sum_out, int64_t* n_valid_out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  if (B < 0 || V < 1 || V > ((int64_t)1 << 40) || B > ((int64_t)1 << 31) - 1) return LCE_ERR_SHAPE;
+  if (B < 0 || V < 1 || V > ((int64_t)1 << 31) - 2 || B > ((int64_t)1 << 31) - 1) return LCE_ERR_SHAPE;
   if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32 && dtype != LCE_DTYPE_F16) return LCE_ERR_DTYPE;
   if (ce_sum_out == nullptr || z_sum_out == nullptr || workspace == nullptr) return LCE_ERR_NULL;
   if (B > 0 && (logits == nullptr || targets == nullptr)) return LCE_ERR_NULL;

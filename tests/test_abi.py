@@ -84,6 +84,7 @@ def fused(lib, **kw):
     (dict(W=None), 1), (dict(loss=None), 1), (dict(ws=None), 1), (dict(hidden=None), 1),
     (dict(targets=None), 1),
     (dict(BT=-1), 2), (dict(V=0), 2), (dict(H=0), 2), (dict(H=12), 2), (dict(H=4), 2),
+    (dict(V=1 << 31), 2),
     (dict(dtype=2), 3), (dict(dtype=-1), 3),
     (dict(hidden=P + 8), 4), (dict(W=P + 4), 4), (dict(gi=P + 2), 4), (dict(ws=P + 8), 4),
     (dict(targets=P + 4), 4), (dict(loss=P + 2), 4),
@@ -206,7 +207,7 @@ def ce(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(logits=None), 1), (dict(ce=None), 1), (dict(z=None), 1), (dict(ws=None), 1),
-    (dict(B=-1), 2), (dict(V=0), 2), (dict(dtype=5), 3),
+    (dict(B=-1), 2), (dict(V=0), 2), (dict(V=1 << 31), 2), (dict(dtype=5), 3),
     (dict(logits=P + 2), 4), (dict(ws=P + 4), 4), (dict(targets=P + 4), 4),
     (dict(wsb=8), 5), (dict(mu=-0.5), 6), (dict(mu=math.nan), 6),
 ])
