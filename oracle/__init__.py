@@ -21,6 +21,7 @@ from .lce import (  # noqa: F401
     TargetRangeError,
     lce_oracle,
     lce_oracle_filtered,
+    vocab_sort_order,
     lce_rows_oracle,
     ce_oracle,
     lse_rows,

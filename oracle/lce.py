@@ -253,10 +253,34 @@ def _block_keep(g: np.ndarray, rows: int, cols: int, eps: float):
     return keep, skipped
 
 
+def vocab_sort_order(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDEX,
+                     rows_per_chunk: Optional[int] = None):
+    """Vocabulary sorting of [P2] "Vocabulary Sorting": each vocabulary entry's average logit
+    over the batch (here over the rows that count, divided by max(n_valid, 1)), and the order
+    of the entries by decreasing average logit (ties by increasing id).  Returns
+    (logit_avg [V], perm [V]) with perm[i] = the id at sorted position i."""
+    h = _f64(hidden)
+    W = _f64(weight)
+    b = _f64(bias)
+    y = np.asarray(targets, dtype=np.int64)
+    BT = h.shape[0]
+    V = W.shape[0]
+    valid = _valid_mask(y, V, ignore_index)
+    total = np.zeros(V)
+    R = rows_per_chunk or _rows_per_chunk(V)
+    for r0 in range(0, BT, R):
+        r1 = min(BT, r0 + R)
+        z = _logits(h[r0:r1], W, b)
+        total += z[valid[r0:r1]].sum(axis=0)
+    avg = total / max(int(valid.sum()), 1)
+    perm = np.argsort(-avg, kind="stable")
+    return avg, perm
+
+
 def lce_oracle_filtered(hidden, weight, bias, targets, *, filter_eps: float,
                         ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
                         reduction: str = "mean", stat_rows: int = 64,
-                        stream_rows: int = 16) -> dict:
+                        stream_rows: int = 16, sort_vocab: bool = False) -> dict:
     """The gradients with CCE-style gradient filtering ([P2] "Gradient Filtering").
 
     Each gradient GEMM sees the dlogits in tiles; a tile whose entries are all below
@@ -270,7 +294,32 @@ def lce_oracle_filtered(hidden, weight, bias, targets, *, filter_eps: float,
     batch size.  The loss is not affected.  Returns the lce_oracle dict with the filtered
     gradients and the tile counts skipped_input / tiles_input, skipped_weight /
     tiles_weight.
+    With sort_vocab, the vocabulary is first put in the order of vocab_sort_order
+    ([P2] "Vocabulary Sorting": W rows, bias entries and target ids permuted), the filtered
+    gradients are computed in that order (so the tiles group entries of similar average
+    logit), and grad_W / grad_b are returned in the original order (plus vocab_perm and
+    logit_avg).
     """
+    if sort_vocab:
+        avg, perm = vocab_sort_order(hidden, weight, bias, targets, ignore_index=ignore_index)
+        pos = np.empty_like(perm)
+        pos[perm] = np.arange(len(perm))
+        y0 = np.asarray(targets, dtype=np.int64)
+        ys = np.where(y0 == ignore_index, y0, pos[np.clip(y0, 0, len(perm) - 1)])
+        Ws = _f64(weight)[perm]
+        bs = None if bias is None else _f64(bias)[perm]
+        out = lce_oracle_filtered(hidden, Ws, bs, ys, filter_eps=filter_eps, ignore_index=ignore_index,
+                                  z_loss=z_loss, reduction=reduction, stat_rows=stat_rows,
+                                  stream_rows=stream_rows)
+        gw = np.empty_like(out["grad_weight"])
+        gw[perm] = out["grad_weight"]
+        out["grad_weight"] = gw
+        if out["grad_bias"] is not None:
+            gb = np.empty_like(out["grad_bias"])
+            gb[perm] = out["grad_bias"]
+            out["grad_bias"] = gb
+        out.update(vocab_perm=perm, logit_avg=avg)
+        return out
     h = _f64(hidden)
     W = _f64(weight)
     b = _f64(bias)

@@ -125,3 +125,59 @@ def test_brute_force_with_mixed_blocks():
     np.testing.assert_allclose(f["grad_input"], np.array(gi), rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(f["grad_weight"], np.array(gw), rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(f["grad_bias"], np.array(gb), rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------- vocabulary sorting
+
+def test_logit_average_is_the_logit_of_the_mean_hidden_row():
+    # linearity: the batch mean of z_t = W h_t + b over the rows that count is W hbar + b
+    inp = make_fused(90, 12, 70, dtype="f32", seed=31, bias_std=0.4, ignore_frac=0.2)
+    avg, perm = oracle.vocab_sort_order(inp.hidden, inp.weight, inp.bias, inp.targets)
+    valid = inp.targets != -100
+    hbar = inp.hidden.astype(np.float64)[valid].mean(axis=0)
+    np.testing.assert_allclose(avg, inp.weight.astype(np.float64) @ hbar + inp.bias, rtol=1e-12, atol=1e-14)
+    assert sorted(perm.tolist()) == list(range(70))
+    assert np.all(np.diff(avg[perm]) <= 0.0)
+
+
+def test_sort_ties_keep_vocabulary_order():
+    inp = make_fused(20, 8, 12, dtype="f32", seed=32, bias_std=None)
+    W = inp.weight.copy()
+    W[[3, 7, 10]] = W[5]                     # four entries with the same average logit
+    avg, perm = oracle.vocab_sort_order(inp.hidden, W, None, inp.targets)
+    tied = [v for v in perm if v in (3, 5, 7, 10)]
+    assert tied == [3, 5, 7, 10]
+
+
+def test_sorting_changes_nothing_without_filtering():
+    inp = make_fused(100, 16, 300, dtype="f32", seed=33, bias_std=0.3, ignore_frac=0.1, z_loss=1e-3)
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=1e-3)
+    r = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=0.0,
+                                   z_loss=1e-3, sort_vocab=True)
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        np.testing.assert_allclose(r[k], ref[k], rtol=1e-10, atol=1e-15, err_msg=k)
+    assert r["skipped_input"] == 0 and r["skipped_weight"] == 0
+
+
+def test_sorting_clusters_the_likely_entries():
+    # 16 "hot" ids, every 16th one, take nearly all the probability and are the targets:
+    # unsorted, every 16-entry tile and every 64-entry block holds one, so nothing is
+    # skipped; sorted, they fill the first tile, and of the 16 grad_input tiles (64 tokens x
+    # 16 entries) 15 are negligible, of the 16 grad_W tiles (64 entries x 16 tokens) 12.
+    BT, H, V = 64, 8, 256
+    inp = make_fused(BT, H, V, dtype="f32", seed=34, w_std=0.01, bias_std=None)
+    hot = np.arange(0, V, 16)
+    b = np.full(V, -20.0)
+    b[hot] = 20.0
+    y = hot[np.arange(BT) % 16]
+    kw = dict(filter_eps=1e-6)
+    plain = oracle.lce_oracle_filtered(inp.hidden, inp.weight, b, y, **kw)
+    srt = oracle.lce_oracle_filtered(inp.hidden, inp.weight, b, y, sort_vocab=True, **kw)
+    assert (plain["skipped_input"], plain["tiles_input"]) == (0, 16)
+    assert (plain["skipped_weight"], plain["tiles_weight"]) == (0, 16)
+    assert (srt["skipped_input"], srt["tiles_input"]) == (15, 16)
+    assert (srt["skipped_weight"], srt["tiles_weight"]) == (12, 16)
+    assert set(srt["vocab_perm"][:16].tolist()) == set(hot.tolist())
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, b, y)
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        np.testing.assert_allclose(srt[k], ref[k], rtol=0, atol=1e-9, err_msg=k)
