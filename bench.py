@@ -100,7 +100,7 @@ def measured_traffic(kernel: str):
     return rec["hbm_bytes_per_launch"]
 
 
-def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT) -> dict:
+def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT, sort_vocab=False) -> dict:
     """The lossy gradient-filtering mode on the same workload: time per step, the fraction
     of skipped tiles in each gradient pass, and how far its gradients are from the exact
     ones (relative Frobenius norm of the difference)."""
@@ -111,11 +111,12 @@ def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT) -> dict:
     bias = fkw.pop("bias", None)
     if bias is not None:
         out["grad_bias"] = torch.empty_like(bias)
-    lce.lce_fwd_bwd(h, W, bias, y, filter_eps=eps, filter_counts=counts, **fkw)
+    r = lce.lce_fwd_bwd(h, W, bias, y, filter_eps=eps, filter_counts=counts, sort_vocab=sort_vocab, **fkw)
+    fkw["workspace"] = r["workspace"]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        lce.lce_fwd_bwd(h, W, bias, y, filter_eps=eps, filter_counts=counts, **fkw)
+        lce.lce_fwd_bwd(h, W, bias, y, filter_eps=eps, filter_counts=counts, sort_vocab=sort_vocab, **fkw)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     c = counts.cpu().tolist()
@@ -125,7 +126,7 @@ def bench_filtered(lce, torch, h, W, y, kw, exact, eps, steps, BT) -> dict:
         b = b.float()
         return float((a - b).norm() / b.norm())
 
-    return {"filter_eps": eps, "ms_per_step": ms, "tokens_per_s": BT / (ms * 1e-3),
+    return {"filter_eps": eps, "sort_vocab": sort_vocab, "ms_per_step": ms, "tokens_per_s": BT / (ms * 1e-3),
             "skip_fraction_grad_input": c[0] / max(c[1], 1), "skip_fraction_grad_weight": c[2] / max(c[3], 1),
             "grad_rel_diff_vs_exact": {"grad_input": rdiff(out["grad_input"], exact["grad_input"]),
                                         "grad_weight": rdiff(out["grad_weight"], exact["grad_weight"])},
@@ -335,11 +336,12 @@ def main():
                 for x in e[0] + e[1]:
                     hip.hipEventDestroy(ctypes.c_void_p(x))
             log(f"{name}: exact {ms_exact:.1f} ms, stages {st_ms}")
-            res_f = bench_filtered(lce, torch, hh, WW, yy, dict(kw2, bias=bb), ex, args.filter_eps,
-                                   args.steps, c.BT)
-            res_f.update(workload=f"{name}: BT={c.BT}, H={c.H}, V={c.V}, Zipf(1.1) targets",
-                         exact_ms_per_step=ms_exact, exact_stage_ms=st_ms)
-            print(json.dumps(res_f), flush=True)
+            for srt in (False, True):
+                res_f = bench_filtered(lce, torch, hh, WW, yy, dict(kw2, bias=bb), ex, args.filter_eps,
+                                       args.steps, c.BT, sort_vocab=srt)
+                res_f.update(workload=f"{name}: BT={c.BT}, H={c.H}, V={c.V}, Zipf(1.1) targets",
+                             exact_ms_per_step=ms_exact, exact_stage_ms=st_ms)
+                print(json.dumps(res_f), flush=True)
             del hh, WW, bb, yy, ex
             torch.cuda.empty_cache()
         return

@@ -66,6 +66,14 @@ typedef enum lce_reduction {
  * of to bf16).  In the chunked entry points the sum over the token chunks is kept in it
  * directly, so their workspace needs no fp32 accumulator of its own. */
 #define LCE_FLAG_GRAD_W_FP32 2u
+/* (lce_fwd_bwd_filtered only) vocabulary sorting before gradient filtering ("Cut Cross
+ * Entropy visualized", "Vocabulary Sorting"): the vocabulary is ordered by each entry's
+ * average logit over the rows that count (W . mean hidden row + b; ties by id), the call
+ * runs on sorted copies of W, the bias and the targets, so the filter's tiles group
+ * entries of similar average logit, and grad_W / grad_b are written in the original order.
+ * The workspace then also holds the sorted copy of W (lce_fwd_bwd_workspace_bytes with this
+ * flag); BT and V at most 2^24. */
+#define LCE_FLAG_SORT_VOCAB 4u
 
 /* Number of device kernels one lce_fwd_bwd call may launch (for lce_fwd_bwd_profiled). */
 #define LCE_NUM_STAGES 7
@@ -140,6 +148,7 @@ lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* b
  *   filter_eps     >= 0 and finite; 0 disables filtering (the call is then lce_fwd_bwd).
  *   filter_counts  device int64[4] or NULL: skipped and examined tiles of the grad_input
  *                  pass, then of the grad_W pass (overwritten; only when filter_eps > 0).
+ * flags: as lce_fwd_bwd, plus LCE_FLAG_SORT_VOCAB.
  * Other arguments, errors and workspace as lce_fwd_bwd (LCE_ERR_ARG for a bad filter_eps).
  */
 lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* bias,

@@ -74,7 +74,7 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
                 check_targets: bool = False, workspace: Optional[torch.Tensor] = None,
                 out: Optional[dict] = None, events=None, filter_eps: float = 0.0,
                 filter_counts: Optional[torch.Tensor] = None, method: str = "fused",
-                grad_weight_fp32: bool = False) -> dict:
+                grad_weight_fp32: bool = False, sort_vocab: bool = False) -> dict:
     """One call of lce_fwd_bwd: loss and the requested gradients (fully overwritten).
 
     `out` may hold preallocated tensors under the keys loss, grad_input, grad_weight,
@@ -86,7 +86,10 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     inputs) makes grad_weight a float32 tensor (in the chunked composition it then holds the
     sum over the chunks directly);
     method="auto" takes the chunked composition for bf16 with H > 1024, else the fused path.
+    sort_vocab (with filter_eps > 0) orders the vocabulary by average logit before filtering.
     """
+    if sort_vocab and not filter_eps > 0.0:
+        raise ValueError("sort_vocab needs filter_eps > 0 (it only changes which tiles are skipped)")
     if method not in ("fused", "chunked", "auto"):
         raise ValueError(f"method must be 'fused', 'chunked' or 'auto', not {method!r}")
     if method == "auto":
@@ -131,6 +134,8 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     if return_lse and lse is None:
         lse = torch.empty(BT, dtype=torch.float32, device=dev)
     flags = _lib.FLAG_CHECK_TARGETS if check_targets else 0
+    if sort_vocab:
+        flags |= _lib.FLAG_SORT_VOCAB
     if grad_weight_fp32:
         flags |= _lib.FLAG_GRAD_W_FP32
         if gw is not None and gw.dtype != torch.float32:

@@ -19,6 +19,7 @@ REDUCTION_MEAN = 0
 REDUCTION_SUM = 1
 FLAG_CHECK_TARGETS = 1
 FLAG_GRAD_W_FP32 = 2
+FLAG_SORT_VOCAB = 4
 NUM_STAGES = 7
 
 EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_fwd_bwd_workspace_bytes",

@@ -60,7 +60,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
                              void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
                              float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
                              void* const* ev_start, void* const* ev_stop, float filter_eps,
-                             int64_t* filter_counts) {
+                             int64_t* filter_counts, bool allow_sort = false) {
   // ---- validation: no HIP calls before this block has passed
   if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
   if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 31) - 2 || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
@@ -70,14 +70,19 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_SUM) return LCE_ERR_ARG;
   if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
   if (grad_b != nullptr && bias == nullptr) return LCE_ERR_ARG;
-  if ((flags & ~(LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32)) != 0) return LCE_ERR_ARG;
+  const uint32_t allowed = LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32 | (allow_sort ? LCE_FLAG_SORT_VOCAB : 0u);
+  if ((flags & ~allowed) != 0) return LCE_ERR_ARG;
+  const bool sort = (flags & LCE_FLAG_SORT_VOCAB) != 0;
+  // (the sort's grids hold one block per 256 hidden rows and one wave per entry)
+  if (sort && (BT > ((int64_t)1 << 24) || V > ((int64_t)1 << 24))) return LCE_ERR_SHAPE;
   if (!(filter_eps >= 0.f) || !std::isfinite(filter_eps)) return LCE_ERR_ARG;
   const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
   if (!aligned(hidden, 16) || !aligned(W, 16) || !aligned(grad_input, 16) || !aligned(grad_W, 16) ||
       !aligned(workspace, 16) || !aligned(bias, es) || !aligned(grad_b, es) || !aligned(targets, 8) ||
       !aligned(loss_out, 4) || !aligned(n_valid_out, 8) || !aligned(lse_out, 4) || !aligned(filter_counts, 8))
     return LCE_ERR_ALIGNMENT;
-  if (workspace_bytes < fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16)) return LCE_ERR_WORKSPACE;
+  const size_t ws_fused = fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16);
+  if (workspace_bytes < ws_fused + (sort ? sort_workspace_bytes(BT, H, V, es) : 0)) return LCE_ERR_WORKSPACE;
 
   FusedArgs a;
   a.hidden = hidden;
@@ -98,6 +103,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   a.n_valid_out = n_valid_out;
   a.lse_out = lse_out;
   a.grad_w_f32 = (flags & LCE_FLAG_GRAD_W_FP32) != 0 && dtype == LCE_DTYPE_BF16;
+  a.out_row_map = nullptr;
   a.filter_eps = filter_eps;
   a.filter_counts = filter_eps > 0.f ? filter_counts : nullptr;
   const FusedWs w = fused_carve(workspace, BT, V);
@@ -107,6 +113,25 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   static const Launch kLaunch[kNumStages] = {launch_targets,    launch_fwd_lse,    launch_target_logit,
                                              launch_merge,      launch_loss,       launch_bwd_dinput,
                                              launch_bwd_dweight};
+  if (sort) {
+    // Vocabulary sorting: count the targets and check them as given, order the vocabulary,
+    // then run every stage on the sorted copies (the first stage again, for the sorted
+    // bias), with grad_W / grad_b rows written back through the order.
+    if (launch_targets(a, w, st) != hipSuccess) return LCE_ERR_HIP;
+    if (flags & LCE_FLAG_CHECK_TARGETS) {
+      int32_t bad = 0;
+      if (hipMemcpyAsync(&bad, w.n_bad, sizeof(bad), hipMemcpyDeviceToHost, st) != hipSuccess) return LCE_ERR_HIP;
+      if (hipStreamSynchronize(st) != hipSuccess) return LCE_ERR_HIP;
+      if (bad != 0) return LCE_ERR_TARGET_RANGE;
+      flags &= ~LCE_FLAG_CHECK_TARGETS;
+    }
+    const SortWs sw = sort_carve(static_cast<char*>(workspace) + ws_fused, BT, H, V, es);
+    if (launch_sort_vocab(a, sw, w.n_valid, st) != hipSuccess) return LCE_ERR_HIP;
+    a.W = sw.Ws;
+    if (a.bias != nullptr) a.bias = sw.bs;
+    if (BT > 0) a.targets = sw.ys;
+    a.out_row_map = sw.perm;
+  }
   for (int k = 0; k < kNumStages; ++k) {
     if (ev_start && ev_start[k] && hipEventRecord(static_cast<hipEvent_t>(ev_start[k]), st) != hipSuccess)
       return LCE_ERR_HIP;
@@ -128,10 +153,11 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
 extern "C" {
 
 size_t lce_fwd_bwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
-  (void)flags;
   if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return 0;
   if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return 0;
-  return lce::fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16);
+  const size_t es = dtype == LCE_DTYPE_BF16 ? 2 : 4;
+  return lce::fused_workspace_bytes(BT, H, V, dtype == LCE_DTYPE_BF16) +
+         ((flags & LCE_FLAG_SORT_VOCAB) ? lce::sort_workspace_bytes(BT, H, V, es) : 0);
 }
 
 lce_status lce_fwd_bwd(const void* hidden, const void* W, const void* bias, const int64_t* targets, int64_t BT,
@@ -163,7 +189,7 @@ lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* b
                                 float filter_eps, int64_t* filter_counts) {
   return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
                          flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
-                         workspace_bytes, stream, nullptr, nullptr, filter_eps, filter_counts);
+                         workspace_bytes, stream, nullptr, nullptr, filter_eps, filter_counts, true);
 }
 
 size_t lce_fwd_bwd_chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {

@@ -52,6 +52,7 @@ struct BwdArgs {
   int mean;
   T* out;
   float* out_f32;  // (bf16 inputs) fp32 output instead of out, or NULL
+  const int32_t* out_row_map;  // (grad_W) output row of each stationary row, or NULL (same row)
   T* grad_b;
   int64_t nchunks;
 };
@@ -447,7 +448,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-          if (row < p.nS && col < H) p.out[row * H + col] = Elem<T>::from_f(cscale * acc[sb][cb][r]);
+          if (row < p.nS && col < H) {
+            const int64_t orow = p.out_row_map != nullptr ? p.out_row_map[row] : row;
+            p.out[orow * H + col] = Elem<T>::from_f(cscale * acc[sb][cb][r]);
+          }
         }
       }
   } else if (p.out_f32 != nullptr) {
@@ -459,7 +463,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-          if (row < p.nS && col < H) p.out_f32[row * H + col] = cscale * acc[sb][cb][r];
+          if (row < p.nS && col < H) {
+            const int64_t orow = p.out_row_map != nullptr ? p.out_row_map[row] : row;
+            p.out_f32[orow * H + col] = cscale * acc[sb][cb][r];
+          }
         }
       }
   }
@@ -474,7 +481,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_kernel(BwdArgs<T> p) {
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, kWave);
       const int64_t srow = s0 + r0 + e;
-      if (c == 0 && srow < p.V) p.grad_b[srow] = Elem<T>::from_f(cscale * v);
+      if (c == 0 && srow < p.V)
+        p.grad_b[p.out_row_map != nullptr ? p.out_row_map[srow] : srow] = Elem<T>::from_f(cscale * v);
     }
   }
 }
@@ -868,7 +876,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-          if (row < p.nS && col < H) p.out[row * H + col] = f2bf(cscale * acc[sb][cb][r]);
+          if (row < p.nS && col < H) {
+            const int64_t orow = p.out_row_map != nullptr ? p.out_row_map[row] : row;
+            p.out[orow * H + col] = f2bf(cscale * acc[sb][cb][r]);
+          }
         }
       }
   } else if (p.out_f32 != nullptr) {
@@ -880,7 +891,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-          if (row < p.nS && col < H) p.out_f32[row * H + col] = cscale * acc[sb][cb][r];
+          if (row < p.nS && col < H) {
+            const int64_t orow = p.out_row_map != nullptr ? p.out_row_map[row] : row;
+            p.out_f32[orow * H + col] = cscale * acc[sb][cb][r];
+          }
         }
       }
   }
@@ -891,7 +905,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
       const int64_t r = s0 + 16 * w + 4 * q + i;
-      if (l16 == 0 && r < p.V) p.grad_b[r] = f2bf(cscale * v);
+      if (l16 == 0 && r < p.V) p.grad_b[p.out_row_map != nullptr ? p.out_row_map[r] : r] = f2bf(cscale * v);
     }
   }
 }
@@ -989,6 +1003,7 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
     a.nX = fa.V;
     a.out = static_cast<T*>(fa.grad_input);
     a.out_f32 = nullptr;
+    a.out_row_map = nullptr;
     a.grad_b = nullptr;
   } else {
     a.S = static_cast<const T*>(fa.W);
@@ -997,6 +1012,7 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
     a.nX = fa.BT;
     a.out = fa.grad_w_f32 ? nullptr : static_cast<T*>(fa.grad_W);
     a.out_f32 = fa.grad_w_f32 ? static_cast<float*>(fa.grad_W) : nullptr;
+    a.out_row_map = fa.out_row_map;
     a.grad_b = static_cast<T*>(fa.grad_b);
   }
   const BwdPlan pl = bwd_plan(fa.H, sizeof(T) == 2);

@@ -50,9 +50,26 @@ struct FusedArgs {
   int64_t* n_valid_out;
   float* lse_out;
   bool grad_w_f32;           // (bf16 inputs) grad_W is written in fp32
+  const int32_t* out_row_map;  // grad_W / grad_b row i goes to row out_row_map[i] (or NULL)
   float filter_eps;          // > 0: gradient filtering (tiles of |dlogits| < eps are skipped)
   int64_t* filter_counts;    // [4] skipped / examined tiles of the grad_input and grad_W passes, or NULL
 };
+
+// Vocabulary sorting for the filtered call: the sorted copies and the sort's scratch.
+struct SortWs {
+  void* Ws;                 // [V][H] W rows in sorted order
+  void* bs;                 // [V] bias in sorted order
+  int64_t* ys;              // [BT] targets as sorted positions
+  int32_t* perm;            // [V] id at each sorted position
+  int32_t* pos;             // [V] sorted position of each id
+  unsigned long long* keys; // [N] sort keys (N = power of two >= V)
+  float* part;              // [nblk][H] block sums of the counted hidden rows
+  float* hbar;              // [H]
+  int64_t N, nblk;
+};
+size_t sort_workspace_bytes(int64_t BT, int64_t H, int64_t V, size_t es);
+SortWs sort_carve(void* ws, int64_t BT, int64_t H, int64_t V, size_t es);
+hipError_t launch_sort_vocab(const FusedArgs& a, const SortWs& s, const int64_t* n_valid, hipStream_t st);
 
 // Stages of the fused call, in launch order.
 enum Stage { kStTargets = 0, kStFwd, kStTargetLogit, kStMerge, kStLoss, kStBwdDX, kStBwdDW, kNumStages };

@@ -118,6 +118,22 @@ def test_filtered_host_errors(lib, eps, counts, kw, status):
     assert fused_filtered(lib, eps, counts, **kw) == status
 
 
+def test_sort_vocab_flag(lib):
+    # only the filtered entry takes it; its workspace adds the sorted copies of W, the bias and
+    # the targets, the order and the sort keys; BT and V are capped at 2^24
+    S = _lib.FLAG_SORT_VOCAB
+    BT, H, V = 100, 64, 1000
+    ws0 = lib.lce_fwd_bwd_workspace_bytes(BT, H, V, BF16, 0)
+    ws1 = lib.lce_fwd_bwd_workspace_bytes(BT, H, V, BF16, S)
+    assert ws1 >= ws0 + V * H * 2 + BT * 4 + V * 8
+    assert lib.lce_fwd_bwd_workspace_bytes(BT, H, V, F32, S) >= ws1 + V * H * 2
+    assert fused(lib, flags=S) == 6
+    assert fused_filtered(lib, 1e-3, flags=S, wsb=ws0) == 5
+    assert fused_filtered(lib, 1e-3, flags=S, BT=(1 << 24) + 1) == 2
+    assert fused_filtered(lib, 1e-3, flags=S, V=(1 << 24) + 1) == 2
+    assert fused_filtered(lib, 1e-3, flags=S | 8) == 6
+
+
 def chunked(lib, **kw):
     a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
              dtype=BF16, ignore=-100, mu=0.0, red=MEAN, flags=0, loss=P + 0x300000,

@@ -89,3 +89,56 @@ def test_tiny_eps_reproduces_exact_call(dtype, H):
     assert counts[0].item() == 0 and counts[2].item() == 0
     for k in ("loss", "grad_input", "grad_weight", "grad_bias"):
         assert torch.equal(exact[k], filt[k]), k
+
+
+# --------------------------------------------------------------------- vocabulary sorting
+
+SORT_CASES = [
+    # (dtype, BT, H, V, seed)
+    ("bf16", 200, 256, 2048, 41),
+    ("bf16", 150, 1152, 1500, 42),   # column-chunked backward
+    ("f32", 130, 128, 1200, 43),
+]
+
+
+def _sort_inputs(dtype, BT, H, V, seed):
+    """Every 64th entry is "hot" (bias 20 + small distinct offsets) and holds all the targets;
+    the others get distinct biases from -30 down in steps of 0.01, and W is tiny, so each
+    entry's average logit is set by its bias alone (well separated: both orders agree) and
+    every non-hot probability is ~e^-50, far below eps."""
+    inp = make_fused(BT, H, V, dtype=dtype, seed=seed, w_std=1e-4, bias_std=None, ignore_frac=0.1)
+    rng = np.random.default_rng(seed)
+    hot = np.arange(0, V, 64)
+    b = -30.0 - 0.01 * rng.permutation(V).astype(np.float64)
+    b[hot] = 20.0 + 0.01 * np.arange(len(hot))
+    inp.bias = b.astype(np.float32)
+    if dtype == "bf16":
+        inp.bias = torch.from_numpy(inp.bias).to(torch.bfloat16).float().numpy()
+    y = inp.targets.copy()
+    keep = y != -100
+    y[keep] = hot[rng.integers(0, len(hot), size=int(keep.sum()))]
+    inp.targets = y
+    return inp
+
+
+@pytest.mark.parametrize("case", SORT_CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}" for c in SORT_CASES])
+def test_sorted_filtering_matches_oracle(case):
+    dtype, BT, H, V, seed = case
+    print(f"sorted filtering {case}", flush=True)
+    inp = _sort_inputs(dtype, BT, H, V, seed)
+    eps = 1e-6
+    ref = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps, sort_vocab=True)
+    plain = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps)
+    assert ref["skipped_input"] > plain["skipped_input"] and ref["skipped_weight"] > plain["skipped_weight"]
+    counts = torch.zeros(4, dtype=torch.int64, device="cuda")
+    r = lce.lce_fwd_bwd(dev(inp.hidden, dtype), dev(inp.weight, dtype), dev(inp.bias, dtype), dev(inp.targets),
+                        filter_eps=eps, filter_counts=counts, sort_vocab=True, return_lse=True)
+    torch.cuda.synchronize()
+    c = counts.cpu().tolist()
+    assert c == [ref["skipped_input"], ref["tiles_input"], ref["skipped_weight"], ref["tiles_weight"]], c
+    tol = TOL[dtype]
+    assert int(r["n_valid"].item()) == ref["n_valid"]
+    assert rel(r["loss"].item(), ref["loss"]) <= tol["loss"]
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        e = rel_fro(host64(r[k]), ref[k])
+        assert e <= tol["grad"], (k, e)
