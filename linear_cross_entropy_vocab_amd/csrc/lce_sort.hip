@@ -23,15 +23,16 @@ template <typename T>
 __global__ void __launch_bounds__(256) hbar_partial_kernel(const T* __restrict__ h, const int64_t* __restrict__ y,
                                                            int64_t BT, int64_t H, int64_t V, int64_t ignore_index,
                                                            float* __restrict__ part) {
-  const int64_t r0 = (int64_t)blockIdx.y * kHbarRows;
+  // blockIdx.x: block of rows (the long grid axis), blockIdx.y: slice of the hidden columns
+  const int64_t r0 = (int64_t)blockIdx.x * kHbarRows;
   const int64_t r1 = (r0 + kHbarRows) < BT ? (r0 + kHbarRows) : BT;
-  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t k = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; k < H; k += (int64_t)gridDim.y * blockDim.x) {
     float acc = 0.f;
     for (int64_t t = r0; t < r1; ++t) {
       const int64_t yt = y[t];
       if (yt != ignore_index && yt >= 0 && yt < V) acc += Elem<T>::to_f(h[t * H + k]);
     }
-    part[(int64_t)blockIdx.y * H + k] = acc;
+    part[(int64_t)blockIdx.x * H + k] = acc;
   }
 }
 
@@ -199,7 +200,7 @@ static hipError_t sort_vocab_t(const FusedArgs& a, const SortWs& s, const int64_
   const T* W = static_cast<const T*>(a.W);
   const T* b = static_cast<const T*>(a.bias);
   if (a.BT > 0) {
-    const dim3 g1((unsigned)((a.H + 255) / 256 < 64 ? (a.H + 255) / 256 : 64), (unsigned)s.nblk);
+    const dim3 g1((unsigned)s.nblk, (unsigned)((a.H + 255) / 256 < 64 ? (a.H + 255) / 256 : 64));
     hipLaunchKernelGGL(hbar_partial_kernel<T>, g1, dim3(256), 0, st, h, a.targets, a.BT, a.H, a.V, a.ignore_index,
                        s.part);
   }

@@ -142,3 +142,64 @@ def test_sorted_filtering_matches_oracle(case):
     for k in ("grad_input", "grad_weight", "grad_bias"):
         e = rel_fro(host64(r[k]), ref[k])
         assert e <= tol["grad"], (k, e)
+
+
+SORT_GENERAL = [
+    # (dtype, BT, H, V, bias, ignore_frac, targets, seed)
+    ("bf16", 300, 256, 3001, True, 0.1, "zipf", 45),
+    ("bf16", 150, 1152, 1500, False, 0.0, "uniform", 46),
+    ("f32", 130, 128, 1200, True, 0.2, "zipf", 47),
+    ("bf16", 64, 128, 700, True, 1.0, "uniform", 48),   # every row ignored: the order is the bias order
+    ("bf16", 0, 128, 700, True, 0.0, "uniform", 49),    # empty batch
+]
+
+
+@pytest.mark.parametrize("case", SORT_GENERAL, ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}" for c in SORT_GENERAL])
+def test_sorted_tiny_eps_matches_exact_oracle(case):
+    """With eps below every |dlogit| nothing is skipped, so the sorted call must give the exact
+    loss and gradients in the original vocabulary order, whatever order the sort chose (near
+    ties between averages may order differently in fp32 and fp64; the result does not depend
+    on it)."""
+    dtype, BT, H, V, with_bias, ign, tg, seed = case
+    print(f"sorted tiny eps {case}", flush=True)
+    inp = make_fused(BT, H, V, dtype=dtype, seed=seed, w_std=H ** -0.5, bias_std=0.5 if with_bias else None,
+                     targets=tg, ignore_frac=ign)
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets)
+    counts = torch.full((4,), -1, dtype=torch.int64, device="cuda")
+    bias = dev(inp.bias, dtype) if with_bias else None
+    r = lce.lce_fwd_bwd(dev(inp.hidden, dtype), dev(inp.weight, dtype), bias, dev(inp.targets),
+                        filter_eps=1e-38, filter_counts=counts, sort_vocab=True, return_lse=True,
+                        check_targets=True)
+    torch.cuda.synchronize()
+    c = counts.cpu().tolist()
+    if ref["n_valid"] == 0:
+        assert c[0] == c[1] and c[2] == c[3], c   # every dlogit is 0: every tile is skipped
+    else:
+        assert c[0] == 0 and c[2] == 0, c
+    tol = TOL[dtype]
+    assert int(r["n_valid"].item()) == ref["n_valid"]
+    if ref["n_valid"] == 0:
+        assert r["loss"].item() == 0.0
+    else:
+        assert rel(r["loss"].item(), ref["loss"]) <= tol["loss"]
+    if BT > 0:
+        lse = host64(r["lse"])
+        assert np.max(np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))) <= tol["lse"]
+    keys = ("grad_input", "grad_weight", "grad_bias") if with_bias else ("grad_input", "grad_weight")
+    for k in keys:
+        want = ref[k]
+        got = host64(r[k])
+        if not np.any(want):
+            assert not np.any(got), k
+        else:
+            assert rel_fro(got, want) <= tol["grad"], k
+
+
+def test_sorted_call_checks_targets_before_sorting():
+    inp = make_fused(100, 128, 500, dtype="bf16", seed=50, bias_std=0.1)
+    y = inp.targets.copy()
+    y[7] = 500
+    with pytest.raises(lce.LCEError):
+        lce.lce_fwd_bwd(dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), dev(inp.bias, "bf16"), dev(y),
+                        filter_eps=1e-6, sort_vocab=True, check_targets=True)
+    torch.cuda.synchronize()
