@@ -308,9 +308,9 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   int buf = 0;
   dma(tl, 0, 0);
   for (;;) {
-    if (tid < kFwdTileV) {  // (the previous tile's epilogue finished reading s_bias)
+    if (bias != nullptr && tid < kFwdTileV) {  // (the previous tile is done with s_bias)
       const int64_t v = tl.v0 + tid;
-      s_bias[tid] = (bias != nullptr && v < V) ? bf2f(bias[v]) : 0.f;
+      s_bias[tid] = v < V ? bf2f(bias[v]) : 0.f;
     }
     const int64_t nblk = blk + gridDim.x;
     const bool has_next = nblk < nwg;
@@ -349,14 +349,49 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fa[kk & 1][vb], fb[kk & 1][tb], acc[vb][tb]);
       }
+      // Pin the order: the first step's six fragment reads, then each step's eight MFMAs
+      // interleaved with the next step's reads (left to itself the compiler issues each read
+      // just before the MFMA that needs it, which exposes the LDS latency).
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       buf ^= 1;
     }
 
+    // z += b as one more MFMA step per accumulator: A holds b[row] at k = 0 (lanes 0..31,
+    // the rows of the 32-row block), B holds 1 at k = 0; both bf16, so the product is exact
+    // and the bias costs no per-element work in the epilogue.
+    if (bias != nullptr) {
+      Frag<bf16_t> fbias[4], fone;
+      zero8(fone);
+      if (lane < 32) fone.v[0] = (short)0x3f80;  // bf16 bits of 1.0
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        zero8(fbias[vb]);
+        if (lane < 32) fbias[vb].v[0] = (short)f2bf(s_bias[wv * 128 + vb * 32 + lane]);
+      }
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fbias[vb], fone, acc[vb][tb]);
+    }
     const int vlim = (int)((V - tl.v0) < kFwdTileV ? (V - tl.v0) : kFwdTileV);
     int ln = lane;
     asm volatile("" : "+v"(ln));  // keeps the row indices below from being hoisted out of the loop
     const int vrow = wv * 128 + 4 * (ln >> 5);
+    // Row vrow + c exists iff c < lim; the checks are needed in the last vocabulary tile only
+    // (a wave-uniform branch) and compare with small constants.
+    const int lim = vlim - vrow;
     if constexpr (STORE) {
+      const bool full = vlim == kFwdTileV;
       // Lane (t, half) holds, per 32-row block vb, vocabulary rows 8 rr + 4 half + 0..3 for
       // rr = 0..3.  Lanes t and t + 32 swap halves so that each owns whole 8-row runs
       // (rr = 2 p + half, p = 0, 1) and writes them as 16-byte stores along the token's row.
@@ -374,8 +409,8 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
             float f[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int vr = vrow + vb * 32 + 8 * rr + e;
-              f[e] = vr < vlim ? acc[vb][tb][4 * rr + e] + s_bias[vr] : 0.f;
+              const int c = vb * 32 + 8 * rr + e;
+              f[e] = (full || c < lim) ? acc[vb][tb][4 * rr + e] : 0.f;
             }
             pk[rr][0] = pack_bf2(f[0], f[1]);
             pk[rr][1] = pack_bf2(f[2], f[3]);
@@ -397,34 +432,40 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         }
       }
       (void)lse_part;
-      __syncthreads();  // every wave is done with s_bias before the next tile rewrites it
+      __syncthreads();  // every wave has read s_bias before the next tile rewrites it
       if (!has_next) break;
       blk = nblk;
       tl = tn;
       continue;
     }
     // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
-    // two lane halves, then the two vocabulary halves of the tile; rows past V (only in the
-    // last vocabulary tile) are skipped.
+    // two lane halves, then the two vocabulary halves of the tile.  Rows past V (only in the
+    // last vocabulary tile) are set to -inf first, so the two passes need no checks.
+    if (vlim < kFwdTileV) {
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vb * 32 + 8 * (r >> 2) + (r & 3) >= lim) acc[vb][tb][r] = -INFINITY;
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       float m = -INFINITY;
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vr = vrow + vb * 32 + 8 * (r >> 2) + (r & 3);
-          if (vr < vlim) m = fmaxf(m, acc[vb][tb][r] + s_bias[vr]);
-        }
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[vb][tb][r]);
       float sm = 0.f;
       if (m != -INFINITY) {
+        // e^(z - m) = 2^(z log2 e - m log2 e): one FMA and the hardware base-2 exponential
+        const float mb = m * kLog2e;
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int vr = vrow + vb * 32 + 8 * (r >> 2) + (r & 3);
-            if (vr < vlim) sm += __expf(acc[vb][tb][r] + s_bias[vr] - m);
-          }
+          for (int r = 0; r < 16; ++r) sm += __builtin_amdgcn_exp2f(fmaf(acc[vb][tb][r], kLog2e, -mb));
       }
       ms_merge(m, sm, __shfl_xor(m, 32, kWave), __shfl_xor(sm, 32, kWave));
       if (lane < 32) {
