@@ -537,6 +537,18 @@ __device__ __forceinline__ bf16x8_t tr_pair(const char* p0, const char* p1) {
   return bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Workgroup barrier that leaves this wave's newest N LDS reads in flight (__syncthreads
+// waits for every outstanding LDS access).  A wave's LDS accesses complete in order, so with
+// at most N accesses outstanding, everything issued before the compiler order point
+// `lds_order()` that precedes those N reads has completed, and writes made before it are
+// visible to the other waves after the barrier.  (Scalar loads share the counter; they can
+// only make the wait longer.)  The reads are waited for where their registers are used.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void barrier_reads_in_flight() {
+  asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Plane j of a tile share: 1 KB of LDS from this lane's 16 bytes at off + 64 j.
 template <int J, int N>
 struct DmaPlanes {
@@ -577,13 +589,19 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
   const int64_t ntiles = (p.nX + kPX - 1) / kPX;
 
-  // ---- per-lane constants of the stationary rows m = 16 w + 4 q + i (after the exchange)
+  // ---- per-lane constants of the stationary rows m = 16 w + 4 q + i (after the exchange).
+  // The dlogit of (row, column) is g = 2^(z log2 e + ra + ca) * f - onehot, where ra and ca
+  // are the row's and the column's additive terms in base 2: -LSE log2 e for a token, the
+  // bias times log2 e for a vocabulary entry, and -inf for a row or column that contributes
+  // nothing (an ignored token, an entry past V), which makes the exponential exactly 0; f is
+  // the token's z-loss factor 1 + 2 mu LSE.  The one-hot term can only match a counted pair.
+  constexpr float kLog2e = 1.4426950408889634f;
   float ra[4], rf[4];
   int32_t ry[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t r = s0 + 16 * w + 4 * q + i;
-    if (!DW) {  // token rows: -LSE, z-loss factor, target (-1: row contributes nothing)
+    if (!DW) {  // token rows: target (-1: the row contributes nothing)
       int32_t yv = -1;
       float L = 0.f;
       if (r < p.BT) {
@@ -591,20 +609,18 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
         yv = __float_as_int(tk.y) - 1;
         L = yv >= 0 ? tk.x : 0.f;
       }
-      ra[i] = -L;
+      ra[i] = yv >= 0 ? -L * kLog2e : -INFINITY;
       rf[i] = 1.f + 2.f * p.mu * L;
       ry[i] = yv;
-    } else {  // vocabulary rows: bias, validity
-      ra[i] = (p.bias != nullptr && r < p.V) ? bf2f(p.bias[r]) : 0.f;
+    } else {  // vocabulary rows (the index is rebuilt from vrow0 where it is needed)
+      ra[i] = r < p.V ? (p.bias != nullptr ? bf2f(p.bias[r]) * kLog2e : 0.f) : -INFINITY;
       rf[i] = 0.f;
-      ry[i] = 0;  // (vocabulary rows: the index is rebuilt from vrow0 where it is needed)
+      ry[i] = 0;
     }
   }
 
-  // vocabulary rows (DW): row 16 w + 4 q + i is vocabulary entry vrow0 + i; rows past V
-  // contribute nothing
+  // vocabulary rows (DW): row 16 w + 4 q + i is vocabulary entry vrow0 + i
   const int32_t vrow0 = (int32_t)(s0 + 16 * w + 4 * q);
-  const int32_t vlim = (int32_t)(p.V < (int64_t)0x7fffffff ? p.V : 0x7fffffff);
 
   // ---- stationary GEMM1 A fragments: rows 16 rb + l16, k = kw0 + 32 ks + 8 q .. + 7
   bf16x8_t sf[NB][4];
@@ -677,8 +693,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     const u32x4_t rx = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
     DmaPlanes<0, NB>::run(rx, xw_lds + (uint32_t)(buf * XW), dma_off);
   };
-  // column values of tile `tile` for column l16: DW: (-LSE, factor, target) of token x0 + l16;
-  // otherwise the bias of vocabulary row x0 + l16
+  // column values of tile `tile` for column l16 (see the row constants above): DW: the
+  // token x0 + l16's additive term, z-loss factor and target (-1: not counted); otherwise the
+  // vocabulary row x0 + l16's term and index (-2 past V, so it matches no row's target)
   float nc_a = 0.f, nc_f = 0.f;
   int32_t nc_y = -1;
   auto take_col = [&](int64_t tile, int buf) {  // after the loads of `tile` have landed
@@ -686,12 +703,13 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
       const float2 t = *reinterpret_cast<const float2*>(cs[w][buf] + 8 * l16);
       const float L = t.x;
       nc_y = __float_as_int(t.y) - 1;
-      nc_a = nc_y >= 0 ? -L : 0.f;
+      nc_a = nc_y >= 0 ? -L * kLog2e : -INFINITY;
       nc_f = nc_y >= 0 ? 1.f + 2.f * p.mu * L : 0.f;
     } else {
       const int64_t xc = tile * kPX + l16;
-      nc_a = *reinterpret_cast<const float*>(cs[w][buf] + 4 * l16);
-      nc_y = xc < p.V ? (int32_t)xc : -1;  // vocabulary index of the column (-1: past V)
+      const float b = *reinterpret_cast<const float*>(cs[w][buf] + 4 * l16);
+      nc_a = xc < p.V ? b * kLog2e : -INFINITY;
+      nc_y = xc < p.V ? (int32_t)xc : -2;
     }
   };
 
@@ -737,20 +755,13 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   };
   // dlogits of one tile for rows 16 w + 4 q + i, column l16 -> LDS (bf16)
   auto dlogits = [&]() {
-    const f32x4v z = zown + zpr[0] + zpr[1] + zpr[2];
+    const f32x4v z = (zown + zpr[0]) + (zpr[1] + zpr[2]);
     float g[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bool ok;
-      float gi;
-      if (!DW) {
-        ok = ry[i] >= 0 && nc_y >= 0;
-        gi = __expf(z[i] + nc_a + ra[i]) * rf[i] - (ry[i] == nc_y ? 1.f : 0.f);
-      } else {
-        ok = vrow0 + i < vlim && nc_y >= 0;
-        gi = __expf(z[i] + ra[i] + nc_a) * nc_f - (nc_y == vrow0 + i ? 1.f : 0.f);
-      }
-      g[i] = ok ? gi : 0.f;
+      const float e = __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, ra[i] + nc_a));
+      if (!DW) g[i] = fmaf(e, rf[i], ry[i] == nc_y ? -1.f : 0.f);
+      else g[i] = fmaf(e, nc_f, nc_y == vrow0 + i ? -1.f : 0.f);
       if (DW) {
         if (FILT) gpend[i] = g[i];  // added to grad_b once the tile is known to be kept
         else gb[i] += g[i];
@@ -827,7 +838,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     gemm1_reads(0, C0{}, CN{});
     gemm1_part(C0{}, CN{});
     put_partials();
-    __syncthreads();
+    vm_wait<(kPBuf - 2) * NQ>();  // tile 1 has landed
+    lds_order();
+    gemm1_reads(1 % kPBuf, C0{}, CH{});  // first half of GEMM1(1), in flight across the barrier
+    barrier_reads_in_flight<NB / 2>();
   }
   // Loads of a wave, in issue order: phase B of iteration i queues the column values and
   // the first half of tile i+4, phase A of iteration i+1 its second half.  At the top of
@@ -840,25 +854,32 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     // not wait for its barrier: the first half covers the latency of the partial-sum reads
     // and runs beside the dlogits of tile i, the second half covers the dlogits reads of
     // GEMM3.  (In the last iteration it works on a stale buffer and its result is unused.)
-    // ---- phase A
-    vm_wait<NQ + NB / 2 + 1>();  // tile i+1 has landed (see above)
+    // ---- phase A (the first half of GEMM1(i+1)'s operands was read before the barrier)
     partial_reads();
     take_col(i, bi);
-    gemm1_reads(bn, C0{}, CH{});
     gemm1_part(C0{}, CH{});
     // (keeps the dlogits arithmetic below the MFMAs, so that it runs while they execute
     // instead of delaying their issue)
     __builtin_amdgcn_sched_barrier(0);
     dlogits();
+    lds_order();
     gemm1_reads(bn, CH{}, CN{});  // in flight across the barrier
     if (i > 0) refill_rest();     // second half of tile i+3 (the buffer of tile i-1)
-    __syncthreads();
+    barrier_reads_in_flight<NB - NB / 2>();
     // ---- phase B: GEMM3 of tile i (refilling its buffer with tile i+4 plane by plane; past
     // the end the last tile is repeated, never read), partial z of tile i+1
     gemm1_part(CH{}, CN{});
     gemm3(bi, more, i + kPBuf < ntiles ? i + kPBuf : ntiles - 1);
     if (more) put_partials();
-    __syncthreads();
+    // The next phase A starts on GEMM1(i+2) at once: its first operand half is read here,
+    // in flight across the barrier, once tile i+2 has landed.  The newest loads are then
+    // those of B(i), A(i) and B(i-1) (tiles i+4 and i+3); everything older, so all of tile
+    // i+2, must have landed.  (In the last two iterations the reads hit a buffer whose
+    // contents are never used.)
+    vm_wait<NQ + NB / 2 + 1>();
+    lds_order();
+    gemm1_reads((int)((i + 2) % kPBuf), C0{}, CH{});
+    barrier_reads_in_flight<NB / 2>();
   }
   vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
   if (FILT && p.filter_counts != nullptr && tid == 0) {
