@@ -549,6 +549,15 @@ __device__ __forceinline__ void barrier_reads_in_flight() {
   asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Plane j of a tile share: 1 KB of LDS from this lane's 16 bytes at off + 64 j.
 template <int J, int N>
 struct DmaPlanes {
@@ -753,29 +762,75 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
 #pragma unroll
     for (int x = 1; x < 4; ++x) zpr[x - 1] = *reinterpret_cast<const f32x4v*>(zx[w ^ x][w] + 16 * lane);
   };
-  // dlogits of one tile for rows 16 w + 4 q + i, column l16 -> LDS (bf16)
-  auto dlogits = [&]() {
-    const f32x4v z = (zown + zpr[0]) + (zpr[1] + zpr[2]);
-    float g[4];
+  // dlogits of one tile for rows 16 w + 4 q + i, column l16 -> LDS (bf16), in eight steps
+  // that the first half of the next tile's GEMM1 interleaves with its MFMAs (one step after
+  // each of eight MFMAs).  Each step starts by passing the values it reads through an empty
+  // asm statement: the compiler cannot move the step's arithmetic above the MFMA before it,
+  // and its results are consumed after the next MFMA, so it executes while the MFMAs run.
+  float dz[4], dt[4], de[4];
+  auto dl_step = [&](auto kc) {
+    constexpr int K = decltype(kc)::value;
+    if constexpr (K == 0) {  // the partial sums have landed by now
+      asm volatile("" : "+v"(zpr[0]), "+v"(zpr[1]), "+v"(zpr[2]), "+v"(zown));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, ra[i] + nc_a));
-      if (!DW) g[i] = fmaf(e, rf[i], ry[i] == nc_y ? -1.f : 0.f);
-      else g[i] = fmaf(e, nc_f, nc_y == vrow0 + i ? -1.f : 0.f);
-      if (DW) {
-        if (FILT) gpend[i] = g[i];  // added to grad_b once the tile is known to be kept
-        else gb[i] += g[i];
+      for (int i = 0; i < 4; ++i) dz[i] = zown[i] + zpr[0][i];
+    } else if constexpr (K == 1 || K == 2) {
+      asm volatile("" : "+v"(dz[0]), "+v"(dz[1]), "+v"(dz[2]), "+v"(dz[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dz[i] += zpr[K][i];
+    } else if constexpr (K == 3) {
+      asm volatile("" : "+v"(dz[0]), "+v"(dz[1]), "+v"(dz[2]), "+v"(dz[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dt[i] = fmaf(dz[i], kLog2e, ra[i] + nc_a);
+    } else if constexpr (K == 4) {
+      asm volatile("" : "+v"(dt[0]), "+v"(dt[1]), "+v"(dt[2]), "+v"(dt[3]));
+      de[0] = __builtin_amdgcn_exp2f(dt[0]);
+      de[1] = __builtin_amdgcn_exp2f(dt[1]);
+    } else if constexpr (K == 5) {
+      asm volatile("" : "+v"(dt[2]), "+v"(dt[3]), "+v"(de[0]), "+v"(de[1]));
+      de[2] = __builtin_amdgcn_exp2f(dt[2]);
+      de[3] = __builtin_amdgcn_exp2f(dt[3]);
+    } else if constexpr (K == 6) {
+      asm volatile("" : "+v"(de[0]), "+v"(de[1]), "+v"(de[2]), "+v"(de[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!DW) dz[i] = fmaf(de[i], rf[i], ry[i] == nc_y ? -1.f : 0.f);
+        else dz[i] = fmaf(de[i], nc_f, nc_y == vrow0 + i ? -1.f : 0.f);
+      }
+    } else {
+      asm volatile("" : "+v"(dz[0]), "+v"(dz[1]), "+v"(dz[2]), "+v"(dz[3]));
+      const float* g = dz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (DW) {
+          if (FILT) gpend[i] = g[i];  // added to grad_b once the tile is known to be kept
+          else gb[i] += g[i];
+        }
+      }
+      *reinterpret_cast<uint2*>(gl + o_gw) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
+      if (FILT) {
+        const float e = p.filter_eps;
+        const bool small = fabsf(g[0]) < e && fabsf(g[1]) < e && fabsf(g[2]) < e && fabsf(g[3]) < e;
+        const bool all_small = __builtin_amdgcn_ballot_w64(!small) == 0;
+        if (lane == 0) s_small[w] = all_small ? 1 : 0;
       }
     }
-    *reinterpret_cast<uint2*>(gl + o_gw) = make_uint2(pack_bf2(g[0], g[1]), pack_bf2(g[2], g[3]));
-    if (FILT) {
-      const float e = p.filter_eps;
-      const bool small = fabsf(g[0]) < e && fabsf(g[1]) < e && fabsf(g[2]) < e && fabsf(g[3]) < e;
-      const bool all_small = __builtin_amdgcn_ballot_w64(!small) == 0;
-      if (lane == 0) s_small[w] = all_small ? 1 : 0;
-    }
   };
-  // (FILT) after the barrier that follows dlogits: is the whole tile negligible?
+  // first half of GEMM1 (the MFMAs of gemm1_part(C0, CH)) with the eight dlogits steps after
+  // MFMAs NM-10 .. NM-3 (the earlier ones cover the latency of the partial-sum reads); with
+  // fewer MFMAs the remaining steps follow them
+  auto gemm1a_dlogits = [&]() {
+    constexpr int NM = 4 * (NB / 2);
+    constexpr int P0 = NM > 10 ? NM - 10 : 0;
+    static_for<0, NM>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      constexpr int ks = n / 4, rb = n % 4;
+      if constexpr (ks == 0) mfma16_v0(sf[ks][rb], xf1[ks], zp[rb]);
+      else mfma16_v(sf[ks][rb], xf1[ks], zp[rb]);
+      if constexpr (n >= P0 && n - P0 < 8) dl_step(std::integral_constant<int, n - P0>{});
+    });
+    static_for<(NM - P0 < 8 ? NM - P0 : 8), 8>([&](auto kc) { dl_step(kc); });
+  };  // (FILT) after the barrier that follows dlogits: is the whole tile negligible?
   auto tile_skipped = [&]() { return FILT && (s_small[0] & s_small[1] & s_small[2] & s_small[3]) != 0; };
   // GEMM3 of one tile: acc[64 x NCOL] += g[64 x 16] . X[16 x NCOL]; with `refill`, planes
   // 0 .. NB/2-1 of the buffer are reloaded (tile `next`) as soon as their last read has
@@ -857,11 +912,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     // ---- phase A (the first half of GEMM1(i+1)'s operands was read before the barrier)
     partial_reads();
     take_col(i, bi);
-    gemm1_part(C0{}, CH{});
-    // (keeps the dlogits arithmetic below the MFMAs, so that it runs while they execute
-    // instead of delaying their issue)
-    __builtin_amdgcn_sched_barrier(0);
-    dlogits();
+    gemm1a_dlogits();
     lds_order();
     gemm1_reads(bn, CH{}, CN{});  // in flight across the barrier
     if (i > 0) refill_rest();     // second half of tile i+3 (the buffer of tile i-1)
