@@ -838,7 +838,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
   // loads of the four waves spread over both phases.
   u32x4_t rx_next;
   uint32_t lds_next = 0;
-  auto gemm3 = [&](int buf, bool refill, int64_t next) {
+  // `mid` runs after GEMM3's operand reads are issued and before its MFMAs.
+  auto gemm3 = [&](int buf, bool refill, int64_t next, auto&& mid) {
     const char* xb = xw + buf * XW;
     const int64_t x0 = next * kPX;
     rx_next = make_rsrc_words(p.X + x0 * H, (p.nX - x0) * row_bytes);
@@ -847,6 +848,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     if (FILT) {
       if (tile_skipped()) {  // no MFMA work; the buffer refill still happens (nothing reads it)
         ++n_skipped;
+        mid();
         if (refill) {
 #pragma unroll
           for (int cb = 0; cb < NB / 2; ++cb) dma16(rx_next, lds_next + 1024 * cb, dma_off + 64 * cb);
@@ -867,6 +869,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     Frag<bf16_t> xf[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) xf[cb].v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
+    mid();
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       mfma_32x32x16(ga[0], xf[cb], acc[0][cb]);
@@ -919,9 +922,12 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_pipe_kernel(BwdArgs<bf16_t
     barrier_reads_in_flight<NB - NB / 2>();
     // ---- phase B: GEMM3 of tile i (refilling its buffer with tile i+4 plane by plane; past
     // the end the last tile is repeated, never read), partial z of tile i+1
+    // (the partial z of tile i+1 are written out between GEMM3's reads and its MFMAs, so the
+    // writes complete while the MFMAs run)
     gemm1_part(CH{}, CN{});
-    gemm3(bi, more, i + kPBuf < ntiles ? i + kPBuf : ntiles - 1);
-    if (more) put_partials();
+    gemm3(bi, more, i + kPBuf < ntiles ? i + kPBuf : ntiles - 1, [&]() {
+      if (more) put_partials();
+    });
     // The next phase A starts on GEMM1(i+2) at once: its first operand half is read here,
     // in flight across the barrier, once tile i+2 has landed.  The newest loads are then
     // those of B(i), A(i) and B(i-1) (tiles i+4 and i+3); everything older, so all of tile
