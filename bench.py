@@ -64,6 +64,30 @@ def _elapsed(hip, a, b):
     return ms.value
 
 
+def measure_extra_hbm(lce, torch, h, W, y, kw, ws_bytes) -> dict:
+    """Peak device memory one fused call adds beyond its inputs and preallocated outputs: the
+    torch allocator's peak delta around a call whose workspace the binding allocates (so it
+    is counted), and the device's free memory before and after a call with every buffer
+    preallocated (the library itself must not allocate)."""
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    lce.lce_fwd_bwd(h, W, None, y, **kw)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=h.device)
+    kw2 = dict(kw, workspace=ws)
+    lce.lce_fwd_bwd(h, W, None, y, **kw2)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    lce.lce_fwd_bwd(h, W, None, y, **kw2)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    del ws
+    return {"torch_peak_delta_bytes": int(peak), "device_free_delta_bytes": int(free0 - free1),
+            "workspace_bytes": int(ws_bytes)}
+
+
 def _sha(path: str) -> str:
     import hashlib
     with open(path, "rb") as f:
@@ -141,6 +165,7 @@ def bench_chunked(lce, torch, h, W, b, y, kw, exact, steps, BT) -> dict:
     torch.cuda.synchronize()
     out = {k: r[k] for k in ("loss", "grad_input", "grad_weight", "grad_bias", "n_valid") if r[k] is not None}
     ws = r["workspace"]
+    ws_bytes = ws.numel()
     t0 = time.perf_counter()
     for _ in range(steps):
         lce.lce_fwd_bwd(h, W, b, y, method="chunked", workspace=ws, out=out, **ckw)
@@ -155,8 +180,23 @@ def bench_chunked(lce, torch, h, W, b, y, kw, exact, steps, BT) -> dict:
     diffs = {k: rdiff(out[k], exact[k]) for k in ("grad_input", "grad_weight", "grad_bias")
              if out.get(k) is not None and exact.get(k) is not None}
     diffs["loss"] = abs(out["loss"].item() - exact["loss"].item()) / abs(exact["loss"].item())
-    return {"ms_per_step": ms, "tokens_per_s": BT / (ms * 1e-3), "workspace_bytes": int(ws.numel()),
-            "rel_diff_vs_fused": diffs}
+    del out, ws, r
+    # fp32 grad_W output (the chunked composition then sums into it directly), both methods
+    fp32 = {}
+    for method in ("fused", "chunked"):
+        r = lce.lce_fwd_bwd(h, W, b, y, method=method, grad_weight_fp32=True, **ckw)
+        torch.cuda.synchronize()
+        o = {k: r[k] for k in ("loss", "grad_input", "grad_weight", "grad_bias", "n_valid") if r[k] is not None}
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            lce.lce_fwd_bwd(h, W, b, y, method=method, grad_weight_fp32=True, workspace=r["workspace"], out=o, **ckw)
+        torch.cuda.synchronize()
+        msf = (time.perf_counter() - t0) * 1e3 / steps
+        fp32[method] = {"ms_per_step": msf, "workspace_bytes": int(r["workspace"].numel()),
+                        "grad_weight_rel_diff_vs_bf16_fused": rdiff(o["grad_weight"], exact["grad_weight"])}
+        del r, o
+    return {"ms_per_step": ms, "tokens_per_s": BT / (ms * 1e-3), "workspace_bytes": int(ws_bytes),
+            "rel_diff_vs_fused": diffs, "grad_weight_fp32": fp32}
 
 
 def bench_rows(lce, torch, h, W, b, y, steps, BT) -> dict:
@@ -238,11 +278,32 @@ def bench_ce(lce, torch, steps: int) -> dict:
     torch.cuda.synchronize()
     ms_copy = e0.elapsed_time(e1) / steps
     copy_gbs = 2 * c.B * c.V * 2 / (ms_copy * 1e-3) / 1e9
+    del dst
+    # the other variants of the same workload: z-loss on, and fp16 / fp32 logits
+    variants = []
+    for dt, mu in (("bf16", 1e-4), ("f16", 0.0), ("f32", 0.0)):
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+        xv = x.to(tdt)
+        wsv = torch.empty(lce.ce_workspace_bytes(c.B, c.V, tdt), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            lce.lce_ce_with_grad_inplace(xv, y, z_loss=mu, workspace=wsv, out=out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            lce.lce_ce_with_grad_inplace(xv, y, z_loss=mu, workspace=wsv, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        msv = e0.elapsed_time(e1) / steps
+        bv = 2 * c.B * c.V * xv.element_size() + 8 * c.B
+        variants.append({"dtype": dt, "z_loss": mu, "ms": msv, "GB/s": bv / (msv * 1e-3) / 1e9,
+                         "frac": bv / (msv * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": bv})
+        del xv, wsv
     return {"workload": f"standalone CE+dlogits in place, [{c.B}, {c.V}] bf16, z-loss 0",
             "ms": ms, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("ce_rows")},
             "algorithmic_bytes": algo_bytes,
-            "device_copy_same_bytes": {"ms": ms_copy, "GB/s": copy_gbs, "ce_vs_copy": gbs / copy_gbs}}
+            "device_copy_same_bytes": {"ms": ms_copy, "GB/s": copy_gbs, "ce_vs_copy": gbs / copy_gbs},
+            "variants": variants}
 
 
 def main():
@@ -374,6 +435,7 @@ def main():
     for _ in range(args.warmup):
         lce.lce_fwd_bwd(h, W, None, y, **kw)
     torch.cuda.synchronize()
+    hbm = measure_extra_hbm(lce, torch, h, W, y, dict(kw, workspace=None), ws_bytes)
     log(f"timing x{args.steps}")
 
     hip = _hip()
@@ -428,6 +490,7 @@ def main():
         "stage_ms": stage_ms,
         "extra_hbm_bytes": ws_bytes,
         "extra_hbm_budget_bytes": 512 * V * 4,
+        "extra_hbm_measured": hbm,
         "loss": loss,
     }
     log(f"fused step {ms_step:.2f} ms")
