@@ -139,7 +139,9 @@ __device__ __forceinline__ void mask_tail(Vec16<float>& v, int64_t c0, int64_t V
 }
 
 // Row cached in registers: NV vectors of 16 B per thread, all loaded before any is used
-// (buffer loads: bytes past the row read as zero and stores there are dropped).  NV is the
+// (buffer loads: bytes past the row read as zero and stores there are dropped; the stores
+// use the non-temporal cache policy, measured 4% faster, the loads the default one, which
+// measured faster than non-temporal loads).  NV is the
 // per-thread vector count rounded up to a power of two, so every vector index below NV/2 is
 // inside the row; the upper half is masked per element (-inf past V), so neither pass needs
 // a mask.  Rows are ld elements apart (ld >= V; ld * sizeof(T) a multiple of 16); the
@@ -207,7 +209,7 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_cached(T* __restrict__ log
 #pragma unroll
       for (int e = 0; e < EPV; ++e) d[e] -= (owner_lane && e == ey) ? 1.f : 0.f;
     }
-    store16(make_rsrc((char*)x + j * kSlice, row_bytes - j * kSlice), lane_off, pack_out(d, T()));
+    store16_nt(make_rsrc((char*)x + j * kSlice, row_bytes - j * kSlice), lane_off, pack_out(d, T()));
   }
   if (tid == 0) {
     out.ce[row] = valid ? (lse - xy) : 0.f;
@@ -271,7 +273,7 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_stream_vec(T* __restrict__
       d[e] = __builtin_amdgcn_exp2f(fmaf(v.get(e), kLog2e, -ll)) * scale;
       if (valid && j * EPV + e == y) d[e] -= 1.f;
     }
-    store16(rs, (uint32_t)(j * 16), pack_out(d, T()));
+    store16_nt(rs, (uint32_t)(j * 16), pack_out(d, T()));
   }
   if (tid == 0) {
     out.ce[row] = valid ? (lse - xy) : 0.f;

@@ -200,6 +200,13 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, 
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
+// The same with the non-temporal cache policy, for data a streaming kernel writes once and
+// no later kernel of the same call reads soon.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicyNT);
+}
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane (4*r + c) supplies the address of
 // row r, columns 4c..4c+3 of a 4 x 16 block of 16-bit values; lane i of the group receives
