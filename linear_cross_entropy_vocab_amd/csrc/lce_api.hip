@@ -9,9 +9,8 @@
 
 namespace lce {
 
-size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
-  (void)H;
-  (void)bf16;
+// The forward's pieces (also what the pipelined and column-chunked backward kernels use).
+size_t fused_base_bytes(int64_t BT, int64_t V) {
   const int64_t bt = BT > 0 ? BT : 1;
   const int64_t nt = (V + kFwdTileV - 1) / kFwdTileV;
   const int64_t nblk = (bt + kMergeThreads - 1) / kMergeThreads;
@@ -25,7 +24,24 @@ size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
   return n;
 }
 
-FusedWs fused_carve(void* ws, int64_t BT, int64_t V) {
+size_t logits_chunk_budget(int64_t BT, int64_t H, int64_t V) {
+  const int64_t inc = (V + H - 1) / H;
+  const int64_t need = (BT + inc - 1) / inc;
+  int64_t cs = 1;
+  while (cs < need) cs <<= 1;
+  return (size_t)cs * (size_t)V * 4;
+}
+
+size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
+  size_t n = fused_base_bytes(BT, V);
+  if (bf16 && H > 1024) {
+    const TwoPass tp = twopass_plan(BT, H, V);
+    if (tp.on) n += tp.bytes;
+  }
+  return n;
+}
+
+FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   const int64_t bt = BT > 0 ? BT : 1;
   FusedWs w;
   w.nt = (V + kFwdTileV - 1) / kFwdTileV;
@@ -46,6 +62,8 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t V) {
   w.tok = reinterpret_cast<float2*>(p);
   p += ws_align((size_t)bt * 8);
   w.biasf = reinterpret_cast<float*>(p);
+  w.big = nullptr;
+  if (bf16 && H > 1024 && twopass_plan(BT, H, V).on) w.big = static_cast<char*>(ws) + fused_base_bytes(BT, V);
   return w;
 }
 
@@ -106,7 +124,7 @@ static lce_status fused_call(const void* hidden, const void* W, const void* bias
   a.out_row_map = nullptr;
   a.filter_eps = filter_eps;
   a.filter_counts = filter_eps > 0.f ? filter_counts : nullptr;
-  const FusedWs w = fused_carve(workspace, BT, V);
+  const FusedWs w = fused_carve(workspace, BT, H, V, dtype == LCE_DTYPE_BF16);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   typedef hipError_t (*Launch)(const FusedArgs&, const FusedWs&, hipStream_t);

@@ -1429,11 +1429,13 @@ hipError_t launch_mat_reduce(const float* part, int nsplit, int64_t rows, int64_
 
 hipError_t launch_bwd_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.grad_input == nullptr || a.BT == 0) return hipSuccess;
+  if (use_twopass(a)) return launch_twopass_dinput(a, w, st);
   return a.bf16 ? launch_bwd<bf16_t>(a, w, false, st) : launch_bwd<float>(a, w, false, st);
 }
 
 hipError_t launch_bwd_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.grad_W == nullptr && a.grad_b == nullptr) return hipSuccess;
+  if (use_twopass(a)) return launch_twopass_dweight(a, w, st);
   return a.bf16 ? launch_bwd<bf16_t>(a, w, true, st) : launch_bwd<float>(a, w, true, st);
 }
 

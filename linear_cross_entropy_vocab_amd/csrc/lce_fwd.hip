@@ -226,18 +226,26 @@ constexpr int kFwdTileT2 = 256;
 // 16 consecutive rows.
 __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// STORE: instead of the (max, sum-exp) epilogue, the logits tile z + b is written in bf16 to
-// zout[t][v] (rows ld elements apart, ld a multiple of 64 and >= V; columns V..ld-1 are
-// written as 0): the logits chunk of the token-chunked composition ("Fused Linear
-// Cross-Entropy: ...", Strategy 1).
-template <bool STORE>
+// MODE kEpiLse: the (max, sum-exp) epilogue, one partial LSE per (vocabulary tile, token).
+// MODE kEpiLogits: the logits tile z + b is written in bf16 to zout[t][v] (rows ld elements
+// apart, ld a multiple of 64 and >= V; columns V..ld-1 are written as 0): the logits chunk of
+// the token-chunked composition ("Fused Linear Cross-Entropy: ...", Strategy 1).
+// MODE kEpiDlogits: as kEpiLogits, but what is written is the dlogit of the summed loss,
+// valid * (e^(z - LSE) (1 + 2 mu LSE) - onehot(y)), from the fp32 accumulator and the
+// per-token (LSE, target + 1) of tok[] (the forward's result); vbase is the vocabulary id of
+// row 0 of W (for the one-hot term when W is a block of the vocabulary).
+constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2;
+template <int MODE>
 __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16_t* __restrict__ W,
                                                                     const bf16_t* __restrict__ h,
                                                                     const bf16_t* __restrict__ bias,
                                                                     int64_t BT, int64_t H, int64_t V,
                                                                     int64_t nt_v, int64_t nt_t,
                                                                     float* __restrict__ lse_part,
-                                                                    bf16_t* __restrict__ zout, int64_t ld) {
+                                                                    bf16_t* __restrict__ zout, int64_t ld,
+                                                                    const float2* __restrict__ tok, float mu,
+                                                                    int64_t vbase) {
+  constexpr bool STORE = MODE != kEpiLse;
   constexpr int ROWB = 128;                       // bytes of one row per stage
   constexpr int TILE_A = kFwdTileV * ROWB;        // 32 KiB
   constexpr int TILE_B = kFwdTileT2 * ROWB;       // 32 KiB
@@ -245,6 +253,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   __shared__ __attribute__((aligned(1024))) char sB[2][TILE_B];
   __shared__ float s_bias[kFwdTileV];
   __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
+  __shared__ float2 s_tok[MODE == kEpiDlogits ? kFwdTileT2 : 1];
 
   const int64_t nwg = nt_v * nt_t;
   const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
@@ -311,6 +320,12 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     if (bias != nullptr && tid < kFwdTileV) {  // (the previous tile is done with s_bias)
       const int64_t v = tl.v0 + tid;
       s_bias[tid] = v < V ? bf2f(bias[v]) : 0.f;
+    }
+    if constexpr (MODE == kEpiDlogits) {  // the tile's tokens: (LSE, target + 1)
+      if (tid < kFwdTileT2) {
+        const int64_t t = tl.t0 + tid;
+        s_tok[tid] = t < BT ? tok[t] : make_float2(0.f, 0.f);
+      }
     }
     const int64_t nblk = blk + gridDim.x;
     const bool has_next = nblk < nwg;
@@ -383,6 +398,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) mfma_32x32x16(fbias[vb], fone, acc[vb][tb]);
     }
+    constexpr float kLog2e = 1.4426950408889634f;
     const int vlim = (int)((V - tl.v0) < kFwdTileV ? (V - tl.v0) : kFwdTileV);
     int ln = lane;
     asm volatile("" : "+v"(ln));  // keeps the row indices below from being hoisted out of the loop
@@ -401,6 +417,17 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int trow = (int)(tcol0 - tl.t0) + tb * 32 + (ln & 31);
+        // (dlogits) the token's base-2 exponent offset (-inf if it does not count), its
+        // z-loss factor, and the column c of its target in this lane's rows (none if < 0)
+        float ra = 0.f, fac = 0.f;
+        int cy = -1;
+        if constexpr (MODE == kEpiDlogits) {
+          const float2 tk = s_tok[trow];
+          const int yv = __float_as_int(tk.y) - 1;
+          ra = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
+          fac = 1.f + 2.f * mu * tk.x;
+          cy = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+        }
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) {
           uint32_t pk[4][2];
@@ -410,7 +437,10 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int c = vb * 32 + 8 * rr + e;
-              f[e] = (full || c < lim) ? acc[vb][tb][4 * rr + e] : 0.f;
+              float zv = acc[vb][tb][4 * rr + e];
+              if constexpr (MODE == kEpiDlogits)
+                zv = fmaf(__builtin_amdgcn_exp2f(fmaf(zv, kLog2e, ra)), fac, c == cy ? -1.f : 0.f);
+              f[e] = (full || c < lim) ? zv : 0.f;
             }
             pk[rr][0] = pack_bf2(f[0], f[1]);
             pk[rr][1] = pack_bf2(f[2], f[3]);
@@ -450,7 +480,6 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
           for (int r = 0; r < 16; ++r)
             if (vb * 32 + 8 * (r >> 2) + (r & 3) >= lim) acc[vb][tb][r] = -INFINITY;
     }
-    constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       float m = -INFINITY;
@@ -505,9 +534,9 @@ hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) 
   if (a.BT == 0) return hipSuccess;
   if (a.bf16) {
     const int64_t nt_t2 = (a.BT + kFwdTileT2 - 1) / kFwdTileT2;
-    hipLaunchKernelGGL(fwd_lse_dma_kernel<false>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0, st,
-                       (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
-                       a.V, w.nt, nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0);
+    hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLse>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
+                       st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
+                       nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0);
     return hipGetLastError();
   }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
@@ -666,8 +695,24 @@ hipError_t launch_logits_chunk(const bf16_t* W, const bf16_t* h_chunk, const bf1
   if (rows <= 0) return hipSuccess;
   const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
-  hipLaunchKernelGGL(fwd_lse_dma_kernel<true>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0, st,
-                     W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, zout, ld);
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
+                     st, W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, zout, ld, (const float2*)nullptr,
+                     0.f, (int64_t)0);
+  return hipGetLastError();
+}
+
+// Dlogits of the summed loss for `rows` tokens (hidden rows h_block, per-token tok_block) against
+// the vocabulary rows vbase .. vbase + V - 1 (W_block = W + vbase * H, bias_block likewise or
+// NULL), as bf16 rows of ld elements (columns V..ld-1 written as 0).
+hipError_t launch_dlogits_block(const bf16_t* W_block, const bf16_t* h_block, const bf16_t* bias_block,
+                                const float2* tok_block, float mu, int64_t rows, int64_t H, int64_t V,
+                                int64_t vbase, bf16_t* gout, int64_t ld, hipStream_t st) {
+  if (rows <= 0 || V <= 0) return hipSuccess;
+  const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
+  const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
+                     st, W_block, h_block, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok_block,
+                     mu, vbase);
   return hipGetLastError();
 }
 

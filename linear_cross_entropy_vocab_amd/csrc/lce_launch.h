@@ -27,11 +27,34 @@ struct FusedWs {
   float* biasf;       // [V] the bias in fp32 (written only when there is a bias)
   int64_t nt;         // number of vocab tiles
   int64_t nblk;       // number of merge blocks
+  char* big;          // the two-pass backward's buffers (bf16, H > 1024), or NULL
 };
 constexpr int kMergeThreads = 256;
 
 size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16);
-FusedWs fused_carve(void* ws, int64_t BT, int64_t V);
+size_t fused_base_bytes(int64_t BT, int64_t V);
+FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16);
+
+// Bytes of one fp32 logits chunk of the pages' chunk-size rule ("Fused Linear Cross-Entropy:
+// ...", "The chunk-size trick"): the extra-memory budget of the fused path.
+size_t logits_chunk_budget(int64_t BT, int64_t H, int64_t V);
+
+// Backward of the fused path for bf16 with H > 1024, in two passes over stored dlogits that
+// fit the budget left by the forward's workspace: pass 1 (grad_W, grad_b) takes blocks of vb
+// vocabulary rows with all tokens, pass 2 (grad_input) blocks of tb tokens with the whole
+// vocabulary; each block's dlogits are recomputed from hidden, W and the forward's LSE by the
+// forward kernel and consumed by the stored-dlogits GEMMs.  on = false: the sizes leave too
+// little room, and the column-chunked kernel is used instead.
+struct TwoPass {
+  bool on;
+  int64_t vb, ldv;          // pass 1: vocabulary rows per block, row length of its buffer
+  int64_t tb, ldt;          // pass 2: tokens per block, row length of its buffer
+  int64_t x_split;          // pass 2: vocabulary rows per partial-sum range
+  int nsplit, nb, hchunks;  // pass 2 ranges; column plan of the GEMMs
+  size_t g_bytes, part_bytes, bytes;
+};
+TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V);
+
 
 struct FusedArgs {
   const void* hidden;
@@ -81,6 +104,9 @@ hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_loss(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_bwd_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_bwd_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+bool use_twopass(const FusedArgs& a);
 
 // Gradient GEMMs on stored (unscaled) dlogits G [g_rows][ld] of one token chunk.
 struct MatArgs {
@@ -105,6 +131,9 @@ hipError_t launch_mat_reduce(const float* part, int nsplit, int64_t rows, int64_
                              const int64_t* n_valid, bool mean, hipStream_t st);
 hipError_t launch_logits_chunk(const uint16_t* W, const uint16_t* h_chunk, const uint16_t* bias, int64_t rows,
                                int64_t H, int64_t V, uint16_t* zout, int64_t ld, hipStream_t st);
+hipError_t launch_dlogits_block(const uint16_t* W_block, const uint16_t* h_block, const uint16_t* bias_block,
+                                const float2* tok_block, float mu, int64_t rows, int64_t H, int64_t V,
+                                int64_t vbase, uint16_t* gout, int64_t ld, hipStream_t st);
 
 // Token-chunked composition (bf16): chunk rows, padded row length of the logits chunk, and
 // the plan of the gradient GEMMs on it.

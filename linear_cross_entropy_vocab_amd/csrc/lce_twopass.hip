@@ -1,0 +1,172 @@
+// Backward of the fused path for bf16 inputs with H > 1024.
+//
+// The pipelined backward keeps a workgroup's 64 stationary rows and their 64 x H fp32
+// accumulators on chip, which stops at H = 1024.  Above that, the recompute of "Fused Linear
+// Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It" ("Why two passes") is
+// done with stored dlogits instead, in blocks that fit the memory the forward leaves of the
+// one-logits-chunk budget ("The chunk-size trick"):
+//   pass 2 (grad_input), for each block of tb tokens:
+//     G = dlogits(hidden[block] . W^T + b, LSE, y)   forward kernel, dlogits epilogue -> bf16
+//     grad_input[block] = c * G . W                    stored-dlogits GEMM (vocabulary ranges
+//                                                      summed by mat_reduce)
+//   pass 1 (grad_W, grad_b), for each block of vb vocabulary rows:
+//     G = dlogits(hidden . W[block]^T + b[block], LSE, y)
+//     grad_W[block] = c * G^T . hidden, grad_b[block] = c * column sums of G
+// Each gradient element is still produced by one workgroup (no atomics) and z is recomputed
+// once per pass, as in the pipelined path (10 BT V H flops in all).  The dlogits are those of
+// the summed loss, formed in fp32 from the GEMM accumulator and the forward's LSE and rounded
+// once to bf16 (the pipelined kernels use the same operand precision).
+#include <algorithm>
+
+#include "lce_common.h"
+#include "lce_launch.h"
+
+namespace lce {
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
+  TwoPass t{};
+  t.on = false;
+  mat_plan(H, &t.nb, &t.hchunks);
+  const size_t budget = logits_chunk_budget(BT, H, V);
+  const size_t base = fused_base_bytes(BT, V);
+  if (budget <= base + 4096) return t;
+  const size_t avail = budget - base - 4096;  // (the 16 bytes of a grad_b placeholder, aligned)
+  const int64_t vpad = round_up(V, 64);
+  // pass 1: as many vocabulary rows per block as fit, all tokens
+  if (BT > 0) {
+    const int64_t v_fit = (int64_t)(avail / ((size_t)BT * 2)) / 64 * 64;
+    if (v_fit < 64) return t;
+    t.vb = std::min<int64_t>(v_fit, vpad);
+  } else {
+    t.vb = vpad;
+  }
+  t.ldv = t.vb;
+  const size_t pass1 = ws_align((size_t)(BT > 0 ? BT : 1) * (size_t)t.ldv * 2);
+  // pass 2: token blocks of 64 .. 1024 rows; the vocabulary split into ranges (about two
+  // workgroups per compute unit, as in the token-chunked composition) as far as their fp32
+  // partial sums fit; the largest block whose grid fills the device, else the largest grid
+  t.ldt = vpad;
+  const int64_t bt_pad = round_up(std::max<int64_t>(BT, 1), 64);
+  int64_t best_tb = 0, best_grid = 0;
+  int best_ns = 0;
+  for (int64_t tb = 1024; tb >= 64; tb /= 2) {
+    const int64_t tbb = std::min(tb, bt_pad);
+    const size_t gb = ws_align((size_t)tbb * (size_t)t.ldt * 2);
+    if (gb >= avail) continue;
+    const int64_t base_wg = (tbb + 63) / 64 * t.hchunks;
+    int64_t ns = (512 + base_wg - 1) / base_wg;
+    const int64_t max_ns = std::max<int64_t>(1, (V + 1023) / 1024);
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, std::min<int64_t>(max_ns, 64)));
+    const int64_t ns_mem = (int64_t)((avail - gb) / ((size_t)tbb * (size_t)H * 4 + kWsAlign));
+    ns = std::min(ns, ns_mem);
+    if (ns < 1) continue;
+    const int64_t grid = base_wg * ns;
+    if (best_tb == 0 || (best_grid < 256 && grid > best_grid)) {
+      best_tb = tbb;
+      best_grid = grid;
+      best_ns = (int)ns;
+    }
+    if (best_grid >= 256) break;
+  }
+  if (best_tb == 0) return t;
+  t.tb = best_tb;
+  t.x_split = round_up((V + best_ns - 1) / best_ns, 16);
+  t.nsplit = (int)((V + t.x_split - 1) / t.x_split);
+  // (pass 1's buffer and pass 2's buffer + partial sums overlap: the passes run one after
+  // the other on the stream)
+  t.g_bytes = ws_align((size_t)t.tb * (size_t)t.ldt * 2);
+  t.part_bytes = ws_align((size_t)t.nsplit * (size_t)t.tb * (size_t)H * 4);
+  t.bytes = 256 + std::max(pass1, t.g_bytes + t.part_bytes);
+  if (t.bytes > avail + 4096) return t;
+  t.on = true;
+  return t;
+}
+
+bool use_twopass(const FusedArgs& a) {
+  return a.bf16 && a.H > 1024 && a.filter_eps == 0.f && a.out_row_map == nullptr && twopass_plan(a.BT, a.H, a.V).on;
+}
+
+// Region layout: [256 B: grad_b placeholder] then pass 1: [G (vb columns)], pass 2:
+// [G (all columns) | partial sums]
+hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  const TwoPass t = twopass_plan(a.BT, a.H, a.V);
+  if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
+  bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
+  float* part = reinterpret_cast<float*>(w.big + 256 + t.g_bytes);
+  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bf16_t* b = static_cast<const bf16_t*>(a.bias);
+  hipError_t e;
+  for (int64_t t0 = 0; t0 < a.BT; t0 += t.tb) {
+    const int64_t rows = std::min(t.tb, a.BT - t0);
+    if ((e = launch_dlogits_block(W, h + t0 * a.H, b, w.tok + t0, a.mu, rows, a.H, a.V, 0, g, t.ldt, st)) !=
+        hipSuccess)
+      return e;
+    MatArgs m{};
+    m.G = g;
+    m.ld = t.ldt;
+    m.g_rows = rows;
+    m.H = a.H;
+    m.hchunks = t.hchunks;
+    m.n_valid = w.n_valid;
+    m.mean = a.mean ? 1 : 0;
+    m.X = W;
+    m.nS = rows;
+    m.nX = a.V;
+    m.x_split = t.x_split;
+    m.nsplit = t.nsplit;
+    m.part = part;
+    if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
+    if ((e = launch_mat_reduce(part, t.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + t0 * a.H, w.n_valid,
+                               a.mean, st)) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  const TwoPass t = twopass_plan(a.BT, a.H, a.V);
+  if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
+  float* gb_flag = reinterpret_cast<float*>(w.big);  // never read or written (one pass per row)
+  bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
+  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bf16_t* b = static_cast<const bf16_t*>(a.bias);
+  hipError_t e;
+  for (int64_t v0 = 0; v0 < a.V; v0 += t.vb) {
+    const int64_t cols = std::min(t.vb, a.V - v0);
+    if ((e = launch_dlogits_block(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, cols, v0,
+                                  g, t.ldv, st)) != hipSuccess)
+      return e;
+    MatArgs m{};
+    m.G = g;
+    m.ld = t.ldv;
+    m.g_rows = a.BT;
+    m.H = a.H;
+    m.hchunks = t.hchunks;
+    m.n_valid = w.n_valid;
+    m.mean = a.mean ? 1 : 0;
+    m.X = h;
+    m.nS = cols;
+    m.nX = a.BT;
+    m.x_split = round_up(std::max<int64_t>(a.BT, 1), 16);
+    m.nsplit = 1;
+    m.part = nullptr;
+    m.acc = nullptr;
+    m.first = 1;
+    m.last = 1;
+    if (a.grad_W != nullptr) {
+      m.out_f32 = a.grad_w_f32 ? 1 : 0;
+      m.out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
+                           : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
+    }
+    m.gb_acc = a.grad_b != nullptr ? gb_flag : nullptr;
+    m.gb_out = a.grad_b != nullptr ? static_cast<bf16_t*>(a.grad_b) + v0 : nullptr;
+    if ((e = launch_mat_gemm(true, m, st)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace lce
