@@ -57,6 +57,10 @@ CASES = [
     ("f32", 150, 64, 2000, None, 0.0, "sum", 0.2, 18),
     ("bf16", 1, 8, 5, None, 0.0, "mean", 0.0, 19),
     ("bf16", 64, 64, 1, 0.1, 0.0, "mean", 0.0, 20),
+    # H > 1024 with room in the budget: the two-pass backward, with ragged vocabulary and
+    # token blocks (3 vocabulary blocks and 10 token blocks; 2 and 5)
+    ("bf16", 600, 1152, 9000, 0.1, 1e-4, "mean", 0.1, 21),
+    ("bf16", 300, 2112, 5000, None, 0.0, "sum", 0.2, 22),
 ]
 
 
@@ -95,8 +99,10 @@ def test_all_ignored_and_empty():
     assert torch.count_nonzero(r["grad_weight"]) == 0  # fully overwritten with zeros
 
 
-def test_grad_subsets():
-    inp = make_fused(120, 256, 900, dtype="bf16", seed=21, bias_std=0.1, ignore_frac=0.1)
+@pytest.mark.parametrize("shape", [(120, 256, 900), (600, 1152, 9000)], ids=["pipelined", "two-pass"])
+def test_grad_subsets(shape):
+    BT, H, V = shape
+    inp = make_fused(BT, H, V, dtype="bf16", seed=21, bias_std=0.1, ignore_frac=0.1)
     ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets)
     r = run_fused(inp, grad_input=False, grad_weight=False, grad_bias=True)
     assert r["grad_input"] is None and r["grad_weight"] is None
@@ -114,14 +120,17 @@ def test_fused_grad_weight_fp32():
     r16 = run_fused(inp)
     # the bf16 output is the same fp32 accumulator rounded once more
     assert torch.equal(r32["grad_weight"].to(torch.bfloat16), r16["grad_weight"])
-    big = make_fused(65, 2304, 257, dtype="bf16", seed=16, ignore_frac=0.05)   # column-chunked kernel
-    a32 = run_fused(big, grad_weight_fp32=True)
-    a16 = run_fused(big)
-    assert torch.equal(a32["grad_weight"].to(torch.bfloat16), a16["grad_weight"])
+    for shape, seed in (((65, 2304, 257), 16),      # column-chunked kernel
+                        ((300, 2112, 5000), 22)):   # two-pass backward
+        big = make_fused(*shape, dtype="bf16", seed=seed, ignore_frac=0.05)
+        a32 = run_fused(big, grad_weight_fp32=True)
+        a16 = run_fused(big)
+        assert torch.equal(a32["grad_weight"].to(torch.bfloat16), a16["grad_weight"]), shape
 
 
-def test_deterministic_bits():
-    inp = make_fused(333, 256, 3001, dtype="bf16", seed=12, bias_std=0.1, ignore_frac=0.1, z_loss=1e-3)
+@pytest.mark.parametrize("shape", [(333, 256, 3001), (600, 1152, 9000)], ids=["pipelined", "two-pass"])
+def test_deterministic_bits(shape):
+    inp = make_fused(*shape, dtype="bf16", seed=12, bias_std=0.1, ignore_frac=0.1, z_loss=1e-3)
     a = run_fused(inp)
     b = run_fused(inp)
     for k in ("loss", "grad_input", "grad_weight", "grad_bias", "lse"):
