@@ -1262,13 +1262,17 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
     }
     const u32x4_t rx = x_rsrc(nxt);
     const uint32_t lds_next = xw_lds + (uint32_t)(bi * XW);
+    // every operand read is issued before the first refill (a refill is an asm statement with
+    // a memory clobber: no LDS read can move across it, and reads issued after it would
+    // leave each pair of MFMAs waiting for its read's latency)
+    Frag<bf16_t> xf[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) xf[cb].v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      Frag<bf16_t> xf;
-      xf.v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
-      mfma_32x32x16(ga[0], xf, acc[0][cb]);
-      mfma_32x32x16(ga[1], xf, acc[1][cb]);
-      dma16_after(rx, lds_next + 1024 * cb, dma_off + 64 * cb, xf.v);
+      mfma_32x32x16(ga[0], xf[cb], acc[0][cb]);
+      mfma_32x32x16(ga[1], xf[cb], acc[1][cb]);
+      dma16_after(rx, lds_next + 1024 * cb, dma_off + 64 * cb, xf[cb].v);
     }
   }
   vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
