@@ -1223,6 +1223,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
   // (DW) grad_b: lane (q, l16) of wave w sums g[n = 4q..4q+3][m = 16 w + l16]
   const bool do_gb = DW && p.gb_acc != nullptr && hc == 0;
   float gbs = 0.f;
+  const bool filt = p.filter_eps > 0.f;
+  unsigned long long n_skipped = 0;
 
   if (ntiles > 0) {
     const int64_t last = ntiles - 1;
@@ -1241,6 +1243,28 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
     g_dma(nxt, (int)((i + kPBuf) % kGBuf));
     const char* gb = gs[gi];
     const char* xb = xw + bi * XW;
+    const u32x4_t rx = x_rsrc(nxt);
+    const uint32_t lds_next = xw_lds + (uint32_t)(bi * XW);
+    if (filt) {
+      // gradient filtering: every wave reads the whole g tile (2 KiB) and skips the tile's
+      // MFMA work (and its grad_b share) when all of it is below filter_eps in magnitude; the
+      // buffer is still refilled, so the load queue keeps its shape
+      const uint4 a0 = *reinterpret_cast<const uint4*>(gb + 16 * lane);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(gb + 1024 + 16 * lane);
+      const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      bool small = true;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        small = small && fabsf(__uint_as_float(wv[k] << 16)) < p.filter_eps &&
+                fabsf(__uint_as_float(wv[k] & 0xffff0000u)) < p.filter_eps;
+      }
+      if (__builtin_amdgcn_ballot_w64(!small) == 0) {
+        ++n_skipped;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) dma16(rx, lds_next + 1024 * cb, dma_off + 64 * cb);
+        continue;
+      }
+    }
     Frag<bf16_t> ga[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -1260,8 +1284,6 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
         gbs += bf2f(*reinterpret_cast<const bf16_t*>(gb + 128 * n + 32 * (w ^ gsw2(n)) + 2 * l16));
       }
     }
-    const u32x4_t rx = x_rsrc(nxt);
-    const uint32_t lds_next = xw_lds + (uint32_t)(bi * XW);
     // every operand read is issued before the first refill (a refill is an asm statement with
     // a memory clobber: no LDS read can move across it, and reads issued after it would
     // leave each pair of MFMAs waiting for its read's latency)
@@ -1276,6 +1298,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
     }
   }
   vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
+  if (filt && p.filter_counts != nullptr && hc == 0 && tid == 0) {  // (each tile counted once)
+    atomicAdd(&p.filter_counts[0], n_skipped);
+    atomicAdd(&p.filter_counts[1], (unsigned long long)ntiles);
+  }
 
   const long long nvalid = *p.n_valid;
   const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
@@ -1324,13 +1350,14 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
           const float4 t = lane_on ? *reinterpret_cast<const float4*>(tb + i * NCOL + 4 * lane) : old[i];
           const float4 v = make_float4(t.x + old[i].x, t.y + old[i].y, t.z + old[i].z, t.w + old[i].w);
           const int64_t k = row * H + col;
+          const int64_t ko = (p.out_row_map != nullptr ? (int64_t)p.out_row_map[row] : row) * H + col;
           if (!p.last) {
             *reinterpret_cast<float4*>(p.acc + k) = v;
           } else if (p.out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + k) =
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + ko) =
                 make_float4(cscale * v.x, cscale * v.y, cscale * v.z, cscale * v.w);
           } else {
-            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.out) + k) =
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.out) + ko) =
                 make_uint2(pack_bf2(cscale * v.x, cscale * v.y), pack_bf2(cscale * v.z, cscale * v.w));
           }
         }
@@ -1345,7 +1372,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
       if (q == 0 && r < p.nS) {
         const float v = gbs + (p.first ? 0.f : p.gb_acc[r]);
         if (!p.last) p.gb_acc[r] = v;
-        else p.gb_out[r] = f2bf(cscale * v);
+        else p.gb_out[p.out_row_map != nullptr ? p.out_row_map[r] : r] = f2bf(cscale * v);
       }
     }
   }

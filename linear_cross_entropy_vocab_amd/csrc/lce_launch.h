@@ -124,6 +124,9 @@ struct MatArgs {
   uint16_t* gb_out;   // grad_b output (bf16)
   const int64_t* n_valid;
   int mean;
+  const int32_t* out_row_map;  // grad_W / grad_b: output row of stationary row i (or NULL: i)
+  float filter_eps;            // > 0: gradient filtering of the g tiles (as the fused kernels)
+  unsigned long long* filter_counts;  // [2] skipped, examined tiles (with filter_eps > 0), or NULL
 };
 void mat_plan(int64_t H, int* nb, int* hchunks);
 hipError_t launch_mat_gemm(bool dw, const MatArgs& a, hipStream_t st);

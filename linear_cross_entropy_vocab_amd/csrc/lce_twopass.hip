@@ -84,8 +84,17 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   return t;
 }
 
-bool use_twopass(const FusedArgs& a) {
-  return a.bf16 && a.H > 1024 && a.filter_eps == 0.f && a.out_row_map == nullptr && twopass_plan(a.BT, a.H, a.V).on;
+bool use_twopass(const FusedArgs& a) { return a.bf16 && a.H > 1024 && twopass_plan(a.BT, a.H, a.V).on; }
+
+// Gradient filtering ("Cut Cross Entropy visualized", "Gradient Filtering") in the stored-
+// dlogits GEMMs: their tiles are the fused kernels' (64 tokens x 16 vocabulary entries for
+// grad_input, 64 entries x 16 tokens for grad_W, aligned at 0: the blocks are multiples of
+// 64 rows and the vocabulary ranges multiples of 16), tested on the stored bf16 dlogits.
+static void set_filter(MatArgs& m, const FusedArgs& a, int which) {
+  m.filter_eps = a.filter_eps;
+  m.filter_counts = a.filter_counts != nullptr && a.filter_eps > 0.f
+                        ? reinterpret_cast<unsigned long long*>(a.filter_counts + 2 * which)
+                        : nullptr;
 }
 
 // Region layout: [256 B: grad_b placeholder] then pass 1: [G (vb columns)], pass 2:
@@ -118,6 +127,7 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
     m.x_split = t.x_split;
     m.nsplit = t.nsplit;
     m.part = part;
+    set_filter(m, a, 0);
     if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
     if ((e = launch_mat_reduce(part, t.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + t0 * a.H, w.n_valid,
                                a.mean, st)) != hipSuccess)
@@ -157,13 +167,17 @@ hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStrea
     m.acc = nullptr;
     m.first = 1;
     m.last = 1;
+    // output rows: the block's rows in place, or (vocabulary sorting) through the order
+    const int64_t o0 = a.out_row_map != nullptr ? 0 : v0;
+    m.out_row_map = a.out_row_map != nullptr ? a.out_row_map + v0 : nullptr;
     if (a.grad_W != nullptr) {
       m.out_f32 = a.grad_w_f32 ? 1 : 0;
-      m.out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
-                           : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
+      m.out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + o0 * a.H)
+                           : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + o0 * a.H);
     }
     m.gb_acc = a.grad_b != nullptr ? gb_flag : nullptr;
-    m.gb_out = a.grad_b != nullptr ? static_cast<bf16_t*>(a.grad_b) + v0 : nullptr;
+    m.gb_out = a.grad_b != nullptr ? static_cast<bf16_t*>(a.grad_b) + o0 : nullptr;
+    set_filter(m, a, 1);
     if ((e = launch_mat_gemm(true, m, st)) != hipSuccess) return e;
   }
   return hipSuccess;
