@@ -1133,7 +1133,9 @@ static hipError_t launch_bwd(const FusedArgs& fa, const FusedWs& w, bool dw, hip
 //     chunks lives in `acc` (or in an fp32 output) and the last chunk writes c * sum; grad_b
 //     is the column sum of G, accumulated the same way.
 // ---------------------------------------------------------------------------
-template <bool DW, int NB>
+// FILT: gradient filtering of the g tiles (a separate instantiation: the skip branch around
+// the MFMAs makes the compiler copy the accumulators, which the unfiltered kernel must not pay).
+template <bool DW, int NB, bool FILT>
 __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
   constexpr int NCOL = 32 * NB;
   constexpr int XW = kPX * NCOL * 2;
@@ -1223,7 +1225,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
   // (DW) grad_b: lane (q, l16) of wave w sums g[n = 4q..4q+3][m = 16 w + l16]
   const bool do_gb = DW && p.gb_acc != nullptr && hc == 0;
   float gbs = 0.f;
-  const bool filt = p.filter_eps > 0.f;
+  constexpr bool filt = FILT;
   unsigned long long n_skipped = 0;
 
   if (ntiles > 0) {
@@ -1245,51 +1247,54 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
     const char* xb = xw + bi * XW;
     const u32x4_t rx = x_rsrc(nxt);
     const uint32_t lds_next = xw_lds + (uint32_t)(bi * XW);
-    if (filt) {
-      // gradient filtering: every wave reads the whole g tile (2 KiB) and skips the tile's
-      // MFMA work (and its grad_b share) when all of it is below filter_eps in magnitude; the
-      // buffer is still refilled, so the load queue keeps its shape
+    bool skip = false;
+    if constexpr (filt) {
+      // gradient filtering: every wave reads the whole g tile (2 KiB) and, when all of it is
+      // below filter_eps in magnitude, takes zero operands instead of reading the tile's X and
+      // g fragments (the LDS traffic is what bounds this kernel; the MFMAs still run, adding
+      // zero, so the accumulators never sit across a branch) and drops its grad_b share
       const uint4 a0 = *reinterpret_cast<const uint4*>(gb + 16 * lane);
       const uint4 a1 = *reinterpret_cast<const uint4*>(gb + 1024 + 16 * lane);
       const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      bool small = true;
+      float mx = 0.f;  // largest magnitude (no short-circuit: no branches per element)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        small = small && fabsf(__uint_as_float(wv[k] << 16)) < p.filter_eps &&
-                fabsf(__uint_as_float(wv[k] & 0xffff0000u)) < p.filter_eps;
-      }
-      if (__builtin_amdgcn_ballot_w64(!small) == 0) {
-        ++n_skipped;
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) dma16(rx, lds_next + 1024 * cb, dma_off + 64 * cb);
-        continue;
-      }
+      for (int k = 0; k < 8; ++k)
+        mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(wv[k] << 16)), fabsf(__uint_as_float(wv[k] & 0xffff0000u))));
+      skip = __builtin_amdgcn_ballot_w64(!(mx < p.filter_eps)) == 0;
+      if (skip) ++n_skipped;
     }
     Frag<bf16_t> ga[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if (DW) {
-        ga[sb].v = tr_pair(gb + o_ga[sb][0], gb + o_ga[sb][1]);
-      } else {
-        // tokens' rows hold vocabulary columns n = 0..15 in order; the B operand pairs its
-        // k index with the columns 0,1,4,5,2,3,6,7 (+8): swap the middle dwords
-        const uint4 r = *reinterpret_cast<const uint4*>(gb + o_ga[sb][0]);
-        ga[sb].v = __builtin_bit_cast(bf16x8_t, make_uint4(r.x, r.z, r.y, r.w));
-      }
-    }
-    if (do_gb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = 4 * q + j;
-        gbs += bf2f(*reinterpret_cast<const bf16_t*>(gb + 128 * n + 32 * (w ^ gsw2(n)) + 2 * l16));
-      }
-    }
     // every operand read is issued before the first refill (a refill is an asm statement with
     // a memory clobber: no LDS read can move across it, and reads issued after it would
     // leave each pair of MFMAs waiting for its read's latency)
     Frag<bf16_t> xf[NB];
+    if (!skip) {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) xf[cb].v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
+      for (int sb = 0; sb < 2; ++sb) {
+        if (DW) {
+          ga[sb].v = tr_pair(gb + o_ga[sb][0], gb + o_ga[sb][1]);
+        } else {
+          // tokens' rows hold vocabulary columns n = 0..15 in order; the B operand pairs its
+          // k index with the columns 0,1,4,5,2,3,6,7 (+8): swap the middle dwords
+          const uint4 r = *reinterpret_cast<const uint4*>(gb + o_ga[sb][0]);
+          ga[sb].v = __builtin_bit_cast(bf16x8_t, make_uint4(r.x, r.z, r.y, r.w));
+        }
+      }
+      if (do_gb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = 4 * q + j;
+          gbs += bf2f(*reinterpret_cast<const bf16_t*>(gb + 128 * n + 32 * (w ^ gsw2(n)) + 2 * l16));
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) xf[cb].v = tr_pair(xb + 1024 * cb + o_g3[0], xb + 1024 * cb + o_g3[1]);
+    } else {
+      zero8(ga[0]);
+      zero8(ga[1]);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) zero8(xf[cb]);
+    }
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       mfma_32x32x16(ga[0], xf[cb], acc[0][cb]);
@@ -1298,7 +1303,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
     }
   }
   vm_wait<0>();  // no load into LDS may still be in flight when the workgroup ends
-  if (filt && p.filter_counts != nullptr && hc == 0 && tid == 0) {  // (each tile counted once)
+  if (FILT && p.filter_counts != nullptr && hc == 0 && tid == 0) {  // (each tile counted once)
     atomicAdd(&p.filter_counts[0], n_skipped);
     atomicAdd(&p.filter_counts[1], (unsigned long long)ntiles);
   }
@@ -1424,12 +1429,21 @@ void mat_plan(int64_t H, int* nb, int* hchunks) {
 
 template <bool DW>
 static hipError_t launch_mat_dw(int nb, const MatArgs& a, dim3 grid, hipStream_t st) {
+  if (a.filter_eps > 0.f) {  // (filtering is used by the two-pass backward, H > 1024: NB 4, 6, 8)
+    switch (nb) {
+      case 4: hipLaunchKernelGGL((mat_gemm_kernel<DW, 4, true>), grid, dim3(kBwdThreads), 0, st, a); break;
+      case 6: hipLaunchKernelGGL((mat_gemm_kernel<DW, 6, true>), grid, dim3(kBwdThreads), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((mat_gemm_kernel<DW, 8, true>), grid, dim3(kBwdThreads), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (nb) {
-    case 1: hipLaunchKernelGGL((mat_gemm_kernel<DW, 1>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((mat_gemm_kernel<DW, 2>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((mat_gemm_kernel<DW, 4>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 6: hipLaunchKernelGGL((mat_gemm_kernel<DW, 6>), grid, dim3(kBwdThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((mat_gemm_kernel<DW, 8>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((mat_gemm_kernel<DW, 1, false>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((mat_gemm_kernel<DW, 2, false>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((mat_gemm_kernel<DW, 4, false>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 6: hipLaunchKernelGGL((mat_gemm_kernel<DW, 6, false>), grid, dim3(kBwdThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((mat_gemm_kernel<DW, 8, false>), grid, dim3(kBwdThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
