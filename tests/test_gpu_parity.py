@@ -61,6 +61,8 @@ CASES = [
     # token blocks (3 vocabulary blocks and 10 token blocks; 2 and 5)
     ("bf16", 600, 1152, 9000, 0.1, 1e-4, "mean", 0.1, 21),
     ("bf16", 300, 2112, 5000, None, 0.0, "sum", 0.2, 22),
+    ("bf16", 2000, 1280, 300, 0.2, 1e-3, "mean", 0.3, 23),   # two token blocks of 1024, one vocabulary block
+    ("bf16", 64, 1088, 70000, None, 0.0, "mean", 0.1, 24),   # budget too small for a block: column-chunked kernel
 ]
 
 
