@@ -328,7 +328,7 @@ def main():
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the fused op "
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); the fused op "
               f"has no multi-GPU path here", file=sys.stderr)
         sys.exit(2)
 
