@@ -220,8 +220,10 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
  * lce_rows_forward / lce_rows_backward -- per-row outputs of the LM head for RL-style use
  * ("Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It",
  * Strategy 2 keeps each row's target log-probability and softmax entropy beside the LSE)
- * and the gradients of any per-row weighted sum of them.  bf16 only; computed by the
- * token-chunked composition (same chunking and workspace as lce_fwd_bwd_chunked).
+ * and the gradients of any per-row weighted sum of them.  bf16 only.  The forward is one pass
+ * over the vocabulary with no logits stored (LSE and the softmax-weighted mean logit kept per
+ * vocabulary tile from the fp32 accumulator, then merged per row); the backward is the
+ * token-chunked composition (same chunking as lce_fwd_bwd_chunked).
  *
  * For row t with z_t = W h_t + b, LSE_t = log sum_v exp(z_tv), p_t = softmax(z_t) and
  * valid_t = (y_t != ignore_index):
@@ -237,8 +239,9 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
  *   alpha_t = valid_t (gl_t (1 + 2 mu LSE_t) - gp_t) + ge_t E_p[z_t],  beta_t = -ge_t,
  *   gamma_t = valid_t (gl_t - gp_t).
  * flags: LCE_FLAG_CHECK_TARGETS; lce_rows_backward also LCE_FLAG_GRAD_W_FP32.  Workspace:
- * lce_rows_workspace_bytes (= lce_fwd_bwd_chunked_workspace_bytes).  Errors as
- * lce_fwd_bwd_chunked.
+ * lce_rows_workspace_bytes (the larger of lce_fwd_bwd_chunked_workspace_bytes and the
+ * forward's per-(vocabulary tile, token) partials); one workspace serves both calls.  Errors
+ * as lce_fwd_bwd_chunked.
  */
 size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);
 lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias, const int64_t* targets,

@@ -292,8 +292,17 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
   return lce::chunk_call(a, lce::kLoss, lce::RowsHost{}, flags, workspace, stream);
 }
 
+// The per-row forward's own pieces: the fused forward's workspace and the per-tile mean logits.
+static size_t rows_forward_bytes(int64_t BT, int64_t V) {
+  const int64_t nt = (V + lce::kFwdTileV - 1) / lce::kFwdTileV;
+  return lce::fused_base_bytes(BT, V) + lce::ws_align((size_t)nt * (size_t)(BT > 0 ? BT : 1) * 4);
+}
+
 size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
-  return lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags);
+  const size_t c = lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags);
+  if (c == 0) return 0;
+  const size_t f = rows_forward_bytes(BT, V);
+  return c > f ? c : f;
 }
 
 lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
@@ -309,8 +318,27 @@ lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias,
   if (!lce::aligned(lse_out, 4) || !lce::aligned(logprobs_out, 4) || !lce::aligned(entropy_out, 4) ||
       !lce::aligned(row_loss_out, 4))
     return LCE_ERR_ALIGNMENT;
-  const lce::RowsHost io{lse_out, logprobs_out, entropy_out, row_loss_out, nullptr, nullptr, nullptr};
-  return lce::chunk_call(a, lce::kRowStats, io, flags, workspace, stream);
+  if (workspace_bytes < rows_forward_bytes(BT, V)) return LCE_ERR_WORKSPACE;
+  // one pass over the vocabulary: the fused forward with an (LSE, mean logit) epilogue
+  const lce::FusedWs w = lce::fused_carve(workspace, BT, H, V, false);
+  float* ez_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lce::fused_base_bytes(BT, V));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  lce::FusedArgs t = a;
+  t.bias = nullptr;  // (the pre-pass only counts; the forward adds the bias itself)
+  if (lce::launch_targets(t, w, st) != hipSuccess) return LCE_ERR_HIP;
+  if (flags & LCE_FLAG_CHECK_TARGETS) {
+    int32_t bad = 0;
+    if (hipMemcpyAsync(&bad, w.n_bad, sizeof(bad), hipMemcpyDeviceToHost, st) != hipSuccess) return LCE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LCE_ERR_HIP;
+    if (bad != 0) return LCE_ERR_TARGET_RANGE;
+  }
+  if (lce::launch_rows_fused_forward(a, w, ez_part, lse_out, logprobs_out, entropy_out, row_loss_out, st) !=
+      hipSuccess)
+    return LCE_ERR_HIP;
+  if (n_valid_out != nullptr &&
+      hipMemcpyAsync(n_valid_out, w.n_valid, sizeof(int64_t), hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return LCE_ERR_HIP;
+  return LCE_OK;
 }
 
 lce_status lce_rows_backward(const void* hidden, const void* W, const void* bias, const int64_t* targets,

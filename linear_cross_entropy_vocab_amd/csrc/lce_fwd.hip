@@ -230,11 +230,27 @@ __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1
 // MODE kEpiLogits: the logits tile z + b is written in bf16 to zout[t][v] (rows ld elements
 // apart, ld a multiple of 64 and >= V; columns V..ld-1 are written as 0): the logits chunk of
 // the token-chunked composition ("Fused Linear Cross-Entropy: ...", Strategy 1).
+// MODE kEpiLseEz: kEpiLse, and beside each partial LSE the tile's softmax-weighted mean logit
+// sum_v e^(z_v - m) z_v / sum_v e^(z_v - m) in ez_part (for the per-row entropy).
 // MODE kEpiDlogits: as kEpiLogits, but what is written is the dlogit of the summed loss,
 // valid * (e^(z - LSE) (1 + 2 mu LSE) - onehot(y)), from the fp32 accumulator and the
 // per-token (LSE, target + 1) of tok[] (the forward's result); vbase is the vocabulary id of
 // row 0 of W (for the one-hot term when W is a block of the vocabulary).
-constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2;
+constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3;
+
+// (m, s, t) with s = sum e^(z - m), t = sum e^(z - m) z, merged with a second such triple
+__device__ __forceinline__ void mst_combine(float& m, float& s, float& t, float m2, float s2, float t2) {
+  if (m2 > m) {
+    const float f = __expf(m - m2);
+    s = s * f + s2;
+    t = t * f + t2;
+    m = m2;
+  } else if (m2 != -INFINITY) {
+    const float f = __expf(m2 - m);
+    s += s2 * f;
+    t += t2 * f;
+  }
+}
 template <int MODE>
 __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16_t* __restrict__ W,
                                                                     const bf16_t* __restrict__ h,
@@ -244,8 +260,9 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
                                                                     float* __restrict__ lse_part,
                                                                     bf16_t* __restrict__ zout, int64_t ld,
                                                                     const float2* __restrict__ tok, float mu,
-                                                                    int64_t vbase) {
-  constexpr bool STORE = MODE != kEpiLse;
+                                                                    int64_t vbase, float* __restrict__ ez_part) {
+  constexpr bool STORE = MODE == kEpiLogits || MODE == kEpiDlogits;
+  constexpr bool EZ = MODE == kEpiLseEz;
   constexpr int ROWB = 128;                       // bytes of one row per stage
   constexpr int TILE_A = kFwdTileV * ROWB;        // 32 KiB
   constexpr int TILE_B = kFwdTileT2 * ROWB;       // 32 KiB
@@ -253,6 +270,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   __shared__ __attribute__((aligned(1024))) char sB[2][TILE_B];
   __shared__ float s_bias[kFwdTileV];
   __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
+  __shared__ float red_t[EZ ? 2 : 1][EZ ? kFwdTileT2 : 1];
   __shared__ float2 s_tok[MODE == kEpiDlogits ? kFwdTileT2 : 1];
 
   const int64_t nwg = nt_v * nt_t;
@@ -487,27 +505,47 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[vb][tb][r]);
-      float sm = 0.f;
+      float sm = 0.f, st = 0.f;
       if (m != -INFINITY) {
         // e^(z - m) = 2^(z log2 e - m log2 e): one FMA and the hardware base-2 exponential
         const float mb = m * kLog2e;
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sm += __builtin_amdgcn_exp2f(fmaf(acc[vb][tb][r], kLog2e, -mb));
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(acc[vb][tb][r], kLog2e, -mb));
+            sm += e;
+            // (rows past V hold -inf and e = 0: the product uses the largest finite value)
+            if constexpr (EZ) st = fmaf(e, fmaxf(acc[vb][tb][r], -3.0e38f), st);
+          }
       }
-      ms_merge(m, sm, __shfl_xor(m, 32, kWave), __shfl_xor(sm, 32, kWave));
+      if constexpr (EZ) {
+        const float m2 = __shfl_xor(m, 32, kWave), s2 = __shfl_xor(sm, 32, kWave), t2 = __shfl_xor(st, 32, kWave);
+        mst_combine(m, sm, st, m2, s2, t2);
+      } else {
+        ms_merge(m, sm, __shfl_xor(m, 32, kWave), __shfl_xor(sm, 32, kWave));
+      }
       if (lane < 32) {
         red_m[wv][wt * 64 + tb * 32 + lane] = m;
         red_s[wv][wt * 64 + tb * 32 + lane] = sm;
+        if constexpr (EZ) red_t[wv][wt * 64 + tb * 32 + lane] = st;
       }
     }
     __syncthreads();
     if (tid < kFwdTileT2) {
       float m = red_m[0][tid], sm = red_s[0][tid];
-      ms_merge(m, sm, red_m[1][tid], red_s[1][tid]);
       const int64_t t = tl.t0 + tid;
-      if (t < BT) lse_part[tl.vtile * BT + t] = m + __logf(sm);
+      if constexpr (EZ) {
+        float st = red_t[0][tid];
+        mst_combine(m, sm, st, red_m[1][tid], red_s[1][tid], red_t[1][tid]);
+        if (t < BT) {
+          lse_part[tl.vtile * BT + t] = m + __logf(sm);
+          ez_part[tl.vtile * BT + t] = sm > 0.f ? st / sm : 0.f;
+        }
+      } else {
+        ms_merge(m, sm, red_m[1][tid], red_s[1][tid]);
+        if (t < BT) lse_part[tl.vtile * BT + t] = m + __logf(sm);
+      }
     }
     if (!has_next) break;
     blk = nblk;
@@ -536,7 +574,8 @@ hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) 
     const int64_t nt_t2 = (a.BT + kFwdTileT2 - 1) / kFwdTileT2;
     hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLse>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
                        st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
-                       nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0);
+                       nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0,
+                       (float*)nullptr);
     return hipGetLastError();
   }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
@@ -654,6 +693,63 @@ hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ per-row outputs
+// Per token, from the per-tile partials of the kEpiLseEz forward: LSE and the softmax-weighted
+// mean logit E_p[z] (online over the tiles, in tile order), then the per-row outputs of
+// "Fused Linear Cross-Entropy: ...", Strategy 2: target log-probability z_y - LSE and row loss
+// LSE - z_y + mu LSE^2 for counted rows (0 otherwise), entropy LSE - E_p[z] for every row.
+__global__ void __launch_bounds__(kMergeThreads) rows_merge_kernel(
+    const float* __restrict__ lse_part, const float* __restrict__ ez_part, int64_t nt, int64_t BT,
+    const float* __restrict__ zy, const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float mu,
+    float* __restrict__ lse_out, float* __restrict__ logprobs, float* __restrict__ entropy,
+    float* __restrict__ row_loss) {
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (t >= BT) return;
+  float m = -INFINITY, s = 0.f, te = 0.f;
+  for (int64_t k = 0; k < nt; ++k) {
+    const float p = lse_part[k * BT + t];
+    const float e = ez_part[k * BT + t];
+    if (p == -INFINITY) continue;
+    if (p > m) {
+      const float f = __expf(m - p);
+      s = s * f + 1.f;
+      te = te * f + e;
+      m = p;
+    } else {
+      const float f = __expf(p - m);
+      s += f;
+      te = fmaf(f, e, te);
+    }
+  }
+  const float L = m + __logf(s);
+  const int64_t yt = y[t];
+  const bool valid = yt != ignore_index && yt >= 0 && yt < V;
+  if (lse_out) lse_out[t] = L;
+  if (entropy) entropy[t] = L - te / s;
+  if (logprobs) logprobs[t] = valid ? zy[t] - L : 0.f;
+  if (row_loss) row_loss[t] = valid ? L - zy[t] + mu * L * L : 0.f;
+}
+
+// The per-row outputs in one pass over the vocabulary (bf16): the forward GEMM with the
+// (LSE, E_p[z]) epilogue, the target-logit dot and the merge above.  The targets pre-pass
+// (n_valid, range check) has run.  ez_part: [number of vocabulary tiles][BT] floats.
+hipError_t launch_rows_fused_forward(const FusedArgs& a, const FusedWs& w, float* ez_part, float* lse_out,
+                                     float* logprobs, float* entropy, float* row_loss, hipStream_t st) {
+  if (a.BT == 0) return hipSuccess;
+  const int64_t nt_t2 = (a.BT + kFwdTileT2 - 1) / kFwdTileT2;
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLseEz>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
+                     st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
+                     nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0,
+                     ez_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_target_logit(a, w, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(rows_merge_kernel, dim3((unsigned)((a.BT + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, st, w.lse_part, ez_part, w.nt, a.BT, w.zy, a.targets, a.V,
+                     a.ignore_index, a.mu, lse_out, logprobs, entropy, row_loss);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ loss
 constexpr int kLossThreads = 256;
 
@@ -697,7 +793,7 @@ hipError_t launch_logits_chunk(const bf16_t* W, const bf16_t* h_chunk, const bf1
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, zout, ld, (const float2*)nullptr,
-                     0.f, (int64_t)0);
+                     0.f, (int64_t)0, (float*)nullptr);
   return hipGetLastError();
 }
 
@@ -712,7 +808,7 @@ hipError_t launch_dlogits_block(const bf16_t* W_block, const bf16_t* h_block, co
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W_block, h_block, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok_block,
-                     mu, vbase);
+                     mu, vbase, (float*)nullptr);
   return hipGetLastError();
 }
 

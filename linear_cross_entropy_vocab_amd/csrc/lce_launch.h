@@ -134,6 +134,8 @@ hipError_t launch_mat_reduce(const float* part, int nsplit, int64_t rows, int64_
                              const int64_t* n_valid, bool mean, hipStream_t st);
 hipError_t launch_logits_chunk(const uint16_t* W, const uint16_t* h_chunk, const uint16_t* bias, int64_t rows,
                                int64_t H, int64_t V, uint16_t* zout, int64_t ld, hipStream_t st);
+hipError_t launch_rows_fused_forward(const FusedArgs& a, const FusedWs& w, float* ez_part, float* lse_out,
+                                     float* logprobs, float* entropy, float* row_loss, hipStream_t st);
 hipError_t launch_dlogits_block(const uint16_t* W_block, const uint16_t* h_block, const uint16_t* bias_block,
                                 const float2* tok_block, float mu, int64_t rows, int64_t H, int64_t V,
                                 int64_t vbase, uint16_t* gout, int64_t ld, hipStream_t st);
