@@ -122,3 +122,36 @@ def test_rows_full_size_headline():
     assert rel_fro(gi, ref["grad_input"]) <= TOL["bf16"]["grad"]
     gw = g["grad_weight"].float()
     assert float(gw.sum(dim=0).norm() / gw.norm()) <= TOL["bf16"]["grad"]
+
+
+@pytest.mark.parametrize("name", ["headline", "gemma_like"])
+def test_filtered_tiny_eps_full_size(name):
+    """Gradient filtering at full size (pipelined backward at the headline, the two-pass
+    stored-dlogits backward at gemma_like): with eps below every |dlogit| no tile is skipped
+    and the filtered call reproduces the exact call bit for bit; with vocabulary sorting on
+    top, the loss and gradients (returned in the original vocabulary order) stay within the
+    bf16 tolerances of the exact call."""
+    c = CONFIGS[name]
+    print(f"full-size filtering, tiny eps: {name} BT={c.BT} H={c.H} V={c.V}", flush=True)
+    inp = make_config(name)
+    b = None if inp.bias is None else dev(inp.bias, c.dtype)
+    args = (dev(inp.hidden, c.dtype), dev(inp.weight, c.dtype), b, dev(inp.targets))
+    kw = dict(z_loss=c.z_loss, reduction=c.reduction)
+    exact = lce.lce_fwd_bwd(*args, **kw)
+    counts = torch.full((4,), -1, dtype=torch.int64, device="cuda")
+    filt = lce.lce_fwd_bwd(*args, filter_eps=1e-38, filter_counts=counts, **kw)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().tolist()
+    assert cnt[0] == 0 and cnt[2] == 0 and cnt[1] > 0 and cnt[3] > 0, cnt
+    keys = ["loss", "grad_input", "grad_weight"] + (["grad_bias"] if b is not None else [])
+    for k in keys:
+        assert torch.equal(exact[k], filt[k]), k
+    del filt
+    srt = lce.lce_fwd_bwd(*args, filter_eps=1e-38, sort_vocab=True, **kw)
+    torch.cuda.synchronize()
+    tol = TOL[c.dtype]
+    assert int(srt["n_valid"].item()) == int(exact["n_valid"].item())
+    assert rel(srt["loss"].item(), exact["loss"].item()) <= tol["loss"]
+    for k in keys[1:]:
+        e = float((srt[k].float() - exact[k].float()).norm() / exact[k].float().norm())
+        assert e <= tol["grad"], (k, e)

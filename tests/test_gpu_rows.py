@@ -130,3 +130,41 @@ def test_autograd_wrapper():
     assert rel_fro(host64(bb.grad), ref["grad_bias"]) <= TOL["bf16"]["grad"]
     ref1 = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, grad_logprobs=a2)
     assert rel_fro(host64(g1), ref1["grad_input"]) <= TOL["bf16"]["grad"]
+
+
+EDGE = [
+    (130, 128, 257, 0.1, 0.0, 0.1, 71),       # last vocabulary tile holds one row
+    (257, 64, 512, None, 1e-3, 0.0, 72),      # V a multiple of the tile; ragged token tile
+    (40, 2112, 9000, 0.1, 1e-4, 0.25, 73),    # H > 1024, many vocabulary tiles
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in EDGE])
+def test_rows_forward_edges_vs_oracle(case):
+    print(f"rows forward edge case {case}", flush=True)
+    inp, h, W, b, y = _inputs(case)
+    ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=inp.z_loss)
+    r = lce.lce_rows_forward(h, W, b, y, z_loss=inp.z_loss)
+    # any subset of the outputs is the same values, bit for bit
+    s = lce.lce_rows_forward(h, W, b, y, z_loss=inp.z_loss, outputs=("entropy",))
+    torch.cuda.synchronize()
+    assert s["lse"] is None and torch.equal(s["entropy"], r["entropy"])
+    assert int(r["n_valid"].item()) == ref["n_valid"]
+    bound = _row_bound(inp)
+    for k in ("lse", "logprobs", "entropy"):
+        err = np.abs(host64(r[k]) - ref[k])
+        assert np.all(err <= bound), (k, float((err / bound).max()))
+    err = np.abs(host64(r["row_loss"]) - ref["row_loss"])
+    assert np.all(err <= bound * (1.0 + 2.0 * inp.z_loss * np.abs(ref["lse"]))), "row_loss"
+
+
+def test_rows_forward_empty_batch_and_target_check():
+    inp, h, W, b, y = _inputs((50, 128, 700, 0.1, 0.0, 0.1, 74))
+    e = lce.lce_rows_forward(h[:0], W, b, y[:0], check_targets=True)
+    torch.cuda.synchronize()
+    assert int(e["n_valid"].item()) == 0 and e["lse"].numel() == 0
+    bad = y.clone()
+    bad[3] = 700
+    with pytest.raises(lce.LCEError):
+        lce.lce_rows_forward(h, W, b, bad, check_targets=True)
+    torch.cuda.synchronize()
