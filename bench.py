@@ -201,11 +201,13 @@ def bench_chunked(lce, torch, h, W, b, y, kw, exact, steps, BT) -> dict:
 
 def bench_rows(lce, torch, h, W, b, y, steps, BT) -> dict:
     """Per-row outputs for RL-style use on the same workload: the forward (LSE, target
-    log-probability, entropy, row loss) and the backward of a per-row weighted sum of them."""
+    log-probability, entropy, row loss) and the backward of a per-row weighted sum of them,
+    given the forward's LSE and entropy (and, for comparison, recomputing them)."""
     r = lce.lce_rows_forward(h, W, b, y)
     ws = r["workspace"]
     g = [torch.randn(BT, device="cuda", dtype=torch.float32) for _ in range(3)]
-    lce.lce_rows_backward(h, W, b, y, grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2], workspace=ws)
+    lce.lce_rows_backward(h, W, b, y, grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2],
+                          lse=r["lse"], entropy=r["entropy"], workspace=ws)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -214,12 +216,18 @@ def bench_rows(lce, torch, h, W, b, y, steps, BT) -> dict:
     t1 = time.perf_counter()
     for _ in range(steps):
         lce.lce_rows_backward(h, W, b, y, grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2],
-                              workspace=ws)
+                              lse=r["lse"], entropy=r["entropy"], workspace=ws)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
+    for _ in range(steps):
+        lce.lce_rows_backward(h, W, b, y, grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2],
+                              workspace=ws)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     fwd = (t1 - t0) * 1e3 / steps
     bwd = (t2 - t1) * 1e3 / steps
-    return {"forward_ms": fwd, "backward_ms": bwd, "tokens_per_s": BT / ((fwd + bwd) * 1e-3),
+    return {"forward_ms": fwd, "backward_ms": bwd, "backward_recompute_stats_ms": (t3 - t2) * 1e3 / steps,
+            "tokens_per_s": BT / ((fwd + bwd) * 1e-3),
             "workspace_bytes": int(ws.numel()),
             "mean_entropy": float(r["entropy"].mean().item())}
 

@@ -238,9 +238,16 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
  *   p_tv (alpha_t + beta_t z_tv) - gamma_t [v == y_t],
  *   alpha_t = valid_t (gl_t (1 + 2 mu LSE_t) - gp_t) + ge_t E_p[z_t],  beta_t = -ge_t,
  *   gamma_t = valid_t (gl_t - gp_t).
+ * lse_saved, entropy_saved: device float[BT] each, both or neither (else LCE_ERR_ARG): the LSE
+ * and entropy that lce_rows_forward wrote for the same inputs.  With them, E_p[z] = LSE - entropy
+ * is known, and each chunk's dlogits come straight from the logits GEMM's fp32 accumulator
+ * (no bf16 logits round trip, no second pass over the chunk); without them the chunk's logits
+ * are stored in bf16 and its statistics recomputed from them.  Values that do not belong to
+ * these inputs give gradients of no meaning (they are not checked).
  * flags: LCE_FLAG_CHECK_TARGETS; lce_rows_backward also LCE_FLAG_GRAD_W_FP32.  Workspace:
- * lce_rows_workspace_bytes (the larger of lce_fwd_bwd_chunked_workspace_bytes and the
- * forward's per-(vocabulary tile, token) partials); one workspace serves both calls.  Errors
+ * lce_rows_workspace_bytes (the larger of lce_fwd_bwd_chunked_workspace_bytes plus 20 bytes
+ * per row, and the forward's per-(vocabulary tile, token) partials); one workspace serves both
+ * calls.  Errors
  * as lce_fwd_bwd_chunked.
  */
 size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);
@@ -252,8 +259,9 @@ lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias,
 lce_status lce_rows_backward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
                              int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
                              float z_loss_mult, uint32_t flags, const float* grad_row_loss,
-                             const float* grad_logprobs, const float* grad_entropy, void* grad_input,
-                             void* grad_W, void* grad_b, void* workspace, size_t workspace_bytes, void* stream);
+                             const float* grad_logprobs, const float* grad_entropy, const float* lse_saved,
+                             const float* entropy_saved, void* grad_input, void* grad_W, void* grad_b,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes lce_ce_with_grad_inplace needs (per-row partial results), or 0 if invalid. */
 size_t lce_ce_workspace_bytes(int64_t B, int64_t V, lce_dtype dtype);

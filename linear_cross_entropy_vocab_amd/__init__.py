@@ -218,17 +218,22 @@ def lce_rows_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional
                       ignore_index: int = -100, z_loss: float = 0.0, grad_input: bool = True,
                       grad_weight: bool = True, grad_bias: Optional[bool] = None,
                       grad_weight_fp32: bool = False, check_targets: bool = False,
+                      lse: Optional[torch.Tensor] = None, entropy: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None) -> dict:
     """lce_rows_backward: gradients of sum_t gl_t row_loss_t + gp_t logprobs_t + ge_t entropy_t
-    (upstream gradients float32 [BT] on the device, or None for zeros)."""
+    (upstream gradients float32 [BT] on the device, or None for zeros).  `lse` and `entropy`,
+    both or neither, are lce_rows_forward's outputs for the same inputs: with them the logits
+    are not stored (each chunk's dlogits come from the GEMM accumulator)."""
     lib = load()
     BT, H, V = _rows_common(hidden, weight, bias, targets)
+    if (lse is None) != (entropy is None):
+        raise ValueError("pass both lse and entropy, or neither")
     ups = []
-    for g in (grad_row_loss, grad_logprobs, grad_entropy):
+    for g in (grad_row_loss, grad_logprobs, grad_entropy, lse, entropy):
         if g is not None:
             _need_gpu(g)
             if g.dtype != torch.float32 or g.numel() != BT:
-                raise TypeError("upstream per-row gradients must be float32 with BT elements")
+                raise TypeError("per-row gradients and saved outputs must be float32 with BT elements")
             g = g.contiguous()
         ups.append(g)
     if grad_bias is None:
@@ -244,13 +249,14 @@ def lce_rows_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     st = lib.lce_rows_backward(_ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets), BT, H, V, _lib.DTYPE_BF16,
                                ignore_index, float(z_loss), flags, _ptr(ups[0]), _ptr(ups[1]), _ptr(ups[2]),
-                               _ptr(gi), _ptr(gw), _ptr(gb), _ptr(workspace), workspace.numel(), stream)
+                               _ptr(ups[3]), _ptr(ups[4]), _ptr(gi), _ptr(gw), _ptr(gb), _ptr(workspace), workspace.numel(), stream)
     _lib.check(st, "lce_rows_backward")
     return dict(grad_input=gi, grad_weight=gw, grad_bias=gb, workspace=workspace)
 
 
 class _LinearRows(torch.autograd.Function):
-    """(logprobs, entropy, row_loss) per row; the backward recomputes the logits chunk by chunk."""
+    """(logprobs, entropy, row_loss) per row; the backward recomputes the logits chunk by chunk,
+    forming the dlogits from the saved LSE and entropy."""
 
     @staticmethod
     def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss):
@@ -258,14 +264,15 @@ class _LinearRows(torch.autograd.Function):
         b = None if bias is None else bias.contiguous()
         y = targets.contiguous()
         r = lce_rows_forward(h, W, b, y, ignore_index=ignore_index, z_loss=z_loss,
-                             outputs=("logprobs", "entropy", "row_loss"))
-        ctx.save_for_backward(h, W, b, y)
+                             outputs=("lse", "logprobs", "entropy", "row_loss"))
+        ent = r["entropy"]
+        ctx.save_for_backward(h, W, b, y, r["lse"], ent.clone())
         ctx.opts = (ignore_index, z_loss)
         return r["logprobs"], r["entropy"], r["row_loss"]
 
     @staticmethod
     def backward(ctx, g_lp, g_ent, g_rl):
-        h, W, b, y = ctx.saved_tensors
+        h, W, b, y, lse, ent = ctx.saved_tensors
         ignore_index, z_loss = ctx.opts
 
         def f32(g):
@@ -273,6 +280,7 @@ class _LinearRows(torch.autograd.Function):
 
         r = lce_rows_backward(h, W, b, y, grad_row_loss=f32(g_rl), grad_logprobs=f32(g_lp),
                               grad_entropy=f32(g_ent), ignore_index=ignore_index, z_loss=z_loss,
+                              lse=lse, entropy=ent,
                               grad_input=ctx.needs_input_grad[0], grad_weight=ctx.needs_input_grad[1],
                               grad_bias=b is not None and ctx.needs_input_grad[2])
         return r["grad_input"], r["grad_weight"], r["grad_bias"], None, None, None

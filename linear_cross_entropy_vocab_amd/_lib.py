@@ -64,7 +64,7 @@ def load() -> ctypes.CDLL:
     rows_head = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_i64, c_f, ctypes.c_uint32]
     lib.lce_rows_forward.argtypes = rows_head + [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
     lib.lce_rows_forward.restype = ctypes.c_int
-    lib.lce_rows_backward.argtypes = rows_head + [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
+    lib.lce_rows_backward.argtypes = rows_head + [c_vp] * 9 + [ctypes.c_size_t, c_vp]
     lib.lce_rows_backward.restype = ctypes.c_int
     lib.lce_stage_name.argtypes = [ctypes.c_int]
     lib.lce_stage_name.restype = ctypes.c_char_p

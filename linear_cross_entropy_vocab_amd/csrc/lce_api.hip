@@ -299,8 +299,9 @@ static size_t rows_forward_bytes(int64_t BT, int64_t V) {
 }
 
 size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
-  const size_t c = lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags);
+  size_t c = lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags);
   if (c == 0) return 0;
+  c += lce::rows_coef_bytes(BT);  // (the backward from saved forward outputs)
   const size_t f = rows_forward_bytes(BT, V);
   return c > f ? c : f;
 }
@@ -344,16 +345,23 @@ lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias,
 lce_status lce_rows_backward(const void* hidden, const void* W, const void* bias, const int64_t* targets,
                              int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
                              float z_loss_mult, uint32_t flags, const float* grad_row_loss,
-                             const float* grad_logprobs, const float* grad_entropy, void* grad_input,
-                             void* grad_W, void* grad_b, void* workspace, size_t workspace_bytes, void* stream) {
+                             const float* grad_logprobs, const float* grad_entropy, const float* lse_saved,
+                             const float* entropy_saved, void* grad_input, void* grad_W, void* grad_b,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   lce::FusedArgs a;
   const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
                                        LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32, grad_input, grad_W, grad_b,
                                        nullptr, workspace, workspace_bytes, &a);
   if (s != LCE_OK) return s;
-  if (!lce::aligned(grad_row_loss, 4) || !lce::aligned(grad_logprobs, 4) || !lce::aligned(grad_entropy, 4))
+  if (!lce::aligned(grad_row_loss, 4) || !lce::aligned(grad_logprobs, 4) || !lce::aligned(grad_entropy, 4) ||
+      !lce::aligned(lse_saved, 4) || !lce::aligned(entropy_saved, 4))
     return LCE_ERR_ALIGNMENT;
-  const lce::RowsHost io{nullptr, nullptr, nullptr, nullptr, grad_row_loss, grad_logprobs, grad_entropy};
+  if ((lse_saved == nullptr) != (entropy_saved == nullptr)) return LCE_ERR_ARG;
+  if (lse_saved != nullptr && BT > 0 &&
+      workspace_bytes < lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags) + lce::rows_coef_bytes(BT))
+    return LCE_ERR_WORKSPACE;
+  const lce::RowsHost io{nullptr,       nullptr,       nullptr,      nullptr,  grad_row_loss,
+                         grad_logprobs, grad_entropy,  lse_saved,    entropy_saved};
   return lce::chunk_call(a, lce::kRowGrads, io, flags, workspace, stream);
 }
 

@@ -56,6 +56,11 @@ size_t chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool grad_w_fp3
   return n;
 }
 
+size_t rows_coef_bytes(int64_t BT) {
+  const size_t bt = (size_t)std::max<int64_t>(BT, 1);
+  return ws_align(bt * 16) + ws_align(bt * 4);
+}
+
 // loss = c * sum_k (ce_k + mu z_k) over the chunks in order, in fp64.
 __global__ void chunk_loss_kernel(const float* __restrict__ ce, const float* __restrict__ z, int64_t nch,
                                   const int64_t* __restrict__ n_valid, float mu, int mean, float* loss_out,
@@ -108,6 +113,11 @@ hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bo
     gw_acc = static_cast<float*>(a.grad_W);
   }
   float* gb_acc = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)a.V * 4);
+  // (per-row backward from saved forward outputs) per-token coefficients and target columns
+  const bool saved = mode == kRowGrads && io.lse_in != nullptr && io.ent_in != nullptr;
+  float4* rtok = reinterpret_cast<float4*>(p);
+  int32_t* rcy = reinterpret_cast<int32_t*>(p + ws_align((size_t)std::max<int64_t>(a.BT, 1) * 16));
 
   // target pre-pass: n_valid (so c is known to every chunk) and the range check
   FusedArgs t = a;
@@ -127,6 +137,9 @@ hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bo
   const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bool grads = mode != kRowStats;
+  if (saved && (e = launch_rows_coef(io.lse_in, io.ent_in, a.targets, a.BT, a.V, a.ignore_index, a.mu, io.gl, io.gp,
+                                     io.ge, rtok, rcy, st)) != hipSuccess)
+    return e;
   const bool want_dw = grads && (a.grad_W != nullptr || a.grad_b != nullptr);
   auto off = [](const float* q, int64_t r0) { return q ? q + r0 : nullptr; };
   auto offw = [](float* q, int64_t r0) { return q ? q + r0 : nullptr; };
@@ -135,10 +148,14 @@ hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bo
     const int64_t r0 = k * c.cs;
     const int64_t rows = std::max<int64_t>(0, std::min<int64_t>(c.cs, a.BT - r0));
     const bf16_t* hk = h + r0 * a.H;
-    if ((e = launch_logits_chunk(W, hk, static_cast<const bf16_t*>(a.bias), rows, a.H, a.V, zbuf, c.ld, st)) !=
-        hipSuccess)
+    if (saved) {
+      // the chunk's dlogits straight from the GEMM accumulator
+      e = launch_rows_dlogits_chunk(W, hk, static_cast<const bf16_t*>(a.bias), rtok + r0, rcy + r0, rows, a.H, a.V,
+                                    zbuf, c.ld, st);
+    } else if ((e = launch_logits_chunk(W, hk, static_cast<const bf16_t*>(a.bias), rows, a.H, a.V, zbuf, c.ld, st)) !=
+               hipSuccess) {
       return e;
-    if (mode == kLoss) {
+    } else if (mode == kLoss) {
       e = launch_ce_inplace(zbuf, kCeBf16, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k, z_k + k,
                             nv_k + k, offw(a.lse_out, r0), ce_ws, st);
     } else {

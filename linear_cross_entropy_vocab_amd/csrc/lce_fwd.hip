@@ -236,7 +236,11 @@ __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1
 // valid * (e^(z - LSE) (1 + 2 mu LSE) - onehot(y)), from the fp32 accumulator and the
 // per-token (LSE, target + 1) of tok[] (the forward's result); vbase is the vocabulary id of
 // row 0 of W (for the one-hot term when W is a block of the vocabulary).
-constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3;
+// MODE kEpiRowsDlogits: as kEpiLogits, but what is written is the dlogit of a per-row weighted
+// sum of row losses, target log-probabilities and entropies, p (alpha + beta z) - gamma [v = y],
+// from the fp32 accumulator and the per-token (-LSE log2 e, alpha, beta, gamma) of rtok[] and
+// target column (or -1) of rcy[].
+constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4;
 
 // (m, s, t) with s = sum e^(z - m), t = sum e^(z - m) z, merged with a second such triple
 __device__ __forceinline__ void mst_combine(float& m, float& s, float& t, float m2, float s2, float t2) {
@@ -260,8 +264,11 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
                                                                     float* __restrict__ lse_part,
                                                                     bf16_t* __restrict__ zout, int64_t ld,
                                                                     const float2* __restrict__ tok, float mu,
-                                                                    int64_t vbase, float* __restrict__ ez_part) {
-  constexpr bool STORE = MODE == kEpiLogits || MODE == kEpiDlogits;
+                                                                    int64_t vbase, float* __restrict__ ez_part,
+                                                                    const float4* __restrict__ rtok,
+                                                                    const int32_t* __restrict__ rcy) {
+  constexpr bool RD = MODE == kEpiRowsDlogits;
+  constexpr bool STORE = MODE == kEpiLogits || MODE == kEpiDlogits || RD;
   constexpr bool EZ = MODE == kEpiLseEz;
   constexpr int ROWB = 128;                       // bytes of one row per stage
   constexpr int TILE_A = kFwdTileV * ROWB;        // 32 KiB
@@ -272,6 +279,8 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
   __shared__ float red_t[EZ ? 2 : 1][EZ ? kFwdTileT2 : 1];
   __shared__ float2 s_tok[MODE == kEpiDlogits ? kFwdTileT2 : 1];
+  __shared__ float4 s_rt[RD ? kFwdTileT2 : 1];
+  __shared__ int32_t s_rcy[RD ? kFwdTileT2 : 1];
 
   const int64_t nwg = nt_v * nt_t;
   const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
@@ -343,6 +352,13 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       if (tid < kFwdTileT2) {
         const int64_t t = tl.t0 + tid;
         s_tok[tid] = t < BT ? tok[t] : make_float2(0.f, 0.f);
+      }
+    }
+    if constexpr (RD) {  // the tile's tokens: coefficients and target column
+      if (tid < kFwdTileT2) {
+        const int64_t t = tl.t0 + tid;
+        s_rt[tid] = t < BT ? rtok[t] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+        s_rcy[tid] = t < BT ? rcy[t] : -1;
       }
     }
     const int64_t nblk = blk + gridDim.x;
@@ -446,6 +462,16 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
           fac = 1.f + 2.f * mu * tk.x;
           cy = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
         }
+        float al = 0.f, be = 0.f, ga = 0.f;
+        if constexpr (RD) {
+          const float4 rt = s_rt[trow];
+          ra = rt.x;
+          al = rt.y;
+          be = rt.z;
+          ga = -rt.w;
+          const int yv = s_rcy[trow];
+          cy = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+        }
 #pragma unroll
         for (int vb = 0; vb < 4; ++vb) {
           uint32_t pk[4][2];
@@ -458,6 +484,8 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
               float zv = acc[vb][tb][4 * rr + e];
               if constexpr (MODE == kEpiDlogits)
                 zv = fmaf(__builtin_amdgcn_exp2f(fmaf(zv, kLog2e, ra)), fac, c == cy ? -1.f : 0.f);
+              if constexpr (RD)
+                zv = fmaf(__builtin_amdgcn_exp2f(fmaf(zv, kLog2e, ra)), fmaf(be, zv, al), c == cy ? ga : 0.f);
               f[e] = (full || c < lim) ? zv : 0.f;
             }
             pk[rr][0] = pack_bf2(f[0], f[1]);
@@ -575,7 +603,7 @@ hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) 
     hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLse>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
                        st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
                        nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0,
-                       (float*)nullptr);
+                       (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
     return hipGetLastError();
   }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
@@ -740,7 +768,7 @@ hipError_t launch_rows_fused_forward(const FusedArgs& a, const FusedWs& w, float
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLseEz>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
                      st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
                      nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0,
-                     ez_part);
+                     ez_part, (const float4*)nullptr, (const int32_t*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_target_logit(a, w, st)) != hipSuccess) return e;
@@ -793,7 +821,7 @@ hipError_t launch_logits_chunk(const bf16_t* W, const bf16_t* h_chunk, const bf1
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, zout, ld, (const float2*)nullptr,
-                     0.f, (int64_t)0, (float*)nullptr);
+                     0.f, (int64_t)0, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
   return hipGetLastError();
 }
 
@@ -808,7 +836,53 @@ hipError_t launch_dlogits_block(const bf16_t* W_block, const bf16_t* h_block, co
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W_block, h_block, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok_block,
-                     mu, vbase, (float*)nullptr);
+                     mu, vbase, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+// Per-token coefficients of the per-row backward from the saved forward outputs (LSE and
+// entropy, so E_p[z] = LSE - entropy): for F = sum_t gl_t row_loss_t + gp_t logprobs_t +
+// ge_t entropy_t ("Fused Linear Cross-Entropy: ...", Strategy 2, per-row outputs), dF/dz_tv =
+// p_tv (alpha_t + beta_t z_tv) - gamma_t [v = y_t] with
+//   alpha = valid (gl (1 + 2 mu LSE) - gp) + ge E_p[z],  beta = -ge,  gamma = valid (gl - gp).
+__global__ void __launch_bounds__(kMergeThreads) rows_coef_kernel(
+    const float* __restrict__ lse, const float* __restrict__ entropy, const int64_t* __restrict__ y, int64_t BT,
+    int64_t V, int64_t ignore_index, float mu, const float* __restrict__ gl, const float* __restrict__ gp,
+    const float* __restrict__ ge, float4* __restrict__ rtok, int32_t* __restrict__ rcy) {
+  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  if (t >= BT) return;
+  const int64_t yt = y[t];
+  const bool valid = yt != ignore_index && yt >= 0 && yt < V;
+  const float L = lse[t];
+  const float ez = L - entropy[t];
+  const float a = gl ? gl[t] : 0.f, b = gp ? gp[t] : 0.f, c = ge ? ge[t] : 0.f;
+  const float alpha = (valid ? a * (1.f + 2.f * mu * L) - b : 0.f) + c * ez;
+  const float gamma = valid ? a - b : 0.f;
+  constexpr float kLog2e = 1.4426950408889634f;
+  rtok[t] = make_float4(-L * kLog2e, alpha, -c, gamma);
+  rcy[t] = valid ? (int32_t)yt : -1;
+}
+
+hipError_t launch_rows_coef(const float* lse, const float* entropy, const int64_t* y, int64_t BT, int64_t V,
+                            int64_t ignore_index, float mu, const float* gl, const float* gp, const float* ge,
+                            float4* rtok, int32_t* rcy, hipStream_t st) {
+  if (BT <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_coef_kernel, dim3((unsigned)((BT + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, st, lse, entropy, y, BT, V, ignore_index, mu, gl, gp, ge, rtok, rcy);
+  return hipGetLastError();
+}
+
+// Per-row dlogits of `rows` tokens (hidden rows h_chunk, coefficients rtok/rcy of those tokens)
+// against the whole vocabulary, as bf16 rows of ld elements (columns V..ld-1 written as 0).
+hipError_t launch_rows_dlogits_chunk(const bf16_t* W, const bf16_t* h_chunk, const bf16_t* bias, const float4* rtok,
+                                     const int32_t* rcy, int64_t rows, int64_t H, int64_t V, bf16_t* gout, int64_t ld,
+                                     hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
+  const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiRowsDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2),
+                     0, st, W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, (const float2*)nullptr,
+                     0.f, (int64_t)0, (float*)nullptr, rtok, rcy);
   return hipGetLastError();
 }
 

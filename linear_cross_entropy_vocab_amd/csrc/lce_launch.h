@@ -136,6 +136,12 @@ hipError_t launch_logits_chunk(const uint16_t* W, const uint16_t* h_chunk, const
                                int64_t H, int64_t V, uint16_t* zout, int64_t ld, hipStream_t st);
 hipError_t launch_rows_fused_forward(const FusedArgs& a, const FusedWs& w, float* ez_part, float* lse_out,
                                      float* logprobs, float* entropy, float* row_loss, hipStream_t st);
+hipError_t launch_rows_coef(const float* lse, const float* entropy, const int64_t* y, int64_t BT, int64_t V,
+                            int64_t ignore_index, float mu, const float* gl, const float* gp, const float* ge,
+                            float4* rtok, int32_t* rcy, hipStream_t st);
+hipError_t launch_rows_dlogits_chunk(const uint16_t* W, const uint16_t* h_chunk, const uint16_t* bias, const float4* rtok,
+                                     const int32_t* rcy, int64_t rows, int64_t H, int64_t V, uint16_t* gout, int64_t ld,
+                                     hipStream_t st);
 hipError_t launch_dlogits_block(const uint16_t* W_block, const uint16_t* h_block, const uint16_t* bias_block,
                                 const float2* tok_block, float mu, int64_t rows, int64_t H, int64_t V,
                                 int64_t vbase, uint16_t* gout, int64_t ld, hipStream_t st);
@@ -157,7 +163,11 @@ struct RowsHost {  // per-row outputs ([BT], each may be NULL) and upstream grad
   const float* gl;
   const float* gp;
   const float* ge;
+  const float* lse_in;  // (kRowGrads) the forward's LSE and entropy, or NULL: then the logits
+  const float* ent_in;  // chunk and its per-row statistics are recomputed
 };
+// Bytes the per-row backward with saved forward outputs adds to the chunked workspace.
+size_t rows_coef_bytes(int64_t BT);
 hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bool grad_w_fp32,
                       bool check_targets, void* workspace, hipStream_t st, bool* bad_targets);
 

@@ -170,11 +170,12 @@ def rows_fwd(lib, **kw):
 def rows_bwd(lib, **kw):
     a = dict(hidden=P, W=P + 0x100000, bias=None, targets=P + 0x200000, BT=100, H=64, V=1000,
              dtype=BF16, ignore=-100, mu=0.0, flags=0, gl=P + 0x300000, gp=None, ge=None,
-             gi=P + 0x400000, gw=P + 0x500000, gb=None, ws=P + 0x700000, wsb=OK_WS, stream=None)
+             lse=None, ent=None, gi=P + 0x400000, gw=P + 0x500000, gb=None, ws=P + 0x700000, wsb=OK_WS,
+             stream=None)
     a.update(kw)
     return lib.lce_rows_backward(a["hidden"], a["W"], a["bias"], a["targets"], a["BT"], a["H"], a["V"],
-                                 a["dtype"], a["ignore"], a["mu"], a["flags"], a["gl"], a["gp"], a["ge"], a["gi"],
-                                 a["gw"], a["gb"], a["ws"], a["wsb"], a["stream"])
+                                 a["dtype"], a["ignore"], a["mu"], a["flags"], a["gl"], a["gp"], a["ge"], a["lse"],
+                                 a["ent"], a["gi"], a["gw"], a["gb"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -189,6 +190,7 @@ def test_rows_forward_host_errors(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(W=None), 1), (dict(hidden=None), 1), (dict(V=0), 2), (dict(dtype=F32), 3), (dict(gl=P + 2), 4),
     (dict(gi=P + 8), 4), (dict(wsb=16), 5), (dict(gb=P + 0x800000), 6), (dict(flags=8), 6),
+    (dict(lse=P + 0x600000), 6), (dict(ent=P + 0x600000), 6), (dict(lse=P + 0x600002, ent=P + 0x610000), 4),
 ])
 def test_rows_backward_host_errors(lib, kw, status):
     assert rows_bwd(lib, **kw) == status

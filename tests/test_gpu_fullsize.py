@@ -95,10 +95,12 @@ def test_ce_full_size(mu):
     assert int(torch.count_nonzero(x[ign])) == 0
 
 
-def test_rows_full_size_headline():
-    """Per-row outputs and their backward at the headline size: sampled rows against the
-    per-row oracle (each row's values and grad_input row depend on that row only), and the
-    vocabulary sum of grad_W, which vanishes for logprob and entropy upstreams alone."""
+@pytest.mark.parametrize("saved", [False, True], ids=["recomputed", "saved"])
+def test_rows_full_size_headline(saved):
+    """Per-row outputs and their backward at the headline size (statistics recomputed, or the
+    forward's LSE and entropy passed in): sampled rows against the per-row oracle (each row's
+    values and grad_input row depend on that row only), and the vocabulary sum of grad_W,
+    which vanishes for logprob and entropy upstreams alone."""
     c = CONFIGS["headline"]
     print(f"full-size per-row parity: headline BT={c.BT} H={c.H} V={c.V}", flush=True)
     inp = make_config("headline")
@@ -107,7 +109,9 @@ def test_rows_full_size_headline():
     rng = np.random.default_rng(4)
     gp = rng.normal(size=c.BT).astype(np.float32)
     ge = rng.normal(size=c.BT).astype(np.float32)
-    g = lce.lce_rows_backward(h, W, None, y, grad_logprobs=dev(gp), grad_entropy=dev(ge), workspace=f["workspace"])
+    st = dict(lse=f["lse"], entropy=f["entropy"]) if saved else {}
+    g = lce.lce_rows_backward(h, W, None, y, grad_logprobs=dev(gp), grad_entropy=dev(ge), workspace=f["workspace"],
+                              **st)
     torch.cuda.synchronize()
     rows = np.array([0, 1, 777, 30000, c.BT - 1] + list(np.nonzero(inp.targets == -100)[0][:2]))
     ref = oracle.lce_rows_oracle(inp.hidden[rows], inp.weight, None, inp.targets[rows],

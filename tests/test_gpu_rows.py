@@ -58,23 +58,51 @@ def test_rows_forward_vs_oracle(case):
     assert np.all(host64(r["logprobs"])[ign] == 0.0) and np.all(host64(r["row_loss"])[ign] == 0.0)
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in CASES])
-def test_rows_backward_vs_oracle(case):
-    print(f"rows backward case {case}", flush=True)
+@pytest.mark.parametrize("saved", [False, True], ids=["recomputed", "saved"])
+@pytest.mark.parametrize("case", CASES + [(40, 2112, 9000, 0.1, 1e-4, 0.25, 66)],
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in CASES] + ["40x2112x9000"])
+def test_rows_backward_vs_oracle(case, saved):
+    """Both forms of the backward: statistics recomputed from the stored bf16 logits chunk, and
+    dlogits formed in the GEMM epilogue from the forward's saved LSE and entropy."""
+    print(f"rows backward case {case} saved={saved}", flush=True)
     inp, h, W, b, y = _inputs(case)
     BT = inp.hidden.shape[0]
     rng = np.random.default_rng(case[-1])
     gl, gp, ge = (rng.normal(size=BT).astype(np.float32) for _ in range(3))
     ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=inp.z_loss,
                                  grad_row_loss=gl, grad_logprobs=gp, grad_entropy=ge)
+    st = {}
+    if saved:
+        f = lce.lce_rows_forward(h, W, b, y, z_loss=inp.z_loss, outputs=("lse", "entropy"))
+        st = dict(lse=f["lse"], entropy=f["entropy"], workspace=f["workspace"])
     r = lce.lce_rows_backward(h, W, b, y, grad_row_loss=dev(gl), grad_logprobs=dev(gp), grad_entropy=dev(ge),
-                              z_loss=inp.z_loss)
+                              z_loss=inp.z_loss, **st)
     torch.cuda.synchronize()
     for k in ("grad_input", "grad_weight", "grad_bias"):
         if ref[k] is None:
             continue
         e = rel_fro(host64(r[k]), ref[k])
         assert e <= TOL["bf16"]["grad"], (k, e)
+
+
+def test_rows_backward_saved_matches_recomputed():
+    """The two forms differ only in where each dlogit is rounded to bf16 (from the fp32
+    accumulator, or after the logits' own bf16 rounding): close, and both deterministic."""
+    inp, h, W, b, y = _inputs((700, 1280, 5000, 0.1, 1e-4, 0.05, 69))
+    BT = inp.hidden.shape[0]
+    rng = np.random.default_rng(69)
+    g = [dev(rng.normal(size=BT).astype(np.float32)) for _ in range(3)]
+    f = lce.lce_rows_forward(h, W, b, y, z_loss=inp.z_loss)
+    kw = dict(grad_row_loss=g[0], grad_logprobs=g[1], grad_entropy=g[2], z_loss=inp.z_loss)
+    r0 = lce.lce_rows_backward(h, W, b, y, **kw)
+    r1 = lce.lce_rows_backward(h, W, b, y, lse=f["lse"], entropy=f["entropy"], **kw)
+    r2 = lce.lce_rows_backward(h, W, b, y, lse=f["lse"], entropy=f["entropy"], **kw)
+    torch.cuda.synchronize()
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        assert torch.equal(r1[k], r2[k]), k
+        assert rel_fro(host64(r1[k]), host64(r0[k])) <= 5e-3, k
+    with pytest.raises(ValueError):
+        lce.lce_rows_backward(h, W, b, y, lse=f["lse"], **kw)
 
 
 def test_rows_backward_single_upstreams_and_fp32_weight():
