@@ -1312,17 +1312,24 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mat_gemm_kernel(MatArgs p) {
   const float cscale = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
   if (!DW) {
     float* part = p.part + (int64_t)split * p.nS * H;
+    auto put = [&](auto add) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int64_t col = kw0 + cb * 32 + (lane & 31);
+        for (int cb = 0; cb < NB; ++cb) {
+          const int64_t col = kw0 + cb * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = s0 + sb * 32 + acc_row(lane, r);
-          if (row < p.nS && col < H) part[row * H + col] = acc[sb][cb][r];
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = s0 + sb * 32 + acc_row(lane, r);
+            if (row < p.nS && col < H) {
+              float* q = part + row * H + col;
+              *q = decltype(add)::value ? acc[sb][cb][r] + *q : acc[sb][cb][r];
+            }
+          }
         }
-      }
+    };
+    if (p.part_add) put(std::true_type{});
+    else put(std::false_type{});
   } else {
     if (p.acc != nullptr || p.out != nullptr) {
       // Read-modify-write of the running fp32 sums in 16-byte pieces: each half (32 rows) of

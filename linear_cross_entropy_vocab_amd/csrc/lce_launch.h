@@ -49,8 +49,9 @@ struct TwoPass {
   bool on;
   int64_t vb, ldv;          // pass 1: vocabulary rows per block, row length of its buffer
   int64_t tb, ldt;          // pass 2: tokens per block, row length of its buffer
-  int64_t x_split;          // pass 2: vocabulary rows per partial-sum range
-  int nsplit, nb, hchunks;  // pass 2 ranges; column plan of the GEMMs
+  int64_t vr;               // pass 2: vocabulary rows per dlogits block (ldt = vr rounded up to 64)
+  int64_t x_split;          // pass 2: vocabulary rows per partial-sum range within a block
+  int nsplit, nb, hchunks;  // pass 2 partial sums (ranges of the first block); column plan
   size_t g_bytes, part_bytes, bytes;
 };
 TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V);
@@ -117,6 +118,7 @@ struct MatArgs {
   int64_t x_split;    // streamed rows per split (multiple of 16)
   int nsplit, hchunks;
   float* part;        // grad_input: [nsplit][nS][H] fp32 partial sums
+  int part_add;       // grad_input: add into the partial sums instead of overwriting them
   float* acc;         // grad_W: [V][H] fp32 sum over the chunks so far (may equal out when out_f32)
   void* out;          // grad_W output (written by the last chunk, scaled by c), or NULL
   int out_f32, first, last;

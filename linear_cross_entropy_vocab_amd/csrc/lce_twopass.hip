@@ -44,16 +44,40 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   }
   t.ldv = t.vb;
   const size_t pass1 = ws_align((size_t)(BT > 0 ? BT : 1) * (size_t)t.ldv * 2);
-  // pass 2: token blocks of 64 .. 1024 rows; the vocabulary split into ranges (about two
-  // workgroups per compute unit, as in the token-chunked composition) as far as their fp32
-  // partial sums fit; the largest block whose grid fills the device, else the largest grid
-  t.ldt = vpad;
+  // pass 2, candidate A: token blocks of 256 rows (the forward kernel's token tile, so its
+  // dlogits GEMM wastes no MFMA work) over vocabulary blocks of vr rows, each block's grad_input
+  // GEMM adding into the same fp32 partial sums (its vocabulary split into ranges: about two
+  // workgroups per compute unit as far as the partial sums fit, with blocks of >= 64Ki rows or
+  // the whole vocabulary, so that each dlogits launch still fills the device)
   const int64_t bt_pad = round_up(std::max<int64_t>(BT, 1), 64);
-  int64_t best_tb = 0, best_grid = 0;
-  int best_ns = 0;
+  int64_t a_tb = 0, a_grid = 0, a_vr = 0;
+  int a_ns = 0;
+  {
+    const int64_t tbb = std::min<int64_t>(256, bt_pad);
+    const int64_t base_wg = (tbb + 63) / 64 * t.hchunks;
+    const int64_t vr_min = std::min<int64_t>(vpad, 65536);
+    for (int64_t ns = std::min<int64_t>((512 + base_wg - 1) / base_wg, 64); ns >= 1; ns /= 2) {
+      const size_t pb = ws_align((size_t)ns * (size_t)tbb * (size_t)H * 4) + kWsAlign;
+      if (pb >= avail) continue;
+      const int64_t vr = std::min(vpad, (int64_t)((avail - pb) / ((size_t)tbb * 2)) / 64 * 64);
+      if (vr < vr_min) continue;
+      // (each block's ranges are multiples of 16 rows; the first block holds the most)
+      const int64_t vr0 = std::min(vr, V);
+      const int64_t xs = round_up((vr0 + ns - 1) / ns, 16);
+      a_tb = tbb;
+      a_grid = base_wg * ((vr0 + xs - 1) / xs);
+      a_ns = (int)ns;
+      a_vr = vr;
+      break;
+    }
+  }
+  // candidate B: token blocks of 64 .. 1024 rows against the whole vocabulary, split into
+  // ranges as above; the largest block whose grid fills the device, else the largest grid
+  int64_t b_tb = 0, b_grid = 0;
+  int b_ns = 0;
   for (int64_t tb = 1024; tb >= 64; tb /= 2) {
     const int64_t tbb = std::min(tb, bt_pad);
-    const size_t gb = ws_align((size_t)tbb * (size_t)t.ldt * 2);
+    const size_t gb = ws_align((size_t)tbb * (size_t)vpad * 2);
     if (gb >= avail) continue;
     const int64_t base_wg = (tbb + 63) / 64 * t.hchunks;
     int64_t ns = (512 + base_wg - 1) / base_wg;
@@ -63,17 +87,32 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
     ns = std::min(ns, ns_mem);
     if (ns < 1) continue;
     const int64_t grid = base_wg * ns;
-    if (best_tb == 0 || (best_grid < 256 && grid > best_grid)) {
-      best_tb = tbb;
-      best_grid = grid;
-      best_ns = (int)ns;
+    if (b_tb == 0 || (b_grid < 256 && grid > b_grid)) {
+      b_tb = tbb;
+      b_grid = grid;
+      b_ns = (int)ns;
     }
-    if (best_grid >= 256) break;
+    if (b_grid >= 256) break;
+  }
+  // A unless its grid-stride GEMMs would leave more of the device idle than B's
+  int64_t best_tb = 0;
+  int best_ns = 0;
+  if (a_tb > 0 && (b_tb == 0 || a_grid >= std::min<int64_t>(256, b_grid))) {
+    best_tb = a_tb;
+    best_ns = a_ns;
+    t.vr = a_vr;
+    t.ldt = a_vr;
+  } else {
+    best_tb = b_tb;
+    best_ns = b_ns;
+    t.vr = V;
+    t.ldt = vpad;
   }
   if (best_tb == 0) return t;
   t.tb = best_tb;
-  t.x_split = round_up((V + best_ns - 1) / best_ns, 16);
-  t.nsplit = (int)((V + t.x_split - 1) / t.x_split);
+  const int64_t vr0 = std::min(t.vr, V);
+  t.x_split = round_up((vr0 + best_ns - 1) / best_ns, 16);
+  t.nsplit = (int)((vr0 + t.x_split - 1) / t.x_split);
   // (pass 1's buffer and pass 2's buffer + partial sums overlap: the passes run one after
   // the other on the stream)
   t.g_bytes = ws_align((size_t)t.tb * (size_t)t.ldt * 2);
@@ -110,25 +149,31 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
   hipError_t e;
   for (int64_t t0 = 0; t0 < a.BT; t0 += t.tb) {
     const int64_t rows = std::min(t.tb, a.BT - t0);
-    if ((e = launch_dlogits_block(W, h + t0 * a.H, b, w.tok + t0, a.mu, rows, a.H, a.V, 0, g, t.ldt, st)) !=
-        hipSuccess)
-      return e;
-    MatArgs m{};
-    m.G = g;
-    m.ld = t.ldt;
-    m.g_rows = rows;
-    m.H = a.H;
-    m.hchunks = t.hchunks;
-    m.n_valid = w.n_valid;
-    m.mean = a.mean ? 1 : 0;
-    m.X = W;
-    m.nS = rows;
-    m.nX = a.V;
-    m.x_split = t.x_split;
-    m.nsplit = t.nsplit;
-    m.part = part;
-    set_filter(m, a, 0);
-    if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
+    // vocabulary blocks of vr rows: dlogits, then their grad_input GEMM adding into the
+    // partial sums of the earlier blocks (ranges of x_split rows, the first block's the most)
+    for (int64_t v0 = 0; v0 < a.V; v0 += t.vr) {
+      const int64_t cols = std::min(t.vr, a.V - v0);
+      if ((e = launch_dlogits_block(W + v0 * a.H, h + t0 * a.H, b != nullptr ? b + v0 : nullptr, w.tok + t0, a.mu,
+                                    rows, a.H, cols, v0, g, t.ldt, st)) != hipSuccess)
+        return e;
+      MatArgs m{};
+      m.G = g;
+      m.ld = t.ldt;
+      m.g_rows = rows;
+      m.H = a.H;
+      m.hchunks = t.hchunks;
+      m.n_valid = w.n_valid;
+      m.mean = a.mean ? 1 : 0;
+      m.X = W + v0 * a.H;
+      m.nS = rows;
+      m.nX = cols;
+      m.x_split = t.x_split;
+      m.nsplit = (int)((cols + t.x_split - 1) / t.x_split);
+      m.part = part;
+      m.part_add = v0 > 0 ? 1 : 0;
+      set_filter(m, a, 0);
+      if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
+    }
     if ((e = launch_mat_reduce(part, t.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + t0 * a.H, w.n_valid,
                                a.mean, st)) != hipSuccess)
       return e;
