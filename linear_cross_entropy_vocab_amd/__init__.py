@@ -85,7 +85,7 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     lce_fwd_bwd_chunked (the token-chunked composition; bf16 only).  grad_weight_fp32 (bf16
     inputs) makes grad_weight a float32 tensor (in the chunked composition it then holds the
     sum over the chunks directly);
-    method="auto" takes the chunked composition for bf16 with H > 1024, else the fused path.
+    method="auto" takes the chunked composition for bf16 with H > 3072, else the fused path.
     sort_vocab (with filter_eps > 0) orders the vocabulary by average logit before filtering.
     """
     if sort_vocab and not filter_eps > 0.0:
@@ -93,9 +93,10 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     if method not in ("fused", "chunked", "auto"):
         raise ValueError(f"method must be 'fused', 'chunked' or 'auto', not {method!r}")
     if method == "auto":
-        # the fused backward keeps a workgroup's rows and accumulators on chip only up to
-        # H = 1024; above that the chunked composition is several times faster
-        method = "chunked" if (hidden.dtype == torch.bfloat16 and hidden.shape[1] > 1024
+        # above H = 1024 the fused path's backward recomputes the logits twice more on stored
+        # dlogits blocks (10 BT V H flops against the composition's 6); measured, it is level
+        # with the composition at H = 2304 (with 5% of its memory) and 1.5x slower at H = 4096
+        method = "chunked" if (hidden.dtype == torch.bfloat16 and hidden.shape[1] > 3072
                                and filter_eps == 0.0 and events is None) else "fused"
     chunked = method == "chunked"
     if grad_weight_fp32 and hidden.dtype != torch.bfloat16:
