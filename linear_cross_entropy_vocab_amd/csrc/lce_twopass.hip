@@ -25,6 +25,10 @@ namespace lce {
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Compute units of the MI355X, for sizing blocks to whole rounds of workgroups (on another
+// device count only the efficiency of the choice changes).
+constexpr int64_t kPlanCUs = 256;
+
 TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   TwoPass t{};
   t.on = false;
@@ -34,11 +38,25 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   if (budget <= base + 4096) return t;
   const size_t avail = budget - base - 4096;  // (the 16 bytes of a grad_b placeholder, aligned)
   const int64_t vpad = round_up(V, 64);
-  // pass 1: as many vocabulary rows per block as fit, all tokens
+  // pass 1: vocabulary blocks with all tokens, at most as many rows as fit.  Each block's
+  // grad_W GEMM is vb/64 row tiles x hchunks workgroups of equal length, about one per compute
+  // unit at a time, so a grid just over a multiple of the device costs a whole extra round:
+  // of the sizes from half the fit to the fit (multiples of 64), the one whose blocks take the
+  // fewest rounds in all, the largest on a tie (fewest dlogits launches)
   if (BT > 0) {
-    const int64_t v_fit = (int64_t)(avail / ((size_t)BT * 2)) / 64 * 64;
+    const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)BT * 2)) / 64 * 64, vpad);
     if (v_fit < 64) return t;
-    t.vb = std::min<int64_t>(v_fit, vpad);
+    auto rounds = [&](int64_t rows) { return ((rows + 63) / 64 * t.hchunks + kPlanCUs - 1) / kPlanCUs; };
+    const int64_t step = std::max<int64_t>(64, round_up(v_fit / 2 / 4096, 64));
+    int64_t best_vb = v_fit, best_cost = -1;
+    for (int64_t vb = v_fit; vb >= 64 && 2 * vb >= v_fit; vb -= step) {
+      const int64_t cost = (V / vb) * rounds(vb) + (V % vb != 0 ? rounds(V % vb) : 0);
+      if (best_cost < 0 || cost < best_cost) {
+        best_vb = vb;
+        best_cost = cost;
+      }
+    }
+    t.vb = best_vb;
   } else {
     t.vb = vpad;
   }
