@@ -289,6 +289,49 @@ def test_row_pieces_equal_full_oracle():
                                full["grad_bias"][vocab], rtol=1e-11, atol=1e-15)
 
 
+def test_minus_inf_bias_equals_smaller_vocabulary():
+    """Entries whose bias is -inf contribute e^-inf = 0 to every LSE ("Cut Cross Entropy
+    visualized", "Forward Kernel": the accumulation starts from -inf): the problem reduces
+    exactly to the vocabulary without them, and their grad_W rows and grad_b entries are 0."""
+    h, W, b, y = _small(BT=41, V=70, ignore_frac=0.1)
+    masked = np.zeros(70, dtype=bool)
+    masked[[0, 1, 2, 33, 34, 69]] = True
+    keep = np.nonzero(~masked)[0]
+    # targets only on kept entries (a target on a masked entry has an infinite loss)
+    valid = y != -100
+    y = np.where(valid, keep[y % keep.size], y)
+    bm = b.copy()
+    bm[masked] = -np.inf
+    new_id = np.full(70, -1)
+    new_id[keep] = np.arange(keep.size)
+    yr = np.where(valid, new_id[np.where(valid, y, 0)], y)
+    for reduction, mu in (("mean", 0.0), ("sum", 1e-2)):
+        full = oracle.lce_oracle(h, W, bm, y, reduction=reduction, z_loss=mu)
+        red = oracle.lce_oracle(h, W[keep], b[keep], yr, reduction=reduction, z_loss=mu)
+        assert np.isfinite(full["loss"])
+        assert full["loss"] == pytest.approx(red["loss"], rel=1e-13)
+        np.testing.assert_allclose(full["lse"], red["lse"], rtol=1e-14)
+        np.testing.assert_allclose(full["grad_input"], red["grad_input"], rtol=1e-11, atol=1e-15)
+        np.testing.assert_allclose(full["grad_weight"][keep], red["grad_weight"], rtol=1e-11, atol=1e-15)
+        np.testing.assert_allclose(full["grad_bias"][keep], red["grad_bias"], rtol=1e-11, atol=1e-15)
+        assert np.all(full["grad_weight"][masked] == 0.0) and np.all(full["grad_bias"][masked] == 0.0)
+
+
+def test_ce_oracle_selected_rows_equal_full_call():
+    """ce_oracle's dlogit_rows branch (only the listed rows of dlogits, in that order) returns
+    exactly the full call's rows and the same sums."""
+    inp = make_ce(29, 301, dtype="f32", seed=5, ignore_frac=0.2)
+    rows = np.array([28, 0, 3, 3, 17])
+    for mu in (0.0, 1e-2):
+        full = oracle.ce_oracle(inp.logits, inp.targets, z_loss=mu, rows_per_chunk=4)
+        part = oracle.ce_oracle(inp.logits, inp.targets, z_loss=mu, dlogit_rows=rows)
+        assert part["dlogits"].shape == (rows.size, 301)
+        np.testing.assert_array_equal(part["dlogits"], full["dlogits"][rows])
+        assert part["ce_sum"] == full["ce_sum"] and part["z_sum"] == full["z_sum"]
+        assert part["n_valid"] == full["n_valid"]
+        np.testing.assert_array_equal(part["lse"], full["lse"])
+
+
 def test_target_out_of_range_raises():
     h, W, b, y = _small()
     y = y.copy()
