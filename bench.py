@@ -7,7 +7,10 @@ One step = one lce_fwd_bwd call (loss, grad_input, grad_W) on the headline LM-he
 workload BT=65535, H=1024, V=176245, bf16, mean reduction, no bias, 20% of the targets
 ignored; inputs are seeded synthetic data already resident in HBM.  Prints ONE JSON line:
 whole-job tokens/s, the dominant kernel's roofline position (per-kernel HIP events
-recorded by the library on the launch stream during the timed steps), the float64 CPU
+recorded by the library on the launch stream during the timed steps; algorithmic flops
+2 BT V H per GEMM of the method, and beside them the executed flops with the logits
+recomputed in each gradient kernel), the same fused step on the Gemma-like and Qwen-like
+workloads (under "configs"), the float64 CPU
 oracle timed on a bounded sample of the same workload, and the standalone
 cross-entropy kernel's HBM throughput on [8192, 128256] bf16 logits, and (under
 "filtered") the lossy gradient-filtering mode on the same workload: its step time, skipped
@@ -232,6 +235,81 @@ def bench_rows(lce, torch, h, W, b, y, steps, BT) -> dict:
             "mean_entropy": float(r["entropy"].mean().item())}
 
 
+def _stage_roofline(stage_ms, btvh, dom=None):
+    """Roofline position of the slowest stage: algorithmic flops (the method's 2 BT V H per
+    GEMM: logits, grad_input, grad_W) and executed flops (with the logits recomputed inside
+    each gradient stage) per launch over its mean event time, against dense bf16 peak."""
+    algo = {"fwd_lse": 2 * btvh, "bwd_dinput": 2 * btvh, "bwd_dweight": 2 * btvh}
+    execd = {"fwd_lse": 2 * btvh, "bwd_dinput": 4 * btvh, "bwd_dweight": 4 * btvh}
+    if dom is None:
+        dom = max(algo, key=lambda n: stage_ms[n])
+    a = algo[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    e = execd[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    return dom, {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": a / PEAK_BF16_TFLOPS, "kernel": dom, "algorithmic_flops_per_launch": algo[dom],
+                 "achieved_executed": e, "frac_executed": e / PEAK_BF16_TFLOPS,
+                 "executed_flops_per_launch": execd[dom]}
+
+
+def bench_config(lce, torch, name, steps, warmup, log) -> dict:
+    """The fused step (lce_fwd_bwd: loss and every gradient) on another named LM-head workload:
+    wall time per step, per-stage event times, the slowest stage's roofline position, and the
+    extra device memory of one call against the one-logits-chunk budget."""
+    from oracle import liger_chunk_plan
+    from workloads import CONFIGS, make_config
+    c = CONFIGS[name]
+    log(f"generating {name}")
+    inp = make_config(name)
+    dt = torch.bfloat16
+    h = torch.from_numpy(inp.hidden).to(dt).cuda()
+    W = torch.from_numpy(inp.weight).to(dt).cuda()
+    b = None if inp.bias is None else torch.from_numpy(inp.bias).to(dt).cuda()
+    y = torch.from_numpy(inp.targets).cuda()
+    del inp
+    kw = dict(reduction=c.reduction, z_loss=c.z_loss)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    r = lce.lce_fwd_bwd(h, W, b, y, **kw)
+    torch.cuda.synchronize()
+    out_bytes = sum(r[k].numel() * r[k].element_size() for k in ("loss", "grad_input", "grad_weight",
+                                                                  "grad_bias", "n_valid") if r[k] is not None)
+    peak_extra = torch.cuda.max_memory_allocated() - base - out_bytes
+    ws = r["workspace"]
+    out = {k: r[k] for k in ("loss", "grad_input", "grad_weight", "grad_bias", "n_valid") if r[k] is not None}
+    for _ in range(warmup):
+        lce.lce_fwd_bwd(h, W, b, y, out=out, workspace=ws, **kw)
+    hip = _hip()
+    n_st = len(lce.stage_names())
+    evs = [([_event(hip) for _ in range(n_st)], [_event(hip) for _ in range(n_st)]) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        lce.lce_fwd_bwd(h, W, b, y, out=out, workspace=ws, events=evs[k], **kw)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    names = lce.stage_names()
+    st = {n: float(np.mean([_elapsed(hip, e[0][i], e[1][i]) for e in evs])) for i, n in enumerate(names)}
+    for e in evs:
+        for x in e[0] + e[1]:
+            hip.hipEventDestroy(ctypes.c_void_p(x))
+    btvh = float(c.BT) * c.V * c.H
+    _, roof = _stage_roofline(st, btvh)
+    budget = liger_chunk_plan(c.BT, c.V, c.H)["chunk_bytes"]
+    res = {"workload": f"{name}: BT={c.BT}, H={c.H}, V={c.V}, bf16, {c.reduction}"
+                       + (", bias" if b is not None else "") + (f", z-loss {c.z_loss:g}" if c.z_loss else ""),
+           "ms_per_step": ms, "tokens_per_s": c.BT / (ms * 1e-3),
+           "tflops_useful": 6 * btvh / (ms * 1e-3) / 1e12, "tflops_executed": 10 * btvh / (ms * 1e-3) / 1e12,
+           "useful_frac": 6 * btvh / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "stage_ms": st, "roofline": roof, "n_valid": int(out["n_valid"].item()),
+           "loss": float(out["loss"].item()),
+           "extra_hbm_bytes": int(ws.numel()), "extra_hbm_torch_peak_bytes": int(peak_extra),
+           "extra_hbm_budget_bytes": int(budget)}
+    del h, W, b, y, r, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(inp, n_tokens: int) -> dict:
     """The float64 oracle (as it stands) on the first n_tokens rows of the same workload."""
     import oracle
@@ -329,6 +407,8 @@ def main():
     ap.add_argument("--filter-eps", type=float, default=FILTER_EPS)
     ap.add_argument("--no-chunked", action="store_true", help="skip the token-chunked composition leg")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row outputs leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the fused step on the Gemma-like and Qwen-like workloads")
     ap.add_argument("--compare-methods", action="store_true",
                     help="only time the fused path and the token-chunked composition on the three "
                          "LM-head workloads and print one JSON line per workload")
@@ -464,9 +544,9 @@ def main():
             hip.hipEventDestroy(ctypes.c_void_p(x))
 
     btvh = float(BT) * V * H
-    algo_flops = {"fwd_lse": 2 * btvh, "bwd_dinput": 4 * btvh, "bwd_dweight": 4 * btvh}
-    dom = max(algo_flops, key=lambda n: stage_ms[n])
-    achieved = algo_flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    dom, roof = _stage_roofline(stage_ms, btvh)
+    roof["traffic"] = measured_traffic(dom)
+    roof["mfma_busy_counter"] = _profile_value(MFMA_FILE, dom, "mfma_busy")
     executed = 10 * btvh / (ms_step * 1e-3) / 1e12
     useful = 6 * btvh / (ms_step * 1e-3) / 1e12
     n_valid = int(out["n_valid"].item())
@@ -488,13 +568,11 @@ def main():
         "config": {"workload": "headline LM head: BT=65535, H=1024, V=176245, bf16, mean, no bias",
                    "BT": BT, "H": H, "V": V, "reduction": c.reduction, "n_valid": n_valid,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom), "kernel": dom,
-                     "algorithmic_flops_per_launch": algo_flops[dom],
-                     "mfma_busy_counter": _profile_value(MFMA_FILE, dom, "mfma_busy")},
+        "roofline": roof,
         "tflops_executed": executed,
         "tflops_useful": useful,
         "mfma_util_executed": executed / PEAK_BF16_TFLOPS,
+        "useful_frac": useful / PEAK_BF16_TFLOPS,
         "stage_ms": stage_ms,
         "extra_hbm_bytes": ws_bytes,
         "extra_hbm_budget_bytes": 512 * V * 4,
@@ -502,6 +580,11 @@ def main():
         "loss": loss,
     }
     log(f"fused step {ms_step:.2f} ms")
+    if not args.no_configs:
+        res["configs"] = {}
+        for name in ("gemma_like", "qwen_like"):
+            res["configs"][name] = bench_config(lce, torch, name, min(args.steps, 10), min(args.warmup, 2), log)
+            log(f"{name}: fused step {res['configs'][name]['ms_per_step']:.2f} ms")
     if not args.no_chunked:
         log("token-chunked composition leg")
         res["chunked"] = bench_chunked(lce, torch, h, W, None, y, kw, out, args.steps, BT)

@@ -38,11 +38,79 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _need_gpu(*ts):
+    """Every tensor on one GPU and contiguous (the C ABI takes raw device pointers)."""
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("all tensors must be on the GPU (no CPU path exists)")
-        if t is not None and not t.is_contiguous():
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"all tensors must be on one device ({dev} and {t.device} given)")
+        if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _tensor(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    return t
+
+
+def _expect(t, name, shape, dtype):
+    """A caller-supplied tensor (input or out=) must have exactly this shape and dtype: the
+    library writes and reads through raw pointers, so a mismatch would reach out of bounds."""
+    if t is None:
+        return
+    _tensor(t, name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _expect_scalar(t, name, dtype):
+    if t is None:
+        return
+    _tensor(t, name)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold exactly one element, not {t.numel()}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _expect_workspace(ws):
+    if ws is None:
+        return
+    _tensor(ws, "workspace")
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
+
+
+def _check_problem(hidden, weight, bias, targets):
+    """[BT, H] hidden, [V, H] weight, [V] bias (or None) of one dtype, [BT] int64 targets."""
+    _tensor(hidden, "hidden")
+    _tensor(weight, "weight")
+    _tensor(targets, "targets")
+    if hidden.dim() != 2:
+        raise ValueError(f"hidden must be 2-D [BT, H], not of shape {tuple(hidden.shape)}")
+    BT, H = hidden.shape
+    if weight.dim() != 2 or weight.shape[1] != H:
+        raise ValueError(f"weight must be [V, {H}], not of shape {tuple(weight.shape)}")
+    V = weight.shape[0]
+    if bias is not None:
+        _tensor(bias, "bias")
+        if tuple(bias.shape) != (V,):
+            raise ValueError(f"bias must be [{V}], not of shape {tuple(bias.shape)}")
+    if tuple(targets.shape) != (BT,):
+        raise ValueError(f"targets must be [{BT}], not of shape {tuple(targets.shape)}")
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    if weight.dtype != hidden.dtype or (bias is not None and bias.dtype != hidden.dtype):
+        raise TypeError("hidden, weight and bias must share a dtype")
+    return BT, H, V
 
 
 def version() -> str:
@@ -99,23 +167,36 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
         method = "chunked" if (hidden.dtype == torch.bfloat16 and hidden.shape[1] > 3072
                                and filter_eps == 0.0 and events is None) else "fused"
     chunked = method == "chunked"
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'sum', not {reduction!r}")
+    BT, H, V = _check_problem(hidden, weight, bias, targets)
     if grad_weight_fp32 and hidden.dtype != torch.bfloat16:
         raise ValueError("grad_weight_fp32 applies to bf16 inputs")
     if chunked and (filter_eps > 0.0 or events is not None):
         raise ValueError("filter_eps and events are not supported with method='chunked'")
-    lib = load()
-    _need_gpu(hidden, weight, bias, targets)
-    BT, H = hidden.shape
-    V = weight.shape[0]
     dt = _dtype_code(hidden)
-    if weight.dtype != hidden.dtype or (bias is not None and bias.dtype != hidden.dtype):
-        raise TypeError("hidden, weight and bias must share a dtype")
-    if targets.dtype != torch.int64:
-        raise TypeError("targets must be int64")
     if grad_bias is None:
         grad_bias = bias is not None
-    dev = hidden.device
+    if grad_bias and bias is None:
+        raise ValueError("grad_bias needs a bias")
     o = dict(out or {})
+    _expect_scalar(o.get("loss"), "out['loss']", torch.float32)
+    _expect(o.get("grad_input") if grad_input else None, "out['grad_input']", (BT, H), hidden.dtype)
+    _expect(o.get("grad_weight") if grad_weight else None, "out['grad_weight']", (V, H),
+            torch.float32 if grad_weight_fp32 else weight.dtype)
+    _expect(o.get("grad_bias") if grad_bias else None, "out['grad_bias']", (V,), None if bias is None else bias.dtype)
+    _expect_scalar(o.get("n_valid"), "out['n_valid']", torch.int64)
+    _expect(o.get("lse") if return_lse else None, "out['lse']", (BT,), torch.float32)
+    _expect_workspace(workspace)
+    if filter_counts is not None:
+        _tensor(filter_counts, "filter_counts")
+        if filter_counts.dtype != torch.int64 or filter_counts.numel() < 4:
+            raise TypeError("filter_counts must be an int64 tensor of 4 elements")
+    _need_gpu(hidden, weight, bias, targets, *(o.get(k) for k in ("loss", "grad_input", "grad_weight",
+                                                                 "grad_bias", "n_valid", "lse")),
+              workspace, filter_counts)
+    lib = load()
+    dev = hidden.device
     loss = o.get("loss")
     if loss is None:
         loss = torch.empty((), dtype=torch.float32, device=dev)
@@ -139,8 +220,6 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
         flags |= _lib.FLAG_SORT_VOCAB
     if grad_weight_fp32:
         flags |= _lib.FLAG_GRAD_W_FP32
-        if gw is not None and gw.dtype != torch.float32:
-            raise TypeError("grad_weight must be float32 with grad_weight_fp32")
     ws_fn = lib.lce_fwd_bwd_chunked_workspace_bytes if chunked else lib.lce_fwd_bwd_workspace_bytes
     need = int(ws_fn(BT, H, V, dt, flags))
     if workspace is None or workspace.numel() < need:
@@ -154,10 +233,6 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     elif filter_eps > 0.0:
         if events is not None:
             raise ValueError("events are not supported with filter_eps")
-        if filter_counts is not None:
-            _need_gpu(filter_counts)
-            if filter_counts.dtype != torch.int64 or filter_counts.numel() < 4:
-                raise TypeError("filter_counts must be an int64 tensor of 4 elements")
         st = lib.lce_fwd_bwd_filtered(*args, float(filter_eps), _ptr(filter_counts))
     elif events is None:
         st = lib.lce_fwd_bwd(*args)
@@ -177,14 +252,10 @@ def rows_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype, grad_weigh
 
 
 def _rows_common(hidden, weight, bias, targets):
-    _need_gpu(hidden, weight, bias, targets)
-    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or (
-            bias is not None and bias.dtype != torch.bfloat16):
+    BT, H, V = _check_problem(hidden, weight, bias, targets)
+    if hidden.dtype != torch.bfloat16:
         raise TypeError("the per-row entry points take bf16 hidden, weight and bias")
-    if targets.dtype != torch.int64:
-        raise TypeError("targets must be int64")
-    BT, H = hidden.shape
-    return BT, H, weight.shape[0]
+    return BT, H, V
 
 
 def lce_rows_forward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
@@ -193,8 +264,10 @@ def lce_rows_forward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[
                      workspace: Optional[torch.Tensor] = None) -> dict:
     """lce_rows_forward: per-row LSE, target log-probability, softmax entropy and row loss
     (reduction 'none'), each only if named in `outputs`; also n_valid."""
-    lib = load()
     BT, H, V = _rows_common(hidden, weight, bias, targets)
+    _expect_workspace(workspace)
+    _need_gpu(hidden, weight, bias, targets, workspace)
+    lib = load()
     dev = hidden.device
     res = {k: (torch.empty(BT, dtype=torch.float32, device=dev) if k in outputs else None)
            for k in ("lse", "logprobs", "entropy", "row_loss")}
@@ -225,20 +298,24 @@ def lce_rows_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional
     (upstream gradients float32 [BT] on the device, or None for zeros).  `lse` and `entropy`,
     both or neither, are lce_rows_forward's outputs for the same inputs: with them the logits
     are not stored (each chunk's dlogits come from the GEMM accumulator)."""
-    lib = load()
     BT, H, V = _rows_common(hidden, weight, bias, targets)
     if (lse is None) != (entropy is None):
         raise ValueError("pass both lse and entropy, or neither")
     ups = []
     for g in (grad_row_loss, grad_logprobs, grad_entropy, lse, entropy):
         if g is not None:
-            _need_gpu(g)
+            _tensor(g, "per-row gradient")
             if g.dtype != torch.float32 or g.numel() != BT:
                 raise TypeError("per-row gradients and saved outputs must be float32 with BT elements")
             g = g.contiguous()
         ups.append(g)
     if grad_bias is None:
         grad_bias = bias is not None
+    if grad_bias and bias is None:
+        raise ValueError("grad_bias needs a bias")
+    _expect_workspace(workspace)
+    _need_gpu(hidden, weight, bias, targets, *ups, workspace)
+    lib = load()
     gi = torch.empty_like(hidden) if grad_input else None
     gw = torch.empty_like(weight, dtype=torch.float32 if grad_weight_fp32 else weight.dtype) if grad_weight else None
     gb = torch.empty_like(bias) if grad_bias else None
@@ -303,14 +380,24 @@ def lce_ce_with_grad_inplace(logits: torch.Tensor, targets: torch.Tensor, *, ign
     Returns device tensors (ce_sum, z_sum, n_valid); the mean loss is
     ce_sum / n_valid.clamp(min=1).
     """
-    lib = load()
-    _need_gpu(logits, targets)
+    _tensor(logits, "logits")
+    _tensor(targets, "targets")
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be 2-D [B, V], not of shape {tuple(logits.shape)}")
     B, V = logits.shape
+    if tuple(targets.shape) != (B,):
+        raise ValueError(f"targets must be [{B}], not of shape {tuple(targets.shape)}")
     dt = _dtype_code(logits)
     if targets.dtype != torch.int64:
         raise TypeError("targets must be int64")
-    dev = logits.device
     o = dict(out or {})
+    _expect_scalar(o.get("ce_sum"), "out['ce_sum']", torch.float32)
+    _expect_scalar(o.get("z_sum"), "out['z_sum']", torch.float32)
+    _expect_scalar(o.get("n_valid"), "out['n_valid']", torch.int64)
+    _expect_workspace(workspace)
+    _need_gpu(logits, targets, o.get("ce_sum"), o.get("z_sum"), o.get("n_valid"), workspace)
+    lib = load()
+    dev = logits.device
     ce = o.get("ce_sum")
     if ce is None:
         ce = torch.empty((), dtype=torch.float32, device=dev)
@@ -332,13 +419,21 @@ def lce_ce_with_grad_inplace(logits: torch.Tensor, targets: torch.Tensor, *, ign
 
 
 class _LinearCrossEntropy(torch.autograd.Function):
-    """Loss with gradients computed in the same fused call (the backward only rescales)."""
+    """Loss with gradients computed in the same fused call (the backward only rescales).
+
+    The gradients are those of the loss itself (upstream gradient 1), rounded once to the
+    input dtype by the library.  The backward multiplies them in place by the upstream
+    gradient g (each product formed in fp32, then rounded to the input dtype): exact for g = 1
+    (the usual case of a loss) and for powers of two; otherwise bf16 outputs carry a second
+    rounding (relative error up to 2^-8 more per element).  In place, so that the backward
+    allocates nothing beyond the gradients themselves; a second backward through the same
+    graph therefore raises (the saved gradients have been modified)."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss, reduction):
+    def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss, reduction, method):
         r = lce_fwd_bwd(hidden.contiguous(), weight.contiguous(),
                         None if bias is None else bias.contiguous(), targets.contiguous(),
-                        ignore_index=ignore_index, z_loss=z_loss, reduction=reduction, method="auto",
+                        ignore_index=ignore_index, z_loss=z_loss, reduction=reduction, method=method,
                         grad_input=ctx.needs_input_grad[0], grad_weight=ctx.needs_input_grad[1],
                         grad_bias=bias is not None and ctx.needs_input_grad[2])
         ctx.save_for_backward(r["grad_input"], r["grad_weight"], r["grad_bias"])
@@ -352,13 +447,19 @@ class _LinearCrossEntropy(torch.autograd.Function):
         def mul(t):
             if t is None or scale is None:
                 return t
-            return (t.to(torch.float32) * scale).to(t.dtype)
+            return t.mul_(scale)
 
-        return mul(gi), mul(gw), mul(gb), None, None, None, None
+        return mul(gi), mul(gw), mul(gb), None, None, None, None, None
 
 
 def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                          bias: Optional[torch.Tensor] = None, *, ignore_index: int = -100,
-                         z_loss: float = 0.0, reduction: str = "mean") -> torch.Tensor:
-    """loss = reduction over rows of CE(hidden @ weight.T + bias, targets) (+ z-loss), differentiable."""
-    return _LinearCrossEntropy.apply(hidden, weight, bias, targets, ignore_index, z_loss, reduction)
+                         z_loss: float = 0.0, reduction: str = "mean", method: str = "fused") -> torch.Tensor:
+    """loss = reduction over rows of CE(hidden @ weight.T + bias, targets) (+ z-loss), differentiable.
+
+    method="fused" (default) keeps the extra device memory within one logits chunk (the
+    workspace of lce_fwd_bwd_workspace_bytes); method="chunked" opts into the token-chunked
+    composition, which is faster at H = 4096 but needs several times that memory."""
+    if method not in ("fused", "chunked"):
+        raise ValueError(f"method must be 'fused' or 'chunked', not {method!r}")
+    return _LinearCrossEntropy.apply(hidden, weight, bias, targets, ignore_index, z_loss, reduction, method)

@@ -608,14 +608,9 @@ hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) 
   }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
   const int64_t n = w.nt * nt_t;
-  if (false)
-    hipLaunchKernelGGL(fwd_lse_kernel<bf16_t>, dim3((unsigned)n), dim3(kFwdThreads), 0, st,
-                       (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H,
-                       a.V, w.nt, nt_t, w.lse_part);
-  else
-    hipLaunchKernelGGL(fwd_lse_kernel<float>, dim3((unsigned)n), dim3(kFwdThreads), 0, st,
-                       (const float*)a.W, (const float*)a.hidden, (const float*)a.bias, a.BT, a.H, a.V,
-                       w.nt, nt_t, w.lse_part);
+  hipLaunchKernelGGL(fwd_lse_kernel<float>, dim3((unsigned)n), dim3(kFwdThreads), 0, st,
+                     (const float*)a.W, (const float*)a.hidden, (const float*)a.bias, a.BT, a.H, a.V,
+                     w.nt, nt_t, w.lse_part);
   return hipGetLastError();
 }
 
@@ -683,6 +678,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     float m = -INFINITY, s = 0.f;
     for (int64_t k = 0; k < nt; ++k) {
       const float p = part[k * BT + t];
+      // a vocabulary tile with no finite logit (every entry masked by a -inf bias) holds
+      // -inf and adds e^-inf = 0: skipped, so that -inf - -inf never occurs
+      if (p == -INFINITY) continue;
       if (p > m) {
         s = s * __expf(m - p) + 1.f;
         m = p;

@@ -1,0 +1,49 @@
+"""Extra device memory of the default training path at full size: the autograd wrapper
+(linear_cross_entropy, forward and backward) must stay within one logits chunk beyond its
+inputs and gradient outputs, the budget of "Fused Linear Cross-Entropy: The Math, the Memory
+Wall, and Two Ways Around It", "The chunk-size trick" / "Memory profile" (Liger's fp32 chunk
+of next_pow2(ceil(BT / ceil(V / H))) rows: 360,949,760 bytes at BT = 65535, V = 176245).
+Measured with the torch allocator's peak around the call; the loss is checked against the
+oracle's stored value so that the measured call is the real one."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import linear_cross_entropy_vocab_amd as lce
+from oracle import liger_chunk_plan
+from workloads import CONFIGS, make_config
+from gpu_util import TOL, dev, rel
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("name", ["headline", "gemma_like", "qwen_like"])
+def test_autograd_extra_memory_within_one_logits_chunk(name):
+    c = CONFIGS[name]
+    print(f"extra device memory, autograd path: {name} BT={c.BT} H={c.H} V={c.V}", flush=True)
+    exp = np.load(os.path.join(HERE, "expected", f"{name}.npz"), allow_pickle=False)
+    inp = make_config(name)
+    h = dev(inp.hidden, c.dtype).requires_grad_(True)
+    W = dev(inp.weight, c.dtype).requires_grad_(True)
+    b = None if inp.bias is None else dev(inp.bias, c.dtype).requires_grad_(True)
+    y = dev(inp.targets)
+    del inp
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    loss = lce.linear_cross_entropy(h, W, y, b, z_loss=c.z_loss, reduction=c.reduction)
+    loss.backward()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    grads = sum(t.grad.numel() * t.grad.element_size() for t in (h, W, b) if t is not None)
+    extra = peak - grads - 64 * 1024  # (loss, n_valid and other scalars: allocator blocks)
+    budget = liger_chunk_plan(c.BT, c.V, c.H)["chunk_bytes"]
+    print(f"  peak delta {peak} B, gradients {grads} B, extra {extra} B, budget {budget} B", flush=True)
+    assert extra <= budget, (extra, budget)
+    assert extra <= lce.fwd_bwd_workspace_bytes(c.BT, c.H, c.V, torch.bfloat16)
+    assert rel(loss.item(), float(exp["loss"])) <= TOL[c.dtype]["loss"]
+    assert torch.isfinite(W.grad.float().norm())

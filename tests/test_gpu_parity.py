@@ -101,6 +101,41 @@ def test_all_ignored_and_empty():
     assert torch.count_nonzero(r["grad_weight"]) == 0  # fully overwritten with zeros
 
 
+MASK_CASES = [
+    # (dtype, BT, H, V, masked vocabulary ranges, z_loss, method): whole 256-entry vocabulary
+    # tiles of the forward (the first one, a middle one, the ragged last one) with bias -inf
+    ("bf16", 300, 256, 1500, ((0, 256), (512, 768)), 1e-3, "fused"),
+    ("f32", 150, 128, 1300, ((0, 256), (768, 1024), (1280, 1300)), 0.0, "fused"),
+    ("bf16", 600, 1152, 9000, ((0, 256), (4096, 4352)), 1e-4, "fused"),   # two-pass backward
+    ("bf16", 300, 256, 1500, ((0, 256), (1280, 1500)), 0.0, "chunked"),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[6]}" for c in MASK_CASES])
+def test_minus_inf_bias_tiles_vs_oracle(case):
+    """Vocabulary entries masked with a -inf bias contribute e^-inf = 0 ("Cut Cross Entropy
+    visualized", "Forward Kernel": the LSE accumulation starts from -inf), also when a whole
+    vocabulary tile of the forward is masked (its partial LSE is -inf and the merge skips it)."""
+    dt, BT, H, V, ranges, mu, method = case
+    print(f"masked-vocabulary case {case}", flush=True)
+    inp = make_fused(BT, H, V, dtype=dt, seed=BT + V, bias_std=0.1, ignore_frac=0.1, z_loss=mu)
+    masked = np.zeros(V, dtype=bool)
+    for a, b in ranges:
+        masked[a:b] = True
+    keep = np.nonzero(~masked)[0]
+    valid = inp.targets != -100
+    inp.targets[:] = np.where(valid, keep[np.where(valid, inp.targets, 0) % keep.size], inp.targets)
+    inp.bias[masked] = -np.inf
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=mu)
+    assert np.isfinite(ref["loss"])
+    r = run_fused(inp, method=method)
+    lse_tol = 2.0 ** -8 if method == "chunked" else None  # (bf16 logits chunk)
+    check_fused(inp, r, ref, lse_tol=lse_tol)
+    for k in ("grad_weight", "grad_bias"):
+        g = r[k][torch.from_numpy(masked).cuda()]
+        assert int(torch.count_nonzero(g)) == 0, k
+
+
 @pytest.mark.parametrize("shape", [(120, 256, 900), (600, 1152, 9000)], ids=["pipelined", "two-pass"])
 def test_grad_subsets(shape):
     BT, H, V = shape
