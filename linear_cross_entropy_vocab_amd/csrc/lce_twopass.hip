@@ -35,8 +35,12 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   mat_plan(H, &t.nb, &t.hchunks);
   const size_t budget = logits_chunk_budget(BT, H, V);
   const size_t base = fused_base_bytes(BT, V);
-  if (budget <= base + 4096) return t;
-  const size_t avail = budget - base - 4096;  // (the 16 bytes of a grad_b placeholder, aligned)
+  // 2 MiB of the budget are left to the caller's allocator: a caching allocator that rounds a
+  // large block up to a multiple of 2 MiB (PyTorch's does) then still holds no more than the
+  // budget for the workspace
+  constexpr size_t kAllocSlack = (size_t)2 << 20;
+  if (budget <= base + 4096 + kAllocSlack) return t;
+  const size_t avail = budget - base - 4096 - kAllocSlack;  // (4096: a grad_b placeholder, aligned)
   const int64_t vpad = round_up(V, 64);
   // pass 1: vocabulary blocks with all tokens, at most as many rows as fit.  Each block's
   // grad_W GEMM is vb/64 row tiles x hchunks workgroups of equal length, about one per compute

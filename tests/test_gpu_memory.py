@@ -38,12 +38,15 @@ def test_autograd_extra_memory_within_one_logits_chunk(name):
     loss = lce.linear_cross_entropy(h, W, y, b, z_loss=c.z_loss, reduction=c.reduction)
     loss.backward()
     torch.cuda.synchronize()
-    peak = torch.cuda.max_memory_allocated() - base
-    grads = sum(t.grad.numel() * t.grad.element_size() for t in (h, W, b) if t is not None)
-    extra = peak - grads - 64 * 1024  # (loss, n_valid and other scalars: allocator blocks)
+    peak = torch.cuda.max_memory_allocated()
+    # what is left after the backward is the gradients (and the loss): the rest of the peak
+    # was transient, the extra memory of the op, as the allocator holds it (large blocks
+    # rounded up to 2 MiB)
+    extra = peak - torch.cuda.memory_allocated()
     budget = liger_chunk_plan(c.BT, c.V, c.H)["chunk_bytes"]
-    print(f"  peak delta {peak} B, gradients {grads} B, extra {extra} B, budget {budget} B", flush=True)
+    ws = lce.fwd_bwd_workspace_bytes(c.BT, c.H, c.V, torch.bfloat16)
+    print(f"  peak delta {peak - base} B, extra {extra} B, workspace {ws} B, budget {budget} B", flush=True)
     assert extra <= budget, (extra, budget)
-    assert extra <= lce.fwd_bwd_workspace_bytes(c.BT, c.H, c.V, torch.bfloat16)
+    assert extra <= ws + (2 << 20), (extra, ws)
     assert rel(loss.item(), float(exp["loss"])) <= TOL[c.dtype]["loss"]
     assert torch.isfinite(W.grad.float().norm())
