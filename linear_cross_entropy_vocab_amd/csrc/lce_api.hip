@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/lce.h: argument validation (before any HIP
 // call), workspace sizing and carving, and the launch sequence on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -9,19 +10,24 @@
 
 namespace lce {
 
-// The forward's pieces (also what the pipelined and column-chunked backward kernels use).
-size_t fused_base_bytes(int64_t BT, int64_t V) {
+// The forward's pieces (also what the pipelined and column-chunked backward kernels use):
+// the small per-token pieces first, then the per-tile LSE partials, which the merge consumes
+// before any backward kernel runs (the two-pass backward reuses their memory).
+size_t fused_small_bytes(int64_t BT, int64_t V) {
   const int64_t bt = BT > 0 ? BT : 1;
-  const int64_t nt = (V + kFwdTileV - 1) / kFwdTileV;
   const int64_t nblk = (bt + kMergeThreads - 1) / kMergeThreads;
   size_t n = ws_align(16);                         // n_valid, n_bad
-  n += ws_align((size_t)nt * (size_t)bt * 4);      // lse_part
   n += ws_align((size_t)bt * 4);                   // lse
   n += ws_align((size_t)bt * 4);                   // zy
   n += ws_align((size_t)nblk * 2 * 8);             // block sums
   n += ws_align((size_t)bt * 8);                   // per-token (LSE, target) for the backward
   n += ws_align((size_t)V * 4);                    // fp32 bias for the backward
   return n;
+}
+size_t fused_base_bytes(int64_t BT, int64_t V) {
+  const int64_t bt = BT > 0 ? BT : 1;
+  const int64_t nt = (V + kFwdTileV - 1) / kFwdTileV;
+  return fused_small_bytes(BT, V) + ws_align((size_t)nt * (size_t)bt * 4);  // + lse_part
 }
 
 size_t logits_chunk_budget(int64_t BT, int64_t H, int64_t V) {
@@ -35,8 +41,10 @@ size_t logits_chunk_budget(int64_t BT, int64_t H, int64_t V) {
 size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
   size_t n = fused_base_bytes(BT, V);
   if (bf16 && H > 1024) {
+    // the two-pass region starts where the LSE partials do
     const TwoPass tp = twopass_plan(BT, H, V);
-    if (tp.on) n += tp.bytes;
+    const SgPlan sp = sg_plan(BT, H, V);
+    n = std::max(n, fused_small_bytes(BT, V) + std::max(tp.on ? tp.bytes : (size_t)0, sp.on ? sp.bytes : (size_t)0));
   }
   return n;
 }
@@ -51,8 +59,6 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   w.n_valid = reinterpret_cast<int64_t*>(p);
   w.n_bad = reinterpret_cast<int32_t*>(p + 8);
   p += ws_align(16);
-  w.lse_part = reinterpret_cast<float*>(p);
-  p += ws_align((size_t)w.nt * (size_t)bt * 4);
   w.lse = reinterpret_cast<float*>(p);
   p += ws_align((size_t)bt * 4);
   w.zy = reinterpret_cast<float*>(p);
@@ -62,8 +68,10 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   w.tok = reinterpret_cast<float2*>(p);
   p += ws_align((size_t)bt * 8);
   w.biasf = reinterpret_cast<float*>(p);
+  p += ws_align((size_t)V * 4);
+  w.lse_part = reinterpret_cast<float*>(p);  // (at fused_small_bytes)
   w.big = nullptr;
-  if (bf16 && H > 1024 && twopass_plan(BT, H, V).on) w.big = static_cast<char*>(ws) + fused_base_bytes(BT, V);
+  if (bf16 && H > 1024 && (twopass_plan(BT, H, V).on || sg_plan(BT, H, V).on)) w.big = p;
   return w;
 }
 

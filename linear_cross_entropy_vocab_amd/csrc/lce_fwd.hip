@@ -240,7 +240,10 @@ __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1
 // sum of row losses, target log-probabilities and entropies, p (alpha + beta z) - gamma [v = y],
 // from the fp32 accumulator and the per-token (-LSE log2 e, alpha, beta, gamma) of rtok[] and
 // target column (or -1) of rcy[].
-constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4;
+// MODE kEpiDlogitsT: the kEpiDlogits values written transposed, G^T[v][t] (vocabulary rows of
+// ld tokens; token columns BT..ld-1 are written as 0): the K-contiguous operand of the grad_W
+// product G^T . hidden.
+constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4, kEpiDlogitsT = 5;
 
 // (m, s, t) with s = sum e^(z - m), t = sum e^(z - m) z, merged with a second such triple
 __device__ __forceinline__ void mst_combine(float& m, float& s, float& t, float m2, float s2, float t2) {
@@ -268,7 +271,9 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
                                                                     const float4* __restrict__ rtok,
                                                                     const int32_t* __restrict__ rcy) {
   constexpr bool RD = MODE == kEpiRowsDlogits;
-  constexpr bool STORE = MODE == kEpiLogits || MODE == kEpiDlogits || RD;
+  constexpr bool DLT = MODE == kEpiDlogitsT;
+  constexpr bool DL = MODE == kEpiDlogits || DLT;
+  constexpr bool STORE = MODE == kEpiLogits || DL || RD;
   constexpr bool EZ = MODE == kEpiLseEz;
   constexpr int ROWB = 128;                       // bytes of one row per stage
   constexpr int TILE_A = kFwdTileV * ROWB;        // 32 KiB
@@ -278,7 +283,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   __shared__ float s_bias[kFwdTileV];
   __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
   __shared__ float red_t[EZ ? 2 : 1][EZ ? kFwdTileT2 : 1];
-  __shared__ float2 s_tok[MODE == kEpiDlogits ? kFwdTileT2 : 1];
+  __shared__ float2 s_tok[DL ? kFwdTileT2 : 1];
   __shared__ float4 s_rt[RD ? kFwdTileT2 : 1];
   __shared__ int32_t s_rcy[RD ? kFwdTileT2 : 1];
 
@@ -348,7 +353,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       const int64_t v = tl.v0 + tid;
       s_bias[tid] = v < V ? bf2f(bias[v]) : 0.f;
     }
-    if constexpr (MODE == kEpiDlogits) {  // the tile's tokens: (LSE, target + 1)
+    if constexpr (DL) {  // the tile's tokens: (LSE, target + 1)
       if (tid < kFwdTileT2) {
         const int64_t t = tl.t0 + tid;
         s_tok[tid] = t < BT ? tok[t] : make_float2(0.f, 0.f);
@@ -440,6 +445,51 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     // Row vrow + c exists iff c < lim; the checks are needed in the last vocabulary tile only
     // (a wave-uniform branch) and compare with small constants.
     const int lim = vlim - vrow;
+    if constexpr (DLT) {
+      // Lane (t, half) holds token t's dlogits for vocabulary rows vrow + vb 32 + 8 rr + e.
+      // Lanes t and t ^ 1 swap one value per pair of rows (e, e + 1), so that the even lane
+      // holds row e and the odd lane row e + 1, each for both tokens: one 4-byte store of two
+      // adjacent tokens per pair.  Rows past V fall outside the store descriptor.
+      const bool odd = (ln & 1) != 0;
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + tl.v0 * ld, (V - tl.v0) * ld * 2);
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int trow = wt * 64 + tb * 32 + (ln & 31);
+        const float2 tk = s_tok[trow];
+        const int yv = __float_as_int(tk.y) - 1;
+        const float ra = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
+        const float fac = 1.f + 2.f * mu * tk.x;
+        const int cy = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+        const int64_t col = tl.t0 + trow - (odd ? 1 : 0);
+        const bool col_ok = col < ld;
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const int c0 = vb * 32 + 8 * rr + e;
+              const float z0 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e], kLog2e, ra)), fac,
+                                    c0 == cy ? -1.f : 0.f);
+              const float z1 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e + 1], kLog2e, ra)), fac,
+                                    c0 + 1 == cy ? -1.f : 0.f);
+              const float send = odd ? z0 : z1;
+              // quad_perm (1, 0, 3, 2): the value of lane ln ^ 1
+              const float recv = __int_as_float(
+                  __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+              const uint32_t v = odd ? pack_bf2(recv, z1) : pack_bf2(z0, recv);
+              const int row = vrow + c0 + (odd ? 1 : 0);
+              const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * ld + col) * 2) : 0x80000000u;
+              __builtin_amdgcn_raw_buffer_store_b32(v, rz, (int)off, 0, 0);
+            }
+      }
+      (void)lse_part;
+      __syncthreads();  // every wave has read s_bias and s_tok before the next tile rewrites them
+      if (!has_next) break;
+      blk = nblk;
+      tl = tn;
+      continue;
+    }
     if constexpr (STORE) {
       const bool full = vlim == kFwdTileV;
       // Lane (t, half) holds, per 32-row block vb, vocabulary rows 8 rr + 4 half + 0..3 for
@@ -835,6 +885,22 @@ hipError_t launch_dlogits_block(const bf16_t* W_block, const bf16_t* h_block, co
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W_block, h_block, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok_block,
                      mu, vbase, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+// Transposed dlogits of the summed loss for the vocabulary rows vbase .. vbase + V - 1 (W_block,
+// bias_block) against all `rows` tokens: gout[v][t] in bf16, rows of ld >= rows tokens (columns
+// rows..ld-1 written as 0).
+hipError_t launch_dlogits_block_t(const bf16_t* W_block, const bf16_t* h, const bf16_t* bias_block,
+                                  const float2* tok, float mu, int64_t rows, int64_t H, int64_t V, int64_t vbase,
+                                  bf16_t* gout, int64_t ld, hipStream_t st) {
+  if (rows <= 0 || V <= 0) return hipSuccess;
+  if (V * ld * 2 > 0x7fffffffll) return hipErrorInvalidValue;
+  const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
+  const int64_t nt_t2 = (ld + kFwdTileT2 - 1) / kFwdTileT2;
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogitsT>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
+                     st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu, vbase,
+                     (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
   return hipGetLastError();
 }
 

@@ -27,12 +27,16 @@ struct FusedWs {
   float* biasf;       // [V] the bias in fp32 (written only when there is a bias)
   int64_t nt;         // number of vocab tiles
   int64_t nblk;       // number of merge blocks
-  char* big;          // the two-pass backward's buffers (bf16, H > 1024), or NULL
+  char* big;          // the two-pass backward's buffers (bf16, H > 1024; over lse_part), or NULL
 };
 constexpr int kMergeThreads = 256;
 
 size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16);
-size_t fused_base_bytes(int64_t BT, int64_t V);
+size_t fused_base_bytes(int64_t BT, int64_t V);   // small pieces + LSE partials
+size_t fused_small_bytes(int64_t BT, int64_t V);  // the pieces the backward reads
+// Of the one-chunk budget, what a caching allocator that rounds large blocks up to 2 MiB
+// (PyTorch's does) may add to a workspace block: 2 MiB for large budgets.
+inline size_t alloc_slack(size_t budget) { return budget / 64 < ((size_t)2 << 20) ? budget / 64 : ((size_t)2 << 20); }
 FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16);
 
 // Bytes of one fp32 logits chunk of the pages' chunk-size rule ("Fused Linear Cross-Entropy:
@@ -55,6 +59,18 @@ struct TwoPass {
   size_t g_bytes, part_bytes, bytes;
 };
 TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V);
+// The same two passes on the stored-operand GEMM (exact calls): pass 1 stores each vocabulary
+// block's dlogits transposed (vb rows of ldv tokens) and writes grad_W rows directly; pass 2
+// takes tb tokens x vr vocabulary rows per dlogits block and sums the GEMM's K-ranges of
+// ksplit rows in nsplit fp32 partial buffers.
+struct SgPlan {
+  bool on;
+  int64_t vb, ldv;
+  int64_t tb, vr, ldt, ksplit;
+  int nsplit;
+  size_t g_bytes, part_bytes, bytes;
+};
+SgPlan sg_plan(int64_t BT, int64_t H, int64_t V);
 
 
 struct FusedArgs {
@@ -147,6 +163,37 @@ hipError_t launch_rows_dlogits_chunk(const uint16_t* W, const uint16_t* h_chunk,
 hipError_t launch_dlogits_block(const uint16_t* W_block, const uint16_t* h_block, const uint16_t* bias_block,
                                 const float2* tok_block, float mu, int64_t rows, int64_t H, int64_t V,
                                 int64_t vbase, uint16_t* gout, int64_t ld, hipStream_t st);
+
+hipError_t launch_dlogits_block_t(const uint16_t* W_block, const uint16_t* h, const uint16_t* bias_block,
+                                  const float2* tok, float mu, int64_t rows, int64_t H, int64_t V, int64_t vbase,
+                                  uint16_t* gout, int64_t ld, hipStream_t st);
+
+// Stored-operand GEMM (bf16, fp32 accumulation): C = A . B over K split into ranges of ksplit
+// (a multiple of 64), one workgroup per (256 x 256 tile, range).  A [M][lda] is K-contiguous,
+// B [K][ldb] N-contiguous; N a multiple of 8, rows 16-byte aligned, elements of A past K up to
+// the next multiple of 8 zero.  With C: range s writes its fp32 partial sums to
+// C + s * split_stride ([M][ldc]), adding to what is there if accumulate; else (one range)
+// out = c * C in bf16 or fp32 (rows ldo apart), c = 1 / max(n_valid, 1) if mean, else 1.
+struct SgArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  int64_t M, N, K, ksplit;
+  int nsplit;
+  float* C;
+  int64_t ldc, split_stride;
+  int accumulate;
+  void* out;
+  int64_t ldo;
+  int out_f32;
+  const int64_t* n_valid;
+  int mean;
+};
+hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);
+// out[i] = c * sum_t g[i][t] over cols tokens (rows ld apart, bf16), one row per vocabulary entry.
+hipError_t launch_rowsum(const uint16_t* g, int64_t ld, int64_t rows, int64_t cols, uint16_t* out,
+                         const int64_t* n_valid, bool mean, hipStream_t st);
 
 // Token-chunked composition (bf16): chunk rows, padded row length of the logits chunk, and
 // the plan of the gradient GEMMs on it.

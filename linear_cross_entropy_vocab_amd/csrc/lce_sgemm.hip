@@ -1,0 +1,256 @@
+// Stored-operand GEMM on gfx950 for the gradient products of stored dlogits blocks
+// ("Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It", "From
+// dlogits to grad_input and grad_W": grad_input = dlogits . W, grad_W = dlogits^T . hidden).
+//
+//   C[m][n] = sum_k A[m][k] B[k][n]      A: [M][lda] bf16, K contiguous (a dlogits block, or
+//                                         its transpose)
+//                                         B: [K][ldb] bf16, N contiguous (W or hidden rows)
+// with fp32 accumulation, over K split into ranges of ksplit: every (256 x 256 tile, range)
+// is one workgroup, which either writes its fp32 partial sums (optionally adding to the
+// values already there) or, with a single range, the scaled result c * C in the output dtype.
+//
+// Workgroup: 8 waves (two per SIMD) in a 2 x 4 grid, each 128 x 64 of the tile on
+// v_mfma_f32_32x32x16_bf16.  K is staged 64 at a time into a double buffer by buffer->LDS
+// loads (8 per wave and stage):
+//  * A stage: 256 rows x 128 bytes, each row's 16-byte chunks XOR-swizzled by the row, read
+//    as 16-byte fragments (conflict free).
+//  * B stage: eight planes of 32 columns; plane p holds the 64 K-rows as rows of 64 bytes
+//    (sub-block j = K-rows 16 j .. 16 j + 15 in 1 KiB).  The B operand of a 32 x 32 x 16 step
+//    (K-rows 8 h .. 8 h + 7 of column c in lane 32 h + c) is two ds_read_b64_tr_b16 of that
+//    layout: a 16-lane group reads a 4-row x 32-byte block and receives it transposed.
+// The next stage's loads are issued right after the barrier that frees their buffer, so they
+// overlap the current stage's MFMAs.
+#include "lce_common.h"
+#include "lce_launch.h"
+
+namespace lce {
+
+constexpr int kSgThreads = 512;
+constexpr int kSgTile = 256;
+
+__device__ __forceinline__ int sg_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ bf16x8_t sg_tr_pair(const char* p0, const char* p1) {
+  const i16x4_t a = lds_read_tr16(reinterpret_cast<const bf16_t*>(p0));
+  const i16x4_t b = lds_read_tr16(reinterpret_cast<const bf16_t*>(p1));
+  return bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
+  constexpr int STAGE = kSgTile * 128;  // 32 KiB: A (256 rows x 64 K) or B (64 K x 256 columns)
+  __shared__ __attribute__((aligned(1024))) char sA[2][STAGE];
+  __shared__ __attribute__((aligned(1024))) char sB[2][STAGE];
+
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int wm = w >> 2, wn = w & 3;
+  // tile of this workgroup: consecutive logical ids stay on one XCD (xcd_remap); columns
+  // fastest, then rows, then K ranges, so that concurrent workgroups share A rows and B ranges
+  const uint32_t ntm = (uint32_t)((p.M + kSgTile - 1) / kSgTile), ntn = (uint32_t)((p.N + kSgTile - 1) / kSgTile);
+  const uint32_t total = ntm * ntn * (uint32_t)p.nsplit;
+  const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xcd_remap(blockIdx.x, total));
+  const uint32_t nt = id % ntn, rest = id / ntn;
+  const uint32_t mt = rest % ntm, split = rest / ntm;
+  const int64_t m0 = (int64_t)mt * kSgTile, n0 = (int64_t)nt * kSgTile;
+  const int64_t kb = (int64_t)split * p.ksplit;
+  const int64_t ke = (kb + p.ksplit) < p.K ? (kb + p.ksplit) : p.K;
+  const int nk = ke > kb ? (int)((ke - kb + 63) / 64) : 0;
+
+  // ---- loads of one stage: A rows 8 (4 w + j) + l / 8, physical chunk l % 8 holding logical
+  // chunk (l % 8) ^ swz(row); B plane w, sub-block j: K-row 16 j + l / 4, columns
+  // 32 w + 8 (l % 4) .. + 7.  Elements past M, N or the K range read as zero.
+  const int64_t mrows = (p.M - m0) < kSgTile ? (p.M - m0) : kSgTile;
+  const u32x4_t ra = make_rsrc_words(p.A + m0 * p.lda, mrows * p.lda * 2);
+  const u32x4_t rb = make_rsrc_words(p.B + kb * p.ldb, (p.K - kb) * p.ldb * 2);
+  int a_k[4];
+  uint32_t a_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * (4 * w + j) + (lane >> 3);
+    a_k[j] = 8 * ((lane & 7) ^ sg_swz(row));
+    a_off[j] = (uint32_t)(row * p.lda * 2 + (kb + a_k[j]) * 2);
+  }
+  const int64_t bcol = n0 + 32 * w + 8 * (lane & 3);
+  const bool bcol_ok = bcol < p.N;
+  const uint32_t b_off0 = (uint32_t)((lane >> 2) * p.ldb * 2 + bcol * 2);
+  const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)sA[0]));
+  const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)sB[0]));
+  const int64_t klen = ke - kb;
+  auto dma = [&](int ks, int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = 64 * ks + a_k[j] < klen;
+      dma16(ra, la + (uint32_t)(buf * STAGE + 1024 * (4 * w + j)), ok ? a_off[j] + 128u * ks : 0x80000000u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kr = 64 * ks + 16 * j + (lane >> 2);
+      const bool ok = bcol_ok && kr < klen;
+      dma16(rb, lb + (uint32_t)(buf * STAGE + 1024 * (4 * w + j)),
+            ok ? b_off0 + (uint32_t)((64 * ks + 16 * j) * p.ldb * 2) : 0x80000000u);
+    }
+  };
+
+  // ---- fragment addresses
+  const int fs = sg_swz(lane & 31);
+  const int g = lane >> 4, r4 = (lane >> 2) & 3, cc = lane & 3;
+  int o_b[2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) o_b[rd] = 64 * (8 * (g >> 1) + 4 * rd + r4) + 32 * (g & 1) + 8 * cc;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  int buf = 0;
+  if (nk > 0) dma(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    vm_wait<0>();     // this wave's loads of stage ks have landed
+    __syncthreads();  // every wave's have; nobody reads the other buffer any more
+    if (ks + 1 < nk) dma(ks + 1, buf ^ 1);
+    const char* a_base = sA[buf] + (wm * 128 + (lane & 31)) * 128;
+    const char* b_base = sB[buf] + (2 * wn) * 4096;
+    Frag<bf16_t> fa[2][4], fb[2][2];
+    auto rd = [&](int kk, int slot) {
+      const int off = ((2 * kk + (lane >> 5)) ^ fs) << 4;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) lds_frag_ptr(fa[slot][vb], a_base + vb * 32 * 128 + off);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const char* pb = b_base + nb * 4096 + kk * 1024;
+        fb[slot][nb].v = sg_tr_pair(pb + o_b[0], pb + o_b[1]);
+      }
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) mfma_32x32x16(fa[kk & 1][vb], fb[kk & 1][nb], acc[vb][nb]);
+    }
+    // the first step's eight fragment reads, then each step's eight MFMAs interleaved with the
+    // next step's reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    buf ^= 1;
+  }
+
+  // ---- epilogue: lane l holds column n0 + 64 wn + 32 nb + l % 32 of rows
+  // m0 + 128 wm + 32 vb + 8 (r / 4) + 4 (l / 32) + r % 4
+  const int64_t ncol = n0 + 64 * wn + (lane & 31);
+  const int mrow0 = 128 * wm + 4 * (lane >> 5);
+  if (p.C != nullptr) {
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(p.C + (int64_t)split * p.split_stride + m0 * p.ldc, mrows * p.ldc * 4);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const bool cok = ncol + 32 * nb < p.N;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        uint32_t off[16];
+        float old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mrow0 + 32 * vb + 8 * (r >> 2) + (r & 3);
+          off[r] = cok ? (uint32_t)((m * p.ldc + ncol + 32 * nb) * 4) : 0x80000000u;
+          old[r] = 0.f;
+        }
+        if (p.accumulate) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            old[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, (int)off[r], 0, 0));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[vb][nb][r] + old[r]), rc,
+                                                (int)off[r], 0, 0);
+      }
+    }
+  } else {
+    const long long nvalid = *p.n_valid;
+    const float cs = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+    const int es = p.out_f32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * es, mrows * p.ldo * es);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const bool cok = ncol + 32 * nb < p.N;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mrow0 + 32 * vb + 8 * (r >> 2) + (r & 3);
+          const uint32_t off = cok ? (uint32_t)((m * p.ldo + ncol + 32 * nb) * es) : 0x80000000u;
+          const float v = cs * acc[vb][nb][r];
+          if (p.out_f32)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, (int)off, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(v), ro, (int)off, 0, 0);
+        }
+    }
+  }
+  vm_wait<0>();
+}
+
+hipError_t launch_sgemm(const SgArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const int64_t ntm = (a.M + kSgTile - 1) / kSgTile, ntn = (a.N + kSgTile - 1) / kSgTile;
+  const int64_t total = ntm * ntn * a.nsplit;
+  if (a.nsplit < 1 || total > 0x7fffffff || a.ksplit % 64 != 0 || a.ksplit <= 0) return hipErrorInvalidValue;
+  // the kernel's 32-bit offsets: every descriptor it forms spans less than 2^31 bytes, so the
+  // offset 2^31 it uses for masked elements is out of range
+  if (kSgTile * a.lda * 2 >= 0x80000000ll || a.K * a.ldb * 2 >= 0x80000000ll) return hipErrorInvalidValue;
+  if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
+  if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sgemm_kernel, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// grad_b of a block of vocabulary rows from its transposed dlogits (rows ld elements apart,
+// cols tokens each): out[i] = c * sum_t G^T[i][t], one wave per row, fixed order.
+__global__ void __launch_bounds__(256) rowsum_kernel(const bf16_t* __restrict__ g, int64_t ld, int64_t rows,
+                                                     int64_t cols, bf16_t* __restrict__ out,
+                                                     const int64_t* __restrict__ n_valid, int mean) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const bf16_t* gr = g + row * ld;
+  float s = 0.f;
+  for (int64_t c = 8 * lane; c < cols; c += 8 * kWave) {
+    const uint4 v = *reinterpret_cast<const uint4*>(gr + c);  // (columns past cols hold 0)
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += __uint_as_float(u[e] << 16) + __uint_as_float(u[e] & 0xffff0000u);
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    const long long nv = *n_valid;
+    const float cs = mean ? 1.f / (float)(nv > 1 ? nv : 1) : 1.f;
+    out[row] = f2bf(cs * s);
+  }
+}
+
+hipError_t launch_rowsum(const bf16_t* g, int64_t ld, int64_t rows, int64_t cols, bf16_t* out,
+                         const int64_t* n_valid, bool mean, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, g, ld, rows, cols, out,
+                     n_valid, mean ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace lce

@@ -34,13 +34,13 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   t.on = false;
   mat_plan(H, &t.nb, &t.hchunks);
   const size_t budget = logits_chunk_budget(BT, H, V);
-  const size_t base = fused_base_bytes(BT, V);
-  // 2 MiB of the budget are left to the caller's allocator: a caching allocator that rounds a
-  // large block up to a multiple of 2 MiB (PyTorch's does) then still holds no more than the
-  // budget for the workspace
-  constexpr size_t kAllocSlack = (size_t)2 << 20;
-  if (budget <= base + 4096 + kAllocSlack) return t;
-  const size_t avail = budget - base - 4096 - kAllocSlack;  // (4096: a grad_b placeholder, aligned)
+  // the region overlaps the forward's LSE partials (consumed by the merge); part of the budget
+  // is left to the caller's allocator (alloc_slack), so that the workspace block it holds
+  // still fits
+  const size_t base = fused_small_bytes(BT, V);
+  const size_t slack = alloc_slack(budget);
+  if (budget <= base + 4096 + slack) return t;
+  const size_t avail = budget - base - 4096 - slack;  // (4096: a grad_b placeholder, aligned)
   const int64_t vpad = round_up(V, 64);
   // pass 1: vocabulary blocks with all tokens, at most as many rows as fit.  Each block's
   // grad_W GEMM is vb/64 row tiles x hchunks workgroups of equal length, about one per compute
@@ -145,7 +145,16 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   return t;
 }
 
-bool use_twopass(const FusedArgs& a) { return a.bf16 && a.H > 1024 && twopass_plan(a.BT, a.H, a.V).on; }
+hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+
+// Exact calls take the stored-operand GEMM plan; filtered and sorted calls (whose skip test
+// and row order live in the stored-dlogits GEMMs of lce_bwd.hip) the plan above.
+static bool exact_call(const FusedArgs& a) { return !(a.filter_eps > 0.f) && a.out_row_map == nullptr; }
+bool use_twopass(const FusedArgs& a) {
+  if (!a.bf16 || a.H <= 1024) return false;
+  return (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) || twopass_plan(a.BT, a.H, a.V).on;
+}
 
 // Gradient filtering ("Cut Cross Entropy visualized", "Gradient Filtering") in the stored-
 // dlogits GEMMs: their tiles are the fused kernels' (64 tokens x 16 vocabulary entries for
@@ -161,6 +170,7 @@ static void set_filter(MatArgs& m, const FusedArgs& a, int which) {
 // Region layout: [256 B: grad_b placeholder] then pass 1: [G (vb columns)], pass 2:
 // [G (all columns) | partial sums]
 hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return launch_sg_dinput(a, w, st);
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
@@ -204,6 +214,7 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
 }
 
 hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return launch_sg_dweight(a, w, st);
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   float* gb_flag = reinterpret_cast<float*>(w.big);  // never read or written (one pass per row)
@@ -246,6 +257,187 @@ hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStrea
     m.gb_out = a.grad_b != nullptr ? static_cast<bf16_t*>(a.grad_b) + o0 : nullptr;
     set_filter(m, a, 1);
     if ((e = launch_mat_gemm(true, m, st)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+
+// ---------------------------------------------------------------------------
+// The exact (unfiltered) call runs both passes on the stored-operand GEMM (lce_sgemm.hip):
+//   pass 1, per block of vb vocabulary rows: G^T = transposed dlogits of the block against all
+//     tokens (forward kernel, kEpiDlogitsT), grad_W[block] = c G^T . hidden straight into the
+//     output, grad_b[block] = c row sums of G^T;
+//   pass 2, per block of tb tokens and vocabulary block of vr rows: G = dlogits (kEpiDlogits),
+//     partial sums over K-ranges of ksplit vocabulary rows += G . W[vocabulary block]; then
+//     grad_input[token block] = c * the sum of the partial sums.
+// Block sizes come from a cost model in units of one 256 x 256 x 64 MFMA stage per compute
+// unit: a launch costs its rounds of workgroups over the device times the stages of one of its
+// tiles, plus a fixed launch cost; the dlogits kernel's tiles are 256 x 256 x H.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr double kLaunchStages = 4.0;   // launch and drain of one kernel
+constexpr double kDlFactor = 1.25;      // a dlogits tile stage against a GEMM stage (exp and stores)
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+double cost_dl(int64_t rows, int64_t cols, int64_t H) {
+  const int64_t tiles = cdiv(rows, 256) * cdiv(cols, 256);
+  return (double)cdiv(tiles, kPlanCUs) * (double)cdiv(H, 64) * kDlFactor + kLaunchStages;
+}
+double cost_gemm(int64_t M, int64_t N, int64_t K, int64_t ksplit) {
+  const int64_t ns = cdiv(K, ksplit);
+  const int64_t tiles = cdiv(M, 256) * cdiv(N, 256) * ns;
+  return (double)cdiv(tiles, kPlanCUs) * (double)cdiv(std::min(K, ksplit), 64) + kLaunchStages;
+}
+// streaming bytes at about 4 TB/s against a stage of about 1.4 us
+double cost_bytes(double bytes) { return bytes / 4e12 / 1.4e-6; }
+}  // namespace
+
+SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
+  SgPlan t{};
+  t.on = false;
+  if (BT <= 0 || V <= 0 || H <= 1024) return t;
+  const size_t budget = logits_chunk_budget(BT, H, V);
+  const size_t base = fused_small_bytes(BT, V);  // (as in twopass_plan)
+  const size_t slack = alloc_slack(budget);
+  if (budget <= base + 4096 + slack) return t;
+  const size_t avail = budget - base - 4096 - slack;
+  // hidden is the B operand of pass 1 (32-bit offsets)
+  if ((int64_t)BT * H * 2 >= 0x7fffffffll) return t;
+  // pass 1: evenly sized vocabulary blocks (multiples of 64 rows) whose G^T fits
+  t.ldv = round_up(BT, 64);
+  const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)t.ldv * 2)) / 64 * 64, round_up(V, 64));
+  if (v_fit < 64) return t;
+  double best1 = -1.0;
+  for (int64_t nb = cdiv(V, v_fit); nb <= cdiv(V, v_fit) + 8 && nb <= cdiv(V, 64); ++nb) {
+    const int64_t vb = std::min(round_up(cdiv(V, nb), 64), v_fit);
+    const int64_t n = cdiv(V, vb), last = V - (n - 1) * vb;
+    const double c1 = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_gemm(vb, H, BT, round_up(BT, 64))) +
+                      cost_dl(BT, last, H) + cost_gemm(last, H, BT, round_up(BT, 64)) +
+                      cost_bytes((double)V * t.ldv * 2);  // (grad_b row sums)
+    if (best1 < 0 || c1 < best1) {
+      best1 = c1;
+      t.vb = vb;
+    }
+  }
+  const size_t pass1 = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
+  // pass 2: token blocks tb, K-ranges of the partial sums, vocabulary blocks vr
+  double best2 = -1.0;
+  const int64_t bt_top = std::min<int64_t>(round_up(BT, 256), 8192);
+  for (int64_t tb0 = 256; tb0 <= bt_top; tb0 *= 2) {
+    const int64_t tb = std::min(tb0, BT);
+    const int64_t ntb = cdiv(BT, tb), tb_last = BT - (ntb - 1) * tb;
+    for (int64_t ns = 1; ns <= 64; ++ns) {
+      const size_t part = ws_align((size_t)ns * (size_t)tb * (size_t)H * 4);
+      if (part + 4096 >= avail) break;
+      const int64_t vr_fit = std::min<int64_t>((int64_t)((avail - part) / ((size_t)tb * 2)) / 256 * 256,
+                                               round_up(V, 256));
+      if (vr_fit < 256 || vr_fit * H * 2 >= 0x7fffffffll) continue;
+      for (int64_t nvb = cdiv(V, vr_fit); nvb <= cdiv(V, vr_fit) + 3; ++nvb) {
+        const int64_t vr = std::min(round_up(cdiv(V, nvb), 256), vr_fit);
+        const int64_t ksplit = round_up(cdiv(vr, ns), 64);
+        const int64_t n = cdiv(V, vr), last = V - (n - 1) * vr;
+        // (each vocabulary block after the first reads and writes the partial sums again)
+        auto block_cost = [&](int64_t rows) {
+          const double pbytes = (double)cdiv(vr, ksplit) * rows * H * 4;
+          return (double)(n - 1) * (cost_dl(rows, vr, H) + cost_gemm(rows, H, vr, ksplit)) +
+                 cost_dl(rows, last, H) + cost_gemm(rows, H, last, ksplit) +
+                 cost_bytes(pbytes * (2.0 * (double)n - 1.0) + pbytes + (double)rows * H * 2) + kLaunchStages;
+        };
+        const double c2 = (double)(ntb - 1) * block_cost(tb) + block_cost(tb_last);
+        if (best2 < 0 || c2 < best2) {
+          best2 = c2;
+          t.tb = tb;
+          t.vr = vr;
+          t.ksplit = ksplit;
+          t.nsplit = (int)cdiv(std::min(vr, V), ksplit);  // ranges of the first (largest) block
+        }
+      }
+    }
+  }
+  if (best2 < 0) return t;
+  t.ldt = round_up(t.vr, 64);
+  t.g_bytes = ws_align((size_t)t.tb * (size_t)t.ldt * 2);
+  t.part_bytes = ws_align((size_t)t.nsplit * (size_t)t.tb * (size_t)H * 4);
+  t.bytes = 256 + std::max(pass1, t.g_bytes + t.part_bytes);
+  if (t.bytes > avail + 4096) return t;
+  t.on = true;
+  return t;
+}
+
+hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  const SgPlan t = sg_plan(a.BT, a.H, a.V);
+  if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
+  bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
+  float* part = reinterpret_cast<float*>(w.big + 256 + t.g_bytes);
+  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bf16_t* b = static_cast<const bf16_t*>(a.bias);
+  hipError_t e;
+  for (int64_t t0 = 0; t0 < a.BT; t0 += t.tb) {
+    const int64_t rows = std::min(t.tb, a.BT - t0);
+    for (int64_t v0 = 0; v0 < a.V; v0 += t.vr) {
+      const int64_t cols = std::min(t.vr, a.V - v0);
+      if ((e = launch_dlogits_block(W + v0 * a.H, h + t0 * a.H, b != nullptr ? b + v0 : nullptr, w.tok + t0, a.mu,
+                                    rows, a.H, cols, v0, g, t.ldt, st)) != hipSuccess)
+        return e;
+      SgArgs m{};
+      m.A = g;
+      m.lda = t.ldt;
+      m.B = W + v0 * a.H;
+      m.ldb = a.H;
+      m.M = rows;
+      m.N = a.H;
+      m.K = cols;
+      m.ksplit = t.ksplit;
+      m.nsplit = (int)((cols + t.ksplit - 1) / t.ksplit);
+      m.C = part;
+      m.ldc = a.H;
+      m.split_stride = rows * a.H;  // (the layout mat_reduce reads: [nsplit][rows][H])
+      m.accumulate = v0 > 0 ? 1 : 0;  // (a later block has at most the first block's ranges)
+      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+    }
+    if ((e = launch_mat_reduce(part, t.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + t0 * a.H, w.n_valid,
+                               a.mean, st)) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  const SgPlan t = sg_plan(a.BT, a.H, a.V);
+  if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
+  bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
+  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bf16_t* b = static_cast<const bf16_t*>(a.bias);
+  hipError_t e;
+  for (int64_t v0 = 0; v0 < a.V; v0 += t.vb) {
+    const int64_t rows = std::min(t.vb, a.V - v0);
+    if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows,
+                                    v0, g, t.ldv, st)) != hipSuccess)
+      return e;
+    if (a.grad_W != nullptr) {
+      SgArgs m{};
+      m.A = g;
+      m.lda = t.ldv;
+      m.B = h;
+      m.ldb = a.H;
+      m.M = rows;
+      m.N = a.H;
+      m.K = a.BT;
+      m.ksplit = round_up(a.BT, 64);
+      m.nsplit = 1;
+      m.out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
+                           : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
+      m.out_f32 = a.grad_w_f32 ? 1 : 0;
+      m.ldo = a.H;
+      m.n_valid = w.n_valid;
+      m.mean = a.mean ? 1 : 0;
+      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+    }
+    if (a.grad_b != nullptr &&
+        (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
+            hipSuccess)
+      return e;
   }
   return hipSuccess;
 }

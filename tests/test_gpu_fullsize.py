@@ -132,9 +132,12 @@ def test_rows_full_size_headline(saved):
 def test_filtered_tiny_eps_full_size(name):
     """Gradient filtering at full size (pipelined backward at the headline, the two-pass
     stored-dlogits backward at gemma_like): with eps below every |dlogit| no tile is skipped
-    and the filtered call reproduces the exact call bit for bit; with vocabulary sorting on
-    top, the loss and gradients (returned in the original vocabulary order) stay within the
-    bf16 tolerances of the exact call."""
+    and the filtered call reproduces the exact call (bit for bit at the headline, where both
+    run the same kernels; within the bf16 tolerances at gemma_like, where the exact call's
+    two-pass backward runs on the stored-operand GEMM and the filtered one on the
+    stored-dlogits GEMMs that test each tile); with vocabulary sorting on top, the loss and
+    gradients (returned in the original vocabulary order) stay within the bf16 tolerances of
+    the exact call."""
     c = CONFIGS[name]
     print(f"full-size filtering, tiny eps: {name} BT={c.BT} H={c.H} V={c.V}", flush=True)
     inp = make_config(name)
@@ -149,12 +152,18 @@ def test_filtered_tiny_eps_full_size(name):
     # every (64-row, 16-row) tile of both gradient passes tested once, none skipped
     assert cnt == [0, -(-c.BT // 64) * -(-c.V // 16), 0, -(-c.V // 64) * -(-c.BT // 16)], cnt
     keys = ["loss", "grad_input", "grad_weight"] + (["grad_bias"] if b is not None else [])
+    tol = TOL[c.dtype]
     for k in keys:
-        assert torch.equal(exact[k], filt[k]), k
+        if c.H <= 1024:
+            assert torch.equal(exact[k], filt[k]), k
+        elif k == "loss":
+            assert torch.equal(exact[k], filt[k]), k  # (the forward is shared)
+        else:
+            e = float((filt[k].float() - exact[k].float()).norm() / exact[k].float().norm())
+            assert e <= tol["grad"] / 4, (k, e)
     del filt
     srt = lce.lce_fwd_bwd(*args, filter_eps=1e-38, sort_vocab=True, **kw)
     torch.cuda.synchronize()
-    tol = TOL[c.dtype]
     assert int(srt["n_valid"].item()) == int(exact["n_valid"].item())
     assert rel(srt["loss"].item(), exact["loss"].item()) <= tol["loss"]
     for k in keys[1:]:
