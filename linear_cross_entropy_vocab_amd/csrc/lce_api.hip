@@ -40,9 +40,10 @@ size_t logits_chunk_budget(int64_t BT, int64_t H, int64_t V) {
 
 size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
   size_t n = fused_base_bytes(BT, V);
-  if (bf16 && H > 1024) {
+  if (bf16) {
     // the two-pass region starts where the LSE partials do
-    const TwoPass tp = twopass_plan(BT, H, V);
+    TwoPass tp{};
+    if (H > 1024) tp = twopass_plan(BT, H, V);
     const SgPlan sp = sg_plan(BT, H, V);
     n = std::max(n, fused_small_bytes(BT, V) + std::max(tp.on ? tp.bytes : (size_t)0, sp.on ? sp.bytes : (size_t)0));
   }
@@ -71,7 +72,7 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   p += ws_align((size_t)V * 4);
   w.lse_part = reinterpret_cast<float*>(p);  // (at fused_small_bytes)
   w.big = nullptr;
-  if (bf16 && H > 1024 && (twopass_plan(BT, H, V).on || sg_plan(BT, H, V).on)) w.big = p;
+  if (bf16 && ((H > 1024 && twopass_plan(BT, H, V).on) || sg_plan(BT, H, V).on)) w.big = p;
   return w;
 }
 

@@ -65,7 +65,9 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V);
 // ksplit rows in nsplit fp32 partial buffers.
 struct SgPlan {
   bool on;
-  int64_t vb, ldv;
+  int64_t vb, ldv, ksplit1;  // pass 1 (ksplit1 < tokens: K-ranges summed in fp32 partial buffers)
+  int nsplit1;
+  size_t g1_bytes, part1_bytes;
   int64_t tb, vr, ldt, ksplit;
   int nsplit;
   size_t g_bytes, part_bytes, bytes;
@@ -191,6 +193,9 @@ struct SgArgs {
   int mean;
 };
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);
+// out[i] = c * sum_s part[s * stride + i] for i < n (n a multiple of 4), in bf16 or fp32.
+hipError_t launch_sg_reduce(const float* part, int nsplit, int64_t n, int64_t stride, void* out, bool out_f32,
+                            const int64_t* n_valid, bool mean, hipStream_t st);
 // out[i] = c * sum_t g[i][t] over cols tokens (rows ld apart, bf16), one row per vocabulary entry.
 hipError_t launch_rowsum(const uint16_t* g, int64_t ld, int64_t rows, int64_t cols, uint16_t* out,
                          const int64_t* n_valid, bool mean, hipStream_t st);

@@ -221,6 +221,42 @@ hipError_t launch_sgemm(const SgArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// out = c * sum over nsplit partial buffers ([nsplit][n] fp32, `stride` floats apart), in bf16
+// or fp32; c = 1 / max(n_valid, 1) if mean, else 1.  n a multiple of 4.
+__global__ void __launch_bounds__(256) sg_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t n,
+                                                        int64_t stride, void* __restrict__ out, int out_f32,
+                                                        const int64_t* __restrict__ n_valid, int mean) {
+  const long long nvalid = *n_valid;
+  const float cs = mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n;
+       i += (int64_t)gridDim.x * blockDim.x * 4) {
+    float4 a = *reinterpret_cast<const float4*>(part + i);
+    for (int s = 1; s < nsplit; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(part + s * stride + i);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    if (out_f32)
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = make_float4(cs * a.x, cs * a.y, cs * a.z, cs * a.w);
+    else
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + i) =
+          make_uint2(pack_bf2(cs * a.x, cs * a.y), pack_bf2(cs * a.z, cs * a.w));
+  }
+}
+
+hipError_t launch_sg_reduce(const float* part, int nsplit, int64_t n, int64_t stride, void* out, bool out_f32,
+                            const int64_t* n_valid, bool mean, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(sg_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, nsplit, n, stride, out,
+                     out_f32 ? 1 : 0, n_valid, mean ? 1 : 0);
+  return hipGetLastError();
+}
+
 // grad_b of a block of vocabulary rows from its transposed dlogits (rows ld elements apart,
 // cols tokens each): out[i] = c * sum_t G^T[i][t], one wave per row, fixed order.
 __global__ void __launch_bounds__(256) rowsum_kernel(const bf16_t* __restrict__ g, int64_t ld, int64_t rows,

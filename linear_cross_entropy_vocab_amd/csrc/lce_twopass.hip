@@ -152,8 +152,9 @@ hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t s
 // and row order live in the stored-dlogits GEMMs of lce_bwd.hip) the plan above.
 static bool exact_call(const FusedArgs& a) { return !(a.filter_eps > 0.f) && a.out_row_map == nullptr; }
 bool use_twopass(const FusedArgs& a) {
-  if (!a.bf16 || a.H <= 1024) return false;
-  return (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) || twopass_plan(a.BT, a.H, a.V).on;
+  if (!a.bf16) return false;
+  if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return true;
+  return a.H > 1024 && twopass_plan(a.BT, a.H, a.V).on;
 }
 
 // Gradient filtering ("Cut Cross Entropy visualized", "Gradient Filtering") in the stored-
@@ -275,6 +276,7 @@ hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStrea
 // tiles, plus a fixed launch cost; the dlogits kernel's tiles are 256 x 256 x H.
 // ---------------------------------------------------------------------------
 namespace {
+constexpr int64_t kSgMinH = 1025;       // below: the pipelined kernels (measured faster at H = 1024)
 constexpr double kLaunchStages = 4.0;   // launch and drain of one kernel
 constexpr double kDlFactor = 1.25;      // a dlogits tile stage against a GEMM stage (exp and stores)
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -294,7 +296,7 @@ double cost_bytes(double bytes) { return bytes / 4e12 / 1.4e-6; }
 SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
   SgPlan t{};
   t.on = false;
-  if (BT <= 0 || V <= 0 || H <= 1024) return t;
+  if (BT <= 0 || V <= 0 || H < kSgMinH) return t;
   const size_t budget = logits_chunk_budget(BT, H, V);
   const size_t base = fused_small_bytes(BT, V);  // (as in twopass_plan)
   const size_t slack = alloc_slack(budget);
@@ -306,19 +308,33 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
   t.ldv = round_up(BT, 64);
   const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)t.ldv * 2)) / 64 * 64, round_up(V, 64));
   if (v_fit < 64) return t;
+  // (with ns1 > 1 the tokens are split into K-ranges whose fp32 partial sums are reduced into
+  // the grad_W rows of the block: more workgroups per block when H gives few column tiles)
   double best1 = -1.0;
-  for (int64_t nb = cdiv(V, v_fit); nb <= cdiv(V, v_fit) + 8 && nb <= cdiv(V, 64); ++nb) {
-    const int64_t vb = std::min(round_up(cdiv(V, nb), 64), v_fit);
-    const int64_t n = cdiv(V, vb), last = V - (n - 1) * vb;
-    const double c1 = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_gemm(vb, H, BT, round_up(BT, 64))) +
-                      cost_dl(BT, last, H) + cost_gemm(last, H, BT, round_up(BT, 64)) +
-                      cost_bytes((double)V * t.ldv * 2);  // (grad_b row sums)
-    if (best1 < 0 || c1 < best1) {
-      best1 = c1;
-      t.vb = vb;
+  for (int64_t ns1 = 1; ns1 <= 16; ++ns1) {
+    const int64_t ks1 = round_up(cdiv(BT, ns1), 64);
+    if (ns1 > 1 && cdiv(BT, ks1) != ns1) continue;
+    const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0);
+    const int64_t fit = std::min<int64_t>((int64_t)(avail / per_row) / 64 * 64, round_up(V, 64));
+    if (fit < 64) continue;
+    for (int64_t nb = cdiv(V, fit); nb <= cdiv(V, fit) + 8 && nb <= cdiv(V, 64); ++nb) {
+      const int64_t vb = std::min(round_up(cdiv(V, nb), 64), fit);
+      const int64_t n = cdiv(V, vb), last = V - (n - 1) * vb;
+      const double red = ns1 > 1 ? cost_bytes((double)V * H * (4.0 * ns1 + 4.0)) + (double)n * kLaunchStages : 0.0;
+      const double c1 = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_gemm(vb, H, BT, ks1)) + cost_dl(BT, last, H) +
+                        cost_gemm(last, H, BT, ks1) + cost_bytes((double)V * t.ldv * 2) + red;
+      if (best1 < 0 || c1 < best1) {
+        best1 = c1;
+        t.vb = vb;
+        t.nsplit1 = (int)ns1;
+        t.ksplit1 = ks1;
+      }
     }
   }
-  const size_t pass1 = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
+  if (best1 < 0) return t;
+  t.g1_bytes = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
+  t.part1_bytes = t.nsplit1 > 1 ? ws_align((size_t)t.nsplit1 * (size_t)t.vb * (size_t)H * 4) : 0;
+  const size_t pass1 = t.g1_bytes + t.part1_bytes;
   // pass 2: token blocks tb, K-ranges of the partial sums, vocabulary blocks vr
   double best2 = -1.0;
   const int64_t bt_top = std::min<int64_t>(round_up(BT, 256), 8192);
@@ -406,6 +422,7 @@ hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t s
   const SgPlan t = sg_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
+  float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
   const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bf16_t* b = static_cast<const bf16_t*>(a.bias);
@@ -416,6 +433,8 @@ hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t s
                                     v0, g, t.ldv, st)) != hipSuccess)
       return e;
     if (a.grad_W != nullptr) {
+      void* out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
+                               : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
       SgArgs m{};
       m.A = g;
       m.lda = t.ldv;
@@ -424,15 +443,24 @@ hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t s
       m.M = rows;
       m.N = a.H;
       m.K = a.BT;
-      m.ksplit = round_up(a.BT, 64);
-      m.nsplit = 1;
-      m.out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
-                           : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
-      m.out_f32 = a.grad_w_f32 ? 1 : 0;
-      m.ldo = a.H;
+      m.ksplit = t.ksplit1;
+      m.nsplit = t.nsplit1;
       m.n_valid = w.n_valid;
       m.mean = a.mean ? 1 : 0;
-      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+      if (t.nsplit1 > 1) {  // K-ranges into partial sums, then c * their sum into the rows
+        m.C = part1;
+        m.ldc = a.H;
+        m.split_stride = rows * a.H;
+        if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+        if ((e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, out, a.grad_w_f32, w.n_valid, a.mean,
+                                  st)) != hipSuccess)
+          return e;
+      } else {
+        m.out = out;
+        m.out_f32 = a.grad_w_f32 ? 1 : 0;
+        m.ldo = a.H;
+        if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+      }
     }
     if (a.grad_b != nullptr &&
         (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
