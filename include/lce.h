@@ -44,7 +44,8 @@ typedef enum lce_status {
   LCE_ERR_WORKSPACE = 5,    /* workspace_bytes smaller than the *_workspace_bytes requirement */
   LCE_ERR_ARG = 6,          /* bad scalar argument (reduction, z_loss_mult < 0 or NaN, grad_b without bias) */
   LCE_ERR_TARGET_RANGE = 7, /* (check mode only) a target is neither ignore_index nor in [0, V) */
-  LCE_ERR_HIP = 8           /* a HIP runtime call or kernel launch failed */
+  LCE_ERR_HIP = 8,          /* a HIP runtime call or kernel launch failed */
+  LCE_ERR_SCRATCH_LIMIT = 9 /* (no-allocation entry point) the size exceeds its fixed scratch */
 } lce_status;
 
 typedef enum lce_dtype {
@@ -189,6 +190,24 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
                                     lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
                                     float* ce_sum_out, float* z_sum_out, int64_t* n_valid_out,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lce_ce_with_grad_inplace_noalloc -- lce_ce_with_grad_inplace for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation and results, with no workspace argument.  Its
+ * scratch (12 bytes per row) lives in a fixed device array of the library, 3 MiB on every GPU
+ * the library runs on, held until the process ends; the call allocates nothing.
+ *   B <= LCE_NOALLOC_MAX_ROWS, else LCE_ERR_SCRATCH_LIMIT (checked before any device work).
+ *   Other arguments and errors as lce_ce_with_grad_inplace.
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap in time on the
+ * same GPU (different streams or threads without ordering between them) race and must not
+ * be made.
+ */
+#define LCE_NOALLOC_MAX_ROWS 262144
+lce_status lce_ce_with_grad_inplace_noalloc(void* logits, const int64_t* targets, int64_t B, int64_t V,
+                                            lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
+                                            float* ce_sum_out, float* z_sum_out, int64_t* n_valid_out,
+                                            void* stream);
 
 /*
  * lce_fwd_bwd_chunked -- the same loss and gradients by the token-chunked composition

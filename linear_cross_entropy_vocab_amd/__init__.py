@@ -418,6 +418,47 @@ def lce_ce_with_grad_inplace(logits: torch.Tensor, targets: torch.Tensor, *, ign
     return ce, zs, nv
 
 
+def lce_ce_with_grad_inplace_noalloc(logits: torch.Tensor, targets: torch.Tensor, *, ignore_index: int = -100,
+                                     z_loss: float = 0.0, out: Optional[dict] = None):
+    """lce_ce_with_grad_inplace_noalloc: the standalone cross-entropy without a workspace (the
+    library's fixed per-GPU scratch, at most NOALLOC_MAX_ROWS rows).  The C call allocates
+    nothing; with `out` holding ce_sum, z_sum and n_valid, neither does this binding."""
+    _tensor(logits, "logits")
+    _tensor(targets, "targets")
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be 2-D [B, V], not of shape {tuple(logits.shape)}")
+    B, V = logits.shape
+    if tuple(targets.shape) != (B,):
+        raise ValueError(f"targets must be [{B}], not of shape {tuple(targets.shape)}")
+    dt = _dtype_code(logits)
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    o = dict(out or {})
+    _expect_scalar(o.get("ce_sum"), "out['ce_sum']", torch.float32)
+    _expect_scalar(o.get("z_sum"), "out['z_sum']", torch.float32)
+    _expect_scalar(o.get("n_valid"), "out['n_valid']", torch.int64)
+    _need_gpu(logits, targets, o.get("ce_sum"), o.get("z_sum"), o.get("n_valid"))
+    lib = load()
+    dev = logits.device
+    ce = o.get("ce_sum")
+    if ce is None:
+        ce = torch.empty((), dtype=torch.float32, device=dev)
+    zs = o.get("z_sum")
+    if zs is None:
+        zs = torch.empty((), dtype=torch.float32, device=dev)
+    nv = o.get("n_valid")
+    if nv is None:
+        nv = torch.empty((), dtype=torch.int64, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = lib.lce_ce_with_grad_inplace_noalloc(_ptr(logits), _ptr(targets), B, V, dt, ignore_index, float(z_loss),
+                                              _ptr(ce), _ptr(zs), _ptr(nv), stream)
+    _lib.check(st, "lce_ce_with_grad_inplace_noalloc")
+    return ce, zs, nv
+
+
+NOALLOC_MAX_ROWS = _lib.NOALLOC_MAX_ROWS
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
     """Loss with gradients computed in the same fused call (the backward only rescales).
 

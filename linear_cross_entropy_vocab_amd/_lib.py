@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(_HERE, "liblce.so")
 LCE_OK = 0
 STATUS_NAMES = {0: "LCE_OK", 1: "LCE_ERR_NULL", 2: "LCE_ERR_SHAPE", 3: "LCE_ERR_DTYPE",
                 4: "LCE_ERR_ALIGNMENT", 5: "LCE_ERR_WORKSPACE", 6: "LCE_ERR_ARG",
-                7: "LCE_ERR_TARGET_RANGE", 8: "LCE_ERR_HIP"}
+                7: "LCE_ERR_TARGET_RANGE", 8: "LCE_ERR_HIP", 9: "LCE_ERR_SCRATCH_LIMIT"}
+NOALLOC_MAX_ROWS = 262144
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_F16 = 2
@@ -26,7 +27,8 @@ EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_f
            "lce_fwd_bwd_chunked", "lce_fwd_bwd_chunked_workspace_bytes",
            "lce_rows_forward", "lce_rows_backward", "lce_rows_workspace_bytes",
            "lce_stage_name",
-           "lce_ce_with_grad_inplace", "lce_ce_workspace_bytes", "lce_status_string", "lce_version")
+           "lce_ce_with_grad_inplace", "lce_ce_with_grad_inplace_noalloc", "lce_ce_workspace_bytes",
+           "lce_status_string", "lce_version")
 
 _lib = None
 
@@ -71,6 +73,9 @@ def load() -> ctypes.CDLL:
     lib.lce_ce_with_grad_inplace.argtypes = [c_vp, c_vp, c_i64, c_i64, ctypes.c_int, c_i64, c_f, c_vp,
                                              c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
     lib.lce_ce_with_grad_inplace.restype = ctypes.c_int
+    lib.lce_ce_with_grad_inplace_noalloc.argtypes = [c_vp, c_vp, c_i64, c_i64, ctypes.c_int, c_i64, c_f, c_vp,
+                                                     c_vp, c_vp, c_vp]
+    lib.lce_ce_with_grad_inplace_noalloc.restype = ctypes.c_int
     lib.lce_ce_workspace_bytes.argtypes = [c_i64, c_i64, ctypes.c_int]
     lib.lce_ce_workspace_bytes.restype = ctypes.c_size_t
     lib.lce_status_string.argtypes = [ctypes.c_int]

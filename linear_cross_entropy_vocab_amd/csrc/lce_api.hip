@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "lce.h"
 #include "lce_launch.h"
@@ -408,6 +409,72 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
   return LCE_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch memory of lce_ce_with_grad_inplace_noalloc: the standalone cross-entropy's
+// workspace (per-row ce, z and valid flag) for up to LCE_NOALLOC_MAX_ROWS rows, in a
+// file-scope device array that each GPU holds from the library's load to the end of the
+// process.  In host code `scratch` only names the variable; its device address, different on
+// every GPU, comes from hipGetSymbolAddress once per device and is what the kernels receive.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kNoAllocScratchBytes = 3 * (size_t)LCE_NOALLOC_MAX_ROWS * 4;
+static_assert(kNoAllocScratchBytes >= 3 * 256, "scratch holds the three per-row arrays");
+}  // namespace
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+lce_status lce_ce_with_grad_inplace_noalloc(void* logits, const int64_t* targets, int64_t B, int64_t V,
+                                            lce_dtype dtype, int64_t ignore_index, float z_loss_mult,
+                                            float* ce_sum_out, float* z_sum_out, int64_t* n_valid_out,
+                                            void* stream) {
+  if (B < 0 || V < 1 || V > ((int64_t)1 << 31) - 2) return LCE_ERR_SHAPE;
+  if (B > LCE_NOALLOC_MAX_ROWS) return LCE_ERR_SCRATCH_LIMIT;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32 && dtype != LCE_DTYPE_F16) return LCE_ERR_DTYPE;
+  if (ce_sum_out == nullptr || z_sum_out == nullptr) return LCE_ERR_NULL;
+  if (B > 0 && (logits == nullptr || targets == nullptr)) return LCE_ERR_NULL;
+  if (!(z_loss_mult >= 0.f) || !std::isfinite(z_loss_mult)) return LCE_ERR_ARG;
+  if (!lce::aligned(logits, 16) || !lce::aligned(targets, 8) || !lce::aligned(ce_sum_out, 4) ||
+      !lce::aligned(z_sum_out, 4) || !lce::aligned(n_valid_out, 8))
+    return LCE_ERR_ALIGNMENT;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return LCE_ERR_HIP;
+  // (the per-row arrays are written for every row before the reduction reads them: nothing
+  // in the scratch needs clearing)
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ct = dtype == LCE_DTYPE_BF16 ? lce::kCeBf16 : (dtype == LCE_DTYPE_F16 ? lce::kCeF16 : lce::kCeF32);
+  if (lce::launch_ce_inplace(logits, ct, targets, B, V, V, ignore_index, z_loss_mult, ce_sum_out, z_sum_out,
+                             n_valid_out, nullptr, ws, st) != hipSuccess)
+    return LCE_ERR_HIP;
+  return LCE_OK;
+}
+
 const char* lce_status_string(lce_status s) {
   switch (s) {
     case LCE_OK: return "ok";
@@ -419,6 +486,7 @@ const char* lce_status_string(lce_status s) {
     case LCE_ERR_ARG: return "invalid argument";
     case LCE_ERR_TARGET_RANGE: return "a target is neither ignore_index nor in [0, V)";
     case LCE_ERR_HIP: return "HIP runtime error";
+    case LCE_ERR_SCRATCH_LIMIT: return "size beyond the no-allocation entry point's scratch (B > LCE_NOALLOC_MAX_ROWS)";
   }
   return "unknown status";
 }

@@ -36,7 +36,7 @@ def test_header_symbols_are_exported(lib):
 
 def test_version_and_strings(lib):
     assert b"gfx950" in lib.lce_version()
-    for code in range(9):
+    for code in range(10):
         assert lib.lce_status_string(code)
     names = [lib.lce_stage_name(k).decode() for k in range(_lib.NUM_STAGES)]
     assert names == ["targets", "fwd_lse", "target_logit", "merge", "loss", "bwd_dinput", "bwd_dweight"]
@@ -234,8 +234,8 @@ def test_ce_host_errors(lib, kw, status):
 
 
 def test_status_strings_are_distinct(lib):
-    s = {lib.lce_status_string(k) for k in range(9)}
-    assert len(s) == 9
+    s = {lib.lce_status_string(k) for k in range(10)}
+    assert len(s) == 10
 
 
 def test_python_binding_refuses_cpu_tensors():
@@ -256,3 +256,19 @@ def test_oracle_not_imported_by_product_package():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_noalloc_ce_host_errors(lib):
+    """The no-allocation cross-entropy checks its arguments on the host, before it looks up
+    its scratch or touches the device: rows beyond the scratch, bad shapes, dtypes, pointers."""
+    p = ctypes.c_void_p(1 << 20)  # well-formed fake device pointers: never dereferenced here
+    f = lib.lce_ce_with_grad_inplace_noalloc
+    nmax = _lib.NOALLOC_MAX_ROWS
+    assert f(p, p, nmax + 1, 10, BF16, -100, 0.0, p, p, p, None) == 9      # LCE_ERR_SCRATCH_LIMIT
+    assert f(p, p, -1, 10, BF16, -100, 0.0, p, p, p, None) == 2            # shape
+    assert f(p, p, 4, 0, BF16, -100, 0.0, p, p, p, None) == 2
+    assert f(p, p, 4, 10, 7, -100, 0.0, p, p, p, None) == 3                # dtype
+    assert f(p, p, 4, 10, BF16, -100, 0.0, None, p, p, None) == 1          # NULL output
+    assert f(p, p, 4, 10, BF16, -100, -1.0, p, p, p, None) == 6            # z-loss < 0
+    assert f(ctypes.c_void_p((1 << 20) + 2), p, 4, 10, BF16, -100, 0.0, p, p, p, None) == 4  # alignment
+    assert b"scratch" in lib.lce_status_string(9)
