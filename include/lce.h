@@ -33,9 +33,15 @@
 
 #ifdef __cplusplus
 extern "C" {
+/* The enums are int-sized in C; in C++ their underlying type is fixed to int as well, so that
+ * any int a caller passes (an invalid dtype, say) is a value of the type and is rejected with
+ * an error code rather than being undefined. */
+#define LCE_ENUM_BASE : int
+#else
+#define LCE_ENUM_BASE
 #endif
 
-typedef enum lce_status {
+typedef enum lce_status LCE_ENUM_BASE {
   LCE_OK = 0,
   LCE_ERR_NULL = 1,         /* a required pointer is NULL */
   LCE_ERR_SHAPE = 2,        /* a size is out of range (negative, V < 1, H not a multiple of 8, ...) */
@@ -48,13 +54,13 @@ typedef enum lce_status {
   LCE_ERR_SCRATCH_LIMIT = 9 /* (no-allocation entry point) the size exceeds its fixed scratch */
 } lce_status;
 
-typedef enum lce_dtype {
+typedef enum lce_dtype LCE_ENUM_BASE {
   LCE_DTYPE_F32 = 0,
   LCE_DTYPE_BF16 = 1,
   LCE_DTYPE_F16 = 2   /* IEEE half: lce_ce_with_grad_inplace only */
 } lce_dtype;
 
-typedef enum lce_reduction {
+typedef enum lce_reduction LCE_ENUM_BASE {
   LCE_REDUCTION_MEAN = 0, /* loss and grads scaled by 1 / max(n_valid, 1) */
   LCE_REDUCTION_SUM = 1   /* unscaled */
 } lce_reduction;

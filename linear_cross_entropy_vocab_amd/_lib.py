@@ -38,15 +38,19 @@ c_f = ctypes.c_float
 
 
 def load() -> ctypes.CDLL:
-    """Load liblce.so (built in-tree by linear_cross_entropy_vocab_amd.build); raise if absent."""
+    """Load liblce.so (built in-tree by linear_cross_entropy_vocab_amd.build); raise if absent.
+
+    LCE_LIBRARY, if set, names another build of the same library to load instead (the
+    host-sanitizer build of build.build_host_sanitized)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    path = os.environ.get("LCE_LIBRARY") or LIB_PATH
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build it first with "
+            f"{path} is missing: build it first with "
             "`python -m linear_cross_entropy_vocab_amd.build` (there is no fallback path)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     fused = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int, c_i64, c_f, ctypes.c_int,
              ctypes.c_uint32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_size_t, c_vp]
     lib.lce_fwd_bwd.argtypes = fused

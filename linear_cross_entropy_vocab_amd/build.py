@@ -60,6 +60,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-sanitizer build: only the host code (the C ABI's argument checks, workspace carving
+# and launch planning) compiled with AddressSanitizer and UndefinedBehaviorSanitizer, as
+# relocatable host objects with no device code; it loads on a machine without a GPU and runs
+# every host-side check of the ABI, never a kernel.  Loaded through LCE_LIBRARY with the
+# sanitizer runtime preloaded (tests/test_host_sanitizers.py).
+SAN_DIR = os.path.join(BUILD, "asan")
+SAN_LIB = os.path.join(SAN_DIR, "liblce_asan.so")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized() -> str:
+    hipcc = _hipcc()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    common = ["-O1", "-g", "-std=c++17", "-fPIC", "-fgpu-rdc", "--offload-host-only", *SAN_HOST,
+              "-I", INCLUDE, "-I", CSRC]
+
+    def comp(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        r = subprocess.run([hipcc, *common, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (host sanitizer build) failed for {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    r = subprocess.run([hipcc, "-shared", "-fPIC", "-fgpu-rdc", "--offload-host-only", *SAN_HOST[:2], "-shared-libsan",
+                        *objs, "-o", SAN_LIB], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (host sanitizer build) failed:\n{r.stderr}")
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime of the ROCm toolchain (preloaded into Python)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
