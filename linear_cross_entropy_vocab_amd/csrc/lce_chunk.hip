@@ -5,8 +5,9 @@
 //   for each chunk of cs tokens:
 //     logits chunk  z = h_chunk W^T + b           (MFMA GEMM, bf16 into one reused buffer)
 //     in place      z <- valid * (softmax(z)(1 + 2 mu LSE) - onehot(y))   (standalone CE)
-//     grad_input[chunk] = c * z . W                (GEMM on the stored dlogits)
-//     grad_W += z^T . h_chunk,  grad_b += column sums of z   (fp32 sums over the chunks)
+//     grad_input[chunk] = c * z . W                (stored-operand GEMM, lce_sgemm.hip)
+//     grad_W += z^T . h_chunk,  grad_b += column sums of z   (fp32 sums over the chunks; z read
+//                                                  transposed by the same GEMM)
 //   loss = c * sum over chunks of (ce_sum + mu z_sum)
 //
 // No logits are recomputed (6 BT V H flops in all), at the price of one bf16 logits chunk and
@@ -165,42 +166,56 @@ hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bo
     }
     if (e != hipSuccess) return e;
     if (!grads) continue;
-    MatArgs m{};
-    m.G = zbuf;
-    m.ld = c.ld;
-    m.g_rows = rows;
-    m.H = a.H;
-    m.hchunks = c.hchunks;
-    m.n_valid = w.n_valid;
-    m.mean = (mode == kLoss && a.mean) ? 1 : 0;  // per-row weights carry their own scale
-    if (a.grad_input != nullptr) {
-      m.X = W;
-      m.nS = rows;
-      m.nX = a.V;
-      m.x_split = c.x_split;
-      m.nsplit = c.nsplit;
-      m.part = part;
-      if ((e = launch_mat_gemm(false, m, st)) != hipSuccess) return e;
-      if ((e = launch_mat_reduce(part, c.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + r0 * a.H,
-                                 w.n_valid, m.mean != 0, st)) != hipSuccess)
+    const bool mean = mode == kLoss && a.mean;  // (per-row weights carry their own scale)
+    if (a.grad_input != nullptr && rows > 0) {
+      // grad_input[chunk] = c * G . W on the stored-operand GEMM: the vocabulary split into
+      // K-ranges (about one workgroup per compute unit, within the partial buffers), summed by
+      // mat_reduce
+      SgArgs m{};
+      m.A = zbuf;
+      m.lda = c.ld;
+      m.B = W;
+      m.ldb = a.H;
+      m.M = rows;
+      m.N = a.H;
+      m.K = a.V;
+      const int64_t tiles = ((rows + 255) / 256) * ((a.H + 255) / 256);
+      const int64_t ns = std::max<int64_t>(1, std::min<int64_t>(c.nsplit, (256 + tiles - 1) / tiles));
+      m.ksplit = ((a.V + ns - 1) / ns + 63) / 64 * 64;
+      m.nsplit = (int)((a.V + m.ksplit - 1) / m.ksplit);
+      m.C = part;
+      m.ldc = a.H;
+      m.split_stride = rows * a.H;
+      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+      if ((e = launch_mat_reduce(part, m.nsplit, rows, a.H, static_cast<bf16_t*>(a.grad_input) + r0 * a.H, w.n_valid,
+                                 mean, st)) != hipSuccess)
         return e;
     }
-    if (want_dw) {
-      m.X = hk;
-      m.nS = a.V;
-      m.nX = rows;
-      m.x_split = (rows + 15) / 16 * 16;
+    if (want_dw && a.grad_W != nullptr) {
+      // grad_W sum over chunks += G^T . h_chunk (G read transposed), in fp32
+      SgArgs m{};
+      m.A = zbuf;
+      m.lda = c.ld;
+      m.B = hk;
+      m.ldb = a.H;
+      m.M = a.V;
+      m.N = a.H;
+      m.K = rows;
+      m.ksplit = std::max<int64_t>(64, (rows + 63) / 64 * 64);
       m.nsplit = 1;
-      m.part = nullptr;
-      m.acc = a.grad_W != nullptr ? gw_acc : nullptr;
-      m.out = a.grad_W;
-      m.out_f32 = grad_w_fp32 ? 1 : 0;
-      m.first = k == 0 ? 1 : 0;
-      m.last = k == nch - 1 ? 1 : 0;
-      m.gb_acc = a.grad_b != nullptr ? gb_acc : nullptr;
-      m.gb_out = static_cast<bf16_t*>(a.grad_b);
-      if ((e = launch_mat_gemm(true, m, st)) != hipSuccess) return e;
+      m.C = gw_acc;
+      m.ldc = a.H;
+      m.split_stride = 0;
+      m.accumulate = k > 0 ? 1 : 0;
+      if ((e = launch_sgemm_at(m, st)) != hipSuccess) return e;
+      if (k == nch - 1 && (e = launch_sg_reduce(gw_acc, 1, a.V * a.H, a.V * a.H, a.grad_W, grad_w_fp32, w.n_valid,
+                                                mean, st)) != hipSuccess)
+        return e;
     }
+    if (want_dw && a.grad_b != nullptr &&
+        (e = launch_colsum(zbuf, c.ld, rows, a.V, gb_acc, k == 0, k == nch - 1, static_cast<bf16_t*>(a.grad_b),
+                           w.n_valid, mean, st)) != hipSuccess)
+      return e;
   }
   if (mode == kLoss) {
     hipLaunchKernelGGL(chunk_loss_kernel, dim3(1), dim3(64), 0, st, ce_k, z_k, nch, w.n_valid, a.mu,

@@ -193,6 +193,13 @@ struct SgArgs {
   int mean;
 };
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);
+// The same with A given transposed: At [K][lda] (M contiguous, a multiple of 8 elements per row
+// read, elements past M zero or never stored beyond lda).
+hipError_t launch_sgemm_at(const SgArgs& a, hipStream_t st);
+// acc[v] = (first ? 0 : acc[v]) + sum over rows of g[t][v] (bf16 rows ld apart), and with last
+// out[v] = c * acc[v] in bf16.
+hipError_t launch_colsum(const uint16_t* g, int64_t ld, int64_t rows, int64_t cols, float* acc, bool first, bool last,
+                         uint16_t* out, const int64_t* n_valid, bool mean, hipStream_t st);
 // out[i] = c * sum_s part[s * stride + i] for i < n (n a multiple of 4), in bf16 or fp32.
 hipError_t launch_sg_reduce(const float* part, int nsplit, int64_t n, int64_t stride, void* out, bool out_f32,
                             const int64_t* n_valid, bool mean, hipStream_t st);

@@ -36,6 +36,10 @@ __device__ __forceinline__ bf16x8_t sg_tr_pair(const char* p0, const char* p1) {
   return bf16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// ATRANS: A is given transposed, At [K][lda] with M contiguous (the dlogits chunk of the
+// token-chunked composition, [tokens][vocabulary], as the grad_W operand G^T): its stage is
+// loaded and read like B's (planes of 32 M-columns, transposed reads).
+template <bool ATRANS>
 __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
   constexpr int STAGE = kSgTile * 128;  // 32 KiB: A (256 rows x 64 K) or B (64 K x 256 columns)
   __shared__ __attribute__((aligned(1024))) char sA[2][STAGE];
@@ -59,7 +63,8 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
   // chunk (l % 8) ^ swz(row); B plane w, sub-block j: K-row 16 j + l / 4, columns
   // 32 w + 8 (l % 4) .. + 7.  Elements past M, N or the K range read as zero.
   const int64_t mrows = (p.M - m0) < kSgTile ? (p.M - m0) : kSgTile;
-  const u32x4_t ra = make_rsrc_words(p.A + m0 * p.lda, mrows * p.lda * 2);
+  const u32x4_t ra = ATRANS ? make_rsrc_words(p.A + kb * p.lda, (p.K - kb) * p.lda * 2)
+                            : make_rsrc_words(p.A + m0 * p.lda, mrows * p.lda * 2);
   const u32x4_t rb = make_rsrc_words(p.B + kb * p.ldb, (p.K - kb) * p.ldb * 2);
   int a_k[4];
   uint32_t a_off[4];
@@ -72,6 +77,10 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
   const int64_t bcol = n0 + 32 * w + 8 * (lane & 3);
   const bool bcol_ok = bcol < p.N;
   const uint32_t b_off0 = (uint32_t)((lane >> 2) * p.ldb * 2 + bcol * 2);
+  // (ATRANS) A plane w: M-columns m0 + 32 w + 8 (l % 4) .. + 7 of K-rows 16 j + l / 4
+  const int64_t acol = m0 + 32 * w + 8 * (lane & 3);
+  const bool acol_ok = acol < p.M;
+  const uint32_t at_off0 = (uint32_t)((lane >> 2) * p.lda * 2 + acol * 2);
   const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)sA[0]));
   const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(
@@ -80,8 +89,15 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
   auto dma = [&](int ks, int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = 64 * ks + a_k[j] < klen;
-      dma16(ra, la + (uint32_t)(buf * STAGE + 1024 * (4 * w + j)), ok ? a_off[j] + 128u * ks : 0x80000000u);
+      if constexpr (ATRANS) {
+        const int kr = 64 * ks + 16 * j + (lane >> 2);
+        const bool ok = acol_ok && kr < klen;
+        dma16(ra, la + (uint32_t)(buf * STAGE + 1024 * (4 * w + j)),
+              ok ? at_off0 + (uint32_t)((64 * ks + 16 * j) * p.lda * 2) : 0x80000000u);
+      } else {
+        const bool ok = 64 * ks + a_k[j] < klen;
+        dma16(ra, la + (uint32_t)(buf * STAGE + 1024 * (4 * w + j)), ok ? a_off[j] + 128u * ks : 0x80000000u);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -113,13 +129,20 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
     vm_wait<0>();     // this wave's loads of stage ks have landed
     __syncthreads();  // every wave's have; nobody reads the other buffer any more
     if (ks + 1 < nk) dma(ks + 1, buf ^ 1);
-    const char* a_base = sA[buf] + (wm * 128 + (lane & 31)) * 128;
+    const char* a_base = ATRANS ? sA[buf] + (4 * wm) * 4096 : sA[buf] + (wm * 128 + (lane & 31)) * 128;
     const char* b_base = sB[buf] + (2 * wn) * 4096;
     Frag<bf16_t> fa[2][4], fb[2][2];
     auto rd = [&](int kk, int slot) {
       const int off = ((2 * kk + (lane >> 5)) ^ fs) << 4;
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb) lds_frag_ptr(fa[slot][vb], a_base + vb * 32 * 128 + off);
+      for (int vb = 0; vb < 4; ++vb) {
+        if constexpr (ATRANS) {
+          const char* pa = a_base + vb * 4096 + kk * 1024;
+          fa[slot][vb].v = sg_tr_pair(pa + o_b[0], pa + o_b[1]);
+        } else {
+          lds_frag_ptr(fa[slot][vb], a_base + vb * 32 * 128 + off);
+        }
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const char* pb = b_base + nb * 4096 + kk * 1024;
@@ -217,7 +240,47 @@ hipError_t launch_sgemm(const SgArgs& a, hipStream_t st) {
   if (kSgTile * a.lda * 2 >= 0x80000000ll || a.K * a.ldb * 2 >= 0x80000000ll) return hipErrorInvalidValue;
   if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
   if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sgemm_kernel, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
+  hipLaunchKernelGGL(sgemm_kernel<false>, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// The same with A given transposed: At [K][lda], M contiguous.
+hipError_t launch_sgemm_at(const SgArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const int64_t ntm = (a.M + kSgTile - 1) / kSgTile, ntn = (a.N + kSgTile - 1) / kSgTile;
+  const int64_t total = ntm * ntn * a.nsplit;
+  if (a.nsplit < 1 || total > 0x7fffffff || a.ksplit % 64 != 0 || a.ksplit <= 0) return hipErrorInvalidValue;
+  if (a.K * a.lda * 2 >= 0x80000000ll || a.K * a.ldb * 2 >= 0x80000000ll) return hipErrorInvalidValue;
+  if (a.M % 8 != 0 && a.lda < (a.M + 7) / 8 * 8) return hipErrorInvalidValue;
+  if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
+  if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sgemm_kernel<true>, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// Column sums of a dlogits chunk G [rows][ld] (bf16) into an fp32 running sum over chunks:
+// acc[v] = (first ? 0 : acc[v]) + sum_t G[t][v]; on the last chunk out[v] = c * acc[v] (bf16).
+__global__ void __launch_bounds__(256) colsum_kernel(const bf16_t* __restrict__ g, int64_t ld, int64_t rows,
+                                                     int64_t cols, float* __restrict__ acc, int first, int last,
+                                                     bf16_t* __restrict__ out, const int64_t* __restrict__ n_valid,
+                                                     int mean) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= cols) return;
+  float s = first ? 0.f : acc[v];
+  for (int64_t t = 0; t < rows; ++t) s += bf2f(g[t * ld + v]);
+  acc[v] = s;
+  if (last) {
+    const long long nv = *n_valid;
+    const float cs = mean ? 1.f / (float)(nv > 1 ? nv : 1) : 1.f;
+    out[v] = f2bf(cs * s);
+  }
+}
+
+hipError_t launch_colsum(const bf16_t* g, int64_t ld, int64_t rows, int64_t cols, float* acc, bool first, bool last,
+                         bf16_t* out, const int64_t* n_valid, bool mean, hipStream_t st) {
+  if (cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, st, g, ld, rows, cols, acc,
+                     first ? 1 : 0, last ? 1 : 0, out, n_valid, mean ? 1 : 0);
   return hipGetLastError();
 }
 
