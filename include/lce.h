@@ -216,6 +216,16 @@ lce_status lce_ce_with_grad_inplace_noalloc(void* logits, const int64_t* targets
                                             void* stream);
 
 /*
+ * lce_stream_bandwidth -- a measurement helper, not part of the loss: streams `bytes` through
+ * device memory with plain 16-byte accesses (mode 0: read src; 1: write dst; 2: copy src to
+ * dst), so that the memory rate this device actually sustains can be timed beside
+ * lce_ce_with_grad_inplace, the HBM-bound kernel.  In mode 0, dst is a 4-byte device scratch
+ * word that is at most written.  bytes a multiple of 16, pointers 16-byte aligned; errors as
+ * above (LCE_ERR_ARG for another mode).
+ */
+lce_status lce_stream_bandwidth(int mode, const void* src, void* dst, size_t bytes, void* stream);
+
+/*
  * lce_fwd_bwd_chunked -- the same loss and gradients by the token-chunked composition
  * ("Fused Linear Cross-Entropy: The Math, the Memory Wall, and Two Ways Around It",
  * Strategy 1 and "The chunk-size trick"; "Greyhound -- Cross-Entropy", "Relationship to

@@ -28,7 +28,7 @@ EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_f
            "lce_rows_forward", "lce_rows_backward", "lce_rows_workspace_bytes",
            "lce_stage_name",
            "lce_ce_with_grad_inplace", "lce_ce_with_grad_inplace_noalloc", "lce_ce_workspace_bytes",
-           "lce_status_string", "lce_version")
+           "lce_stream_bandwidth", "lce_status_string", "lce_version")
 
 _lib = None
 
@@ -80,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.lce_ce_with_grad_inplace_noalloc.argtypes = [c_vp, c_vp, c_i64, c_i64, ctypes.c_int, c_i64, c_f, c_vp,
                                                      c_vp, c_vp, c_vp]
     lib.lce_ce_with_grad_inplace_noalloc.restype = ctypes.c_int
+    lib.lce_stream_bandwidth.argtypes = [ctypes.c_int, c_vp, c_vp, ctypes.c_size_t, c_vp]
+    lib.lce_stream_bandwidth.restype = ctypes.c_int
     lib.lce_ce_workspace_bytes.argtypes = [c_i64, c_i64, ctypes.c_int]
     lib.lce_ce_workspace_bytes.restype = ctypes.c_size_t
     lib.lce_status_string.argtypes = [ctypes.c_int]

@@ -138,6 +138,26 @@ __device__ __forceinline__ void mask_tail(Vec16<float>& v, int64_t c0, int64_t V
   for (int d = 0; d < 4; ++d) (&v.raw.x)[d] = (c0 + d < V) ? (&v.raw.x)[d] : 0xff800000u;
 }
 
+// The same for a vector whose first element is element `first` of a run with `rem` elements
+// before V (32-bit arithmetic): elements at or past rem become -inf.
+template <typename T>
+__device__ __forceinline__ void mask_run(Vec16<T>& v, int first, int rem) {
+  constexpr int EPV = Vec16<T>::N;
+  if constexpr (EPV == 4) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) (&v.raw.x)[d] = (first + d < rem) ? (&v.raw.x)[d] : 0xff800000u;
+  } else {
+    const uint32_t ninf = Vec16<T>::neg_inf().x;  // two -inf halves
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t& x = (&v.raw.x)[d];
+      const uint32_t lo = (first + 2 * d < rem) ? (x & 0x0000ffffu) : (ninf & 0x0000ffffu);
+      const uint32_t hi = (first + 2 * d + 1 < rem) ? (x & 0xffff0000u) : (ninf & 0xffff0000u);
+      x = lo | hi;
+    }
+  }
+}
+
 // Row cached in registers: NV vectors of 16 B per thread, all loaded before any is used
 // (buffer loads: bytes past the row read as zero and stores there are dropped; the stores
 // use the non-temporal cache policy, measured 4% faster, the loads the default one, which
@@ -211,6 +231,135 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_cached(T* __restrict__ log
     }
     store16_nt(make_rsrc((char*)x + j * kSlice, row_bytes - j * kSlice), lane_off, pack_out(d, T()));
   }
+  if (tid == 0) {
+    out.ce[row] = valid ? (lse - xy) : 0.f;
+    out.zsq[row] = valid ? lse * lse : 0.f;
+    out.valid[row] = valid ? 1 : 0;
+    if (out.lse != nullptr) out.lse[row] = lse;
+  }
+}
+
+// Rows longer than the register cache of a 1024-thread workgroup and at most 512 KiB (the fp32
+// rows of a 128Ki-entry vocabulary, 513 KB): a 512-thread workgroup (256 registers per lane)
+// keeps NVR 16-byte vectors per thread in VGPRs and NVL more in LDS (NVL x 8 KiB), the latter
+// loaded straight into LDS by buffer->LDS loads, so that HBM still sees one read and one write
+// per element.  The row is cut into 64 runs of NV = NVR + NVL lines of 128 bytes; lanes
+// 8 g .. 8 g + 7 of the workgroup own run g, lane c of them the 16-byte column c of each line,
+// so a thread's vectors sit at immediate offsets 128 j from one base and every load instruction
+// still reads whole lines.  Each thread reads back only the LDS vectors its own wave loaded
+// (no barrier needed).
+constexpr int kCELThreads = 512;
+constexpr int kCELWaves = kCELThreads / kWave;
+template <typename T, int NVR, int NVL>
+__global__ void __launch_bounds__(kCELThreads) ce_rows_cached_lds(T* __restrict__ logits,
+                                                                   const int64_t* __restrict__ targets,
+                                                                   int64_t V, int64_t ld, int64_t ignore_index,
+                                                                   float mu, CERowOut out) {
+  constexpr int EPV = Vec16<T>::N;
+  constexpr int NV = NVR + NVL;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float sm[kCELWaves], ss[kCELWaves];
+  __shared__ __attribute__((aligned(1024))) char lv[NVL][kCELThreads * 16];
+  const int64_t row = blockIdx.x;
+  T* x = logits + row * ld;
+  const int tid = threadIdx.x;
+  const int64_t y = targets[row];
+  const bool valid = (y != ignore_index) && (y >= 0) && (y < V);
+  const int64_t row_bytes = ld * (int64_t)sizeof(T);
+  const int g = tid >> 3, c = tid & 7;
+  const uint32_t base = (uint32_t)(g * NV * 128 + c * 16);  // byte offset of vector 0
+  const int64_t e0 = (int64_t)base / (int64_t)sizeof(T);       // its first element
+  constexpr int64_t kStepE = 128 / (int64_t)sizeof(T);         // elements between vectors j, j + 1
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(x, row_bytes);
+  const u32x4_t rw = make_rsrc_words(x, row_bytes);
+  const float xy = Vec16<T>::elem(rs, (tid == 0 && valid) ? (uint32_t)(y * (int64_t)sizeof(T)) : 0xfffffff0u);
+  // LDS part first (its loads are the oldest, so they land first), then the register part
+  const uint32_t lds0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lv[0]));
+  const uint32_t wave_lds = lds0 + (uint32_t)(wave_id() * kWave * 16);
+#pragma unroll
+  for (int j = NVR; j < NV; ++j)
+    dma16(rw, wave_lds + (uint32_t)((j - NVR) * kCELThreads * 16), base + (uint32_t)j * 128u);
+  Vec16<T> buf[NVR];
+#pragma unroll
+  for (int j = NVR - 1; j >= 0; --j) buf[j].raw = load16(rs, base + (uint32_t)j * 128u);
+  // elements of this thread's run that lie before V (32-bit; clamped): element e of vector j is
+  // read as -inf at or past it (a select on each value read, so the cached vectors themselves
+  // are never rewritten)
+  const int64_t rem64 = V - e0;
+  const int rem = (int)(rem64 < 0 ? 0 : (rem64 > NV * kStepE ? NV * kStepE : rem64));
+  // (each pass takes its own opaque copy of rem, so the compiler cannot hoist one predicate per
+  // element out of the passes and keep them all alive)
+  int rem_p = rem;
+  auto fresh_rem = [&]() {
+    rem_p = rem;
+    asm volatile("" : "+v"(rem_p));
+  };
+  auto val = [&](float f, int j, int e) { return (j * (int)kStepE + e < rem_p) ? f : -INFINITY; };
+  auto lds_vec = [&](int j) {
+    Vec16<T> v;
+    v.raw = *reinterpret_cast<const uint4*>(&lv[j - NVR][tid * 16]);
+    return v;
+  };
+  vm_wait<0>();
+
+  float m = -INFINITY;
+  fresh_rem();
+#pragma unroll
+  for (int j = NV - 1; j >= NVR; --j) {
+    const Vec16<T> v = lds_vec(j);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) m = fmaxf(m, val(v.get(e), j, e));
+  }
+#pragma unroll
+  for (int j = NVR - 1; j >= 0; --j)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) m = fmaxf(m, val(buf[j].get(e), j, e));
+  float s = 0.f;
+  const float ml = m * kLog2e;
+  fresh_rem();
+#pragma unroll
+  for (int j = NV - 1; j >= NVR; --j) {
+    const Vec16<T> v = lds_vec(j);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s += __builtin_amdgcn_exp2f(fmaf(val(v.fresh(e), j, e), kLog2e, -ml));
+  }
+#pragma unroll
+  for (int j = NVR - 1; j >= 0; --j)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s += __builtin_amdgcn_exp2f(fmaf(val(buf[j].fresh(e), j, e), kLog2e, -ml));
+  if (m == -INFINITY) s = 0.f;
+  // workgroup (max, sum): waves, then the kCELWaves partials in a fixed order
+  wave_ms(m, s);
+  {
+    const int w = tid / kWave, l = tid % kWave;
+    if (l == 0) { sm[w] = m; ss[w] = s; }
+    __syncthreads();
+    m = -INFINITY;
+    s = 0.f;
+    for (int i = 0; i < kCELWaves; ++i) ms_merge(m, s, sm[i], ss[i]);
+  }
+  const float lse = m + __logf(s);
+  const float scale = valid ? (1.f + 2.f * mu * lse) : 0.f;
+  const float ll = lse * kLog2e;
+  // the thread and vector holding column y: line L = byte / 128 is vector L % NV of run L / NV
+  const int64_t yb = valid ? y * (int64_t)sizeof(T) : 0;
+  const int64_t yl = yb / 128;
+  const int ty = (int)(8 * (yl / NV) + (yb % 128) / 16), jy = (int)(yl % NV), ey = (int)((yb % 16) / sizeof(T));
+  const bool owner = valid && ty == tid;
+  auto emit = [&](int j, const Vec16<T>& v) {
+    float d[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) d[e] = __builtin_amdgcn_exp2f(fmaf(val(v.fresh(e), j, e), kLog2e, -ll)) * scale;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) d[e] -= (owner && j == jy && e == ey) ? 1.f : 0.f;
+    store16_nt(rs, base + (uint32_t)j * 128u, pack_out(d, T()));
+  };
+  fresh_rem();
+#pragma unroll
+  for (int j = 0; j < NVR; ++j) emit(j, buf[j]);
+#pragma unroll
+  for (int j = NVR; j < NV; ++j) emit(j, lds_vec(j));
   if (tid == 0) {
     out.ce[row] = valid ? (lse - xy) : 0.f;
     out.zsq[row] = valid ? lse * lse : 0.f;
@@ -515,6 +664,10 @@ static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int6
     else if (per <= 4) hipLaunchKernelGGL((ce_rows_cached<T, 4>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
     else if (per <= 8) hipLaunchKernelGGL((ce_rows_cached<T, 8>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
     else hipLaunchKernelGGL((ce_rows_cached<T, 16>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
+  } else if (vec_ok && ld * (int64_t)sizeof(T) <= 64 * 64 * 128) {
+    // rows up to 512 KiB: 64 runs of 64 lines, 45 of them per thread in registers, 19 in LDS
+    hipLaunchKernelGGL((ce_rows_cached_lds<T, 45, 19>), grid, dim3(kCELThreads), 0, st, logits, targets, V, ld,
+                       ignore_index, mu, out);
   } else if (vec_ok) {
     hipLaunchKernelGGL((ce_rows_stream_vec<T>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
   } else {

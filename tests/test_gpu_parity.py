@@ -253,3 +253,23 @@ def test_ce_empty_batch():
     y = torch.empty(0, dtype=torch.int64, device="cuda")
     ce_sum, z_sum, nv = lce.lce_ce_with_grad_inplace(x, y, z_loss=1e-4)
     assert ce_sum.item() == 0.0 and z_sum.item() == 0.0 and int(nv.item()) == 0
+
+
+def test_stream_bandwidth_helper_moves_the_bytes():
+    """The bandwidth-measurement helper (read, write, copy) does what it says on a small buffer."""
+    import ctypes
+    lib = lce.load()
+    src = torch.arange(4096, dtype=torch.int32, device="cuda")
+    dst = torch.full_like(src, 7)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nb = src.numel() * 4
+    assert lib.lce_stream_bandwidth(2, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nb, st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert lib.lce_stream_bandwidth(1, None, ctypes.c_void_p(dst.data_ptr()), nb, st) == 0
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dst)) == 0
+    assert lib.lce_stream_bandwidth(0, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(sink.data_ptr()), nb, st) == 0
+    assert lib.lce_stream_bandwidth(3, None, ctypes.c_void_p(dst.data_ptr()), nb, st) == 6
+    torch.cuda.synchronize()
