@@ -404,7 +404,7 @@ lce_status lce_ce_with_grad_inplace(void* logits, const int64_t* targets, int64_
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int ct = dtype == LCE_DTYPE_BF16 ? lce::kCeBf16 : (dtype == LCE_DTYPE_F16 ? lce::kCeF16 : lce::kCeF32);
   if (lce::launch_ce_inplace(logits, ct, targets, B, V, V, ignore_index, z_loss_mult,
-                             ce_sum_out, z_sum_out, n_valid_out, nullptr, workspace, st) != hipSuccess)
+                             ce_sum_out, z_sum_out, n_valid_out, nullptr, workspace, false, st) != hipSuccess)
     return LCE_ERR_HIP;
   return LCE_OK;
 }
@@ -470,7 +470,7 @@ lce_status lce_ce_with_grad_inplace_noalloc(void* logits, const int64_t* targets
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int ct = dtype == LCE_DTYPE_BF16 ? lce::kCeBf16 : (dtype == LCE_DTYPE_F16 ? lce::kCeF16 : lce::kCeF32);
   if (lce::launch_ce_inplace(logits, ct, targets, B, V, V, ignore_index, z_loss_mult, ce_sum_out, z_sum_out,
-                             n_valid_out, nullptr, ws, st) != hipSuccess)
+                             n_valid_out, nullptr, ws, false, st) != hipSuccess)
     return LCE_ERR_HIP;
   return LCE_OK;
 }

@@ -651,7 +651,7 @@ hipError_t launch_rows_stats(void* logits, const int64_t* targets, int64_t B, in
 
 template <typename T>
 static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int64_t V, int64_t ld,
-                              int64_t ignore_index, float mu, CERowOut out, hipStream_t st) {
+                              int64_t ignore_index, float mu, CERowOut out, bool resident, hipStream_t st) {
   constexpr int EPV = 16 / (int)sizeof(T);
   const bool vec_ok = ((ld * (int64_t)sizeof(T)) % 16) == 0 &&
                       (reinterpret_cast<uintptr_t>(logits) % 16) == 0;
@@ -664,7 +664,7 @@ static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int6
     else if (per <= 4) hipLaunchKernelGGL((ce_rows_cached<T, 4>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
     else if (per <= 8) hipLaunchKernelGGL((ce_rows_cached<T, 8>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
     else hipLaunchKernelGGL((ce_rows_cached<T, 16>), grid, block, 0, st, logits, targets, V, ld, ignore_index, mu, out);
-  } else if (vec_ok && ld * (int64_t)sizeof(T) <= 64 * 64 * 128) {
+  } else if (vec_ok && !resident && ld * (int64_t)sizeof(T) <= 64 * 64 * 128) {
     // rows up to 512 KiB: 64 runs of 64 lines, 45 of them per thread in registers, 19 in LDS
     hipLaunchKernelGGL((ce_rows_cached_lds<T, 45, 19>), grid, dim3(kCELThreads), 0, st, logits, targets, V, ld,
                        ignore_index, mu, out);
@@ -679,7 +679,7 @@ static hipError_t launch_rows(T* logits, const int64_t* targets, int64_t B, int6
 
 hipError_t launch_ce_inplace(void* logits, int dtype, const int64_t* targets, int64_t B, int64_t V,
                              int64_t ld, int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
-                             int64_t* n_valid, float* lse_rows, void* workspace, hipStream_t st) {
+                             int64_t* n_valid, float* lse_rows, void* workspace, bool resident, hipStream_t st) {
   CERowOut out;
   out.lse = lse_rows;
   char* ws = static_cast<char*>(workspace);
@@ -690,11 +690,11 @@ hipError_t launch_ce_inplace(void* logits, int dtype, const int64_t* targets, in
   hipError_t e = hipSuccess;
   if (B > 0) {
     if (dtype == kCeBf16)
-      e = launch_rows<bf16_t>(static_cast<bf16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
+      e = launch_rows<bf16_t>(static_cast<bf16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, resident, st);
     else if (dtype == kCeF16)
-      e = launch_rows<f16_t>(static_cast<f16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
+      e = launch_rows<f16_t>(static_cast<f16_t*>(logits), targets, B, V, ld, ignore_index, mu, out, resident, st);
     else
-      e = launch_rows<float>(static_cast<float*>(logits), targets, B, V, ld, ignore_index, mu, out, st);
+      e = launch_rows<float>(static_cast<float*>(logits), targets, B, V, ld, ignore_index, mu, out, resident, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(ce_reduce, dim3(1), dim3(kCEThreads), 0, st, out.ce, out.zsq, out.valid, B,

@@ -158,7 +158,7 @@ hipError_t chunk_loop(const FusedArgs& a, ChunkMode mode, const RowsHost& io, bo
       return e;
     } else if (mode == kLoss) {
       e = launch_ce_inplace(zbuf, kCeBf16, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, ce_k + k, z_k + k,
-                            nv_k + k, offw(a.lse_out, r0), ce_ws, st);
+                            nv_k + k, offw(a.lse_out, r0), ce_ws, true, st);
     } else {
       e = launch_rows_stats(zbuf, a.targets + r0, rows, a.V, c.ld, a.ignore_index, a.mu, offw(io.lse, r0),
                             offw(io.logprobs, r0), offw(io.entropy, r0), offw(io.row_loss, r0), off(io.gl, r0),

@@ -243,10 +243,14 @@ hipError_t launch_rows_stats(void* logits, const int64_t* targets, int64_t B, in
 // Standalone cross-entropy.
 size_t ce_workspace_bytes(int64_t B);
 // Rows are ld >= V elements apart; with ld > V the rows must be 16-byte aligned and the
-// columns V..ld-1 are overwritten with 0.
+// columns V..ld-1 are overwritten with 0.  `resident` says the logits were just written and are
+// still held in the device's caches: rows longer than the register cache then take the
+// two-pass streaming kernel (its second read hits cache, at full occupancy) rather than the
+// single-read register+LDS kernel, which runs one 512-thread workgroup per compute unit.
 enum { kCeF32 = 0, kCeBf16 = 1, kCeF16 = 2 };  // element type of the logits
 hipError_t launch_ce_inplace(void* logits, int dtype, const int64_t* targets, int64_t B, int64_t V,
                              int64_t ld, int64_t ignore_index, float mu, float* ce_sum, float* z_sum,
-                             int64_t* n_valid, float* lse_rows, void* workspace, hipStream_t st);
+                             int64_t* n_valid, float* lse_rows, void* workspace, bool resident,
+                             hipStream_t st);
 
 }  // namespace lce
