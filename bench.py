@@ -14,7 +14,10 @@ workloads (under "configs"), the float64 CPU
 oracle timed on a bounded sample of the same workload, and the standalone
 cross-entropy kernel's HBM throughput on [8192, 128256] bf16 logits, and (under
 "filtered") the lossy gradient-filtering mode on the same workload: its step time, skipped
-tile fractions and distance from the exact gradients.
+tile fractions and distance from the exact gradients.  Under "vendor_gemm_reference" (per
+workload) the vendor GEMM library's rate on the step's three contractions with the logits
+materialised: a measured reference for these shapes on this device, not a path of the
+library.
 
 The `traffic` fields are HBM bytes per launch from FETCH_SIZE / WRITE_SIZE counter runs of
 this script (profiles/hbm_traffic.json, scaled by the same counters' reading for a plain
@@ -251,7 +254,39 @@ def _stage_roofline(stage_ms, btvh, dom=None):
                  "executed_flops_per_launch": execd[dom]}
 
 
-def bench_config(lce, torch, name, steps, warmup, log) -> dict:
+def vendor_gemm_reference(torch, h, W, reps: int = 3) -> dict:
+    """The vendor GEMM library (hipBLASLt, through torch.matmul) on the three contractions of
+    one step with the logits materialised: z = h W^T [BT, V], grad_input = G W and
+    grad_W = G^T h for a bf16 [BT, V] matrix G.  Plain GEMMs, no LSE epilogue, no recompute,
+    BT*V*2 bytes of logits in HBM: a measured reference for what this device's MFMAs deliver
+    on these shapes (the clock throttles under dense MFMA load), not a path of the library."""
+    BT, H = h.shape
+    V = W.shape[0]
+    z = torch.empty((BT, V), dtype=h.dtype, device=h.device)
+    gi = torch.empty_like(h)
+    gw = torch.empty_like(W)
+    flop = 2.0 * BT * V * H
+    res = {"library": "hipBLASLt via torch.matmul", "logits_bytes": int(z.numel() * z.element_size())}
+    for key, f in (("logits", lambda: torch.matmul(h, W.t(), out=z)),
+                   ("grad_input", lambda: torch.matmul(z, W, out=gi)),
+                   ("grad_weight", lambda: torch.matmul(z.t(), h, out=gw))):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[key] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12}
+    res["three_gemms_ms"] = sum(res[k]["ms"] for k in ("logits", "grad_input", "grad_weight"))
+    del z, gi, gw
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_config(lce, torch, name, steps, warmup, log, vendor=True) -> dict:
     """The fused step (lce_fwd_bwd: loss and every gradient) on another named LM-head workload:
     wall time per step, per-stage event times, the slowest stage's roofline position, and the
     extra device memory of one call against the one-logits-chunk budget."""
@@ -305,7 +340,11 @@ def bench_config(lce, torch, name, steps, warmup, log) -> dict:
            "loss": float(out["loss"].item()),
            "extra_hbm_bytes": int(ws.numel()), "extra_hbm_torch_peak_bytes": int(peak_extra),
            "extra_hbm_budget_bytes": int(budget)}
-    del h, W, b, y, r, out, ws
+    del r, out, ws
+    torch.cuda.empty_cache()
+    if vendor:
+        res["vendor_gemm_reference"] = vendor_gemm_reference(torch, h, W)
+    del h, W, b, y
     torch.cuda.empty_cache()
     return res
 
@@ -431,6 +470,8 @@ def main():
                          "Qwen-like) and print one JSON line per workload")
     ap.add_argument("--filter-eps", type=float, default=FILTER_EPS)
     ap.add_argument("--no-chunked", action="store_true", help="skip the token-chunked composition leg")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip the vendor GEMM reference (hipBLASLt on the step's three contractions)")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row outputs leg")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the fused step on the Gemma-like and Qwen-like workloads")
@@ -608,8 +649,12 @@ def main():
     if not args.no_configs:
         res["configs"] = {}
         for name in ("gemma_like", "qwen_like"):
-            res["configs"][name] = bench_config(lce, torch, name, min(args.steps, 10), min(args.warmup, 2), log)
+            res["configs"][name] = bench_config(lce, torch, name, min(args.steps, 10), min(args.warmup, 2), log,
+                                                vendor=not args.no_vendor_gemm)
             log(f"{name}: fused step {res['configs'][name]['ms_per_step']:.2f} ms")
+    if not args.no_vendor_gemm:
+        log("vendor GEMM reference (materialised logits)")
+        res["vendor_gemm_reference"] = vendor_gemm_reference(torch, h, W)
     if not args.no_chunked:
         log("token-chunked composition leg")
         res["chunked"] = bench_chunked(lce, torch, h, W, None, y, kw, out, args.steps, BT)
