@@ -238,12 +238,28 @@ def bench_rows(lce, torch, h, W, b, y, steps, BT) -> dict:
             "mean_entropy": float(r["entropy"].mean().item())}
 
 
+def one_pass_backward(stage_ms) -> bool:
+    """The library's one-pass backward (bf16, H > 1024, when its planner prefers it) computes
+    grad_input, grad_W and grad_b in the grad_input stage from one recompute of the dlogits,
+    leaving the grad_W stage empty."""
+    return stage_ms["bwd_dweight"] < 0.02 * stage_ms["bwd_dinput"]
+
+
+def executed_flops(stage_ms, btvh) -> float:
+    """Executed flops of a step: the forward GEMM and, per gradient stage, the recompute of the
+    logits and the gradient GEMM (10 BT V H); one recompute in the one-pass backward (8)."""
+    return (8 if one_pass_backward(stage_ms) else 10) * btvh
+
+
 def _stage_roofline(stage_ms, btvh, dom=None):
     """Roofline position of the slowest stage: algorithmic flops (the method's 2 BT V H per
     GEMM: logits, grad_input, grad_W) and executed flops (with the logits recomputed inside
-    each gradient stage) per launch over its mean event time, against dense bf16 peak."""
+    each gradient stage) per launch over its mean event time, against dense bf16 peak.  In
+    the one-pass backward the grad_input stage holds both gradient GEMMs and one recompute."""
     algo = {"fwd_lse": 2 * btvh, "bwd_dinput": 2 * btvh, "bwd_dweight": 2 * btvh}
     execd = {"fwd_lse": 2 * btvh, "bwd_dinput": 4 * btvh, "bwd_dweight": 4 * btvh}
+    if one_pass_backward(stage_ms):
+        algo["bwd_dinput"], execd["bwd_dinput"] = 4 * btvh, 6 * btvh
     if dom is None:
         dom = max(algo, key=lambda n: stage_ms[n])
     a = algo[dom] / (stage_ms[dom] * 1e-3) / 1e12
@@ -334,7 +350,9 @@ def bench_config(lce, torch, name, steps, warmup, log, vendor=True) -> dict:
     res = {"workload": f"{name}: BT={c.BT}, H={c.H}, V={c.V}, bf16, {c.reduction}"
                        + (", bias" if b is not None else "") + (f", z-loss {c.z_loss:g}" if c.z_loss else ""),
            "ms_per_step": ms, "tokens_per_s": c.BT / (ms * 1e-3),
-           "tflops_useful": 6 * btvh / (ms * 1e-3) / 1e12, "tflops_executed": 10 * btvh / (ms * 1e-3) / 1e12,
+           "tflops_useful": 6 * btvh / (ms * 1e-3) / 1e12,
+           "tflops_executed": executed_flops(st, btvh) / (ms * 1e-3) / 1e12,
+           "backward": "one pass" if one_pass_backward(st) else "two gradient stages",
            "useful_frac": 6 * btvh / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "stage_ms": st, "roofline": roof, "n_valid": int(out["n_valid"].item()),
            "loss": float(out["loss"].item()),
@@ -613,7 +631,7 @@ def main():
     dom, roof = _stage_roofline(stage_ms, btvh)
     roof["traffic"] = measured_traffic(dom)
     roof["mfma_busy_counter"] = _profile_value(MFMA_FILE, dom, "mfma_busy")
-    executed = 10 * btvh / (ms_step * 1e-3) / 1e12
+    executed = executed_flops(stage_ms, btvh) / (ms_step * 1e-3) / 1e12
     useful = 6 * btvh / (ms_step * 1e-3) / 1e12
     n_valid = int(out["n_valid"].item())
     loss = float(out["loss"].item())

@@ -71,6 +71,10 @@ struct SgPlan {
   int64_t tb, vr, ldt, ksplit;
   int nsplit;
   size_t g_bytes, part_bytes, bytes;
+  // one pass: grad_input is summed over pass 1's vocabulary blocks from the same stored
+  // transposed dlogits (hi in the output, lo_bytes of bf16 remainders), and pass 2 is dropped
+  bool one;
+  size_t lo_bytes;
 };
 SgPlan sg_plan(int64_t BT, int64_t H, int64_t V);
 
@@ -191,6 +195,13 @@ struct SgArgs {
   int out_f32;
   const int64_t* n_valid;
   int mean;
+  // Running sum over several launches (bf16 out only, one K-range): the sum is kept as
+  // hi + lo, hi (bf16) in `out` and lo (bf16, the rounding remainder) in `lo`, about 16
+  // significant bits.  hilo = 1: the first launch writes hi and lo; 2: later launches add;
+  // 3: the last one adds and writes c * sum to `out`; 0: plain output (c * C).
+  int hilo;
+  uint16_t* lo;
+  int64_t ldlo;
 };
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);
 // The same with A given transposed: At [K][lda] (M contiguous, a multiple of 8 elements per row

@@ -204,6 +204,49 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
                                                 (int)off[r], 0, 0);
       }
     }
+  } else if (p.hilo != 0) {
+    // running sum over launches as hi + lo (bf16 each): s = C + hi + lo, then either the next
+    // hi = bf16(s) and lo = bf16(s - hi), or, in the last launch, c * s to the output
+    const long long nvalid = *p.n_valid;
+    const float cs = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * 2, mrows * p.ldo * 2);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lo + m0 * p.ldlo, mrows * p.ldlo * 2);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const bool cok = ncol + 32 * nb < p.N;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        uint32_t oh[16], ol[16];
+        float sum[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mrow0 + 32 * vb + 8 * (r >> 2) + (r & 3);
+          oh[r] = cok ? (uint32_t)((m * p.ldo + ncol + 32 * nb) * 2) : 0x80000000u;
+          ol[r] = cok ? (uint32_t)((m * p.ldlo + ncol + 32 * nb) * 2) : 0x80000000u;
+          sum[r] = acc[vb][nb][r];
+        }
+        if (p.hilo != 1) {
+          uint16_t hv[16], lv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            hv[r] = __builtin_amdgcn_raw_buffer_load_b16(rh, (int)oh[r], 0, 0);
+            lv[r] = __builtin_amdgcn_raw_buffer_load_b16(rl, (int)ol[r], 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum[r] += bf2f(hv[r]) + bf2f(lv[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (p.hilo == 3) {
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(cs * sum[r]), rh, (int)oh[r], 0, 0);
+          } else {
+            const bf16_t hi = f2bf(sum[r]);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)hi, rh, (int)oh[r], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(sum[r] - bf2f(hi)), rl, (int)ol[r], 0, 0);
+          }
+        }
+      }
+    }
   } else {
     const long long nvalid = *p.n_valid;
     const float cs = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
@@ -230,6 +273,13 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
   vm_wait<0>();
 }
 
+// the running-sum output: bf16 out, one K-range, a remainder buffer (32-bit offsets per tile)
+static bool hilo_ok(const SgArgs& a) {
+  if (a.hilo == 0) return true;
+  return a.hilo >= 1 && a.hilo <= 3 && a.C == nullptr && !a.out_f32 && a.nsplit == 1 && a.lo != nullptr &&
+         kSgTile * a.ldlo * 2 < 0x80000000ll;
+}
+
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   const int64_t ntm = (a.M + kSgTile - 1) / kSgTile, ntn = (a.N + kSgTile - 1) / kSgTile;
@@ -240,6 +290,7 @@ hipError_t launch_sgemm(const SgArgs& a, hipStream_t st) {
   if (kSgTile * a.lda * 2 >= 0x80000000ll || a.K * a.ldb * 2 >= 0x80000000ll) return hipErrorInvalidValue;
   if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
   if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
+  if (!hilo_ok(a)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sgemm_kernel<false>, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -254,6 +305,7 @@ hipError_t launch_sgemm_at(const SgArgs& a, hipStream_t st) {
   if (a.M % 8 != 0 && a.lda < (a.M + 7) / 8 * 8) return hipErrorInvalidValue;
   if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
   if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
+  if (!hilo_ok(a)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sgemm_kernel<true>, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -21,6 +21,8 @@
 #include "lce_common.h"
 #include "lce_launch.h"
 
+#include <vector>
+
 namespace lce {
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -147,6 +149,7 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
 
 hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+hipError_t launch_sg_onepass(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 
 // Exact calls take the stored-operand GEMM plan; filtered and sorted calls (whose skip test
 // and row order live in the stored-dlogits GEMMs of lce_bwd.hip) the plan above.
@@ -170,8 +173,13 @@ static void set_filter(MatArgs& m, const FusedArgs& a, int which) {
 
 // Region layout: [256 B: grad_b placeholder] then pass 1: [G (vb columns)], pass 2:
 // [G (all columns) | partial sums]
+// With the one-pass plan the grad_input stage runs the whole backward and the grad_W stage has
+// nothing left to do (unless grad_input is not asked for: then the grad_W stage runs pass 1).
 hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return launch_sg_dinput(a, w, st);
+  if (exact_call(a)) {
+    const SgPlan t = sg_plan(a.BT, a.H, a.V);
+    if (t.on) return t.one ? launch_sg_onepass(a, w, st) : launch_sg_dinput(a, w, st);
+  }
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
@@ -215,7 +223,13 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
 }
 
 hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return launch_sg_dweight(a, w, st);
+  if (exact_call(a)) {
+    const SgPlan t = sg_plan(a.BT, a.H, a.V);
+    if (t.on) {
+      if (t.one && a.grad_input != nullptr && a.BT > 0) return hipSuccess;  // (done with grad_input)
+      return launch_sg_dweight(a, w, st);
+    }
+  }
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   float* gb_flag = reinterpret_cast<float*>(w.big);  // never read or written (one pass per row)
@@ -376,6 +390,55 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
   t.bytes = 256 + std::max(pass1, t.g_bytes + t.part_bytes);
   if (t.bytes > avail + 4096) return t;
   t.on = true;
+  // One pass instead: pass 1's blocks also give grad_input, summed over the blocks as hi + lo
+  // (hi in the output, lo here), so the dlogits are formed once: 8 instead of 10 BT V H flops.
+  // Taken when the cost model prefers it with the smaller blocks the lo buffer leaves.
+  const size_t lo = ws_align((size_t)BT * (size_t)H * 2);
+  if (lo + 4096 < avail && (int64_t)BT * H * 2 < 0x7fffffffll) {
+    const size_t avail1 = avail - lo;
+    double best = -1.0;
+    int64_t vb1 = 0, ks1b = 0;
+    int ns1b = 0;
+    for (int64_t ns1 = 1; ns1 <= 16; ++ns1) {
+      const int64_t ks1 = round_up(cdiv(BT, ns1), 64);
+      if (ns1 > 1 && cdiv(BT, ks1) != ns1) continue;
+      const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0);
+      const int64_t fit = std::min<int64_t>((int64_t)(avail1 / per_row) / 64 * 64, round_up(V, 64));
+      if (fit < 64) continue;
+      // candidates: evenly sized blocks near the fit, and multiples of 256 rows down to half of
+      // it (whole 256-row tiles: a grad_W launch of whole rounds of workgroups)
+      std::vector<int64_t> cand;
+      for (int64_t nb = cdiv(V, fit); nb <= cdiv(V, fit) + 8 && nb <= cdiv(V, 64); ++nb)
+        cand.push_back(std::min(round_up(cdiv(V, nb), 64), fit));
+      for (int64_t vb = fit / 256 * 256; vb >= 256 && 2 * vb >= fit; vb -= 256) cand.push_back(vb);
+      for (const int64_t vb : cand) {
+        const int64_t n = cdiv(V, vb), last = V - (n - 1) * vb;
+        const double red = ns1 > 1 ? cost_bytes((double)V * H * (4.0 * ns1 + 4.0)) + (double)n * kLaunchStages : 0.0;
+        // the running sum's traffic (2-byte accesses: counted at half the streaming rate)
+        const double sum_bytes = (double)BT * H * (8.0 * (double)n - 6.0);
+        const double c = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_gemm(vb, H, BT, ks1) + cost_gemm(BT, H, vb, vb)) +
+                         cost_dl(BT, last, H) + cost_gemm(last, H, BT, ks1) + cost_gemm(BT, H, last, last) +
+                         cost_bytes((double)V * t.ldv * 2) + red + 2.0 * cost_bytes(sum_bytes);
+        if (best < 0 || c < best) {
+          best = c;
+          vb1 = vb;
+          ns1b = (int)ns1;
+          ks1b = ks1;
+        }
+      }
+    }
+    if (best >= 0 && best < best1 + best2) {
+      t.one = true;
+      t.lo_bytes = lo;
+      t.vb = vb1;
+      t.nsplit1 = ns1b;
+      t.ksplit1 = ks1b;
+      t.g1_bytes = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
+      t.part1_bytes = t.nsplit1 > 1 ? ws_align((size_t)t.nsplit1 * (size_t)t.vb * (size_t)H * 4) : 0;
+      t.bytes = 256 + t.g1_bytes + t.part1_bytes + t.lo_bytes;
+      if (t.bytes > avail + 4096) t.on = false;
+    }
+  }
   return t;
 }
 
@@ -418,56 +481,101 @@ hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st
   return hipSuccess;
 }
 
-hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  const SgPlan t = sg_plan(a.BT, a.H, a.V);
-  if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
-  bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
-  float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
+// One vocabulary block of pass 1: G^T of the block against all tokens, then grad_W[block] and
+// grad_b[block] from it.
+static hipError_t sg_pass1_block(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bf16_t* g, float* part1,
+                                 int64_t v0, int64_t rows, hipStream_t st) {
   const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bf16_t* b = static_cast<const bf16_t*>(a.bias);
   hipError_t e;
-  for (int64_t v0 = 0; v0 < a.V; v0 += t.vb) {
-    const int64_t rows = std::min(t.vb, a.V - v0);
-    if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows,
-                                    v0, g, t.ldv, st)) != hipSuccess)
-      return e;
-    if (a.grad_W != nullptr) {
-      void* out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
-                               : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
-      SgArgs m{};
-      m.A = g;
-      m.lda = t.ldv;
-      m.B = h;
-      m.ldb = a.H;
-      m.M = rows;
-      m.N = a.H;
-      m.K = a.BT;
-      m.ksplit = t.ksplit1;
-      m.nsplit = t.nsplit1;
-      m.n_valid = w.n_valid;
-      m.mean = a.mean ? 1 : 0;
-      if (t.nsplit1 > 1) {  // K-ranges into partial sums, then c * their sum into the rows
-        m.C = part1;
-        m.ldc = a.H;
-        m.split_stride = rows * a.H;
-        if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
-        if ((e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, out, a.grad_w_f32, w.n_valid, a.mean,
-                                  st)) != hipSuccess)
-          return e;
-      } else {
-        m.out = out;
-        m.out_f32 = a.grad_w_f32 ? 1 : 0;
-        m.ldo = a.H;
-        if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
-      }
+  if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows, v0,
+                                  g, t.ldv, st)) != hipSuccess)
+    return e;
+  if (a.grad_W != nullptr) {
+    void* out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
+                             : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
+    SgArgs m{};
+    m.A = g;
+    m.lda = t.ldv;
+    m.B = h;
+    m.ldb = a.H;
+    m.M = rows;
+    m.N = a.H;
+    m.K = a.BT;
+    m.ksplit = t.ksplit1;
+    m.nsplit = t.nsplit1;
+    m.n_valid = w.n_valid;
+    m.mean = a.mean ? 1 : 0;
+    if (t.nsplit1 > 1) {  // K-ranges into partial sums, then c * their sum into the rows
+      m.C = part1;
+      m.ldc = a.H;
+      m.split_stride = rows * a.H;
+      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
+      if ((e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, out, a.grad_w_f32, w.n_valid, a.mean,
+                                st)) != hipSuccess)
+        return e;
+    } else {
+      m.out = out;
+      m.out_f32 = a.grad_w_f32 ? 1 : 0;
+      m.ldo = a.H;
+      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
     }
-    if (a.grad_b != nullptr &&
-        (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
-            hipSuccess)
-      return e;
+  }
+  if (a.grad_b != nullptr &&
+      (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
+          hipSuccess)
+    return e;
+  return hipSuccess;
+}
+
+// Pass 1 (grad_W, grad_b) and, with `dinput`, grad_input in the same sweep (one-pass plan):
+// grad_input += G . W[block] from the block's stored G^T (read transposed), kept as hi + lo
+// between blocks and written as c * the sum by the last one.
+static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bool dinput, hipStream_t st) {
+  bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
+  float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
+  bf16_t* lo = reinterpret_cast<bf16_t*>(w.big + 256 + t.g1_bytes + t.part1_bytes);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const int64_t nblk = (a.V + t.vb - 1) / t.vb;
+  hipError_t e;
+  for (int64_t k = 0; k < nblk; ++k) {
+    const int64_t v0 = k * t.vb, rows = std::min(t.vb, a.V - v0);
+    if ((e = sg_pass1_block(a, w, t, g, part1, v0, rows, st)) != hipSuccess) return e;
+    if (!dinput) continue;
+    SgArgs m{};
+    m.A = g;  // G^T [rows][ldv]: A = G read transposed, K = the block's vocabulary rows
+    m.lda = t.ldv;
+    m.B = W + v0 * a.H;
+    m.ldb = a.H;
+    m.M = a.BT;
+    m.N = a.H;
+    m.K = rows;
+    m.ksplit = (rows + 63) / 64 * 64;
+    m.nsplit = 1;
+    m.out = a.grad_input;
+    m.ldo = a.H;
+    m.n_valid = w.n_valid;
+    m.mean = a.mean ? 1 : 0;
+    m.hilo = nblk == 1 ? 0 : (k == 0 ? 1 : (k == nblk - 1 ? 3 : 2));
+    m.lo = reinterpret_cast<uint16_t*>(lo);
+    m.ldlo = a.H;
+    if ((e = launch_sgemm_at(m, st)) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  const SgPlan t = sg_plan(a.BT, a.H, a.V);
+  if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
+  return sg_sweep(a, w, t, false, st);
+}
+
+// One-pass plan: the whole backward (grad_input and, as requested, grad_W and grad_b).
+hipError_t launch_sg_onepass(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
+  const SgPlan t = sg_plan(a.BT, a.H, a.V);
+  if (!t.on || !t.one || w.big == nullptr) return hipErrorInvalidValue;
+  return sg_sweep(a, w, t, a.grad_input != nullptr && a.BT > 0, st);
 }
 
 }  // namespace lce
