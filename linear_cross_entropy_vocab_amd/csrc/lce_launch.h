@@ -207,6 +207,9 @@ hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);
 // The same with A given transposed: At [K][lda] (M contiguous, a multiple of 8 elements per row
 // read, elements past M zero or never stored beyond lda).
 hipError_t launch_sgemm_at(const SgArgs& a, hipStream_t st);
+// Both in one grid (the tiles of p0, as launch_sgemm takes it, then those of p1, A given
+// transposed): the rounds of workgroups over the device are filled with both products.
+hipError_t launch_sgemm_pair(const SgArgs& p0, const SgArgs& p1, hipStream_t st);
 // acc[v] = (first ? 0 : acc[v]) + sum over rows of g[t][v] (bf16 rows ld apart), and with last
 // out[v] = c * acc[v] in bf16.
 hipError_t launch_colsum(const uint16_t* g, int64_t ld, int64_t rows, int64_t cols, float* acc, bool first, bool last,

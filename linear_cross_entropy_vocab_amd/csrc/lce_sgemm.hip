@@ -39,19 +39,20 @@ __device__ __forceinline__ bf16x8_t sg_tr_pair(const char* p0, const char* p1) {
 // ATRANS: A is given transposed, At [K][lda] with M contiguous (the dlogits chunk of the
 // token-chunked composition, [tokens][vocabulary], as the grad_W operand G^T): its stage is
 // loaded and read like B's (planes of 32 M-columns, transposed reads).
-template <bool ATRANS>
-__global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
-  constexpr int STAGE = kSgTile * 128;  // 32 KiB: A (256 rows x 64 K) or B (64 K x 256 columns)
-  __shared__ __attribute__((aligned(1024))) char sA[2][STAGE];
-  __shared__ __attribute__((aligned(1024))) char sB[2][STAGE];
+constexpr int kSgStage = kSgTile * 128;  // 32 KiB: A (256 rows x 64 K) or B (64 K x 256 columns)
 
+__device__ __forceinline__ uint32_t sg_tiles(const SgArgs& p) {
+  return (uint32_t)((p.M + kSgTile - 1) / kSgTile) * (uint32_t)((p.N + kSgTile - 1) / kSgTile) * (uint32_t)p.nsplit;
+}
+
+// One workgroup's tile `id` of problem p (ids: columns fastest, then rows, then K ranges, so
+// that concurrent workgroups share A rows and B ranges), staged through sA / sB.
+template <bool ATRANS>
+__device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*sA)[kSgStage], char (*sB)[kSgStage]) {
+  constexpr int STAGE = kSgStage;
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int wm = w >> 2, wn = w & 3;
-  // tile of this workgroup: consecutive logical ids stay on one XCD (xcd_remap); columns
-  // fastest, then rows, then K ranges, so that concurrent workgroups share A rows and B ranges
   const uint32_t ntm = (uint32_t)((p.M + kSgTile - 1) / kSgTile), ntn = (uint32_t)((p.N + kSgTile - 1) / kSgTile);
-  const uint32_t total = ntm * ntn * (uint32_t)p.nsplit;
-  const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xcd_remap(blockIdx.x, total));
   const uint32_t nt = id % ntn, rest = id / ntn;
   const uint32_t mt = rest % ntm, split = rest / ntm;
   const int64_t m0 = (int64_t)mt * kSgTile, n0 = (int64_t)nt * kSgTile;
@@ -216,21 +217,23 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
       const bool cok = ncol + 32 * nb < p.N;
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
-        uint32_t oh[16], ol[16];
+        // element r of the group: row m0 + mrow0 + 32 vb + 8 (r / 4) + r % 4 (offsets from one
+        // base per buffer; the memory fence at the end keeps the next group's loads from being
+        // hoisted above these stores, which would hold every group's values at once)
+        const int mb = mrow0 + 32 * vb;
+        const uint32_t bh = cok ? (uint32_t)((mb * p.ldo + ncol + 32 * nb) * 2) : 0x80000000u;
+        const uint32_t bl = cok ? (uint32_t)((mb * p.ldlo + ncol + 32 * nb) * 2) : 0x80000000u;
+        auto oh = [&](int r) { return cok ? bh + (uint32_t)((8 * (r >> 2) + (r & 3)) * p.ldo * 2) : bh; };
+        auto ol = [&](int r) { return cok ? bl + (uint32_t)((8 * (r >> 2) + (r & 3)) * p.ldlo * 2) : bl; };
         float sum[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mrow0 + 32 * vb + 8 * (r >> 2) + (r & 3);
-          oh[r] = cok ? (uint32_t)((m * p.ldo + ncol + 32 * nb) * 2) : 0x80000000u;
-          ol[r] = cok ? (uint32_t)((m * p.ldlo + ncol + 32 * nb) * 2) : 0x80000000u;
-          sum[r] = acc[vb][nb][r];
-        }
+        for (int r = 0; r < 16; ++r) sum[r] = acc[vb][nb][r];
         if (p.hilo != 1) {
           uint16_t hv[16], lv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            hv[r] = __builtin_amdgcn_raw_buffer_load_b16(rh, (int)oh[r], 0, 0);
-            lv[r] = __builtin_amdgcn_raw_buffer_load_b16(rl, (int)ol[r], 0, 0);
+            hv[r] = __builtin_amdgcn_raw_buffer_load_b16(rh, (int)oh(r), 0, 0);
+            lv[r] = __builtin_amdgcn_raw_buffer_load_b16(rl, (int)ol(r), 0, 0);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) sum[r] += bf2f(hv[r]) + bf2f(lv[r]);
@@ -238,13 +241,14 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           if (p.hilo == 3) {
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(cs * sum[r]), rh, (int)oh[r], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(cs * sum[r]), rh, (int)oh(r), 0, 0);
           } else {
             const bf16_t hi = f2bf(sum[r]);
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)hi, rh, (int)oh[r], 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(sum[r] - bf2f(hi)), rl, (int)ol[r], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)hi, rh, (int)oh(r), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(sum[r] - bf2f(hi)), rl, (int)ol(r), 0, 0);
           }
         }
+        asm volatile("" ::: "memory");
       }
     }
   } else {
@@ -273,6 +277,35 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
   vm_wait<0>();
 }
 
+// Consecutive logical tile ids stay on one XCD (xcd_remap).
+template <bool ATRANS>
+__global__ void __launch_bounds__(kSgThreads, 1) sgemm_kernel(SgArgs p) {
+  __shared__ __attribute__((aligned(1024))) char sA[2][kSgStage];
+  __shared__ __attribute__((aligned(1024))) char sB[2][kSgStage];
+  const uint32_t total = sg_tiles(p);
+  const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xcd_remap(blockIdx.x, total));
+  sgemm_tile<ATRANS>(p, id, sA, sB);
+}
+
+// Two products in one grid, the tiles of p0 (A K-contiguous) first, then those of p1 (A given
+// transposed): a launch whose products are each short of a whole number of workgroup rounds
+// over the device fills the rounds with both.  Each product's tiles are spread over all XCDs
+// (XCD-contiguous within the product); p0's part of the grid is padded to a multiple of 8 with
+// workgroups that do nothing, so that both parts start on XCD 0.
+__global__ void __launch_bounds__(kSgThreads, 1) sgemm_pair_kernel(SgArgs p0, SgArgs p1) {
+  __shared__ __attribute__((aligned(1024))) char sA[2][kSgStage];
+  __shared__ __attribute__((aligned(1024))) char sB[2][kSgStage];
+  const uint32_t t0 = sg_tiles(p0), t0p = (t0 + 7) / 8 * 8;
+  const uint32_t b = blockIdx.x;
+  if (b < t0p) {
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xcd_remap(b, t0p));
+    if (id < t0) sgemm_tile<false>(p0, id, sA, sB);
+  } else {
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xcd_remap(b - t0p, sg_tiles(p1)));
+    sgemm_tile<true>(p1, id, sA, sB);
+  }
+}
+
 // the running-sum output: bf16 out, one K-range, a remainder buffer (32-bit offsets per tile)
 static bool hilo_ok(const SgArgs& a) {
   if (a.hilo == 0) return true;
@@ -280,33 +313,40 @@ static bool hilo_ok(const SgArgs& a) {
          kSgTile * a.ldlo * 2 < 0x80000000ll;
 }
 
+static int64_t sg_total(const SgArgs& a) {
+  const int64_t ntm = (a.M + kSgTile - 1) / kSgTile, ntn = (a.N + kSgTile - 1) / kSgTile;
+  return ntm * ntn * a.nsplit;
+}
+
+// Shapes the kernel takes: K-ranges of whole 64-element stages, and every descriptor the kernel
+// forms spanning less than 2^31 bytes (the offset 2^31 it uses for masked elements is then out
+// of range).  ATRANS: At [K][lda] with rows of whole 8-element vectors.
+static bool sg_args_ok(const SgArgs& a, bool atrans) {
+  if (a.nsplit < 1 || sg_total(a) > 0x7fffffff || a.ksplit % 64 != 0 || a.ksplit <= 0) return false;
+  if (atrans) {
+    if (a.K * a.lda * 2 >= 0x80000000ll) return false;
+    if (a.M % 8 != 0 && a.lda < (a.M + 7) / 8 * 8) return false;
+  } else if (kSgTile * a.lda * 2 >= 0x80000000ll) {
+    return false;
+  }
+  if (a.K * a.ldb * 2 >= 0x80000000ll) return false;
+  if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return false;
+  if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return false;
+  return hilo_ok(a);
+}
+
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const int64_t ntm = (a.M + kSgTile - 1) / kSgTile, ntn = (a.N + kSgTile - 1) / kSgTile;
-  const int64_t total = ntm * ntn * a.nsplit;
-  if (a.nsplit < 1 || total > 0x7fffffff || a.ksplit % 64 != 0 || a.ksplit <= 0) return hipErrorInvalidValue;
-  // the kernel's 32-bit offsets: every descriptor it forms spans less than 2^31 bytes, so the
-  // offset 2^31 it uses for masked elements is out of range
-  if (kSgTile * a.lda * 2 >= 0x80000000ll || a.K * a.ldb * 2 >= 0x80000000ll) return hipErrorInvalidValue;
-  if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
-  if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
-  if (!hilo_ok(a)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sgemm_kernel<false>, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
+  if (!sg_args_ok(a, false)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sgemm_kernel<false>, dim3((unsigned)sg_total(a)), dim3(kSgThreads), 0, st, a);
   return hipGetLastError();
 }
 
 // The same with A given transposed: At [K][lda], M contiguous.
 hipError_t launch_sgemm_at(const SgArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const int64_t ntm = (a.M + kSgTile - 1) / kSgTile, ntn = (a.N + kSgTile - 1) / kSgTile;
-  const int64_t total = ntm * ntn * a.nsplit;
-  if (a.nsplit < 1 || total > 0x7fffffff || a.ksplit % 64 != 0 || a.ksplit <= 0) return hipErrorInvalidValue;
-  if (a.K * a.lda * 2 >= 0x80000000ll || a.K * a.ldb * 2 >= 0x80000000ll) return hipErrorInvalidValue;
-  if (a.M % 8 != 0 && a.lda < (a.M + 7) / 8 * 8) return hipErrorInvalidValue;
-  if (a.C != nullptr && kSgTile * a.ldc * 4 >= 0x80000000ll) return hipErrorInvalidValue;
-  if (a.C == nullptr && (a.out == nullptr || kSgTile * a.ldo * 4 >= 0x80000000ll)) return hipErrorInvalidValue;
-  if (!hilo_ok(a)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sgemm_kernel<true>, dim3((unsigned)total), dim3(kSgThreads), 0, st, a);
+  if (!sg_args_ok(a, true)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sgemm_kernel<true>, dim3((unsigned)sg_total(a)), dim3(kSgThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -401,6 +441,17 @@ hipError_t launch_rowsum(const bf16_t* g, int64_t ld, int64_t rows, int64_t cols
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, g, ld, rows, cols, out,
                      n_valid, mean ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Two products in one launch: p0 as launch_sgemm takes it, p1 as launch_sgemm_at.
+hipError_t launch_sgemm_pair(const SgArgs& p0, const SgArgs& p1, hipStream_t st) {
+  if (p0.M <= 0 || p0.N <= 0) return launch_sgemm_at(p1, st);
+  if (p1.M <= 0 || p1.N <= 0) return launch_sgemm(p0, st);
+  if (!sg_args_ok(p0, false) || !sg_args_ok(p1, true)) return hipErrorInvalidValue;
+  const int64_t total = (sg_total(p0) + 7) / 8 * 8 + sg_total(p1);
+  if (total > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sgemm_pair_kernel, dim3((unsigned)total), dim3(kSgThreads), 0, st, p0, p1);
   return hipGetLastError();
 }
 

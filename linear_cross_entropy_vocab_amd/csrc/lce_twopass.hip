@@ -481,86 +481,83 @@ hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st
   return hipSuccess;
 }
 
-// One vocabulary block of pass 1: G^T of the block against all tokens, then grad_W[block] and
-// grad_b[block] from it.
-static hipError_t sg_pass1_block(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bf16_t* g, float* part1,
-                                 int64_t v0, int64_t rows, hipStream_t st) {
-  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
-  const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  const bf16_t* b = static_cast<const bf16_t*>(a.bias);
-  hipError_t e;
-  if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows, v0,
-                                  g, t.ldv, st)) != hipSuccess)
-    return e;
-  if (a.grad_W != nullptr) {
-    void* out = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
-                             : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
-    SgArgs m{};
-    m.A = g;
-    m.lda = t.ldv;
-    m.B = h;
-    m.ldb = a.H;
-    m.M = rows;
-    m.N = a.H;
-    m.K = a.BT;
-    m.ksplit = t.ksplit1;
-    m.nsplit = t.nsplit1;
-    m.n_valid = w.n_valid;
-    m.mean = a.mean ? 1 : 0;
-    if (t.nsplit1 > 1) {  // K-ranges into partial sums, then c * their sum into the rows
-      m.C = part1;
-      m.ldc = a.H;
-      m.split_stride = rows * a.H;
-      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
-      if ((e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, out, a.grad_w_f32, w.n_valid, a.mean,
-                                st)) != hipSuccess)
-        return e;
-    } else {
-      m.out = out;
-      m.out_f32 = a.grad_w_f32 ? 1 : 0;
-      m.ldo = a.H;
-      if ((e = launch_sgemm(m, st)) != hipSuccess) return e;
-    }
-  }
-  if (a.grad_b != nullptr &&
-      (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
-          hipSuccess)
-    return e;
-  return hipSuccess;
-}
-
-// Pass 1 (grad_W, grad_b) and, with `dinput`, grad_input in the same sweep (one-pass plan):
-// grad_input += G . W[block] from the block's stored G^T (read transposed), kept as hi + lo
-// between blocks and written as c * the sum by the last one.
+// Pass 1 (grad_W, grad_b) and, with `dinput`, grad_input in the same sweep (one-pass plan).
+// Per block of vb vocabulary rows: G^T of the block against all tokens (forward kernel,
+// kEpiDlogitsT); grad_W[block] = c G^T . hidden (directly, or over K-ranges of tokens into fp32
+// partial sums reduced into the rows); grad_b[block] = c row sums of G^T; with `dinput`,
+// grad_input += G . W[block] from the same G^T read transposed, kept as hi + lo between blocks
+// and written as c * the sum by the last block.  The two products of a block share one launch.
 static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bool dinput, hipStream_t st) {
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
   float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
   bf16_t* lo = reinterpret_cast<bf16_t*>(w.big + 256 + t.g1_bytes + t.part1_bytes);
+  const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bf16_t* b = static_cast<const bf16_t*>(a.bias);
   const int64_t nblk = (a.V + t.vb - 1) / t.vb;
   hipError_t e;
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t v0 = k * t.vb, rows = std::min(t.vb, a.V - v0);
-    if ((e = sg_pass1_block(a, w, t, g, part1, v0, rows, st)) != hipSuccess) return e;
-    if (!dinput) continue;
-    SgArgs m{};
-    m.A = g;  // G^T [rows][ldv]: A = G read transposed, K = the block's vocabulary rows
-    m.lda = t.ldv;
-    m.B = W + v0 * a.H;
-    m.ldb = a.H;
-    m.M = a.BT;
-    m.N = a.H;
-    m.K = rows;
-    m.ksplit = (rows + 63) / 64 * 64;
-    m.nsplit = 1;
-    m.out = a.grad_input;
-    m.ldo = a.H;
-    m.n_valid = w.n_valid;
-    m.mean = a.mean ? 1 : 0;
-    m.hilo = nblk == 1 ? 0 : (k == 0 ? 1 : (k == nblk - 1 ? 3 : 2));
-    m.lo = reinterpret_cast<uint16_t*>(lo);
-    m.ldlo = a.H;
-    if ((e = launch_sgemm_at(m, st)) != hipSuccess) return e;
+    if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows,
+                                    v0, g, t.ldv, st)) != hipSuccess)
+      return e;
+    void* wout = nullptr;
+    SgArgs mw{};  // grad_W[block] = c G^T . hidden
+    if (a.grad_W != nullptr) {
+      wout = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
+                          : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
+      mw.A = g;
+      mw.lda = t.ldv;
+      mw.B = h;
+      mw.ldb = a.H;
+      mw.M = rows;
+      mw.N = a.H;
+      mw.K = a.BT;
+      mw.ksplit = t.ksplit1;
+      mw.nsplit = t.nsplit1;
+      mw.n_valid = w.n_valid;
+      mw.mean = a.mean ? 1 : 0;
+      if (t.nsplit1 > 1) {  // K-ranges into partial sums, reduced into the rows below
+        mw.C = part1;
+        mw.ldc = a.H;
+        mw.split_stride = rows * a.H;
+      } else {
+        mw.out = wout;
+        mw.out_f32 = a.grad_w_f32 ? 1 : 0;
+        mw.ldo = a.H;
+      }
+    }
+    SgArgs mi{};  // grad_input += G . W[block]
+    if (dinput) {
+      mi.A = g;  // G^T [rows][ldv]: A = G read transposed, K = the block's vocabulary rows
+      mi.lda = t.ldv;
+      mi.B = W + v0 * a.H;
+      mi.ldb = a.H;
+      mi.M = a.BT;
+      mi.N = a.H;
+      mi.K = rows;
+      mi.ksplit = (rows + 63) / 64 * 64;
+      mi.nsplit = 1;
+      mi.out = a.grad_input;
+      mi.ldo = a.H;
+      mi.n_valid = w.n_valid;
+      mi.mean = a.mean ? 1 : 0;
+      mi.hilo = nblk == 1 ? 0 : (k == 0 ? 1 : (k == nblk - 1 ? 3 : 2));
+      mi.lo = reinterpret_cast<uint16_t*>(lo);
+      mi.ldlo = a.H;
+    }
+    if (a.grad_W != nullptr && dinput) e = launch_sgemm_pair(mw, mi, st);
+    else if (a.grad_W != nullptr) e = launch_sgemm(mw, st);
+    else if (dinput) e = launch_sgemm_at(mi, st);
+    if (e != hipSuccess) return e;
+    if (a.grad_W != nullptr && t.nsplit1 > 1 &&
+        (e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, wout, a.grad_w_f32, w.n_valid, a.mean, st)) !=
+            hipSuccess)
+      return e;
+    if (a.grad_b != nullptr &&
+        (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
+            hipSuccess)
+      return e;
   }
   return hipSuccess;
 }
