@@ -303,6 +303,14 @@ double cost_gemm(int64_t M, int64_t N, int64_t K, int64_t ksplit) {
   const int64_t tiles = cdiv(M, 256) * cdiv(N, 256) * ns;
   return (double)cdiv(tiles, kPlanCUs) * (double)cdiv(std::min(K, ksplit), 64) + kLaunchStages;
 }
+// two products in one grouped launch: the longer of one tile of the first and the whole work
+// spread over the device (workgroups are dispatched as compute units free up)
+double cost_pair(int64_t M0, int64_t N0, int64_t K0, int64_t ks0, int64_t M1, int64_t N1, int64_t K1) {
+  const double s0 = (double)cdiv(std::min(K0, ks0), 64), s1 = (double)cdiv(K1, 64);
+  const double work = (double)(cdiv(M0, 256) * cdiv(N0, 256) * cdiv(K0, ks0)) * s0 +
+                      (double)(cdiv(M1, 256) * cdiv(N1, 256)) * s1;
+  return std::max(s0, work / (double)kPlanCUs) + kLaunchStages;
+}
 // streaming bytes at about 4 TB/s against a stage of about 1.4 us
 double cost_bytes(double bytes) { return bytes / 4e12 / 1.4e-6; }
 }  // namespace
@@ -416,8 +424,9 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
         const double red = ns1 > 1 ? cost_bytes((double)V * H * (4.0 * ns1 + 4.0)) + (double)n * kLaunchStages : 0.0;
         // the running sum's traffic (2-byte accesses: counted at half the streaming rate)
         const double sum_bytes = (double)BT * H * (8.0 * (double)n - 6.0);
-        const double c = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_gemm(vb, H, BT, ks1) + cost_gemm(BT, H, vb, vb)) +
-                         cost_dl(BT, last, H) + cost_gemm(last, H, BT, ks1) + cost_gemm(BT, H, last, last) +
+        // (grad_W and grad_input of a block in one grouped launch)
+        const double c = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_pair(vb, H, BT, ks1, BT, H, vb)) +
+                         cost_dl(BT, last, H) + cost_pair(last, H, BT, ks1, BT, H, last) +
                          cost_bytes((double)V * t.ldv * 2) + red + 2.0 * cost_bytes(sum_bytes);
         if (best < 0 || c < best) {
           best = c;
