@@ -153,7 +153,8 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     lce_fwd_bwd_chunked (the token-chunked composition; bf16 only).  grad_weight_fp32 (bf16
     inputs) makes grad_weight a float32 tensor (in the chunked composition it then holds the
     sum over the chunks directly);
-    method="auto" takes the chunked composition for bf16 with H > 3072, else the fused path.
+    method="auto" takes the fused path (the one within one logits chunk of extra memory; measured
+    as fast as the composition at H = 4096 and faster at 2304).
     sort_vocab (with filter_eps > 0) orders the vocabulary by average logit before filtering.
     """
     if sort_vocab and not filter_eps > 0.0:
@@ -161,11 +162,10 @@ def lce_fwd_bwd(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional[torch
     if method not in ("fused", "chunked", "auto"):
         raise ValueError(f"method must be 'fused', 'chunked' or 'auto', not {method!r}")
     if method == "auto":
-        # above H = 1024 the fused path's backward recomputes the logits twice more on stored
-        # dlogits blocks (10 BT V H flops against the composition's 6); measured, it is 1.26x
-        # faster than the composition at H = 2304 (with 5% of its memory), 1.3x slower at 4096
-        method = "chunked" if (hidden.dtype == torch.bfloat16 and hidden.shape[1] > 3072
-                               and filter_eps == 0.0 and events is None) else "fused"
+        # the fused path's one-pass backward above H = 1024 measured 73.8 vs 74.1 ms (H = 4096)
+        # and 35.5 vs 62.0 ms (H = 2304) against the composition, with a tenth of its memory;
+        # at H = 1024 the composition is faster but needs 6.7x the memory
+        method = "fused"
     chunked = method == "chunked"
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be 'mean' or 'sum', not {reduction!r}")
