@@ -178,7 +178,122 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
   // m0 + 128 wm + 32 vb + 8 (r / 4) + 4 (l / 32) + r % 4
   const int64_t ncol = n0 + 64 * wn + (lane & 31);
   const int mrow0 = 128 * wm + 4 * (lane >> 5);
-  if (p.C != nullptr) {
+  // Rows of whole 8-element groups: each 32-row block of the wave's results goes through its
+  // own LDS region (waves 0-3 in the A buffers, 4-7 in the B buffers; rows 72 floats apart, so
+  // the two row groups of a write fall on disjoint banks), and each lane then handles 8
+  // consecutive columns of a row with 16-byte global accesses (8x fewer than one per element).
+  const bool vec = p.N % 8 == 0 && (p.C != nullptr ? p.ldc % 8 == 0
+                                                     : p.ldo % 8 == 0 && (p.hilo == 0 || p.ldlo % 8 == 0));
+  if (vec) {
+    constexpr int kPitch = 72;
+    __syncthreads();  // every wave has read its last stage: the buffers are free
+    float* reg = reinterpret_cast<float*>(w < 4 ? &sA[0][0] : &sB[0][0]) + (w & 3) * 32 * kPitch;
+    const long long nvalid = *p.n_valid;
+    const float cs = p.C != nullptr ? 1.f : (p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f);
+    const int rl = lane >> 3, cl = 8 * (lane & 7);  // this lane: rows 8 i + rl, columns cl .. cl + 7
+    const int64_t n8 = n0 + 64 * wn + cl;
+    const bool cok = n8 < p.N;
+    const int es = p.C != nullptr ? 4 : (p.out_f32 ? 4 : 2);
+    const int64_t ld = p.C != nullptr ? p.ldc : p.ldo;
+    char* const base = p.C != nullptr ? reinterpret_cast<char*>(p.C + (int64_t)split * p.split_stride + m0 * p.ldc)
+                                      : static_cast<char*>(p.out) + m0 * p.ldo * es;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(base, mrows * ld * es);
+    const __amdgpu_buffer_rsrc_t rl16 =
+        make_rsrc(p.hilo != 0 ? reinterpret_cast<char*>(p.lo + m0 * p.ldlo) : base, p.hilo != 0 ? mrows * p.ldlo * 2 : 0);
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + 32 * nb + (lane & 31)] = acc[vb][nb][r];
+      float v[4][8];
+      uint32_t off[4], offl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl);
+        const float4 b = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl + 4);
+        v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+        v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+        const int m = 128 * wm + 32 * vb + 8 * i + rl;
+        off[i] = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
+        offl[i] = cok ? (uint32_t)((m * p.ldlo + n8) * 2) : 0x80000000u;
+      }
+      if (p.C != nullptr) {  // fp32 partial sums, written or added
+        if (p.accumulate) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[i], 0, 0));
+            const float4 b =
+                __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)(off[i] + 16), 0, 0));
+            v[i][0] += a.x; v[i][1] += a.y; v[i][2] += a.z; v[i][3] += a.w;
+            v[i][4] += b.x; v[i][5] += b.y; v[i][6] += b.z; v[i][7] += b.w;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][0], v[i][1], v[i][2], v[i][3])),
+                                                 ro, (int)off[i], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][4], v[i][5], v[i][6], v[i][7])),
+                                                 ro, (int)(off[i] + 16), 0, 0);
+        }
+      } else if (p.hilo != 0) {  // running sum hi + lo (see the scalar path below)
+        if (p.hilo != 1) {
+          u32x4_t hv[4], lv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[i], 0, 0);
+            lv[i] = __builtin_amdgcn_raw_buffer_load_b128(rl16, (int)offl[i], 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t hw = hv[i][e >> 1], lw = lv[i][e >> 1];
+              const bf16_t h16 = (bf16_t)((e & 1) ? (hw >> 16) : (hw & 0xffffu));
+              const bf16_t l16 = (bf16_t)((e & 1) ? (lw >> 16) : (lw & 0xffffu));
+              v[i][e] += bf2f(h16) + bf2f(l16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4_t ho, lo;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            if (p.hilo == 3) {
+              ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
+            } else {
+              const bf16_t h0 = f2bf(v[i][e]), h1 = f2bf(v[i][e + 1]);
+              ho[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+              lo[e >> 1] = (uint32_t)f2bf(v[i][e] - bf2f(h0)) | ((uint32_t)f2bf(v[i][e + 1] - bf2f(h1)) << 16);
+            }
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
+          if (p.hilo != 3) __builtin_amdgcn_raw_buffer_store_b128(lo, rl16, (int)offl[i], 0, 0);
+        }
+      } else if (p.out_f32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t, make_float4(cs * v[i][0], cs * v[i][1], cs * v[i][2], cs * v[i][3])), ro,
+              (int)off[i], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4_t, make_float4(cs * v[i][4], cs * v[i][5], cs * v[i][6], cs * v[i][7])), ro,
+              (int)(off[i] + 16), 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4_t ho;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
+        }
+      }
+      asm volatile("" ::: "memory");  // (the region is rewritten for the next block)
+    }
+  } else if (p.C != nullptr) {
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(p.C + (int64_t)split * p.split_stride + m0 * p.ldc, mrows * p.ldc * 4);
 #pragma unroll

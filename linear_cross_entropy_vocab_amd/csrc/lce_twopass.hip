@@ -290,7 +290,11 @@ hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStrea
 // tiles, plus a fixed launch cost; the dlogits kernel's tiles are 256 x 256 x H.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int64_t kSgMinH = 1025;       // below: the pipelined kernels (measured faster at H = 1024)
+// Against the pipelined kernels (H <= 1024): at H = 1024 the one-pass plan measured faster
+// (backward 84.9 against 90.5 ms at the headline) and the two-pass plan slower (grad_W 56.9
+// against 46.2 ms); narrower rows keep the pipelined kernels (not measured).
+constexpr int64_t kSgMinH = 1024;       // the stored-operand plans from here
+constexpr int64_t kSgTwoPassMinH = 1025;  // the two-pass plan from here (one pass only at 1024)
 constexpr double kLaunchStages = 4.0;   // launch and drain of one kernel
 constexpr double kDlFactor = 1.25;      // a dlogits tile stage against a GEMM stage (exp and stores)
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -391,13 +395,12 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
       }
     }
   }
-  if (best2 < 0) return t;
+  if (best2 < 0 && H >= kSgTwoPassMinH) return t;
   t.ldt = round_up(t.vr, 64);
   t.g_bytes = ws_align((size_t)t.tb * (size_t)t.ldt * 2);
   t.part_bytes = ws_align((size_t)t.nsplit * (size_t)t.tb * (size_t)H * 4);
   t.bytes = 256 + std::max(pass1, t.g_bytes + t.part_bytes);
-  if (t.bytes > avail + 4096) return t;
-  t.on = true;
+  t.on = best2 >= 0 && t.bytes <= avail + 4096 && H >= kSgTwoPassMinH;
   // One pass instead: pass 1's blocks also give grad_input, summed over the blocks as hi + lo
   // (hi in the output, lo here), so the dlogits are formed once: 8 instead of 10 BT V H flops.
   // Taken when the cost model prefers it with the smaller blocks the lo buffer leaves.
@@ -436,7 +439,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
         }
       }
     }
-    if (best >= 0 && best < best1 + best2) {
+    if (best >= 0 && (!t.on || best < best1 + best2)) {
       t.one = true;
       t.lo_bytes = lo;
       t.vb = vb1;
@@ -445,9 +448,10 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
       t.g1_bytes = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
       t.part1_bytes = t.nsplit1 > 1 ? ws_align((size_t)t.nsplit1 * (size_t)t.vb * (size_t)H * 4) : 0;
       t.bytes = 256 + t.g1_bytes + t.part1_bytes + t.lo_bytes;
-      if (t.bytes > avail + 4096) t.on = false;
+      t.on = t.bytes <= avail + 4096;
     }
   }
+  if (!t.on) t.one = false;
   return t;
 }
 

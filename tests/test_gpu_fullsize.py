@@ -130,14 +130,13 @@ def test_rows_full_size_headline(saved):
 
 @pytest.mark.parametrize("name", ["headline", "gemma_like"])
 def test_filtered_tiny_eps_full_size(name):
-    """Gradient filtering at full size (pipelined backward at the headline, the two-pass
-    stored-dlogits backward at gemma_like): with eps below every |dlogit| no tile is skipped
-    and the filtered call reproduces the exact call (bit for bit at the headline, where both
-    run the same kernels; within the bf16 tolerances at gemma_like, where the exact call's
-    two-pass backward runs on the stored-operand GEMM and the filtered one on the
-    stored-dlogits GEMMs that test each tile); with vocabulary sorting on top, the loss and
-    gradients (returned in the original vocabulary order) stay within the bf16 tolerances of
-    the exact call."""
+    """Gradient filtering at full size (the pipelined backward's filtering instantiation at the
+    headline, the stored-dlogits GEMMs at gemma_like): with eps below every |dlogit| no tile is
+    skipped, the loss is the exact call's bit for bit (the forward is shared) and the gradients
+    stay within a quarter of the bf16 tolerance of it (the exact call's backward runs on the
+    stored-operand GEMM, with its own rounding of the dlogits and of the sums); with vocabulary
+    sorting on top, the loss and gradients (returned in the original vocabulary order) stay
+    within the bf16 tolerances of the exact call."""
     c = CONFIGS[name]
     print(f"full-size filtering, tiny eps: {name} BT={c.BT} H={c.H} V={c.V}", flush=True)
     inp = make_config(name)
@@ -154,9 +153,7 @@ def test_filtered_tiny_eps_full_size(name):
     keys = ["loss", "grad_input", "grad_weight"] + (["grad_bias"] if b is not None else [])
     tol = TOL[c.dtype]
     for k in keys:
-        if c.H <= 1024:
-            assert torch.equal(exact[k], filt[k]), k
-        elif k == "loss":
+        if k == "loss":
             assert torch.equal(exact[k], filt[k]), k  # (the forward is shared)
         else:
             e = float((filt[k].float() - exact[k].float()).norm() / exact[k].float().norm())
