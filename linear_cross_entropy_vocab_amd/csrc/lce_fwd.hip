@@ -448,40 +448,60 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     if constexpr (DLT) {
       // Lane (t, half) holds token t's dlogits for vocabulary rows vrow + vb 32 + 8 rr + e.
       // Lanes t and t ^ 1 swap one value per pair of rows (e, e + 1), so that the even lane
-      // holds row e and the odd lane row e + 1, each for both tokens: one 4-byte store of two
-      // adjacent tokens per pair.  Rows past V fall outside the store descriptor.
+      // holds row e and the odd lane row e + 1, each for both tokens; these 4-byte pairs go to
+      // an LDS block of the wave's 32 rows x 64 tokens (the stage buffer the last K step read:
+      // waves 0-3 in A's, 4-7 in B's), and each lane then stores 8 tokens of one row with one
+      // 16-byte store.  Rows past V fall outside the store descriptor; token groups at or past
+      // ld are not stored.
+      constexpr int kPitch = 144;  // bytes per staged row (64 tokens and 16 bytes of padding)
       const bool odd = (ln & 1) != 0;
       const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + tl.v0 * ld, (V - tl.v0) * ld * 2);
+      __syncthreads();  // every wave has read the last K step's buffers
+      char* const stg = (w < 4 ? sA[buf ^ 1] : sB[buf ^ 1]) + (w & 3) * 32 * kPitch;
+      float ra2[2], fac2[2];
+      int cy2[2];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const int trow = wt * 64 + tb * 32 + (ln & 31);
-        const float2 tk = s_tok[trow];
+        const float2 tk = s_tok[wt * 64 + tb * 32 + (ln & 31)];
         const int yv = __float_as_int(tk.y) - 1;
-        const float ra = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
-        const float fac = 1.f + 2.f * mu * tk.x;
-        const int cy = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
-        const int64_t col = tl.t0 + trow - (odd ? 1 : 0);
-        const bool col_ok = col < ld;
+        ra2[tb] = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
+        fac2[tb] = 1.f + 2.f * mu * tk.x;
+        cy2[tb] = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+      }
+      const int rl = ln >> 3, cl = 8 * (ln & 7);  // read-back: rows 8 i + rl, tokens cl .. cl + 7
+      const int64_t tcol = tl.t0 + wt * 64 + cl;
+      const bool col_ok = tcol + 8 <= ld;
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb)
+      for (int vb = 0; vb < 4; ++vb) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
               const int c0 = vb * 32 + 8 * rr + e;
-              const float z0 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e], kLog2e, ra)), fac,
-                                    c0 == cy ? -1.f : 0.f);
-              const float z1 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e + 1], kLog2e, ra)), fac,
-                                    c0 + 1 == cy ? -1.f : 0.f);
+              const float z0 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e], kLog2e, ra2[tb])), fac2[tb],
+                                    c0 == cy2[tb] ? -1.f : 0.f);
+              const float z1 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e + 1], kLog2e, ra2[tb])),
+                                    fac2[tb], c0 + 1 == cy2[tb] ? -1.f : 0.f);
               const float send = odd ? z0 : z1;
               // quad_perm (1, 0, 3, 2): the value of lane ln ^ 1
               const float recv = __int_as_float(
                   __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
               const uint32_t v = odd ? pack_bf2(recv, z1) : pack_bf2(z0, recv);
-              const int row = vrow + c0 + (odd ? 1 : 0);
-              const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * ld + col) * 2) : 0x80000000u;
-              __builtin_amdgcn_raw_buffer_store_b32(v, rz, (int)off, 0, 0);
+              // staged row 4 half + 8 rr + e (+1 odd), tokens tb 32 + t (even lane's t)
+              const int srow = 4 * (ln >> 5) + 8 * rr + e + (odd ? 1 : 0);
+              const int scol = tb * 32 + (ln & 31) - (odd ? 1 : 0);
+              *reinterpret_cast<uint32_t*>(stg + srow * kPitch + 2 * scol) = v;
             }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t q = *reinterpret_cast<const u32x4_t*>(stg + (8 * i + rl) * kPitch + 2 * cl);
+          const int row = wv * 128 + vb * 32 + 8 * i + rl;  // of the tile
+          const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * ld + tcol) * 2) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(q, rz, (int)off, 0, 0);
+        }
+        asm volatile("" ::: "memory");  // (the block is rewritten for the next vb)
       }
       (void)lse_part;
       __syncthreads();  // every wave has read s_bias and s_tok before the next tile rewrites them
