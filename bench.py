@@ -264,10 +264,17 @@ def _stage_roofline(stage_ms, btvh, dom=None):
         dom = max(algo, key=lambda n: stage_ms[n])
     a = algo[dom] / (stage_ms[dom] * 1e-3) / 1e12
     e = execd[dom] / (stage_ms[dom] * 1e-3) / 1e12
-    return dom, {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                 "frac": a / PEAK_BF16_TFLOPS, "kernel": dom, "algorithmic_flops_per_launch": algo[dom],
-                 "achieved_executed": e, "frac_executed": e / PEAK_BF16_TFLOPS,
-                 "executed_flops_per_launch": execd[dom]}
+    roof = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": a / PEAK_BF16_TFLOPS, "kernel": dom, "algorithmic_flops_per_launch": algo[dom],
+            "achieved_executed": e, "frac_executed": e / PEAK_BF16_TFLOPS,
+            "executed_flops_per_launch": execd[dom]}
+    if dom == "bwd_dinput" and one_pass_backward(stage_ms):
+        # the stage is the whole backward: per vocabulary block one transposed-dlogits forward
+        # launch and one grouped grad_W + grad_input GEMM launch (plus a partial-sum reduce)
+        dom = "bwd_onepass"
+        roof["kernel"] = dom
+        roof["launch"] = "one backward stage (per vocabulary block: transposed dlogits, grouped grad_W + grad_input GEMM)"
+    return dom, roof
 
 
 def vendor_gemm_reference(torch, h, W, reps: int = 3) -> dict:
