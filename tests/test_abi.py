@@ -52,6 +52,21 @@ def test_workspace_within_one_logits_chunk(lib, name):
     assert 0 < ws <= budget, (ws, budget)
 
 
+@pytest.mark.parametrize("H", [1024, 1152, 2048, 2304, 4096])
+def test_workspace_within_budget_over_shapes(lib, H):
+    """The backward's block plans (one pass from H = 1024, two passes above) size their region
+    to what the forward leaves of the one-chunk budget: over a grid of token and vocabulary
+    counts the workspace never exceeds it (budget of "Fused Linear Cross-Entropy: The Math,
+    the Memory Wall, and Two Ways Around It", "The chunk-size trick")."""
+    for BT in (1, 64, 130, 700, 4096, 16384, 65535):
+        for V in (1, 300, 3001, 20000, 151936, 256128):
+            ws = lib.lce_fwd_bwd_workspace_bytes(BT, H, V, BF16, 0)
+            budget = liger_chunk_plan(BT, V, H)["chunk_bytes"]
+            base = 16 + 8 * BT + 16 * ((BT + 255) // 256) + 8 * BT + 4 * V + 4 * BT * ((V + 255) // 256)
+            # (the forward's own pieces come first; the plans only add within the budget)
+            assert ws <= max(budget, base + 64 * 256), (BT, H, V, ws, budget)
+
+
 def test_workspace_sizes(lib):
     assert lib.lce_fwd_bwd_workspace_bytes(-1, 64, 10, BF16, 0) == 0
     assert lib.lce_fwd_bwd_workspace_bytes(10, 12, 10, BF16, 0) == 0   # H % 8 != 0

@@ -49,7 +49,7 @@ CASES = [
     # (dtype, BT, H, V, bias_std, z_loss, reduction, ignore_frac, seed)
     ("bf16", 200, 128, 1000, None, 0.0, "mean", 0.2, 11),
     ("bf16", 333, 256, 3001, 0.1, 1e-3, "sum", 0.1, 12),
-    ("bf16", 130, 1024, 700, None, 0.0, "mean", 0.0, 13),
+    ("bf16", 130, 1024, 700, None, 0.0, "mean", 0.0, 13),   # one-pass backward, one vocabulary block
     ("bf16", 97, 200, 513, 0.2, 1e-2, "mean", 0.3, 14),
     ("bf16", 100, 1152, 600, 0.1, 1e-4, "mean", 0.1, 15),
     ("bf16", 65, 2304, 257, None, 0.0, "sum", 0.05, 16),
@@ -57,11 +57,13 @@ CASES = [
     ("f32", 150, 64, 2000, None, 0.0, "sum", 0.2, 18),
     ("bf16", 1, 8, 5, None, 0.0, "mean", 0.0, 19),
     ("bf16", 64, 64, 1, 0.1, 0.0, "mean", 0.0, 20),
-    # H > 1024 with room in the budget: the two-pass backward, with ragged vocabulary and
-    # token blocks (3 vocabulary blocks and 10 token blocks; 2 and 5)
+    # H >= 1024 with room in the budget: the backward on stored dlogits blocks.  One pass
+    # (grad_input summed over the vocabulary blocks as hi + lo): 9, 4 and 3 blocks, the last
+    # ragged; two passes: one vocabulary block, two token blocks
+    ("bf16", 700, 1024, 20000, 0.1, 1e-4, "mean", 0.1, 25),
     ("bf16", 600, 1152, 9000, 0.1, 1e-4, "mean", 0.1, 21),
     ("bf16", 300, 2112, 5000, None, 0.0, "sum", 0.2, 22),
-    ("bf16", 2000, 1280, 300, 0.2, 1e-3, "mean", 0.3, 23),   # two token blocks of 1024, one vocabulary block
+    ("bf16", 2000, 1280, 300, 0.2, 1e-3, "mean", 0.3, 23),
     ("bf16", 64, 1088, 70000, None, 0.0, "mean", 0.1, 24),   # budget too small for a block: column-chunked kernel
 ]
 
@@ -136,7 +138,8 @@ def test_minus_inf_bias_tiles_vs_oracle(case):
         assert int(torch.count_nonzero(g)) == 0, k
 
 
-@pytest.mark.parametrize("shape", [(120, 256, 900), (600, 1152, 9000)], ids=["pipelined", "two-pass"])
+@pytest.mark.parametrize("shape", [(120, 256, 900), (600, 1152, 9000), (700, 1024, 20000)],
+                         ids=["pipelined", "one-pass", "one-pass-1024"])
 def test_grad_subsets(shape):
     BT, H, V = shape
     inp = make_fused(BT, H, V, dtype="bf16", seed=21, bias_std=0.1, ignore_frac=0.1)
@@ -165,7 +168,8 @@ def test_fused_grad_weight_fp32():
         assert torch.equal(a32["grad_weight"].to(torch.bfloat16), a16["grad_weight"]), shape
 
 
-@pytest.mark.parametrize("shape", [(333, 256, 3001), (600, 1152, 9000)], ids=["pipelined", "two-pass"])
+@pytest.mark.parametrize("shape", [(333, 256, 3001), (600, 1152, 9000), (700, 1024, 20000), (2000, 1280, 300)],
+                         ids=["pipelined", "one-pass", "one-pass-1024", "two-pass"])
 def test_deterministic_bits(shape):
     inp = make_fused(*shape, dtype="bf16", seed=12, bias_std=0.1, ignore_frac=0.1, z_loss=1e-3)
     a = run_fused(inp)
