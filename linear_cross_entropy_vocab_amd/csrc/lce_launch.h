@@ -72,7 +72,7 @@ struct SgPlan {
   int nsplit;
   size_t g_bytes, part_bytes, bytes;
   // one pass: grad_input is summed over pass 1's vocabulary blocks from the same stored
-  // transposed dlogits (hi in the output, lo_bytes of bf16 remainders), and pass 2 is dropped
+  // transposed dlogits (hi in the output, lo_bytes of 8-bit remainder codes), and pass 2 is dropped
   bool one;
   size_t lo_bytes;
 };
@@ -195,12 +195,13 @@ struct SgArgs {
   int out_f32;
   const int64_t* n_valid;
   int mean;
-  // Running sum over several launches (bf16 out only, one K-range): the sum is kept as
-  // hi + lo, hi (bf16) in `out` and lo (bf16, the rounding remainder) in `lo`, about 16
-  // significant bits.  hilo = 1: the first launch writes hi and lo; 2: later launches add;
-  // 3: the last one adds and writes c * sum to `out`; 0: plain output (c * C).
+  // Running sum over several launches (bf16 out only, one K-range, N a multiple of 8): the
+  // sum is kept as hi (bf16, in `out`) and an 8-bit code of the remainder s - hi in `lo` (in
+  // steps of 2^-8 of hi's last place: about 16 significant bits).  hilo = 1: the first launch
+  // writes both; 2: later launches add; 3: the last one adds and writes c * sum to `out`;
+  // 0: plain output (c * C).
   int hilo;
-  uint16_t* lo;
+  uint8_t* lo;
   int64_t ldlo;
 };
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);

@@ -41,6 +41,23 @@ __device__ __forceinline__ bf16x8_t sg_tr_pair(const char* p0, const char* p1) {
 // loaded and read like B's (planes of 32 M-columns, transposed reads).
 constexpr int kSgStage = kSgTile * 128;  // 32 KiB: A (256 rows x 64 K) or B (64 K x 256 columns)
 
+// Running sum over launches: s = hi + q 2^(e - 142), hi the bf16 nearest to s (exponent field
+// e) and q an int8, the remainder s - hi (at most half of hi's unit in the last place, 2^(e -
+// 134)) in steps of 2^-8 of that unit, so s keeps about 16 significant bits.  Sums below 2^-111
+// keep hi only.
+__device__ __forceinline__ float rem_step(uint32_t hi) {  // 2^(e - 142)
+  const uint32_t e = (hi >> 7) & 0xffu;
+  return e >= 16 ? __uint_as_float((e - 15u) << 23) : 0.f;
+}
+__device__ __forceinline__ float rem_inv(uint32_t hi) {  // 2^(142 - e)
+  const uint32_t e = (hi >> 7) & 0xffu;
+  return e >= 16 ? __uint_as_float((269u - e) << 23) : 0.f;
+}
+__device__ __forceinline__ uint32_t rem_code(float s, uint32_t hi) {  // q as a byte
+  const float q = fminf(fmaxf(rintf((s - bf2f((bf16_t)hi)) * rem_inv(hi)), -128.f), 127.f);
+  return (uint32_t)(int32_t)q & 0xffu;
+}
+
 __device__ __forceinline__ uint32_t sg_tiles(const SgArgs& p) {
   return (uint32_t)((p.M + kSgTile - 1) / kSgTile) * (uint32_t)((p.N + kSgTile - 1) / kSgTile) * (uint32_t)p.nsplit;
 }
@@ -198,8 +215,8 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
     char* const base = p.C != nullptr ? reinterpret_cast<char*>(p.C + (int64_t)split * p.split_stride + m0 * p.ldc)
                                       : static_cast<char*>(p.out) + m0 * p.ldo * es;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(base, mrows * ld * es);
-    const __amdgpu_buffer_rsrc_t rl16 =
-        make_rsrc(p.hilo != 0 ? reinterpret_cast<char*>(p.lo + m0 * p.ldlo) : base, p.hilo != 0 ? mrows * p.ldlo * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rl8 =
+        make_rsrc(p.hilo != 0 ? reinterpret_cast<char*>(p.lo + m0 * p.ldlo) : base, p.hilo != 0 ? mrows * p.ldlo : 0);
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb) {
 #pragma unroll
@@ -217,7 +234,7 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
         v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
         const int m = 128 * wm + 32 * vb + 8 * i + rl;
         off[i] = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
-        offl[i] = cok ? (uint32_t)((m * p.ldlo + n8) * 2) : 0x80000000u;
+        offl[i] = cok ? (uint32_t)(m * p.ldlo + n8) : 0x80000000u;
       }
       if (p.C != nullptr) {  // fp32 partial sums, written or added
         if (p.accumulate) {
@@ -237,39 +254,45 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][4], v[i][5], v[i][6], v[i][7])),
                                                  ro, (int)(off[i] + 16), 0, 0);
         }
-      } else if (p.hilo != 0) {  // running sum hi + lo (see the scalar path below)
+      } else if (p.hilo != 0) {  // running sum hi + q (rem_step above): 16 + 8 bytes per lane
         if (p.hilo != 1) {
-          u32x4_t hv[4], lv[4];
+          u32x4_t hv[4];
+          uint32_t lv[4][2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             hv[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[i], 0, 0);
-            lv[i] = __builtin_amdgcn_raw_buffer_load_b128(rl16, (int)offl[i], 0, 0);
+            const auto l2 = __builtin_amdgcn_raw_buffer_load_b64(rl8, (int)offl[i], 0, 0);
+            lv[i][0] = l2[0];
+            lv[i][1] = l2[1];
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const uint32_t hw = hv[i][e >> 1], lw = lv[i][e >> 1];
-              const bf16_t h16 = (bf16_t)((e & 1) ? (hw >> 16) : (hw & 0xffffu));
-              const bf16_t l16 = (bf16_t)((e & 1) ? (lw >> 16) : (lw & 0xffffu));
-              v[i][e] += bf2f(h16) + bf2f(l16);
+              const uint32_t h16 = (e & 1) ? (hv[i][e >> 1] >> 16) : (hv[i][e >> 1] & 0xffffu);
+              const int32_t q = (int32_t)(int8_t)((lv[i][e >> 2] >> (8 * (e & 3))) & 0xffu);
+              v[i][e] += bf2f((bf16_t)h16) + (float)q * rem_step(h16);
             }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          u32x4_t ho, lo;
+          u32x4_t ho;
+          uint32_t lo[2] = {0u, 0u};
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             if (p.hilo == 3) {
               ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
             } else {
-              const bf16_t h0 = f2bf(v[i][e]), h1 = f2bf(v[i][e + 1]);
-              ho[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-              lo[e >> 1] = (uint32_t)f2bf(v[i][e] - bf2f(h0)) | ((uint32_t)f2bf(v[i][e + 1] - bf2f(h1)) << 16);
+              const uint32_t h0 = f2bf(v[i][e]), h1 = f2bf(v[i][e + 1]);
+              ho[e >> 1] = h0 | (h1 << 16);
+              lo[e >> 2] |= (rem_code(v[i][e], h0) | (rem_code(v[i][e + 1], h1) << 8)) << (8 * (e & 2));
             }
           }
           __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
-          if (p.hilo != 3) __builtin_amdgcn_raw_buffer_store_b128(lo, rl16, (int)offl[i], 0, 0);
+          if (p.hilo != 3) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo[0], lo[1]}, rl8, (int)offl[i], 0, 0);
+          }
         }
       } else if (p.out_f32) {
 #pragma unroll
@@ -318,52 +341,6 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
         for (int r = 0; r < 16; ++r)
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[vb][nb][r] + old[r]), rc,
                                                 (int)off[r], 0, 0);
-      }
-    }
-  } else if (p.hilo != 0) {
-    // running sum over launches as hi + lo (bf16 each): s = C + hi + lo, then either the next
-    // hi = bf16(s) and lo = bf16(s - hi), or, in the last launch, c * s to the output
-    const long long nvalid = *p.n_valid;
-    const float cs = p.mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
-    const __amdgpu_buffer_rsrc_t rh = make_rsrc(static_cast<char*>(p.out) + m0 * p.ldo * 2, mrows * p.ldo * 2);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lo + m0 * p.ldlo, mrows * p.ldlo * 2);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const bool cok = ncol + 32 * nb < p.N;
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
-        // element r of the group: row m0 + mrow0 + 32 vb + 8 (r / 4) + r % 4 (offsets from one
-        // base per buffer; the memory fence at the end keeps the next group's loads from being
-        // hoisted above these stores, which would hold every group's values at once)
-        const int mb = mrow0 + 32 * vb;
-        const uint32_t bh = cok ? (uint32_t)((mb * p.ldo + ncol + 32 * nb) * 2) : 0x80000000u;
-        const uint32_t bl = cok ? (uint32_t)((mb * p.ldlo + ncol + 32 * nb) * 2) : 0x80000000u;
-        auto oh = [&](int r) { return cok ? bh + (uint32_t)((8 * (r >> 2) + (r & 3)) * p.ldo * 2) : bh; };
-        auto ol = [&](int r) { return cok ? bl + (uint32_t)((8 * (r >> 2) + (r & 3)) * p.ldlo * 2) : bl; };
-        float sum[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] = acc[vb][nb][r];
-        if (p.hilo != 1) {
-          uint16_t hv[16], lv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            hv[r] = __builtin_amdgcn_raw_buffer_load_b16(rh, (int)oh(r), 0, 0);
-            lv[r] = __builtin_amdgcn_raw_buffer_load_b16(rl, (int)ol(r), 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sum[r] += bf2f(hv[r]) + bf2f(lv[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (p.hilo == 3) {
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(cs * sum[r]), rh, (int)oh(r), 0, 0);
-          } else {
-            const bf16_t hi = f2bf(sum[r]);
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)hi, rh, (int)oh(r), 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f2bf(sum[r] - bf2f(hi)), rl, (int)ol(r), 0, 0);
-          }
-        }
-        asm volatile("" ::: "memory");
       }
     }
   } else {
@@ -421,11 +398,12 @@ __global__ void __launch_bounds__(kSgThreads, 1) sgemm_pair_kernel(SgArgs p0, Sg
   }
 }
 
-// the running-sum output: bf16 out, one K-range, a remainder buffer (32-bit offsets per tile)
+// the running-sum output: bf16 out, one K-range, rows of whole 8-element groups (the staged
+// epilogue), a remainder buffer (32-bit offsets per tile)
 static bool hilo_ok(const SgArgs& a) {
   if (a.hilo == 0) return true;
   return a.hilo >= 1 && a.hilo <= 3 && a.C == nullptr && !a.out_f32 && a.nsplit == 1 && a.lo != nullptr &&
-         kSgTile * a.ldlo * 2 < 0x80000000ll;
+         a.N % 8 == 0 && a.ldo % 8 == 0 && a.ldlo % 8 == 0 && kSgTile * a.ldlo < 0x80000000ll;
 }
 
 static int64_t sg_total(const SgArgs& a) {

@@ -404,7 +404,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
   // One pass instead: pass 1's blocks also give grad_input, summed over the blocks as hi + lo
   // (hi in the output, lo here), so the dlogits are formed once: 8 instead of 10 BT V H flops.
   // Taken when the cost model prefers it with the smaller blocks the lo buffer leaves.
-  const size_t lo = ws_align((size_t)BT * (size_t)H * 2);
+  const size_t lo = ws_align((size_t)BT * (size_t)H);  // (one byte of remainder per element)
   if (lo + 4096 < avail && (int64_t)BT * H * 2 < 0x7fffffffll) {
     const size_t avail1 = avail - lo;
     double best = -1.0;
@@ -425,12 +425,12 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
       for (const int64_t vb : cand) {
         const int64_t n = cdiv(V, vb), last = V - (n - 1) * vb;
         const double red = ns1 > 1 ? cost_bytes((double)V * H * (4.0 * ns1 + 4.0)) + (double)n * kLaunchStages : 0.0;
-        // the running sum's traffic (2-byte accesses: counted at half the streaming rate)
-        const double sum_bytes = (double)BT * H * (8.0 * (double)n - 6.0);
+        // the running sum's traffic (3 bytes per element read and written between blocks)
+        const double sum_bytes = (double)BT * H * (6.0 * (double)n - 5.0);
         // (grad_W and grad_input of a block in one grouped launch)
         const double c = (double)(n - 1) * (cost_dl(BT, vb, H) + cost_pair(vb, H, BT, ks1, BT, H, vb)) +
                          cost_dl(BT, last, H) + cost_pair(last, H, BT, ks1, BT, H, last) +
-                         cost_bytes((double)V * t.ldv * 2) + red + 2.0 * cost_bytes(sum_bytes);
+                         cost_bytes((double)V * t.ldv * 2) + red + cost_bytes(sum_bytes);
         if (best < 0 || c < best) {
           best = c;
           vb1 = vb;
@@ -498,12 +498,12 @@ hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st
 // Per block of vb vocabulary rows: G^T of the block against all tokens (forward kernel,
 // kEpiDlogitsT); grad_W[block] = c G^T . hidden (directly, or over K-ranges of tokens into fp32
 // partial sums reduced into the rows); grad_b[block] = c row sums of G^T; with `dinput`,
-// grad_input += G . W[block] from the same G^T read transposed, kept as hi + lo between blocks
-// and written as c * the sum by the last block.  The two products of a block share one launch.
+// grad_input += G . W[block] from the same G^T read transposed, kept as hi (bf16) + an 8-bit
+// remainder code between blocks and written as c * the sum by the last block.  The two products of a block share one launch.
 static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bool dinput, hipStream_t st) {
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
   float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
-  bf16_t* lo = reinterpret_cast<bf16_t*>(w.big + 256 + t.g1_bytes + t.part1_bytes);
+  uint8_t* lo = reinterpret_cast<uint8_t*>(w.big + 256 + t.g1_bytes + t.part1_bytes);
   const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bf16_t* b = static_cast<const bf16_t*>(a.bias);
@@ -556,7 +556,7 @@ static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t
       mi.n_valid = w.n_valid;
       mi.mean = a.mean ? 1 : 0;
       mi.hilo = nblk == 1 ? 0 : (k == 0 ? 1 : (k == nblk - 1 ? 3 : 2));
-      mi.lo = reinterpret_cast<uint16_t*>(lo);
+      mi.lo = lo;
       mi.ldlo = a.H;
     }
     if (a.grad_W != nullptr && dinput) e = launch_sgemm_pair(mw, mi, st);
