@@ -146,8 +146,11 @@ lce_status lce_fwd_bwd_profiled(const void* hidden, const void* W, const void* b
  * The gradient GEMMs consume the dlogits in tiles; a tile whose entries are all below
  * filter_eps in magnitude contributes nothing to the gradient it feeds (its MFMA work is
  * skipped, and for grad_W its share of grad_b is dropped too).  The tiles are
- *   grad_input: 64 tokens x 16 vocabulary entries (aligned at token 0, vocabulary entry 0);
- *   grad_W, grad_b: 64 vocabulary entries x 16 tokens.
+ *   grad_input: R tokens x C vocabulary entries (aligned at token 0, vocabulary entry 0);
+ *   grad_W, grad_b: R vocabulary entries x C tokens,
+ * with (R, C) = (256, 64) where the bf16 backward runs on the stored-operand GEMM (from
+ * H = 1024, when its one-pass plan fits the workspace) and (64, 16) otherwise:
+ * lce_filter_tile_shape gives them.
  * The test applies to the dlogits of the summed loss, valid * (softmax * (1 + 2 mu LSE) -
  * onehot), i.e. before the 1/n_valid of the mean, so it does not depend on the batch size.
  * The loss, n_valid and LSE are exact.  The gradients differ from lce_fwd_bwd's by the
@@ -165,6 +168,11 @@ lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* b
                                 void* grad_input, void* grad_W, void* grad_b, int64_t* n_valid_out,
                                 float* lse_out, void* workspace, size_t workspace_bytes,
                                 void* stream, float filter_eps, int64_t* filter_counts);
+
+/* The filter tiles of lce_fwd_bwd_filtered for these sizes ("Cut Cross Entropy visualized",
+ * "Gradient Filtering"): *rows = R and *cols = C as described there (host only, no device
+ * work).  LCE_ERR_ARG for NULL outputs, invalid sizes or dtype. */
+lce_status lce_filter_tile_shape(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t* rows, int64_t* cols);
 
 /* Exact number of workspace bytes lce_fwd_bwd needs for these sizes (its whole extra
  * device memory), or 0 if the sizes are invalid. */

@@ -126,6 +126,15 @@ def fwd_bwd_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype) -> int:
     return int(load().lce_fwd_bwd_workspace_bytes(BT, H, V, _DTYPES[dtype], 0))
 
 
+def filter_tile_shape(BT: int, H: int, V: int, dtype: torch.dtype):
+    """(R, C): the gradient-filtering tiles of lce_fwd_bwd_filtered for these sizes, R tokens x C
+    vocabulary entries for grad_input and R entries x C tokens for grad_W and grad_b."""
+    r, c = ctypes.c_int64(0), ctypes.c_int64(0)
+    _lib.check(load().lce_filter_tile_shape(BT, H, V, _DTYPES[dtype], ctypes.byref(r), ctypes.byref(c)),
+               "lce_filter_tile_shape")
+    return int(r.value), int(c.value)
+
+
 def chunked_workspace_bytes(BT: int, H: int, V: int, dtype: torch.dtype, grad_weight_fp32: bool = False) -> int:
     flags = _lib.FLAG_GRAD_W_FP32 if grad_weight_fp32 else 0
     return int(load().lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, _DTYPES[dtype], flags))

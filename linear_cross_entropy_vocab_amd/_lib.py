@@ -23,7 +23,8 @@ FLAG_GRAD_W_FP32 = 2
 FLAG_SORT_VOCAB = 4
 NUM_STAGES = 7
 
-EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_fwd_bwd_workspace_bytes",
+EXPORTS = ("lce_fwd_bwd", "lce_fwd_bwd_profiled", "lce_fwd_bwd_filtered", "lce_filter_tile_shape",
+           "lce_fwd_bwd_workspace_bytes",
            "lce_fwd_bwd_chunked", "lce_fwd_bwd_chunked_workspace_bytes",
            "lce_rows_forward", "lce_rows_backward", "lce_rows_workspace_bytes",
            "lce_stage_name",
@@ -59,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.lce_fwd_bwd_profiled.restype = ctypes.c_int
     lib.lce_fwd_bwd_filtered.argtypes = fused + [c_f, c_vp]
     lib.lce_fwd_bwd_filtered.restype = ctypes.c_int
+    lib.lce_filter_tile_shape.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, c_vp, c_vp]
+    lib.lce_filter_tile_shape.restype = ctypes.c_int
     lib.lce_fwd_bwd_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_uint32]
     lib.lce_fwd_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.lce_fwd_bwd_chunked.argtypes = fused

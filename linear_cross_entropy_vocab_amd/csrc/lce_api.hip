@@ -45,8 +45,9 @@ size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
     // the two-pass region starts where the LSE partials do
     TwoPass tp{};
     if (H > 1024) tp = twopass_plan(BT, H, V);
-    const SgPlan sp = sg_plan(BT, H, V);
-    n = std::max(n, fused_small_bytes(BT, V) + std::max(tp.on ? tp.bytes : (size_t)0, sp.on ? sp.bytes : (size_t)0));
+    const SgPlan sp = sg_plan(BT, H, V), sf = sg_plan(BT, H, V, true);  // (exact, filtered or sorted)
+    n = std::max(n, fused_small_bytes(BT, V) + std::max({tp.on ? tp.bytes : (size_t)0, sp.on ? sp.bytes : (size_t)0,
+                                                         sf.on ? sf.bytes : (size_t)0}));
   }
   return n;
 }
@@ -73,7 +74,8 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   p += ws_align((size_t)V * 4);
   w.lse_part = reinterpret_cast<float*>(p);  // (at fused_small_bytes)
   w.big = nullptr;
-  if (bf16 && ((H > 1024 && twopass_plan(BT, H, V).on) || sg_plan(BT, H, V).on)) w.big = p;
+  if (bf16 && ((H > 1024 && twopass_plan(BT, H, V).on) || sg_plan(BT, H, V).on || sg_plan(BT, H, V, true).on))
+    w.big = p;
   return w;
 }
 
@@ -218,6 +220,15 @@ lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* b
   return lce::fused_call(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, reduction,
                          flags, loss_out, grad_input, grad_W, grad_b, n_valid_out, lse_out, workspace,
                          workspace_bytes, stream, nullptr, nullptr, filter_eps, filter_counts, true);
+}
+
+lce_status lce_filter_tile_shape(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t* rows, int64_t* cols) {
+  if (rows == nullptr || cols == nullptr || BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_ARG;
+  if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_ARG;
+  const bool one = dtype == LCE_DTYPE_BF16 && lce::sg_plan(BT, H, V, true).on;
+  *rows = one ? 256 : 64;
+  *cols = one ? 64 : 16;
+  return LCE_OK;
 }
 
 size_t lce_fwd_bwd_chunked_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {

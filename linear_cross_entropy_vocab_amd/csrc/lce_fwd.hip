@@ -243,7 +243,12 @@ __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1
 // MODE kEpiDlogitsT: the kEpiDlogits values written transposed, G^T[v][t] (vocabulary rows of
 // ld tokens; token columns BT..ld-1 are written as 0): the K-contiguous operand of the grad_W
 // product G^T . hidden.
-constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4, kEpiDlogitsT = 5;
+// MODE kEpiDlogitsTF: kEpiDlogitsT, and the tile flags of gradient filtering ("Cut Cross Entropy
+// visualized", "Gradient Filtering") in flt: whether each 64-entry quarter of the tile (all 256
+// of its tokens) and each 64-token quarter (all 256 of its entries) holds a dlogit (the fp32
+// value, before rounding) of magnitude >= flt.eps; with the counts of quarters without one.
+constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4, kEpiDlogitsT = 5,
+              kEpiDlogitsTF = 6;
 
 // (m, s, t) with s = sum e^(z - m), t = sum e^(z - m) z, merged with a second such triple
 __device__ __forceinline__ void mst_combine(float& m, float& s, float& t, float m2, float s2, float t2) {
@@ -269,9 +274,10 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
                                                                     const float2* __restrict__ tok, float mu,
                                                                     int64_t vbase, float* __restrict__ ez_part,
                                                                     const float4* __restrict__ rtok,
-                                                                    const int32_t* __restrict__ rcy) {
+                                                                    const int32_t* __restrict__ rcy, DltExtra flt) {
   constexpr bool RD = MODE == kEpiRowsDlogits;
-  constexpr bool DLT = MODE == kEpiDlogitsT;
+  constexpr bool FLT = MODE == kEpiDlogitsTF;
+  constexpr bool DLT = MODE == kEpiDlogitsT || FLT;
   constexpr bool DL = MODE == kEpiDlogits || DLT;
   constexpr bool STORE = MODE == kEpiLogits || DL || RD;
   constexpr bool EZ = MODE == kEpiLseEz;
@@ -286,6 +292,11 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   __shared__ float2 s_tok[DL ? kFwdTileT2 : 1];
   __shared__ float4 s_rt[RD ? kFwdTileT2 : 1];
   __shared__ int32_t s_rcy[RD ? kFwdTileT2 : 1];
+  __shared__ int s_flw[FLT ? 8 : 1];  // (FLT) per wave: bit 0 / 1 its first / second 64 rows hold a large dlogit
+  __shared__ float s_gb[DLT ? 8 : 1][DLT ? 128 : 1];  // (DLT, grad_b) per wave: its rows' sums over its 64 tokens
+  // (FLT) threads 0-3: grad_input quarters (entries 64 tid ..) examined and skipped over this
+  // workgroup's tiles; threads 4-7: grad_W quarters (tokens 64 (tid - 4) ..)
+  unsigned long long n_exam = 0, n_skip = 0;
 
   const int64_t nwg = nt_v * nt_t;
   const int tid = threadIdx.x, w = wave_id(), lane = tid % kWave;
@@ -471,8 +482,13 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       const int rl = ln >> 3, cl = 8 * (ln & 7);  // read-back: rows 8 i + rl, tokens cl .. cl + 7
       const int64_t tcol = tl.t0 + wt * 64 + cl;
       const bool col_ok = tcol + 8 <= ld;
+      bool big[2] = {false, false};  // (FLT) a large dlogit in the wave's rows 0-63 / 64-127
+      const bool gbs = flt.gbp != nullptr;  // (grad_b: row sums of the fp32 values)
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
+        float rs[16];  // (grad_b) rows 8 (r / 4) + r % 4 of this vb: the sum over the lane's two tokens
+#pragma unroll
+        for (int r = 0; r < 16; ++r) rs[r] = 0.f;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -484,6 +500,11 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
                                     c0 == cy2[tb] ? -1.f : 0.f);
               const float z1 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e + 1], kLog2e, ra2[tb])),
                                     fac2[tb], c0 + 1 == cy2[tb] ? -1.f : 0.f);
+              if constexpr (FLT)  // (rows past the block do not count; tokens past BT hold 0)
+                big[vb >> 1] = big[vb >> 1] || (c0 < lim && !(fabsf(z0) < flt.eps)) ||
+                               (c0 + 1 < lim && !(fabsf(z1) < flt.eps));
+              rs[4 * rr + e] += z0;
+              rs[4 * rr + e + 1] += z1;
               const float send = odd ? z0 : z1;
               // quad_perm (1, 0, 3, 2): the value of lane ln ^ 1
               const float recv = __int_as_float(
@@ -502,9 +523,75 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
           __builtin_amdgcn_raw_buffer_store_b128(q, rz, (int)off, 0, 0);
         }
         asm volatile("" ::: "memory");  // (the block is rewritten for the next vb)
+        if (gbs) {
+          // Sums over the 32 lanes (tokens) of each half: four halving exchanges leave lane t
+          // with row index r(t) = bits 1-4 of t (the lower half of its values kept where the
+          // partner's bit is set, and the upper half where it is clear), then a last one adds
+          // the partner t ^ 1's sum of the same row.
+          const int t = ln & 31;
+          float v8[8], v4[4], v2[2];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const bool up = (t & 16) != 0;
+            v8[i] = (up ? rs[i + 8] : rs[i]) + __shfl_xor(up ? rs[i] : rs[i + 8], 16, kWave);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool up = (t & 8) != 0;
+            v4[i] = (up ? v8[i + 4] : v8[i]) + __shfl_xor(up ? v8[i] : v8[i + 4], 8, kWave);
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const bool up = (t & 4) != 0;
+            v2[i] = (up ? v4[i + 2] : v4[i]) + __shfl_xor(up ? v4[i] : v4[i + 2], 4, kWave);
+          }
+          const bool up = (t & 2) != 0;
+          float v1 = (up ? v2[1] : v2[0]) + __shfl_xor(up ? v2[0] : v2[1], 2, kWave);
+          v1 += __shfl_xor(v1, 1, kWave);
+          const int r = ((t >> 1) & 1) | (((t >> 2) & 1) << 1) | (((t >> 3) & 1) << 2) | (((t >> 4) & 1) << 3);
+          if ((t & 1) == 0) s_gb[w][vb * 32 + 8 * (r >> 2) + (r & 3) + 4 * (ln >> 5)] = v1;
+        }
       }
       (void)lse_part;
+      if constexpr (FLT) {
+        const bool b0 = __builtin_amdgcn_ballot_w64(big[0]) != 0, b1 = __builtin_amdgcn_ballot_w64(big[1]) != 0;
+        if (ln == 0) s_flw[w] = (b0 ? 1 : 0) | (b1 ? 2 : 0);
+      }
       __syncthreads();  // every wave has read s_bias and s_tok before the next tile rewrites them
+      if (gbs && tid < kFwdTileV && tid < vlim) {
+        // the tile's rows: the sum of the four waves' 64-token sums (with filtering, of the
+        // 64-token groups whose grad_W flag is set), in order
+        const int wv0 = tid >> 7, rw = tid & 127;
+        float acc1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bool inc = true;
+          if constexpr (FLT) inc = (s_flw[q] | s_flw[4 + q]) != 0;
+          if (inc) acc1 += s_gb[4 * wv0 + q][rw];
+        }
+        flt.gbp[(tl.t0 / kFwdTileT2) * flt.ldgb + tl.v0 + tid] = acc1;
+      }
+      if constexpr (FLT) {
+        // (s_flw and s_gb are rewritten only after the next tile's K loop and its barriers)
+        if (tid < 4) {  // entries 64 tid .. of the tile against its 256 tokens: waves 4 (tid / 2) + 0..3
+          const int q = tid, f = s_flw[4 * (q >> 1)] | s_flw[4 * (q >> 1) + 1] | s_flw[4 * (q >> 1) + 2] |
+                                     s_flw[4 * (q >> 1) + 3];
+          if (64 * q < vlim) {
+            const uint8_t on = (uint8_t)((f >> (q & 1)) & 1);
+            flt.fin[(tl.t0 / kFwdTileT2) * flt.ldfi + tl.vtile * 4 + q] = on;
+            ++n_exam;
+            n_skip += on ? 0 : 1;
+          }
+        } else if (tid < 8) {  // tokens 64 q .. of the tile against its 256 entries: waves q, 4 + q
+          const int q = tid - 4;
+          if (tl.t0 + 64 * q < BT) {
+            const uint8_t on = (uint8_t)((s_flw[q] | s_flw[4 + q]) != 0 ? 1 : 0);
+            flt.fw[tl.vtile * flt.ldfw + tl.t0 / 64 + q] = on;
+            ++n_exam;
+            n_skip += on ? 0 : 1;
+          }
+        }
+      }
       if (!has_next) break;
       blk = nblk;
       tl = tn;
@@ -649,6 +736,12 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     blk = nblk;
     tl = tn;
   }
+  if constexpr (FLT) {
+    if (tid < 8 && flt.cnt != nullptr && n_exam > 0) {
+      atomicAdd(&flt.cnt[tid < 4 ? 0 : 2], n_skip);
+      atomicAdd(&flt.cnt[tid < 4 ? 1 : 3], n_exam);
+    }
+  }
   vm_wait<0>();
 }
 
@@ -673,7 +766,7 @@ hipError_t launch_fwd_lse(const FusedArgs& a, const FusedWs& w, hipStream_t st) 
     hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLse>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
                        st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
                        nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0,
-                       (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
+                       (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, DltExtra{});
     return hipGetLastError();
   }
   const int64_t nt_t = (a.BT + kFwdTileT - 1) / kFwdTileT;
@@ -836,7 +929,7 @@ hipError_t launch_rows_fused_forward(const FusedArgs& a, const FusedWs& w, float
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLseEz>, dim3((unsigned)fwd_grid(w.nt * nt_t2)), dim3(kFwdThreads2), 0,
                      st, (const bf16_t*)a.W, (const bf16_t*)a.hidden, (const bf16_t*)a.bias, a.BT, a.H, a.V, w.nt,
                      nt_t2, w.lse_part, (bf16_t*)nullptr, (int64_t)0, (const float2*)nullptr, 0.f, (int64_t)0,
-                     ez_part, (const float4*)nullptr, (const int32_t*)nullptr);
+                     ez_part, (const float4*)nullptr, (const int32_t*)nullptr, DltExtra{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_target_logit(a, w, st)) != hipSuccess) return e;
@@ -889,7 +982,7 @@ hipError_t launch_logits_chunk(const bf16_t* W, const bf16_t* h_chunk, const bf1
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiLogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, zout, ld, (const float2*)nullptr,
-                     0.f, (int64_t)0, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
+                     0.f, (int64_t)0, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, DltExtra{});
   return hipGetLastError();
 }
 
@@ -904,23 +997,35 @@ hipError_t launch_dlogits_block(const bf16_t* W_block, const bf16_t* h_block, co
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W_block, h_block, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok_block,
-                     mu, vbase, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
+                     mu, vbase, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, DltExtra{});
   return hipGetLastError();
 }
 
 // Transposed dlogits of the summed loss for the vocabulary rows vbase .. vbase + V - 1 (W_block,
 // bias_block) against all `rows` tokens: gout[v][t] in bf16, rows of ld >= rows tokens (columns
 // rows..ld-1 written as 0).
+// With flt.fin, also the tile flags of gradient filtering; with flt.gbp, the grad_b partial
+// sums (DltExtra).
 hipError_t launch_dlogits_block_t(const bf16_t* W_block, const bf16_t* h, const bf16_t* bias_block,
                                   const float2* tok, float mu, int64_t rows, int64_t H, int64_t V, int64_t vbase,
-                                  bf16_t* gout, int64_t ld, hipStream_t st) {
+                                  bf16_t* gout, int64_t ld, hipStream_t st, const DltExtra& flt) {
   if (rows <= 0 || V <= 0) return hipSuccess;
   if (V * ld * 2 > 0x7fffffffll) return hipErrorInvalidValue;
   const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
   const int64_t nt_t2 = (ld + kFwdTileT2 - 1) / kFwdTileT2;
+  // every grad_b partial lands inside its row
+  if (flt.gbp != nullptr && flt.ldgb < V) return hipErrorInvalidValue;
+  if (flt.fin != nullptr) {
+    // every flag lands inside its row
+    if (flt.fw == nullptr || flt.ldfi < 4 * nt_v || flt.ldfw < 4 * nt_t2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogitsTF>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2),
+                       0, st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu,
+                       vbase, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, flt);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogitsT>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu, vbase,
-                     (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr);
+                     (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, flt);
   return hipGetLastError();
 }
 
@@ -966,7 +1071,7 @@ hipError_t launch_rows_dlogits_chunk(const bf16_t* W, const bf16_t* h_chunk, con
   const int64_t nt_t2 = (rows + kFwdTileT2 - 1) / kFwdTileT2;
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiRowsDlogits>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2),
                      0, st, W, h_chunk, bias, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, (const float2*)nullptr,
-                     0.f, (int64_t)0, (float*)nullptr, rtok, rcy);
+                     0.f, (int64_t)0, (float*)nullptr, rtok, rcy, DltExtra{});
   return hipGetLastError();
 }
 

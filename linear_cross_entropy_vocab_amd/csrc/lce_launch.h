@@ -75,8 +75,19 @@ struct SgPlan {
   // transposed dlogits (hi in the output, lo_bytes of 8-bit remainder codes), and pass 2 is dropped
   bool one;
   size_t lo_bytes;
+  // gradient filtering on the one-pass plan: per block, one byte per (256 tokens x 64
+  // vocabulary entries) of grad_input (rows ldfi apart, one per token tile) and per (256
+  // vocabulary entries x 64 tokens) of grad_W (rows ldfw apart, one per vocabulary tile), 1
+  // where the tile holds a dlogit of magnitude >= eps
+  int64_t ldfi, ldfw;
+  size_t fl_bytes;
+  // grad_b: per block, partial sums of the fp32 dlogits per token tile of 256 (DltExtra.gbp),
+  // rows of vb floats
+  size_t gb_bytes;
 };
-SgPlan sg_plan(int64_t BT, int64_t H, int64_t V);
+// filt: the plan of a filtered call (one pass only, blocks of whole 256-row tiles, room for the
+// tile flags); on = false if it does not fit.
+SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, bool filt = false);
 
 
 struct FusedArgs {
@@ -170,9 +181,26 @@ hipError_t launch_dlogits_block(const uint16_t* W_block, const uint16_t* h_block
                                 const float2* tok_block, float mu, int64_t rows, int64_t H, int64_t V,
                                 int64_t vbase, uint16_t* gout, int64_t ld, hipStream_t st);
 
+// Extra outputs of the transposed dlogits kernel.
+//  * Gradient filtering, with fin != NULL: tile flags as SgPlan describes them (fin[token tile *
+//    ldfi + entry / 64], fw[entry / 256 * ldfw + token / 64], entries of the block), and in cnt[4]
+//    the skipped and examined tiles of grad_input, then of grad_W, added to by every launch.
+//  * grad_b, with gbp != NULL: per token tile of 256, the sum of each entry's fp32 dlogits over
+//    the tile's tokens (with filtering, over its 64-token groups whose grad_W flag is set):
+//    gbp[token tile * ldgb + entry] for the block's entries.
+struct DltExtra {
+  float eps;
+  uint8_t* fin;
+  int64_t ldfi;
+  uint8_t* fw;
+  int64_t ldfw;
+  unsigned long long* cnt;
+  float* gbp;
+  int64_t ldgb;
+};
 hipError_t launch_dlogits_block_t(const uint16_t* W_block, const uint16_t* h, const uint16_t* bias_block,
                                   const float2* tok, float mu, int64_t rows, int64_t H, int64_t V, int64_t vbase,
-                                  uint16_t* gout, int64_t ld, hipStream_t st);
+                                  uint16_t* gout, int64_t ld, hipStream_t st, const DltExtra& flt = DltExtra{});
 
 // Stored-operand GEMM (bf16, fp32 accumulation): C = A . B over K split into ranges of ksplit
 // (a multiple of 64), one workgroup per (256 x 256 tile, range).  A [M][lda] is K-contiguous,
@@ -203,6 +231,14 @@ struct SgArgs {
   int hilo;
   uint8_t* lo;
   int64_t ldlo;
+  // Gradient filtering: K-stage s of row tile mt runs only if kflags[mt * ldkf + kb / 64 + s]
+  // is 1 (kb the first K of the tile's range; flags 0 or 1; rows of ldkf bytes, a multiple of
+  // 16, from a 16-byte aligned base).  NULL: every stage runs.
+  const uint8_t* kflags;
+  int64_t ldkf;
+  // (plain output, hilo 0, one K-range) output row of each row of A: row_map[m] for m < M, or
+  // NULL for row m of `out`
+  const int32_t* row_map;
 };
 hipError_t launch_sgemm(const SgArgs& a, hipStream_t st);
 // The same with A given transposed: At [K][lda] (M contiguous, a multiple of 8 elements per row
@@ -215,12 +251,15 @@ hipError_t launch_sgemm_pair(const SgArgs& p0, const SgArgs& p1, hipStream_t st)
 // out[v] = c * acc[v] in bf16.
 hipError_t launch_colsum(const uint16_t* g, int64_t ld, int64_t rows, int64_t cols, float* acc, bool first, bool last,
                          uint16_t* out, const int64_t* n_valid, bool mean, hipStream_t st);
-// out[i] = c * sum_s part[s * stride + i] for i < n (n a multiple of 4), in bf16 or fp32.
+// out[i] = c * sum_s part[s * stride + i] for i < n (n a multiple of 4), in bf16 or fp32; with
+// row_map, element i of row r = i / width goes to row row_map[r] of out (width a multiple of 4).
 hipError_t launch_sg_reduce(const float* part, int nsplit, int64_t n, int64_t stride, void* out, bool out_f32,
-                            const int64_t* n_valid, bool mean, hipStream_t st);
-// out[i] = c * sum_t g[i][t] over cols tokens (rows ld apart, bf16), one row per vocabulary entry.
-hipError_t launch_rowsum(const uint16_t* g, int64_t ld, int64_t rows, int64_t cols, uint16_t* out,
-                         const int64_t* n_valid, bool mean, hipStream_t st);
+                            const int64_t* n_valid, bool mean, hipStream_t st, const int32_t* row_map = nullptr,
+                            int64_t width = 0);
+// out[i] = c * sum_s part[s * ld + i] over nparts partial sums (fp32, in order of s), in bf16,
+// for i < n; with row_map, into out[row_map[i]].
+hipError_t launch_part_sum(const float* part, int64_t ld, int64_t nparts, int64_t n, uint16_t* out,
+                           const int64_t* n_valid, bool mean, hipStream_t st, const int32_t* row_map = nullptr);
 
 // Token-chunked composition (bf16): chunk rows, padded row length of the logits chunk, and
 // the plan of the gradient GEMMs on it.

@@ -77,6 +77,63 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
   const int64_t ke = (kb + p.ksplit) < p.K ? (kb + p.ksplit) : p.K;
   const int nk = ke > kb ? (int)((ke - kb + 63) / 64) : 0;
 
+  // ---- the K stages to run, in increasing order (wave-uniform: every wave walks the same
+  // flags).  Gradient filtering: the row tile's flags of global stages [s0, s1) are read a page
+  // of 1024 at a time (16 per lane, one 16-byte load; bytes outside the range masked), then
+  // taken a 16-stage group at a time from the lane that holds it.
+  const bool filt = p.kflags != nullptr;
+  const int s0 = (int)(kb / 64), s1 = s0 + nk;
+  const uint8_t* krow = filt ? p.kflags + (int64_t)mt * p.ldkf : nullptr;
+  int seq = 0;                       // (no filtering) the next stage
+  int pg = s0 & ~15;                 // first stage of the loaded page
+  u32x4_t fl = {0u, 0u, 0u, 0u};     // lane l: flags of stages pg + 16 l .. + 15
+  uint64_t groups = 0;               // groups of the page with a flag left to take
+  uint32_t steps = 0;                // stages of the current group left to run
+  int gbase = 0;
+  auto load_page = [&]() {
+    const int first = pg + 16 * lane;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (first < s1 && first + 16 > s0) v = *reinterpret_cast<const u32x4_t*>(krow + first);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = first + 4 * i;  // bytes b .. b + 3 of dword i: keep those in [s0, s1)
+      uint32_t m = 0xffffffffu;
+      const int lo = s0 - b, hi = s1 - b;
+      if (lo > 0) m = lo >= 4 ? 0u : m << (8 * lo);
+      if (hi < 4) m = hi <= 0 ? 0u : m & (0xffffffffu >> (8 * (4 - hi)));
+      v[i] &= m;
+    }
+    fl = v;
+    groups = __builtin_amdgcn_ballot_w64((v[0] | v[1] | v[2] | v[3]) != 0u);
+  };
+  auto next_stage = [&]() -> int {  // stage index relative to s0, or -1 when done
+    if (!filt) return seq < nk ? seq++ : -1;
+    for (;;) {
+      if (steps != 0) {
+        const int b = __builtin_ctz(steps);
+        steps &= steps - 1;
+        return gbase + b - s0;
+      }
+      if (groups == 0) {
+        pg += 1024;
+        if (pg >= s1) return -1;
+        load_page();
+        continue;
+      }
+      const int g = __builtin_ctzll(groups);
+      groups &= groups - 1;
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // flag bytes (0 or 1) of lane g -> 4 bits per dword
+        const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)fl[i], g);
+        m |= ((d & 1u) | ((d >> 7) & 2u) | ((d >> 14) & 4u) | ((d >> 21) & 8u)) << (4 * i);
+      }
+      steps = m;
+      gbase = pg + 16 * g;
+    }
+  };
+  if (filt && nk > 0) load_page();
+
   // ---- loads of one stage: A rows 8 (4 w + j) + l / 8, physical chunk l % 8 holding logical
   // chunk (l % 8) ^ swz(row); B plane w, sub-block j: K-row 16 j + l / 4, columns
   // 32 w + 8 (l % 4) .. + 7.  Elements past M, N or the K range read as zero.
@@ -142,11 +199,16 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   int buf = 0;
-  if (nk > 0) dma(0, 0);
-  for (int ks = 0; ks < nk; ++ks) {
-    vm_wait<0>();     // this wave's loads of stage ks have landed
+  int cur = next_stage();
+  const bool any = cur >= 0;
+  // A running sum to which this tile adds nothing stays as it is.
+  if (!any && p.hilo == 2) return;
+  if (any) dma(cur, 0);
+  while (cur >= 0) {
+    vm_wait<0>();     // this wave's loads of stage cur have landed
+    const int nxt = next_stage();
     __syncthreads();  // every wave's have; nobody reads the other buffer any more
-    if (ks + 1 < nk) dma(ks + 1, buf ^ 1);
+    if (nxt >= 0) dma(nxt, buf ^ 1);
     const char* a_base = ATRANS ? sA[buf] + (4 * wm) * 4096 : sA[buf] + (wm * 128 + (lane & 31)) * 128;
     const char* b_base = sB[buf] + (2 * wn) * 4096;
     Frag<bf16_t> fa[2][4], fb[2][2];
@@ -189,6 +251,7 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     buf ^= 1;
+    cur = nxt;
   }
 
   // ---- epilogue: lane l holds column n0 + 64 wn + 32 nb + l % 32 of rows
@@ -226,6 +289,7 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
           reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + 32 * nb + (lane & 31)] = acc[vb][nb][r];
       float v[4][8];
       uint32_t off[4], offl[4];
+      int64_t orow[4];  // (row_map) output row, or -1 past the tile's rows or columns
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 a = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl);
@@ -235,6 +299,7 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
         const int m = 128 * wm + 32 * vb + 8 * i + rl;
         off[i] = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
         offl[i] = cok ? (uint32_t)(m * p.ldlo + n8) : 0x80000000u;
+        orow[i] = p.row_map != nullptr && cok && m < mrows ? (int64_t)p.row_map[m0 + m] : -1;
       }
       if (p.C != nullptr) {  // fp32 partial sums, written or added
         if (p.accumulate) {
@@ -292,6 +357,22 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
           if (p.hilo != 3) {
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo[0], lo[1]}, rl8, (int)offl[i], 0, 0);
+          }
+        }
+      } else if (p.row_map != nullptr) {  // rows through the map (64-bit addresses)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (orow[i] < 0) continue;
+          if (p.out_f32) {
+            float4* d = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow[i] * p.ldo + n8);
+            d[0] = make_float4(cs * v[i][0], cs * v[i][1], cs * v[i][2], cs * v[i][3]);
+            d[1] = make_float4(cs * v[i][4], cs * v[i][5], cs * v[i][6], cs * v[i][7]);
+          } else {
+            u32x4_t ho;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+              ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
+            *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(p.out) + orow[i] * p.ldo + n8) = ho;
           }
         }
       } else if (p.out_f32) {
@@ -416,6 +497,12 @@ static int64_t sg_total(const SgArgs& a) {
 // of range).  ATRANS: At [K][lda] with rows of whole 8-element vectors.
 static bool sg_args_ok(const SgArgs& a, bool atrans) {
   if (a.nsplit < 1 || sg_total(a) > 0x7fffffff || a.ksplit % 64 != 0 || a.ksplit <= 0) return false;
+  // the mapped rows take the staged epilogue's plain output; flag rows of whole 16-byte loads
+  if (a.row_map != nullptr && (a.C != nullptr || a.hilo != 0 || a.nsplit != 1 || a.N % 8 != 0 || a.ldo % 8 != 0))
+    return false;
+  if (a.kflags != nullptr &&
+      (a.ldkf % 16 != 0 || reinterpret_cast<uintptr_t>(a.kflags) % 16 != 0 || a.ldkf < (a.K + 63) / 64))
+    return false;
   if (atrans) {
     if (a.K * a.lda * 2 >= 0x80000000ll) return false;
     if (a.M % 8 != 0 && a.lda < (a.M + 7) / 8 * 8) return false;
@@ -470,10 +557,12 @@ hipError_t launch_colsum(const bf16_t* g, int64_t ld, int64_t rows, int64_t cols
 }
 
 // out = c * sum over nsplit partial buffers ([nsplit][n] fp32, `stride` floats apart), in bf16
-// or fp32; c = 1 / max(n_valid, 1) if mean, else 1.  n a multiple of 4.
+// or fp32; c = 1 / max(n_valid, 1) if mean, else 1.  n a multiple of 4.  With row_map, element
+// i (row i / width) goes to row row_map[i / width] of out.
 __global__ void __launch_bounds__(256) sg_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t n,
                                                         int64_t stride, void* __restrict__ out, int out_f32,
-                                                        const int64_t* __restrict__ n_valid, int mean) {
+                                                        const int64_t* __restrict__ n_valid, int mean,
+                                                        const int32_t* __restrict__ row_map, int64_t width) {
   const long long nvalid = *n_valid;
   const float cs = mean ? 1.f / (float)(nvalid > 1 ? nvalid : 1) : 1.f;
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n;
@@ -486,54 +575,53 @@ __global__ void __launch_bounds__(256) sg_reduce_kernel(const float* __restrict_
       a.z += b.z;
       a.w += b.w;
     }
+    int64_t o = i;
+    if (row_map != nullptr) {
+      const int64_t r = i / width;
+      o = (int64_t)row_map[r] * width + (i - r * width);
+    }
     if (out_f32)
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = make_float4(cs * a.x, cs * a.y, cs * a.z, cs * a.w);
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = make_float4(cs * a.x, cs * a.y, cs * a.z, cs * a.w);
     else
-      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + i) =
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + o) =
           make_uint2(pack_bf2(cs * a.x, cs * a.y), pack_bf2(cs * a.z, cs * a.w));
   }
 }
 
 hipError_t launch_sg_reduce(const float* part, int nsplit, int64_t n, int64_t stride, void* out, bool out_f32,
-                            const int64_t* n_valid, bool mean, hipStream_t st) {
+                            const int64_t* n_valid, bool mean, hipStream_t st, const int32_t* row_map,
+                            int64_t width) {
   if (n <= 0) return hipSuccess;
   if (n % 4 != 0) return hipErrorInvalidValue;
+  if (row_map != nullptr && (width <= 0 || width % 4 != 0 || n % width != 0)) return hipErrorInvalidValue;
   int64_t blocks = (n / 4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(sg_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, nsplit, n, stride, out,
-                     out_f32 ? 1 : 0, n_valid, mean ? 1 : 0);
+                     out_f32 ? 1 : 0, n_valid, mean ? 1 : 0, row_map, width);
   return hipGetLastError();
 }
 
-// grad_b of a block of vocabulary rows from its transposed dlogits (rows ld elements apart,
-// cols tokens each): out[i] = c * sum_t G^T[i][t], one wave per row, fixed order.
-__global__ void __launch_bounds__(256) rowsum_kernel(const bf16_t* __restrict__ g, int64_t ld, int64_t rows,
-                                                     int64_t cols, bf16_t* __restrict__ out,
-                                                     const int64_t* __restrict__ n_valid, int mean) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const bf16_t* gr = g + row * ld;
+// grad_b of a block of vocabulary rows from the transposed dlogits kernel's partial sums (one
+// row of fp32 sums per token tile): out[i] = c * sum_s part[s * ld + i], in order of s.
+__global__ void __launch_bounds__(256) part_sum_kernel(const float* __restrict__ part, int64_t ld, int64_t nparts,
+                                                       int64_t n, bf16_t* __restrict__ out,
+                                                       const int64_t* __restrict__ n_valid, int mean,
+                                                       const int32_t* __restrict__ row_map) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
   float s = 0.f;
-  for (int64_t c = 8 * lane; c < cols; c += 8 * kWave) {
-    const uint4 v = *reinterpret_cast<const uint4*>(gr + c);  // (columns past cols hold 0)
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s += __uint_as_float(u[e] << 16) + __uint_as_float(u[e] & 0xffff0000u);
-  }
-  s = wave_sum(s);
-  if (lane == 0) {
-    const long long nv = *n_valid;
-    const float cs = mean ? 1.f / (float)(nv > 1 ? nv : 1) : 1.f;
-    out[row] = f2bf(cs * s);
-  }
+  for (int64_t k = 0; k < nparts; ++k) s += part[k * ld + i];
+  const long long nv = *n_valid;
+  const float cs = mean ? 1.f / (float)(nv > 1 ? nv : 1) : 1.f;
+  out[row_map != nullptr ? (int64_t)row_map[i] : i] = f2bf(cs * s);
 }
 
-hipError_t launch_rowsum(const bf16_t* g, int64_t ld, int64_t rows, int64_t cols, bf16_t* out,
-                         const int64_t* n_valid, bool mean, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, g, ld, rows, cols, out,
-                     n_valid, mean ? 1 : 0);
+hipError_t launch_part_sum(const float* part, int64_t ld, int64_t nparts, int64_t n, bf16_t* out,
+                           const int64_t* n_valid, bool mean, hipStream_t st, const int32_t* row_map) {
+  if (n <= 0) return hipSuccess;
+  if (ld < n || nparts < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(part_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, ld, nparts, n, out,
+                     n_valid, mean ? 1 : 0, row_map);
   return hipGetLastError();
 }
 

@@ -151,12 +151,14 @@ hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st
 hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_sg_onepass(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 
-// Exact calls take the stored-operand GEMM plan; filtered and sorted calls (whose skip test
-// and row order live in the stored-dlogits GEMMs of lce_bwd.hip) the plan above.
+// Exact calls take the stored-operand GEMM plan; filtered and sorted calls its one-pass plan
+// for filtering (flags of 256 x 64 tiles, rows through the sort's order) where that fits,
+// else the plan above (the stored-dlogits GEMMs of lce_bwd.hip, 64 x 16 tiles).
 static bool exact_call(const FusedArgs& a) { return !(a.filter_eps > 0.f) && a.out_row_map == nullptr; }
 bool use_twopass(const FusedArgs& a) {
   if (!a.bf16) return false;
   if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return true;
+  if (!exact_call(a) && sg_plan(a.BT, a.H, a.V, true).on) return true;
   return a.H > 1024 && twopass_plan(a.BT, a.H, a.V).on;
 }
 
@@ -179,6 +181,8 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
   if (exact_call(a)) {
     const SgPlan t = sg_plan(a.BT, a.H, a.V);
     if (t.on) return t.one ? launch_sg_onepass(a, w, st) : launch_sg_dinput(a, w, st);
+  } else if (sg_plan(a.BT, a.H, a.V, true).on) {
+    return launch_sg_onepass(a, w, st);
   }
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
@@ -223,12 +227,10 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
 }
 
 hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  if (exact_call(a)) {
-    const SgPlan t = sg_plan(a.BT, a.H, a.V);
-    if (t.on) {
-      if (t.one && a.grad_input != nullptr && a.BT > 0) return hipSuccess;  // (done with grad_input)
-      return launch_sg_dweight(a, w, st);
-    }
+  const SgPlan sp = sg_plan(a.BT, a.H, a.V, !exact_call(a));
+  if (sp.on) {
+    if (sp.one && a.grad_input != nullptr && a.BT > 0) return hipSuccess;  // (done with grad_input)
+    return launch_sg_dweight(a, w, st);
   }
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
@@ -281,7 +283,8 @@ hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStrea
 // The exact (unfiltered) call runs both passes on the stored-operand GEMM (lce_sgemm.hip):
 //   pass 1, per block of vb vocabulary rows: G^T = transposed dlogits of the block against all
 //     tokens (forward kernel, kEpiDlogitsT), grad_W[block] = c G^T . hidden straight into the
-//     output, grad_b[block] = c row sums of G^T;
+//     output, grad_b[block] = c row sums of the dlogits (summed in fp32 by the dlogits kernel
+//     per token tile of 256, then over the tiles);
 //   pass 2, per block of tb tokens and vocabulary block of vr rows: G = dlogits (kEpiDlogits),
 //     partial sums over K-ranges of ksplit vocabulary rows += G . W[vocabulary block]; then
 //     grad_input[token block] = c * the sum of the partial sums.
@@ -317,9 +320,15 @@ double cost_pair(int64_t M0, int64_t N0, int64_t K0, int64_t ks0, int64_t M1, in
 }
 // streaming bytes at about 4 TB/s against a stage of about 1.4 us
 double cost_bytes(double bytes) { return bytes / 4e12 / 1.4e-6; }
+// tile flags of gradient filtering for blocks of vb vocabulary rows (SgPlan)
+int64_t flag_ldfi(int64_t vb) { return round_up(4 * cdiv(vb, 256), 16); }
+int64_t flag_ldfw(int64_t BT) { return round_up(4 * cdiv(BT, 256), 16); }
+size_t flag_bytes(int64_t BT, int64_t vb) {
+  return ws_align((size_t)cdiv(BT, 256) * (size_t)flag_ldfi(vb)) + ws_align((size_t)cdiv(vb, 256) * (size_t)flag_ldfw(BT));
+}
 }  // namespace
 
-SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
+SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, bool filt) {
   SgPlan t{};
   t.on = false;
   if (BT <= 0 || V <= 0 || H < kSgMinH) return t;
@@ -332,15 +341,18 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
   if ((int64_t)BT * H * 2 >= 0x7fffffffll) return t;
   // pass 1: evenly sized vocabulary blocks (multiples of 64 rows) whose G^T fits
   t.ldv = round_up(BT, 64);
+  // (grad_b: fp32 partial sums of each vocabulary row per token tile of 256)
+  const size_t gb_row = (size_t)cdiv(BT, 256) * 4;
   const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)t.ldv * 2)) / 64 * 64, round_up(V, 64));
   if (v_fit < 64) return t;
+  double best1 = -1.0, best2 = -1.0;
+  if (!filt) {  // (a filtered call takes the one-pass plan below or none)
   // (with ns1 > 1 the tokens are split into K-ranges whose fp32 partial sums are reduced into
   // the grad_W rows of the block: more workgroups per block when H gives few column tiles)
-  double best1 = -1.0;
   for (int64_t ns1 = 1; ns1 <= 16; ++ns1) {
     const int64_t ks1 = round_up(cdiv(BT, ns1), 64);
     if (ns1 > 1 && cdiv(BT, ks1) != ns1) continue;
-    const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0);
+    const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0) + gb_row;
     const int64_t fit = std::min<int64_t>((int64_t)(avail / per_row) / 64 * 64, round_up(V, 64));
     if (fit < 64) continue;
     for (int64_t nb = cdiv(V, fit); nb <= cdiv(V, fit) + 8 && nb <= cdiv(V, 64); ++nb) {
@@ -360,9 +372,9 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
   if (best1 < 0) return t;
   t.g1_bytes = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
   t.part1_bytes = t.nsplit1 > 1 ? ws_align((size_t)t.nsplit1 * (size_t)t.vb * (size_t)H * 4) : 0;
-  const size_t pass1 = t.g1_bytes + t.part1_bytes;
+  t.gb_bytes = ws_align(gb_row * (size_t)t.vb);
+  const size_t pass1 = t.g1_bytes + t.part1_bytes + t.gb_bytes;
   // pass 2: token blocks tb, K-ranges of the partial sums, vocabulary blocks vr
-  double best2 = -1.0;
   const int64_t bt_top = std::min<int64_t>(round_up(BT, 256), 8192);
   for (int64_t tb0 = 256; tb0 <= bt_top; tb0 *= 2) {
     const int64_t tb = std::min(tb0, BT);
@@ -395,25 +407,31 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
       }
     }
   }
-  if (best2 < 0 && H >= kSgTwoPassMinH) return t;
-  t.ldt = round_up(t.vr, 64);
-  t.g_bytes = ws_align((size_t)t.tb * (size_t)t.ldt * 2);
-  t.part_bytes = ws_align((size_t)t.nsplit * (size_t)t.tb * (size_t)H * 4);
-  t.bytes = 256 + std::max(pass1, t.g_bytes + t.part_bytes);
-  t.on = best2 >= 0 && t.bytes <= avail + 4096 && H >= kSgTwoPassMinH;
+  if (best2 >= 0) {  // (else only the one-pass plan below)
+    t.ldt = round_up(t.vr, 64);
+    t.g_bytes = ws_align((size_t)t.tb * (size_t)t.ldt * 2);
+    t.part_bytes = ws_align((size_t)t.nsplit * (size_t)t.tb * (size_t)H * 4);
+    t.bytes = 256 + std::max(pass1, t.g_bytes + t.part_bytes);
+    t.on = t.bytes <= avail + 4096 && H >= kSgTwoPassMinH;
+  }
+  }
   // One pass instead: pass 1's blocks also give grad_input, summed over the blocks as hi + lo
   // (hi in the output, lo here), so the dlogits are formed once: 8 instead of 10 BT V H flops.
   // Taken when the cost model prefers it with the smaller blocks the lo buffer leaves.
+  // A filtered call also keeps the tile flags (room for them at the largest block) and takes
+  // blocks of whole 256-row tiles (or one block), so that the tiles of grad_W start at multiples
+  // of 256 vocabulary entries.
   const size_t lo = ws_align((size_t)BT * (size_t)H);  // (one byte of remainder per element)
-  if (lo + 4096 < avail && (int64_t)BT * H * 2 < 0x7fffffffll) {
-    const size_t avail1 = avail - lo;
+  const size_t fl_res = filt ? flag_bytes(BT, round_up(V, 256)) : 0;
+  if (lo + fl_res + 4096 < avail && (int64_t)BT * H * 2 < 0x7fffffffll) {
+    const size_t avail1 = avail - lo - fl_res;
     double best = -1.0;
     int64_t vb1 = 0, ks1b = 0;
     int ns1b = 0;
     for (int64_t ns1 = 1; ns1 <= 16; ++ns1) {
       const int64_t ks1 = round_up(cdiv(BT, ns1), 64);
       if (ns1 > 1 && cdiv(BT, ks1) != ns1) continue;
-      const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0);
+      const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0) + gb_row;
       const int64_t fit = std::min<int64_t>((int64_t)(avail1 / per_row) / 64 * 64, round_up(V, 64));
       if (fit < 64) continue;
       // candidates: evenly sized blocks near the fit, and multiples of 256 rows down to half of
@@ -423,6 +441,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
         cand.push_back(std::min(round_up(cdiv(V, nb), 64), fit));
       for (int64_t vb = fit / 256 * 256; vb >= 256 && 2 * vb >= fit; vb -= 256) cand.push_back(vb);
       for (const int64_t vb : cand) {
+        if (filt && vb % 256 != 0 && vb < V) continue;
         const int64_t n = cdiv(V, vb), last = V - (n - 1) * vb;
         const double red = ns1 > 1 ? cost_bytes((double)V * H * (4.0 * ns1 + 4.0)) + (double)n * kLaunchStages : 0.0;
         // the running sum's traffic (3 bytes per element read and written between blocks)
@@ -439,7 +458,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
         }
       }
     }
-    if (best >= 0 && (!t.on || best < best1 + best2)) {
+    if (best >= 0 && (filt || !t.on || best < best1 + best2)) {
       t.one = true;
       t.lo_bytes = lo;
       t.vb = vb1;
@@ -447,7 +466,13 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V) {
       t.ksplit1 = ks1b;
       t.g1_bytes = ws_align((size_t)t.vb * (size_t)t.ldv * 2);
       t.part1_bytes = t.nsplit1 > 1 ? ws_align((size_t)t.nsplit1 * (size_t)t.vb * (size_t)H * 4) : 0;
-      t.bytes = 256 + t.g1_bytes + t.part1_bytes + t.lo_bytes;
+      if (filt) {
+        t.ldfi = flag_ldfi(t.vb);
+        t.ldfw = flag_ldfw(BT);
+        t.fl_bytes = flag_bytes(BT, t.vb);
+      }
+      t.gb_bytes = ws_align(gb_row * (size_t)t.vb);
+      t.bytes = 256 + t.g1_bytes + t.part1_bytes + t.lo_bytes + t.fl_bytes + t.gb_bytes;
       t.on = t.bytes <= avail + 4096;
     }
   }
@@ -497,13 +522,35 @@ hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st
 // Pass 1 (grad_W, grad_b) and, with `dinput`, grad_input in the same sweep (one-pass plan).
 // Per block of vb vocabulary rows: G^T of the block against all tokens (forward kernel,
 // kEpiDlogitsT); grad_W[block] = c G^T . hidden (directly, or over K-ranges of tokens into fp32
-// partial sums reduced into the rows); grad_b[block] = c row sums of G^T; with `dinput`,
-// grad_input += G . W[block] from the same G^T read transposed, kept as hi (bf16) + an 8-bit
-// remainder code between blocks and written as c * the sum by the last block.  The two products of a block share one launch.
+// partial sums reduced into the rows); grad_b[block] = c row sums of the fp32 dlogits (the
+// dlogits kernel's sums per token tile, then a fixed-order sum over the tiles: rounding each
+// dlogit to bf16 first would bias the sum when many tokens have nearly the same probability);
+// with `dinput`, grad_input += G . W[block] from the same G^T read transposed, kept as hi (bf16)
+// + an 8-bit remainder code between blocks and written as c * the sum by the last block.  The
+// two products of a block share one launch.
+// Filtered and sorted calls (their plan): with filter_eps > 0 the transposed dlogits kernel also
+// flags the tiles of both products that hold a dlogit of magnitude >= filter_eps, and the GEMMs
+// run the flagged K stages only (grad_b likewise sums the flagged token groups only); with the
+// sort's order, the rows of grad_W and grad_b go to out_row_map[row].
 static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bool dinput, hipStream_t st) {
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
   float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
   uint8_t* lo = reinterpret_cast<uint8_t*>(w.big + 256 + t.g1_bytes + t.part1_bytes);
+  DltExtra flt{};
+  if (a.filter_eps > 0.f) {
+    if (t.fl_bytes == 0) return hipErrorInvalidValue;
+    flt.eps = a.filter_eps;
+    flt.fin = lo + t.lo_bytes;
+    flt.ldfi = t.ldfi;
+    flt.fw = flt.fin + ws_align((size_t)((a.BT + 255) / 256) * (size_t)t.ldfi);
+    flt.ldfw = t.ldfw;
+    flt.cnt = reinterpret_cast<unsigned long long*>(a.filter_counts);
+  }
+  const int32_t* map = a.out_row_map;
+  if (a.grad_b != nullptr) {  // (after the flags: [256 | G^T | partial sums | lo | flags | grad_b partials])
+    flt.gbp = reinterpret_cast<float*>(lo + t.lo_bytes + t.fl_bytes);
+    flt.ldgb = t.vb;
+  }
   const bf16_t* h = static_cast<const bf16_t*>(a.hidden);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bf16_t* b = static_cast<const bf16_t*>(a.bias);
@@ -512,13 +559,16 @@ static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t v0 = k * t.vb, rows = std::min(t.vb, a.V - v0);
     if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows,
-                                    v0, g, t.ldv, st)) != hipSuccess)
+                                    v0, g, t.ldv, st, flt)) != hipSuccess)
       return e;
     void* wout = nullptr;
+    const int64_t o0 = map != nullptr ? 0 : v0;  // (sorted: rows through the order)
     SgArgs mw{};  // grad_W[block] = c G^T . hidden
     if (a.grad_W != nullptr) {
-      wout = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + v0 * a.H)
-                          : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + v0 * a.H);
+      wout = a.grad_w_f32 ? static_cast<void*>(static_cast<float*>(a.grad_W) + o0 * a.H)
+                          : static_cast<void*>(static_cast<bf16_t*>(a.grad_W) + o0 * a.H);
+      mw.kflags = flt.fw;
+      mw.ldkf = flt.ldfw;
       mw.A = g;
       mw.lda = t.ldv;
       mw.B = h;
@@ -538,6 +588,7 @@ static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t
         mw.out = wout;
         mw.out_f32 = a.grad_w_f32 ? 1 : 0;
         mw.ldo = a.H;
+        mw.row_map = map != nullptr ? map + v0 : nullptr;
       }
     }
     SgArgs mi{};  // grad_input += G . W[block]
@@ -558,32 +609,34 @@ static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t
       mi.hilo = nblk == 1 ? 0 : (k == 0 ? 1 : (k == nblk - 1 ? 3 : 2));
       mi.lo = lo;
       mi.ldlo = a.H;
+      mi.kflags = flt.fin;
+      mi.ldkf = flt.ldfi;
     }
     if (a.grad_W != nullptr && dinput) e = launch_sgemm_pair(mw, mi, st);
     else if (a.grad_W != nullptr) e = launch_sgemm(mw, st);
     else if (dinput) e = launch_sgemm_at(mi, st);
     if (e != hipSuccess) return e;
     if (a.grad_W != nullptr && t.nsplit1 > 1 &&
-        (e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, wout, a.grad_w_f32, w.n_valid, a.mean, st)) !=
-            hipSuccess)
+        (e = launch_sg_reduce(part1, t.nsplit1, rows * a.H, rows * a.H, wout, a.grad_w_f32, w.n_valid, a.mean, st,
+                              map != nullptr ? map + v0 : nullptr, a.H)) != hipSuccess)
       return e;
     if (a.grad_b != nullptr &&
-        (e = launch_rowsum(g, t.ldv, rows, a.BT, static_cast<bf16_t*>(a.grad_b) + v0, w.n_valid, a.mean, st)) !=
-            hipSuccess)
+        (e = launch_part_sum(flt.gbp, t.vb, (a.BT + 255) / 256, rows, static_cast<bf16_t*>(a.grad_b) + o0, w.n_valid,
+                             a.mean, st, map != nullptr ? map + v0 : nullptr)) != hipSuccess)
       return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  const SgPlan t = sg_plan(a.BT, a.H, a.V);
+  const SgPlan t = sg_plan(a.BT, a.H, a.V, !exact_call(a));
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   return sg_sweep(a, w, t, false, st);
 }
 
 // One-pass plan: the whole backward (grad_input and, as requested, grad_W and grad_b).
 hipError_t launch_sg_onepass(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  const SgPlan t = sg_plan(a.BT, a.H, a.V);
+  const SgPlan t = sg_plan(a.BT, a.H, a.V, !exact_call(a));
   if (!t.on || !t.one || w.big == nullptr) return hipErrorInvalidValue;
   return sg_sweep(a, w, t, a.grad_input != nullptr && a.BT > 0, st);
 }

@@ -54,7 +54,8 @@ def test_workspace_within_one_logits_chunk(lib, name):
 
 @pytest.mark.parametrize("H", [1024, 1152, 2048, 2304, 4096])
 def test_workspace_within_budget_over_shapes(lib, H):
-    """The backward's block plans (one pass from H = 1024, two passes above) size their region
+    """The backward's block plans (one pass from H = 1024, two passes above; the filtered calls'
+    one-pass plan with its tile flags) size their region
     to what the forward leaves of the one-chunk budget: over a grid of token and vocabulary
     counts the workspace never exceeds it (budget of "Fused Linear Cross-Entropy: The Math,
     the Memory Wall, and Two Ways Around It", "The chunk-size trick")."""
@@ -65,6 +66,30 @@ def test_workspace_within_budget_over_shapes(lib, H):
             base = 16 + 8 * BT + 16 * ((BT + 255) // 256) + 8 * BT + 4 * V + 4 * BT * ((V + 255) // 256)
             # (the forward's own pieces come first; the plans only add within the budget)
             assert ws <= max(budget, base + 64 * 256), (BT, H, V, ws, budget)
+
+
+ERR_ARG = 6  # LCE_ERR_ARG
+
+
+def test_filter_tile_shape(lib):
+    """Filter tiles (host query): 256 x 64 where the bf16 backward takes the one-pass
+    stored-operand plan (from H = 1024, the plan fitting the one-chunk workspace), 64 x 16 on
+    the other kernels; invalid sizes, dtypes and NULL outputs are refused."""
+    def shape(BT, H, V, dt):
+        r, c = ctypes.c_int64(-1), ctypes.c_int64(-1)
+        st = lib.lce_filter_tile_shape(BT, H, V, dt, ctypes.byref(r), ctypes.byref(c))
+        return st, r.value, c.value
+    for name in ("headline", "gemma_like", "qwen_like"):
+        cf = CONFIGS[name]
+        assert shape(cf.BT, cf.H, cf.V, BF16) == (_lib.LCE_OK, 256, 64), name
+        assert shape(cf.BT, cf.H, cf.V, F32) == (_lib.LCE_OK, 64, 16), name
+    assert shape(200, 256, 2048, BF16) == (_lib.LCE_OK, 64, 16)       # pipelined kernel
+    assert shape(2000, 1280, 300, BF16) == (_lib.LCE_OK, 64, 16)      # no room for the one-pass plan
+    assert shape(700, 1024, 20000, BF16) == (_lib.LCE_OK, 256, 64)
+    assert shape(10, 12, 10, BF16)[0] == ERR_ARG
+    assert shape(10, 64, 0, BF16)[0] == ERR_ARG
+    assert shape(10, 64, 10, 7)[0] == ERR_ARG
+    assert lib.lce_filter_tile_shape(10, 64, 10, BF16, None, None) == ERR_ARG
 
 
 def test_workspace_sizes(lib):

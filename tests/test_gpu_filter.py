@@ -4,13 +4,15 @@ visualized", "Gradient Filtering") against the filtered float64 oracle.
 Inputs make every tile decision unambiguous: a vocabulary range, aligned to the tiles and
 holding no target, is pushed to probability ~e^-60 by its bias, and eps = 1e-6 sits far
 from both e^-60 and the smallest probability any other tile can reach.  So the tile counts
-must match the oracle exactly, and the gradients to the usual bf16 / fp32 tolerances.
-Covered: the pipelined kernel (bf16, H <= 1024), the two-pass stored-dlogits backward (bf16,
-H > 1024) and the fp32 kernel; grad_b; both reductions; and eps below every |dlogit|, where the
-filtered call must reproduce the exact call: bit for bit where both run the same kernels
-(fp32, bf16 below H = 1024), within a quarter of the bf16 tolerance from H = 1024 on, where the
-exact call's backward runs on the stored-operand GEMM and the filtered one on kernels that
-test each tile.
+must match the oracle exactly, and the gradients to the usual bf16 / fp32 tolerances.  The
+oracle takes the call's tile shape (lce_filter_tile_shape: 256 x 64 on the stored-operand
+GEMM's one-pass plan, 64 x 16 on the other kernels).
+Covered: the pipelined kernel (bf16, H < 1024), the one-pass stored-operand backward (bf16,
+from H = 1024: one and several vocabulary blocks, whole blocks without a kept tile, grad_W
+over several token ranges) and the fp32 kernel; grad_b; both reductions; and eps below every
+|dlogit|, where the filtered call must reproduce the exact call: bit for bit where both run
+the same kernels (fp32, bf16 below H = 1024), within a quarter of the bf16 tolerance from
+H = 1024 on (the plans of the two calls may cut the vocabulary into different blocks).
 """
 
 import numpy as np
@@ -30,7 +32,17 @@ CASES = [
     ("bf16", 333, 1024, 3001, (1024, 2048), "sum", 1e-3, 32),
     ("bf16", 150, 1152, 1500, (256, 1024), "mean", 0.0, 33),
     ("f32", 130, 128, 1200, (128, 896), "mean", 1e-3, 34),
+    # 8 vocabulary blocks of 2560 entries: blocks 1-3 keep no tile at all
+    ("bf16", 700, 1024, 20000, (2560, 10240), "mean", 1e-4, 36),
+    # grad_W over two token ranges of 47 stages (flag pages not aligned to the ranges)
+    ("bf16", 6000, 1024, 1500, (512, 1280), "mean", 0.0, 37),
 ]
+
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _tiles(dtype, BT, H, V):
+    return lce.filter_tile_shape(BT, H, V, _TORCH_DT[dtype])
 
 
 def _inputs(dtype, BT, H, V, rng_v, seed, z_loss, reduction):
@@ -59,8 +71,10 @@ def test_filtered_matches_filtered_oracle(case):
     print(f"filtered parity {case}", flush=True)
     inp = _inputs(dtype, BT, H, V, rv, seed, mu, reduction)
     eps = 1e-6
+    R, C = _tiles(dtype, BT, H, V)
+    print(f"  tiles {R} x {C}", flush=True)
     ref = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps,
-                                     z_loss=mu, reduction=reduction)
+                                     z_loss=mu, reduction=reduction, stat_rows=R, stream_rows=C)
     counts = torch.zeros(4, dtype=torch.int64, device="cuda")
     r = _run(inp, eps, counts)
     c = counts.cpu().tolist()
@@ -71,12 +85,12 @@ def test_filtered_matches_filtered_oracle(case):
     assert rel(r["loss"].item(), ref["loss"]) <= tol["loss"]
     for k in ("grad_input", "grad_weight", "grad_bias"):
         assert rel_fro(host64(r[k]), ref[k]) <= tol["grad"], k
-    # the skipped vocabulary rows get exactly zero grad_W and grad_b
+    # the vocabulary rows of skipped grad_W tiles get exactly zero grad_W and grad_b
     lo, hi = rv
-    lo64, hi64 = -(-lo // 64) * 64, (hi // 64) * 64
-    if hi64 > lo64:
-        assert int(torch.count_nonzero(r["grad_weight"][lo64:hi64])) == 0
-        assert int(torch.count_nonzero(r["grad_bias"][lo64:hi64])) == 0
+    lo_r, hi_r = -(-lo // R) * R, (hi // R) * R
+    if hi_r > lo_r:
+        assert int(torch.count_nonzero(r["grad_weight"][lo_r:hi_r])) == 0
+        assert int(torch.count_nonzero(r["grad_bias"][lo_r:hi_r])) == 0
 
 
 @pytest.mark.parametrize("dtype,H", [("bf16", 256), ("bf16", 1152), ("f32", 128)])
@@ -105,8 +119,9 @@ def test_tiny_eps_reproduces_exact_call(dtype, H):
 SORT_CASES = [
     # (dtype, BT, H, V, seed)
     ("bf16", 200, 256, 2048, 41),
-    ("bf16", 150, 1152, 1500, 42),   # column-chunked backward
+    ("bf16", 150, 1152, 1500, 42),   # one-pass plan: grad_W rows through the order
     ("f32", 130, 128, 1200, 43),
+    ("bf16", 6000, 1024, 1500, 44),  # ... from partial sums over two token ranges
 ]
 
 
@@ -136,8 +151,11 @@ def test_sorted_filtering_matches_oracle(case):
     print(f"sorted filtering {case}", flush=True)
     inp = _sort_inputs(dtype, BT, H, V, seed)
     eps = 1e-6
-    ref = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps, sort_vocab=True)
-    plain = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps)
+    R, C = _tiles(dtype, BT, H, V)
+    ref = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps, sort_vocab=True,
+                                     stat_rows=R, stream_rows=C)
+    plain = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps,
+                                       stat_rows=R, stream_rows=C)
     assert ref["skipped_input"] > plain["skipped_input"] and ref["skipped_weight"] > plain["skipped_weight"]
     counts = torch.zeros(4, dtype=torch.int64, device="cuda")
     r = lce.lce_fwd_bwd(dev(inp.hidden, dtype), dev(inp.weight, dtype), dev(inp.bias, dtype), dev(inp.targets),

@@ -130,13 +130,12 @@ def test_rows_full_size_headline(saved):
 
 @pytest.mark.parametrize("name", ["headline", "gemma_like"])
 def test_filtered_tiny_eps_full_size(name):
-    """Gradient filtering at full size (the pipelined backward's filtering instantiation at the
-    headline, the stored-dlogits GEMMs at gemma_like): with eps below every |dlogit| no tile is
-    skipped, the loss is the exact call's bit for bit (the forward is shared) and the gradients
-    stay within a quarter of the bf16 tolerance of it (the exact call's backward runs on the
-    stored-operand GEMM, with its own rounding of the dlogits and of the sums); with vocabulary
-    sorting on top, the loss and gradients (returned in the original vocabulary order) stay
-    within the bf16 tolerances of the exact call."""
+    """Gradient filtering at full size (the one-pass stored-operand backward with tile flags,
+    grad_W over token ranges at the headline, in one range at gemma_like): with eps below every
+    |dlogit| no tile is skipped, the loss is the exact call's bit for bit (the forward is shared)
+    and the gradients stay within a quarter of the bf16 tolerance of it; with vocabulary
+    sorting on top (grad_W rows through the order), the loss and gradients (returned in the
+    original vocabulary order) stay within the bf16 tolerances of the exact call."""
     c = CONFIGS[name]
     print(f"full-size filtering, tiny eps: {name} BT={c.BT} H={c.H} V={c.V}", flush=True)
     inp = make_config(name)
@@ -148,8 +147,9 @@ def test_filtered_tiny_eps_full_size(name):
     filt = lce.lce_fwd_bwd(*args, filter_eps=1e-38, filter_counts=counts, **kw)
     torch.cuda.synchronize()
     cnt = counts.cpu().tolist()
-    # every (64-row, 16-row) tile of both gradient passes tested once, none skipped
-    assert cnt == [0, -(-c.BT // 64) * -(-c.V // 16), 0, -(-c.V // 64) * -(-c.BT // 16)], cnt
+    # every tile of both gradient products tested once, none skipped
+    R, C = lce.filter_tile_shape(c.BT, c.H, c.V, torch.bfloat16)
+    assert cnt == [0, -(-c.BT // R) * -(-c.V // C), 0, -(-c.V // R) * -(-c.BT // C)], (cnt, R, C)
     keys = ["loss", "grad_input", "grad_weight"] + (["grad_bias"] if b is not None else [])
     tol = TOL[c.dtype]
     for k in keys:
