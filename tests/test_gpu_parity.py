@@ -168,6 +168,41 @@ def test_fused_grad_weight_fp32():
         assert torch.equal(a32["grad_weight"].to(torch.bfloat16), a16["grad_weight"]), shape
 
 
+@pytest.mark.parametrize("shape", [(333, 256, 3001), (6000, 1024, 1500), (4096, 2304, 3000), (2000, 1280, 300)],
+                         ids=["pipelined", "one-pass-1024-split", "one-pass", "two-pass"])
+def test_grad_bias_closed_form_identical_rows(shape):
+    """grad_b when every token has the same softmax (W = 0, so z_t = b for every t): by the
+    dlogits formula ("Fused Linear Cross-Entropy: ...", "The identity that makes fused fwbw
+    possible"; z-loss factor of "Greyhound — Cross-Entropy", "Kernel design") the sum over
+    tokens is n_valid p (1 + 2 mu LSE(b)) - count_v, with p = softmax(b) and count_v the
+    targets equal to v: grad_b = that / n_valid.  24 entries hold most of the mass and the
+    targets are drawn from p, so count_v nearly cancels n_valid p_v: a sum of per-token
+    bf16-rounded dlogits (each rounded the same way) is off by 1.5-3% here, the fp32 sums stay
+    within bf16 output rounding.  grad_input = G . 0 is exactly zero."""
+    BT, H, V = shape
+    mu = 1e-3
+    inp = make_fused(BT, H, V, dtype="bf16", seed=27, w_std=0.0, bias_std=0.5, ignore_frac=0.1, z_loss=mu)
+    rng = np.random.default_rng(27)
+    hot = rng.choice(V, size=24, replace=False)
+    b = inp.bias.astype(np.float64) - 2.0
+    b[hot] = 3.0 + 0.05 * np.arange(24)
+    inp.bias = torch.from_numpy(b.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    b = inp.bias.astype(np.float64)
+    L = float(np.log(np.sum(np.exp(b - b.max()))) + b.max())
+    p = np.exp(b - L)
+    y = inp.targets.copy()
+    keep = y != -100
+    y[keep] = rng.choice(V, size=int(keep.sum()), p=p / p.sum())
+    inp.targets = y
+    r = run_fused(inp)
+    n = int(keep.sum())
+    count = np.bincount(y[keep], minlength=V).astype(np.float64)
+    want = (n * p * (1.0 + 2.0 * mu * L) - count) / n
+    e = rel_fro(host64(r["grad_bias"]), want)
+    assert e <= 2.0 ** -8, e
+    assert int(torch.count_nonzero(r["grad_input"])) == 0
+
+
 @pytest.mark.parametrize("shape", [(333, 256, 3001), (600, 1152, 9000), (700, 1024, 20000), (2000, 1280, 300)],
                          ids=["pipelined", "one-pass", "one-pass-1024", "two-pass"])
 def test_deterministic_bits(shape):

@@ -74,6 +74,25 @@ def test_zero_weight_gives_log_V(reduction, mu):
     np.testing.assert_allclose(gw, G.T @ h, rtol=1e-13, atol=1e-15)
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_zero_weight_grad_bias_closed_form(reduction):
+    """W = 0 with a bias: every row's logits are b, so LSE = log sum e^b for every row and
+    grad_b[v] = c (n_valid softmax(b)_v (1 + 2 mu LSE) - #{t valid: y_t = v})."""
+    h, W, b, y = _small(BT=41, H=8, V=300)
+    W[:] = 0.0
+    mu = 2e-2
+    out = oracle.lce_oracle(h, W, b, y, reduction=reduction, z_loss=mu)
+    bb = b.astype(np.float64)
+    L = math.log(float(np.sum(np.exp(bb))))
+    p = np.exp(bb) / np.sum(np.exp(bb))
+    valid = y != -100
+    n = int(valid.sum())
+    c = 1.0 / n if reduction == "mean" else 1.0
+    count = np.bincount(y[valid], minlength=300)
+    np.testing.assert_allclose(out["lse"], L, rtol=1e-14)
+    np.testing.assert_allclose(out["grad_bias"], c * (n * p * (1.0 + 2.0 * mu * L) - count), rtol=1e-11, atol=1e-14)
+
+
 def test_all_ignored_gives_zero():
     h, W, b, y = _small()
     y[:] = -100
