@@ -391,10 +391,6 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     for (int64_t ks = 0; ks < nk; ++ks) {
       vm_wait<0>();     // this wave's part of stage ks has landed
       __syncthreads();  // stage ks is in LDS for every wave; the other buffer is no longer read
-      // the next stage, which after the last one is the first stage of the next tile (so its
-      // load overlaps this tile's epilogue)
-      if (ks + 1 < nk) dma(tl, ks + 1, buf ^ 1);
-      else if (has_next) dma(tn, 0, buf ^ 1);
       const char* a_base = sA[buf] + (wv * 128 + (lane & 31)) * ROWB;
       const char* b_base = sB[buf] + (wt * 64 + (lane & 31)) * ROWB;
       Frag<bf16_t> fa[2][4], fb[2][2];
@@ -406,6 +402,11 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         for (int tb = 0; tb < 2; ++tb) lds_frag_ptr(fb[slot][tb], b_base + tb * 32 * ROWB + off);
       };
       rd(0, 0);
+      // the next stage, which after the last one is the first stage of the next tile (so its
+      // load overlaps this tile's epilogue), issued after the first step's fragment reads so
+      // that their latency overlaps the load issue
+      if (ks + 1 < nk) dma(tl, ks + 1, buf ^ 1);
+      else if (has_next) dma(tn, 0, buf ^ 1);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);

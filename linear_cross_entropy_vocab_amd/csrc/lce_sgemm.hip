@@ -208,7 +208,6 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
     vm_wait<0>();     // this wave's loads of stage cur have landed
     const int nxt = next_stage();
     __syncthreads();  // every wave's have; nobody reads the other buffer any more
-    if (nxt >= 0) dma(nxt, buf ^ 1);
     const char* a_base = ATRANS ? sA[buf] + (4 * wm) * 4096 : sA[buf] + (wm * 128 + (lane & 31)) * 128;
     const char* b_base = sB[buf] + (2 * wn) * 4096;
     Frag<bf16_t> fa[2][4], fb[2][2];
@@ -230,6 +229,9 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
       }
     };
     rd(0, 0);
+    // the next stage's loads after the first step's fragment reads, so that their latency
+    // overlaps the load issue
+    if (nxt >= 0) dma(nxt, buf ^ 1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);
@@ -238,13 +240,19 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) mfma_32x32x16(fa[kk & 1][vb], fb[kk & 1][nb], acc[vb][nb]);
     }
-    // the first step's eight fragment reads, then each step's eight MFMAs interleaved with the
-    // next step's reads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // the first step's fragment reads (8, or 12 with A read transposed), then each step's eight
+    // MFMAs interleaved with the next step's reads (two after each of the first four MFMAs when
+    // there are 12)
+    __builtin_amdgcn_sched_group_barrier(0x100, ATRANS ? 12 : 8, 0);
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, ATRANS ? 2 : 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
