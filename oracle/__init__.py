@@ -29,5 +29,7 @@ from .lce import (  # noqa: F401
     grad_input_rows,
     grad_weight_rows,
     grad_bias_entries,
+    filtered_grad_input_tile,
+    filtered_grad_weight_tile,
     liger_chunk_plan,
 )

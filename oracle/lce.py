@@ -483,6 +483,53 @@ def grad_bias_entries(hidden, weight, bias, targets, vocab, lse, *,
     return G.sum(axis=0)
 
 
+def filtered_grad_input_tile(hidden, weight, bias, targets, t0, *, stat_rows: int, stream_rows: int,
+                             filter_eps: float, ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
+                             reduction: str = "mean") -> dict:
+    """grad_input of one token tile under gradient filtering ([P2] "Gradient Filtering"), as
+    lce_oracle_filtered computes it: the tokens t0 .. t0 + stat_rows - 1 (t0 a multiple of
+    stat_rows; fewer at the end of the batch) against the whole vocabulary, in blocks of
+    stream_rows entries aligned at 0; a block whose unscaled dlogits are all below filter_eps in
+    magnitude adds nothing.  Each of these rows depends only on its own token, so the tile is
+    computed exactly as the full call would, from the rows' own logits.  Returns grad_input
+    (the filtered rows), grad_input_exact (the same rows unfiltered), skipped and blocks."""
+    W = _f64(weight)
+    b = _f64(bias)
+    y_all = np.asarray(targets, dtype=np.int64)
+    V = W.shape[0]
+    valid_all = _valid_mask(y_all, V, ignore_index)
+    c = _scale(int(valid_all.sum()), reduction)
+    rows = np.arange(t0, min(int(t0) + stat_rows, y_all.shape[0]))
+    z = _logits(_f64(np.asarray(hidden)[rows]), W, b)
+    g = _dlogits(z, _lse(z), y_all[rows], valid_all[rows], 1.0, float(z_loss))
+    keep, skipped = _block_keep(g, stat_rows, stream_rows, filter_eps)
+    return dict(grad_input=c * (np.where(keep, g, 0.0) @ W), grad_input_exact=c * (g @ W),
+                skipped=skipped, blocks=-(-V // stream_rows))
+
+
+def filtered_grad_weight_tile(hidden, weight, bias, targets, v0, lse, *, stat_rows: int, stream_rows: int,
+                              filter_eps: float, ignore_index: int = IGNORE_INDEX, z_loss: float = 0.0,
+                              reduction: str = "mean") -> dict:
+    """grad_W and grad_b of one vocabulary tile under gradient filtering ([P2] "Gradient
+    Filtering"), as lce_oracle_filtered computes them: the entries v0 .. v0 + stat_rows - 1
+    (v0 a multiple of stat_rows; fewer at the end of the vocabulary) against every token, in
+    blocks of stream_rows tokens aligned at 0, given every token's LSE; a block whose
+    unscaled dlogits are all below filter_eps in magnitude adds nothing.  Returns grad_weight,
+    grad_bias (the filtered rows and entries), their unfiltered values, skipped and blocks."""
+    V = np.asarray(weight).shape[0]
+    BT = np.asarray(hidden).shape[0]
+    vocab = np.arange(v0, min(int(v0) + stat_rows, V))
+    y = np.asarray(targets, dtype=np.int64)
+    c = _scale(int(_valid_mask(y, V, ignore_index).sum()), reduction)
+    G = _dlogit_columns(hidden, weight, bias, targets, vocab, np.asarray(lse, np.float64), ignore_index, z_loss,
+                        "sum")  # (unscaled: the threshold applies before c)
+    keep_t, skipped = _block_keep(G.T, stat_rows, stream_rows, filter_eps)
+    Gk = np.where(keep_t.T, G, 0.0)
+    h = _f64(hidden)
+    return dict(grad_weight=c * (Gk.T @ h), grad_weight_exact=c * (G.T @ h), grad_bias=c * Gk.sum(axis=0),
+                grad_bias_exact=c * G.sum(axis=0), skipped=skipped, blocks=-(-BT // stream_rows))
+
+
 def liger_chunk_plan(BT: int, V: int, H: int) -> dict:
     """Token-chunk sizing of [P1] "The chunk-size trick": inc_factor = ceil(V/H),
     chunk_size = next power of two >= ceil(BT/inc_factor), num_chunks = ceil(BT/chunk_size),

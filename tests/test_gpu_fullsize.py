@@ -166,3 +166,53 @@ def test_filtered_tiny_eps_full_size(name):
     for k in keys[1:]:
         e = float((srt[k].float() - exact[k].float()).norm() / exact[k].float().norm())
         assert e <= tol["grad"], (k, e)
+
+
+@pytest.mark.parametrize("name", ["headline", "gemma_like", "qwen_like"])
+def test_filtered_full_size_sampled_tiles(name):
+    """Gradient filtering at full size with the bench's threshold (eps = 2^-12, "Cut Cross
+    Entropy visualized", "Gradient Filtering"), against the filtered oracle on sampled tiles
+    in the call's own tile shape: grad_input of the first and last token tiles, grad_W (and
+    grad_b) of the first, a middle and the last vocabulary tile, each computed by the oracle
+    from the definitions (every token's LSE from the stored oracle values).  Where the
+    filtered values differ from the exact ones by more than twice the bf16 tolerance, the GPU
+    must be within a quarter of that difference of the filtered oracle, so that the tiles it
+    skipped are the oracle's; a tile with every block skipped must come out exactly zero."""
+    c = CONFIGS[name]
+    print(f"full-size filtering, sampled tiles: {name} BT={c.BT} H={c.H} V={c.V}", flush=True)
+    exp = _expected(name)
+    inp = make_config(name)
+    eps = 2.0 ** -12
+    R, C = lce.filter_tile_shape(c.BT, c.H, c.V, torch.bfloat16)
+    b = None if inp.bias is None else dev(inp.bias, c.dtype)
+    counts = torch.zeros(4, dtype=torch.int64, device="cuda")
+    r = lce.lce_fwd_bwd(dev(inp.hidden, c.dtype), dev(inp.weight, c.dtype), b, dev(inp.targets),
+                        z_loss=c.z_loss, reduction=c.reduction, filter_eps=eps, filter_counts=counts)
+    torch.cuda.synchronize()
+    cnt = counts.cpu().tolist()
+    assert cnt[1] == -(-c.BT // R) * -(-c.V // C) and cnt[3] == -(-c.V // R) * -(-c.BT // C), cnt
+    assert 0 < cnt[0] < cnt[1] and 0 <= cnt[2] < cnt[3], cnt
+    tol = TOL[c.dtype]["grad"]
+    kw = dict(stat_rows=R, stream_rows=C, filter_eps=eps, z_loss=c.z_loss, reduction=c.reduction)
+
+    def check(got, filt, exact, what):
+        if not np.any(filt):
+            assert not np.any(got), what  # every block skipped
+            return
+        d = rel_fro(filt, exact)
+        e = rel_fro(got, filt)
+        print(f"  {what}: filtered vs exact {d:.4f}, GPU vs filtered {e:.4f}", flush=True)
+        assert e <= tol, (what, e)
+        if d > 2 * tol:
+            assert e <= d / 4, (what, e, d)
+
+    for t0 in (0, (c.BT - 1) // R * R):
+        o = oracle.filtered_grad_input_tile(inp.hidden, inp.weight, inp.bias, inp.targets, t0, **kw)
+        got = host64(r["grad_input"][t0:t0 + R])
+        check(got, o["grad_input"], o["grad_input_exact"], f"grad_input tokens {t0}..")
+    for v0 in (0, (c.V // 2) // R * R, (c.V - 1) // R * R):
+        o = oracle.filtered_grad_weight_tile(inp.hidden, inp.weight, inp.bias, inp.targets, v0, exp["lse"], **kw)
+        got = host64(r["grad_weight"][v0:v0 + R])
+        check(got, o["grad_weight"], o["grad_weight_exact"], f"grad_W entries {v0}..")
+        if b is not None:
+            check(host64(r["grad_bias"][v0:v0 + R]), o["grad_bias"], o["grad_bias_exact"], f"grad_b entries {v0}..")

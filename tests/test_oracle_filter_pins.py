@@ -181,3 +181,45 @@ def test_sorting_clusters_the_likely_entries():
     ref = oracle.lce_oracle(inp.hidden, inp.weight, b, y)
     for k in ("grad_input", "grad_weight", "grad_bias"):
         np.testing.assert_allclose(srt[k], ref[k], rtol=0, atol=1e-9, err_msg=k)
+
+
+@pytest.mark.parametrize("R,C", [(64, 16), (256, 64)])
+@pytest.mark.parametrize("mu,reduction", [(0.0, "mean"), (1e-2, "sum")])
+def test_tile_pieces_reassemble_the_filtered_oracle(R, C, mu, reduction):
+    """The one-tile pieces used by full-size checks (filtered_grad_input_tile over R tokens,
+    filtered_grad_weight_tile over R vocabulary entries given every row's LSE) put back
+    together give lce_oracle_filtered's gradients and skip counts, with ragged last tiles in
+    both directions and an eps at which both kept and skipped blocks occur."""
+    BT, V = 3 * R - 7, 5 * R + 3
+    h, W, b, y = _case(BT, 8, V, seed=5, w_std=1.5)
+    eps = 0.1
+    full = oracle.lce_oracle_filtered(h, W, b, y, filter_eps=eps, z_loss=mu, reduction=reduction,
+                                      stat_rows=R, stream_rows=C)
+    assert 0 < full["skipped_input"] < full["tiles_input"]
+    assert 0 < full["skipped_weight"] < full["tiles_weight"]
+    ref = oracle.lce_oracle(h, W, b, y, z_loss=mu, reduction=reduction)
+    kw = dict(stat_rows=R, stream_rows=C, filter_eps=eps, z_loss=mu, reduction=reduction)
+    gi, gie, ski, nbi = [], [], 0, 0
+    for t0 in range(0, BT, R):
+        t = oracle.filtered_grad_input_tile(h, W, b, y, t0, **kw)
+        gi.append(t["grad_input"])
+        gie.append(t["grad_input_exact"])
+        ski += t["skipped"]
+        nbi += t["blocks"]
+    np.testing.assert_allclose(np.concatenate(gi), full["grad_input"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(np.concatenate(gie), ref["grad_input"], rtol=1e-12, atol=1e-15)
+    assert (ski, nbi) == (full["skipped_input"], full["tiles_input"])
+    gw, gb, gwe, gbe, skw, nbw = [], [], [], [], 0, 0
+    for v0 in range(0, V, R):
+        t = oracle.filtered_grad_weight_tile(h, W, b, y, v0, ref["lse"], **kw)
+        gw.append(t["grad_weight"])
+        gb.append(t["grad_bias"])
+        gwe.append(t["grad_weight_exact"])
+        gbe.append(t["grad_bias_exact"])
+        skw += t["skipped"]
+        nbw += t["blocks"]
+    np.testing.assert_allclose(np.concatenate(gw), full["grad_weight"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(np.concatenate(gb), full["grad_bias"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(np.concatenate(gwe), ref["grad_weight"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(np.concatenate(gbe), ref["grad_bias"], rtol=1e-12, atol=1e-15)
+    assert (skw, nbw) == (full["skipped_weight"], full["tiles_weight"])
