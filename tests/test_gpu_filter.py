@@ -93,6 +93,37 @@ def test_filtered_matches_filtered_oracle(case):
         assert int(torch.count_nonzero(r["grad_bias"][lo_r:hi_r])) == 0
 
 
+@pytest.mark.parametrize("case", [("bf16", 700, 1024, 20000, (2560, 10240), "mean", 1e-4, 36),
+                                  ("bf16", 6000, 1024, 1500, (512, 1280), "sum", 0.0, 37)],
+                         ids=["8-blocks", "split-grad_W"])
+def test_filtered_gradient_subsets(case):
+    """A filtered call asked for one gradient only runs that product alone with the tile flags
+    (grad_W and grad_b without the grad_input product, or grad_input by itself): each equals the
+    filtered oracle's, and the counts of the tiles examined stay those of the full call."""
+    dtype, BT, H, V, rv, reduction, mu, seed = case
+    print(f"filtered gradient subsets {case}", flush=True)
+    inp = _inputs(dtype, BT, H, V, rv, seed, mu, reduction)
+    eps = 1e-6
+    R, C = _tiles(dtype, BT, H, V)
+    ref = oracle.lce_oracle_filtered(inp.hidden, inp.weight, inp.bias, inp.targets, filter_eps=eps,
+                                     z_loss=mu, reduction=reduction, stat_rows=R, stream_rows=C)
+    args = (dev(inp.hidden, dtype), dev(inp.weight, dtype), dev(inp.bias, dtype), dev(inp.targets))
+    kw = dict(z_loss=mu, reduction=reduction, filter_eps=eps)
+    tol = TOL[dtype]["grad"]
+    counts = torch.zeros(4, dtype=torch.int64, device="cuda")
+    w = lce.lce_fwd_bwd(*args, grad_input=False, filter_counts=counts, **kw)
+    torch.cuda.synchronize()
+    assert w["grad_input"] is None
+    assert rel_fro(host64(w["grad_weight"]), ref["grad_weight"]) <= tol
+    assert rel_fro(host64(w["grad_bias"]), ref["grad_bias"]) <= tol
+    assert counts[2:].cpu().tolist() == [ref["skipped_weight"], ref["tiles_weight"]]
+    del w
+    i = lce.lce_fwd_bwd(*args, grad_weight=False, grad_bias=False, **kw)
+    torch.cuda.synchronize()
+    assert i["grad_weight"] is None and i["grad_bias"] is None
+    assert rel_fro(host64(i["grad_input"]), ref["grad_input"]) <= tol
+
+
 @pytest.mark.parametrize("dtype,H", [("bf16", 256), ("bf16", 1152), ("f32", 128)])
 def test_tiny_eps_reproduces_exact_call(dtype, H):
     inp = make_fused(160, H, 1000, dtype=dtype, seed=35, w_std=H ** -0.5, bias_std=0.1,
