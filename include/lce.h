@@ -265,8 +265,11 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
  * Strategy 2 keeps each row's target log-probability and softmax entropy beside the LSE)
  * and the gradients of any per-row weighted sum of them.  bf16 only.  The forward is one pass
  * over the vocabulary with no logits stored (LSE and the softmax-weighted mean logit kept per
- * vocabulary tile from the fp32 accumulator, then merged per row); the backward is the
- * token-chunked composition (same chunking as lce_fwd_bwd_chunked).
+ * vocabulary tile from the fp32 accumulator, then merged per row; the tokens in as many
+ * launches as the workspace needs).  The backward runs as lce_fwd_bwd's does, in vocabulary
+ * blocks whose dlogits are formed once from per-token coefficients and feed both gradient
+ * products, within the same one-chunk workspace; where that plan does not fit (tiny sizes) it is
+ * the token-chunked composition of lce_fwd_bwd_chunked.
  *
  * For row t with z_t = W h_t + b, LSE_t = log sum_v exp(z_tv), p_t = softmax(z_t) and
  * valid_t = (y_t != ignore_index):
@@ -283,14 +286,14 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
  *   gamma_t = valid_t (gl_t - gp_t).
  * lse_saved, entropy_saved: device float[BT] each, both or neither (else LCE_ERR_ARG): the LSE
  * and entropy that lce_rows_forward wrote for the same inputs.  With them, E_p[z] = LSE - entropy
- * is known, and each chunk's dlogits come straight from the logits GEMM's fp32 accumulator
- * (no bf16 logits round trip, no second pass over the chunk); without them the chunk's logits
- * are stored in bf16 and its statistics recomputed from them.  Values that do not belong to
- * these inputs give gradients of no meaning (they are not checked).
+ * is known and the dlogits come straight from the logits GEMM's fp32 accumulator; without them
+ * the backward first recomputes LSE and entropy with the forward's pass (on the token-chunked
+ * composition: from the chunk's bf16 logits).  Values that do not belong to these inputs give
+ * gradients of no meaning (they are not checked).
  * flags: LCE_FLAG_CHECK_TARGETS; lce_rows_backward also LCE_FLAG_GRAD_W_FP32.  Workspace:
- * lce_rows_workspace_bytes (the larger of lce_fwd_bwd_chunked_workspace_bytes plus 20 bytes
- * per row, and the forward's per-(vocabulary tile, token) partials); one workspace serves both
- * calls.  Errors
+ * lce_rows_workspace_bytes, within one logits chunk of lce_fwd_bwd wherever the block plan fits
+ * (otherwise the larger of lce_fwd_bwd_chunked_workspace_bytes plus 20 bytes per row and the
+ * forward's per-(vocabulary tile, token) partials); one workspace serves both calls.  Errors
  * as lce_fwd_bwd_chunked.
  */
 size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags);

@@ -45,7 +45,7 @@ size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16) {
     // the two-pass region starts where the LSE partials do
     TwoPass tp{};
     if (H > 1024) tp = twopass_plan(BT, H, V);
-    const SgPlan sp = sg_plan(BT, H, V), sf = sg_plan(BT, H, V, true);  // (exact, filtered or sorted)
+    const SgPlan sp = sg_plan(BT, H, V), sf = sg_plan(BT, H, V, kSgFiltered);  // (exact, filtered or sorted)
     n = std::max(n, fused_small_bytes(BT, V) + std::max({tp.on ? tp.bytes : (size_t)0, sp.on ? sp.bytes : (size_t)0,
                                                          sf.on ? sf.bytes : (size_t)0}));
   }
@@ -74,7 +74,7 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   p += ws_align((size_t)V * 4);
   w.lse_part = reinterpret_cast<float*>(p);  // (at fused_small_bytes)
   w.big = nullptr;
-  if (bf16 && ((H > 1024 && twopass_plan(BT, H, V).on) || sg_plan(BT, H, V).on || sg_plan(BT, H, V, true).on))
+  if (bf16 && ((H > 1024 && twopass_plan(BT, H, V).on) || sg_plan(BT, H, V).on || sg_plan(BT, H, V, kSgFiltered).on))
     w.big = p;
   return w;
 }
@@ -225,7 +225,7 @@ lce_status lce_fwd_bwd_filtered(const void* hidden, const void* W, const void* b
 lce_status lce_filter_tile_shape(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t* rows, int64_t* cols) {
   if (rows == nullptr || cols == nullptr || BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_ARG;
   if (dtype != LCE_DTYPE_BF16 && dtype != LCE_DTYPE_F32) return LCE_ERR_ARG;
-  const bool one = dtype == LCE_DTYPE_BF16 && lce::sg_plan(BT, H, V, true).on;
+  const bool one = dtype == LCE_DTYPE_BF16 && lce::sg_plan(BT, H, V, lce::kSgFiltered).on;
   *rows = one ? 256 : 64;
   *cols = one ? 64 : 16;
   return LCE_OK;
@@ -247,7 +247,7 @@ static lce_status chunk_args(const void* hidden, const void* W, const void* bias
                              int64_t BT, int64_t H, int64_t V, lce_dtype dtype, int64_t ignore_index,
                              float z_loss_mult, uint32_t flags, uint32_t allowed_flags, void* grad_input,
                              void* grad_W, void* grad_b, int64_t* n_valid_out, void* workspace,
-                             size_t workspace_bytes, FusedArgs* a) {
+                             size_t workspace_bytes, size_t need, FusedArgs* a) {
   if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0) return LCE_ERR_SHAPE;
   // (V <= 2^22: the byte offsets inside a 256-row logits tile of the chunk stay 32-bit)
   if (BT > ((int64_t)1 << 40) || V > ((int64_t)1 << 22) || H > ((int64_t)1 << 20)) return LCE_ERR_SHAPE;
@@ -261,8 +261,7 @@ static lce_status chunk_args(const void* hidden, const void* W, const void* bias
       !aligned(workspace, 16) || !aligned(bias, 2) || !aligned(grad_b, 2) || !aligned(targets, 8) ||
       !aligned(n_valid_out, 8))
     return LCE_ERR_ALIGNMENT;
-  if (workspace_bytes < chunked_workspace_bytes(BT, H, V, (flags & LCE_FLAG_GRAD_W_FP32) != 0))
-    return LCE_ERR_WORKSPACE;
+  if (workspace_bytes < need) return LCE_ERR_WORKSPACE;
   *a = FusedArgs{};
   a->hidden = hidden;
   a->W = W;
@@ -279,6 +278,70 @@ static lce_status chunk_args(const void* hidden, const void* W, const void* bias
   a->grad_b = grad_b;
   a->n_valid_out = n_valid_out;
   return LCE_OK;
+}
+
+// the token-chunked composition's workspace (0 for sizes it does not take: chunk_args then
+// reports the shape error)
+static size_t chunk_need(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
+  if (BT < 0 || V < 1 || H < 8 || (H % 8) != 0 || dtype != LCE_DTYPE_BF16) return 0;
+  return chunked_workspace_bytes(BT, H, V, (flags & LCE_FLAG_GRAD_W_FP32) != 0);
+}
+
+// Per-row outputs and their backward on the one-pass plan (kSgRows), when it fits: workspace
+// [fused small pieces | per-token coefficients and entropy | region], the region holding either
+// the forward's LSE and mean-logit partials for fsub tokens at a time or the one-pass plan's
+// buffers.  Everything stays within the one-chunk budget.  one = false: the token-chunked
+// composition instead.
+struct RowsLayout {
+  bool one;
+  SgPlan plan;
+  size_t extra;     // coefficients (rows_coef_bytes) + entropy [BT]
+  int64_t fsub;     // tokens per forward launch (a multiple of 256, or all)
+  size_t part;      // bytes of one partial array (nt x fsub floats)
+  size_t bytes;
+};
+static RowsLayout rows_layout(int64_t BT, int64_t H, int64_t V) {
+  RowsLayout r{};
+  const int64_t bt = BT > 0 ? BT : 1;
+  r.extra = rows_coef_bytes(BT) + ws_align((size_t)bt * 4);
+  r.plan = sg_plan(bt, H, V, kSgRows, r.extra);
+  const int64_t nt = (V + kFwdTileV - 1) / kFwdTileV;
+  const size_t budget = logits_chunk_budget(bt, H, V);
+  const size_t fixed = fused_small_bytes(BT, V) + r.extra + 4096 + alloc_slack(budget);
+  if (!r.plan.on || !r.plan.one || budget <= fixed) return r;
+  // the forward's two partial arrays in the region: as many tokens per launch as fit (all, or
+  // a multiple of 256)
+  const size_t room = std::max(budget - fixed, r.plan.bytes);
+  const size_t half = room / 2 > kWsAlign ? room / 2 - kWsAlign : 0;
+  const int64_t fit = (int64_t)(half / ((size_t)nt * 4));
+  r.fsub = fit >= bt ? bt : fit / 256 * 256;
+  if (r.fsub < 1) return r;
+  r.part = ws_align((size_t)nt * (size_t)r.fsub * 4);
+  r.bytes = fused_small_bytes(BT, V) + r.extra + std::max(r.plan.bytes, 2 * r.part);
+  r.one = true;
+  return r;
+}
+
+// The per-row forward (lse .. row_loss, each may be NULL) in launches of fsub tokens whose
+// partials go to lse_part / ez_part; zy from w.
+static hipError_t rows_forward_sub(const FusedArgs& a, const FusedWs& w, float* lse_part, float* ez_part, int64_t fsub,
+                                   float* lse, float* lp, float* ent, float* rl, hipStream_t st) {
+  const uint16_t* h = static_cast<const uint16_t*>(a.hidden);  // (bf16 rows)
+  auto off = [](float* q, int64_t r0) { return q ? q + r0 : nullptr; };
+  for (int64_t r0 = 0; r0 < a.BT; r0 += fsub) {
+    const int64_t rows = std::min(fsub, a.BT - r0);
+    FusedArgs s = a;
+    s.hidden = h + r0 * a.H;
+    s.targets = a.targets + r0;
+    s.BT = rows;
+    FusedWs ws = w;
+    ws.lse_part = lse_part;
+    ws.zy = w.zy + r0;
+    const hipError_t e = launch_rows_fused_forward(s, ws, ez_part, off(lse, r0), off(lp, r0), off(ent, r0),
+                                                   off(rl, r0), st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 static lce_status chunk_call(const FusedArgs& a, ChunkMode mode, const RowsHost& io, uint32_t flags, void* ws,
@@ -302,7 +365,8 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
   lce::FusedArgs a;
   const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
                                        LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32, grad_input, grad_W, grad_b,
-                                       n_valid_out, workspace, workspace_bytes, &a);
+                                       n_valid_out, workspace, workspace_bytes,
+                                       lce::chunk_need(BT, H, V, dtype, flags), &a);
   if (s != LCE_OK) return s;
   if (loss_out == nullptr) return LCE_ERR_NULL;
   if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_SUM) return LCE_ERR_ARG;
@@ -313,7 +377,8 @@ lce_status lce_fwd_bwd_chunked(const void* hidden, const void* W, const void* bi
   return lce::chunk_call(a, lce::kLoss, lce::RowsHost{}, flags, workspace, stream);
 }
 
-// The per-row forward's own pieces: the fused forward's workspace and the per-tile mean logits.
+// The per-row forward's own pieces (without the one-pass layout): the fused forward's workspace
+// and the per-tile mean logits.
 static size_t rows_forward_bytes(int64_t BT, int64_t V) {
   const int64_t nt = (V + lce::kFwdTileV - 1) / lce::kFwdTileV;
   return lce::fused_base_bytes(BT, V) + lce::ws_align((size_t)nt * (size_t)(BT > 0 ? BT : 1) * 4);
@@ -322,6 +387,8 @@ static size_t rows_forward_bytes(int64_t BT, int64_t V) {
 size_t lce_rows_workspace_bytes(int64_t BT, int64_t H, int64_t V, lce_dtype dtype, uint32_t flags) {
   size_t c = lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags);
   if (c == 0) return 0;
+  const lce::RowsLayout r = lce::rows_layout(BT, H, V);
+  if (r.one) return r.bytes;
   c += lce::rows_coef_bytes(BT);  // (the backward from saved forward outputs)
   const size_t f = rows_forward_bytes(BT, V);
   return c > f ? c : f;
@@ -335,15 +402,14 @@ lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias,
   lce::FusedArgs a;
   const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
                                        LCE_FLAG_CHECK_TARGETS, nullptr, nullptr, nullptr, n_valid_out, workspace,
-                                       workspace_bytes, &a);
+                                       workspace_bytes, lce_rows_workspace_bytes(BT, H, V, dtype, flags), &a);
   if (s != LCE_OK) return s;
   if (!lce::aligned(lse_out, 4) || !lce::aligned(logprobs_out, 4) || !lce::aligned(entropy_out, 4) ||
       !lce::aligned(row_loss_out, 4))
     return LCE_ERR_ALIGNMENT;
-  if (workspace_bytes < rows_forward_bytes(BT, V)) return LCE_ERR_WORKSPACE;
   // one pass over the vocabulary: the fused forward with an (LSE, mean logit) epilogue
   const lce::FusedWs w = lce::fused_carve(workspace, BT, H, V, false);
-  float* ez_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lce::fused_base_bytes(BT, V));
+  const lce::RowsLayout r = lce::rows_layout(BT, H, V);
   hipStream_t st = static_cast<hipStream_t>(stream);
   lce::FusedArgs t = a;
   t.bias = nullptr;  // (the pre-pass only counts; the forward adds the bias itself)
@@ -354,9 +420,17 @@ lce_status lce_rows_forward(const void* hidden, const void* W, const void* bias,
     if (hipStreamSynchronize(st) != hipSuccess) return LCE_ERR_HIP;
     if (bad != 0) return LCE_ERR_TARGET_RANGE;
   }
-  if (lce::launch_rows_fused_forward(a, w, ez_part, lse_out, logprobs_out, entropy_out, row_loss_out, st) !=
-      hipSuccess)
-    return LCE_ERR_HIP;
+  if (r.one) {  // (partials of r.fsub tokens at a time, in the region after the per-row pieces)
+    char* region = static_cast<char*>(workspace) + lce::fused_small_bytes(BT, V) + r.extra;
+    if (lce::rows_forward_sub(a, w, reinterpret_cast<float*>(region), reinterpret_cast<float*>(region + r.part),
+                              r.fsub, lse_out, logprobs_out, entropy_out, row_loss_out, st) != hipSuccess)
+      return LCE_ERR_HIP;
+  } else {
+    float* ez_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lce::fused_base_bytes(BT, V));
+    if (lce::launch_rows_fused_forward(a, w, ez_part, lse_out, logprobs_out, entropy_out, row_loss_out, st) !=
+        hipSuccess)
+      return LCE_ERR_HIP;
+  }
   if (n_valid_out != nullptr &&
       hipMemcpyAsync(n_valid_out, w.n_valid, sizeof(int64_t), hipMemcpyDeviceToDevice, st) != hipSuccess)
     return LCE_ERR_HIP;
@@ -372,18 +446,55 @@ lce_status lce_rows_backward(const void* hidden, const void* W, const void* bias
   lce::FusedArgs a;
   const lce_status s = lce::chunk_args(hidden, W, bias, targets, BT, H, V, dtype, ignore_index, z_loss_mult, flags,
                                        LCE_FLAG_CHECK_TARGETS | LCE_FLAG_GRAD_W_FP32, grad_input, grad_W, grad_b,
-                                       nullptr, workspace, workspace_bytes, &a);
+                                       nullptr, workspace, workspace_bytes,
+                                       lce_rows_workspace_bytes(BT, H, V, dtype, flags), &a);
   if (s != LCE_OK) return s;
   if (!lce::aligned(grad_row_loss, 4) || !lce::aligned(grad_logprobs, 4) || !lce::aligned(grad_entropy, 4) ||
       !lce::aligned(lse_saved, 4) || !lce::aligned(entropy_saved, 4))
     return LCE_ERR_ALIGNMENT;
   if ((lse_saved == nullptr) != (entropy_saved == nullptr)) return LCE_ERR_ARG;
-  if (lse_saved != nullptr && BT > 0 &&
-      workspace_bytes < lce_fwd_bwd_chunked_workspace_bytes(BT, H, V, dtype, flags) + lce::rows_coef_bytes(BT))
-    return LCE_ERR_WORKSPACE;
-  const lce::RowsHost io{nullptr,       nullptr,       nullptr,      nullptr,  grad_row_loss,
-                         grad_logprobs, grad_entropy,  lse_saved,    entropy_saved};
-  return lce::chunk_call(a, lce::kRowGrads, io, flags, workspace, stream);
+  const lce::RowsLayout r = lce::rows_layout(BT, H, V);
+  if (!r.one) {
+    const lce::RowsHost io{nullptr,       nullptr,       nullptr,      nullptr,  grad_row_loss,
+                           grad_logprobs, grad_entropy,  lse_saved,    entropy_saved};
+    return lce::chunk_call(a, lce::kRowGrads, io, flags, workspace, stream);
+  }
+  // One pass: the per-token coefficients (from the saved LSE and entropy, or from a per-row
+  // forward into the workspace), then the one-pass sweep with the per-row dlogits.
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  lce::FusedWs w = lce::fused_carve(workspace, BT, H, V, false);
+  const size_t bt = (size_t)(BT > 0 ? BT : 1);
+  char* ex = static_cast<char*>(workspace) + lce::fused_small_bytes(BT, V);
+  float4* rtok = reinterpret_cast<float4*>(ex);
+  int32_t* rcy = reinterpret_cast<int32_t*>(ex + lce::ws_align(bt * 16));
+  float* ent = reinterpret_cast<float*>(ex + lce::rows_coef_bytes(BT));
+  char* region = ex + r.extra;
+  lce::FusedArgs t = a;
+  t.bias = nullptr;
+  if (lce::launch_targets(t, w, st) != hipSuccess) return LCE_ERR_HIP;
+  if (flags & LCE_FLAG_CHECK_TARGETS) {
+    int32_t bad = 0;
+    if (hipMemcpyAsync(&bad, w.n_bad, sizeof(bad), hipMemcpyDeviceToHost, st) != hipSuccess) return LCE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LCE_ERR_HIP;
+    if (bad != 0) return LCE_ERR_TARGET_RANGE;
+  }
+  const float* lse = lse_saved;
+  const float* entropy = entropy_saved;
+  if (lse == nullptr) {
+    if (lce::rows_forward_sub(a, w, reinterpret_cast<float*>(region), reinterpret_cast<float*>(region + r.part),
+                              r.fsub, w.lse, nullptr, ent, nullptr, st) != hipSuccess)
+      return LCE_ERR_HIP;
+    lse = w.lse;
+    entropy = ent;
+  }
+  if (lce::launch_rows_coef(lse, entropy, a.targets, a.BT, a.V, a.ignore_index, a.mu, grad_row_loss, grad_logprobs,
+                            grad_entropy, rtok, rcy, st) != hipSuccess)
+    return LCE_ERR_HIP;
+  w.big = region;
+  a.mean = false;  // (the per-row weights carry their own scale)
+  a.grad_w_f32 = (flags & LCE_FLAG_GRAD_W_FP32) != 0;
+  if (lce::launch_rows_onepass(a, w, r.plan, rtok, rcy, st) != hipSuccess) return LCE_ERR_HIP;
+  return LCE_OK;
 }
 
 const char* lce_stage_name(int k) {

@@ -247,8 +247,10 @@ __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1
 // visualized", "Gradient Filtering") in flt: whether each 64-entry quarter of the tile (all 256
 // of its tokens) and each 64-token quarter (all 256 of its entries) holds a dlogit (the fp32
 // value, before rounding) of magnitude >= flt.eps; with the counts of quarters without one.
+// MODE kEpiRowsDlogitsT: the kEpiRowsDlogits values written transposed, as kEpiDlogitsT writes
+// its own (the grad_W operand of the per-row backward).
 constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4, kEpiDlogitsT = 5,
-              kEpiDlogitsTF = 6;
+              kEpiDlogitsTF = 6, kEpiRowsDlogitsT = 7;
 
 // (m, s, t) with s = sum e^(z - m), t = sum e^(z - m) z, merged with a second such triple
 __device__ __forceinline__ void mst_combine(float& m, float& s, float& t, float m2, float s2, float t2) {
@@ -275,10 +277,10 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
                                                                     int64_t vbase, float* __restrict__ ez_part,
                                                                     const float4* __restrict__ rtok,
                                                                     const int32_t* __restrict__ rcy, DltExtra flt) {
-  constexpr bool RD = MODE == kEpiRowsDlogits;
+  constexpr bool RD = MODE == kEpiRowsDlogits || MODE == kEpiRowsDlogitsT;
   constexpr bool FLT = MODE == kEpiDlogitsTF;
-  constexpr bool DLT = MODE == kEpiDlogitsT || FLT;
-  constexpr bool DL = MODE == kEpiDlogits || DLT;
+  constexpr bool DLT = MODE == kEpiDlogitsT || FLT || MODE == kEpiRowsDlogitsT;
+  constexpr bool DL = MODE == kEpiDlogits || MODE == kEpiDlogitsT || FLT;  // (per-token LSE and target)
   constexpr bool STORE = MODE == kEpiLogits || DL || RD;
   constexpr bool EZ = MODE == kEpiLseEz;
   constexpr int ROWB = 128;                       // bytes of one row per stage
@@ -470,15 +472,30 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + tl.v0 * ld, (V - tl.v0) * ld * 2);
       __syncthreads();  // every wave has read the last K step's buffers
       char* const stg = (w < 4 ? sA[buf ^ 1] : sB[buf ^ 1]) + (w & 3) * 32 * kPitch;
-      float ra2[2], fac2[2];
+      // per token: the base-2 exponent offset, the factor of p (the z-loss factor, or with RD
+      // alpha + beta z: fac2 = alpha, be2 = beta), the value added at the target column (-1, or
+      // -gamma) and that column in this lane's rows (none if < 0)
+      float ra2[2], fac2[2], be2[2], tg2[2];
       int cy2[2];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const float2 tk = s_tok[wt * 64 + tb * 32 + (ln & 31)];
-        const int yv = __float_as_int(tk.y) - 1;
-        ra2[tb] = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
-        fac2[tb] = 1.f + 2.f * mu * tk.x;
-        cy2[tb] = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+        if constexpr (RD) {
+          const float4 rt = s_rt[wt * 64 + tb * 32 + (ln & 31)];
+          const int yv = s_rcy[wt * 64 + tb * 32 + (ln & 31)];
+          ra2[tb] = rt.x;
+          fac2[tb] = rt.y;
+          be2[tb] = rt.z;
+          tg2[tb] = -rt.w;
+          cy2[tb] = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+        } else {
+          const float2 tk = s_tok[wt * 64 + tb * 32 + (ln & 31)];
+          const int yv = __float_as_int(tk.y) - 1;
+          ra2[tb] = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
+          fac2[tb] = 1.f + 2.f * mu * tk.x;
+          be2[tb] = 0.f;
+          tg2[tb] = -1.f;
+          cy2[tb] = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
+        }
       }
       const int rl = ln >> 3, cl = 8 * (ln & 7);  // read-back: rows 8 i + rl, tokens cl .. cl + 7
       const int64_t tcol = tl.t0 + wt * 64 + cl;
@@ -497,10 +514,12 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
               const int c0 = vb * 32 + 8 * rr + e;
-              const float z0 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e], kLog2e, ra2[tb])), fac2[tb],
-                                    c0 == cy2[tb] ? -1.f : 0.f);
-              const float z1 = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[vb][tb][4 * rr + e + 1], kLog2e, ra2[tb])),
-                                    fac2[tb], c0 + 1 == cy2[tb] ? -1.f : 0.f);
+              const float a0 = acc[vb][tb][4 * rr + e], a1 = acc[vb][tb][4 * rr + e + 1];
+              const float f0 = RD ? fmaf(be2[tb], a0, fac2[tb]) : fac2[tb];
+              const float f1 = RD ? fmaf(be2[tb], a1, fac2[tb]) : fac2[tb];
+              const float z0 = fmaf(__builtin_amdgcn_exp2f(fmaf(a0, kLog2e, ra2[tb])), f0, c0 == cy2[tb] ? tg2[tb] : 0.f);
+              const float z1 =
+                  fmaf(__builtin_amdgcn_exp2f(fmaf(a1, kLog2e, ra2[tb])), f1, c0 + 1 == cy2[tb] ? tg2[tb] : 0.f);
               if constexpr (FLT)  // (rows past the block do not count; tokens past BT hold 0)
                 big[vb >> 1] = big[vb >> 1] || (c0 < lim && !(fabsf(z0) < flt.eps)) ||
                                (c0 + 1 < lim && !(fabsf(z1) < flt.eps));
@@ -1027,6 +1046,25 @@ hipError_t launch_dlogits_block_t(const bf16_t* W_block, const bf16_t* h, const 
   hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogitsT>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
                      st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu, vbase,
                      (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, flt);
+  return hipGetLastError();
+}
+
+// Transposed per-row dlogits (kEpiRowsDlogitsT) of the vocabulary rows vbase .. vbase + V - 1
+// (W_block, bias_block) against all `rows` tokens, from the per-token coefficients rtok / rcy
+// (rows_coef_kernel): gout[v][t] in bf16, rows of ld >= rows tokens (columns rows..ld-1 written
+// as 0); with ext.gbp, grad_b partial sums as DltExtra describes them.
+hipError_t launch_rows_dlogits_block_t(const bf16_t* W_block, const bf16_t* h, const bf16_t* bias_block,
+                                       const float4* rtok, const int32_t* rcy, int64_t rows, int64_t H, int64_t V,
+                                       int64_t vbase, bf16_t* gout, int64_t ld, hipStream_t st,
+                                       const DltExtra& ext) {
+  if (rows <= 0 || V <= 0) return hipSuccess;
+  if (V * ld * 2 > 0x7fffffffll || ld < rows) return hipErrorInvalidValue;
+  if (ext.fin != nullptr || (ext.gbp != nullptr && ext.ldgb < V)) return hipErrorInvalidValue;
+  const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
+  const int64_t nt_t2 = (ld + kFwdTileT2 - 1) / kFwdTileT2;
+  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiRowsDlogitsT>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2),
+                     0, st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld,
+                     (const float2*)nullptr, 0.f, vbase, (float*)nullptr, rtok, rcy, ext);
   return hipGetLastError();
 }
 

@@ -85,9 +85,12 @@ struct SgPlan {
   // rows of vb floats
   size_t gb_bytes;
 };
-// filt: the plan of a filtered call (one pass only, blocks of whole 256-row tiles, room for the
-// tile flags); on = false if it does not fit.
-SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, bool filt = false);
+// kSgExact: the exact call's plan (H >= 1024; one pass, or two above H = 1024).
+// kSgFiltered: a filtered or sorted call's (one pass only, blocks of whole 256-row tiles, room
+// for the tile flags).  kSgRows: the per-row backward's (one pass only, any H).  `reserve`
+// bytes of the one-chunk budget are left to the caller.  on = false if the plan does not fit.
+enum SgPlanKind { kSgExact = 0, kSgFiltered = 1, kSgRows = 2 };
+SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, int kind = kSgExact, size_t reserve = 0);
 
 
 struct FusedArgs {
@@ -140,6 +143,9 @@ hipError_t launch_bwd_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t s
 hipError_t launch_bwd_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st);
 hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st);
+// The per-row backward on the one-pass plan t (kSgRows), from per-token coefficients.
+hipError_t launch_rows_onepass(const FusedArgs& a, const FusedWs& w, const SgPlan& t, const float4* rtok,
+                               const int32_t* rcy, hipStream_t st);
 bool use_twopass(const FusedArgs& a);
 
 // Gradient GEMMs on stored (unscaled) dlogits G [g_rows][ld] of one token chunk.
@@ -201,6 +207,11 @@ struct DltExtra {
 hipError_t launch_dlogits_block_t(const uint16_t* W_block, const uint16_t* h, const uint16_t* bias_block,
                                   const float2* tok, float mu, int64_t rows, int64_t H, int64_t V, int64_t vbase,
                                   uint16_t* gout, int64_t ld, hipStream_t st, const DltExtra& flt = DltExtra{});
+// Transposed per-row dlogits (the per-row backward's G^T), coefficients rtok / rcy per token.
+hipError_t launch_rows_dlogits_block_t(const uint16_t* W_block, const uint16_t* h, const uint16_t* bias_block,
+                                       const float4* rtok, const int32_t* rcy, int64_t rows, int64_t H, int64_t V,
+                                       int64_t vbase, uint16_t* gout, int64_t ld, hipStream_t st,
+                                       const DltExtra& ext = DltExtra{});
 
 // Stored-operand GEMM (bf16, fp32 accumulation): C = A . B over K split into ranges of ksplit
 // (a multiple of 64), one workgroup per (256 x 256 tile, range).  A [M][lda] is K-contiguous,

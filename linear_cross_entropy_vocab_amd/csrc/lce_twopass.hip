@@ -158,7 +158,7 @@ static bool exact_call(const FusedArgs& a) { return !(a.filter_eps > 0.f) && a.o
 bool use_twopass(const FusedArgs& a) {
   if (!a.bf16) return false;
   if (exact_call(a) && sg_plan(a.BT, a.H, a.V).on) return true;
-  if (!exact_call(a) && sg_plan(a.BT, a.H, a.V, true).on) return true;
+  if (!exact_call(a) && sg_plan(a.BT, a.H, a.V, kSgFiltered).on) return true;
   return a.H > 1024 && twopass_plan(a.BT, a.H, a.V).on;
 }
 
@@ -181,7 +181,7 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
   if (exact_call(a)) {
     const SgPlan t = sg_plan(a.BT, a.H, a.V);
     if (t.on) return t.one ? launch_sg_onepass(a, w, st) : launch_sg_dinput(a, w, st);
-  } else if (sg_plan(a.BT, a.H, a.V, true).on) {
+  } else if (sg_plan(a.BT, a.H, a.V, kSgFiltered).on) {
     return launch_sg_onepass(a, w, st);
   }
   const TwoPass t = twopass_plan(a.BT, a.H, a.V);
@@ -227,7 +227,7 @@ hipError_t launch_twopass_dinput(const FusedArgs& a, const FusedWs& w, hipStream
 }
 
 hipError_t launch_twopass_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  const SgPlan sp = sg_plan(a.BT, a.H, a.V, !exact_call(a));
+  const SgPlan sp = sg_plan(a.BT, a.H, a.V, exact_call(a) ? kSgExact : kSgFiltered);
   if (sp.on) {
     if (sp.one && a.grad_input != nullptr && a.BT > 0) return hipSuccess;  // (done with grad_input)
     return launch_sg_dweight(a, w, st);
@@ -328,15 +328,16 @@ size_t flag_bytes(int64_t BT, int64_t vb) {
 }
 }  // namespace
 
-SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, bool filt) {
+SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, int kind, size_t reserve) {
   SgPlan t{};
   t.on = false;
-  if (BT <= 0 || V <= 0 || H < kSgMinH) return t;
+  const bool filt = kind == kSgFiltered, one_only = kind != kSgExact;
+  if (BT <= 0 || V <= 0 || (kind != kSgRows && H < kSgMinH)) return t;
   const size_t budget = logits_chunk_budget(BT, H, V);
   const size_t base = fused_small_bytes(BT, V);  // (as in twopass_plan)
   const size_t slack = alloc_slack(budget);
-  if (budget <= base + 4096 + slack) return t;
-  const size_t avail = budget - base - 4096 - slack;
+  if (budget <= base + 4096 + slack + reserve) return t;
+  const size_t avail = budget - base - 4096 - slack - reserve;
   // hidden is the B operand of pass 1 (32-bit offsets)
   if ((int64_t)BT * H * 2 >= 0x7fffffffll) return t;
   // pass 1: evenly sized vocabulary blocks (multiples of 64 rows) whose G^T fits
@@ -346,7 +347,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, bool filt) {
   const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)t.ldv * 2)) / 64 * 64, round_up(V, 64));
   if (v_fit < 64) return t;
   double best1 = -1.0, best2 = -1.0;
-  if (!filt) {  // (a filtered call takes the one-pass plan below or none)
+  if (!one_only) {  // (filtered, sorted and per-row calls take the one-pass plan below or none)
   // (with ns1 > 1 the tokens are split into K-ranges whose fp32 partial sums are reduced into
   // the grad_W rows of the block: more workgroups per block when H gives few column tiles)
   for (int64_t ns1 = 1; ns1 <= 16; ++ns1) {
@@ -458,7 +459,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, bool filt) {
         }
       }
     }
-    if (best >= 0 && (filt || !t.on || best < best1 + best2)) {
+    if (best >= 0 && (one_only || !t.on || best < best1 + best2)) {
       t.one = true;
       t.lo_bytes = lo;
       t.vb = vb1;
@@ -532,7 +533,10 @@ hipError_t launch_sg_dinput(const FusedArgs& a, const FusedWs& w, hipStream_t st
 // flags the tiles of both products that hold a dlogit of magnitude >= filter_eps, and the GEMMs
 // run the flagged K stages only (grad_b likewise sums the flagged token groups only); with the
 // sort's order, the rows of grad_W and grad_b go to out_row_map[row].
-static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bool dinput, hipStream_t st) {
+// With rtok / rcy (the per-row backward), the dlogits are those of the per-row weighted sum
+// (kEpiRowsDlogitsT, coefficients of rows_coef_kernel) and a.mean is false.
+static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t, bool dinput, hipStream_t st,
+                           const float4* rtok = nullptr, const int32_t* rcy = nullptr) {
   bf16_t* g = reinterpret_cast<bf16_t*>(w.big + 256);
   float* part1 = reinterpret_cast<float*>(w.big + 256 + t.g1_bytes);
   uint8_t* lo = reinterpret_cast<uint8_t*>(w.big + 256 + t.g1_bytes + t.part1_bytes);
@@ -558,9 +562,11 @@ static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t
   hipError_t e;
   for (int64_t k = 0; k < nblk; ++k) {
     const int64_t v0 = k * t.vb, rows = std::min(t.vb, a.V - v0);
-    if ((e = launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT, a.H, rows,
-                                    v0, g, t.ldv, st, flt)) != hipSuccess)
-      return e;
+    e = rtok != nullptr ? launch_rows_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, rtok, rcy,
+                                                      a.BT, a.H, rows, v0, g, t.ldv, st, flt)
+                        : launch_dlogits_block_t(W + v0 * a.H, h, b != nullptr ? b + v0 : nullptr, w.tok, a.mu, a.BT,
+                                                 a.H, rows, v0, g, t.ldv, st, flt);
+    if (e != hipSuccess) return e;
     void* wout = nullptr;
     const int64_t o0 = map != nullptr ? 0 : v0;  // (sorted: rows through the order)
     SgArgs mw{};  // grad_W[block] = c G^T . hidden
@@ -629,16 +635,25 @@ static hipError_t sg_sweep(const FusedArgs& a, const FusedWs& w, const SgPlan& t
 }
 
 hipError_t launch_sg_dweight(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  const SgPlan t = sg_plan(a.BT, a.H, a.V, !exact_call(a));
+  const SgPlan t = sg_plan(a.BT, a.H, a.V, exact_call(a) ? kSgExact : kSgFiltered);
   if (!t.on || w.big == nullptr) return hipErrorInvalidValue;
   return sg_sweep(a, w, t, false, st);
 }
 
 // One-pass plan: the whole backward (grad_input and, as requested, grad_W and grad_b).
 hipError_t launch_sg_onepass(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
-  const SgPlan t = sg_plan(a.BT, a.H, a.V, !exact_call(a));
+  const SgPlan t = sg_plan(a.BT, a.H, a.V, exact_call(a) ? kSgExact : kSgFiltered);
   if (!t.on || !t.one || w.big == nullptr) return hipErrorInvalidValue;
   return sg_sweep(a, w, t, a.grad_input != nullptr && a.BT > 0, st);
+}
+
+// The per-row backward on the one-pass plan (kSgRows): grad_input, grad_W and grad_b of
+// sum_t gl row_loss_t + gp logprobs_t + ge entropy_t from the per-token coefficients rtok / rcy,
+// with the same grouped GEMMs and running sum as the exact call.  a.mean must be false.
+hipError_t launch_rows_onepass(const FusedArgs& a, const FusedWs& w, const SgPlan& t, const float4* rtok,
+                               const int32_t* rcy, hipStream_t st) {
+  if (!t.on || !t.one || w.big == nullptr || a.mean || rtok == nullptr || rcy == nullptr) return hipErrorInvalidValue;
+  return sg_sweep(a, w, t, a.grad_input != nullptr && a.BT > 0, st, rtok, rcy);
 }
 
 }  // namespace lce

@@ -92,6 +92,18 @@ def test_filter_tile_shape(lib):
     assert lib.lce_filter_tile_shape(10, 64, 10, BF16, None, None) == ERR_ARG
 
 
+@pytest.mark.parametrize("name", ["gemma_like", "headline", "qwen_like"])
+def test_rows_workspace_within_one_logits_chunk(lib, name):
+    """The per-row entry points (forward, and the backward on the one-pass plan) keep their
+    workspace within the same one-chunk budget as the fused call."""
+    c = CONFIGS[name]
+    lib.lce_rows_workspace_bytes.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_int, ctypes.c_uint32]
+    lib.lce_rows_workspace_bytes.restype = ctypes.c_size_t
+    ws = lib.lce_rows_workspace_bytes(c.BT, c.H, c.V, BF16, 0)
+    budget = liger_chunk_plan(c.BT, c.V, c.H)["chunk_bytes"]
+    assert 0 < ws <= budget, (ws, budget)
+
+
 def test_workspace_sizes(lib):
     assert lib.lce_fwd_bwd_workspace_bytes(-1, 64, 10, BF16, 0) == 0
     assert lib.lce_fwd_bwd_workspace_bytes(10, 12, 10, BF16, 0) == 0   # H % 8 != 0
