@@ -342,8 +342,9 @@ def lce_rows_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional
 
 
 class _LinearRows(torch.autograd.Function):
-    """(logprobs, entropy, row_loss) per row; the backward recomputes the logits chunk by chunk,
-    forming the dlogits from the saved LSE and entropy."""
+    """(logprobs, entropy, row_loss) per row; the backward recomputes the logits block by
+    block, forming the dlogits from the saved LSE and entropy (within the same one-chunk
+    workspace as the forward)."""
 
     @staticmethod
     def forward(ctx, hidden, weight, bias, targets, ignore_index, z_loss):
