@@ -305,8 +305,8 @@ def lce_rows_backward(hidden: torch.Tensor, weight: torch.Tensor, bias: Optional
                       workspace: Optional[torch.Tensor] = None) -> dict:
     """lce_rows_backward: gradients of sum_t gl_t row_loss_t + gp_t logprobs_t + ge_t entropy_t
     (upstream gradients float32 [BT] on the device, or None for zeros).  `lse` and `entropy`,
-    both or neither, are lce_rows_forward's outputs for the same inputs: with them the logits
-    are not stored (each chunk's dlogits come from the GEMM accumulator)."""
+    both or neither, are lce_rows_forward's outputs for the same inputs: with them the backward
+    does not recompute them (the dlogits come straight from the GEMM accumulator)."""
     BT, H, V = _rows_common(hidden, weight, bias, targets)
     if (lse is None) != (entropy is None):
         raise ValueError("pass both lse and entropy, or neither")
