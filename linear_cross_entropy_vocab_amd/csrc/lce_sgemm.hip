@@ -18,8 +18,12 @@
 //    (sub-block j = K-rows 16 j .. 16 j + 15 in 1 KiB).  The B operand of a 32 x 32 x 16 step
 //    (K-rows 8 h .. 8 h + 7 of column c in lane 32 h + c) is two ds_read_b64_tr_b16 of that
 //    layout: a 16-lane group reads a 4-row x 32-byte block and receives it transposed.
-// The next stage's loads are issued right after the barrier that frees their buffer, so they
-// overlap the current stage's MFMAs.
+// The next stage's loads are issued right after the barrier that frees their buffer (after the
+// first step's fragment reads), so they overlap the current stage's MFMAs.
+// Gradient filtering ("Cut Cross Entropy visualized", "Gradient Filtering"): with per-tile
+// stage flags (SgArgs::kflags), a tile runs only its flagged K stages, in order, through the
+// same load pipeline; a running-sum tile with none leaves the sum as it is.  With a row map
+// (SgArgs::row_map) the plain output's rows go where the map says (vocabulary sorting).
 #include "lce_common.h"
 #include "lce_launch.h"
 
