@@ -288,12 +288,14 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
   constexpr int TILE_B = kFwdTileT2 * ROWB;       // 32 KiB
   __shared__ __attribute__((aligned(1024))) char sA[2][TILE_A];
   __shared__ __attribute__((aligned(1024))) char sB[2][TILE_B];
-  __shared__ float s_bias[kFwdTileV];
+  // Per-tile side data, loaded into LDS one tile ahead (double buffer): bf16 bias entries
+  // (1 KiB region), then (DL) the tokens' (LSE, target + 1) or (RD) their coefficients and
+  // target columns.
+  constexpr int kSideTok = 1024, kSideRcy = kSideTok + (RD ? 16 : 8) * kFwdTileT2;
+  constexpr int kSide = kSideTok + (DL ? 8 * kFwdTileT2 : 0) + (RD ? 20 * kFwdTileT2 : 0);
+  __shared__ __attribute__((aligned(16))) char s_side[2][kSide];
   __shared__ float red_m[2][kFwdTileT2], red_s[2][kFwdTileT2];
   __shared__ float red_t[EZ ? 2 : 1][EZ ? kFwdTileT2 : 1];
-  __shared__ float2 s_tok[DL ? kFwdTileT2 : 1];
-  __shared__ float4 s_rt[RD ? kFwdTileT2 : 1];
-  __shared__ int32_t s_rcy[RD ? kFwdTileT2 : 1];
   __shared__ int s_flw[FLT ? 8 : 1];  // (FLT) per wave: bit 0 / 1 its first / second 64 rows hold a large dlogit
   __shared__ float s_gb[DLT ? 8 : 1][DLT ? 128 : 1];  // (DLT, grad_b) per wave: its rows' sums over its 64 tokens
   // (FLT) threads 0-3: grad_input quarters (entries 64 tid ..) examined and skipped over this
@@ -353,32 +355,54 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     }
   };
 
+  // A tile's side data, one 16-byte load into LDS per lane from one wave each: wave 0 the
+  // bias entries (from the 16-byte boundary at or below the tile's first entry: bsh entries
+  // earlier), waves 1-2 the token pairs, or waves 3-6 the coefficients and wave 7 the target
+  // columns.  A 16-byte load is whole or zero, so each range is taken up to the end of its last
+  // 16-byte block (the token arrays' workspace regions are padded to 256 bytes; a block never
+  // crosses a page); entries past V and tokens past BT are masked where they are read.
+  const uint32_t lside = lds_addr(s_side[0]);
+  const int bsh = (int)((reinterpret_cast<uintptr_t>(bias) & 15) >> 1);
+  auto side = [&](const Tile& t1, int sb) {
+    const uint32_t ls = lside + (uint32_t)(sb * kSide);
+    if (w == 0 && bias != nullptr) {
+      const bf16_t* b0 = bias + t1.v0 - bsh;  // 16-byte aligned
+      const u32x4_t r = make_rsrc_words(b0, ((V - t1.v0 + bsh) * 2 + 15) & ~(int64_t)15);
+      dma16(r, ls, lane < 33 ? (uint32_t)(16 * lane) : 0x80000000u);
+    }
+    if constexpr (DL) {
+      if (w == 1 || w == 2) {
+        const u32x4_t r = make_rsrc_words(tok + t1.t0, ((BT - t1.t0) * 8 + 15) & ~(int64_t)15);
+        dma16(r, ls + kSideTok + 1024u * (w - 1), (uint32_t)(1024 * (w - 1) + 16 * lane));
+      }
+    }
+    if constexpr (RD) {
+      if (w >= 3 && w <= 6) {
+        const u32x4_t r = make_rsrc_words(rtok + t1.t0, (BT - t1.t0) * 16);
+        dma16(r, ls + kSideTok + 1024u * (w - 3), (uint32_t)(1024 * (w - 3) + 16 * lane));
+      } else if (w == 7) {
+        const u32x4_t r = make_rsrc_words(rcy + t1.t0, ((BT - t1.t0) * 4 + 15) & ~(int64_t)15);
+        dma16(r, ls + kSideRcy, (uint32_t)(16 * lane));
+      }
+    }
+  };
+
   // fragment rows: (wv*128 + vb*32 + lane%32) and (wt*64 + tb*32 + lane%32); the swizzle
   // depends only on row % 16 = lane % 16, so one XOR value serves every block
   const int fs = fsw(lane & 31);
   int64_t blk = blockIdx.x;
   if (blk >= nwg) return;
   Tile tl = tile_of(blk);
-  int buf = 0;
+  int buf = 0, sb = 0;
+  bool first = true;
   dma(tl, 0, 0);
+  side(tl, 0);
   for (;;) {
-    if (bias != nullptr && tid < kFwdTileV) {  // (the previous tile is done with s_bias)
-      const int64_t v = tl.v0 + tid;
-      s_bias[tid] = v < V ? bf2f(bias[v]) : 0.f;
-    }
-    if constexpr (DL) {  // the tile's tokens: (LSE, target + 1)
-      if (tid < kFwdTileT2) {
-        const int64_t t = tl.t0 + tid;
-        s_tok[tid] = t < BT ? tok[t] : make_float2(0.f, 0.f);
-      }
-    }
-    if constexpr (RD) {  // the tile's tokens: coefficients and target column
-      if (tid < kFwdTileT2) {
-        const int64_t t = tl.t0 + tid;
-        s_rt[tid] = t < BT ? rtok[t] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
-        s_rcy[tid] = t < BT ? rcy[t] : -1;
-      }
-    }
+    const bf16_t* const s_bias = reinterpret_cast<const bf16_t*>(s_side[sb]) + bsh;
+    const float2* const s_tok = reinterpret_cast<const float2*>(s_side[sb] + kSideTok);
+    const float4* const s_rt = reinterpret_cast<const float4*>(s_side[sb] + kSideTok);
+    const int32_t* const s_rcy = reinterpret_cast<const int32_t*>(s_side[sb] + kSideRcy);
+    (void)s_tok; (void)s_rt; (void)s_rcy;
     const int64_t nblk = blk + gridDim.x;
     const bool has_next = nblk < nwg;
     const Tile tn = has_next ? tile_of(nblk) : tl;
@@ -391,7 +415,11 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     for (int64_t ks = 0; ks < nk; ++ks) {
-      vm_wait<0>();     // this wave's part of stage ks has landed
+      // this wave's part of stage ks (and, at ks = 0, of the tile's side data) has landed;
+      // after a transposed-dlogits tile its 16 stores per lane followed these loads, and the
+      // counter retires loads and stores in issue order, so they need not have completed
+      if (DLT && ks == 0 && !first) vm_wait<16>();
+      else vm_wait<0>();
       __syncthreads();  // stage ks is in LDS for every wave; the other buffer is no longer read
       const char* a_base = sA[buf] + (wv * 128 + (lane & 31)) * ROWB;
       const char* b_base = sB[buf] + (wt * 64 + (lane & 31)) * ROWB;
@@ -407,8 +435,12 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       // the next stage, which after the last one is the first stage of the next tile (so its
       // load overlaps this tile's epilogue), issued after the first step's fragment reads so
       // that their latency overlaps the load issue
-      if (ks + 1 < nk) dma(tl, ks + 1, buf ^ 1);
-      else if (has_next) dma(tn, 0, buf ^ 1);
+      if (ks + 1 < nk) {
+        dma(tl, ks + 1, buf ^ 1);
+      } else if (has_next) {
+        dma(tn, 0, buf ^ 1);
+        side(tn, sb ^ 1);  // (the previous tile, the last reader of that buffer, is done)
+      }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk + 1 < 4) rd(kk + 1, (kk + 1) & 1);
@@ -434,6 +466,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       buf ^= 1;
     }
 
+    first = false;
     // z += b as one more MFMA step per accumulator: A holds b[row] at k = 0 (lanes 0..31,
     // the rows of the 32-row block), B holds 1 at k = 0; both bf16, so the product is exact
     // and the bias costs no per-element work in the epilogue.
@@ -444,7 +477,8 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
         zero8(fbias[vb]);
-        if (lane < 32) fbias[vb].v[0] = (short)f2bf(s_bias[wv * 128 + vb * 32 + lane]);
+        const int bi = wv * 128 + vb * 32 + lane;
+        if (lane < 32 && tl.v0 + bi < V) fbias[vb].v[0] = (short)s_bias[bi];
       }
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb)
@@ -480,15 +514,18 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         if constexpr (RD) {
-          const float4 rt = s_rt[wt * 64 + tb * 32 + (ln & 31)];
-          const int yv = s_rcy[wt * 64 + tb * 32 + (ln & 31)];
+          const int tr = wt * 64 + tb * 32 + (ln & 31);
+          const bool tv = tl.t0 + tr < BT;
+          const float4 rt = tv ? s_rt[tr] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+          const int yv = tv ? s_rcy[tr] : -1;
           ra2[tb] = rt.x;
           fac2[tb] = rt.y;
           be2[tb] = rt.z;
           tg2[tb] = -rt.w;
           cy2[tb] = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
         } else {
-          const float2 tk = s_tok[wt * 64 + tb * 32 + (ln & 31)];
+          const int tr = wt * 64 + tb * 32 + (ln & 31);
+          const float2 tk = tl.t0 + tr < BT ? s_tok[tr] : make_float2(0.f, 0.f);
           const int yv = __float_as_int(tk.y) - 1;
           ra2[tb] = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
           fac2[tb] = 1.f + 2.f * mu * tk.x;
@@ -615,6 +652,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       if (!has_next) break;
       blk = nblk;
       tl = tn;
+      sb ^= 1;
       continue;
     }
     if constexpr (STORE) {
@@ -633,7 +671,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         float ra = 0.f, fac = 0.f;
         int cy = -1;
         if constexpr (MODE == kEpiDlogits) {
-          const float2 tk = s_tok[trow];
+          const float2 tk = tl.t0 + trow < BT ? s_tok[trow] : make_float2(0.f, 0.f);
           const int yv = __float_as_int(tk.y) - 1;
           ra = yv >= 0 ? -tk.x * kLog2e : -INFINITY;
           fac = 1.f + 2.f * mu * tk.x;
@@ -641,12 +679,13 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         }
         float al = 0.f, be = 0.f, ga = 0.f;
         if constexpr (RD) {
-          const float4 rt = s_rt[trow];
+          const bool tv = tl.t0 + trow < BT;
+          const float4 rt = tv ? s_rt[trow] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
           ra = rt.x;
           al = rt.y;
           be = rt.z;
           ga = -rt.w;
-          const int yv = s_rcy[trow];
+          const int yv = tv ? s_rcy[trow] : -1;
           cy = yv >= 0 ? yv - (int)(vbase + tl.v0) - vrow : -1;
         }
 #pragma unroll
@@ -689,6 +728,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       if (!has_next) break;
       blk = nblk;
       tl = tn;
+      sb ^= 1;
       continue;
     }
     // Epilogue: per token column, (max, sum exp) over this wave's 128 vocabulary rows, the
@@ -755,6 +795,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
     if (!has_next) break;
     blk = nblk;
     tl = tn;
+    sb ^= 1;
   }
   if constexpr (FLT) {
     if (tid < 8 && flt.cnt != nullptr && n_exam > 0) {
