@@ -577,7 +577,7 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
           const u32x4_t q = *reinterpret_cast<const u32x4_t*>(stg + (8 * i + rl) * kPitch + 2 * cl);
           const int row = wv * 128 + vb * 32 + 8 * i + rl;  // of the tile
           const uint32_t off = col_ok ? (uint32_t)(((int64_t)row * ld + tcol) * 2) : 0x80000000u;
-          __builtin_amdgcn_raw_buffer_store_b128(q, rz, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(q, rz, (int)off, 0, 2);  // (nt: streaming)
         }
         asm volatile("" ::: "memory");  // (the block is rewritten for the next vb)
         if (gbs) {
