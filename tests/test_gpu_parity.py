@@ -138,6 +138,50 @@ def test_minus_inf_bias_tiles_vs_oracle(case):
         assert int(torch.count_nonzero(g)) == 0, k
 
 
+def _offset_copy(x: torch.Tensor, k: int) -> torch.Tensor:
+    """x copied into a fresh buffer k elements past its (256-byte aligned) start."""
+    big = torch.zeros(x.numel() + 16, dtype=x.dtype, device=x.device)
+    v = big[k:k + x.numel()]
+    v.copy_(x)
+    return v
+
+
+@pytest.mark.parametrize("shape", [(333, 256, 3001), (700, 1024, 20000), (130, 1152, 600)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bias_at_any_element_offset(shape):
+    """A bf16 bias that starts 1, 3 or 7 elements past a 16-byte boundary (a view into a larger
+    buffer) gives bit for bit the results of the same bias at an aligned address: the fused
+    call, the per-row forward and backward, and the token-chunked composition (the forward
+    kernels take the bias entries of a tile from the 16-byte boundary below the tile)."""
+    BT, H, V = shape
+    print(f"offset-bias case {shape}", flush=True)
+    inp = make_fused(BT, H, V, dtype="bf16", seed=BT + H, bias_std=0.3, ignore_frac=0.1, z_loss=1e-4)
+    h, w, y = dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), dev(inp.targets)
+    b0 = dev(inp.bias, "bf16")
+    assert b0.data_ptr() % 16 == 0
+    ref = lce.lce_fwd_bwd(h, w, b0, y, z_loss=1e-4, return_lse=True)
+    rf0 = lce.lce_rows_forward(h, w, b0, y, z_loss=1e-4)
+    gl = torch.linspace(-1.0, 1.0, BT, device="cuda", dtype=torch.float32)
+    rb0 = lce.lce_rows_backward(h, w, b0, y, grad_row_loss=gl, grad_entropy=0.5 * gl, z_loss=1e-4)
+    ch0 = lce.lce_fwd_bwd(h, w, b0, y, z_loss=1e-4, method="chunked")
+    torch.cuda.synchronize()
+    oref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=1e-4)
+    check_fused(inp, ref, oref)
+    for k in (1, 3, 7):
+        b = _offset_copy(b0, k)
+        assert b.data_ptr() % 16 == 2 * k
+        r = lce.lce_fwd_bwd(h, w, b, y, z_loss=1e-4, return_lse=True)
+        rf = lce.lce_rows_forward(h, w, b, y, z_loss=1e-4)
+        rb = lce.lce_rows_backward(h, w, b, y, grad_row_loss=gl, grad_entropy=0.5 * gl, z_loss=1e-4)
+        ch = lce.lce_fwd_bwd(h, w, b, y, z_loss=1e-4, method="chunked")
+        torch.cuda.synchronize()
+        for name, x, x0 in (("fused", r, ref), ("rows forward", rf, rf0), ("rows backward", rb, rb0),
+                            ("chunked", ch, ch0)):
+            for key, t0 in x0.items():
+                if isinstance(t0, torch.Tensor) and key != "workspace":  # (scratch contents)
+                    assert torch.equal(x[key], t0), (name, key, k)
+
+
 @pytest.mark.parametrize("shape", [(120, 256, 900), (600, 1152, 9000), (700, 1024, 20000)],
                          ids=["pipelined", "one-pass", "one-pass-1024"])
 def test_grad_subsets(shape):
