@@ -292,65 +292,53 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(base, mrows * ld * es);
     const __amdgpu_buffer_rsrc_t rl8 =
         make_rsrc(p.hilo != 0 ? reinterpret_cast<char*>(p.lo + m0 * p.ldlo) : base, p.hilo != 0 ? mrows * p.ldlo : 0);
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + 32 * nb + (lane & 31)] = acc[vb][nb][r];
-      float v[4][8];
-      uint32_t off[4], offl[4];
-      int64_t orow[4];  // (row_map) output row, or -1 past the tile's rows or columns
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 a = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl);
-        const float4 b = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl + 4);
-        v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
-        v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
-        const int m = 128 * wm + 32 * vb + 8 * i + rl;
-        off[i] = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
-        offl[i] = cok ? (uint32_t)(m * p.ldlo + n8) : 0x80000000u;
-        orow[i] = p.row_map != nullptr && cok && m < mrows ? (int64_t)p.row_map[m0 + m] : -1;
-      }
-      if (p.C != nullptr) {  // fp32 partial sums, written or added
-        if (p.accumulate) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[i], 0, 0));
-            const float4 b =
-                __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)(off[i] + 16), 0, 0));
-            v[i][0] += a.x; v[i][1] += a.y; v[i][2] += a.z; v[i][3] += a.w;
-            v[i][4] += b.x; v[i][5] += b.y; v[i][6] += b.z; v[i][7] += b.w;
-          }
-        }
+    if (p.hilo >= 2) {
+      // the running sum's middle and last blocks (read, add, write): each 32-row block's hi and
+      // remainder loads are issued two blocks ahead, so that their round trips overlap (all four
+      // ahead would not fit the registers)
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      u32x4_t hv[2][4];
+      u32x2_t lv[2][4];
+      auto issue = [&](int vb, int slot) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][0], v[i][1], v[i][2], v[i][3])),
-                                                 ro, (int)off[i], 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][4], v[i][5], v[i][6], v[i][7])),
-                                                 ro, (int)(off[i] + 16), 0, 0);
+          const int m = 128 * wm + 32 * vb + 8 * i + rl;
+          const uint32_t o = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
+          const uint32_t ol = cok ? (uint32_t)(m * p.ldlo + n8) : 0x80000000u;
+          hv[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)o, 0, 0);
+          lv[slot][i] = __builtin_amdgcn_raw_buffer_load_b64(rl8, (int)ol, 0, 0);
         }
-      } else if (p.hilo != 0) {  // running sum hi + q (rem_step above): 16 + 8 bytes per lane
-        if (p.hilo != 1) {
-          u32x4_t hv[4];
-          uint32_t lv[4][2];
+      };
+      issue(0, 0);
+      issue(1, 1);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hv[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[i], 0, 0);
-            const auto l2 = __builtin_amdgcn_raw_buffer_load_b64(rl8, (int)offl[i], 0, 0);
-            lv[i][0] = l2[0];
-            lv[i][1] = l2[1];
+      for (int vb = 0; vb < 4; ++vb) {
+        const int slot = vb & 1;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + 32 * nb + (lane & 31)] = acc[vb][nb][r];
+        float v[4][8];
+        uint32_t off[4], offl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 a = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl);
+          const float4 b = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl + 4);
+          v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+          v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+          const int m = 128 * wm + 32 * vb + 8 * i + rl;
+          off[i] = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
+          offl[i] = cok ? (uint32_t)(m * p.ldlo + n8) : 0x80000000u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t h16 = (e & 1) ? (hv[slot][i][e >> 1] >> 16) : (hv[slot][i][e >> 1] & 0xffffu);
+            const int32_t q = (int32_t)(int8_t)((lv[slot][i][e >> 2] >> (8 * (e & 3))) & 0xffu);
+            v[i][e] += bf2f((bf16_t)h16) + (float)q * rem_step(h16);
           }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t h16 = (e & 1) ? (hv[i][e >> 1] >> 16) : (hv[i][e >> 1] & 0xffffu);
-              const int32_t q = (int32_t)(int8_t)((lv[i][e >> 2] >> (8 * (e & 3))) & 0xffu);
-              v[i][e] += bf2f((bf16_t)h16) + (float)q * rem_step(h16);
-            }
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           u32x4_t ho;
@@ -366,48 +354,104 @@ __device__ __forceinline__ void sgemm_tile(const SgArgs& p, uint32_t id, char (*
             }
           }
           __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
-          if (p.hilo != 3) {
+          if (p.hilo != 3) __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo[0], lo[1]}, rl8, (int)offl[i], 0, 0);
+        }
+        if (vb + 2 < 4) issue(vb + 2, slot);
+        asm volatile("" ::: "memory");  // (the region is rewritten for the next block)
+      }
+    } else {
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            reg[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kPitch + 32 * nb + (lane & 31)] = acc[vb][nb][r];
+        float v[4][8];
+        uint32_t off[4], offl[4];
+        int64_t orow[4];  // (row_map) output row, or -1 past the tile's rows or columns
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 a = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl);
+          const float4 b = *reinterpret_cast<const float4*>(reg + (8 * i + rl) * kPitch + cl + 4);
+          v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+          v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+          const int m = 128 * wm + 32 * vb + 8 * i + rl;
+          off[i] = cok ? (uint32_t)((m * ld + n8) * es) : 0x80000000u;
+          offl[i] = cok ? (uint32_t)(m * p.ldlo + n8) : 0x80000000u;
+          orow[i] = p.row_map != nullptr && cok && m < mrows ? (int64_t)p.row_map[m0 + m] : -1;
+        }
+        if (p.C != nullptr) {  // fp32 partial sums, written or added
+          if (p.accumulate) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)off[i], 0, 0));
+              const float4 b =
+                  __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (int)(off[i] + 16), 0, 0));
+              v[i][0] += a.x; v[i][1] += a.y; v[i][2] += a.z; v[i][3] += a.w;
+              v[i][4] += b.x; v[i][5] += b.y; v[i][6] += b.z; v[i][7] += b.w;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][0], v[i][1], v[i][2], v[i][3])),
+                                                   ro, (int)off[i], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, make_float4(v[i][4], v[i][5], v[i][6], v[i][7])),
+                                                   ro, (int)(off[i] + 16), 0, 0);
+          }
+        } else if (p.hilo != 0) {  // the running sum's first block: hi + q (rem_step above), written
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            u32x4_t ho;
+            uint32_t lo[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const uint32_t h0 = f2bf(v[i][e]), h1 = f2bf(v[i][e + 1]);
+              ho[e >> 1] = h0 | (h1 << 16);
+              lo[e >> 2] |= (rem_code(v[i][e], h0) | (rem_code(v[i][e + 1], h1) << 8)) << (8 * (e & 2));
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo[0], lo[1]}, rl8, (int)offl[i], 0, 0);
           }
-        }
-      } else if (p.row_map != nullptr) {  // rows through the map (64-bit addresses)
+        } else if (p.row_map != nullptr) {  // rows through the map (64-bit addresses)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (orow[i] < 0) continue;
-          if (p.out_f32) {
-            float4* d = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow[i] * p.ldo + n8);
-            d[0] = make_float4(cs * v[i][0], cs * v[i][1], cs * v[i][2], cs * v[i][3]);
-            d[1] = make_float4(cs * v[i][4], cs * v[i][5], cs * v[i][6], cs * v[i][7]);
-          } else {
+          for (int i = 0; i < 4; ++i) {
+            if (orow[i] < 0) continue;
+            if (p.out_f32) {
+              float4* d = reinterpret_cast<float4*>(static_cast<float*>(p.out) + orow[i] * p.ldo + n8);
+              d[0] = make_float4(cs * v[i][0], cs * v[i][1], cs * v[i][2], cs * v[i][3]);
+              d[1] = make_float4(cs * v[i][4], cs * v[i][5], cs * v[i][6], cs * v[i][7]);
+            } else {
+              u32x4_t ho;
+#pragma unroll
+              for (int e = 0; e < 8; e += 2)
+                ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
+              *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(p.out) + orow[i] * p.ldo + n8) = ho;
+            }
+          }
+        } else if (p.out_f32) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, make_float4(cs * v[i][0], cs * v[i][1], cs * v[i][2], cs * v[i][3])), ro,
+                (int)off[i], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, make_float4(cs * v[i][4], cs * v[i][5], cs * v[i][6], cs * v[i][7])), ro,
+                (int)(off[i] + 16), 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
             u32x4_t ho;
 #pragma unroll
             for (int e = 0; e < 8; e += 2)
               ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
-            *reinterpret_cast<u32x4_t*>(static_cast<bf16_t*>(p.out) + orow[i] * p.ldo + n8) = ho;
+            __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
           }
         }
-      } else if (p.out_f32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(u32x4_t, make_float4(cs * v[i][0], cs * v[i][1], cs * v[i][2], cs * v[i][3])), ro,
-              (int)off[i], 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(u32x4_t, make_float4(cs * v[i][4], cs * v[i][5], cs * v[i][6], cs * v[i][7])), ro,
-              (int)(off[i] + 16), 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x4_t ho;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            ho[e >> 1] = (uint32_t)f2bf(cs * v[i][e]) | ((uint32_t)f2bf(cs * v[i][e + 1]) << 16);
-          __builtin_amdgcn_raw_buffer_store_b128(ho, ro, (int)off[i], 0, 0);
-        }
+        asm volatile("" ::: "memory");  // (the region is rewritten for the next block)
       }
-      asm volatile("" ::: "memory");  // (the region is rewritten for the next block)
     }
   } else if (p.C != nullptr) {
     const __amdgpu_buffer_rsrc_t rc =
