@@ -945,32 +945,64 @@ hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
 
 // ------------------------------------------------------------------ per-row outputs
 // Per token, from the per-tile partials of the kEpiLseEz forward: LSE and the softmax-weighted
-// mean logit E_p[z] (online over the tiles, in tile order), then the per-row outputs of
-// "Fused Linear Cross-Entropy: ...", Strategy 2: target log-probability z_y - LSE and row loss
-// LSE - z_y + mu LSE^2 for counted rows (0 otherwise), entropy LSE - E_p[z] for every row.
-__global__ void __launch_bounds__(kMergeThreads) rows_merge_kernel(
+// mean logit E_p[z], then the per-row outputs of "Fused Linear Cross-Entropy: ...", Strategy 2:
+// target log-probability z_y - LSE and row loss LSE - z_y + mu LSE^2 for counted rows (0
+// otherwise), entropy LSE - E_p[z] for every row.
+// The partials of a token are split into kMergeSlices contiguous ranges of vocabulary tiles,
+// one wave per range and 64 tokens per workgroup (so that a launch of a few thousand tokens
+// fills the device: one pass per token, as in merge_kernel, is bound by the latency of its
+// sequential loads there), merged online within a range, four loads in flight, then across the
+// ranges in order.  Tiles holding -inf are skipped as in merge_kernel.
+static_assert(kMergeTok == kWave, "one wave of tokens per merge workgroup");
+__device__ __forceinline__ void merge_range(const float* __restrict__ part, const float* __restrict__ ez, int64_t BT,
+                                            int64_t t, int64_t k0, int64_t k1, float& m, float& s, float& te) {
+  m = -INFINITY;
+  s = 0.f;
+  te = 0.f;
+  for (int64_t k = k0; k < k1; k += 4) {
+    float p[4], e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = k + i < k1 ? part[(k + i) * BT + t] : -INFINITY;
+      e[i] = ez != nullptr && k + i < k1 ? ez[(k + i) * BT + t] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (p[i] == -INFINITY) continue;
+      if (p[i] > m) {
+        const float f = __expf(m - p[i]);
+        s = s * f + 1.f;
+        te = te * f + e[i];
+        m = p[i];
+      } else {
+        const float f = __expf(p[i] - m);
+        s += f;
+        te = fmaf(f, e[i], te);
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kMergeTok * kMergeSlices) rows_merge_kernel(
     const float* __restrict__ lse_part, const float* __restrict__ ez_part, int64_t nt, int64_t BT,
     const float* __restrict__ zy, const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float mu,
     float* __restrict__ lse_out, float* __restrict__ logprobs, float* __restrict__ entropy,
     float* __restrict__ row_loss) {
-  const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
-  if (t >= BT) return;
+  __shared__ float s_m[kMergeSlices][kMergeTok], s_s[kMergeSlices][kMergeTok], s_t[kMergeSlices][kMergeTok];
+  const int lane = threadIdx.x % kMergeTok, sl = threadIdx.x / kMergeTok;
+  const int64_t t = (int64_t)blockIdx.x * kMergeTok + lane;
   float m = -INFINITY, s = 0.f, te = 0.f;
-  for (int64_t k = 0; k < nt; ++k) {
-    const float p = lse_part[k * BT + t];
-    const float e = ez_part[k * BT + t];
-    if (p == -INFINITY) continue;
-    if (p > m) {
-      const float f = __expf(m - p);
-      s = s * f + 1.f;
-      te = te * f + e;
-      m = p;
-    } else {
-      const float f = __expf(p - m);
-      s += f;
-      te = fmaf(f, e, te);
-    }
-  }
+  if (t < BT) merge_range(lse_part, ez_part, BT, t, nt * sl / kMergeSlices, nt * (sl + 1) / kMergeSlices, m, s, te);
+  s_m[sl][lane] = m;
+  s_s[sl][lane] = s;
+  s_t[sl][lane] = te;
+  __syncthreads();
+  if (sl != 0 || t >= BT) return;
+  m = -INFINITY;
+  s = 0.f;
+  te = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMergeSlices; ++j) mst_combine(m, s, te, s_m[j][lane], s_s[j][lane], s_t[j][lane]);
   const float L = m + __logf(s);
   const int64_t yt = y[t];
   const bool valid = yt != ignore_index && yt >= 0 && yt < V;
@@ -994,8 +1026,8 @@ hipError_t launch_rows_fused_forward(const FusedArgs& a, const FusedWs& w, float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_target_logit(a, w, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(rows_merge_kernel, dim3((unsigned)((a.BT + kMergeThreads - 1) / kMergeThreads)),
-                     dim3(kMergeThreads), 0, st, w.lse_part, ez_part, w.nt, a.BT, w.zy, a.targets, a.V,
+  hipLaunchKernelGGL(rows_merge_kernel, dim3((unsigned)((a.BT + kMergeTok - 1) / kMergeTok)),
+                     dim3(kMergeTok * kMergeSlices), 0, st, w.lse_part, ez_part, w.nt, a.BT, w.zy, a.targets, a.V,
                      a.ignore_index, a.mu, lse_out, logprobs, entropy, row_loss);
   return hipGetLastError();
 }

@@ -30,6 +30,9 @@ struct FusedWs {
   char* big;          // the two-pass backward's buffers (bf16, H > 1024; over lse_part), or NULL
 };
 constexpr int kMergeThreads = 256;
+// per-row merge of the per-tile partials: tokens per workgroup (one wave) and ranges of
+// vocabulary tiles per token (one wave each)
+constexpr int kMergeTok = 64, kMergeSlices = 16;
 
 size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16);
 size_t fused_base_bytes(int64_t BT, int64_t V);   // small pieces + LSE partials
