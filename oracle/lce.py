@@ -152,8 +152,11 @@ def lce_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE_INDE
 
 
 def _mean_logit(z: np.ndarray, lse: np.ndarray) -> np.ndarray:
-    """E_p[z] = sum_v p_v z_v per row, p = exp(z - LSE)."""
-    return (np.exp(z - lse[:, None]) * z).sum(axis=1)
+    """E_p[z] = sum_v p_v z_v per row, p = exp(z - LSE); an entry with p_v = 0 (a logit of
+    -inf: a vocabulary entry masked by a -inf bias) adds nothing, the limit of p log p -> 0
+    in the entropy -sum_v p_v log p_v."""
+    p = np.exp(z - lse[:, None])
+    return (p * np.where(p > 0.0, z, 0.0)).sum(axis=1)
 
 
 def _row_coefficients(lse, ez, valid, gl, gp, ge, mu):
@@ -222,7 +225,9 @@ def lce_rows_oracle(hidden, weight, bias, targets, *, ignore_index: int = IGNORE
             gpc = gp[r0:r1] if gp is not None else np.zeros(n)
             gec = ge[r0:r1] if ge is not None else np.zeros(n)
             alpha, beta, gamma = _row_coefficients(L, ez[r0:r1], vr, glc, gpc, gec, mu)
-            g = np.exp(z - L[:, None]) * (alpha[:, None] + beta[:, None] * z)
+            p = np.exp(z - L[:, None])
+            # (p = 0 entries, masked by a -inf bias, have zero gradient: p (alpha + beta z) -> 0)
+            g = p * (alpha[:, None] + beta[:, None] * np.where(p > 0.0, z, 0.0))
             g[idx, y[r0:r1][idx]] -= gamma[idx]
             gi[r0:r1] = g @ W
             gw += g.T @ h[r0:r1]

@@ -88,6 +88,35 @@ def test_bias_shift_invariance():
         np.testing.assert_allclose(c[k], a[k], rtol=1e-9, atol=1e-12, err_msg=k)
 
 
+def test_masked_entries_equal_removed_entries():
+    """Entries masked with a -inf bias (p = 0) are the same as entries that do not exist: every
+    per-row output and every gradient of the kept entries equals that of the problem over the
+    kept entries alone (targets renumbered), and the masked rows of grad_W and grad_b are 0."""
+    h, W, b, y = _small(seed=5)
+    V = W.shape[0]
+    masked = np.zeros(V, dtype=bool)
+    masked[[0, 3, 4, V - 1]] = True
+    keep = np.nonzero(~masked)[0]
+    y = y.copy()
+    valid = y != -100
+    y[valid] = keep[y[valid] % keep.size]
+    bm = b.copy()
+    bm[masked] = -np.inf
+    gl, gp, ge = _upstream(len(y), 5)
+    a = oracle.lce_rows_oracle(h, W, bm, y, z_loss=0.03, grad_row_loss=gl, grad_logprobs=gp, grad_entropy=ge)
+    pos = np.full(V, -1)
+    pos[keep] = np.arange(keep.size)
+    yk = np.where(valid, pos[np.where(valid, y, 0)], y)
+    c = oracle.lce_rows_oracle(h, W[keep], b[keep], yk, z_loss=0.03, grad_row_loss=gl, grad_logprobs=gp,
+                               grad_entropy=ge)
+    for k in ("lse", "logprobs", "entropy", "row_loss", "grad_input"):
+        assert np.all(np.isfinite(a[k])), k
+        np.testing.assert_allclose(a[k], c[k], rtol=1e-12, atol=1e-13, err_msg=k)
+    np.testing.assert_allclose(a["grad_weight"][keep], c["grad_weight"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a["grad_bias"][keep], c["grad_bias"], rtol=1e-12, atol=1e-13)
+    assert np.all(a["grad_weight"][masked] == 0.0) and np.all(a["grad_bias"][masked] == 0.0)
+
+
 # --------------------------------------------------------------------- textbook routine
 
 @pytest.mark.parametrize("mu,bias", [(0.0, True), (0.02, True), (0.0, False)])
