@@ -552,11 +552,14 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
             for (int e = 0; e < 4; e += 2) {
               const int c0 = vb * 32 + 8 * rr + e;
               const float a0 = acc[vb][tb][4 * rr + e], a1 = acc[vb][tb][4 * rr + e + 1];
-              const float f0 = RD ? fmaf(be2[tb], a0, fac2[tb]) : fac2[tb];
-              const float f1 = RD ? fmaf(be2[tb], a1, fac2[tb]) : fac2[tb];
-              const float z0 = fmaf(__builtin_amdgcn_exp2f(fmaf(a0, kLog2e, ra2[tb])), f0, c0 == cy2[tb] ? tg2[tb] : 0.f);
-              const float z1 =
-                  fmaf(__builtin_amdgcn_exp2f(fmaf(a1, kLog2e, ra2[tb])), f1, c0 + 1 == cy2[tb] ? tg2[tb] : 0.f);
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(a0, kLog2e, ra2[tb]));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, ra2[tb]));
+              // (RD: an entry with p = 0, e.g. a -inf logit of an entry masked by a -inf bias,
+              // has dlogit 0: p (alpha + beta z) -> 0, while 0 * (beta * -inf) would be NaN)
+              const float f0 = RD ? (p0 != 0.f ? fmaf(be2[tb], a0, fac2[tb]) : 0.f) : fac2[tb];
+              const float f1 = RD ? (p1 != 0.f ? fmaf(be2[tb], a1, fac2[tb]) : 0.f) : fac2[tb];
+              const float z0 = fmaf(p0, f0, c0 == cy2[tb] ? tg2[tb] : 0.f);
+              const float z1 = fmaf(p1, f1, c0 + 1 == cy2[tb] ? tg2[tb] : 0.f);
               if constexpr (FLT)  // (rows past the block do not count; tokens past BT hold 0)
                 big[vb >> 1] = big[vb >> 1] || (c0 < lim && !(fabsf(z0) < flt.eps)) ||
                                (c0 + 1 < lim && !(fabsf(z1) < flt.eps));
@@ -700,8 +703,10 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
               float zv = acc[vb][tb][4 * rr + e];
               if constexpr (MODE == kEpiDlogits)
                 zv = fmaf(__builtin_amdgcn_exp2f(fmaf(zv, kLog2e, ra)), fac, c == cy ? -1.f : 0.f);
-              if constexpr (RD)
-                zv = fmaf(__builtin_amdgcn_exp2f(fmaf(zv, kLog2e, ra)), fmaf(be, zv, al), c == cy ? ga : 0.f);
+              if constexpr (RD) {  // (p = 0: dlogit 0, as in the transposed form)
+                const float pv = __builtin_amdgcn_exp2f(fmaf(zv, kLog2e, ra));
+                zv = fmaf(pv, pv != 0.f ? fmaf(be, zv, al) : 0.f, c == cy ? ga : 0.f);
+              }
               f[e] = (full || c < lim) ? zv : 0.f;
             }
             pk[rr][0] = pack_bf2(f[0], f[1]);

@@ -86,6 +86,54 @@ def test_rows_backward_vs_oracle(case, saved):
         assert e <= TOL["bf16"]["grad"], (k, e)
 
 
+ROWS_MASK = [
+    # (BT, H, V, masked vocabulary ranges, z_loss, seed): whole 256-entry tiles of the forward
+    # (the first, a middle one, the ragged last one) and a part of one tile, bias -inf
+    (300, 256, 1500, ((0, 256), (512, 768), (1000, 1010)), 1e-3, 81),
+    (130, 1152, 2000, ((0, 256), (1792, 2000)), 0.0, 82),
+    (700, 1024, 5000, ((256, 512), (4864, 5000)), 1e-4, 83),
+    (64, 1088, 70000, ((0, 256), (30000, 30256), (69888, 70000)), 1e-4, 84),   # token-chunked backward
+]
+
+
+@pytest.mark.parametrize("saved", [False, True], ids=["recomputed", "saved"])
+@pytest.mark.parametrize("case", ROWS_MASK, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in ROWS_MASK])
+def test_rows_minus_inf_bias_vs_oracle(case, saved):
+    """Vocabulary entries masked with a -inf bias in the per-row forward and backward: a tile
+    with no finite logit is skipped by the merge, and a masked entry (p = 0) adds nothing to
+    the entropy or the dlogits, so its rows of grad_W and grad_b stay exactly 0."""
+    BT, H, V, ranges, mu, seed = case
+    print(f"rows masked-vocabulary case {case} saved={saved}", flush=True)
+    inp = make_fused(BT, H, V, dtype="bf16", seed=seed, bias_std=0.1, ignore_frac=0.1, z_loss=mu)
+    masked = np.zeros(V, dtype=bool)
+    for a, b_ in ranges:
+        masked[a:b_] = True
+    keep = np.nonzero(~masked)[0]
+    valid = inp.targets != -100
+    inp.targets[:] = np.where(valid, keep[np.where(valid, inp.targets, 0) % keep.size], inp.targets)
+    inp.bias[masked] = -np.inf
+    h, W, b, y = dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), dev(inp.bias, "bf16"), dev(inp.targets)
+    rng = np.random.default_rng(seed)
+    gl, gp, ge = (rng.normal(size=BT).astype(np.float32) for _ in range(3))
+    ref = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=mu,
+                                 grad_row_loss=gl, grad_logprobs=gp, grad_entropy=ge)
+    f = lce.lce_rows_forward(h, W, b, y, z_loss=mu)
+    st = dict(lse=f["lse"], entropy=f["entropy"]) if saved else {}
+    r = lce.lce_rows_backward(h, W, b, y, grad_row_loss=dev(gl), grad_logprobs=dev(gp), grad_entropy=dev(ge),
+                              z_loss=mu, **st)
+    torch.cuda.synchronize()
+    bound = _row_bound(ref)
+    for k in ("lse", "logprobs", "entropy"):
+        err = np.abs(host64(f[k]) - ref[k])
+        assert np.all(err <= bound), (k, float((err / bound).max()))
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        e = rel_fro(host64(r[k]), ref[k])
+        assert e <= TOL["bf16"]["grad"], (k, e)
+    mk = torch.from_numpy(masked).cuda()
+    assert int(torch.count_nonzero(r["grad_weight"][mk])) == 0
+    assert int(torch.count_nonzero(r["grad_bias"][mk])) == 0
+
+
 def test_rows_backward_saved_matches_recomputed():
     """On the one-pass plan the recomputed form takes its statistics from the same per-row
     forward as the saved ones (on the token-chunked backward it recomputes them from the bf16
