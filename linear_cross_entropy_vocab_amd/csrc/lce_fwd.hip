@@ -249,6 +249,7 @@ __device__ __forceinline__ int fsw(int row) { return (row & 7) ^ ((row >> 3) & 1
 // value, before rounding) of magnitude >= flt.eps; with the counts of quarters without one.
 // MODE kEpiRowsDlogitsT: the kEpiRowsDlogits values written transposed, as kEpiDlogitsT writes
 // its own (the grad_W operand of the per-row backward).
+// GB (transposed modes): also the grad_b partial sums into flt.gbp (which is then not null).
 constexpr int kEpiLse = 0, kEpiLogits = 1, kEpiDlogits = 2, kEpiLseEz = 3, kEpiRowsDlogits = 4, kEpiDlogitsT = 5,
               kEpiDlogitsTF = 6, kEpiRowsDlogitsT = 7;
 
@@ -265,7 +266,7 @@ __device__ __forceinline__ void mst_combine(float& m, float& s, float& t, float 
     t += t2 * f;
   }
 }
-template <int MODE>
+template <int MODE, bool GB = false>
 __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16_t* __restrict__ W,
                                                                     const bf16_t* __restrict__ h,
                                                                     const bf16_t* __restrict__ bias,
@@ -538,7 +539,10 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
       const int64_t tcol = tl.t0 + wt * 64 + cl;
       const bool col_ok = tcol + 8 <= ld;
       bool big[2] = {false, false};  // (FLT) a large dlogit in the wave's rows 0-63 / 64-127
-      const bool gbs = flt.gbp != nullptr;  // (grad_b: row sums of the fp32 values)
+      constexpr bool gbs = GB;  // (grad_b: row sums of the fp32 values)
+      // byte selector of the pair exchange below: the even lane takes its own row-e value and
+      // its partner's, the odd lane its partner's row-(e + 1) value and its own
+      const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
         float rs[16];  // (grad_b) rows 8 (r / 4) + r % 4 of this vb: the sum over the lane's two tokens
@@ -547,34 +551,47 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
+          for (int rr = 0; rr < 4; ++rr) {
+            const int c0 = vb * 32 + 8 * rr;  // this lane's rows c0 .. c0 + 3 (+ vrow) of the 4-row group
+            float pe[4], fe[4], z[4];
 #pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-              const int c0 = vb * 32 + 8 * rr + e;
-              const float a0 = acc[vb][tb][4 * rr + e], a1 = acc[vb][tb][4 * rr + e + 1];
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(a0, kLog2e, ra2[tb]));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(a1, kLog2e, ra2[tb]));
+            for (int e = 0; e < 4; ++e) {
+              const float a = acc[vb][tb][4 * rr + e];
+              pe[e] = __builtin_amdgcn_exp2f(fmaf(a, kLog2e, ra2[tb]));
               // (RD: an entry with p = 0, e.g. a -inf logit of an entry masked by a -inf bias,
               // has dlogit 0: p (alpha + beta z) -> 0, while 0 * (beta * -inf) would be NaN)
-              const float f0 = RD ? (p0 != 0.f ? fmaf(be2[tb], a0, fac2[tb]) : 0.f) : fac2[tb];
-              const float f1 = RD ? (p1 != 0.f ? fmaf(be2[tb], a1, fac2[tb]) : 0.f) : fac2[tb];
-              const float z0 = fmaf(p0, f0, c0 == cy2[tb] ? tg2[tb] : 0.f);
-              const float z1 = fmaf(p1, f1, c0 + 1 == cy2[tb] ? tg2[tb] : 0.f);
-              if constexpr (FLT)  // (rows past the block do not count; tokens past BT hold 0)
-                big[vb >> 1] = big[vb >> 1] || (c0 < lim && !(fabsf(z0) < flt.eps)) ||
-                               (c0 + 1 < lim && !(fabsf(z1) < flt.eps));
-              rs[4 * rr + e] += z0;
-              rs[4 * rr + e + 1] += z1;
-              const float send = odd ? z0 : z1;
-              // quad_perm (1, 0, 3, 2): the value of lane ln ^ 1
-              const float recv = __int_as_float(
-                  __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-              const uint32_t v = odd ? pack_bf2(recv, z1) : pack_bf2(z0, recv);
+              fe[e] = RD ? (pe[e] != 0.f ? fmaf(be2[tb], a, fac2[tb]) : 0.f) : fac2[tb];
+              z[e] = fmaf(pe[e], fe[e], 0.f);
+            }
+            // the token's target column is at most one of the four rows, and rarely any of
+            // them (a wave-divergent branch): there the target term enters the same fmaf
+            const int dt = cy2[tb] - c0;
+            if ((unsigned)dt < 4u) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (e == dt) z[e] = fmaf(pe[e], fe[e], tg2[tb]);
+            }
+            if constexpr (FLT) {  // (rows past the block do not count; tokens past BT hold 0)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) big[vb >> 1] = big[vb >> 1] || (c0 + e < lim && !(fabsf(z[e]) < flt.eps));
+            }
+            if constexpr (GB) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) rs[4 * rr + e] += z[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              // lanes t and t ^ 1 (quad_perm (1, 0, 3, 2)) swap their packed rows e, e + 1, and
+              // each keeps one row of both tokens: the even lane row e, the odd lane row e + 1
+              const uint32_t pk = pack_bf2(z[e], z[e + 1]);
+              const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, false);
+              const uint32_t v = __builtin_amdgcn_perm(other, pk, psel);
               // staged row 4 half + 8 rr + e (+1 odd), tokens tb 32 + t (even lane's t)
               const int srow = 4 * (ln >> 5) + 8 * rr + e + (odd ? 1 : 0);
               const int scol = tb * 32 + (ln & 31) - (odd ? 1 : 0);
               *reinterpret_cast<uint32_t*>(stg + srow * kPitch + 2 * scol) = v;
             }
+          }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const u32x4_t q = *reinterpret_cast<const u32x4_t*>(stg + (8 * i + rl) * kPitch + 2 * cl);
@@ -1116,14 +1133,16 @@ hipError_t launch_dlogits_block_t(const bf16_t* W_block, const bf16_t* h, const 
   if (flt.fin != nullptr) {
     // every flag lands inside its row
     if (flt.fw == nullptr || flt.ldfi < 4 * nt_v || flt.ldfw < 4 * nt_t2) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogitsTF>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2),
-                       0, st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu,
-                       vbase, (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, flt);
+    auto k = flt.gbp != nullptr ? fwd_lse_dma_kernel<kEpiDlogitsTF, true> : fwd_lse_dma_kernel<kEpiDlogitsTF, false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0, st, W_block, h, bias_block,
+                       rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu, vbase, (float*)nullptr,
+                       (const float4*)nullptr, (const int32_t*)nullptr, flt);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiDlogitsT>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0,
-                     st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu, vbase,
-                     (float*)nullptr, (const float4*)nullptr, (const int32_t*)nullptr, flt);
+  auto k = flt.gbp != nullptr ? fwd_lse_dma_kernel<kEpiDlogitsT, true> : fwd_lse_dma_kernel<kEpiDlogitsT, false>;
+  hipLaunchKernelGGL(k, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0, st, W_block, h, bias_block,
+                     rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, tok, mu, vbase, (float*)nullptr,
+                     (const float4*)nullptr, (const int32_t*)nullptr, flt);
   return hipGetLastError();
 }
 
@@ -1140,9 +1159,10 @@ hipError_t launch_rows_dlogits_block_t(const bf16_t* W_block, const bf16_t* h, c
   if (ext.fin != nullptr || (ext.gbp != nullptr && ext.ldgb < V)) return hipErrorInvalidValue;
   const int64_t nt_v = (V + kFwdTileV - 1) / kFwdTileV;
   const int64_t nt_t2 = (ld + kFwdTileT2 - 1) / kFwdTileT2;
-  hipLaunchKernelGGL(fwd_lse_dma_kernel<kEpiRowsDlogitsT>, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2),
-                     0, st, W_block, h, bias_block, rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld,
-                     (const float2*)nullptr, 0.f, vbase, (float*)nullptr, rtok, rcy, ext);
+  auto k = ext.gbp != nullptr ? fwd_lse_dma_kernel<kEpiRowsDlogitsT, true> : fwd_lse_dma_kernel<kEpiRowsDlogitsT, false>;
+  hipLaunchKernelGGL(k, dim3((unsigned)fwd_grid(nt_v * nt_t2)), dim3(kFwdThreads2), 0, st, W_block, h, bias_block,
+                     rows, H, V, nt_v, nt_t2, (float*)nullptr, gout, ld, (const float2*)nullptr, 0.f, vbase,
+                     (float*)nullptr, rtok, rcy, ext);
   return hipGetLastError();
 }
 
