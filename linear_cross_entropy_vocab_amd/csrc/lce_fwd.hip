@@ -634,7 +634,9 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         const bool b0 = __builtin_amdgcn_ballot_w64(big[0]) != 0, b1 = __builtin_amdgcn_ballot_w64(big[1]) != 0;
         if (ln == 0) s_flw[w] = (b0 ? 1 : 0) | (b1 ? 2 : 0);
       }
-      __syncthreads();  // every wave has read s_bias and s_tok before the next tile rewrites them
+      // (the staging regions and the side data need no barrier here: the next tile rewrites the
+      // former only after the barrier of its first K stage, the latter a tile later)
+      if constexpr (FLT || GB) __syncthreads();  // every wave's flags and row sums are in LDS
       if (gbs && tid < kFwdTileV && tid < vlim) {
         // the tile's rows: the sum of the four waves' 64-token sums (with filtering, of the
         // 64-token groups whose grad_W flag is set), in order
@@ -746,7 +748,6 @@ __global__ void __launch_bounds__(kFwdThreads2, 1) fwd_lse_dma_kernel(const bf16
         }
       }
       (void)lse_part;
-      __syncthreads();  // every wave has read s_bias before the next tile rewrites it
       if (!has_next) break;
       blk = nblk;
       tl = tn;
