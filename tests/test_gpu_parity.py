@@ -108,7 +108,7 @@ MASK_CASES = [
     # tiles of the forward (the first one, a middle one, the ragged last one) with bias -inf
     ("bf16", 300, 256, 1500, ((0, 256), (512, 768)), 1e-3, "fused"),
     ("f32", 150, 128, 1300, ((0, 256), (768, 1024), (1280, 1300)), 0.0, "fused"),
-    ("bf16", 600, 1152, 9000, ((0, 256), (4096, 4352)), 1e-4, "fused"),   # two-pass backward
+    ("bf16", 600, 1152, 9000, ((0, 256), (4096, 4352)), 1e-4, "fused"),   # one-pass backward (stored dlogits)
     ("bf16", 300, 256, 1500, ((0, 256), (1280, 1500)), 0.0, "chunked"),
 ]
 
