@@ -450,7 +450,7 @@ __global__ void __launch_bounds__(kCEThreads) ce_rows_stream(T* __restrict__ log
     if (v > m) {
       s = s * __expf(m - v) + 1.f;
       m = v;
-    } else {
+    } else if (m != -INFINITY) {  // (-inf entries so far: e^-inf = 0, never -inf - -inf)
       s += __expf(v - m);
     }
   }

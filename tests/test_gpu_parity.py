@@ -334,6 +334,37 @@ def test_ce_small_vs_oracle(case):
     assert np.all(d[ign_rows] == 0.0)
 
 
+@pytest.mark.parametrize("case", [c for c in CE_CASES if c[2] > 1][:6] + [CE_CASES[9], CE_CASES[10]],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}")
+def test_ce_masked_entries_vs_oracle(case):
+    """Logits of -inf (vocabulary entries masked out; never a counted target) add e^-inf = 0 to
+    the LSE and get a dlogit of exactly 0, on each row-length path of the kernel."""
+    dt, B, V, mu, ign, seed = case
+    print(f"ce masked case {case}", flush=True)
+    inp = make_ce(B, V, dtype=dt, seed=seed, ignore_frac=ign)
+    rng = np.random.default_rng(seed)
+    masked = rng.random(V) < 0.3
+    masked[0] = True
+    masked[V - 1] = True
+    keep = np.nonzero(~masked)[0]
+    valid = inp.targets != -100
+    inp.targets[:] = np.where(valid, keep[np.where(valid, inp.targets, 0) % keep.size], inp.targets)
+    logits = np.array(inp.logits, dtype=np.float32)
+    logits[:, masked] = -np.inf
+    ref = oracle.ce_oracle(logits, inp.targets, z_loss=mu)
+    assert np.isfinite(ref["ce_sum"])
+    x = dev(logits, dt)
+    ce_sum, z_sum, nv = lce.lce_ce_with_grad_inplace(x, dev(inp.targets), z_loss=mu)
+    torch.cuda.synchronize()
+    tol = CE_TOL[dt]
+    assert int(nv.item()) == ref["n_valid"]
+    assert rel(ce_sum.item(), ref["ce_sum"]) <= tol["sums"]
+    d = host64(x)
+    assert np.all(np.isfinite(d))
+    assert np.all(d[:, masked] == 0.0)
+    assert rel_fro(d, ref["dlogits"]) <= tol["dlogits"]
+
+
 def test_ce_empty_batch():
     x = torch.empty(0, 100, dtype=torch.bfloat16, device="cuda")
     y = torch.empty(0, dtype=torch.int64, device="cuda")
