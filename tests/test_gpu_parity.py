@@ -112,6 +112,8 @@ MASK_CASES = [
     ("bf16", 300, 256, 1500, ((0, 256), (1280, 1500)), 0.0, "chunked"),
     ("bf16", 2000, 1280, 300, ((0, 256),), 1e-3, "fused"),                  # two-pass backward
     ("bf16", 700, 1024, 20000, ((0, 256), (9984, 10240)), 1e-4, "filtered"),  # flagged tiles, eps 2^-20
+    ("bf16", 700, 1024, 20000, ((0, 256), (9984, 10240)), 1e-4, "sorted"),    # and the vocabulary sorted
+    ("bf16", 300, 256, 1500, ((0, 256), (512, 768)), 1e-3, "sorted"),          # sorted, pipelined backward
 ]
 
 
@@ -132,7 +134,8 @@ def test_minus_inf_bias_tiles_vs_oracle(case):
     inp.bias[masked] = -np.inf
     ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=mu)
     assert np.isfinite(ref["loss"])
-    kw = dict(filter_eps=2.0 ** -20) if method == "filtered" else dict(method=method)
+    kw = (dict(filter_eps=2.0 ** -20) if method == "filtered" else
+          dict(filter_eps=2.0 ** -20, sort_vocab=True) if method == "sorted" else dict(method=method))
     r = run_fused(inp, **kw)
     lse_tol = 2.0 ** -8 if method == "chunked" else None  # (bf16 logits chunk)
     check_fused(inp, r, ref, lse_tol=lse_tol)
