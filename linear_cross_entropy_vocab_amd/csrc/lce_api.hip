@@ -16,7 +16,7 @@ namespace lce {
 // before any backward kernel runs (the two-pass backward reuses their memory).
 size_t fused_small_bytes(int64_t BT, int64_t V) {
   const int64_t bt = BT > 0 ? BT : 1;
-  const int64_t nblk = (bt + kMergeThreads - 1) / kMergeThreads;
+  const int64_t nblk = merge_blocks(bt);
   size_t n = ws_align(16);                         // n_valid, n_bad
   n += ws_align((size_t)bt * 4);                   // lse
   n += ws_align((size_t)bt * 4);                   // zy
@@ -56,8 +56,8 @@ FusedWs fused_carve(void* ws, int64_t BT, int64_t H, int64_t V, bool bf16) {
   const int64_t bt = BT > 0 ? BT : 1;
   FusedWs w;
   w.nt = (V + kFwdTileV - 1) / kFwdTileV;
-  w.nblk = (BT + kMergeThreads - 1) / kMergeThreads;
-  const int64_t nblk_alloc = (bt + kMergeThreads - 1) / kMergeThreads;
+  w.nblk = BT > 0 ? merge_blocks(BT) : 0;
+  const int64_t nblk_alloc = merge_blocks(bt);
   char* p = static_cast<char*>(ws);
   w.n_valid = reinterpret_cast<int64_t*>(p);
   w.n_bad = reinterpret_cast<int32_t*>(p + 8);

@@ -913,6 +913,42 @@ hipError_t launch_target_logit(const FusedArgs& a, const FusedWs& w, hipStream_t
 }
 
 // ------------------------------------------------------------------ merge
+// Sliced merge (the per-row merge, and the fused call's for up to kMergeSlicedMaxBT tokens):
+// the partials of a token are split into kMergeSlices contiguous ranges of vocabulary tiles,
+// one wave per range and 64 tokens per workgroup (so that a launch of a few thousand tokens
+// fills the device: one pass per token, as in merge_kernel, is bound by the latency of its
+// sequential loads there), merged online within a range, four loads in flight, then across the
+// ranges in order.  Tiles holding -inf are skipped as in merge_kernel.
+static_assert(kMergeTok == kWave, "one wave of tokens per merge workgroup");
+__device__ __forceinline__ void merge_range(const float* __restrict__ part, const float* __restrict__ ez, int64_t BT,
+                                            int64_t t, int64_t k0, int64_t k1, float& m, float& s, float& te) {
+  m = -INFINITY;
+  s = 0.f;
+  te = 0.f;
+  for (int64_t k = k0; k < k1; k += 4) {
+    float p[4], e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = k + i < k1 ? part[(k + i) * BT + t] : -INFINITY;
+      e[i] = ez != nullptr && k + i < k1 ? ez[(k + i) * BT + t] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (p[i] == -INFINITY) continue;
+      if (p[i] > m) {
+        const float f = __expf(m - p[i]);
+        s = s * f + 1.f;
+        te = te * f + e[i];
+        m = p[i];
+      } else {
+        const float f = __expf(p[i] - m);
+        s += f;
+        te = fmaf(f, e[i], te);
+      }
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     const float* __restrict__ part, int64_t nt, int64_t BT, const float* __restrict__ zy,
     const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float* __restrict__ lse,
@@ -958,11 +994,58 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
   }
 }
 
+__global__ void __launch_bounds__(kMergeTok * kMergeSlices) merge_sliced_kernel(
+    const float* __restrict__ part, int64_t nt, int64_t BT, const float* __restrict__ zy,
+    const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float* __restrict__ lse,
+    float* __restrict__ lse_out, double* __restrict__ blk_ce, double* __restrict__ blk_z,
+    float2* __restrict__ tok) {
+  __shared__ float s_m[kMergeSlices][kMergeTok], s_s[kMergeSlices][kMergeTok];
+  const int lane = threadIdx.x % kMergeTok, sl = threadIdx.x / kMergeTok;
+  const int64_t t = (int64_t)blockIdx.x * kMergeTok + lane;
+  float m = -INFINITY, s = 0.f, te;
+  if (t < BT) merge_range(part, nullptr, BT, t, nt * sl / kMergeSlices, nt * (sl + 1) / kMergeSlices, m, s, te);
+  s_m[sl][lane] = m;
+  s_s[sl][lane] = s;
+  __syncthreads();
+  if (sl != 0) return;
+  double ce = 0.0, zz = 0.0;
+  if (t < BT) {
+    m = -INFINITY;
+    s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeSlices; ++j) ms_merge(m, s, s_m[j][lane], s_s[j][lane]);
+    const float L = m + __logf(s);
+    lse[t] = L;
+    if (lse_out) lse_out[t] = L;
+    const int64_t yt = y[t];
+    const bool valid = yt != ignore_index && yt >= 0 && yt < V;
+    if (valid) {
+      ce = (double)L - (double)zy[t];
+      zz = (double)L * (double)L;
+    }
+    tok[t] = make_float2(L, __int_as_float(valid ? (int32_t)yt + 1 : 0));
+  }
+  ce = wave_sum_d(ce);
+  zz = wave_sum_d(zz);
+  if (lane == 0) {
+    blk_ce[blockIdx.x] = ce;
+    blk_z[blockIdx.x] = zz;
+  }
+}
+
+// One pass per token where the tokens fill the device (at the largest sizes the step measured
+// no faster with the sliced merge, which alone is faster); w.nblk (merge_blocks) follows the
+// choice.
 hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
   if (a.BT == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)w.nblk), dim3(kMergeThreads), 0, st, w.lse_part, w.nt,
-                     a.BT, w.zy, a.targets, a.V, a.ignore_index, w.lse, a.lse_out, w.blk,
-                     w.blk + w.nblk, w.nblk, w.tok);
+  if (a.BT <= kMergeSlicedMaxBT)
+    hipLaunchKernelGGL(merge_sliced_kernel, dim3((unsigned)w.nblk), dim3(kMergeTok * kMergeSlices), 0, st,
+                       w.lse_part, w.nt, a.BT, w.zy, a.targets, a.V, a.ignore_index, w.lse, a.lse_out, w.blk,
+                       w.blk + w.nblk, w.tok);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)w.nblk), dim3(kMergeThreads), 0, st, w.lse_part, w.nt,
+                       a.BT, w.zy, a.targets, a.V, a.ignore_index, w.lse, a.lse_out, w.blk,
+                       w.blk + w.nblk, w.nblk, w.tok);
   return hipGetLastError();
 }
 
@@ -971,41 +1054,6 @@ hipError_t launch_merge(const FusedArgs& a, const FusedWs& w, hipStream_t st) {
 // mean logit E_p[z], then the per-row outputs of "Fused Linear Cross-Entropy: ...", Strategy 2:
 // target log-probability z_y - LSE and row loss LSE - z_y + mu LSE^2 for counted rows (0
 // otherwise), entropy LSE - E_p[z] for every row.
-// The partials of a token are split into kMergeSlices contiguous ranges of vocabulary tiles,
-// one wave per range and 64 tokens per workgroup (so that a launch of a few thousand tokens
-// fills the device: one pass per token, as in merge_kernel, is bound by the latency of its
-// sequential loads there), merged online within a range, four loads in flight, then across the
-// ranges in order.  Tiles holding -inf are skipped as in merge_kernel.
-static_assert(kMergeTok == kWave, "one wave of tokens per merge workgroup");
-__device__ __forceinline__ void merge_range(const float* __restrict__ part, const float* __restrict__ ez, int64_t BT,
-                                            int64_t t, int64_t k0, int64_t k1, float& m, float& s, float& te) {
-  m = -INFINITY;
-  s = 0.f;
-  te = 0.f;
-  for (int64_t k = k0; k < k1; k += 4) {
-    float p[4], e[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = k + i < k1 ? part[(k + i) * BT + t] : -INFINITY;
-      e[i] = ez != nullptr && k + i < k1 ? ez[(k + i) * BT + t] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (p[i] == -INFINITY) continue;
-      if (p[i] > m) {
-        const float f = __expf(m - p[i]);
-        s = s * f + 1.f;
-        te = te * f + e[i];
-        m = p[i];
-      } else {
-        const float f = __expf(p[i] - m);
-        s += f;
-        te = fmaf(f, e[i], te);
-      }
-    }
-  }
-}
-
 __global__ void __launch_bounds__(kMergeTok * kMergeSlices) rows_merge_kernel(
     const float* __restrict__ lse_part, const float* __restrict__ ez_part, int64_t nt, int64_t BT,
     const float* __restrict__ zy, const int64_t* __restrict__ y, int64_t V, int64_t ignore_index, float mu,

@@ -30,9 +30,15 @@ struct FusedWs {
   char* big;          // the two-pass backward's buffers (bf16, H > 1024; over lse_part), or NULL
 };
 constexpr int kMergeThreads = 256;
-// per-row merge of the per-tile partials: tokens per workgroup (one wave) and ranges of
-// vocabulary tiles per token (one wave each)
+// sliced merge of the per-tile partials: tokens per workgroup (one wave) and ranges of
+// vocabulary tiles per token (one wave each); the fused call takes it up to kMergeSlicedMaxBT
+// tokens (one pass per token, kMergeThreads tokens per workgroup, above)
 constexpr int kMergeTok = 64, kMergeSlices = 16;
+constexpr int64_t kMergeSlicedMaxBT = 32768;
+// workgroups of the fused call's merge (one block sum pair each)
+inline int64_t merge_blocks(int64_t BT) {
+  return BT <= kMergeSlicedMaxBT ? (BT + kMergeTok - 1) / kMergeTok : (BT + kMergeThreads - 1) / kMergeThreads;
+}
 
 size_t fused_workspace_bytes(int64_t BT, int64_t H, int64_t V, bool bf16);
 size_t fused_base_bytes(int64_t BT, int64_t V);   // small pieces + LSE partials
