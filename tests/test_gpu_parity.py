@@ -263,6 +263,50 @@ def test_deterministic_bits(shape):
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("ignore_index", [0, -1, 7])
+@pytest.mark.parametrize("shape", [(200, 128, 1000), (700, 1024, 20000)], ids=lambda s: "x".join(map(str, s)))
+def test_custom_ignore_index_vs_oracle(shape, ignore_index):
+    """ignore_index other than -100, including a vocabulary id (its rows count for nothing, in
+    the fused call, the token-chunked composition, the per-row outputs and the standalone CE)."""
+    BT, H, V = shape
+    print(f"ignore_index case {shape} {ignore_index}", flush=True)
+    inp = make_fused(BT, H, V, dtype="bf16", seed=BT + ignore_index, bias_std=0.1, ignore_frac=0.0, z_loss=1e-4)
+    rng = np.random.default_rng(BT)
+    inp.targets[rng.random(BT) < 0.2] = ignore_index
+    inp.targets[:3] = ignore_index
+    h, W, b, y = dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), dev(inp.bias, "bf16"), dev(inp.targets)
+    ref = oracle.lce_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=1e-4, ignore_index=ignore_index)
+    for method in ("fused", "chunked"):
+        r = lce.lce_fwd_bwd(h, W, b, y, z_loss=1e-4, ignore_index=ignore_index, return_lse=True, method=method)
+        torch.cuda.synchronize()
+        lse_tol = 2.0 ** -8 if method == "chunked" else TOL["bf16"]["lse"]  # (chunked: bf16 logits chunk)
+        lse = host64(r["lse"])
+        assert np.max(np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))) <= lse_tol, method
+        assert int(r["n_valid"].item()) == ref["n_valid"], method
+        assert rel(r["loss"].item(), ref["loss"]) <= TOL["bf16"]["loss"], method
+        for k in ("grad_input", "grad_weight", "grad_bias"):
+            assert rel_fro(host64(r[k]), ref[k]) <= TOL["bf16"]["grad"], (method, k)
+        ign = inp.targets == ignore_index
+        assert np.all(host64(r["grad_input"])[ign] == 0.0), method
+    rr = oracle.lce_rows_oracle(inp.hidden, inp.weight, inp.bias, inp.targets, z_loss=1e-4,
+                                ignore_index=ignore_index)
+    f = lce.lce_rows_forward(h, W, b, y, z_loss=1e-4, ignore_index=ignore_index)
+    torch.cuda.synchronize()
+    assert int(f["n_valid"].item()) == rr["n_valid"]
+    bound = TOL["bf16"]["lse"] * np.maximum(1.0, np.abs(rr["lse"]))
+    for k in ("logprobs", "entropy"):
+        assert np.all(np.abs(host64(f[k]) - rr[k]) <= bound), k
+    ce = make_ce(64, 1000, dtype="bf16", seed=5, ignore_frac=0.0)
+    ce.targets[::3] = ignore_index
+    cref = oracle.ce_oracle(ce.logits, ce.targets, z_loss=1e-4, ignore_index=ignore_index)
+    x = dev(ce.logits, "bf16")
+    ce_sum, z_sum, nv = lce.lce_ce_with_grad_inplace(x, dev(ce.targets), z_loss=1e-4, ignore_index=ignore_index)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == cref["n_valid"]
+    assert rel(ce_sum.item(), cref["ce_sum"]) <= CE_TOL["bf16"]["sums"]
+    assert rel_fro(host64(x), cref["dlogits"]) <= CE_TOL["bf16"]["dlogits"]
+
+
 def test_target_range_check():
     inp = make_fused(40, 64, 100, dtype="bf16", seed=5)
     inp.targets[7] = 100  # == V: out of range
