@@ -307,6 +307,38 @@ def test_custom_ignore_index_vs_oracle(shape, ignore_index):
     assert rel_fro(host64(x), cref["dlogits"]) <= CE_TOL["bf16"]["dlogits"]
 
 
+@pytest.mark.parametrize("shape", [(200, 128, 1000), (700, 1024, 20000), (300, 2112, 5000)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_large_logits_vs_oracle(shape):
+    """Logits in the hundreds (hidden scaled by 40, a bias of +-50): the exponentials stay
+    relative to the running maximum everywhere, so the loss, LSE and gradients stay finite and
+    match the oracle (fused call, per-row outputs)."""
+    BT, H, V = shape
+    print(f"large-logits case {shape}", flush=True)
+    inp = make_fused(BT, H, V, dtype="bf16", seed=BT + 3, bias_std=0.1, ignore_frac=0.1, z_loss=1e-4)
+    inp.hidden[:] = (inp.hidden * 40.0).astype(inp.hidden.dtype)
+    inp.bias[:] = np.where(np.arange(V) % 2 == 0, 50.0, -50.0).astype(inp.bias.dtype)
+    h, W, b, y = dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), dev(inp.bias, "bf16"), dev(inp.targets)
+    hb, Wb, bb = host64(h), host64(W), host64(b)   # the bf16 values the kernels see
+    ref = oracle.lce_oracle(hb, Wb, bb, inp.targets, z_loss=1e-4)
+    assert np.all(np.isfinite(ref["lse"])) and np.max(np.abs(ref["lse"])) > 100.0
+    r = lce.lce_fwd_bwd(h, W, b, y, z_loss=1e-4, return_lse=True)
+    torch.cuda.synchronize()
+    assert rel(r["loss"].item(), ref["loss"]) <= TOL["bf16"]["loss"]
+    lse = host64(r["lse"])
+    assert np.max(np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))) <= TOL["bf16"]["lse"]
+    for k in ("grad_input", "grad_weight", "grad_bias"):
+        g = host64(r[k])
+        assert np.all(np.isfinite(g)), k
+        assert rel_fro(g, ref[k]) <= TOL["bf16"]["grad"], k
+    rr = oracle.lce_rows_oracle(hb, Wb, bb, inp.targets, z_loss=1e-4)
+    f = lce.lce_rows_forward(h, W, b, y, z_loss=1e-4)
+    torch.cuda.synchronize()
+    bound = TOL["bf16"]["lse"] * np.maximum(1.0, np.abs(rr["lse"]))
+    for k in ("lse", "logprobs", "entropy"):
+        assert np.all(np.abs(host64(f[k]) - rr[k]) <= bound), k
+
+
 def test_target_range_check():
     inp = make_fused(40, 64, 100, dtype="bf16", seed=5)
     inp.targets[7] = 100  # == V: out of range
