@@ -100,7 +100,9 @@ typedef enum lce_reduction LCE_ENUM_BASE {
  *
  * Arguments
  *   hidden      [BT, H] in `dtype`.                     W      [V, H] in `dtype`.
- *   bias        [V] in `dtype`, or NULL for no bias.
+ *   bias        [V] in `dtype`, or NULL for no bias.  An entry of -inf masks its vocabulary
+ *               entry: e^-inf = 0 in every sum, its dlogits and its rows of grad_W and grad_b
+ *               are 0 (a counted target must not be masked).
  *   targets     [BT] int64; ignore_index marks rows that contribute nothing.
  *   BT >= 0, 8 <= H <= 2^20 with H a multiple of 8, V >= 1.
  *   dtype       LCE_DTYPE_BF16 or LCE_DTYPE_F32 (arithmetic: products accumulated in fp32;
@@ -195,7 +197,8 @@ const char* lce_stage_name(int k);
  * rounded to the logits' dtype; ignored rows are written as zeros.  A mean-reduced loss is
  * ce_sum / max(n_valid, 1) and its gradient is these dlogits times the same factor.
  *   logits      [B, V] in `dtype` (LCE_DTYPE_BF16, LCE_DTYPE_F16 or LCE_DTYPE_F32; the page's
- *               kernel takes float16, bfloat16 and float32 logits), read then overwritten.
+ *               kernel takes float16, bfloat16 and float32 logits), read then overwritten; -inf
+ *               entries (masked, never a counted target) add nothing and get dlogit 0.
  *   targets     [B] int64.   B >= 0, V >= 1.   z_loss_mult >= 0.
  *   workspace   >= lce_ce_workspace_bytes(B, V, dtype) bytes.
  * Targets outside [0, V) that are not ignore_index are treated as ignored.
