@@ -339,6 +339,39 @@ def test_large_logits_vs_oracle(shape):
         assert np.all(np.abs(host64(f[k]) - rr[k]) <= bound), k
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two calls in flight at once on two streams (separate workspaces; the library keeps no
+    state between calls) give bit for bit the results of the same calls made one at a time:
+    fused calls with the one-pass and the pipelined backward, and per-row outputs."""
+    cases = [(700, 1024, 20000, 0.1), (600, 1152, 9000, None), (333, 256, 3001, 0.1)]
+    inputs = []
+    for BT, H, V, bstd in cases:
+        inp = make_fused(BT, H, V, dtype="bf16", seed=BT + 11, bias_std=bstd, ignore_frac=0.1, z_loss=1e-4)
+        b = None if inp.bias is None else dev(inp.bias, "bf16")
+        inputs.append((dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), b, dev(inp.targets)))
+
+    def run(i):
+        h, W, b, y = inputs[i]
+        r = lce.lce_fwd_bwd(h, W, b, y, z_loss=1e-4, return_lse=True)
+        f = lce.lce_rows_forward(h, W, b, y, z_loss=1e-4)
+        return {**{k: v for k, v in r.items() if isinstance(v, torch.Tensor) and k != "workspace"},
+                **{"rows_" + k: v for k, v in f.items() if isinstance(v, torch.Tensor) and k != "workspace"}}
+
+    alone = [run(i) for i in range(len(cases))]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in cases]
+    together = [None] * len(cases)
+    for rep in range(3):
+        for i, st in enumerate(streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                together[i] = run(i)
+        torch.cuda.synchronize()
+        for i in range(len(cases)):
+            for k, v in alone[i].items():
+                assert torch.equal(together[i][k], v), (rep, i, k)
+
+
 def test_target_range_check():
     inp = make_fused(40, 64, 100, dtype="bf16", seed=5)
     inp.targets[7] = 100  # == V: out of range
