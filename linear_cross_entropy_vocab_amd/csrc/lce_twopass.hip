@@ -50,7 +50,9 @@ TwoPass twopass_plan(int64_t BT, int64_t H, int64_t V) {
   // of the sizes from half the fit to the fit (multiples of 64), the one whose blocks take the
   // fewest rounds in all, the largest on a tie (fewest dlogits launches)
   if (BT > 0) {
-    const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)BT * 2)) / 64 * 64, vpad);
+    // (each stored block under 2^31 bytes: one buffer descriptor with 32-bit offsets)
+    const int64_t v_fit =
+        std::min<int64_t>({(int64_t)(avail / ((size_t)BT * 2)) / 64 * 64, vpad, (0x7fffffffll / (BT * 2)) / 64 * 64});
     if (v_fit < 64) return t;
     auto rounds = [&](int64_t rows) { return ((rows + 63) / 64 * t.hchunks + kPlanCUs - 1) / kPlanCUs; };
     const int64_t step = std::max<int64_t>(64, round_up(v_fit / 2 / 4096, 64));
@@ -342,9 +344,14 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, int kind, size_t reserve) {
   if ((int64_t)BT * H * 2 >= 0x7fffffffll) return t;
   // pass 1: evenly sized vocabulary blocks (multiples of 64 rows) whose G^T fits
   t.ldv = round_up(BT, 64);
+  // Every stored dlogits block spans less than 2^31 bytes: its kernels address it through one
+  // buffer descriptor with 32-bit offsets and park masked lanes at offset 2^31, which must lie
+  // past the descriptor's range (and the grouped GEMM declines larger transposed operands).
+  const int64_t g_rows_max = (0x7fffffffll / (t.ldv * 2)) / 64 * 64;
   // (grad_b: fp32 partial sums of each vocabulary row per token tile of 256)
   const size_t gb_row = (size_t)cdiv(BT, 256) * 4;
-  const int64_t v_fit = std::min<int64_t>((int64_t)(avail / ((size_t)t.ldv * 2)) / 64 * 64, round_up(V, 64));
+  const int64_t v_fit =
+      std::min<int64_t>({(int64_t)(avail / ((size_t)t.ldv * 2)) / 64 * 64, round_up(V, 64), g_rows_max});
   if (v_fit < 64) return t;
   double best1 = -1.0, best2 = -1.0;
   if (!one_only) {  // (filtered, sorted and per-row calls take the one-pass plan below or none)
@@ -354,7 +361,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, int kind, size_t reserve) {
     const int64_t ks1 = round_up(cdiv(BT, ns1), 64);
     if (ns1 > 1 && cdiv(BT, ks1) != ns1) continue;
     const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0) + gb_row;
-    const int64_t fit = std::min<int64_t>((int64_t)(avail / per_row) / 64 * 64, round_up(V, 64));
+    const int64_t fit = std::min<int64_t>({(int64_t)(avail / per_row) / 64 * 64, round_up(V, 64), g_rows_max});
     if (fit < 64) continue;
     for (int64_t nb = cdiv(V, fit); nb <= cdiv(V, fit) + 8 && nb <= cdiv(V, 64); ++nb) {
       const int64_t vb = std::min(round_up(cdiv(V, nb), 64), fit);
@@ -383,8 +390,8 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, int kind, size_t reserve) {
     for (int64_t ns = 1; ns <= 64; ++ns) {
       const size_t part = ws_align((size_t)ns * (size_t)tb * (size_t)H * 4);
       if (part + 4096 >= avail) break;
-      const int64_t vr_fit = std::min<int64_t>((int64_t)((avail - part) / ((size_t)tb * 2)) / 256 * 256,
-                                               round_up(V, 256));
+      const int64_t vr_fit = std::min<int64_t>({(int64_t)((avail - part) / ((size_t)tb * 2)) / 256 * 256,
+                                                round_up(V, 256), (0x7fffffffll / (tb * 2)) / 256 * 256});
       if (vr_fit < 256 || vr_fit * H * 2 >= 0x7fffffffll) continue;
       for (int64_t nvb = cdiv(V, vr_fit); nvb <= cdiv(V, vr_fit) + 3; ++nvb) {
         const int64_t vr = std::min(round_up(cdiv(V, nvb), 256), vr_fit);
@@ -433,7 +440,7 @@ SgPlan sg_plan(int64_t BT, int64_t H, int64_t V, int kind, size_t reserve) {
       const int64_t ks1 = round_up(cdiv(BT, ns1), 64);
       if (ns1 > 1 && cdiv(BT, ks1) != ns1) continue;
       const size_t per_row = (size_t)t.ldv * 2 + (ns1 > 1 ? (size_t)ns1 * (size_t)H * 4 : 0) + gb_row;
-      const int64_t fit = std::min<int64_t>((int64_t)(avail1 / per_row) / 64 * 64, round_up(V, 64));
+      const int64_t fit = std::min<int64_t>({(int64_t)(avail1 / per_row) / 64 * 64, round_up(V, 64), g_rows_max});
       if (fit < 64) continue;
       // candidates: evenly sized blocks near the fit, and multiples of 256 rows down to half of
       // it (whole 256-row tiles: a grad_W launch of whole rounds of workgroups)

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import linear_cross_entropy_vocab_amd as lce
-from workloads import CONFIGS, make_config
+from workloads import CONFIGS, make_config, make_fused
 from gpu_util import TOL, CE_TOL, dev, host64, rel, rel_fro
 
 pytestmark = pytest.mark.gpu
@@ -216,3 +216,31 @@ def test_filtered_full_size_sampled_tiles(name):
         check(got, o["grad_weight"], o["grad_weight_exact"], f"grad_W entries {v0}..")
         if b is not None:
             check(host64(r["grad_bias"][v0:v0 + R]), o["grad_bias"], o["grad_bias_exact"], f"grad_b entries {v0}..")
+
+
+def test_long_sequence_dlogits_blocks_under_2gib():
+    """400000 tokens, H = 2048, V = 32000: the one-chunk budget (3.9 GiB) would hold a 3 GiB
+    block of stored transposed dlogits, but every block is kept under 2^31 bytes (one buffer
+    descriptor with 32-bit offsets per block), so the call runs the one-pass backward.
+    Sampled tokens' LSE and grad_input rows against the oracle; grad_W by its vanishing
+    vocabulary sum (no z-loss); ignored rows of grad_input exactly zero."""
+    BT, H, V = 400000, 2048, 32000
+    print(f"long-sequence fused call: BT={BT} H={H} V={V}", flush=True)
+    inp = make_fused(BT, H, V, seed=11, ignore_frac=0.05)
+    tol = TOL["bf16"]
+    r = lce.lce_fwd_bwd(dev(inp.hidden, "bf16"), dev(inp.weight, "bf16"), None, dev(inp.targets),
+                        reduction="mean", return_lse=True, method="fused")
+    torch.cuda.synchronize()
+    assert int(r["n_valid"].item()) == int((inp.targets != -100).sum())
+    rows = np.random.default_rng(5).choice(BT, 24, replace=False)
+    rows[:2] = [0, BT - 1]
+    lse = host64(r["lse"][torch.from_numpy(rows).cuda()])
+    want = oracle.lse_rows(inp.hidden, inp.weight, None, rows)
+    assert np.max(np.abs(lse - want) / np.maximum(1.0, np.abs(want))) <= tol["lse"]
+    gi = host64(r["grad_input"][torch.from_numpy(rows).cuda()])
+    assert rel_fro(gi, oracle.grad_input_rows(inp.hidden, inp.weight, None, inp.targets, rows)) <= tol["grad"]
+    ign = torch.from_numpy(inp.targets == -100).cuda()
+    assert bool(ign.any()) and int(torch.count_nonzero(r["grad_input"][ign])) == 0
+    gw = r["grad_weight"].float()
+    assert torch.isfinite(gw).all()
+    assert float(gw.sum(dim=0).norm() / gw.norm()) <= tol["grad"]
